@@ -1,0 +1,503 @@
+// C ABI of the decoder-block library (declared in include/blk.h): argument
+// checks, carving of the caller's saved/scratch buffers, and the launch
+// sequences of the forward and backward passes.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <set>
+#include <vector>
+
+#include "../../include/blk.h"
+#include "attention.cuh"
+#include "elementwise.cuh"
+#include "gemm.cuh"
+
+using namespace blk;
+
+namespace {
+
+// ---------------------------------------------------------------- layout
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* p) : base(static_cast<char*>(p)) {}
+  template <typename X> X* take(size_t count) {
+    off = (off + 255) & ~size_t(255);
+    X* p = base ? reinterpret_cast<X*>(base + off) : nullptr;
+    off += count * sizeof(X);
+    return p;
+  }
+};
+
+// Activations block_fwd keeps for block_bwd (element type T).
+template <typename T> struct Saved {
+  float2* cs;    // [T][64] rotary (cos, sin)
+  float* r1;     // [N]
+  T* h1;         // [N, C]
+  T* qkv;        // [N, 3C]  q'' | k'' | v
+  float* rho;    // [2][N][H]
+  T* o;          // [N, C]
+  float* lse;    // [B*H][T]
+  float* r2;     // [N]
+  T* h2;         // [N, C]
+  T* u;          // [N, F]
+  T* a;          // [N, F]
+  size_t bytes;
+};
+
+template <typename T> Saved<T> carve_saved(const blk_cfg& c, void* p) {
+  const long N = (long)c.B * c.T;
+  Carver k(p);
+  Saved<T> s;
+  s.cs = k.take<float2>((size_t)c.T * 64);
+  s.r1 = k.take<float>(N);
+  s.h1 = k.take<T>(N * c.C);
+  s.qkv = k.take<T>(N * 3 * c.C);
+  s.rho = k.take<float>(2 * N * c.H);
+  s.o = k.take<T>(N * c.C);
+  s.lse = k.take<float>((size_t)c.B * c.H * c.T);
+  s.r2 = k.take<float>(N);
+  s.h2 = k.take<T>(N * c.C);
+  s.u = k.take<T>(N * c.F);
+  s.a = k.take<T>(N * c.F);
+  s.bytes = (k.off + 255) & ~size_t(255);
+  return s;
+}
+
+// Split-k factor of a weight-gradient GEMM: enough workgroups to fill the
+// chip about four times over, each split at least 8 k-steps long.
+int wgrad_splits(int M, int N, long K, int BK) {
+  const int tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  int s = std::max(1, 1024 / tiles);
+  const long ksteps = (K + BK - 1) / BK;
+  s = (int)std::min<long>(s, std::max<long>(1, ksteps / 8));
+  return s;
+}
+
+template <typename T> struct BwdScratch {
+  T* du;        // [N, F]
+  T* dh;        // [N, C] (dh2, later dh1)
+  T* dy1;       // [N, C]
+  T* dO;        // [N, C]
+  T* dqkv;      // [N, 3C]
+  float* delta; // [B*H][T]
+  float* part;  // split-k partial sums
+  size_t bytes;
+};
+
+template <typename T> BwdScratch<T> carve_bwd(const blk_cfg& c, void* p) {
+  const long N = (long)c.B * c.T;
+  Carver k(p);
+  BwdScratch<T> s;
+  s.du = k.take<T>(N * c.F);
+  s.dh = k.take<T>(N * c.C);
+  s.dy1 = k.take<T>(N * c.C);
+  s.dO = k.take<T>(N * c.C);
+  s.dqkv = k.take<T>(N * 3 * c.C);
+  s.delta = k.take<float>((size_t)c.B * c.H * c.T);
+  constexpr int BK = GemmTile<T>::BK;
+  size_t part = 0;
+  const int shapes[4][2] = {{c.C, c.F}, {c.F, c.C}, {c.C, c.C}, {3 * c.C, c.C}};
+  for (auto& sh : shapes) {
+    int sp = wgrad_splits(sh[0], sh[1], N, BK);
+    if (sp > 1) part = std::max(part, (size_t)sp * sh[0] * sh[1]);
+  }
+  s.part = k.take<float>(part);
+  s.bytes = (k.off + 255) & ~size_t(255);
+  return s;
+}
+
+size_t elt_size(const blk_cfg& c) { return c.dtype == BLK_BF16 ? 2 : 4; }
+
+int check_cfg(const blk_cfg* c) {
+  if (!c) return BLK_EINVAL;
+  if (c->B < 1 || c->T < 1 || c->H < 1 || c->D != 128 || c->C != c->H * c->D || c->F != 4 * c->C) return BLK_EINVAL;
+  if (!(c->eps >= 0.f) || !(c->rope_base > 0.f)) return BLK_EINVAL;
+  if (c->dtype != BLK_F32 && c->dtype != BLK_BF16) return BLK_EINVAL;
+  if (c->gemm != BLK_GEMM_NATIVE && c->gemm != BLK_GEMM_FP8_E4M3) return BLK_EINVAL;
+  if (c->gemm == BLK_GEMM_FP8_E4M3) return BLK_EUNSUPPORTED;
+  // row kernels keep a row in registers: 8 chunks of 16 bytes per lane
+  if ((long)c->C * (c->dtype == BLK_BF16 ? 2 : 4) > 8L * 64 * 16) return BLK_EUNSUPPORTED;
+  if ((long)c->B * c->T * 3L * c->C >= (1L << 31)) return BLK_EUNSUPPORTED;
+  return BLK_OK;
+}
+
+bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+int launch_status() { return hipGetLastError() == hipSuccess ? BLK_OK : BLK_ELAUNCH; }
+
+// ---------------------------------------------------------------- timing
+// Optional per-launch timing: while enabled, every launch site records a
+// pair of hipEvents around its kernel(s) on the call's stream.
+struct TimingRec { const char* name; hipEvent_t a, b; };
+std::mutex g_tmu;
+bool g_timing = false;
+std::vector<TimingRec> g_recs;
+std::vector<hipEvent_t> g_pool;
+size_t g_pool_used = 0;
+
+hipEvent_t pool_event() {
+  if (g_pool_used == g_pool.size()) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    g_pool.push_back(e);
+  }
+  return g_pool[g_pool_used++];
+}
+
+struct Timed {
+  const char* name;
+  hipStream_t st;
+  hipEvent_t a = nullptr;
+  Timed(const char* n, hipStream_t s) : name(n), st(s) {
+    if (!g_timing) return;
+    std::lock_guard<std::mutex> l(g_tmu);
+    a = pool_event();
+    if (a) hipEventRecord(a, st);
+  }
+  ~Timed() {
+    if (!a) return;
+    std::lock_guard<std::mutex> l(g_tmu);
+    hipEvent_t b = pool_event();
+    if (!b) return;
+    hipEventRecord(b, st);
+    g_recs.push_back({name, a, b});
+  }
+};
+
+// ---------------------------------------------------------------- launchers
+std::mutex g_attr_mu;
+std::set<const void*> g_attr_done;
+
+void need_lds(const void* kern, int bytes) {
+  std::lock_guard<std::mutex> l(g_attr_mu);
+  if (g_attr_done.insert(kern).second)
+    hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+}
+
+template <typename TI>
+void gemm(void (*kern)(GemmArgs), const char* name, GemmArgs g, int splits, hipStream_t st) {
+  constexpr int LDS = GemmTile<TI>::LDS;
+  need_lds(reinterpret_cast<const void*>(kern), LDS);
+  g.tiles_m = (g.M + 255) / 256;
+  g.tiles_n = (g.N + 255) / 256;
+  if (splits <= 1) {
+    g.k_split = g.K;
+    splits = 1;
+  } else {
+    constexpr int BK = GemmTile<TI>::BK;
+    long per = ((long)g.K + splits - 1) / splits;
+    g.k_split = (int)(((per + BK - 1) / BK) * BK);
+    splits = (g.K + g.k_split - 1) / g.k_split;
+  }
+  Timed t(name, st);
+  hipLaunchKernelGGL(kern, dim3(g.tiles_m * g.tiles_n, splits), dim3(256), LDS, st, g);
+}
+
+GemmArgs gargs(const void* A, long lda, const void* B, long ldb, int M, int N, int K) {
+  GemmArgs g{};
+  g.A = A; g.lda = lda; g.B = B; g.ldb = ldb;
+  g.M = M; g.N = N; g.K = K;
+  g.alpha = 1.f;
+  return g;
+}
+
+// Weight gradient dW[M, N] (+)= sum_t G[t, m] X[t, n]  (G: [K, M], X: [K, N]).
+template <typename T>
+void wgrad(void (*kern)(GemmArgs), void (*kern_acc)(GemmArgs), const char* name, const T* G, const T* X, float* dW,
+           int M, int N, int K, int accumulate, float* part, hipStream_t st) {
+  GemmArgs g = gargs(G, M, X, N, M, N, K);
+  int sp = wgrad_splits(M, N, K, GemmTile<T>::BK);
+  if (sp <= 1) {
+    g.out = dW; g.ldo = N;
+    gemm<T>(accumulate ? kern_acc : kern, name, g, 1, st);
+    return;
+  }
+  g.out = part; g.ldo = N;
+  gemm<T>(kern, name, g, sp, st);
+  // the launcher may round the split count down; recompute it identically
+  constexpr int BK = GemmTile<T>::BK;
+  long per = ((long)K + sp - 1) / sp;
+  int ks = (int)(((per + BK - 1) / BK) * BK);
+  int real = (K + ks - 1) / ks;
+  const long n = (long)M * N;
+  Timed t("splitk_reduce", st);
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, st, dW,
+                     (const float*)part, n, real, accumulate);
+}
+
+unsigned row_blocks(long rows) { return (unsigned)((rows + 3) / 4); }
+
+// ---------------------------------------------------------------- forward
+template <typename T> AttnArgs attn_args(const blk_cfg& c) {
+  AttnArgs a{};
+  a.B = c.B; a.T = c.T; a.H = c.H; a.C = c.C;
+  a.sl2 = (float)(1.4426950408889634 / std::sqrt(128.0));   // log2(e) / sqrt(D)
+  a.rsd = (float)(1.0 / std::sqrt(128.0));
+  return a;
+}
+
+template <typename T>
+int fwd_impl(const blk_cfg& c, const T* x, const T* wqkv, const T* wo, const T* wfc, const T* wproj, T* y,
+             const Saved<T>& s, hipStream_t st) {
+  const int N = c.B * c.T, C = c.C, F = c.F, H = c.H;
+  {  // rotary angle table
+    Timed t("rope_table", st);
+    hipLaunchKernelGGL(rope_table_kernel, dim3((c.T * 64 + 255) / 256), dim3(256), 0, st, s.cs, c.T, 128,
+                       (double)c.rope_base);
+  }
+  {  // 1 h1 = rmsnorm(x)
+    Timed t("rmsnorm_fwd", st);
+    hipLaunchKernelGGL(rmsnorm_fwd_kernel<T>, dim3(row_blocks(N)), dim3(256), 0, st, x, s.h1, s.r1, N, C, c.eps);
+  }
+  {  // 2 qkv = h1 W_qkv^T
+    GemmArgs g = gargs(s.h1, C, wqkv, C, N, 3 * C, C);
+    g.out = s.qkv; g.ldo = 3 * C;
+    gemm<T>(gemm_qkv_fwd<T>, "gemm_qkv_fwd", g, 1, st);
+  }
+  {  // 3-4 rotary, QK-norm (in place on q, k)
+    Timed t("rope_qknorm_fwd", st);
+    hipLaunchKernelGGL(rope_qknorm_fwd_kernel<T>, dim3(row_blocks((long)N * H * 2)), dim3(256), 0, st, s.qkv,
+                       s.rho, (const float2*)s.cs, N, c.T, H, C, c.eps);
+  }
+  {  // 5 causal attention
+    AttnArgs a = attn_args<T>(c);
+    a.qkv = s.qkv; a.o = s.o; a.lse = s.lse;
+    need_lds(reinterpret_cast<const void*>(attn_fwd_kernel<T>), attn_fwd_lds<T>());
+    const int nqt = (c.T + 127) / 128;
+    Timed t("attn_fwd", st);
+    hipLaunchKernelGGL(attn_fwd_kernel<T>, dim3(nqt * c.B * H), dim3(256), attn_fwd_lds<T>(), st, a);
+  }
+  {  // 6 y1 = x + o W_o^T   (y1 is kept in y)
+    GemmArgs g = gargs(s.o, C, wo, C, N, C, C);
+    g.out = y; g.ldo = C; g.aux = x; g.ldaux = C;
+    gemm<T>(gemm_o_fwd<T>, "gemm_o_fwd", g, 1, st);
+  }
+  {  // 7 h2 = rmsnorm(y1)
+    Timed t("rmsnorm_fwd", st);
+    hipLaunchKernelGGL(rmsnorm_fwd_kernel<T>, dim3(row_blocks(N)), dim3(256), 0, st, (const T*)y, s.h2, s.r2, N,
+                       C, c.eps);
+  }
+  {  // 8 u = h2 W_fc^T, a = relu(u)^2
+    GemmArgs g = gargs(s.h2, C, wfc, C, N, F, C);
+    g.out = s.u; g.ldo = F; g.out2 = s.a; g.ldo2 = F;
+    gemm<T>(gemm_fc_fwd<T>, "gemm_fc_fwd", g, 1, st);
+  }
+  {  // 9 y = y1 + a W_proj^T   (in place on y)
+    GemmArgs g = gargs(s.a, F, wproj, F, N, C, F);
+    g.out = y; g.ldo = C; g.aux = y; g.ldaux = C;
+    gemm<T>(gemm_proj_fwd<T>, "gemm_proj_fwd", g, 1, st);
+  }
+  return launch_status();
+}
+
+// ---------------------------------------------------------------- backward
+template <typename T>
+int bwd_impl(const blk_cfg& c, const T* dy, const T* x, const T* wqkv, const T* wo, const T* wfc, const T* wproj,
+             const Saved<T>& s, T* dx, float* dwqkv, float* dwo, float* dwfc, float* dwproj, int acc,
+             const BwdScratch<T>& w, hipStream_t st) {
+  (void)x;
+  const int N = c.B * c.T, C = c.C, F = c.F, H = c.H;
+  {  // 9: du = (dy W_proj) * 2 max(u, 0)
+    GemmArgs g = gargs(dy, C, wproj, F, N, F, C);
+    g.out = w.du; g.ldo = F; g.aux = s.u; g.ldaux = F;
+    gemm<T>(gemm_proj_dgrad<T>, "gemm_proj_dgrad", g, 1, st);
+  }
+  //    dW_proj = dy^T a
+  wgrad<T>(gemm_proj_wgrad<T>, gemm_proj_wgrad_acc<T>, "gemm_proj_wgrad", dy, s.a, dwproj, C, F, N, acc, w.part,
+           st);
+  {  // 8: dh2 = du W_fc
+    GemmArgs g = gargs(w.du, F, wfc, C, N, C, F);
+    g.out = w.dh; g.ldo = C;
+    gemm<T>(gemm_fc_dgrad<T>, "gemm_fc_dgrad", g, 1, st);
+  }
+  //    dW_fc = du^T h2
+  wgrad<T>(gemm_fc_wgrad<T>, gemm_fc_wgrad_acc<T>, "gemm_fc_wgrad", w.du, s.h2, dwfc, F, C, N, acc, w.part, st);
+  {  // 7: dy1 = dy + rmsnorm backward
+    Timed t("rmsnorm_bwd", st);
+    hipLaunchKernelGGL(rmsnorm_bwd_kernel<T>, dim3(row_blocks(N)), dim3(256), 0, st, dy, (const T*)w.dh,
+                       (const T*)s.h2, (const float*)s.r2, w.dy1, N, C);
+  }
+  {  // 6: do = dy1 W_o
+    GemmArgs g = gargs(w.dy1, C, wo, C, N, C, C);
+    g.out = w.dO; g.ldo = C;
+    gemm<T>(gemm_o_dgrad<T>, "gemm_o_dgrad", g, 1, st);
+  }
+  //    dW_o = dy1^T o
+  wgrad<T>(gemm_o_wgrad<T>, gemm_o_wgrad_acc<T>, "gemm_o_wgrad", w.dy1, s.o, dwo, C, C, N, acc, w.part, st);
+  {  // 5: attention backward
+    {
+      Timed t("attn_delta", st);
+      hipLaunchKernelGGL(attn_delta_kernel<T>, dim3(row_blocks((long)N * H)), dim3(256), 0, st, (const T*)w.dO,
+                         (const T*)s.o, w.delta, N, c.T, H, C);
+    }
+    AttnArgs a = attn_args<T>(c);
+    a.qkv = s.qkv; a.lse = s.lse; a.dO = w.dO; a.delta = w.delta; a.dqkv = w.dqkv;
+    need_lds(reinterpret_cast<const void*>(attn_bwd_dq_kernel<T>), attn_dq_lds<T>());
+    need_lds(reinterpret_cast<const void*>(attn_bwd_dkdv_kernel<T>), attn_dkdv_lds<T>());
+    const int nqt = (c.T + 127) / 128;
+    {
+      Timed t("attn_bwd_dkdv", st);
+      hipLaunchKernelGGL(attn_bwd_dkdv_kernel<T>, dim3(nqt * c.B * H), dim3(256), attn_dkdv_lds<T>(), st, a);
+    }
+    {
+      Timed t("attn_bwd_dq", st);
+      hipLaunchKernelGGL(attn_bwd_dq_kernel<T>, dim3(nqt * c.B * H), dim3(256), attn_dq_lds<T>(), st, a);
+    }
+  }
+  {  // 4-3: QK-norm and rotary backward (in place on dq, dk)
+    Timed t("qknorm_rope_bwd", st);
+    hipLaunchKernelGGL(qknorm_rope_bwd_kernel<T>, dim3(row_blocks((long)N * H * 2)), dim3(256), 0, st, w.dqkv,
+                       (const T*)s.qkv, (const float*)s.rho, (const float2*)s.cs, N, c.T, H, C);
+  }
+  {  // 2: dh1 = dqkv W_qkv
+    GemmArgs g = gargs(w.dqkv, 3 * C, wqkv, C, N, C, 3 * C);
+    g.out = w.dh; g.ldo = C;
+    gemm<T>(gemm_qkv_dgrad<T>, "gemm_qkv_dgrad", g, 1, st);
+  }
+  //    dW_qkv = dqkv^T h1
+  wgrad<T>(gemm_qkv_wgrad<T>, gemm_qkv_wgrad_acc<T>, "gemm_qkv_wgrad", w.dqkv, s.h1, dwqkv, 3 * C, C, N, acc,
+           w.part, st);
+  {  // 1: dx = dy1 + rmsnorm backward
+    Timed t("rmsnorm_bwd", st);
+    hipLaunchKernelGGL(rmsnorm_bwd_kernel<T>, dim3(row_blocks(N)), dim3(256), 0, st, (const T*)w.dy1,
+                       (const T*)w.dh, (const T*)s.h1, (const float*)s.r1, dx, N, C);
+  }
+  return launch_status();
+}
+
+size_t saved_bytes(const blk_cfg& c) {
+  return c.dtype == BLK_BF16 ? carve_saved<bf16>(c, nullptr).bytes : carve_saved<float>(c, nullptr).bytes;
+}
+size_t bwd_bytes(const blk_cfg& c) {
+  return c.dtype == BLK_BF16 ? carve_bwd<bf16>(c, nullptr).bytes : carve_bwd<float>(c, nullptr).bytes;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t block_saved_bytes(const blk_cfg* cfg) {
+  if (check_cfg(cfg) != BLK_OK) return 0;
+  return saved_bytes(*cfg);
+}
+
+size_t block_scratch_bytes(const blk_cfg* cfg) {
+  if (check_cfg(cfg) != BLK_OK) return 0;
+  return std::max(saved_bytes(*cfg), bwd_bytes(*cfg));
+}
+
+int block_fwd(const blk_cfg* cfg, const void* x, const void* w_qkv, const void* w_o, const void* w_fc,
+              const void* w_proj, void* y, void* saved, size_t saved_sz, void* scratch, size_t scratch_sz,
+              void* stream) {
+  int e = check_cfg(cfg);
+  if (e) return e;
+  const blk_cfg& c = *cfg;
+  if (!x || !w_qkv || !w_o || !w_fc || !w_proj || !y) return BLK_EINVAL;
+  if (x == y) return BLK_EINVAL;
+  for (const void* p : {x, w_qkv, w_o, w_fc, w_proj, (const void*)y})
+    if (!aligned(p)) return BLK_EALIGN;
+  const size_t need = saved_bytes(c);
+  void* store = saved;
+  if (saved) {
+    if (!aligned(saved)) return BLK_EALIGN;
+    if (saved_sz < need) return BLK_ENOSPC;
+  } else {
+    if (!scratch) return BLK_EINVAL;
+    if (!aligned(scratch)) return BLK_EALIGN;
+    if (scratch_sz < need) return BLK_ENOSPC;
+    store = scratch;
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipGetLastError();
+  if (c.dtype == BLK_BF16)
+    return fwd_impl<bf16>(c, (const bf16*)x, (const bf16*)w_qkv, (const bf16*)w_o, (const bf16*)w_fc,
+                          (const bf16*)w_proj, (bf16*)y, carve_saved<bf16>(c, store), st);
+  return fwd_impl<float>(c, (const float*)x, (const float*)w_qkv, (const float*)w_o, (const float*)w_fc,
+                         (const float*)w_proj, (float*)y, carve_saved<float>(c, store), st);
+}
+
+int block_bwd(const blk_cfg* cfg, const void* dy, const void* x, const void* w_qkv, const void* w_o,
+              const void* w_fc, const void* w_proj, const void* saved, size_t saved_sz, void* dx, float* dw_qkv,
+              float* dw_o, float* dw_fc, float* dw_proj, int accumulate, void* scratch, size_t scratch_sz,
+              void* stream) {
+  int e = check_cfg(cfg);
+  if (e) return e;
+  const blk_cfg& c = *cfg;
+  if (!dy || !x || !w_qkv || !w_o || !w_fc || !w_proj || !saved || !dx || !dw_qkv || !dw_o || !dw_fc || !dw_proj ||
+      !scratch)
+    return BLK_EINVAL;
+  if (accumulate != 0 && accumulate != 1) return BLK_EINVAL;
+  for (const void* p : {dy, x, w_qkv, w_o, w_fc, w_proj, saved, (const void*)dx, (const void*)dw_qkv,
+                        (const void*)dw_o, (const void*)dw_fc, (const void*)dw_proj, (const void*)scratch})
+    if (!aligned(p)) return BLK_EALIGN;
+  if (saved_sz < saved_bytes(c) || scratch_sz < bwd_bytes(c)) return BLK_ENOSPC;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipGetLastError();
+  if (c.dtype == BLK_BF16)
+    return bwd_impl<bf16>(c, (const bf16*)dy, (const bf16*)x, (const bf16*)w_qkv, (const bf16*)w_o,
+                          (const bf16*)w_fc, (const bf16*)w_proj, carve_saved<bf16>(c, const_cast<void*>(saved)),
+                          (bf16*)dx, dw_qkv, dw_o, dw_fc, dw_proj, accumulate, carve_bwd<bf16>(c, scratch), st);
+  return bwd_impl<float>(c, (const float*)dy, (const float*)x, (const float*)w_qkv, (const float*)w_o,
+                         (const float*)w_fc, (const float*)w_proj, carve_saved<float>(c, const_cast<void*>(saved)),
+                         (float*)dx, dw_qkv, dw_o, dw_fc, dw_proj, accumulate, carve_bwd<float>(c, scratch), st);
+}
+
+size_t decode_scratch_bytes(const blk_dcfg* cfg) {
+  (void)cfg;
+  return 0;
+}
+
+int decode_step(const blk_dcfg* cfg, const void* x, const void* w_qkv, const void* w_o, const void* w_fc,
+                const void* w_proj, void* k_cache, void* v_cache, const int32_t* cache_len, void* y, void* scratch,
+                size_t scratch_bytes, void* stream) {
+  (void)cfg; (void)x; (void)w_qkv; (void)w_o; (void)w_fc; (void)w_proj; (void)k_cache; (void)v_cache;
+  (void)cache_len; (void)y; (void)scratch; (void)scratch_bytes; (void)stream;
+  return BLK_EUNSUPPORTED;
+}
+
+void block_timing_enable(int on) {
+  std::lock_guard<std::mutex> l(g_tmu);
+  g_timing = on != 0;
+  g_recs.clear();
+  g_pool_used = 0;
+}
+
+int block_timing_read(int max, const char** names, double* total_ms, int* counts) {
+  std::lock_guard<std::mutex> l(g_tmu);
+  int n = 0;
+  for (const TimingRec& r : g_recs) {
+    if (hipEventSynchronize(r.b) != hipSuccess) return -1;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) return -1;
+    int i = 0;
+    while (i < n && std::strcmp(names[i], r.name) != 0) ++i;
+    if (i == n) {
+      if (n == max) continue;
+      names[n] = r.name; total_ms[n] = 0.0; counts[n] = 0;
+      ++n;
+    }
+    total_ms[i] += ms;
+    counts[i] += 1;
+  }
+  g_recs.clear();
+  g_pool_used = 0;
+  return n;
+}
+
+const char* block_strerror(int code) {
+  switch (code) {
+    case BLK_OK: return "ok";
+    case BLK_EINVAL: return "invalid argument (size, dtype, mode or null pointer)";
+    case BLK_EALIGN: return "pointer not 16-byte aligned";
+    case BLK_ENOSPC: return "saved or scratch buffer too small";
+    case BLK_EUNSUPPORTED: return "configuration not supported";
+    case BLK_ELAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

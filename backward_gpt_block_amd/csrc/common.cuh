@@ -1,0 +1,153 @@
+// Device-side basics shared by the gfx950 kernels: element types, 16-byte
+// chunk moves, MFMA operand traits, wave reductions and the LDS tile swizzle.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace blk {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+
+// One E4M3 code (OCP FP8); a distinct type so templates can tell it apart.
+struct fp8e4 { uint8_t v; };
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16 v) { return (float)v; }
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return (bf16)v; }  // RNE (v_cvt_pk_bf16_f32)
+
+// 16-byte global/LDS moves.
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ __forceinline__ u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
+__device__ __forceinline__ void st8(void* p, u32x2 v) { *reinterpret_cast<u32x2*>(p) = v; }
+
+// Elements of one 16-byte chunk, as float.
+template <typename T> struct Chunk;
+template <> struct Chunk<bf16> {
+  static constexpr int N = 8;
+  __device__ static void unpack(u32x4 c, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(c[i] << 16);
+      f[2 * i + 1] = __uint_as_float(c[i] & 0xffff0000u);
+    }
+  }
+  __device__ static u32x4 pack(const float* f) {
+    bf16x8 b;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) b[i] = (bf16)f[i];
+    return __builtin_bit_cast(u32x4, b);
+  }
+};
+template <> struct Chunk<float> {
+  static constexpr int N = 4;
+  __device__ static void unpack(u32x4 c, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(c[i]);
+  }
+  __device__ static u32x4 pack(const float* f) {
+    u32x4 c;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c[i] = __float_as_uint(f[i]);
+    return c;
+  }
+};
+
+// MFMA 32x32 operand traits.  One instruction: D[32x32] += A[32xKI] B[KIx32].
+// Lane l holds, of A, row l%32 and E consecutive k-slots starting at
+// (l/32)*E; of B, column l%32 and the same k-slots.  The float32 result: lane
+// l, register j holds D[8*(j/4) + 4*(l/32) + j%4][l%32].
+template <typename T> struct Mfma;
+template <> struct Mfma<bf16> {
+  static constexpr int KI = 16, E = 8;
+  typedef bf16x8 frag;
+  __device__ static f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct Mfma<float> {
+  static constexpr int KI = 2, E = 1;
+  typedef float frag;
+  __device__ static f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct Mfma<fp8e4> {
+  static constexpr int KI = 64, E = 32;
+  typedef i32x8 frag;
+  __device__ static f32x16 mma(frag a, frag b, f32x16 c) {
+    // format code 0 = E4M3 for both operands; unit (2^0) block scales
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+  }
+};
+
+__device__ __forceinline__ int acc_row(int j, int lane) { return 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3); }
+
+// Wave-wide reductions (64 lanes).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// LDS tiles are arrays of rows made of 16-byte chunks.  Chunk c of row r is
+// stored at chunk position c ^ swz(r): rows that are read together by the
+// 32 lanes of an MFMA fragment (consecutive rows) and rows written together
+// by the transposing stagers (rows 8 apart) fall on different banks.
+__device__ __forceinline__ int swz(int row, int nchunks) { return (row ^ (row >> 3)) & (nchunks - 1); }
+__device__ __forceinline__ int tile_off(int row, int chunk, int nchunks) {
+  return (row * nchunks + (chunk ^ swz(row, nchunks))) * 16;
+}
+
+// Transpose an n x n block of elements held as n 16-byte rows (n = 8 for
+// 2-byte, 4 for 4-byte elements): out[c] element r = in[r] element c.
+__device__ __forceinline__ void transpose_chunks(const u32x4* in, u32x4* out, bf16*) {
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t lo = in[2 * i][c >> 1], hi = in[2 * i + 1][c >> 1];
+      lo = (c & 1) ? (lo >> 16) : (lo & 0xffffu);
+      hi = (c & 1) ? (hi & 0xffff0000u) : (hi << 16);
+      out[c][i] = lo | hi;
+    }
+  }
+}
+__device__ __forceinline__ void transpose_chunks(const u32x4* in, u32x4* out, float*) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) out[c][r] = in[r][c];
+}
+__device__ __forceinline__ void transpose_chunks(const u32x4* in, u32x4* out, fp8e4*) {
+  // 16 x 16 bytes
+#pragma unroll
+  for (int c = 0; c < 16; ++c) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t w = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        uint32_t src = in[4 * i + b][c >> 2];
+        w |= ((src >> (8 * (c & 3))) & 0xffu) << (8 * b);
+      }
+      out[c][i] = w;
+    }
+  }
+}
+
+}  // namespace blk

@@ -1,0 +1,197 @@
+// Row-wise kernels of the block: RMSNorm forward/backward, the rotary angle
+// table, rotary + QK-norm forward/backward, the attention-backward row dot
+// product and the split-k reduction of weight gradients.  All are HBM-bound:
+// one wave per row, 16-byte accesses along the row.
+#pragma once
+#include "common.cuh"
+
+namespace blk {
+
+constexpr int MAXCH = 8;   // 16-byte chunks per lane a row kernel keeps in registers
+
+// h = x * r, r = (mean(x^2) + eps)^-1/2 per row of C elements.
+// Parameter-free RMSNorm (flicky.cc nanochat page, section on the model,
+// and its glossary entry for RMSNorm, without the gain).
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const T* __restrict__ x, T* __restrict__ h,
+                                                          float* __restrict__ r, int N, int C, float eps) {
+  constexpr int EL = Chunk<T>::N;
+  const int lane = threadIdx.x & 63;
+  const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= N) return;
+  const int nch = C / EL;
+  const T* xr = x + row * C;
+  u32x4 c[MAXCH];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXCH; ++i) {
+    int ch = lane + i * 64;
+    if (ch < nch) {
+      c[i] = ld16(xr + ch * EL);
+      float f[EL];
+      Chunk<T>::unpack(c[i], f);
+#pragma unroll
+      for (int e = 0; e < EL; ++e) ss += f[e] * f[e];
+    }
+  }
+  ss = wave_sum(ss);
+  const float rr = 1.f / sqrtf(ss / (float)C + eps);
+  if (lane == 0 && r) r[row] = rr;
+#pragma unroll
+  for (int i = 0; i < MAXCH; ++i) {
+    int ch = lane + i * 64;
+    if (ch < nch) {
+      float f[EL];
+      Chunk<T>::unpack(c[i], f);
+#pragma unroll
+      for (int e = 0; e < EL; ++e) f[e] *= rr;
+      st16(h + row * C + ch * EL, Chunk<T>::pack(f));
+    }
+  }
+}
+
+// out = resid + r * (dh - hn * mean(dh * hn)): RMSNorm backward (hn is the
+// normalised output) plus the gradient arriving through the residual path.
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const T* __restrict__ resid, const T* __restrict__ dh,
+                                                          const T* __restrict__ hn, const float* __restrict__ r,
+                                                          T* __restrict__ out, int N, int C) {
+  constexpr int EL = Chunk<T>::N;
+  const int lane = threadIdx.x & 63;
+  const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= N) return;
+  const int nch = C / EL;
+  u32x4 cd[MAXCH], ch_[MAXCH];
+  float dot = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXCH; ++i) {
+    int ch = lane + i * 64;
+    if (ch < nch) {
+      cd[i] = ld16(dh + row * C + ch * EL);
+      ch_[i] = ld16(hn + row * C + ch * EL);
+      float a[EL], b[EL];
+      Chunk<T>::unpack(cd[i], a);
+      Chunk<T>::unpack(ch_[i], b);
+#pragma unroll
+      for (int e = 0; e < EL; ++e) dot += a[e] * b[e];
+    }
+  }
+  dot = wave_sum(dot);
+  const float mean = dot / (float)C;
+  const float rr = r[row];
+#pragma unroll
+  for (int i = 0; i < MAXCH; ++i) {
+    int ch = lane + i * 64;
+    if (ch < nch) {
+      float a[EL], b[EL], g[EL];
+      Chunk<T>::unpack(cd[i], a);
+      Chunk<T>::unpack(ch_[i], b);
+      Chunk<T>::unpack(ld16(resid + row * C + ch * EL), g);
+#pragma unroll
+      for (int e = 0; e < EL; ++e) g[e] += rr * (a[e] - b[e] * mean);
+      st16(out + row * C + ch * EL, Chunk<T>::pack(g));
+    }
+  }
+}
+
+// cs[t][i] = (cos, sin) of t * base^(-2i/D), i < D/2, computed in double
+// precision and rounded to float.
+__global__ void rope_table_kernel(float2* __restrict__ cs, int T, int D, double base) {
+  const int half = D / 2;
+  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (long)T * half) return;
+  const int t = idx / half, i = idx % half;
+  const double inv = pow(base, -2.0 * i / (double)D);
+  double s, c;
+  sincos((double)t * inv, &s, &c);
+  cs[idx] = make_float2((float)c, (float)s);
+}
+
+// In place on the q and k parts of qkv [N, 3C]: rotate each pair
+// (z[i], z[i+64]) of a 128-wide head by the token's angle, then RMS-normalise
+// the head (QK-norm).  One wave per (token, head, q|k); lane i owns pair i.
+// rho[(which*N + row)*H + head] = the QK-norm factor.
+// (Rotary embedding and QK-norm: flicky.cc nanochat page, section on the
+// model; CSDN nanochat article, section 一 item 1.)
+template <typename T>
+__global__ __launch_bounds__(256) void rope_qknorm_fwd_kernel(T* __restrict__ qkv, float* __restrict__ rho,
+                                                              const float2* __restrict__ cs, int N, int Tlen,
+                                                              int H, int C, float eps) {
+  const int lane = threadIdx.x & 63;
+  const long w = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const long total = (long)N * H * 2;
+  if (w >= total) return;
+  const int which = w % 2;
+  const int head = (w / 2) % H;
+  const long row = w / (2 * H);
+  const int t = row % Tlen;
+  T* z = qkv + row * 3 * C + which * C + head * 128;
+  const float z1 = to_f32(z[lane]), z2 = to_f32(z[lane + 64]);
+  const float2 a = cs[(long)t * 64 + lane];
+  const float r1 = z1 * a.x - z2 * a.y;
+  const float r2 = z1 * a.y + z2 * a.x;
+  const float ss = wave_sum(r1 * r1 + r2 * r2);
+  const float p = 1.f / sqrtf(ss / 128.f + eps);
+  z[lane] = from_f32<T>(r1 * p);
+  z[lane + 64] = from_f32<T>(r2 * p);
+  if (lane == 0) rho[((long)which * N + row) * H + head] = p;
+}
+
+// In place on the dq, dk parts of dqkv [N, 3C]: QK-norm backward
+// (dz' = rho * (dz'' - z'' * mean(dz'' * z''))) then the transpose rotation.
+// zn = the saved normalised q'' | k'' (qkv layout).
+template <typename T>
+__global__ __launch_bounds__(256) void qknorm_rope_bwd_kernel(T* __restrict__ dqkv, const T* __restrict__ zn,
+                                                              const float* __restrict__ rho,
+                                                              const float2* __restrict__ cs, int N, int Tlen,
+                                                              int H, int C) {
+  const int lane = threadIdx.x & 63;
+  const long w = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const long total = (long)N * H * 2;
+  if (w >= total) return;
+  const int which = w % 2;
+  const int head = (w / 2) % H;
+  const long row = w / (2 * H);
+  const int t = row % Tlen;
+  const long off = row * 3 * C + which * C + head * 128;
+  T* g = dqkv + off;
+  const T* z = zn + off;
+  const float g1 = to_f32(g[lane]), g2 = to_f32(g[lane + 64]);
+  const float z1 = to_f32(z[lane]), z2 = to_f32(z[lane + 64]);
+  const float mean = wave_sum(g1 * z1 + g2 * z2) / 128.f;
+  const float p = rho[((long)which * N + row) * H + head];
+  const float d1 = p * (g1 - z1 * mean), d2 = p * (g2 - z2 * mean);
+  const float2 a = cs[(long)t * 64 + lane];
+  g[lane] = from_f32<T>(d1 * a.x + d2 * a.y);
+  g[lane + 64] = from_f32<T>(-d1 * a.y + d2 * a.x);
+}
+
+// delta[(b*H + head)*T + t] = sum_d do[row, head*128 + d] * o[row, head*128 + d]
+// for row = b*T + t: the row dot product of attention's backward.  One wave
+// per (token, head).
+template <typename T>
+__global__ __launch_bounds__(256) void attn_delta_kernel(const T* __restrict__ dO, const T* __restrict__ O,
+                                                         float* __restrict__ delta, int N, int Tlen, int H, int C) {
+  const int lane = threadIdx.x & 63;
+  const long w = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (w >= (long)N * H) return;
+  const long row = w / H;
+  const int head = w % H;
+  const long off = row * C + head * 128;
+  float s = to_f32(dO[off + lane]) * to_f32(O[off + lane]) + to_f32(dO[off + lane + 64]) * to_f32(O[off + lane + 64]);
+  s = wave_sum(s);
+  const long b = row / Tlen, t = row % Tlen;
+  if (lane == 0) delta[(b * H + head) * Tlen + t] = s;
+}
+
+// dst[i] = (accumulate ? dst[i] : 0) + sum_s part[s*n + i], in split order.
+__global__ void splitk_reduce_kernel(float* __restrict__ dst, const float* __restrict__ part, long n, int splits,
+                                     int accumulate) {
+  const long i4 = ((long)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (i4 >= n) return;
+  f32x4 s = accumulate ? *reinterpret_cast<const f32x4*>(dst + i4) : f32x4{0, 0, 0, 0};
+  for (int k = 0; k < splits; ++k) s += *reinterpret_cast<const f32x4*>(part + (long)k * n + i4);
+  *reinterpret_cast<f32x4*>(dst + i4) = s;
+}
+
+}  // namespace blk

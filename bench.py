@@ -1,0 +1,204 @@
+#!/usr/bin/env python3
+"""Benchmark one training step (forward + backward) of the d20 decoder block
+(B=32, T=2048, width 1280, 10 heads of 128, MLP 5120, bf16) on one MI355X.
+
+Prints ONE JSON line on stdout (details go to stderr):
+  value       tokens per second of the whole step (inputs resident in HBM)
+  tflops      algorithmic FLOP/s of the step (causal attention counted once:
+              per token 72*C^2 for the linear layers + 6*C*(T+1) for attention)
+  roofline    the launch site with the largest share of the step, timed with
+              hipEvents around each of its launches over a second pass of the
+              same K steps (block_timing_*), against the bf16 dense MFMA peak
+  cpu_baseline the float64 CPU oracle on a bounded sample of the workload
+              (whole sequences of it), on this host's cores
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "training tokens/sec and TFLOP/s per decoder block (d20, T=2048) on 1 MI355X"
+PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3, "fp8": 5033.2}
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def step_flops(sh) -> float:
+    N, C, T = sh.B * sh.T, sh.C, sh.T
+    return float(N) * (72.0 * C * C + 6.0 * C * (T + 1))
+
+
+def step_flops_nanochat(sh) -> float:
+    """The convention of nanochat's estimate_flops (6 x matmul params + 12*C*T
+    per token for attention), which reproduces the depth table on the
+    flicky.cc nanochat page."""
+    N, C, T = sh.B * sh.T, sh.C, sh.T
+    return float(N) * (72.0 * C * C + 12.0 * C * T)
+
+
+def site_flops(sh) -> dict:
+    """Algorithmic FLOPs of one launch of each launch site."""
+    N, C, F, T = sh.B * sh.T, sh.C, sh.F, sh.T
+    att = float(N) * C * (T + 1)          # one causal T x T x D matmul over all heads
+    g = {
+        "gemm_qkv_fwd": 2.0 * N * C * 3 * C, "gemm_o_fwd": 2.0 * N * C * C,
+        "gemm_fc_fwd": 2.0 * N * C * F, "gemm_proj_fwd": 2.0 * N * F * C,
+        "attn_fwd": 2 * att,
+        "attn_bwd_dkdv": 3 * att,      # dV = P^T dO, dP = dO V^T, dK = dS^T Q
+        "attn_bwd_dq": 1 * att,        # dQ = dS K
+    }
+    for p in ("qkv", "o", "fc", "proj"):
+        g[f"gemm_{p}_dgrad"] = g[f"gemm_{p}_fwd"]
+        g[f"gemm_{p}_wgrad"] = g[f"gemm_{p}_fwd"]
+    return g
+
+
+def cpu_baseline(sh, inp, budget_s: float = 12.0) -> dict:
+    """Oracle forward + backward on whole sequences of the workload until the
+    budget is spent (at least one sequence)."""
+    from oracle import block as ob
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:
+        threads = os.cpu_count() or 1
+    W = (inp["w_qkv"], inp["w_o"], inp["w_fc"], inp["w_proj"])
+    t0 = time.perf_counter()
+    nseq = 0
+    while nseq < sh.B:
+        c = ob.block_fwd(inp["x"][nseq:nseq + 1], *W, H=sh.H, eps=sh.eps, rope_base=sh.rope_base)
+        ob.block_bwd(inp["dy"][nseq:nseq + 1], c, *W, H=sh.H)
+        nseq += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": nseq * sh.T / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{nseq} of {sh.B} sequences (T={sh.T}) of the workload, float64 numpy, {dt:.1f} s",
+            "seconds": dt, "host_cpus": os.cpu_count(),
+            "affinity_cpus": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="d20_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: the block step is measured on one GPU's share "
+              "(see the sharding notes); --gpus must be 1", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import backward_gpt_block_amd as bl
+    from blockinputs import WORKLOADS, make_block_inputs, to_storage
+
+    sh = WORKLOADS[args.workload]
+    dt = sh.dtype
+    log(f"workload {args.workload}: {sh}")
+    t0 = time.perf_counter()
+    inp = make_block_inputs(sh, seed=0)
+    log(f"inputs generated in {time.perf_counter() - t0:.1f} s")
+
+    def dev(a):
+        st = to_storage(a, dt)
+        t = torch.from_numpy(st.view(np.int16) if dt == "bf16" else st)
+        return (t.view(torch.bfloat16) if dt == "bf16" else t).to("cuda:0")
+
+    x, dy = dev(inp["x"]), dev(inp["dy"])
+    W = [dev(inp[k]) for k in ("w_qkv", "w_o", "w_fc", "w_proj")]
+    cfg = bl.BlockConfig(B=sh.B, T=sh.T, C=sh.C, H=sh.H, F=sh.F, eps=sh.eps, rope_base=sh.rope_base,
+                         dtype=bl.BLK_BF16 if dt == "bf16" else bl.BLK_F32,
+                         gemm=bl.BLK_GEMM_FP8_E4M3 if sh.gemm == "fp8" else bl.BLK_GEMM_NATIVE)
+    y, dx = torch.empty_like(x), torch.empty_like(x)
+    dW = [torch.empty(w.shape, dtype=torch.float32, device="cuda:0") for w in W]
+    saved = torch.empty(bl.block_saved_bytes(cfg), dtype=torch.uint8, device="cuda:0")
+    scratch = torch.empty(bl.block_scratch_bytes(cfg), dtype=torch.uint8, device="cuda:0")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        bl.block_fwd(cfg, x, *W, y, saved, scratch, stream=stream)
+        bl.block_bwd(cfg, dy, x, *W, saved, dx, *dW, 0, scratch, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K steps between two synchronisations, hipEvents on the stream
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    log(f"step: {ms:.3f} ms (wall {1e3 * wall / args.steps:.3f} ms)")
+
+    # per-launch-site times over a second pass of the same K steps
+    bl.block_timing_enable(True)
+    for _ in range(args.steps):
+        step()
+    sites = bl.block_timing_read()
+    bl.block_timing_enable(False)
+    torch.cuda.synchronize()
+    total_inst = sum(v[0] for v in sites.values())
+    fl = site_flops(sh)
+    log(f"{'site':22s} {'ms/step':>9s} {'share':>6s} {'avg ms':>8s} {'TFLOP/s':>8s}")
+    for k, (tot, cnt) in sorted(sites.items(), key=lambda kv: -kv[1][0]):
+        avg = tot / cnt
+        tf = fl[k] / (avg * 1e-3) / 1e12 if k in fl else float("nan")
+        log(f"{k:22s} {tot / args.steps:9.3f} {tot / total_inst:6.1%} {avg:8.3f} {tf:8.1f}")
+    dom = max(sites.items(), key=lambda kv: kv[1][0])
+    dname, (dtot, dcnt) = dom
+    davg_ms = dtot / dcnt
+    if dname in fl:
+        achieved = fl[dname] / (davg_ms * 1e-3) / 1e12
+        peak = PEAK_TFLOPS["fp8" if sh.gemm == "fp8" and dname.startswith("gemm") else dt]
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": None, "kernel": dname,
+                "avg_launch_ms": round(davg_ms, 4), "flops_per_launch": fl[dname]}
+    else:
+        roof = {"bound": "hbm", "achieved": None, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": None,
+                "traffic": None, "kernel": dname, "avg_launch_ms": round(davg_ms, 4)}
+
+    tokens = sh.B * sh.T
+    tflops = step_flops(sh) / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS["bf16" if dt == "bf16" else dt]
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        cpu = cpu_baseline(sh, inp, args.cpu_budget)
+        log(f"cpu baseline: {cpu}")
+    out = {
+        "metric": METRIC, "value": round(tokens / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": dt, "data": "synthetic",
+        "config": {"workload": args.workload, "B": sh.B, "T": sh.T, "C": sh.C, "H": sh.H, "D": sh.D, "F": sh.F,
+                   "gemm": sh.gemm, "tokens_per_step": tokens, "parallelism": "none (1 GPU)"},
+        "tflops": round(tflops, 2), "frac_of_peak": round(tflops / peak, 4),
+        "tflops_nanochat_convention": round(step_flops_nanochat(sh) / (ms * 1e-3) / 1e12, 2),
+        "roofline": roof, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

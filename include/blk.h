@@ -1,0 +1,159 @@
+/*
+ * blk.h -- C ABI of the MI355X (gfx950) decoder-block library.
+ *
+ * One training step (forward + backward) and one KV-cache decode step of the
+ * dense GPT decoder block that nanochat trains:
+ *
+ *   h1 = rmsnorm(x)                       parameter-free RMSNorm
+ *   [q|k|v] = h1 W_qkv^T                  fused QKV projection, no bias
+ *   q, k <- rotary(q, k); q, k <- rmsnorm  rotary embedding, then QK-norm
+ *   o = softmax(q k^T / sqrt(D), causal) v   multi-head attention, D = 128
+ *   y1 = x + o W_o^T                      output projection + residual
+ *   h2 = rmsnorm(y1)
+ *   y = y1 + relu(h2 W_fc^T)^2 W_proj^T   4x MLP with ReLU^2 + residual
+ *
+ * Sources: the flicky.cc course page "nanochat: свой ChatGPT от токенизатора
+ * до чата", section "Модель: что изменилось со времён GPT-2" (rotary, QK-norm,
+ * ReLU^2, parameter-free RMSNorm, no biases); the CSDN article "4小时100美元！
+ * Andrej Karpathy新开源项目nanochat..." section 一 item 1 (dense Llama-like
+ * transformer, rotary, QK norm); the 7minutos.es article, section "Modelo,
+ * escalado y objetivo de speedrun" (d20: 1280 channels, 10 heads of 128); the
+ * README mirror "karpathy/nanochat", section "精度 / dtype" (weights kept in
+ * fp32 and cast to the compute dtype inside the linear layer; bf16 compute).
+ *
+ * Conventions shared by every entry point
+ *   - Every data pointer is a DEVICE pointer, 16-byte aligned, to a dense
+ *     row-major array; the caller allocates and owns every buffer.  The
+ *     library allocates no memory, keeps no pointer after returning, and
+ *     holds no state between calls (except the lazily loaded kernels).
+ *   - Weights are [out, in] and act as y = x W^T (the PyTorch Linear layout).
+ *   - Element type of activations and weights: cfg->dtype (BLK_F32 or
+ *     BLK_BF16).  Weight gradients are always float32.  Statistics, softmax
+ *     and every MFMA accumulation are float32.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  All work is
+ *     enqueued on it, in order, with no host synchronisation; results are
+ *     ready when the stream reaches that point.
+ *   - Return value: BLK_OK, or an error code below.  Every argument is
+ *     checked on the host before any launch; on an error nothing has been
+ *     enqueued.  Device faults surface at the caller's next synchronisation.
+ *     No C++ exception crosses this interface.
+ *   - Sizes: D must be 128, C == H*D, F == 4*C; B, T >= 1.  Any T is
+ *     accepted (ragged tiles are masked inside the kernels).
+ */
+#ifndef BLK_H
+#define BLK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum blk_status {
+  BLK_OK = 0,
+  BLK_EINVAL = 1,        /* bad size, dtype, mode or NULL pointer            */
+  BLK_EALIGN = 2,        /* a pointer is not 16-byte aligned                 */
+  BLK_ENOSPC = 3,        /* saved/scratch buffer smaller than required       */
+  BLK_EUNSUPPORTED = 4,  /* valid but not provided (e.g. fp8 with float32)   */
+  BLK_ELAUNCH = 5        /* a kernel launch failed (hipGetLastError)          */
+};
+
+enum blk_dtype { BLK_F32 = 0, BLK_BF16 = 1 };
+
+/* GEMM mode of the four linear layers.  BLK_GEMM_FP8_E4M3: every GEMM of
+ * every linear layer (forward, input gradient, weight gradient) takes OCP
+ * E4M3 operands with per-tensor current scaling s = amax/448, accumulates in
+ * float32 and applies s_A*s_B in its epilogue; attention, norms and rotary
+ * stay in bf16.  Requires dtype == BLK_BF16.  (FP8 training of the linear
+ * layers: the flicky.cc page's repository map row for nanochat/fp8.py and the
+ * README mirror's leaderboard row "d26 ... +fp8".) */
+enum blk_gemm_mode { BLK_GEMM_NATIVE = 0, BLK_GEMM_FP8_E4M3 = 1 };
+
+typedef struct {
+  int32_t B, T;        /* sequences, tokens per sequence                     */
+  int32_t C, H, D, F;  /* width, heads, head size (128), MLP width (4C)     */
+  float eps;           /* RMSNorm / QK-norm epsilon (1e-6 in the workloads) */
+  float rope_base;     /* rotary base (10000)                                */
+  int32_t dtype;       /* enum blk_dtype                                     */
+  int32_t gemm;        /* enum blk_gemm_mode                                 */
+} blk_cfg;
+
+typedef struct {
+  int32_t B;           /* sequences, one new token each                      */
+  int32_t C, H, D, F;
+  int32_t S_max;       /* cache capacity (slots) per sequence and head       */
+  float eps, rope_base;
+  int32_t dtype;       /* BLK_BF16 or BLK_F32                                */
+} blk_dcfg;
+
+/* Bytes of the activation store that block_fwd fills for block_bwd.
+ * Returns 0 for an invalid cfg. */
+size_t block_saved_bytes(const blk_cfg* cfg);
+
+/* Bytes of temporary device memory block_fwd / block_bwd need (the larger
+ * of the two; covers block_fwd with saved == NULL).  0 for an invalid cfg. */
+size_t block_scratch_bytes(const blk_cfg* cfg);
+
+/* Forward of the block.
+ *   x      [B,T,C]   input rows (dtype)
+ *   w_qkv  [3C,C], w_o [C,C], w_fc [F,C], w_proj [C,F]   (dtype)
+ *   y      [B,T,C]   output (dtype); may not alias x
+ *   saved  activation store of block_saved_bytes(cfg) bytes, written here and
+ *          read by block_bwd; NULL for inference only
+ *   scratch            block_scratch_bytes(cfg) bytes
+ * The rotary angle of token t of each sequence is t * rope_base^(-2i/D). */
+int block_fwd(const blk_cfg* cfg, const void* x,
+              const void* w_qkv, const void* w_o, const void* w_fc, const void* w_proj,
+              void* y, void* saved, size_t saved_bytes,
+              void* scratch, size_t scratch_bytes, void* stream);
+
+/* Backward of the block: gradients of <dy, y>.
+ *   dy     [B,T,C]   upstream gradient (dtype)
+ *   x, weights: as passed to the block_fwd that filled `saved`
+ *   dx     [B,T,C]   input gradient (dtype), written
+ *   dw_*   float32 weight gradients, same shapes as the weights; overwritten
+ *          when accumulate == 0, added to when accumulate == 1 (gradient
+ *          accumulation over micro-batches)
+ * Deterministic: the same inputs give bitwise the same outputs. */
+int block_bwd(const blk_cfg* cfg, const void* dy, const void* x,
+              const void* w_qkv, const void* w_o, const void* w_fc, const void* w_proj,
+              const void* saved, size_t saved_bytes, void* dx,
+              float* dw_qkv, float* dw_o, float* dw_fc, float* dw_proj, int accumulate,
+              void* scratch, size_t scratch_bytes, void* stream);
+
+/* Bytes of temporary device memory decode_step needs.  0 for invalid cfg. */
+size_t decode_scratch_bytes(const blk_dcfg* cfg);
+
+/* One decode step: a new token per sequence at position p_b = cache_len[b].
+ *   x       [B,C]               new rows (dtype)
+ *   k_cache, v_cache [B,H,S_max,D]  (dtype) keys after rotary and QK-norm,
+ *           and values; slot p_b of each (b, h) is written here, slots
+ *           0..p_b are attended, slots beyond p_b are neither read nor written
+ *   cache_len [B] int32 DEVICE array, read only (the caller advances it);
+ *           every entry must satisfy 0 <= cache_len[b] <= S_max-1 (entries
+ *           outside that range are clamped into it by the kernels)
+ *   y       [B,C] output (dtype) */
+int decode_step(const blk_dcfg* cfg, const void* x,
+                const void* w_qkv, const void* w_o, const void* w_fc, const void* w_proj,
+                void* k_cache, void* v_cache, const int32_t* cache_len, void* y,
+                void* scratch, size_t scratch_bytes, void* stream);
+
+/* Measurement hooks (for benchmarks; not needed to compute anything).
+ * block_timing_enable(1) starts recording, for every kernel launch site of
+ * the calls above, a pair of hipEvents around the launch on the call's
+ * stream; block_timing_enable(0) stops.  Either call drops what was recorded.
+ * block_timing_read waits for the recorded events, then fills up to `max`
+ * entries: names[i] (static strings naming the launch site, e.g.
+ * "gemm_fc_fwd", "attn_fwd"), total_ms[i] and counts[i] (launches), clears
+ * the records, and returns the number of entries (-1 on a HIP error). */
+void block_timing_enable(int on);
+int block_timing_read(int max, const char** names, double* total_ms, int* counts);
+
+/* Static, human-readable text of a status code. */
+const char* block_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BLK_H */

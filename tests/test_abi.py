@@ -1,0 +1,112 @@
+"""Host-side checks of the C ABI (no GPU needed): the built library loads and
+exports every function include/blk.h declares; size queries; every argument
+error is reported before any HIP call (fake, never-dereferenced addresses)."""
+import os
+import re
+
+import pytest
+
+import backward_gpt_block_amd as bl
+from blockinputs import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bl.library_path()):
+        from backward_gpt_block_amd.build import build
+        build()
+    return bl.library()
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "blk.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_function(lib):
+    names = _header_functions()
+    assert {"block_fwd", "block_bwd", "decode_step", "block_saved_bytes", "block_scratch_bytes",
+            "decode_scratch_bytes", "block_strerror"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def _cfg(**kw):
+    sh = WORKLOADS["d20_bf16"]
+    d = dict(B=sh.B, T=sh.T, C=sh.C, H=sh.H, F=sh.F)
+    d.update(kw)
+    return bl.BlockConfig(**d)
+
+
+def test_size_queries(lib):
+    c = _cfg()
+    saved = bl.block_saved_bytes(c)
+    N, C, F = 32 * 2048, 1280, 5120
+    # saved activations: h1, o, h2 (N*C), qkv (3NC), u, a (N*F) in bf16, plus small fp32 vectors
+    assert saved >= 2 * (6 * N * C + 2 * N * F)
+    assert saved < 2 * (6 * N * C + 2 * N * F) * 1.05
+    assert bl.block_scratch_bytes(c) >= saved
+    f32 = _cfg(dtype=bl.BLK_F32)
+    assert bl.block_saved_bytes(f32) > 1.9 * saved
+    for bad in (_cfg(D=64), _cfg(C=1000), _cfg(F=4000), _cfg(B=0), _cfg(T=0), _cfg(dtype=7)):
+        assert bl.block_saved_bytes(bad) == 0
+        assert bl.block_scratch_bytes(bad) == 0
+
+
+A = 0x10000     # aligned fake addresses: the calls below must fail before any use
+MIS = 0x10008
+
+
+def _fwd(cfg, **kw):
+    args = dict(x=A, w_qkv=A + 0x100, w_o=A + 0x200, w_fc=A + 0x300, w_proj=A + 0x400, y=A + 0x500,
+                saved=A + 0x600, scratch=A + 0x700, saved_bytes=1 << 40, scratch_bytes=1 << 40)
+    args.update(kw)
+    return bl.block_fwd(cfg, args.pop("x"), args.pop("w_qkv"), args.pop("w_o"), args.pop("w_fc"),
+                        args.pop("w_proj"), args.pop("y"), args.pop("saved"), args.pop("scratch"),
+                        raise_on_error=False, stream=0, **args)
+
+
+def _bwd(cfg, **kw):
+    args = dict(dy=A, x=A, w_qkv=A, w_o=A, w_fc=A, w_proj=A, saved=A, dx=A + 0x800, dw_qkv=A, dw_o=A, dw_fc=A,
+                dw_proj=A, accumulate=0, scratch=A, saved_bytes=1 << 40, scratch_bytes=1 << 40)
+    args.update(kw)
+    pos = [args.pop(k) for k in ("dy", "x", "w_qkv", "w_o", "w_fc", "w_proj", "saved", "dx", "dw_qkv", "dw_o",
+                                 "dw_fc", "dw_proj", "accumulate", "scratch")]
+    return bl.block_bwd(cfg, *pos, raise_on_error=False, stream=0, **args)
+
+
+def test_fwd_argument_errors(lib):
+    c = _cfg()
+    assert _fwd(_cfg(D=64)) == bl.binding.BLK_EINVAL
+    assert _fwd(_cfg(C=1000)) == bl.binding.BLK_EINVAL
+    assert _fwd(c, x=None) == bl.binding.BLK_EINVAL
+    assert _fwd(c, w_proj=None) == bl.binding.BLK_EINVAL
+    assert _fwd(c, y=A) == bl.binding.BLK_EINVAL          # y aliases x
+    assert _fwd(c, w_o=MIS) == bl.binding.BLK_EALIGN
+    assert _fwd(c, saved_bytes=10) == bl.binding.BLK_ENOSPC
+    assert _fwd(c, saved=None, scratch_bytes=10) == bl.binding.BLK_ENOSPC
+    assert _fwd(c, saved=None, scratch=None) == bl.binding.BLK_EINVAL
+    assert _fwd(_cfg(gemm=bl.BLK_GEMM_FP8_E4M3, dtype=bl.BLK_F32)) == bl.binding.BLK_EUNSUPPORTED
+    assert _fwd(_cfg(gemm=5)) == bl.binding.BLK_EINVAL
+    assert _fwd(_cfg(eps=float("nan"))) == bl.binding.BLK_EINVAL
+
+
+def test_bwd_argument_errors(lib):
+    c = _cfg()
+    assert _bwd(c, saved=None) == bl.binding.BLK_EINVAL
+    assert _bwd(c, dw_fc=None) == bl.binding.BLK_EINVAL
+    assert _bwd(c, scratch=None) == bl.binding.BLK_EINVAL
+    assert _bwd(c, accumulate=2) == bl.binding.BLK_EINVAL
+    assert _bwd(c, dx=MIS) == bl.binding.BLK_EALIGN
+    assert _bwd(c, scratch_bytes=100) == bl.binding.BLK_ENOSPC
+    assert _bwd(c, saved_bytes=100) == bl.binding.BLK_ENOSPC
+    assert _bwd(_cfg(H=0, C=0, F=0)) == bl.binding.BLK_EINVAL
+
+
+def test_strerror(lib):
+    for code in range(6):
+        assert isinstance(bl.block_strerror(code), str) and bl.block_strerror(code)
+    assert "unknown" in bl.block_strerror(99)

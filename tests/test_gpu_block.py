@@ -1,0 +1,116 @@
+"""GPU parity of block_fwd + block_bwd (through the C ABI) against the CPU
+float64 oracle, on seeded inputs, plus invariants the method fixes
+(causality, T = 1, determinism, accumulation).
+
+Gate: relative Frobenius error per output tensor (y, dx, dW_qkv, dW_o,
+dW_fc, dW_proj) <= 1e-4 for float32 and <= 2e-2 for bfloat16 operands."""
+import numpy as np
+import pytest
+
+from blockinputs import WORKLOADS, BlockShape, make_block_inputs
+
+from gpu_util import TOL, GpuBlock, compare, note, oracle_step, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(sh: BlockShape, seed=0):
+    inp = make_block_inputs(sh, seed=seed)
+    g = GpuBlock(sh, inp)
+    g.fwd()
+    g.bwd()
+    return g, inp
+
+
+def _parity(sh: BlockShape, seed=0):
+    note(f"parity B={sh.B} T={sh.T} C={sh.C} H={sh.H} dtype={sh.dtype} seed={seed}")
+    g, inp = _run(sh, seed)
+    return compare(g.results(), oracle_step(sh, inp), TOL[sh.dtype])
+
+
+def test_d6_f32_full_workload():
+    _parity(WORKLOADS["d6_f32"])
+
+
+@pytest.mark.parametrize("B,T,C", [
+    (2, 300, 256),    # two query tiles of 128 and a ragged tail of 44
+    (1, 77, 384),     # one partial tile
+    (3, 1, 256),      # T = 1
+    (1, 520, 768),    # d12 width, ragged
+])
+def test_bf16_ragged(B, T, C):
+    _parity(BlockShape(B=B, T=T, C=C, H=C // 128, F=4 * C, dtype="bf16"))
+
+
+@pytest.mark.parametrize("T", [1, 45, 130])
+def test_f32_ragged(T):
+    _parity(BlockShape(B=2, T=T, C=256, H=2, F=1024, dtype="f32"), seed=3)
+
+
+def _sampled_full(name, keep):
+    """Full-size workload; the upstream gradient is zero outside the sampled
+    sequences, so every gradient (dx and dW) comes from them alone and the
+    oracle only needs those sequences."""
+    sh = WORKLOADS[name]
+    note(f"sampled full-size {name} keep={keep}")
+    inp = make_block_inputs(sh, seed=0)
+    mask = np.zeros(sh.B, dtype=bool)
+    mask[list(keep)] = True
+    inp["dy"] = np.where(mask[:, None, None], inp["dy"], 0.0)
+    g = GpuBlock(sh, inp)
+    g.fwd()
+    g.bwd()
+    res = g.results()
+    ref = oracle_step(sh, inp, batch=list(keep))
+    res["y"] = res["y"][list(keep)]
+    res["dx"] = res["dx"][list(keep)]
+    return compare(res, ref, TOL[sh.dtype])
+
+
+def test_d12_full_size_sampled():
+    _sampled_full("d12_bf16", (0, 7))
+
+
+def test_d20_full_size_sampled():
+    _sampled_full("d20_bf16", (0, 31))
+
+
+def test_causality_bitwise():
+    sh = BlockShape(B=2, T=200, C=256, H=2, F=1024, dtype="bf16")
+    note("causality")
+    inp = make_block_inputs(sh, seed=5)
+    g = GpuBlock(sh, inp)
+    g.fwd()
+    y0 = g.results()["y"].copy()
+    t = 97
+    x2 = inp["x"].copy()
+    x2[:, t + 1:] = np.random.default_rng(7).standard_normal(x2[:, t + 1:].shape)
+    g.fwd(x=to_dev(x2, "bf16"))
+    y1 = g.results()["y"]
+    assert np.array_equal(y0[:, :t + 1], y1[:, :t + 1])
+    assert not np.array_equal(y0[:, t + 1:], y1[:, t + 1:])
+
+
+def test_determinism_and_accumulate():
+    sh = BlockShape(B=2, T=160, C=256, H=2, F=1024, dtype="bf16")
+    note("determinism / accumulate")
+    g, inp = _run(sh, seed=2)
+    r1 = g.results()
+    g.fwd()
+    g.bwd()
+    r2 = g.results()
+    for k in r1:
+        assert np.array_equal(r1[k], r2[k]), k
+    g.bwd(accumulate=1)
+    r3 = g.results()
+    for k in ("dw_qkv", "dw_o", "dw_fc", "dw_proj"):
+        assert np.allclose(r3[k], 2 * r1[k], rtol=1e-6, atol=1e-6), k
+
+
+def test_t1_value_path_gradients_vanish_for_q_k():
+    sh = BlockShape(B=4, T=1, C=256, H=2, F=1024, dtype="f32")
+    note("T=1 value path")
+    g, inp = _run(sh, seed=4)
+    r = g.results()
+    C = sh.C
+    assert np.max(np.abs(r["dw_qkv"][:2 * C])) <= 1e-5 * np.max(np.abs(r["dw_qkv"][2 * C:]))
