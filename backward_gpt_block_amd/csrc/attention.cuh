@@ -19,6 +19,7 @@
 // rotary precede it: flicky.cc nanochat page, section on the model.)
 #pragma once
 #include "common.cuh"
+#include "gemm.cuh"
 
 namespace blk {
 
@@ -356,7 +357,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(AttnArgs a) {
       for (int kb = 0; kb < A::NB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float p = exp2f(s[kb][r] * a.sl2 - lse);
+          float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], a.sl2, -lse));
           if (need_mask) {
             const int key = k0 + kb * 32 + acc_row(r, lane);
             if (key > q || key >= a.T) p = 0.f;
@@ -460,7 +461,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(AttnArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * g + e;
-            float p = exp2f(s[r] * a.sl2 - lv[e]);
+            float p = __builtin_amdgcn_exp2f(fmaf(s[r], a.sl2, -lv[e]));
             if (need_mask && key > q0 + qi + e) p = 0.f;
             s[r] = p;
             dp[r] = p * (dp[r] - dv4[e]);    // dS
@@ -487,6 +488,451 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(AttnArgs a) {
     store_acc_row<T>(row + a.C, dk, a.rsd, lane);
     store_acc_row<T>(row + 2 * a.C, dv, 1.f, lane);
   }
+}
+
+// ---- forward, bf16, direct-to-LDS pipeline ------------------------------------------
+// One workgroup = 256 queries of one (sequence, head): 4 waves x 64 queries
+// (two 32-query MFMA blocks that share every K and V fragment read, halving
+// LDS traffic per MFMA).  Key tiles of 64 rows, K and V row-major in LDS,
+// staged by buffer loads straight into LDS in a three-slot ring (prefetch
+// distance two tiles).  V^T fragments come from the row-major V tile through
+// the LDS transpose read (ds_read_b64_tr_b16).  Row layout: 16 chunks of 16
+// bytes per 128-wide row, chunk c of row r stored at c ^ (r & 15).
+namespace fa {
+constexpr int QW = 64;                 // queries per wave
+constexpr int QWG = 4 * QW;            // queries per workgroup
+constexpr int KT = 64;                 // keys per tile
+constexpr int TILE = KT * 256;         // bytes of one [64][128] bf16 tile
+constexpr int SLOT = 2 * TILE;         // K + V
+constexpr int NSLOT = 3;
+constexpr int LDS = NSLOT * SLOT;      // 96 KiB
+
+__device__ __forceinline__ int off(int row, int chunk) { return row * 256 + ((chunk ^ (row & 15)) << 4); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Issue the direct-to-LDS loads of key rows k0.. of K and V (rows >= T read 0).
+__device__ __forceinline__ void issue_kv(char* slot, i32x4 rs, int k0, long ldb, int koff, int voff, int wave,
+                                         int lane) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {                 // K, then V
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int base = wave * 256 + i * 64;     // chunk index in the tile (64 per issue)
+      const int p = base + lane;
+      const int row = p >> 4, c = (p & 15) ^ (row & 15);
+      const uint32_t o = (uint32_t)((long)(k0 + row) * ldb + (t ? voff : koff) + c * 16);
+      lds_u32* dst = (lds_u32*)(slot + t * TILE + __builtin_amdgcn_readfirstlane(base) * 16);
+      raw_buffer_load_lds(rs, dst, 16, (int)o, 0, 0, 0);
+    }
+  }
+}
+
+// A fragment (rows = keys kb*32 + l%32, k-substep ks over d) of a row tile.
+__device__ __forceinline__ bf16x8 frag_k(const char* tile, int kb, int ks, int lane) {
+  const int row = kb * 32 + (lane & 31);
+  return __builtin_bit_cast(bf16x8, ld16(tile + off(row, 2 * ks + (lane >> 5))));
+}
+
+// Per-lane byte offsets of the row-tile fragment reads, k-substep ks (add
+// kb*8192 for key block kb): row l%32, chunk 2ks + l/32, swizzled.
+__device__ __forceinline__ void frag_k_offsets(int* o, int lane) {
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) o[ks] = off(lane & 31, 2 * ks + (lane >> 5));
+}
+
+// Per-lane byte offsets of the V^T transpose reads, run (0, 1) and d-block db
+// (add mm*4096 for MFMA chunk mm: 16 rows of 256 bytes, the swizzle only
+// depends on row & 15).
+__device__ __forceinline__ void frag_vt_offsets(int* o, int lane) {
+  const int g = (lane >> 4) & 3, s = lane & 15;
+#pragma unroll
+  for (int run = 0; run < 2; ++run)
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int key = 4 * (g >> 1) + (s >> 2) + 8 * run;
+      const int col = db * 32 + 16 * (g & 1) + 4 * (s & 3);
+      o[run * 4 + db] = off(key, col >> 3) + (col & 7) * 2;
+    }
+}
+
+typedef __attribute__((address_space(3))) char lds_char;
+
+__device__ __forceinline__ bf16x8 frag_vt_at(const lds_char* tile, const int* vo, int mm, int db) {
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + mm * 4096 + vo[db]));
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + mm * 4096 + vo[4 + db]));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// A fragment of V^T for MFMA chunk mm (16 keys) and d-block db: lane l holds
+// d = db*32 + l%32 and keys 16mm + 4h + {0..3}, 16mm + 8 + 4h + {0..3} (h = l/32),
+// the key order of the P^T fragment built from the score registers.
+__device__ __forceinline__ bf16x8 frag_vt(const char* tile, int mm, int db, int lane) {
+  const int g = (lane >> 4) & 3, s = lane & 15;
+  const int key = 16 * mm + 4 * (g >> 1) + (s >> 2);
+  const int col = db * 32 + 16 * (g & 1) + 4 * (s & 3);
+  const char* p0 = tile + off(key, col >> 3) + (col & 7) * 2;
+  const char* p1 = tile + off(key + 8, col >> 3) + (col & 7) * 2;
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p1);
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, r);
+}
+}  // namespace fa
+
+__global__ __launch_bounds__(256, 1) void attn_fwd_bf16_kernel(AttnArgs a) {
+  using namespace fa;
+  typedef Mfma<bf16> MM;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h = lane >> 5;
+  const int BH = a.B * a.H;
+  const int nqt = (a.T + QWG - 1) / QWG;
+  const int qt = nqt - 1 - (int)(blockIdx.x / BH);     // longest rows first
+  const int bh = blockIdx.x % BH;
+  const int b = bh / a.H, head = bh % a.H;
+  const long ldb = 3L * a.C * 2;                       // row stride in bytes
+  const bf16* qkv = static_cast<const bf16*>(a.qkv);
+  const i32x4 rs = make_rsrc(qkv + (long)b * a.T * 3 * a.C, clamp_bytes((long)a.T * ldb));
+  const int koff = (a.C + head * HD) * 2, voff = (2 * a.C + head * HD) * 2;
+  const int qw0 = qt * QWG + wave * QW;
+
+  bf16x8 qf[2][8];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int q = qw0 + qb * 32 + (lane & 31);
+    frag_row_global<bf16>(qf[qb], qkv + ((long)b * a.T + q) * 3 * a.C + head * HD, q < a.T, lane);
+  }
+  f32x16 o[2][4];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[qb][i][r] = 0.f;
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  int ko[8], vo[8];
+  frag_k_offsets(ko, lane);
+  frag_vt_offsets(vo, lane);
+
+  const int last_key = min(a.T - 1, qt * QWG + QWG - 1);
+  const int nkt = last_key / KT + 1;
+  issue_kv(smem, rs, 0, ldb, koff, voff, wave, lane);
+  if (nkt > 1) issue_kv(smem + SLOT, rs, KT, ldb, koff, voff, wave, lane);
+  for (int kt = 0; kt < nkt; ++kt) {
+    // tile kt landed (own loads, then everyone's); slot of tile kt-1 is free
+    if (kt + 1 < nkt) __builtin_amdgcn_s_waitcnt(0x3f70 | 8);   // vmcnt(8): the next tile may stay in flight
+    else __builtin_amdgcn_s_waitcnt(0x3f70);                    // vmcnt(0)
+    __syncthreads();
+    if (kt + 2 < nkt) issue_kv(smem + ((kt + 2) % NSLOT) * SLOT, rs, (kt + 2) * KT, ldb, koff, voff, wave, lane);
+    const lds_char* kt_ = (const lds_char*)smem + (kt % NSLOT) * SLOT;
+    const lds_char* vt_ = kt_ + TILE;
+    const int k0 = kt * KT;
+    if (k0 > qw0 + QW - 1) continue;                  // every key of this tile is in this wave's future
+    f32x16 s[2][2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[qb][kb][r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
+      const bf16x8 k0f = *(lds_bf16x8*)(kt_ + ko[ks]);
+      const bf16x8 k1f = *(lds_bf16x8*)(kt_ + 8192 + ko[ks]);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        s[qb][0] = MM::mma(k0f, qf[qb][ks], s[qb][0]);
+        s[qb][1] = MM::mma(k1f, qf[qb][ks], s[qb][1]);
+      }
+    }
+    // Online softmax with a lazily updated reference: scores are exponentiated
+    // against m_run, which only moves (rescaling l and O) when some lane's tile
+    // maximum exceeds it by more than 8 (a factor 256, far from overflow).
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int q = qw0 + qb * 32 + (lane & 31);
+      if ((k0 + KT - 1 > qw0 + qb * 32) || (k0 + KT > a.T)) {     // diagonal or ragged tile
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + kb * 32 + acc_row(r, lane);
+            if (key > q || key >= a.T) s[qb][kb][r] = -INFINITY;
+          }
+      }
+      float mt = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[qb][kb][r]);
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * a.sl2;
+      if (__ballot(mt > m_run[qb] + 8.f) != 0) {
+        const float m_new = fmaxf(m_run[qb], mt);
+        const float alpha = exp2f(m_run[qb] - m_new);
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) o[qb][db] *= alpha;
+        m_run[qb] = m_new;
+      }
+      const float ref = m_run[qb];
+      float ls = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][r], a.sl2, -ref));
+          s[qb][kb][r] = p;
+          ls += p;
+        }
+      l_run[qb] += ls;
+    }
+#pragma unroll
+    for (int mm = 0; mm < 4; ++mm) {
+      const bf16x8 p0 = frag_regs<bf16>(s[0][mm >> 1], (mm & 1) * 8);
+      const bf16x8 p1 = frag_regs<bf16>(s[1][mm >> 1], (mm & 1) * 8);
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const bf16x8 vf = frag_vt_at(vt_, vo, mm, db);
+        o[0][db] = MM::mma(vf, p0, o[0][db]);
+        o[1][db] = MM::mma(vf, p1, o[1][db]);
+      }
+    }
+  }
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int q = qw0 + qb * 32 + (lane & 31);
+    const float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 32, 64);
+    if (q < a.T) {
+      store_acc_row<bf16>(static_cast<bf16*>(a.o) + ((long)b * a.T + q) * a.C + head * HD, o[qb], 1.f / l_tot, lane);
+      if (h == 0) a.lse[(long)bh * a.T + q] = m_run[qb] + log2f(l_tot);
+    }
+  }
+}
+
+// ---- backward, bf16, direct-to-LDS pipelines ----------------------------------------
+namespace fa {
+// Issue direct-to-LDS loads of 64 rows (r0..) x 128 bf16 of one matrix view:
+// row stride ldb bytes, column offset coff bytes; rows past the buffer read 0.
+__device__ __forceinline__ void issue_tile(char* dst, i32x4 rs, int r0, long ldb, int coff, int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int base = wave * 256 + i * 64;
+    const int p = base + lane;
+    const int row = p >> 4, c = (p & 15) ^ (row & 15);
+    const uint32_t o = (uint32_t)((long)(r0 + row) * ldb + coff + c * 16);
+    raw_buffer_load_lds(rs, (lds_u32*)(dst + __builtin_amdgcn_readfirstlane(base) * 16), 16, (int)o, 0, 0, 0);
+  }
+}
+// 64 floats of a vector at index r0.. into dst[0..63] (one issue: lanes 0-15
+// carry the data, the other lanes read past the end and write zeros to
+// dst[64..255], so dst must hold 1 KiB).
+__device__ __forceinline__ void issue_vec(char* dst, i32x4 rv, int r0, int lane) {
+  const uint32_t o = lane < 16 ? (uint32_t)((r0 + lane * 4) * 4) : 0xffffffffu;
+  raw_buffer_load_lds(rv, (lds_u32*)dst, 16, (int)o, 0, 0, 0);
+}
+typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) const f32x4 lds_f32x4;
+}  // namespace fa
+
+// dK, dV: one workgroup = 128 keys of one (sequence, head), 4 waves x 32 keys
+// (K and V fragments in registers); walks the 64-query tiles at and after the
+// diagonal.  Q and dO tiles are row-major in LDS (3-slot ring); their
+// transposes for dV^T += dO^T P and dK^T += Q^T dS come from transpose reads.
+__global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_bf16_kernel(AttnArgs a) {
+  using namespace fa;
+  typedef Mfma<bf16> MM;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  constexpr int QT = 64;
+  constexpr int SLOTB = 2 * TILE + 2048;      // Q, dO, lse (1 KiB), delta (1 KiB)
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int BH = a.B * a.H;
+  const int kt = (int)(blockIdx.x / BH);      // first key tiles have the most queries
+  const int bh = blockIdx.x % BH;
+  const int b = bh / a.H, head = bh % a.H;
+  const long ldq = 3L * a.C * 2, ldo = (long)a.C * 2;
+  const bf16* qkv = static_cast<const bf16*>(a.qkv);
+  const i32x4 rsq = make_rsrc(qkv + (long)b * a.T * 3 * a.C, clamp_bytes((long)a.T * ldq));
+  const i32x4 rso = make_rsrc(static_cast<const bf16*>(a.dO) + (long)b * a.T * a.C, clamp_bytes((long)a.T * ldo));
+  const i32x4 rsl = make_rsrc(a.lse + (long)bh * a.T, (uint32_t)a.T * 4);
+  const i32x4 rsd = make_rsrc(a.delta + (long)bh * a.T, (uint32_t)a.T * 4);
+  const int qoff = head * HD * 2;
+  const int kw0 = kt * 128 + wave * 32;
+  const int key = kw0 + (lane & 31);
+  const bool kv = key < a.T;
+
+  bf16x8 kf[8], vf[8];
+  frag_row_global<bf16>(kf, qkv + ((long)b * a.T + key) * 3 * a.C + a.C + head * HD, kv, lane);
+  frag_row_global<bf16>(vf, qkv + ((long)b * a.T + key) * 3 * a.C + 2 * a.C + head * HD, kv, lane);
+  f32x16 dk[4], dv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { dk[i][r] = 0.f; dv[i][r] = 0.f; }
+  int ko[8], vo[8];
+  frag_k_offsets(ko, lane);
+  frag_vt_offsets(vo, lane);
+
+  auto issue = [&](int slot, int q0) {
+    char* d = smem + slot * SLOTB;
+    issue_tile(d, rsq, q0, ldq, qoff, wave, lane);
+    issue_tile(d + TILE, rso, q0, ldo, qoff, wave, lane);
+    if (wave == 0) {
+      issue_vec(d + 2 * TILE, rsl, q0, lane);
+      issue_vec(d + 2 * TILE + 1024, rsd, q0, lane);
+    }
+  };
+  const int qt0 = (kt * 128) / QT;
+  const int nqt = (a.T + QT - 1) / QT;
+  const int n = nqt - qt0;
+  issue(0, qt0 * QT);
+  if (n > 1) issue(1, (qt0 + 1) * QT);
+  for (int it = 0; it < n; ++it) {
+    if (it + 1 < n) {
+      if (wave == 0) __builtin_amdgcn_s_waitcnt(0x0f70 | 10);  // vmcnt(10): the next tile's 10 issues in flight
+      else __builtin_amdgcn_s_waitcnt(0x0f70 | 8);             // vmcnt(8)
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x0f70);
+    }
+    __syncthreads();
+    if (it + 2 < n) issue((it + 2) % 3, (qt0 + it + 2) * QT);
+    const int q0 = (qt0 + it) * QT;
+    const lds_char* qt_ = (const lds_char*)smem + (it % 3) * SLOTB;
+    const lds_char* ot_ = qt_ + TILE;
+    const float* vec = (const float*)(smem + (it % 3) * SLOTB + 2 * TILE);
+    if (q0 + QT - 1 < kw0) continue;             // all queries precede all keys of this wave
+    const bool need_mask = (q0 < kw0 + 31) || (q0 + QT > a.T);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      f32x16 sv, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) { sv[r] = 0.f; dp[r] = 0.f; }
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const bf16x8 qa = *(lds_bf16x8*)(qt_ + qb * 8192 + ko[ks]);
+        const bf16x8 oa = *(lds_bf16x8*)(ot_ + qb * 8192 + ko[ks]);
+        sv = MM::mma(qa, kf[ks], sv);       // S  (query x key)
+        dp = MM::mma(oa, vf[ks], dp);       // dP (query x key)
+      }
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int qi = qb * 32 + 8 * g + 4 * (lane >> 5);
+        const f32x4 lv = *(const lds_f32x4*)((const lds_char*)vec + qi * 4);
+        const f32x4 dl = *(const lds_f32x4*)((const lds_char*)vec + 1024 + qi * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          float p = __builtin_amdgcn_exp2f(fmaf(sv[r], a.sl2, -lv[e]));
+          if (need_mask && (key > q0 + qi + e || q0 + qi + e >= a.T)) p = 0.f;
+          sv[r] = p;
+          dp[r] = p * (dp[r] - dl[e]);      // dS
+        }
+      }
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm) {
+        const bf16x8 pf = frag_regs<bf16>(sv, mm * 8);
+        const bf16x8 sf = frag_regs<bf16>(dp, mm * 8);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          dv[db] = MM::mma(frag_vt_at(ot_, vo, 2 * qb + mm, db), pf, dv[db]);
+          dk[db] = MM::mma(frag_vt_at(qt_, vo, 2 * qb + mm, db), sf, dk[db]);
+        }
+      }
+    }
+  }
+  if (kv) {
+    bf16* row = static_cast<bf16*>(a.dqkv) + ((long)b * a.T + key) * 3 * a.C + head * HD;
+    store_acc_row<bf16>(row + a.C, dk, a.rsd, lane);
+    store_acc_row<bf16>(row + 2 * a.C, dv, 1.f, lane);
+  }
+}
+
+// dQ: one workgroup = 128 queries of one (sequence, head), 4 waves x 32
+// queries (Q and dO fragments in registers); walks the 64-key tiles up to the
+// diagonal.  K and V tiles row-major in LDS (3-slot ring); K^T for
+// dQ^T += K^T dS^T comes from transpose reads.
+__global__ __launch_bounds__(256, 1) void attn_bwd_dq_bf16_kernel(AttnArgs a) {
+  using namespace fa;
+  typedef Mfma<bf16> MM;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int BH = a.B * a.H;
+  const int nqt = (a.T + 127) / 128;
+  const int qt = nqt - 1 - (int)(blockIdx.x / BH);
+  const int bh = blockIdx.x % BH;
+  const int b = bh / a.H, head = bh % a.H;
+  const long ldb = 3L * a.C * 2;
+  const bf16* qkv = static_cast<const bf16*>(a.qkv);
+  const i32x4 rs = make_rsrc(qkv + (long)b * a.T * 3 * a.C, clamp_bytes((long)a.T * ldb));
+  const int koff = (a.C + head * HD) * 2, voff = (2 * a.C + head * HD) * 2;
+  const int qw0 = qt * 128 + wave * 32;
+  const int q = qw0 + (lane & 31);
+  const bool qv = q < a.T;
+
+  bf16x8 qf[8], df[8];
+  frag_row_global<bf16>(qf, qkv + ((long)b * a.T + q) * 3 * a.C + head * HD, qv, lane);
+  frag_row_global<bf16>(df, static_cast<const bf16*>(a.dO) + ((long)b * a.T + q) * a.C + head * HD, qv, lane);
+  const float lse = qv ? a.lse[(long)bh * a.T + q] : INFINITY;
+  const float dlt = qv ? a.delta[(long)bh * a.T + q] : 0.f;
+  f32x16 acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+  int ko[8], vo[8];
+  frag_k_offsets(ko, lane);
+  frag_vt_offsets(vo, lane);
+
+  const int last_key = min(a.T - 1, qt * 128 + 127);
+  const int nkt = last_key / KT + 1;
+  issue_kv(smem, rs, 0, ldb, koff, voff, wave, lane);
+  if (nkt > 1) issue_kv(smem + SLOT, rs, KT, ldb, koff, voff, wave, lane);
+  for (int kt = 0; kt < nkt; ++kt) {
+    if (kt + 1 < nkt) __builtin_amdgcn_s_waitcnt(0x0f70 | 8);
+    else __builtin_amdgcn_s_waitcnt(0x0f70);
+    __syncthreads();
+    if (kt + 2 < nkt) issue_kv(smem + ((kt + 2) % NSLOT) * SLOT, rs, (kt + 2) * KT, ldb, koff, voff, wave, lane);
+    const lds_char* kt_ = (const lds_char*)smem + (kt % NSLOT) * SLOT;
+    const lds_char* vt_ = kt_ + TILE;
+    const int k0 = kt * KT;
+    if (k0 > qw0 + 31) continue;
+    f32x16 sv[2], dp[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) { sv[kb][r] = 0.f; dp[kb][r] = 0.f; }
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        sv[kb] = MM::mma(*(lds_bf16x8*)(kt_ + kb * 8192 + ko[ks]), qf[ks], sv[kb]);   // S^T
+        dp[kb] = MM::mma(*(lds_bf16x8*)(vt_ + kb * 8192 + ko[ks]), df[ks], dp[kb]);   // dP^T
+      }
+    }
+    const bool need_mask = (k0 + KT - 1 > qw0) || (k0 + KT > a.T);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = __builtin_amdgcn_exp2f(fmaf(sv[kb][r], a.sl2, -lse));
+        if (need_mask) {
+          const int kk = k0 + kb * 32 + acc_row(r, lane);
+          if (kk > q || kk >= a.T) p = 0.f;
+        }
+        sv[kb][r] = p * (dp[kb][r] - dlt);   // dS^T
+      }
+#pragma unroll
+    for (int mm = 0; mm < 4; ++mm) {
+      const bf16x8 sf = frag_regs<bf16>(sv[mm >> 1], (mm & 1) * 8);
+#pragma unroll
+      for (int db = 0; db < 4; ++db) acc[db] = MM::mma(frag_vt_at(kt_, vo, mm, db), sf, acc[db]);
+    }
+  }
+  if (qv) store_acc_row<bf16>(static_cast<bf16*>(a.dqkv) + ((long)b * a.T + q) * 3 * a.C + head * HD, acc, a.rsd, lane);
 }
 
 template <typename T> constexpr int attn_fwd_lds() { return 2 * (AttnCfg<T>::ROWT + AttnCfg<T>::TRT); }

@@ -83,6 +83,7 @@ template <typename T> struct BwdScratch {
   T* dy1;       // [N, C]
   T* dO;        // [N, C]
   T* dqkv;      // [N, 3C]
+  T* wt;        // transposed weights: W_proj^T [F,C], W_fc^T [C,F], W_o^T [C,C], W_qkv^T [C,3C]
   float* delta; // [B*H][T]
   float* part;  // split-k partial sums
   size_t bytes;
@@ -97,6 +98,7 @@ template <typename T> BwdScratch<T> carve_bwd(const blk_cfg& c, void* p) {
   s.dy1 = k.take<T>(N * c.C);
   s.dO = k.take<T>(N * c.C);
   s.dqkv = k.take<T>(N * 3 * c.C);
+  s.wt = k.take<T>(12L * c.C * c.C);
   s.delta = k.take<float>((size_t)c.B * c.H * c.T);
   constexpr int BK = GemmTile<T>::BK;
   size_t part = 0;
@@ -266,10 +268,16 @@ int fwd_impl(const blk_cfg& c, const T* x, const T* wqkv, const T* wo, const T* 
   {  // 5 causal attention
     AttnArgs a = attn_args<T>(c);
     a.qkv = s.qkv; a.o = s.o; a.lse = s.lse;
-    need_lds(reinterpret_cast<const void*>(attn_fwd_kernel<T>), attn_fwd_lds<T>());
-    const int nqt = (c.T + 127) / 128;
     Timed t("attn_fwd", st);
-    hipLaunchKernelGGL(attn_fwd_kernel<T>, dim3(nqt * c.B * H), dim3(256), attn_fwd_lds<T>(), st, a);
+    if constexpr (sizeof(T) == 2) {
+      need_lds(reinterpret_cast<const void*>(attn_fwd_bf16_kernel), fa::LDS);
+      const int nqt = (c.T + fa::QWG - 1) / fa::QWG;
+      hipLaunchKernelGGL(attn_fwd_bf16_kernel, dim3(nqt * c.B * H), dim3(256), fa::LDS, st, a);
+    } else {
+      need_lds(reinterpret_cast<const void*>(attn_fwd_kernel<T>), attn_fwd_lds<T>());
+      const int nqt = (c.T + 127) / 128;
+      hipLaunchKernelGGL(attn_fwd_kernel<T>, dim3(nqt * c.B * H), dim3(256), attn_fwd_lds<T>(), st, a);
+    }
   }
   {  // 6 y1 = x + o W_o^T   (y1 is kept in y)
     GemmArgs g = gargs(s.o, C, wo, C, N, C, C);
@@ -301,8 +309,23 @@ int bwd_impl(const blk_cfg& c, const T* dy, const T* x, const T* wqkv, const T* 
              const BwdScratch<T>& w, hipStream_t st) {
   (void)x;
   const int N = c.B * c.T, C = c.C, F = c.F, H = c.H;
+  // input-gradient GEMMs read the weights k-contiguous: W^T, made once per call
+  T* wt_proj = w.wt;                       // [F, C]
+  T* wt_fc = wt_proj + (long)F * C;        // [C, F]
+  T* wt_o = wt_fc + (long)C * F;           // [C, C]
+  T* wt_qkv = wt_o + (long)C * C;          // [C, 3C]
+  {
+    Timed t("transpose_weights", st);
+    auto tr = [&](const T* src, T* dst, int rows, int cols) {
+      hipLaunchKernelGGL(transpose_kernel<T>, dim3(cols / 64, rows / 64), dim3(256), 0, st, src, dst, rows, cols);
+    };
+    tr(wproj, wt_proj, C, F);
+    tr(wfc, wt_fc, F, C);
+    tr(wo, wt_o, C, C);
+    tr(wqkv, wt_qkv, 3 * C, C);
+  }
   {  // 9: du = (dy W_proj) * 2 max(u, 0)
-    GemmArgs g = gargs(dy, C, wproj, F, N, F, C);
+    GemmArgs g = gargs(dy, C, wt_proj, C, N, F, C);
     g.out = w.du; g.ldo = F; g.aux = s.u; g.ldaux = F;
     gemm<T>(gemm_proj_dgrad<T>, "gemm_proj_dgrad", g, 1, st);
   }
@@ -310,7 +333,7 @@ int bwd_impl(const blk_cfg& c, const T* dy, const T* x, const T* wqkv, const T* 
   wgrad<T>(gemm_proj_wgrad<T>, gemm_proj_wgrad_acc<T>, "gemm_proj_wgrad", dy, s.a, dwproj, C, F, N, acc, w.part,
            st);
   {  // 8: dh2 = du W_fc
-    GemmArgs g = gargs(w.du, F, wfc, C, N, C, F);
+    GemmArgs g = gargs(w.du, F, wt_fc, F, N, C, F);
     g.out = w.dh; g.ldo = C;
     gemm<T>(gemm_fc_dgrad<T>, "gemm_fc_dgrad", g, 1, st);
   }
@@ -322,7 +345,7 @@ int bwd_impl(const blk_cfg& c, const T* dy, const T* x, const T* wqkv, const T* 
                        (const T*)s.h2, (const float*)s.r2, w.dy1, N, C);
   }
   {  // 6: do = dy1 W_o
-    GemmArgs g = gargs(w.dy1, C, wo, C, N, C, C);
+    GemmArgs g = gargs(w.dy1, C, wt_o, C, N, C, C);
     g.out = w.dO; g.ldo = C;
     gemm<T>(gemm_o_dgrad<T>, "gemm_o_dgrad", g, 1, st);
   }
@@ -336,16 +359,30 @@ int bwd_impl(const blk_cfg& c, const T* dy, const T* x, const T* wqkv, const T* 
     }
     AttnArgs a = attn_args<T>(c);
     a.qkv = s.qkv; a.lse = s.lse; a.dO = w.dO; a.delta = w.delta; a.dqkv = w.dqkv;
-    need_lds(reinterpret_cast<const void*>(attn_bwd_dq_kernel<T>), attn_dq_lds<T>());
-    need_lds(reinterpret_cast<const void*>(attn_bwd_dkdv_kernel<T>), attn_dkdv_lds<T>());
     const int nqt = (c.T + 127) / 128;
-    {
-      Timed t("attn_bwd_dkdv", st);
-      hipLaunchKernelGGL(attn_bwd_dkdv_kernel<T>, dim3(nqt * c.B * H), dim3(256), attn_dkdv_lds<T>(), st, a);
-    }
-    {
-      Timed t("attn_bwd_dq", st);
-      hipLaunchKernelGGL(attn_bwd_dq_kernel<T>, dim3(nqt * c.B * H), dim3(256), attn_dq_lds<T>(), st, a);
+    if constexpr (sizeof(T) == 2) {
+      constexpr int DKDV_LDS = 3 * (2 * fa::TILE + 2048);
+      need_lds(reinterpret_cast<const void*>(attn_bwd_dkdv_bf16_kernel), DKDV_LDS);
+      need_lds(reinterpret_cast<const void*>(attn_bwd_dq_bf16_kernel), fa::LDS);
+      {
+        Timed t("attn_bwd_dkdv", st);
+        hipLaunchKernelGGL(attn_bwd_dkdv_bf16_kernel, dim3(nqt * c.B * H), dim3(256), DKDV_LDS, st, a);
+      }
+      {
+        Timed t("attn_bwd_dq", st);
+        hipLaunchKernelGGL(attn_bwd_dq_bf16_kernel, dim3(nqt * c.B * H), dim3(256), fa::LDS, st, a);
+      }
+    } else {
+      need_lds(reinterpret_cast<const void*>(attn_bwd_dq_kernel<T>), attn_dq_lds<T>());
+      need_lds(reinterpret_cast<const void*>(attn_bwd_dkdv_kernel<T>), attn_dkdv_lds<T>());
+      {
+        Timed t("attn_bwd_dkdv", st);
+        hipLaunchKernelGGL(attn_bwd_dkdv_kernel<T>, dim3(nqt * c.B * H), dim3(256), attn_dkdv_lds<T>(), st, a);
+      }
+      {
+        Timed t("attn_bwd_dq", st);
+        hipLaunchKernelGGL(attn_bwd_dq_kernel<T>, dim3(nqt * c.B * H), dim3(256), attn_dq_lds<T>(), st, a);
+      }
     }
   }
   {  // 4-3: QK-norm and rotary backward (in place on dq, dk)
@@ -354,7 +391,7 @@ int bwd_impl(const blk_cfg& c, const T* dy, const T* x, const T* wqkv, const T* 
                        (const T*)s.qkv, (const float*)s.rho, (const float2*)s.cs, N, c.T, H, C);
   }
   {  // 2: dh1 = dqkv W_qkv
-    GemmArgs g = gargs(w.dqkv, 3 * C, wqkv, C, N, C, 3 * C);
+    GemmArgs g = gargs(w.dqkv, 3 * C, wt_qkv, 3 * C, N, C, 3 * C);
     g.out = w.dh; g.ldo = C;
     gemm<T>(gemm_qkv_dgrad<T>, "gemm_qkv_dgrad", g, 1, st);
   }

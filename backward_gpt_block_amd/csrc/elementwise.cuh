@@ -184,6 +184,21 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(const T* __restrict__ d
   if (lane == 0) delta[(b * H + head) * Tlen + t] = s;
 }
 
+// dst[c][r] = src[r][c] for a rows x cols matrix (both multiples of 64):
+// 64 x 64 tiles through LDS, 256 threads.
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ src, T* __restrict__ dst, int rows,
+                                                        int cols) {
+  __shared__ T t[64][65];
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) t[ty + 4 * i][tx] = src[(long)(r0 + ty + 4 * i) * cols + c0 + tx];
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) dst[(long)(c0 + ty + 4 * i) * rows + r0 + tx] = t[tx][ty + 4 * i];
+}
+
 // dst[i] = (accumulate ? dst[i] : 0) + sum_s part[s*n + i], in split order.
 __global__ void splitk_reduce_kernel(float* __restrict__ dst, const float* __restrict__ part, long n, int splits,
                                      int accumulate) {

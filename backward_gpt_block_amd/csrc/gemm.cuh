@@ -1,28 +1,35 @@
 // MFMA GEMM for gfx950:  C[m, n] = sum_k A(m, k) * B(n, k)  (fp32 accumulate)
 //
 // A(m, k) is A[m*lda + k] when A is "k-contiguous" (KA = true), else
-// A[k*lda + m]; likewise B.  Forward projections (y = x W^T) have both
-// operands k-contiguous; input gradients (dx = dy W) have a k-contiguous A and
-// an n-contiguous B; weight gradients (dW = dy^T x) have both operands
-// contiguous along m/n with k (tokens) strided.
+// A[k*lda + m]; likewise B.  Forward projections (y = x W^T) and input
+// gradients (dx = dy W, with W passed transposed) have both operands
+// k-contiguous; weight gradients (dW = dy^T x) have both operands contiguous
+// along m/n with k (tokens) strided.
 //
 // Workgroup tile 256 x 256, four waves in a 2 x 2 grid, each wave 128 x 128
-// as 4 x 4 MFMA 32x32 blocks.  Each k-step stages a 256-row x 128-byte slab of
-// A and of B into LDS (double-buffered, next slab prefetched into registers
-// while the current one feeds the MFMAs).  LDS always holds rows of the m (n)
-// index with k contiguous, so fragment reads are single 16-byte loads; an
-// operand that is contiguous along m (n) in memory is transposed in registers
-// (8 x 8 element blocks) between the global load and the LDS store.
+// as 4 x 4 MFMA 32x32 blocks; a k-step stages a 256-row x 128-byte slab of A
+// and of B in LDS (two stages, 128 KiB).  LDS rows hold k contiguously, with
+// an XOR swizzle of the 16-byte chunks, so every MFMA fragment is one LDS
+// read.
+//   k-contiguous operands: buffer loads straight into LDS (no registers),
+//     issued one k-step ahead; each lane fetches the global chunk that
+//     belongs at its LDS slot, so the swizzle costs nothing.  Rows and k past
+//     the matrix edge are given an out-of-range offset and read as zero.
+//   m/n-contiguous operands: buffer loads into registers one k-step ahead,
+//     transposed in registers (8 x 8 element blocks), then written to LDS.
+// Epilogue: each wave parks its 128 x 128 fp32 results in LDS (two halves of
+// 64 rows), then every lane handles 8 consecutive columns of a row: 16-byte
+// loads of the residual / pre-activation, 16-byte stores.
 #pragma once
 #include "common.cuh"
 
 namespace blk {
 
 enum EpiKind : int {
-  EPI_STORE = 0,    // out = alpha*acc                         (element T)
-  EPI_RESID = 1,    // out = aux + alpha*acc                   (T)
-  EPI_RELU2 = 2,    // out = v, out2 = max(v,0)^2, v = alpha*acc (T)
-  EPI_DRELU2 = 3,   // out = alpha*acc * 2*max(aux, 0)         (T)
+  EPI_STORE = 0,    // out = alpha*acc                         (element TO)
+  EPI_RESID = 1,    // out = aux + alpha*acc                   (TO)
+  EPI_RELU2 = 2,    // out = v, out2 = max(v,0)^2, v = alpha*acc (TO)
+  EPI_DRELU2 = 3,   // out = alpha*acc * 2*max(aux, 0)         (TO)
   EPI_F32 = 4,      // out[split] = alpha*acc                  (float)
   EPI_F32_ADD = 5,  // out += alpha*acc                        (float)
 };
@@ -49,71 +56,75 @@ template <typename TI> struct GemmTile {
   static constexpr int LDS = 2 * SLAB;           // 128 KiB
 };
 
-// Staging of one operand slab: R rows of the m (n) index x BK of k.
-template <typename TI, bool KC, int R>
-struct Stager {
-  typedef GemmTile<TI> G;
-  static constexpr int ELEM = G::ELEM;
-  // k-contiguous: R*8 chunks, consecutive threads take consecutive chunks of a row.
-  // m-contiguous: (BK/ELEM) x (R/ELEM) blocks of ELEM x ELEM elements.
-  static constexpr int NCH = KC ? (R * 8) / G::NT : ((G::BK / ELEM) * (R / ELEM) * ELEM) / G::NT;
-  u32x4 reg[NCH];
+// ---- buffer resources -------------------------------------------------------
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
 
-  // rows r0.. (< rows_valid), k in [k0, k_end)
-  __device__ void load(const TI* P, long ld, int r0, int rows_valid, int k0, int k_end) {
-    const int t = threadIdx.x;
-    if constexpr (KC) {
+__device__ void raw_buffer_load_lds(i32x4 rsrc, lds_u32* lds, int size, int voffset, int soffset, int offset,
+                                    int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+__device__ u32x4 raw_buffer_load_b128(i32x4 rsrc, int voffset, int soffset, int aux) __asm(
+    "llvm.amdgcn.raw.buffer.load.v4i32");
+
+// Buffer resource over [p, p + bytes): loads at offsets >= bytes return 0.
+__device__ __forceinline__ i32x4 make_rsrc(const void* p, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  return i32x4{(int)(uint32_t)a, (int)((a >> 32) & 0xffff), (int)bytes, 0x00020000};
+}
+
+__device__ __forceinline__ uint32_t clamp_bytes(long b) { return b > 0xffffffffL ? 0xffffffffu : (uint32_t)b; }
+
+// ---- staging ------------------------------------------------------------------
+// k-contiguous slab of R rows: 8 chunks per row, R*8 chunks, 64 per wave issue.
+template <typename TI, int R>
+__device__ __forceinline__ void stage_direct(char* lds, i32x4 rs, uint32_t oob, long ld, int r0, int rows_valid,
+                                             int k0, int k_end, int wave, int lane) {
+  constexpr int ELEM = GemmTile<TI>::ELEM;
+  constexpr int PER_WAVE = R * 8 / 4;            // chunks per wave
 #pragma unroll
-      for (int i = 0; i < NCH; ++i) {
-        int idx = t + i * G::NT;
-        int row = idx >> 3, ch = idx & 7;
-        int gr = r0 + row, gk = k0 + ch * ELEM;
-        if (gr < rows_valid && gk < k_end)
-          reg[i] = ld16(P + (long)gr * ld + gk);
-        else
-          reg[i] = u32x4{0, 0, 0, 0};
-      }
-    } else {
-      constexpr int RB = R / ELEM;                 // blocks along the row index
-      constexpr int NB = NCH / ELEM;               // blocks per thread
+  for (int i = 0; i < PER_WAVE / 64; ++i) {
+    const int base = wave * PER_WAVE + i * 64;   // wave-uniform first LDS chunk
+    const int p = base + lane;
+    const int row = p >> 3, pc = p & 7;
+    const int c = pc ^ swz(row, 8);
+    const int gr = r0 + row, gk = k0 + c * ELEM;
+    const uint32_t off = (gr < rows_valid && gk < k_end) ? (uint32_t)(((long)gr * ld + gk) * sizeof(TI)) : oob;
+    lds_u32* dst = (lds_u32*)(lds + __builtin_amdgcn_readfirstlane(base) * 16);
+    raw_buffer_load_lds(rs, dst, 16, (int)off, 0, 0, 0);
+  }
+}
+
+// m-contiguous slab of R rows (of the m/n index) x BK of k: ELEM x ELEM blocks.
+template <typename TI, int R>
+struct StageTrans {
+  static constexpr int ELEM = GemmTile<TI>::ELEM;
+  static constexpr int RB = R / ELEM;
+  static constexpr int NB = (GemmTile<TI>::BK / ELEM) * RB / GemmTile<TI>::NT;   // blocks per thread
+  static_assert(NB >= 1, "slab too small for the transposing stager");
+  u32x4 reg[NB * ELEM];
+
+  __device__ __forceinline__ void load(i32x4 rs, uint32_t oob, long ld, int r0, int rows_valid, int k0, int k_end) {
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        int blkid = t + b * G::NT;
-        int rb = blkid % RB, kb = blkid / RB;
-        int gr = r0 + rb * ELEM;
+    for (int b = 0; b < NB; ++b) {
+      const int blkid = threadIdx.x + b * GemmTile<TI>::NT;
+      const int rb = blkid % RB, kb = blkid / RB;
+      const int gr = r0 + rb * ELEM;
 #pragma unroll
-        for (int i = 0; i < ELEM; ++i) {
-          int gk = k0 + kb * ELEM + i;
-          if (gr < rows_valid && gk < k_end)
-            reg[b * ELEM + i] = ld16(P + (long)gk * ld + gr);
-          else
-            reg[b * ELEM + i] = u32x4{0, 0, 0, 0};
-        }
+      for (int i = 0; i < ELEM; ++i) {
+        const int gk = k0 + kb * ELEM + i;
+        const uint32_t off = (gr < rows_valid && gk < k_end) ? (uint32_t)(((long)gk * ld + gr) * sizeof(TI)) : oob;
+        reg[b * ELEM + i] = raw_buffer_load_b128(rs, (int)off, 0, 0);
       }
     }
   }
-
-  __device__ void store(char* lds) {
-    const int t = threadIdx.x;
-    if constexpr (KC) {
+  __device__ __forceinline__ void store(char* lds) {
 #pragma unroll
-      for (int i = 0; i < NCH; ++i) {
-        int idx = t + i * G::NT;
-        int row = idx >> 3, ch = idx & 7;
-        st16(lds + tile_off(row, ch, 8), reg[i]);
-      }
-    } else {
-      constexpr int RB = R / ELEM;
-      constexpr int NB = NCH / ELEM;
+    for (int b = 0; b < NB; ++b) {
+      const int blkid = threadIdx.x + b * GemmTile<TI>::NT;
+      const int rb = blkid % RB, kb = blkid / RB;
+      u32x4 tr[ELEM];
+      transpose_chunks(&reg[b * ELEM], tr, (TI*)nullptr);
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        int blkid = t + b * G::NT;
-        int rb = blkid % RB, kb = blkid / RB;
-        u32x4 tr[ELEM];
-        transpose_chunks(&reg[b * ELEM], tr, (TI*)nullptr);
-#pragma unroll
-        for (int j = 0; j < ELEM; ++j) st16(lds + tile_off(rb * ELEM + j, kb, 8), tr[j]);
-      }
+      for (int j = 0; j < ELEM; ++j) st16(lds + tile_off(rb * ELEM + j, kb, 8), tr[j]);
     }
   }
 };
@@ -140,29 +151,6 @@ __device__ __forceinline__ typename Mfma<TI>::frag load_frag(const char* lds, in
   }
 }
 
-template <typename TO, int EPI>
-__device__ __forceinline__ void epi_store(const GemmArgs& g, float alpha, int split, int row, int col, float v) {
-  v *= alpha;
-  if constexpr (EPI == EPI_STORE) {
-    static_cast<TO*>(g.out)[(long)row * g.ldo + col] = from_f32<TO>(v);
-  } else if constexpr (EPI == EPI_RESID) {
-    float r = to_f32(static_cast<const TO*>(g.aux)[(long)row * g.ldaux + col]);
-    static_cast<TO*>(g.out)[(long)row * g.ldo + col] = from_f32<TO>(r + v);
-  } else if constexpr (EPI == EPI_RELU2) {
-    static_cast<TO*>(g.out)[(long)row * g.ldo + col] = from_f32<TO>(v);
-    float p = fmaxf(v, 0.f);
-    static_cast<TO*>(g.out2)[(long)row * g.ldo2 + col] = from_f32<TO>(p * p);
-  } else if constexpr (EPI == EPI_DRELU2) {
-    float u = to_f32(static_cast<const TO*>(g.aux)[(long)row * g.ldaux + col]);
-    static_cast<TO*>(g.out)[(long)row * g.ldo + col] = from_f32<TO>(v * 2.f * fmaxf(u, 0.f));
-  } else if constexpr (EPI == EPI_F32) {
-    static_cast<float*>(g.out)[(long)split * g.M * g.ldo + (long)row * g.ldo + col] = v;
-  } else {
-    float* p = static_cast<float*>(g.out) + (long)row * g.ldo + col;
-    *p = *p + v;
-  }
-}
-
 // Workgroup index -> (tile_m, tile_n, split).  Workgroups are dealt round
 // robin to the 8 XCDs; the remap gives each XCD a contiguous run of logical
 // tiles, and tiles are walked in groups of 8 m-tiles so that an XCD's
@@ -183,6 +171,88 @@ __device__ __forceinline__ void tile_coords(const GemmArgs& g, int& tm, int& tn,
   tn = in_group / gsize;
 }
 
+// ---- epilogue ------------------------------------------------------------------
+// 8 consecutive results of one row (fp32, already scaled) -> memory.
+template <typename TO, int EPI>
+__device__ __forceinline__ void epi8(const GemmArgs& g, int split, int row, int col, float* f) {
+  if constexpr (EPI == EPI_F32 || EPI == EPI_F32_ADD) {
+    float* p = static_cast<float*>(g.out) + (EPI == EPI_F32 ? (long)split * g.M * g.ldo : 0L) + (long)row * g.ldo + col;
+    u32x4 a = Chunk<float>::pack(f), b = Chunk<float>::pack(f + 4);
+    if constexpr (EPI == EPI_F32_ADD) {
+      float o[8];
+      Chunk<float>::unpack(ld16(p), o);
+      Chunk<float>::unpack(ld16(p + 4), o + 4);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] += f[e];
+      a = Chunk<float>::pack(o);
+      b = Chunk<float>::pack(o + 4);
+    }
+    st16(p, a);
+    st16(p + 4, b);
+  } else {
+    constexpr int EL = Chunk<TO>::N;     // 8 bf16 or 4 float per chunk
+    TO* o = static_cast<TO*>(g.out) + (long)row * g.ldo + col;
+    if constexpr (EPI == EPI_RESID || EPI == EPI_DRELU2) {
+      const TO* x = static_cast<const TO*>(g.aux) + (long)row * g.ldaux + col;
+      float xv[8];
+#pragma unroll
+      for (int h = 0; h < 8 / EL; ++h) Chunk<TO>::unpack(ld16(x + h * EL), xv + h * EL);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = (EPI == EPI_RESID) ? xv[e] + f[e] : f[e] * 2.f * fmaxf(xv[e], 0.f);
+    }
+#pragma unroll
+    for (int h = 0; h < 8 / EL; ++h) st16(o + h * EL, Chunk<TO>::pack(f + h * EL));
+    if constexpr (EPI == EPI_RELU2) {
+      TO* o2 = static_cast<TO*>(g.out2) + (long)row * g.ldo2 + col;
+      float a[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { const float p = fmaxf(f[e], 0.f); a[e] = p * p; }
+#pragma unroll
+      for (int h = 0; h < 8 / EL; ++h) st16(o2 + h * EL, Chunk<TO>::pack(a + h * EL));
+    }
+  }
+}
+
+// Staging area of one wave's half tile: 64 rows x 128 fp32 (32 KiB), rows of
+// 32 chunks; chunk c of row r at c ^ (8 * bit 2 of r) so that the two
+// half-waves (rows r and r + 4) write disjoint bank halves.
+__device__ __forceinline__ int epi_off(int row, int chunk) { return row * 512 + ((chunk ^ (((row >> 2) & 1) << 3)) << 4); }
+
+template <typename TO, int EPI>
+__device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[4][4], char* smem, int m0, int n0,
+                                         int split, int wave, int lane) {
+  const int wm = wave >> 1, wn = wave & 1;
+  float alpha = g.alpha;
+  if (g.alpha_ptr) alpha *= g.alpha_ptr[0] * g.alpha_ptr[1];
+  char* wreg = smem + wave * 32768;
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    __syncthreads();
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = ii * 32 + acc_row(r, lane), col = j * 32 + (lane & 31);
+          *reinterpret_cast<float*>(wreg + epi_off(row, col >> 2) + (col & 3) * 4) = acc[2 * pass + ii][j][r] * alpha;
+        }
+    __syncthreads();
+#pragma unroll 4
+    for (int it = 0; it < 16; ++it) {
+      const int q = it * 64 + lane;
+      const int row = q >> 4, cg = q & 15;
+      float f[8];
+      Chunk<float>::unpack(ld16(wreg + epi_off(row, 2 * cg)), f);
+      Chunk<float>::unpack(ld16(wreg + epi_off(row, 2 * cg + 1)), f + 4);
+      const int grow = m0 + wm * 128 + pass * 64 + row;
+      const int gcol = n0 + wn * 128 + cg * 8;
+      if (grow < g.M && gcol < g.N) epi8<TO, EPI>(g, split, grow, gcol, f);
+    }
+  }
+}
+
+// ---- main body -------------------------------------------------------------------
 template <typename TI, typename TO, bool KA, bool KB, int EPI>
 __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   typedef GemmTile<TI> G;
@@ -199,10 +269,24 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   const int kend = min(g.K, kbeg + g.k_split);
   const int nk = (kend - kbeg + G::BK - 1) / G::BK;
 
-  const TI* A = static_cast<const TI*>(g.A);
-  const TI* B = static_cast<const TI*>(g.B);
-  Stager<TI, KA, G::BM> sa;
-  Stager<TI, KB, G::BN> sb;
+  const uint32_t bytesA = clamp_bytes((KA ? (long)g.M * g.lda : (long)g.K * g.lda) * (long)sizeof(TI));
+  const uint32_t bytesB = clamp_bytes((KB ? (long)g.N * g.ldb : (long)g.K * g.ldb) * (long)sizeof(TI));
+  const i32x4 rsA = make_rsrc(g.A, bytesA), rsB = make_rsrc(g.B, bytesB);
+
+  StageTrans<TI, G::BM> ta;
+  StageTrans<TI, G::BN> tb;
+  auto issue = [&](int stage, int k0) {
+    char* s = smem + stage * G::SLAB;
+    if constexpr (KA) stage_direct<TI, G::BM>(s, rsA, bytesA, g.lda, m0, g.M, k0, kend, wave, lane);
+    else ta.load(rsA, bytesA, g.lda, m0, g.M, k0, kend);
+    if constexpr (KB) stage_direct<TI, G::BN>(s + G::BM * G::ROWB, rsB, bytesB, g.ldb, n0, g.N, k0, kend, wave, lane);
+    else tb.load(rsB, bytesB, g.ldb, n0, g.N, k0, kend);
+  };
+  auto commit = [&](int stage) {   // register-staged operands -> LDS
+    char* s = smem + stage * G::SLAB;
+    if constexpr (!KA) ta.store(s);
+    if constexpr (!KB) tb.store(s + G::BM * G::ROWB);
+  };
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -213,20 +297,15 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   if (nk > 0) {
-    sa.load(A, g.lda, m0, g.M, kbeg, kend);
-    sb.load(B, g.ldb, n0, g.N, kbeg, kend);
-    sa.store(smem);
-    sb.store(smem + G::BM * G::ROWB);
+    issue(0, kbeg);
+    commit(0);
   }
-  __syncthreads();
-
   for (int kt = 0; kt < nk; ++kt) {
+    // stage kt is complete (own loads, then everyone's); stage kt-1 is free
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (kt + 1 < nk) issue((kt + 1) & 1, kbeg + (kt + 1) * G::BK);
     const char* cur = smem + (kt & 1) * G::SLAB;
-    if (kt + 1 < nk) {
-      const int k0 = kbeg + (kt + 1) * G::BK;
-      sa.load(A, g.lda, m0, g.M, k0, kend);
-      sb.load(B, g.ldb, n0, g.N, k0, kend);
-    }
 #pragma unroll
     for (int ks = 0; ks < G::BK / MM::KI; ++ks) {
       typename MM::frag fa[4], fb[4];
@@ -239,28 +318,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = MM::mma(fa[i], fb[j], acc[i][j]);
     }
-    if (kt + 1 < nk) {
-      char* nxt = smem + ((kt + 1) & 1) * G::SLAB;
-      sa.store(nxt);
-      sb.store(nxt + G::BM * G::ROWB);
-    }
-    __syncthreads();
+    if (kt + 1 < nk) commit((kt + 1) & 1);
   }
-
-  float alpha = g.alpha;
-  if (g.alpha_ptr) alpha *= g.alpha_ptr[0] * g.alpha_ptr[1];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int col = n0 + wn * 128 + j * 32 + (lane & 31);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * 128 + i * 32 + acc_row(r, lane);
-        if (row < g.M && col < g.N) epi_store<TO, EPI>(g, alpha, split, row, col, acc[i][j][r]);
-      }
-    }
-  }
+  epilogue<TO, EPI>(g, acc, smem, m0, n0, split, wave, lane);
 }
 
 }  // namespace blk
@@ -278,10 +338,10 @@ BLK_GEMM_KERNEL(gemm_qkv_fwd, true, true, EPI_STORE, T)
 BLK_GEMM_KERNEL(gemm_o_fwd, true, true, EPI_RESID, T)
 BLK_GEMM_KERNEL(gemm_fc_fwd, true, true, EPI_RELU2, T)
 BLK_GEMM_KERNEL(gemm_proj_fwd, true, true, EPI_RESID, T)
-BLK_GEMM_KERNEL(gemm_proj_dgrad, true, false, EPI_DRELU2, T)
-BLK_GEMM_KERNEL(gemm_fc_dgrad, true, false, EPI_STORE, T)
-BLK_GEMM_KERNEL(gemm_o_dgrad, true, false, EPI_STORE, T)
-BLK_GEMM_KERNEL(gemm_qkv_dgrad, true, false, EPI_STORE, T)
+BLK_GEMM_KERNEL(gemm_proj_dgrad, true, true, EPI_DRELU2, T)
+BLK_GEMM_KERNEL(gemm_fc_dgrad, true, true, EPI_STORE, T)
+BLK_GEMM_KERNEL(gemm_o_dgrad, true, true, EPI_STORE, T)
+BLK_GEMM_KERNEL(gemm_qkv_dgrad, true, true, EPI_STORE, T)
 BLK_GEMM_KERNEL(gemm_proj_wgrad, false, false, EPI_F32, float)
 BLK_GEMM_KERNEL(gemm_fc_wgrad, false, false, EPI_F32, float)
 BLK_GEMM_KERNEL(gemm_o_wgrad, false, false, EPI_F32, float)
