@@ -497,7 +497,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(AttnArgs a) {
 // staged by buffer loads straight into LDS in a three-slot ring (prefetch
 // distance two tiles).  V^T fragments come from the row-major V tile through
 // the LDS transpose read (ds_read_b64_tr_b16).  Row layout: 16 chunks of 16
-// bytes per 128-wide row, chunk c of row r stored at c ^ (r & 15).
+// bytes per 128-wide row, swizzled by fa::sw.
 namespace fa {
 constexpr int QW = 64;                 // queries per wave
 constexpr int QWG = 4 * QW;            // queries per workgroup
@@ -507,7 +507,12 @@ constexpr int SLOT = 2 * TILE;         // K + V
 constexpr int NSLOT = 3;
 constexpr int LDS = NSLOT * SLOT;      // 96 KiB
 
-__device__ __forceinline__ int off(int row, int chunk) { return row * 256 + ((chunk ^ (row & 15)) << 4); }
+// Chunk c of row r is stored at c ^ sw(r), sw(r) = 2 * (r & 7): the 8
+// consecutive rows an MFMA fragment read touches per LDS cycle land on 8
+// distinct chunks, and the 4 rows x 2 adjacent chunks a 16-lane transpose
+// read touches land on 8 distinct chunks.
+__device__ __forceinline__ int sw(int row) { return (row << 1) & 14; }
+__device__ __forceinline__ int off(int row, int chunk) { return row * 256 + ((chunk ^ sw(row)) << 4); }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -521,7 +526,7 @@ __device__ __forceinline__ void issue_kv(char* slot, i32x4 rs, int k0, long ldb,
     for (int i = 0; i < 4; ++i) {
       const int base = wave * 256 + i * 64;     // chunk index in the tile (64 per issue)
       const int p = base + lane;
-      const int row = p >> 4, c = (p & 15) ^ (row & 15);
+      const int row = p >> 4, c = (p & 15) ^ sw(row);
       const uint32_t o = (uint32_t)((long)(k0 + row) * ldb + (t ? voff : koff) + c * 16);
       lds_u32* dst = (lds_u32*)(slot + t * TILE + __builtin_amdgcn_readfirstlane(base) * 16);
       raw_buffer_load_lds(rs, dst, 16, (int)o, 0, 0, 0);
@@ -544,7 +549,7 @@ __device__ __forceinline__ void frag_k_offsets(int* o, int lane) {
 
 // Per-lane byte offsets of the V^T transpose reads, run (0, 1) and d-block db
 // (add mm*4096 for MFMA chunk mm: 16 rows of 256 bytes, the swizzle only
-// depends on row & 15).
+// depends on row & 7).
 __device__ __forceinline__ void frag_vt_offsets(int* o, int lane) {
   const int g = (lane >> 4) & 3, s = lane & 15;
 #pragma unroll
@@ -723,7 +728,7 @@ __device__ __forceinline__ void issue_tile(char* dst, i32x4 rs, int r0, long ldb
   for (int i = 0; i < 4; ++i) {
     const int base = wave * 256 + i * 64;
     const int p = base + lane;
-    const int row = p >> 4, c = (p & 15) ^ (row & 15);
+    const int row = p >> 4, c = (p & 15) ^ sw(row);
     const uint32_t o = (uint32_t)((long)(r0 + row) * ldb + coff + c * 16);
     raw_buffer_load_lds(rs, (lds_u32*)(dst + __builtin_amdgcn_readfirstlane(base) * 16), 16, (int)o, 0, 0, 0);
   }

@@ -75,23 +75,39 @@ __device__ __forceinline__ uint32_t clamp_bytes(long b) { return b > 0xffffffffL
 
 // ---- staging ------------------------------------------------------------------
 // k-contiguous slab of R rows: 8 chunks per row, R*8 chunks, 64 per wave issue.
+// Each lane's LDS slot is fixed (slot = issue base + lane); the lane fetches
+// the global chunk that the swizzle puts there.  The row part of the global
+// offset is computed once; each k-step adds k0.
 template <typename TI, int R>
-__device__ __forceinline__ void stage_direct(char* lds, i32x4 rs, uint32_t oob, long ld, int r0, int rows_valid,
-                                             int k0, int k_end, int wave, int lane) {
-  constexpr int ELEM = GemmTile<TI>::ELEM;
-  constexpr int PER_WAVE = R * 8 / 4;            // chunks per wave
+struct DirectStager {
+  static constexpr int ELEM = GemmTile<TI>::ELEM;
+  static constexpr int PER_WAVE = R * 8 / 4;       // chunks per wave
+  static constexpr int NI = PER_WAVE / 64;         // issues per wave
+  uint32_t row_off[NI];                            // byte offset of (row, chunk) at k = 0
+  int kel[NI];                                     // element offset of the chunk along k
+  bool row_ok[NI];
+
+  __device__ __forceinline__ void init(long ld, int r0, int rows_valid, int wave, int lane) {
 #pragma unroll
-  for (int i = 0; i < PER_WAVE / 64; ++i) {
-    const int base = wave * PER_WAVE + i * 64;   // wave-uniform first LDS chunk
-    const int p = base + lane;
-    const int row = p >> 3, pc = p & 7;
-    const int c = pc ^ swz(row, 8);
-    const int gr = r0 + row, gk = k0 + c * ELEM;
-    const uint32_t off = (gr < rows_valid && gk < k_end) ? (uint32_t)(((long)gr * ld + gk) * sizeof(TI)) : oob;
-    lds_u32* dst = (lds_u32*)(lds + __builtin_amdgcn_readfirstlane(base) * 16);
-    raw_buffer_load_lds(rs, dst, 16, (int)off, 0, 0, 0);
+    for (int i = 0; i < NI; ++i) {
+      const int p = wave * PER_WAVE + i * 64 + lane;
+      const int row = p >> 3, c = (p & 7) ^ swz(row, 8);
+      row_ok[i] = r0 + row < rows_valid;
+      kel[i] = c * ELEM;
+      row_off[i] = (uint32_t)(((long)(r0 + row) * ld + c * ELEM) * sizeof(TI));
+    }
   }
-}
+  // k0 >= k_end (past the last k-step) reads nothing: every offset is out of range
+  __device__ __forceinline__ void issue(char* lds, i32x4 rs, uint32_t oob, int k0, int k_end, int wave) const {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const bool ok = row_ok[i] && (k0 + kel[i] < k_end);
+      const uint32_t off = ok ? row_off[i] + (uint32_t)(k0 * (int)sizeof(TI)) : oob;
+      lds_u32* dst = (lds_u32*)(lds + __builtin_amdgcn_readfirstlane(wave * PER_WAVE + i * 64) * 16);
+      raw_buffer_load_lds(rs, dst, 16, (int)off, 0, 0, 0);
+    }
+  }
+};
 
 // m-contiguous slab of R rows (of the m/n index) x BK of k: ELEM x ELEM blocks.
 template <typename TI, int R>
@@ -273,21 +289,6 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   const uint32_t bytesB = clamp_bytes((KB ? (long)g.N * g.ldb : (long)g.K * g.ldb) * (long)sizeof(TI));
   const i32x4 rsA = make_rsrc(g.A, bytesA), rsB = make_rsrc(g.B, bytesB);
 
-  StageTrans<TI, G::BM> ta;
-  StageTrans<TI, G::BN> tb;
-  auto issue = [&](int stage, int k0) {
-    char* s = smem + stage * G::SLAB;
-    if constexpr (KA) stage_direct<TI, G::BM>(s, rsA, bytesA, g.lda, m0, g.M, k0, kend, wave, lane);
-    else ta.load(rsA, bytesA, g.lda, m0, g.M, k0, kend);
-    if constexpr (KB) stage_direct<TI, G::BN>(s + G::BM * G::ROWB, rsB, bytesB, g.ldb, n0, g.N, k0, kend, wave, lane);
-    else tb.load(rsB, bytesB, g.ldb, n0, g.N, k0, kend);
-  };
-  auto commit = [&](int stage) {   // register-staged operands -> LDS
-    char* s = smem + stage * G::SLAB;
-    if constexpr (!KA) ta.store(s);
-    if constexpr (!KB) tb.store(s + G::BM * G::ROWB);
-  };
-
   f32x16 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -296,6 +297,26 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+  DirectStager<TI, G::BM> da;
+  DirectStager<TI, G::BN> db;
+  StageTrans<TI, G::BM> ta;
+  StageTrans<TI, G::BN> tb;
+  if constexpr (KA) da.init(g.lda, m0, g.M, wave, lane);
+  if constexpr (KB) db.init(g.ldb, n0, g.N, wave, lane);
+  auto issue = [&](int stage, int k0) {
+    char* s = smem + stage * G::SLAB;
+    if constexpr (KA) da.issue(s, rsA, bytesA, k0, kend, wave);
+    else ta.load(rsA, bytesA, g.lda, m0, g.M, k0, kend);
+    if constexpr (KB) db.issue(s + G::BM * G::ROWB, rsB, bytesB, k0, kend, wave);
+    else tb.load(rsB, bytesB, g.ldb, n0, g.N, k0, kend);
+  };
+  auto commit = [&](int stage) {   // register-staged operands -> LDS
+    char* s = smem + stage * G::SLAB;
+    if constexpr (!KA) ta.store(s);
+    if constexpr (!KB) tb.store(s + G::BM * G::ROWB);
+  };
+
+  constexpr int KS = G::BK / MM::KI;          // MFMA k-substeps per k-step
   if (nk > 0) {
     issue(0, kbeg);
     commit(0);
@@ -304,22 +325,45 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     // stage kt is complete (own loads, then everyone's); stage kt-1 is free
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (kt + 1 < nk) issue((kt + 1) & 1, kbeg + (kt + 1) * G::BK);
+    // next stage (past the end: out-of-range offsets, nothing is read)
+    issue((kt + 1) & 1, kbeg + (kt + 1) * G::BK);
     const char* cur = smem + (kt & 1) * G::SLAB;
+    // fragments of substep ks+1 are read while the MFMAs of substep ks run
+    typename MM::frag fa[2][4], fb[2][4];
 #pragma unroll
-    for (int ks = 0; ks < G::BK / MM::KI; ++ks) {
-      typename MM::frag fa[4], fb[4];
+    for (int i = 0; i < 4; ++i) fa[0][i] = load_frag<TI>(cur, wm * 128 + i * 32, 0, lane);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) fa[i] = load_frag<TI>(cur, wm * 128 + i * 32, ks, lane);
+    for (int j = 0; j < 4; ++j) fb[0][j] = load_frag<TI>(cur + G::BM * G::ROWB, wn * 128 + j * 32, 0, lane);
+    __builtin_amdgcn_sched_group_barrier(0x020, 16, 0);      // next stage's 16 global loads first
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);       // then substep 0's LDS reads
 #pragma unroll
-      for (int j = 0; j < 4; ++j) fb[j] = load_frag<TI>(cur + G::BM * G::ROWB, wn * 128 + j * 32, ks, lane);
+    for (int ks = 0; ks < KS; ++ks) {
+      const int c = ks & 1, n = c ^ 1;
+      if (ks + 1 < KS) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fa[n][i] = load_frag<TI>(cur, wm * 128 + i * 32, ks + 1, lane);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) fb[n][j] = load_frag<TI>(cur + G::BM * G::ROWB, wn * 128 + j * 32, ks + 1, lane);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = MM::mma(fa[i], fb[j], acc[i][j]);
+        for (int j = 0; j < 4; ++j) acc[i][j] = MM::mma(fa[c][i], fb[c][j], acc[i][j]);
+      if (ks + 1 < KS) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // 2 MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
+        }
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+      }
     }
     if (kt + 1 < nk) commit((kt + 1) & 1);
   }
+  // the past-the-end loads write zeros into LDS: let them land before the
+  // epilogue reuses LDS
+  __builtin_amdgcn_s_waitcnt(0);
   epilogue<TO, EPI>(g, acc, smem, m0, n0, split, wave, lane);
 }
 
