@@ -98,6 +98,8 @@ def library() -> ctypes.CDLL:
         lib.decode_scratch_bytes.restype = sz
         lib.decode_step.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.decode_step.restype = i32
+        lib.block_fp8_quantize.argtypes = [vp, sz, vp, vp, vp]
+        lib.block_fp8_quantize.restype = i32
         lib.block_timing_enable.argtypes = [i32]
         lib.block_timing_enable.restype = None
         lib.block_timing_read.argtypes = [i32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_double),
@@ -183,6 +185,11 @@ def decode_step(cfg: DecodeConfig, x, w_qkv, w_o, w_fc, w_proj, k_cache, v_cache
                                  _ptr(k_cache), _ptr(v_cache), _ptr(cache_len), _ptr(y), _ptr(scratch),
                                  _nbytes(scratch, scratch_bytes), _stream(stream))
     return _check(code, "decode_step", raise_on_error)
+
+
+def block_fp8_quantize(x, n: int, codes, amax, *, stream=None, raise_on_error=True) -> int:
+    code = library().block_fp8_quantize(_ptr(x), int(n), _ptr(codes), _ptr(amax), _stream(stream))
+    return _check(code, "block_fp8_quantize", raise_on_error)
 
 
 def block_timing_enable(on: bool) -> None:

@@ -13,6 +13,7 @@
 #include "../../include/blk.h"
 #include "attention.cuh"
 #include "elementwise.cuh"
+#include "fp8.cuh"
 #include "gemm.cuh"
 
 using namespace blk;
@@ -45,8 +46,14 @@ template <typename T> struct Saved {
   T* h2;         // [N, C]
   T* u;          // [N, F]
   T* a;          // [N, F]
+  // fp8 mode: transposed E4M3 copies of the weight-gradient operands, [*, Np]
+  // with Np = N rounded up to 64 (zero padding), and the 16 amax slots
+  uint8_t *h1_8t = nullptr, *o_8t = nullptr, *h2_8t = nullptr, *a_8t = nullptr;
+  unsigned* amax = nullptr;
   size_t bytes;
 };
+
+long pad64(long n) { return (n + 63) / 64 * 64; }
 
 template <typename T> Saved<T> carve_saved(const blk_cfg& c, void* p) {
   const long N = (long)c.B * c.T;
@@ -63,8 +70,37 @@ template <typename T> Saved<T> carve_saved(const blk_cfg& c, void* p) {
   s.h2 = k.take<T>(N * c.C);
   s.u = k.take<T>(N * c.F);
   s.a = k.take<T>(N * c.F);
+  if (c.gemm == BLK_GEMM_FP8_E4M3) {
+    const long Np = pad64(N);
+    s.h1_8t = k.take<uint8_t>(c.C * Np);
+    s.o_8t = k.take<uint8_t>(c.C * Np);
+    s.h2_8t = k.take<uint8_t>(c.C * Np);
+    s.a_8t = k.take<uint8_t>(c.F * Np);
+    s.amax = k.take<unsigned>(16);
+  }
   s.bytes = (k.off + 255) & ~size_t(255);
   return s;
+}
+
+// fp8-mode forward temporaries: row-major E4M3 operands and weights.
+struct Fwd8 {
+  uint8_t *h1, *o, *h2, *a, *wqkv, *wo, *wfc, *wproj;
+  size_t bytes;
+};
+Fwd8 carve_fwd8(const blk_cfg& c, void* p) {
+  const long N = (long)c.B * c.T, C = c.C, F = c.F;
+  Carver k(p);
+  Fwd8 f;
+  f.h1 = k.take<uint8_t>(N * C);
+  f.o = k.take<uint8_t>(N * C);
+  f.h2 = k.take<uint8_t>(N * C);
+  f.a = k.take<uint8_t>(N * F);
+  f.wqkv = k.take<uint8_t>(3 * C * C);
+  f.wo = k.take<uint8_t>(C * C);
+  f.wfc = k.take<uint8_t>(F * C);
+  f.wproj = k.take<uint8_t>(C * F);
+  f.bytes = (k.off + 255) & ~size_t(255);
+  return f;
 }
 
 // Split-k factor of a weight-gradient GEMM: enough workgroups to fill the
@@ -86,6 +122,10 @@ template <typename T> struct BwdScratch {
   T* wt;        // transposed weights: W_proj^T [F,C], W_fc^T [C,F], W_o^T [C,C], W_qkv^T [C,3C]
   float* delta; // [B*H][T]
   float* part;  // split-k partial sums
+  // fp8 mode: E4M3 copies of the gradients (row-major and transposed [*, Np])
+  // and of the transposed weights
+  uint8_t *g8 = nullptr, *g8t = nullptr, *du8 = nullptr, *du8t = nullptr, *dqkv8 = nullptr, *dqkv8t = nullptr,
+          *wt8 = nullptr;
   size_t bytes;
 };
 
@@ -100,14 +140,24 @@ template <typename T> BwdScratch<T> carve_bwd(const blk_cfg& c, void* p) {
   s.dqkv = k.take<T>(N * 3 * c.C);
   s.wt = k.take<T>(12L * c.C * c.C);
   s.delta = k.take<float>((size_t)c.B * c.H * c.T);
-  constexpr int BK = GemmTile<T>::BK;
   size_t part = 0;
   const int shapes[4][2] = {{c.C, c.F}, {c.F, c.C}, {c.C, c.C}, {3 * c.C, c.C}};
-  for (auto& sh : shapes) {
-    int sp = wgrad_splits(sh[0], sh[1], N, BK);
-    if (sp > 1) part = std::max(part, (size_t)sp * sh[0] * sh[1]);
-  }
+  for (int bk : {GemmTile<T>::BK, GemmTile<fp8e4>::BK})
+    for (auto& sh : shapes) {
+      int sp = wgrad_splits(sh[0], sh[1], N, bk);
+      if (sp > 1) part = std::max(part, (size_t)sp * sh[0] * sh[1]);
+    }
   s.part = k.take<float>(part);
+  if (c.gemm == BLK_GEMM_FP8_E4M3) {
+    const long Np = pad64(N);
+    s.g8 = k.take<uint8_t>(N * c.C);
+    s.g8t = k.take<uint8_t>(c.C * Np);
+    s.du8 = k.take<uint8_t>(N * c.F);
+    s.du8t = k.take<uint8_t>(c.F * Np);
+    s.dqkv8 = k.take<uint8_t>(N * 3 * c.C);
+    s.dqkv8t = k.take<uint8_t>(3 * c.C * Np);
+    s.wt8 = k.take<uint8_t>(12L * c.C * c.C);
+  }
   s.bytes = (k.off + 255) & ~size_t(255);
   return s;
 }
@@ -120,7 +170,7 @@ int check_cfg(const blk_cfg* c) {
   if (!(c->eps >= 0.f) || !(c->rope_base > 0.f)) return BLK_EINVAL;
   if (c->dtype != BLK_F32 && c->dtype != BLK_BF16) return BLK_EINVAL;
   if (c->gemm != BLK_GEMM_NATIVE && c->gemm != BLK_GEMM_FP8_E4M3) return BLK_EINVAL;
-  if (c->gemm == BLK_GEMM_FP8_E4M3) return BLK_EUNSUPPORTED;
+  if (c->gemm == BLK_GEMM_FP8_E4M3 && c->dtype != BLK_BF16) return BLK_EUNSUPPORTED;
   // row kernels keep a row in registers: 8 chunks of 16 bytes per lane
   if ((long)c->C * (c->dtype == BLK_BF16 ? 2 : 4) > 8L * 64 * 16) return BLK_EUNSUPPORTED;
   if ((long)c->B * c->T * 3L * c->C >= (1L << 31)) return BLK_EUNSUPPORTED;
@@ -406,11 +456,220 @@ int bwd_impl(const blk_cfg& c, const T* dy, const T* x, const T* wqkv, const T* 
   return launch_status();
 }
 
+// ---------------------------------------------------------------- fp8 mode
+unsigned elt_grid(long n) { return (unsigned)std::min<long>(std::max<long>((n / 8 + 255) / 256, 1), 4096); }
+
+// amax of x (rows x cols bf16) max-accumulated into *am; then, if given, the
+// row-major codes q and the transposed codes qt ([cols][ldt], zero padded).
+void quantize(const bf16* x, long rows, long cols, unsigned* am, uint8_t* q, uint8_t* qt, long ldt, bool amax,
+              hipStream_t st) {
+  const long n = rows * cols;
+  Timed t("fp8_quantize", st);
+  if (amax) hipLaunchKernelGGL(amax_kernel, dim3(elt_grid(n)), dim3(256), 0, st, x, n, am);
+  if (q) hipLaunchKernelGGL(quant_kernel, dim3(elt_grid(n)), dim3(256), 0, st, x, n, (const unsigned*)am, q);
+  if (qt)
+    hipLaunchKernelGGL(quant_trans_kernel, dim3((unsigned)(cols / 64), (unsigned)(ldt / 64)), dim3(256), 0, st, x,
+                       (int)rows, (int)cols, (const unsigned*)am, qt, (int)ldt);
+}
+
+GemmArgs gargs8(const uint8_t* A, long lda, const unsigned* ama, const uint8_t* B, long ldb, const unsigned* amb,
+                int M, int N, int K) {
+  GemmArgs g = gargs(A, lda, B, ldb, M, N, K);
+  g.amax_a = ama;
+  g.amax_b = amb;
+  return g;
+}
+
+// dW[M, N] (+)= sum_k GT[m, k] XT[n, k], E4M3 operands [*, ld], fp32 out.
+void wgrad8(void (*kern)(GemmArgs), void (*kern_acc)(GemmArgs), const char* name, const uint8_t* GT, const unsigned* ama,
+            const uint8_t* XT, const unsigned* amb, long ld, float* dW, int M, int N, int K, int accumulate,
+            float* part, hipStream_t st) {
+  GemmArgs g = gargs8(GT, ld, ama, XT, ld, amb, M, N, K);
+  constexpr int BK = GemmTile<fp8e4>::BK;
+  const int sp = wgrad_splits(M, N, K, BK);
+  if (sp <= 1) {
+    g.out = dW; g.ldo = N;
+    gemm<fp8e4>(accumulate ? kern_acc : kern, name, g, 1, st);
+    return;
+  }
+  g.out = part; g.ldo = N;
+  gemm<fp8e4>(kern, name, g, sp, st);
+  long per = ((long)K + sp - 1) / sp;
+  int ks = (int)(((per + BK - 1) / BK) * BK);
+  int real = (K + ks - 1) / ks;
+  const long n = (long)M * N;
+  Timed t("splitk_reduce", st);
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, st, dW,
+                     (const float*)part, n, real, accumulate);
+}
+
+// amax slots: forward h1 o h2 a | W_qkv W_o W_fc W_proj ; backward dy du dy1 dqkv
+enum { AM_H1, AM_O, AM_H2, AM_A, AM_WQKV, AM_WO, AM_WFC, AM_WPROJ, AM_DY, AM_DU, AM_DY1, AM_DQKV };
+
+int fwd_fp8(const blk_cfg& c, const bf16* x, const bf16* wqkv, const bf16* wo, const bf16* wfc, const bf16* wproj,
+            bf16* y, const Saved<bf16>& s, const Fwd8& f, hipStream_t st) {
+  const int N = c.B * c.T, C = c.C, F = c.F, H = c.H;
+  const long Np = pad64(N);
+  unsigned* am = s.amax;
+  hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, st, am, 16);
+  {
+    Timed t("rope_table", st);
+    hipLaunchKernelGGL(rope_table_kernel, dim3((c.T * 64 + 255) / 256), dim3(256), 0, st, s.cs, c.T, 128,
+                       (double)c.rope_base);
+  }
+  {
+    Timed t("rmsnorm_fwd", st);
+    hipLaunchKernelGGL(rmsnorm_fwd_kernel<bf16>, dim3(row_blocks(N)), dim3(256), 0, st, x, s.h1, s.r1, N, C, c.eps);
+  }
+  quantize(wqkv, 3 * C, C, am + AM_WQKV, f.wqkv, nullptr, 0, true, st);
+  quantize(wo, C, C, am + AM_WO, f.wo, nullptr, 0, true, st);
+  quantize(wfc, F, C, am + AM_WFC, f.wfc, nullptr, 0, true, st);
+  quantize(wproj, C, F, am + AM_WPROJ, f.wproj, nullptr, 0, true, st);
+  quantize(s.h1, N, C, am + AM_H1, f.h1, s.h1_8t, Np, true, st);
+  {
+    GemmArgs g = gargs8(f.h1, C, am + AM_H1, f.wqkv, C, am + AM_WQKV, N, 3 * C, C);
+    g.out = s.qkv; g.ldo = 3 * C;
+    gemm<fp8e4>(gemm8_qkv_fwd, "gemm_qkv_fwd", g, 1, st);
+  }
+  {
+    Timed t("rope_qknorm_fwd", st);
+    hipLaunchKernelGGL(rope_qknorm_fwd_kernel<bf16>, dim3(row_blocks((long)N * H * 2)), dim3(256), 0, st, s.qkv,
+                       s.rho, (const float2*)s.cs, N, c.T, H, C, c.eps);
+  }
+  {
+    AttnArgs a = attn_args<bf16>(c);
+    a.qkv = s.qkv; a.o = s.o; a.lse = s.lse;
+    Timed t("attn_fwd", st);
+    need_lds(reinterpret_cast<const void*>(attn_fwd_bf16_kernel), fa::LDS);
+    const int nqt = (c.T + fa::QWG - 1) / fa::QWG;
+    hipLaunchKernelGGL(attn_fwd_bf16_kernel, dim3(nqt * c.B * H), dim3(256), fa::LDS, st, a);
+  }
+  quantize(s.o, N, C, am + AM_O, f.o, s.o_8t, Np, true, st);
+  {
+    GemmArgs g = gargs8(f.o, C, am + AM_O, f.wo, C, am + AM_WO, N, C, C);
+    g.out = y; g.ldo = C; g.aux = x; g.ldaux = C;
+    gemm<fp8e4>(gemm8_o_fwd, "gemm_o_fwd", g, 1, st);
+  }
+  {
+    Timed t("rmsnorm_fwd", st);
+    hipLaunchKernelGGL(rmsnorm_fwd_kernel<bf16>, dim3(row_blocks(N)), dim3(256), 0, st, (const bf16*)y, s.h2, s.r2, N,
+                       C, c.eps);
+  }
+  quantize(s.h2, N, C, am + AM_H2, f.h2, s.h2_8t, Np, true, st);
+  {
+    GemmArgs g = gargs8(f.h2, C, am + AM_H2, f.wfc, C, am + AM_WFC, N, F, C);
+    g.out = s.u; g.ldo = F; g.out2 = s.a; g.ldo2 = F;
+    gemm<fp8e4>(gemm8_fc_fwd, "gemm_fc_fwd", g, 1, st);
+  }
+  quantize(s.a, N, F, am + AM_A, f.a, s.a_8t, Np, true, st);
+  {
+    GemmArgs g = gargs8(f.a, F, am + AM_A, f.wproj, F, am + AM_WPROJ, N, C, F);
+    g.out = y; g.ldo = C; g.aux = y; g.ldaux = C;
+    gemm<fp8e4>(gemm8_proj_fwd, "gemm_proj_fwd", g, 1, st);
+  }
+  return launch_status();
+}
+
+int bwd_fp8(const blk_cfg& c, const bf16* dy, const bf16* wqkv, const bf16* wo, const bf16* wfc, const bf16* wproj,
+            const Saved<bf16>& s, bf16* dx, float* dwqkv, float* dwo, float* dwfc, float* dwproj, int acc,
+            const BwdScratch<bf16>& w, hipStream_t st) {
+  const int N = c.B * c.T, C = c.C, F = c.F, H = c.H;
+  const long Np = pad64(N);
+  unsigned* am = s.amax;     // forward slots hold the weights' and activations' maxima
+  hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, st, am + AM_DY, 4);
+  // transposed E4M3 weights (same scales as the forward's row-major copies)
+  uint8_t* wt_proj = w.wt8;                 // [F, C]
+  uint8_t* wt_fc = wt_proj + (long)F * C;   // [C, F]
+  uint8_t* wt_o = wt_fc + (long)C * F;      // [C, C]
+  uint8_t* wt_qkv = wt_o + (long)C * C;     // [C, 3C]
+  quantize(wproj, C, F, am + AM_WPROJ, nullptr, wt_proj, C, false, st);
+  quantize(wfc, F, C, am + AM_WFC, nullptr, wt_fc, F, false, st);
+  quantize(wo, C, C, am + AM_WO, nullptr, wt_o, C, false, st);
+  quantize(wqkv, 3 * C, C, am + AM_WQKV, nullptr, wt_qkv, 3 * C, false, st);
+
+  quantize(dy, N, C, am + AM_DY, w.g8, w.g8t, Np, true, st);
+  {  // du = (dy W_proj) * 2 max(u, 0)
+    GemmArgs g = gargs8(w.g8, C, am + AM_DY, wt_proj, C, am + AM_WPROJ, N, F, C);
+    g.out = w.du; g.ldo = F; g.aux = s.u; g.ldaux = F;
+    gemm<fp8e4>(gemm8_proj_dgrad, "gemm_proj_dgrad", g, 1, st);
+  }
+  wgrad8(gemm8_proj_wgrad, gemm8_proj_wgrad_acc, "gemm_proj_wgrad", w.g8t, am + AM_DY, s.a_8t, am + AM_A, Np, dwproj,
+         C, F, N, acc, w.part, st);
+  quantize(w.du, N, F, am + AM_DU, w.du8, w.du8t, Np, true, st);
+  {  // dh2 = du W_fc
+    GemmArgs g = gargs8(w.du8, F, am + AM_DU, wt_fc, F, am + AM_WFC, N, C, F);
+    g.out = w.dh; g.ldo = C;
+    gemm<fp8e4>(gemm8_fc_dgrad, "gemm_fc_dgrad", g, 1, st);
+  }
+  wgrad8(gemm8_fc_wgrad, gemm8_fc_wgrad_acc, "gemm_fc_wgrad", w.du8t, am + AM_DU, s.h2_8t, am + AM_H2, Np, dwfc, F, C,
+         N, acc, w.part, st);
+  {
+    Timed t("rmsnorm_bwd", st);
+    hipLaunchKernelGGL(rmsnorm_bwd_kernel<bf16>, dim3(row_blocks(N)), dim3(256), 0, st, dy, (const bf16*)w.dh,
+                       (const bf16*)s.h2, (const float*)s.r2, w.dy1, N, C);
+  }
+  quantize(w.dy1, N, C, am + AM_DY1, w.g8, w.g8t, Np, true, st);
+  {  // do = dy1 W_o
+    GemmArgs g = gargs8(w.g8, C, am + AM_DY1, wt_o, C, am + AM_WO, N, C, C);
+    g.out = w.dO; g.ldo = C;
+    gemm<fp8e4>(gemm8_o_dgrad, "gemm_o_dgrad", g, 1, st);
+  }
+  wgrad8(gemm8_o_wgrad, gemm8_o_wgrad_acc, "gemm_o_wgrad", w.g8t, am + AM_DY1, s.o_8t, am + AM_O, Np, dwo, C, C, N,
+         acc, w.part, st);
+  {
+    {
+      Timed t("attn_delta", st);
+      hipLaunchKernelGGL(attn_delta_kernel<bf16>, dim3(row_blocks((long)N * H)), dim3(256), 0, st,
+                         (const bf16*)w.dO, (const bf16*)s.o, w.delta, N, c.T, H, C);
+    }
+    AttnArgs a = attn_args<bf16>(c);
+    a.qkv = s.qkv; a.lse = s.lse; a.dO = w.dO; a.delta = w.delta; a.dqkv = w.dqkv;
+    constexpr int DKDV_LDS = 3 * (2 * fa::TILE + 2048);
+    need_lds(reinterpret_cast<const void*>(attn_bwd_dkdv_bf16_kernel), DKDV_LDS);
+    need_lds(reinterpret_cast<const void*>(attn_bwd_dq_bf16_kernel), fa::LDS);
+    const int nqt = (c.T + 127) / 128;
+    {
+      Timed t("attn_bwd_dkdv", st);
+      hipLaunchKernelGGL(attn_bwd_dkdv_bf16_kernel, dim3(nqt * c.B * H), dim3(256), DKDV_LDS, st, a);
+    }
+    {
+      Timed t("attn_bwd_dq", st);
+      hipLaunchKernelGGL(attn_bwd_dq_bf16_kernel, dim3(nqt * c.B * H), dim3(256), fa::LDS, st, a);
+    }
+  }
+  {
+    Timed t("qknorm_rope_bwd", st);
+    hipLaunchKernelGGL(qknorm_rope_bwd_kernel<bf16>, dim3(row_blocks((long)N * H * 2)), dim3(256), 0, st, w.dqkv,
+                       (const bf16*)s.qkv, (const float*)s.rho, (const float2*)s.cs, N, c.T, H, C);
+  }
+  quantize(w.dqkv, N, 3 * C, am + AM_DQKV, w.dqkv8, w.dqkv8t, Np, true, st);
+  {  // dh1 = dqkv W_qkv
+    GemmArgs g = gargs8(w.dqkv8, 3 * C, am + AM_DQKV, wt_qkv, 3 * C, am + AM_WQKV, N, C, 3 * C);
+    g.out = w.dh; g.ldo = C;
+    gemm<fp8e4>(gemm8_qkv_dgrad, "gemm_qkv_dgrad", g, 1, st);
+  }
+  wgrad8(gemm8_qkv_wgrad, gemm8_qkv_wgrad_acc, "gemm_qkv_wgrad", w.dqkv8t, am + AM_DQKV, s.h1_8t, am + AM_H1, Np,
+         dwqkv, 3 * C, C, N, acc, w.part, st);
+  {
+    Timed t("rmsnorm_bwd", st);
+    hipLaunchKernelGGL(rmsnorm_bwd_kernel<bf16>, dim3(row_blocks(N)), dim3(256), 0, st, (const bf16*)w.dy1,
+                       (const bf16*)w.dh, (const bf16*)s.h1, (const float*)s.r1, dx, N, C);
+  }
+  return launch_status();
+}
+
 size_t saved_bytes(const blk_cfg& c) {
   return c.dtype == BLK_BF16 ? carve_saved<bf16>(c, nullptr).bytes : carve_saved<float>(c, nullptr).bytes;
 }
 size_t bwd_bytes(const blk_cfg& c) {
   return c.dtype == BLK_BF16 ? carve_bwd<bf16>(c, nullptr).bytes : carve_bwd<float>(c, nullptr).bytes;
+}
+// forward temporaries: the saved store itself when saved == NULL, then the
+// fp8 operand copies in fp8 mode
+size_t fwd_scratch_bytes(const blk_cfg& c, bool with_saved) {
+  size_t b = with_saved ? saved_bytes(c) : 0;
+  if (c.gemm == BLK_GEMM_FP8_E4M3) b += carve_fwd8(c, nullptr).bytes;
+  return b;
 }
 
 }  // namespace
@@ -424,7 +683,7 @@ size_t block_saved_bytes(const blk_cfg* cfg) {
 
 size_t block_scratch_bytes(const blk_cfg* cfg) {
   if (check_cfg(cfg) != BLK_OK) return 0;
-  return std::max(saved_bytes(*cfg), bwd_bytes(*cfg));
+  return std::max(fwd_scratch_bytes(*cfg, true), bwd_bytes(*cfg));
 }
 
 int block_fwd(const blk_cfg* cfg, const void* x, const void* w_qkv, const void* w_o, const void* w_fc,
@@ -442,14 +701,21 @@ int block_fwd(const blk_cfg* cfg, const void* x, const void* w_qkv, const void* 
   if (saved) {
     if (!aligned(saved)) return BLK_EALIGN;
     if (saved_sz < need) return BLK_ENOSPC;
-  } else {
+  }
+  const size_t scratch_need = fwd_scratch_bytes(c, saved == nullptr);
+  if (scratch_need > 0) {
     if (!scratch) return BLK_EINVAL;
     if (!aligned(scratch)) return BLK_EALIGN;
-    if (scratch_sz < need) return BLK_ENOSPC;
-    store = scratch;
+    if (scratch_sz < scratch_need) return BLK_ENOSPC;
   }
+  if (!saved) store = scratch;
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipGetLastError();
+  if (c.gemm == BLK_GEMM_FP8_E4M3) {
+    char* f8 = static_cast<char*>(scratch) + (saved ? 0 : need);
+    return fwd_fp8(c, (const bf16*)x, (const bf16*)w_qkv, (const bf16*)w_o, (const bf16*)w_fc, (const bf16*)w_proj,
+                   (bf16*)y, carve_saved<bf16>(c, store), carve_fwd8(c, f8), st);
+  }
   if (c.dtype == BLK_BF16)
     return fwd_impl<bf16>(c, (const bf16*)x, (const bf16*)w_qkv, (const bf16*)w_o, (const bf16*)w_fc,
                           (const bf16*)w_proj, (bf16*)y, carve_saved<bf16>(c, store), st);
@@ -474,6 +740,10 @@ int block_bwd(const blk_cfg* cfg, const void* dy, const void* x, const void* w_q
   if (saved_sz < saved_bytes(c) || scratch_sz < bwd_bytes(c)) return BLK_ENOSPC;
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipGetLastError();
+  if (c.gemm == BLK_GEMM_FP8_E4M3)
+    return bwd_fp8(c, (const bf16*)dy, (const bf16*)w_qkv, (const bf16*)w_o, (const bf16*)w_fc, (const bf16*)w_proj,
+                   carve_saved<bf16>(c, const_cast<void*>(saved)), (bf16*)dx, dw_qkv, dw_o, dw_fc, dw_proj, accumulate,
+                   carve_bwd<bf16>(c, scratch), st);
   if (c.dtype == BLK_BF16)
     return bwd_impl<bf16>(c, (const bf16*)dy, (const bf16*)x, (const bf16*)w_qkv, (const bf16*)w_o,
                           (const bf16*)w_fc, (const bf16*)w_proj, carve_saved<bf16>(c, const_cast<void*>(saved)),
@@ -494,6 +764,17 @@ int decode_step(const blk_dcfg* cfg, const void* x, const void* w_qkv, const voi
   (void)cfg; (void)x; (void)w_qkv; (void)w_o; (void)w_fc; (void)w_proj; (void)k_cache; (void)v_cache;
   (void)cache_len; (void)y; (void)scratch; (void)scratch_bytes; (void)stream;
   return BLK_EUNSUPPORTED;
+}
+
+int block_fp8_quantize(const void* x, size_t n, void* codes, uint32_t* amax, void* stream) {
+  if (!x || !codes || !amax) return BLK_EINVAL;
+  if (n == 0 || n % 8 != 0) return BLK_EINVAL;
+  if (!aligned(x) || !aligned(codes) || (reinterpret_cast<uintptr_t>(amax) & 3)) return BLK_EALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipGetLastError();
+  hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, st, (unsigned*)amax, 1);
+  quantize(static_cast<const bf16*>(x), 1, (long)n, (unsigned*)amax, static_cast<uint8_t*>(codes), nullptr, 0, true, st);
+  return launch_status();
 }
 
 void block_timing_enable(int on) {

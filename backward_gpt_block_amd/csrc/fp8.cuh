@@ -1,0 +1,107 @@
+// FP8 (OCP E4M3) support for the fp8 mode of the linear layers: per-tensor
+// absolute maximum, quantisation to E4M3 codes (row-major and transposed
+// copies) with current scaling s = amax/448, saturating at +-448, rounding to
+// nearest even (the conversion instruction's default mode).
+//
+// FP8 training of the linear layers is named on the flicky.cc nanochat page
+// (repository map, nanochat/fp8.py) and in the README mirror's leaderboard
+// ("d26 ... +fp8"); the format and the scaling recipe are not on the pages.
+#pragma once
+#include "common.cuh"
+
+namespace blk {
+
+constexpr float E4M3_MAX = 448.f;
+
+// Non-negative floats order like their bit patterns, so max is an integer max.
+__device__ __forceinline__ float amax_value(const unsigned* a) { return __uint_as_float(*a); }
+__device__ __forceinline__ float quant_inv(float amax) { return amax > 0.f ? E4M3_MAX / amax : 1.f; }
+__device__ __forceinline__ float quant_scale(float amax) { return amax > 0.f ? amax / E4M3_MAX : 1.f; }
+
+// Two floats (already scaled) -> two E4M3 codes in the low 16 bits.
+__device__ __forceinline__ uint32_t e4m3x2(float a, float b) {
+  a = fminf(fmaxf(a, -E4M3_MAX), E4M3_MAX);
+  b = fminf(fmaxf(b, -E4M3_MAX), E4M3_MAX);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xffffu;
+}
+
+__global__ void zero_u32_kernel(unsigned* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// out = max(out, max |x|) over n elements (n % 8 == 0), bf16 input.
+__global__ __launch_bounds__(256) void amax_kernel(const bf16* __restrict__ x, long n, unsigned* __restrict__ out) {
+  float m = 0.f;
+  for (long i = ((long)blockIdx.x * 256 + threadIdx.x) * 8; i < n; i += (long)gridDim.x * 256 * 8) {
+    float f[8];
+    Chunk<bf16>::unpack(ld16(x + i), f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(f[e]));
+  }
+  m = wave_max(m);
+  __shared__ float wm[4];
+  if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
+    atomicMax(out, __float_as_uint(m));
+  }
+}
+
+// q[i] = e4m3(x[i] * 448/amax), n % 8 == 0.
+__global__ __launch_bounds__(256) void quant_kernel(const bf16* __restrict__ x, long n, const unsigned* __restrict__ amax,
+                                                    uint8_t* __restrict__ q) {
+  const float inv = quant_inv(amax_value(amax));
+  for (long i = ((long)blockIdx.x * 256 + threadIdx.x) * 8; i < n; i += (long)gridDim.x * 256 * 8) {
+    float f[8];
+    Chunk<bf16>::unpack(ld16(x + i), f);
+    u32x2 o;
+    o[0] = e4m3x2(f[0] * inv, f[1] * inv) | (e4m3x2(f[2] * inv, f[3] * inv) << 16);
+    o[1] = e4m3x2(f[4] * inv, f[5] * inv) | (e4m3x2(f[6] * inv, f[7] * inv) << 16);
+    st8(q + i, o);
+  }
+}
+
+// qT[c][r] = e4m3(x[r][c] * 448/amax) for a rows x cols bf16 matrix (cols %
+// 64 == 0); qT has leading dimension ldT >= rows (a multiple of 64) and the
+// padding columns rows..ldT-1 are written as 0.  64 x 64 tiles through LDS.
+__global__ __launch_bounds__(256) void quant_trans_kernel(const bf16* __restrict__ x, int rows, int cols,
+                                                          const unsigned* __restrict__ amax, uint8_t* __restrict__ qT,
+                                                          int ldT) {
+  __shared__ uint8_t t[64][65];
+  const float inv = quant_inv(amax_value(amax));
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int tx = threadIdx.x & 7, ty = threadIdx.x >> 3;      // 8 chunks of 8 columns x 32 rows per pass
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int r = ty + 32 * p;
+    float f[8];
+    if (r0 + r < rows) {
+      Chunk<bf16>::unpack(ld16(x + (long)(r0 + r) * cols + c0 + tx * 8), f);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const uint32_t two = e4m3x2(f[e] * inv, f[e + 1] * inv);
+      t[tx * 8 + e][r] = (uint8_t)(two & 0xff);
+      t[tx * 8 + e + 1][r] = (uint8_t)(two >> 8);
+    }
+  }
+  __syncthreads();
+  // write: row c of qT gets 64 bytes (r0..r0+63); 4 threads x 16 bytes per row
+  const int wr = threadIdx.x >> 2, wq = threadIdx.x & 3;
+  u32x4 v;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) word |= (uint32_t)t[wr][wq * 16 + w * 4 + b] << (8 * b);
+    v[w] = word;
+  }
+  st16(qT + (long)(c0 + wr) * ldT + r0 + wq * 16, v);
+}
+
+}  // namespace blk

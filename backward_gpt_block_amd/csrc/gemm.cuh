@@ -44,7 +44,10 @@ struct GemmArgs {
   void* out2; long ldo2;
   const void* aux; long ldaux;
   float alpha;
-  const float* alpha_ptr;  // if non-null, alpha *= alpha_ptr[0] * alpha_ptr[1]
+  // fp8 operands: per-tensor absolute maxima (float bits); the epilogue
+  // multiplies by (amax_a/448) * (amax_b/448) (a zero amax counts as 448)
+  const unsigned* amax_a;
+  const unsigned* amax_b;
 };
 
 template <typename TI> struct GemmTile {
@@ -115,10 +118,10 @@ struct StageTrans {
   static constexpr int ELEM = GemmTile<TI>::ELEM;
   static constexpr int RB = R / ELEM;
   static constexpr int NB = (GemmTile<TI>::BK / ELEM) * RB / GemmTile<TI>::NT;   // blocks per thread
-  static_assert(NB >= 1, "slab too small for the transposing stager");
-  u32x4 reg[NB * ELEM];
+  u32x4 reg[NB > 0 ? NB * ELEM : 1];
 
   __device__ __forceinline__ void load(i32x4 rs, uint32_t oob, long ld, int r0, int rows_valid, int k0, int k_end) {
+    static_assert(NB >= 1, "slab too small for the transposing stager");
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       const int blkid = threadIdx.x + b * GemmTile<TI>::NT;
@@ -239,7 +242,10 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[4][4],
                                          int split, int wave, int lane) {
   const int wm = wave >> 1, wn = wave & 1;
   float alpha = g.alpha;
-  if (g.alpha_ptr) alpha *= g.alpha_ptr[0] * g.alpha_ptr[1];
+  if (g.amax_a) {
+    const float a = __uint_as_float(*g.amax_a), b = __uint_as_float(*g.amax_b);
+    alpha *= (a > 0.f ? a / 448.f : 1.f) * (b > 0.f ? b / 448.f : 1.f);
+  }
   char* wreg = smem + wave * 32768;
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
@@ -394,4 +400,30 @@ BLK_GEMM_KERNEL(gemm_proj_wgrad_acc, false, false, EPI_F32_ADD, float)
 BLK_GEMM_KERNEL(gemm_fc_wgrad_acc, false, false, EPI_F32_ADD, float)
 BLK_GEMM_KERNEL(gemm_o_wgrad_acc, false, false, EPI_F32_ADD, float)
 BLK_GEMM_KERNEL(gemm_qkv_wgrad_acc, false, false, EPI_F32_ADD, float)
+}  // namespace blk
+
+// FP8 (E4M3) linear layers: every GEMM takes k-contiguous operands (weights
+// and activations quantised row-major, or transposed for weight gradients).
+#define BLK_GEMM8_KERNEL(NAME, EPI, TO)                                           \
+  __global__ __launch_bounds__(256, 1) void NAME(GemmArgs g) {                   \
+    gemm_body<fp8e4, TO, true, true, EPI>(g);                                   \
+  }
+
+namespace blk {
+BLK_GEMM8_KERNEL(gemm8_qkv_fwd, EPI_STORE, bf16)
+BLK_GEMM8_KERNEL(gemm8_o_fwd, EPI_RESID, bf16)
+BLK_GEMM8_KERNEL(gemm8_fc_fwd, EPI_RELU2, bf16)
+BLK_GEMM8_KERNEL(gemm8_proj_fwd, EPI_RESID, bf16)
+BLK_GEMM8_KERNEL(gemm8_proj_dgrad, EPI_DRELU2, bf16)
+BLK_GEMM8_KERNEL(gemm8_fc_dgrad, EPI_STORE, bf16)
+BLK_GEMM8_KERNEL(gemm8_o_dgrad, EPI_STORE, bf16)
+BLK_GEMM8_KERNEL(gemm8_qkv_dgrad, EPI_STORE, bf16)
+BLK_GEMM8_KERNEL(gemm8_proj_wgrad, EPI_F32, float)
+BLK_GEMM8_KERNEL(gemm8_fc_wgrad, EPI_F32, float)
+BLK_GEMM8_KERNEL(gemm8_o_wgrad, EPI_F32, float)
+BLK_GEMM8_KERNEL(gemm8_qkv_wgrad, EPI_F32, float)
+BLK_GEMM8_KERNEL(gemm8_proj_wgrad_acc, EPI_F32_ADD, float)
+BLK_GEMM8_KERNEL(gemm8_fc_wgrad_acc, EPI_F32_ADD, float)
+BLK_GEMM8_KERNEL(gemm8_o_wgrad_acc, EPI_F32_ADD, float)
+BLK_GEMM8_KERNEL(gemm8_qkv_wgrad_acc, EPI_F32_ADD, float)
 }  // namespace blk

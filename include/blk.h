@@ -97,6 +97,7 @@ size_t block_scratch_bytes(const blk_cfg* cfg);
 
 /* Forward of the block.
  *   x      [B,T,C]   input rows (dtype)
+ *   (fp8 mode: scratch is always required; it holds the E4M3 operand copies)
  *   w_qkv  [3C,C], w_o [C,C], w_fc [F,C], w_proj [C,F]   (dtype)
  *   y      [B,T,C]   output (dtype); may not alias x
  *   saved  activation store of block_saved_bytes(cfg) bytes, written here and
@@ -138,6 +139,13 @@ int decode_step(const blk_dcfg* cfg, const void* x,
                 const void* w_qkv, const void* w_o, const void* w_fc, const void* w_proj,
                 void* k_cache, void* v_cache, const int32_t* cache_len, void* y,
                 void* scratch, size_t scratch_bytes, void* stream);
+
+/* The quantiser of the fp8 mode as a standalone call: amax = max |x| over
+ * the n bf16 values at x (n a multiple of 8), written as float bits to the
+ * device word *amax, and codes[i] = E4M3(x[i] * 448/amax) rounded to nearest
+ * even, saturating at +-448 (amax == 0 gives scale 1).  x and codes are
+ * device pointers, 16-byte aligned; codes holds n bytes. */
+int block_fp8_quantize(const void* x, size_t n, void* codes, uint32_t* amax, void* stream);
 
 /* Measurement hooks (for benchmarks; not needed to compute anything).
  * block_timing_enable(1) starts recording, for every kernel launch site of

@@ -14,7 +14,9 @@ with ties to an even code, saturating at +-448.
 
 Quantisation decisions are taken in float32, as the kernels take them:
 inv = fp32(448) / fp32(amax); scaled = fp32(fp32(x) * inv); code =
-nearest-even E4M3 of scaled.
+nearest-even E4M3 of scaled.  In the block, the quantiser's input is the
+tensor as the bf16 pipeline holds it: round_bf16 gives that rounding
+(float32, then nearest-even to 8 significant bits).
 """
 from __future__ import annotations
 
@@ -62,24 +64,40 @@ def e4m3_encode(x: np.ndarray) -> np.ndarray:
     return (code | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
 
 
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Nearest bfloat16 (1 sign, 8 exponent, 7 stored mantissa bits) of each
+    value, ties to even, via float32; returned as float64."""
+    b = np.ascontiguousarray(np.asarray(x, dtype=np.float32)).view(np.uint32).astype(np.uint64)
+    b = (b + 0x7FFF + ((b >> 16) & 1)) & 0xFFFF0000
+    return b.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
 def e4m3_values(codes: np.ndarray) -> np.ndarray:
     return e4m3_table()[np.asarray(codes, dtype=np.int64)]
 
 
-def quantize_tensor(x: np.ndarray):
+def quantize_tensor(x: np.ndarray, amax=None):
     """Per-tensor current scaling: returns (codes uint8, scale float32) with
-    x ~= value(codes) * scale.  Decisions in float32 as stated above."""
+    x ~= value(codes) * scale.  Decisions in float32 as stated above.
+
+    amax: the tensor's absolute maximum when x is only part of the tensor
+    the scale belongs to (default: max |x|).  amax = 0 gives inv = s = 1, and
+    the values (all zeros, of either sign) go through the same rounding, so
+    -0 keeps its sign code 0x80."""
     x32 = np.asarray(x, dtype=np.float32)
-    amax = np.float32(np.max(np.abs(x32))) if x32.size else np.float32(0)
-    if amax == 0:
-        return np.zeros(x32.shape, dtype=np.uint8), np.float32(1.0)
-    inv = np.float32(E4M3_MAX) / amax
+    if amax is None:
+        amax = np.max(np.abs(x32)) if x32.size else 0.0
+    amax = np.float32(amax)
+    if amax > 0:
+        inv = np.float32(E4M3_MAX) / amax
+        scale = np.float32(amax / np.float32(E4M3_MAX))
+    else:
+        inv = scale = np.float32(1.0)
     scaled = (x32 * inv).astype(np.float32)
-    scale = (amax / np.float32(E4M3_MAX)).astype(np.float32)
     return e4m3_encode(scaled.astype(np.float64)), scale
 
 
-def fake_quant(x: np.ndarray) -> np.ndarray:
+def fake_quant(x: np.ndarray, amax=None) -> np.ndarray:
     """Round trip through the quantiser, as float64."""
-    codes, s = quantize_tensor(x)
+    codes, s = quantize_tensor(x, amax)
     return e4m3_values(codes) * np.float64(s)

@@ -1,0 +1,102 @@
+"""GPU checks of the fp8 (E4M3) mode of the linear layers.
+
+- the quantiser (block_fp8_quantize) matches the oracle's codes bit for bit
+  and its amax exactly (byte results: bit-exact bar);
+- the block with fp8 GEMMs matches the float64 oracle of the fp8 block (the
+  same GEMM operands rounded to E4M3, code choices taken on bf16 values as
+  the kernels take them, everything else exact) within 6e-2 relative
+  Frobenius error per output, on ragged and full-size shapes;
+- the GPU's distance from the UNQUANTISED block is no larger than the fp8
+  oracle's own (the recipe's rounding error, 0.05-0.10 for the weight
+  gradients here), within 15%: the kernels add no error of their own.
+
+Exception, at the d26 width only: dW_qkv and dW_o sit at the end of a chain
+of eight quantisations, where a difference of one bf16 rounding upstream
+moves a growing share of later E4M3 codes to the neighbouring code.  Two
+exact emulations that differ only in the precision of their code decisions
+(float64 against bf16) already differ there by 6.1% and 5.5% relative (one
+sequence of 1024 tokens at width 1664), so
+the fp8 result is not defined to 6e-2 at those two outputs: they are held to
+0.10 against the fp8 oracle, beside the accuracy check above."""
+import numpy as np
+import pytest
+
+from blockinputs import WORKLOADS, BlockShape, make_block_inputs, round_to
+
+from gpu_util import TOL, GpuBlock, compare, note, oracle_step, rel_err, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def test_quantizer_bit_exact():
+    import torch
+    import backward_gpt_block_amd as bl
+    from oracle import fp8
+    rng = np.random.default_rng(21)
+    for scale, n in ((1.0, 1 << 20), (1e-3, 4096), (300.0, 65536), (0.0, 1024)):
+        note(f"fp8 quantizer scale={scale} n={n}")
+        x = round_to(rng.standard_normal(n) * scale, "bf16")
+        if scale == 1.0:
+            x[:8] = [0.0, -0.0, 1e-30, -1e-30, 2.0 ** -20, 448.0, -448.0, 3.0]
+            x = round_to(x, "bf16")
+        xd = to_dev(x, "bf16")
+        codes = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+        amax = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+        bl.block_fp8_quantize(xd, n, codes, amax)
+        torch.cuda.synchronize()
+        want, s = fp8.quantize_tensor(x)
+        got = codes.cpu().numpy()
+        amax_got = np.array([amax.cpu().item()], dtype=np.int32).view(np.float32)[0]
+        assert amax_got == np.float32(np.max(np.abs(x))), (amax_got, np.max(np.abs(x)))
+        bad = np.nonzero(got != want)[0]
+        assert bad.size == 0, f"{bad.size} codes differ, e.g. x={x[bad[:5]]} got={got[bad[:5]]} want={want[bad[:5]]}"
+
+
+ACCURACY_RATIO = 1.15
+DEEP_TOL = 0.10
+
+
+def _fp8_parity(sh: BlockShape, seed=0, keep=None, deep=()):
+    from oracle import fp8_block
+    note(f"fp8 block B={sh.B} T={sh.T} C={sh.C} keep={keep} seed={seed}")
+    inp = make_block_inputs(sh, seed=seed)
+    if keep is not None:
+        mask = np.zeros(sh.B, dtype=bool)
+        mask[list(keep)] = True
+        inp["dy"] = np.where(mask[:, None, None], inp["dy"], 0.0)
+    g = GpuBlock(sh, inp)
+    g.fwd()
+    g.bwd()
+    res = g.results()
+    del g
+    if keep is not None:
+        res["y"], res["dx"] = res["y"][list(keep)], res["dx"][list(keep)]
+    emu = fp8_block.block_fwd_bwd(inp["x"], inp["w_qkv"], inp["w_o"], inp["w_fc"], inp["w_proj"], inp["dy"],
+                                  H=sh.H, eps=sh.eps, rope_base=sh.rope_base,
+                                  batch=None if keep is None else list(keep), log=note)
+    keys = [k for k in emu if k not in deep]
+    errs = compare(res, emu, TOL["fp8"], keys=keys)
+    for k in deep:
+        errs[k] = rel_err(res[k], emu[k])
+        print(f"  {k} vs fp8 oracle {errs[k]:.2e} (held to {DEEP_TOL})", flush=True)
+        assert errs[k] <= DEEP_TOL, (k, errs[k])
+    ref = oracle_step(sh, inp, batch=None if keep is None else list(keep))
+    gpu_acc = {k: rel_err(res[k], ref[k]) for k in ref}
+    emu_acc = {k: rel_err(emu[k], ref[k]) for k in ref}
+    print("  distance from the unquantised block, GPU / fp8 oracle: "
+          + ", ".join(f"{k}={gpu_acc[k]:.2e}/{emu_acc[k]:.2e}" for k in ref), flush=True)
+    for k in ref:
+        assert gpu_acc[k] <= ACCURACY_RATIO * emu_acc[k] + 1e-3, (k, gpu_acc[k], emu_acc[k])
+    return errs
+
+
+@pytest.mark.parametrize("B,T,C", [(2, 256, 256), (1, 77, 384), (3, 130, 256)])
+def test_fp8_block_ragged(B, T, C):
+    _fp8_parity(BlockShape(B=B, T=T, C=C, H=C // 128, F=4 * C, dtype="bf16", gemm="fp8"))
+
+
+@pytest.mark.timeout(900)
+def test_d26_fp8_full_size_sampled():
+    # the oracle's forward pass over all 16 sequences (for the per-tensor
+    # scales) takes a minute or two of host time
+    _fp8_parity(WORKLOADS["d26_fp8"], keep=(0, 15), deep=("dw_qkv", "dw_o"))

@@ -48,6 +48,19 @@ def test_in_range_rounding_matches_torch_cast():
     assert np.array_equal(ours, theirs)
 
 
+def test_round_bf16_ties_and_torch_cast():
+    torch = pytest.importorskip("torch")
+    # ties go to the even 8-bit significand; the sign and zero are kept
+    assert fp8.round_bf16(np.array([1 + 2.0 ** -8]))[0] == 1.0
+    assert fp8.round_bf16(np.array([1 + 3 * 2.0 ** -8]))[0] == 1 + 2.0 ** -6
+    assert fp8.round_bf16(np.array([-(1 + 2.0 ** -8 + 2.0 ** -20)]))[0] == -(1 + 2.0 ** -7)
+    assert np.signbit(fp8.round_bf16(np.array([-0.0]))[0])
+    rng = np.random.default_rng(2)
+    x = (rng.standard_normal(50000) * np.exp(rng.uniform(-20, 20, 50000))).astype(np.float32)
+    want = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(fp8.round_bf16(x), want)
+
+
 def test_quantize_tensor_scale_and_error_bound():
     rng = np.random.default_rng(1)
     x = rng.standard_normal(4096) * 3
@@ -57,5 +70,84 @@ def test_quantize_tensor_scale_and_error_bound():
     # relative error of a 3-bit-mantissa rounding is at most 2^-4 for normals
     big = np.abs(x) > 2.0 ** -6 * s * 2
     assert np.all(np.abs(deq[big] - x[big]) <= np.abs(x[big]) * 2.0 ** -4 + 1e-12)
-    z, s0 = fp8.quantize_tensor(np.zeros(10))
-    assert s0 == 1.0 and np.all(z == 0)
+    z, s0 = fp8.quantize_tensor(np.array([0.0, -0.0, 0.0]))
+    assert s0 == 1.0 and list(z) == [0x00, 0x80, 0x00]
+    # a given amax overrides the slice's own maximum
+    c2, s2 = fp8.quantize_tensor(np.array([1.0, -2.0]), amax=448.0)
+    assert s2 == 1.0 and list(fp8.e4m3_values(c2)) == [1.0, -2.0]
+
+
+def _small_block(seed, B=2, T=9, C=256):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((B, T, C))
+    W = [rng.standard_normal(s) * 0.05 for s in ((3 * C, C), (C, C), (4 * C, C), (C, 4 * C))]
+    dy = rng.standard_normal((B, T, C))
+    return x, W, dy
+
+
+def _exact(x, W, dy, H):
+    from oracle import block as ob
+    c = ob.block_fwd(x, *W, H=H)
+    ref = ob.block_bwd(dy, c, *W, H=H)
+    ref["y"] = c.y
+    return ref
+
+
+def test_fp8_block_without_rounding_is_the_exact_block():
+    # with the operand rounding replaced by the identity, the fp8 oracle must
+    # be the unquantised block (pinned by finite differences and autograd)
+    from oracle import fp8_block
+    x, W, dy = _small_block(3)
+    ident = lambda t, amax=None: np.asarray(t, dtype=np.float64)
+    got = fp8_block.block_fwd_bwd(x, *W, dy, H=2, quant=ident)
+    ref = _exact(x, W, dy, 2)
+    for k in ref:
+        assert np.allclose(got[k], ref[k], rtol=1e-12, atol=1e-12), k
+
+
+def test_fp8_block_rounds_every_gemm_operand():
+    # counts the roundings: 4 weights, 4 forward activations, 4 backward
+    # gradients; each a distinct tensor of the expected shape
+    from oracle import fp8_block
+    x, W, dy = _small_block(4, B=1, T=5)
+    seen = []
+
+    def rec(t, amax=None):
+        seen.append(np.shape(t))
+        return np.asarray(t, dtype=np.float64)
+
+    fp8_block.block_fwd_bwd(x, *W, dy, H=2, quant=rec)
+    C = x.shape[-1]
+    act = (1, 5, C)
+    assert sorted(seen) == sorted([(3 * C, C), (C, C), (4 * C, C), (C, 4 * C),
+                                   act, act, act, (1, 5, 4 * C),            # h1, o, h2, a
+                                   act, (1, 5, 4 * C), act, (1, 5, 3 * C)])  # dy, du, dy1, dqkv
+
+
+def test_fp8_emulating_block_tracks_exact_block():
+    # quantising the GEMM operands perturbs each output by a few percent at
+    # most (3-bit mantissas, per-tensor scales), and by a visible amount
+    from oracle import fp8_block
+    x, W, dy = _small_block(3)
+    emu = fp8_block.block_fwd_bwd(x, *W, dy, H=2)
+    ref = _exact(x, W, dy, 2)
+    for k in emu:
+        err = np.linalg.norm(emu[k] - ref[k]) / np.linalg.norm(ref[k])
+        assert 1e-4 < err < 0.1, (k, err)
+
+
+def test_fp8_block_selected_sequences_match_whole_batch():
+    # with dy zero outside the selection, the selection's outputs and the
+    # weight gradients equal those of the whole batch: the forward scales come
+    # from the whole batch, the backward tensors vanish outside the selection
+    from oracle import fp8_block
+    x, W, dy = _small_block(5, B=3, T=7)
+    dy[1] = 0.0
+    whole = fp8_block.block_fwd_bwd(x, *W, dy, H=2)
+    sub = fp8_block.block_fwd_bwd(x, *W, dy, H=2, batch=[0, 2])
+    for k in ("y", "dx"):
+        assert np.allclose(sub[k], whole[k][[0, 2]], rtol=0, atol=1e-12), k
+    for k in ("dw_qkv", "dw_o", "dw_fc", "dw_proj"):
+        assert np.allclose(sub[k], whole[k], rtol=1e-12, atol=1e-12), k
+    with pytest.raises(ValueError):
+        fp8_block.block_fwd_bwd(x, *W, dy, H=2, batch=[0])
