@@ -12,6 +12,7 @@
 
 #include "../../include/blk.h"
 #include "attention.cuh"
+#include "decode.cuh"
 #include "elementwise.cuh"
 #include "fp8.cuh"
 #include "gemm.cuh"
@@ -658,6 +659,73 @@ int bwd_fp8(const blk_cfg& c, const bf16* dy, const bf16* wqkv, const bf16* wo, 
   return launch_status();
 }
 
+// ---------------------------------------------------------------- decode
+int check_dcfg(const blk_dcfg* c) {
+  if (!c) return BLK_EINVAL;
+  if (c->B < 1 || c->H < 1 || c->D != 128 || c->C != c->H * c->D || c->F != 4 * c->C || c->S_max < 1)
+    return BLK_EINVAL;
+  if (!(c->eps >= 0.f) || !(c->rope_base > 0.f)) return BLK_EINVAL;
+  if (c->dtype != BLK_F32 && c->dtype != BLK_BF16) return BLK_EINVAL;
+  if (c->dtype != BLK_BF16) return BLK_EUNSUPPORTED;   // the decode kernels are bf16 only
+  if (c->C > 2048 || c->B > 65535) return BLK_EUNSUPPORTED;
+  if ((long)c->B * c->H * c->S_max * 128 >= (1L << 40)) return BLK_EUNSUPPORTED;
+  return BLK_OK;
+}
+
+struct DecSplit { int S, cps; };
+
+// K-splits of a skinny GEMM: enough workgroups for about one per CU, at
+// least 4 K-steps (one per wave) per split.
+DecSplit dec_split(int M, int N, int K) {
+  const int tiles = (N / dec::NBLK) * ((M + dec::MBLK - 1) / dec::MBLK);
+  const int ks = K / dec::KCH;
+  int S = (256 + tiles - 1) / tiles;
+  S = std::max(1, std::min(S, std::max(1, ks / 4)));
+  const int cps = (ks + S - 1) / S;
+  return {(ks + cps - 1) / cps, cps};
+}
+
+struct DecScratch {
+  bf16* h1;       // [B, C]
+  float* part;    // [S][B][N], the largest of the four GEMMs
+  float* q;       // [B, H, 128]
+  float* opart;   // [B, H, NS, 128]
+  float2* ml;     // [B, H, NS]
+  bf16* o;        // [B, C]
+  float* y1;      // [B, C]
+  bf16* h2;       // [B, C]
+  bf16* a;        // [B, F]
+  size_t bytes;
+};
+
+DecScratch carve_dec(const blk_dcfg& c, void* p) {
+  const long B = c.B, C = c.C, F = c.F, H = c.H;
+  const long NS = (c.S_max + dec::KEYS - 1) / dec::KEYS;
+  long part = 0;
+  const long nk[4][2] = {{3 * C, C}, {C, C}, {F, C}, {C, F}};   // (N, K) of the four GEMMs
+  for (const auto& g : nk) part = std::max(part, (long)dec_split((int)B, (int)g[0], (int)g[1]).S * B * g[0]);
+  Carver k(p);
+  DecScratch d;
+  d.h1 = k.take<bf16>(B * C);
+  d.part = k.take<float>(part);
+  d.q = k.take<float>(B * H * 128);
+  d.opart = k.take<float>(B * H * NS * 128);
+  d.ml = k.take<float2>(B * H * NS);
+  d.o = k.take<bf16>(B * C);
+  d.y1 = k.take<float>(B * C);
+  d.h2 = k.take<bf16>(B * C);
+  d.a = k.take<bf16>(B * F);
+  d.bytes = (k.off + 255) & ~size_t(255);
+  return d;
+}
+
+void dec_gemm(const char* name, const bf16* A, int M, const bf16* W, int N, int K, DecSplit sp, float* part,
+              hipStream_t st) {
+  Timed t(name, st);
+  hipLaunchKernelGGL(dec::skinny_gemm_kernel, dim3(N / dec::NBLK, sp.S, (M + dec::MBLK - 1) / dec::MBLK), dim3(256),
+                     0, st, A, M, W, N, K, sp.cps, part);
+}
+
 size_t saved_bytes(const blk_cfg& c) {
   return c.dtype == BLK_BF16 ? carve_saved<bf16>(c, nullptr).bytes : carve_saved<float>(c, nullptr).bytes;
 }
@@ -754,16 +822,78 @@ int block_bwd(const blk_cfg* cfg, const void* dy, const void* x, const void* w_q
 }
 
 size_t decode_scratch_bytes(const blk_dcfg* cfg) {
-  (void)cfg;
-  return 0;
+  if (check_dcfg(cfg) != BLK_OK) return 0;
+  return carve_dec(*cfg, nullptr).bytes;
 }
 
 int decode_step(const blk_dcfg* cfg, const void* x, const void* w_qkv, const void* w_o, const void* w_fc,
                 const void* w_proj, void* k_cache, void* v_cache, const int32_t* cache_len, void* y, void* scratch,
                 size_t scratch_bytes, void* stream) {
-  (void)cfg; (void)x; (void)w_qkv; (void)w_o; (void)w_fc; (void)w_proj; (void)k_cache; (void)v_cache;
-  (void)cache_len; (void)y; (void)scratch; (void)scratch_bytes; (void)stream;
-  return BLK_EUNSUPPORTED;
+  if (int e = check_dcfg(cfg)) return e;
+  const blk_dcfg& c = *cfg;
+  for (const void* p : {x, w_qkv, w_o, w_fc, w_proj, (const void*)k_cache, (const void*)v_cache, (const void*)y,
+                        (const void*)scratch})
+    if (!p) return BLK_EINVAL;
+  if (!cache_len || k_cache == v_cache) return BLK_EINVAL;
+  for (const void* p : {x, w_qkv, w_o, w_fc, w_proj, (const void*)k_cache, (const void*)v_cache, (const void*)y,
+                        (const void*)scratch})
+    if (!aligned(p)) return BLK_EALIGN;
+  if (reinterpret_cast<uintptr_t>(cache_len) & 3) return BLK_EALIGN;
+  const DecScratch d = carve_dec(c, scratch);
+  if (scratch_bytes < d.bytes) return BLK_ENOSPC;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipGetLastError();
+  const int B = c.B, C = c.C, H = c.H, F = c.F;
+  const bf16* xb = static_cast<const bf16*>(x);
+  bf16* kc = static_cast<bf16*>(k_cache);
+  bf16* vc = static_cast<bf16*>(v_cache);
+  const int NS = (c.S_max + dec::KEYS - 1) / dec::KEYS;
+  {  // h1 = rmsnorm(x)
+    Timed t("dec_rmsnorm", st);
+    hipLaunchKernelGGL(dec::dec_rmsnorm_kernel, dim3(B), dim3(256), 0, st, xb, C, c.eps, d.h1);
+  }
+  const DecSplit sq = dec_split(B, 3 * C, C);
+  dec_gemm("dec_gemm_qkv", d.h1, B, static_cast<const bf16*>(w_qkv), 3 * C, C, sq, d.part, st);
+  {  // rotary + QK-norm at position cache_len[b]; k, v into the caches
+    Timed t("dec_qkv_epi", st);
+    hipLaunchKernelGGL(dec::dec_qkv_epi_kernel, dim3(H, B), dim3(192), 0, st, (const float*)d.part, sq.S, B, H,
+                       cache_len, c.S_max, c.eps, (double)c.rope_base, d.q, kc, vc);
+  }
+  {  // attention of the new token over slots 0..cache_len[b]
+    Timed t("dec_attn", st);
+    hipLaunchKernelGGL(dec::dec_attn_kernel, dim3(NS, H, B), dim3(256), 0, st, (const float*)d.q,
+                       (const bf16*)kc, (const bf16*)vc, cache_len, H, c.S_max, NS,
+                       (float)(1.4426950408889634 / std::sqrt(128.0)), d.opart, d.ml);
+  }
+  {
+    Timed t("dec_combine", st);
+    hipLaunchKernelGGL(dec::dec_combine_kernel, dim3(H, B), dim3(128), 0, st, (const float*)d.opart,
+                       (const float2*)d.ml, cache_len, H, c.S_max, NS, d.o);
+  }
+  const DecSplit so = dec_split(B, C, C);
+  dec_gemm("dec_gemm_o", d.o, B, static_cast<const bf16*>(w_o), C, C, so, d.part, st);
+  {  // y1 = x + o W_o^T; h2 = rmsnorm(y1)
+    Timed t("dec_resid_norm", st);
+    hipLaunchKernelGGL(dec::dec_resid_norm_kernel, dim3(B), dim3(256), 0, st, (const float*)d.part, so.S, B, C, xb,
+                       c.eps, d.y1, d.h2);
+  }
+  const DecSplit sf = dec_split(B, F, C);
+  dec_gemm("dec_gemm_fc", d.h2, B, static_cast<const bf16*>(w_fc), F, C, sf, d.part, st);
+  {
+    Timed t("dec_relu2", st);
+    const long n = (long)B * F;
+    hipLaunchKernelGGL(dec::dec_relu2_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                       (const float*)d.part, sf.S, n, d.a);
+  }
+  const DecSplit sp = dec_split(B, C, F);
+  dec_gemm("dec_gemm_proj", d.a, B, static_cast<const bf16*>(w_proj), C, F, sp, d.part, st);
+  {
+    Timed t("dec_out", st);
+    const long n = (long)B * C;
+    hipLaunchKernelGGL(dec::dec_out_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                       (const float*)d.part, sp.S, n, (const float*)d.y1, static_cast<bf16*>(y));
+  }
+  return launch_status();
 }
 
 int block_fp8_quantize(const void* x, size_t n, void* codes, uint32_t* amax, void* stream) {

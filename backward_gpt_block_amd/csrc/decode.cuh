@@ -1,0 +1,349 @@
+// KV-cache decode step of the block: one new token per sequence attends to
+// its cached keys and values.  Inference with a KV cache (prefill, then one
+// token per step) is named on the 7minutos.es page, section on midtraining,
+// SFT and tool use, and in the launch thread on the same subject.
+//
+// The step reads every weight once (12 C^2 values) and each sequence's cache
+// (2 x H x L x 128 values): it is bound by HBM bandwidth, not by MFMA.
+//
+//   dec_rmsnorm_kernel     h1 = rmsnorm(x)                          [B, C]
+//   skinny_gemm_kernel     part[s] = A W^T over K-split s           (x4)
+//   dec_qkv_epi_kernel     rotary + QK-norm of q, k; k, v into slot p
+//   dec_attn_kernel        per 256-key split: max, sum, sum p v
+//   dec_combine_kernel     merge the splits -> o                    [B, C]
+//   dec_resid_norm_kernel  y1 = x + o W_o^T; h2 = rmsnorm(y1)
+//   dec_relu2_kernel       a = relu(h2 W_fc^T)^2
+//   dec_out_kernel         y = y1 + a W_proj^T
+#pragma once
+#include "common.cuh"
+
+namespace blk {
+namespace dec {
+
+constexpr int KEYS = 256;        // keys per attention workgroup (4 waves x 64)
+constexpr int NBLK = 32;         // output columns per skinny-GEMM workgroup
+constexpr int MBLK = 64;         // rows per skinny-GEMM workgroup
+constexpr int KCH = 64;          // K elements per skinny-GEMM step (4 MFMAs)
+
+__device__ __forceinline__ float block_sum256(float v, float* sh) {
+  v = wave_sum(v);
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+  __syncthreads();
+  v = sh[0] + sh[1] + sh[2] + sh[3];
+  __syncthreads();
+  return v;
+}
+
+// h[b, :] = bf16(x[b, :] / rms(x[b, :])), C % 8 == 0, C <= 256 * 8 * 4.
+__global__ __launch_bounds__(256) void dec_rmsnorm_kernel(const bf16* __restrict__ x, int C, float eps,
+                                                          bf16* __restrict__ h) {
+  __shared__ float sh[4];
+  const long row = blockIdx.x;
+  const int nch = C / 8;
+  float f[4][8];
+  float ss = 0.f;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int ch = threadIdx.x + 256 * u;
+    if (ch < nch) {
+      Chunk<bf16>::unpack(ld16(x + row * C + ch * 8), f[u]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += f[u][e] * f[u][e];
+    }
+  }
+  const float r = 1.f / sqrtf(block_sum256(ss, sh) / (float)C + eps);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int ch = threadIdx.x + 256 * u;
+    if (ch < nch) {
+      float g[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) g[e] = f[u][e] * r;
+      st16(h + row * C + ch * 8, Chunk<bf16>::pack(g));
+    }
+  }
+}
+
+// Skinny GEMM for a few rows: part[s][m][n] = sum over K-split s of
+// A[m, k] W[n, k], fp32.  A [M, K] and W [N, K] row-major bf16; N % 32 == 0,
+// K % 64 == 0.  Grid (N/32, S, ceil(M/64)); 4 waves share the workgroup's
+// 64 x 32 tile and take its K-steps in turn, then add up through LDS.
+//
+// Within a 64-wide K-step, lane l (column/row l%32, half g = l/32) loads 32
+// consecutive elements k0 + 32g .. k0 + 32g + 31 of its W row and of its A
+// rows, and MFMA e (of 4) takes elements 8e..8e+7 of them: the contraction
+// is over a permutation of the step's 64 k that both operands share.
+__global__ __launch_bounds__(256) void skinny_gemm_kernel(const bf16* __restrict__ A, int M,
+                                                          const bf16* __restrict__ W, int N, int K, int cps,
+                                                          float* __restrict__ part) {
+  __shared__ float red[4][MBLK * NBLK];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int n0 = blockIdx.x * NBLK, s = blockIdx.y, m0 = blockIdx.z * MBLK;
+  const int ksteps = K / KCH;
+  const int c0 = s * cps, c1 = min(ksteps, c0 + cps);
+  const int l32 = lane & 31, g = lane >> 5;
+  const bf16* wrow = W + (long)(n0 + l32) * K + 32 * g;
+  const int ra = m0 + l32, rb = m0 + 32 + l32;
+  const bool oka = ra < M, okb = rb < M;
+  const bf16* arow = A + (long)(oka ? ra : 0) * K + 32 * g;
+  const bf16* brow = A + (long)(okb ? rb : 0) * K + 32 * g;
+  f32x16 acc0 = {}, acc1 = {};
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  for (int c = c0 + wv; c < c1; c += 4) {
+    const long k0 = (long)c * KCH;
+    u32x4 wb[4], xa[4], xb[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      wb[e] = ld16(wrow + k0 + 8 * e);
+      xa[e] = oka ? ld16(arow + k0 + 8 * e) : zero;
+      xb[e] = okb ? ld16(brow + k0 + 8 * e) : zero;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bf16x8 w8 = __builtin_bit_cast(bf16x8, wb[e]);
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xa[e]), w8, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xb[e]), w8, acc1, 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int r = acc_row(j, lane);
+    red[wv][r * NBLK + l32] = acc0[j];
+    red[wv][(r + 32) * NBLK + l32] = acc1[j];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < MBLK * NBLK / 256; ++i) {
+    const int e = threadIdx.x + 256 * i;
+    const int r = e / NBLK, col = e % NBLK;
+    if (m0 + r < M)
+      part[((long)s * M + m0 + r) * N + n0 + col] = red[0][e] + red[1][e] + red[2][e] + red[3][e];
+  }
+}
+
+__device__ __forceinline__ float sum_parts(const float* __restrict__ part, int S, long stride, long idx) {
+  float v = 0.f;
+  for (int s = 0; s < S; ++s) v += part[s * stride + idx];
+  return v;
+}
+
+__device__ __forceinline__ int clamp_pos(const int* __restrict__ cache_len, int b, int S_max) {
+  return min(max(cache_len[b], 0), S_max - 1);
+}
+
+// From the QKV partials of row b: q and k rotated by the angle of position
+// p = cache_len[b] and RMS-normalised per head (QK-norm); q (float32) into
+// qbuf[b, h, :], k and v (bf16) into slot p of the caches.  Grid (H, B),
+// 3 waves: q, k, v of head h; lane i owns the pair (i, i + 64).
+__global__ __launch_bounds__(192) void dec_qkv_epi_kernel(const float* __restrict__ part, int S, int B, int H,
+                                                          const int* __restrict__ cache_len, int S_max, float eps,
+                                                          double rope_base, float* __restrict__ qbuf,
+                                                          bf16* __restrict__ kc, bf16* __restrict__ vc) {
+  const int h = blockIdx.x, b = blockIdx.y, which = threadIdx.x >> 6, i = threadIdx.x & 63;
+  const int C = H * 128;
+  const long stride = (long)B * 3 * C;
+  const long base = (long)b * 3 * C + which * C + h * 128;
+  float z1 = sum_parts(part, S, stride, base + i), z2 = sum_parts(part, S, stride, base + i + 64);
+  const int p = clamp_pos(cache_len, b, S_max);
+  const long slot = ((long)(b * H + h) * S_max + p) * 128;
+  if (which == 2) {
+    vc[slot + i] = (bf16)z1;
+    vc[slot + i + 64] = (bf16)z2;
+    return;
+  }
+  double sn, cs;
+  sincos((double)p * pow(rope_base, -2.0 * i / 128.0), &sn, &cs);
+  const float c = (float)cs, s = (float)sn;
+  const float y1 = z1 * c - z2 * s, y2 = z1 * s + z2 * c;
+  const float r = 1.f / sqrtf(wave_sum(y1 * y1 + y2 * y2) / 128.f + eps);
+  if (which == 0) {
+    float* q = qbuf + (long)(b * H + h) * 128;
+    q[i] = y1 * r;
+    q[i + 64] = y2 * r;
+  } else {
+    kc[slot + i] = (bf16)(y1 * r);
+    kc[slot + i + 64] = (bf16)(y2 * r);
+  }
+}
+
+// One split of KEYS keys of one (sequence, head): keys j in
+// [s*KEYS, min((s+1)*KEYS, L)), L = cache_len[b] + 1.  Writes the split's
+// running maximum m (log2 units), sum l = sum 2^(t_j - m) and unnormalised
+// output sum 2^(t_j - m) v_j, t_j = log2(e) q.k_j / sqrt(128).
+// Grid (NS, H, B), 4 waves of 64 keys.  Lane (g = lane/16, r = lane%16)
+// holds dims 8r..8r+7 of keys base + 4i + g, i = 0..15.
+__global__ __launch_bounds__(256) void dec_attn_kernel(const float* __restrict__ qbuf, const bf16* __restrict__ kc,
+                                                       const bf16* __restrict__ vc, const int* __restrict__ cache_len,
+                                                       int H, int S_max, int NS, float sl2,
+                                                       float* __restrict__ opart, float2* __restrict__ ml) {
+  __shared__ float wo[4][128];
+  __shared__ float wm[4], wl[4];
+  const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int L = clamp_pos(cache_len, b, S_max) + 1;
+  if (s * KEYS >= L) return;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int g = lane >> 4, r = lane & 15;
+  const int kb = s * KEYS + wv * 64;
+  const long head = (long)(b * H + h);
+  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, l = 0.f;
+  if (kb < L) {
+    float q[8];
+    {
+      const float* qp = qbuf + head * 128 + r * 8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) q[e] = qp[e] * sl2;
+    }
+    const bf16* kp = kc + head * S_max * 128 + r * 8;
+    const bf16* vp = vc + head * S_max * 128 + r * 8;
+    u32x4 kr[16], vr[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const long j = min(kb + 4 * i + g, L - 1);   // past the end: a valid key, masked below
+      kr[i] = ld16(kp + j * 128);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const long j = min(kb + 4 * i + g, L - 1);
+      vr[i] = ld16(vp + j * 128);
+    }
+    // partial dot products over this lane's 8 dims, then a transposing
+    // butterfly over the 16 lanes of the key group: after the steps with
+    // masks 8, 4, 2, 1 lane r holds the full score of key base + 4r + g
+    float t[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float f[8];
+      Chunk<bf16>::unpack(kr[i], f);
+      float a = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a += q[e] * f[e];
+      t[i] = a;
+    }
+#pragma unroll
+    for (int half = 8; half >= 1; half >>= 1) {
+      const bool up = (r & half) != 0;
+#pragma unroll
+      for (int i = 0; i < half; ++i) {
+        const float send = up ? t[i] : t[i + half];
+        const float keep = up ? t[i + half] : t[i];
+        t[i] = keep + __shfl_xor(send, half, 64);
+      }
+    }
+    const bool valid = kb + 4 * r + g < L;
+    const float sc = valid ? t[0] : -INFINITY;
+    m = wave_max(sc);
+    const float p = valid ? __builtin_amdgcn_exp2f(sc - m) : 0.f;
+    l = wave_sum(p);
+    float pk[16];   // p of the keys this lane multiplies: held by lanes 16g + i
+#pragma unroll
+    for (int i = 0; i < 16; ++i) pk[i] = __shfl(p, 16 * g + i, 64);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float f[8];
+      Chunk<bf16>::unpack(vr[i], f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] += pk[i] * f[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      o[e] += __shfl_xor(o[e], 16, 64);
+      o[e] += __shfl_xor(o[e], 32, 64);
+    }
+  }
+  if (lane < 16) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) wo[wv][lane * 8 + e] = o[e];
+  }
+  if (lane == 0) {
+    wm[wv] = m;
+    wl[wv] = l;
+  }
+  __syncthreads();
+  if (threadIdx.x < 128) {
+    const int d = threadIdx.x;
+    const float M = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));   // finite: wave 0 has keys
+    float acc = 0.f, lsum = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float f = wm[w] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(wm[w] - M);
+      acc += f * wo[w][d];
+      lsum += f * wl[w];
+    }
+    const long slot = head * NS + s;
+    opart[slot * 128 + d] = acc;
+    if (d == 0) ml[slot] = make_float2(M, lsum);
+  }
+}
+
+// o[b, h*128 + d] = sum_s 2^(m_s - M) o_s[d] / sum_s 2^(m_s - M) l_s over the
+// splits that hold keys.  Grid (H, B), 128 threads.
+__global__ __launch_bounds__(128) void dec_combine_kernel(const float* __restrict__ opart,
+                                                          const float2* __restrict__ ml,
+                                                          const int* __restrict__ cache_len, int H, int S_max,
+                                                          int NS, bf16* __restrict__ o) {
+  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  const int L = clamp_pos(cache_len, b, S_max) + 1;
+  const int nv = (L + KEYS - 1) / KEYS;
+  const long head = (long)(b * H + h);
+  float M = -INFINITY;
+  for (int s = 0; s < nv; ++s) M = fmaxf(M, ml[head * NS + s].x);
+  float acc = 0.f, lsum = 0.f;
+  for (int s = 0; s < nv; ++s) {
+    const float2 v = ml[head * NS + s];
+    const float f = __builtin_amdgcn_exp2f(v.x - M);
+    acc += f * opart[(head * NS + s) * 128 + d];
+    lsum += f * v.y;
+  }
+  o[(long)b * H * 128 + h * 128 + d] = (bf16)(acc / lsum);
+}
+
+// y1 = x + sum_s part[s] (float32), h2 = bf16(y1 / rms(y1)).  Grid B.
+__global__ __launch_bounds__(256) void dec_resid_norm_kernel(const float* __restrict__ part, int S, int B, int C,
+                                                             const bf16* __restrict__ x, float eps,
+                                                             float* __restrict__ y1, bf16* __restrict__ h2) {
+  __shared__ float sh[4];
+  const long row = blockIdx.x;
+  const long stride = (long)B * C;
+  float v[8];
+  float ss = 0.f;
+  const int per = (C + 255) / 256;   // <= 8
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int c = threadIdx.x + 256 * u;
+    v[u] = 0.f;
+    if (u < per && c < C) {
+      v[u] = (float)x[row * C + c] + sum_parts(part, S, stride, row * C + c);
+      ss += v[u] * v[u];
+    }
+  }
+  const float r = 1.f / sqrtf(block_sum256(ss, sh) / (float)C + eps);
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int c = threadIdx.x + 256 * u;
+    if (u < per && c < C) {
+      y1[row * C + c] = v[u];
+      h2[row * C + c] = (bf16)(v[u] * r);
+    }
+  }
+}
+
+// a = bf16(relu(sum_s part[s])^2) over n values.
+__global__ __launch_bounds__(256) void dec_relu2_kernel(const float* __restrict__ part, int S, long n,
+                                                        bf16* __restrict__ a) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const float u = fmaxf(sum_parts(part, S, n, i), 0.f);
+  a[i] = (bf16)(u * u);
+}
+
+// y = bf16(y1 + sum_s part[s]) over n values.
+__global__ __launch_bounds__(256) void dec_out_kernel(const float* __restrict__ part, int S, long n,
+                                                      const float* __restrict__ y1, bf16* __restrict__ y) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  y[i] = (bf16)(y1[i] + sum_parts(part, S, n, i));
+}
+
+}  // namespace dec
+}  // namespace blk

@@ -11,6 +11,11 @@ Prints ONE JSON line on stdout (details go to stderr):
               same K steps (block_timing_*), against the bf16 dense MFMA peak
   cpu_baseline the float64 CPU oracle on a bounded sample of the workload
               (whole sequences of it), on this host's cores
+
+--workload d20_decode measures the KV-cache decode step instead (64
+sequences, one new token each, caches of 2048 keys; the ragged 128..2048
+variant is reported beside it): decode tokens/s, and the HBM roofline of the
+split-KV attention kernel from the cache bytes it must read.
 """
 from __future__ import annotations
 
@@ -24,6 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "training tokens/sec and TFLOP/s per decoder block (d20, T=2048) on 1 MI355X"
+DECODE_METRIC = "decode tokens/sec per decoder block (d20, batch 64, KV cache 2048) on 1 MI355X"
 PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3, "fp8": 5033.2}
 HBM_PEAK_GBS = 8000.0
 
@@ -100,7 +106,13 @@ def main() -> int:
         print("bench.py runs on exactly one GPU: the block step is measured on one GPU's share "
               "(see the sharding notes); --gpus must be 1", file=sys.stderr)
         return 2
+    from blockinputs import DECODE_WORKLOADS
+    if args.workload in DECODE_WORKLOADS:
+        return bench_decode(args)
+    return bench_train(args)
 
+
+def bench_train(args) -> int:
     import numpy as np
     import torch
 
@@ -194,6 +206,137 @@ def main() -> int:
                    "gemm": sh.gemm, "tokens_per_step": tokens, "parallelism": "none (1 GPU)"},
         "tflops": round(tflops, 2), "frac_of_peak": round(tflops / peak, 4),
         "tflops_nanochat_convention": round(step_flops_nanochat(sh) / (ms * 1e-3) / 1e12, 2),
+        "roofline": roof, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def decode_attn_bytes(sh, lens) -> float:
+    """Algorithmic HBM bytes of one decode attention launch: the keys and
+    values of slots 0..L_b of every (sequence, head), bf16, and the q rows."""
+    import numpy as np
+    kv = 2.0 * sh.H * 128 * 2 * float(np.sum(np.asarray(lens, dtype=np.int64) + 1))
+    return kv + sh.B * sh.H * 128 * 4.0
+
+
+def decode_step_bytes(sh, lens) -> float:
+    """Algorithmic HBM bytes of one decode step: every weight once (bf16),
+    the cache reads, the new slot writes, x in and y out."""
+    C, F = sh.C, sh.F
+    w = 2.0 * (4 * C * C + 2 * C * F)
+    return w + decode_attn_bytes(sh, lens) + sh.B * (2.0 * sh.H * 128 * 2 + 2 * C * 2)
+
+
+def cpu_decode_baseline(sh, inp, lens, budget_s: float) -> dict:
+    """Oracle decode on whole sequences of the workload (a sub-batch with its
+    own caches) until the budget is spent (at least one sequence)."""
+    from oracle import block as ob
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:
+        threads = os.cpu_count() or 1
+    W = (inp["w_qkv"], inp["w_o"], inp["w_fc"], inp["w_proj"])
+    t0 = time.perf_counter()
+    n = 0
+    while n < sh.B:
+        sl = slice(n, n + 1)
+        ob.decode_step(inp["x"][sl], *W, inp["k_cache"][sl], inp["v_cache"][sl], lens[sl], H=sh.H, eps=sh.eps,
+                       rope_base=sh.rope_base)
+        n += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} of {sh.B} sequences (cache length {int(lens[0])}) of the workload, float64 numpy, "
+                      f"{dt:.1f} s", "seconds": dt, "host_cpus": os.cpu_count()}
+
+
+def bench_decode(args) -> int:
+    import numpy as np
+    import torch
+
+    import backward_gpt_block_amd as bl
+    from blockinputs import DECODE_WORKLOADS, make_decode_inputs, ragged_lengths, to_storage
+
+    sh = DECODE_WORKLOADS[args.workload]
+    log(f"workload {args.workload}: {sh}")
+    t0 = time.perf_counter()
+    inp = make_decode_inputs(sh, seed=0, cache_len=sh.S_max - 1)
+    rag = ragged_lengths(sh.B, 128, sh.S_max - 1, seed=0)
+    log(f"inputs generated in {time.perf_counter() - t0:.1f} s")
+
+    def dev(a):
+        return torch.from_numpy(to_storage(a, "bf16").view(np.int16)).view(torch.bfloat16).to("cuda:0")
+
+    x = dev(inp["x"])
+    W = [dev(inp[k]) for k in ("w_qkv", "w_o", "w_fc", "w_proj")]
+    kc, vc = dev(inp["k_cache"]), dev(inp["v_cache"])
+    cfg = bl.DecodeConfig(B=sh.B, C=sh.C, H=sh.H, F=sh.F, S_max=sh.S_max, eps=sh.eps, rope_base=sh.rope_base)
+    y = torch.empty_like(x)
+    scratch = torch.empty(bl.decode_scratch_bytes(cfg), dtype=torch.uint8, device="cuda:0")
+    stream = torch.cuda.current_stream()
+
+    def run(lens_np):
+        lens = torch.from_numpy(np.asarray(lens_np, dtype=np.int32)).to("cuda:0")
+
+        def step():
+            bl.decode_step(cfg, x, *W, kc, vc, lens, y, scratch, stream=stream)
+
+        for _ in range(args.warmup):
+            step()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for _ in range(args.steps):
+            step()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        ms = ev0.elapsed_time(ev1) / args.steps
+        bl.block_timing_enable(True)
+        for _ in range(args.steps):
+            step()
+        sites = bl.block_timing_read()
+        bl.block_timing_enable(False)
+        torch.cuda.synchronize()
+        return ms, sites
+
+    lens_u = inp["cache_len"]
+    ms, sites = run(lens_u)
+    ms_r, sites_r = run(rag)
+    step_b = decode_step_bytes(sh, lens_u)
+    log(f"decode step: {ms * 1e3:.1f} us, {step_b / (ms * 1e-3) / 1e9:.0f} GB/s of algorithmic traffic "
+        f"({step_b / 1e6:.1f} MB); ragged 128..2048: {ms_r * 1e3:.1f} us")
+    total = sum(v[0] for v in sites.values())
+    for k, (tot, cnt) in sorted(sites.items(), key=lambda kv: -kv[1][0]):
+        log(f"  {k:16s} {1e3 * tot / args.steps:8.1f} us/step {tot / total:6.1%}")
+    dname, (dtot, dcnt) = max(sites.items(), key=lambda kv: kv[1][0])
+    davg = dtot / dcnt
+    roof = {"bound": "hbm", "achieved": None, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": None, "traffic": None,
+            "kernel": dname, "avg_launch_ms": round(davg, 5)}
+    if dname == "dec_attn":
+        b = decode_attn_bytes(sh, lens_u)
+        ach = b / (davg * 1e-3) / 1e9
+        roof.update(achieved=round(ach, 1), frac=round(ach / HBM_PEAK_GBS, 4), bytes_per_launch=b)
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        cpu = cpu_decode_baseline(sh, inp, lens_u, args.cpu_budget)
+        log(f"cpu baseline: {cpu}")
+    ra = sites_r.get("dec_attn")
+    out = {
+        "metric": DECODE_METRIC, "value": round(sh.B / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "B": sh.B, "C": sh.C, "H": sh.H, "D": sh.D, "F": sh.F,
+                   "S_max": sh.S_max, "cache_len": int(lens_u[0]), "parallelism": "none (1 GPU)"},
+        "step_gbs": round(step_b / (ms * 1e-3) / 1e9, 1), "step_frac_of_hbm": round(step_b / (ms * 1e-3) / 1e12 / 8.0, 4),
+        "ragged_variant": {"cache_len": "uniform 128..2048", "ms_per_step": round(ms_r, 5),
+                           "value": round(sh.B / (ms_r * 1e-3), 1),
+                           "step_gbs": round(decode_step_bytes(sh, rag) / (ms_r * 1e-3) / 1e9, 1),
+                           "attn_gbs": None if ra is None else
+                           round(decode_attn_bytes(sh, rag) / (ra[0] / ra[1] * 1e-3) / 1e9, 1)},
         "roofline": roof, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

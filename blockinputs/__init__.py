@@ -25,7 +25,7 @@ import numpy as np
 __all__ = [
     "BlockShape", "DecodeShape", "WORKLOADS", "DECODE_WORKLOADS",
     "from_depth", "round_to", "to_storage", "from_storage",
-    "make_block_inputs", "make_decode_inputs",
+    "make_block_inputs", "make_decode_inputs", "ragged_lengths",
 ]
 
 
@@ -161,6 +161,12 @@ def make_block_inputs(shape: BlockShape, seed: int = 0) -> dict[str, np.ndarray]
     return out
 
 
+def ragged_lengths(B: int, lo: int, hi: int, seed: int = 0) -> np.ndarray:
+    """B cache lengths, uniform integers in [lo, hi], from their own stream
+    (default_rng(seed + 1))."""
+    return np.random.default_rng(seed + 1).integers(lo, hi, size=B, endpoint=True).astype(np.int32)
+
+
 def make_decode_inputs(shape: DecodeShape, seed: int = 0, cache_len: int | None = None,
                        ragged: bool = False, ragged_lo: int = 128,
                        ragged_hi: int | None = None) -> dict[str, np.ndarray]:
@@ -185,7 +191,7 @@ def make_decode_inputs(shape: DecodeShape, seed: int = 0, cache_len: int | None 
         out[name] = round_to(v, shape.dtype)
     hi = S - 1 if ragged_hi is None else ragged_hi
     if ragged:
-        lens = rng.integers(ragged_lo, hi, size=B, endpoint=True)
+        lens = ragged_lengths(B, ragged_lo, hi, seed)
     else:
         lens = np.full(B, S - 1 if cache_len is None else cache_len)
     if np.any(lens + 1 > S) or np.any(lens < 0):

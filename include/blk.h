@@ -126,15 +126,25 @@ int block_bwd(const blk_cfg* cfg, const void* dy, const void* x,
 /* Bytes of temporary device memory decode_step needs.  0 for invalid cfg. */
 size_t decode_scratch_bytes(const blk_dcfg* cfg);
 
-/* One decode step: a new token per sequence at position p_b = cache_len[b].
- *   x       [B,C]               new rows (dtype)
- *   k_cache, v_cache [B,H,S_max,D]  (dtype) keys after rotary and QK-norm,
+/* One decode step of the block: a new token per sequence at position
+ * p_b = cache_len[b] attends to the cached keys and values of slots
+ * 0..p_b (its own included).  Inference with a KV cache (prefill, then one
+ * token per step) is named on the 7minutos.es page, section on midtraining,
+ * SFT and tool use, and in the launch thread on the same subject; the block
+ * computed for the new row is the one described at the top of this file.
+ *   x       [B,C]               new rows (bf16)
+ *   k_cache, v_cache [B,H,S_max,D]  (bf16) keys after rotary and QK-norm,
  *           and values; slot p_b of each (b, h) is written here, slots
  *           0..p_b are attended, slots beyond p_b are neither read nor written
  *   cache_len [B] int32 DEVICE array, read only (the caller advances it);
  *           every entry must satisfy 0 <= cache_len[b] <= S_max-1 (entries
  *           outside that range are clamped into it by the kernels)
- *   y       [B,C] output (dtype) */
+ *   y       [B,C] output (bf16); may be the same buffer as x
+ *   scratch at least decode_scratch_bytes(cfg) bytes of device memory
+ * Only cfg->dtype == BLK_BF16 and C <= 2048 are implemented (else
+ * BLK_EUNSUPPORTED).  BLK_EINVAL for a bad cfg, a NULL pointer, or
+ * k_cache == v_cache; BLK_EALIGN for a data pointer not 16-byte aligned or
+ * cache_len not 4-byte aligned; BLK_ENOSPC for a short scratch. */
 int decode_step(const blk_dcfg* cfg, const void* x,
                 const void* w_qkv, const void* w_o, const void* w_fc, const void* w_proj,
                 void* k_cache, void* v_cache, const int32_t* cache_len, void* y,

@@ -106,6 +106,40 @@ def test_bwd_argument_errors(lib):
     assert _bwd(_cfg(H=0, C=0, F=0)) == bl.binding.BLK_EINVAL
 
 
+def _dcfg(**kw):
+    d = dict(B=64, C=1280, H=10, F=5120, S_max=2049)
+    d.update(kw)
+    return bl.DecodeConfig(**d)
+
+
+def _dec(cfg, **kw):
+    args = dict(x=A, w_qkv=A + 0x100, w_o=A + 0x200, w_fc=A + 0x300, w_proj=A + 0x400, k_cache=A + 0x500,
+                v_cache=A + 0x600, cache_len=A + 0x700, y=A + 0x800, scratch=A + 0x900, scratch_bytes=1 << 40)
+    args.update(kw)
+    pos = [args.pop(k) for k in ("x", "w_qkv", "w_o", "w_fc", "w_proj", "k_cache", "v_cache", "cache_len", "y",
+                                 "scratch")]
+    return bl.decode_step(cfg, *pos, raise_on_error=False, stream=0, **args)
+
+
+def test_decode_sizes_and_argument_errors(lib):
+    c = _dcfg()
+    need = bl.decode_scratch_bytes(c)
+    # at least the activations h1, o, h2 (bf16), y1, q (fp32), a (bf16) and the split partials
+    assert need >= 64 * (1280 * (2 * 3 + 4) + 1280 * 4 + 5120 * 2)
+    assert need < 64 << 20
+    for bad in (_dcfg(D=64), _dcfg(C=1000), _dcfg(F=100), _dcfg(B=0), _dcfg(S_max=0), _dcfg(dtype=7)):
+        assert bl.decode_scratch_bytes(bad) == 0
+        assert _dec(bad) == bl.binding.BLK_EINVAL
+    assert _dec(_dcfg(dtype=bl.BLK_F32)) == bl.binding.BLK_EUNSUPPORTED
+    assert _dec(_dcfg(C=4096, H=32, F=16384)) == bl.binding.BLK_EUNSUPPORTED
+    assert _dec(c, x=None) == bl.binding.BLK_EINVAL
+    assert _dec(c, cache_len=None) == bl.binding.BLK_EINVAL
+    assert _dec(c, v_cache=A + 0x500) == bl.binding.BLK_EINVAL      # v_cache aliases k_cache
+    assert _dec(c, w_fc=MIS) == bl.binding.BLK_EALIGN
+    assert _dec(c, cache_len=A + 0x702) == bl.binding.BLK_EALIGN
+    assert _dec(c, scratch_bytes=need - 1) == bl.binding.BLK_ENOSPC
+
+
 def test_strerror(lib):
     for code in range(6):
         assert isinstance(bl.block_strerror(code), str) and bl.block_strerror(code)
