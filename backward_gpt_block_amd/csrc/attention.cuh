@@ -180,13 +180,64 @@ __device__ __forceinline__ void store_acc_row(T* dst, const f32x16* acc, float s
   }
 }
 
+// Stores the gradient of q' or k' (before QK-norm and rotary) of one row:
+// g = acc * scale is the gradient of the normalised row z (this lane holds
+// dims db*32 + 8i + 4h + e, h = lane/32; lane ^ 32 the rest), p its QK-norm
+// factor, cs the row's 64 angles.  QK-norm backward
+// dz' = p (g - z mean(g z)), then the transposed rotation of each pair
+// (d, d + 64).  (Rotary embedding and QK-norm: flicky.cc nanochat page,
+// section on the model.)
+__device__ __forceinline__ void store_acc_row_qk(bf16* dst, const bf16* z, float p, const float2* cs,
+                                                 const f32x16* acc, float scale, int lane) {
+  const int h = lane >> 5;
+  float gv[4][16], zv[4][16];
+  float dot = 0.f;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bf16x4 zz = __builtin_bit_cast(bf16x4, ld8(z + db * 32 + 8 * i + 4 * h));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        gv[db][4 * i + e] = acc[db][4 * i + e] * scale;
+        zv[db][4 * i + e] = (float)zz[e];
+        dot += gv[db][4 * i + e] * zv[db][4 * i + e];
+      }
+    }
+  dot += __shfl_xor(dot, 32, 64);
+  const float mean = dot * (1.f / 128.f);
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float* cp = reinterpret_cast<const float*>(cs + db * 32 + 8 * i + 4 * h);
+      float c8[8];
+      Chunk<float>::unpack(ld16(cp), c8);
+      Chunk<float>::unpack(ld16(cp + 4), c8 + 4);
+      bf16x4 lo, hi;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * i + e;
+        const float d1 = p * (gv[db][r] - zv[db][r] * mean);
+        const float d2 = p * (gv[db + 2][r] - zv[db + 2][r] * mean);
+        const float c = c8[2 * e], sn = c8[2 * e + 1];
+        lo[e] = (bf16)(d1 * c + d2 * sn);
+        hi[e] = (bf16)(d2 * c - d1 * sn);
+      }
+      st8(dst + db * 32 + 8 * i + 4 * h, __builtin_bit_cast(u32x2, lo));
+      st8(dst + (db + 2) * 32 + 8 * i + 4 * h, __builtin_bit_cast(u32x2, hi));
+    }
+}
+
 struct AttnArgs {
   const void* qkv;   // [B*T, 3C]: q'' | k'' | v, heads contiguous in each
   void* o;           // [B*T, C]
   float* lse;        // [B*H, T], log2-domain log-sum-exp of the scaled scores
   const void* dO;    // [B*T, C]
   const float* delta;  // [B*H, T] rowsum(dO * O)
-  void* dqkv;        // [B*T, 3C]: dq'' | dk'' | dv
+  void* dqkv;        // [B*T, 3C]: dq'' | dk'' | dv; bf16 kernels: dq' | dk' | dv
+  const float* rho;    // [2][B*T][H] QK-norm factors (bf16 backward kernels)
+  const float2* cs;    // [T][64] rotary angles (bf16 backward kernels)
   int B, T, H, C;
   float sl2;         // log2(e) / sqrt(D)
   float rsd;         // 1 / sqrt(D)
@@ -850,8 +901,11 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_bf16_kernel(AttnArgs a) 
     }
   }
   if (kv) {
-    bf16* row = static_cast<bf16*>(a.dqkv) + ((long)b * a.T + key) * 3 * a.C + head * HD;
-    store_acc_row<bf16>(row + a.C, dk, a.rsd, lane);
+    const long rowi = (long)b * a.T + key;
+    bf16* row = static_cast<bf16*>(a.dqkv) + rowi * 3 * a.C + head * HD;
+    const bf16* zk = qkv + rowi * 3 * a.C + a.C + head * HD;
+    store_acc_row_qk(row + a.C, zk, a.rho[((long)a.B * a.T + rowi) * a.H + head], a.cs + (long)key * 64, dk, a.rsd,
+                     lane);
     store_acc_row<bf16>(row + 2 * a.C, dv, 1.f, lane);
   }
 }
@@ -937,7 +991,11 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_bf16_kernel(AttnArgs a) {
       for (int db = 0; db < 4; ++db) acc[db] = MM::mma(frag_vt_at(kt_, vo, mm, db), sf, acc[db]);
     }
   }
-  if (qv) store_acc_row<bf16>(static_cast<bf16*>(a.dqkv) + ((long)b * a.T + q) * 3 * a.C + head * HD, acc, a.rsd, lane);
+  if (qv) {
+    const long rowi = (long)b * a.T + q;
+    store_acc_row_qk(static_cast<bf16*>(a.dqkv) + rowi * 3 * a.C + head * HD, qkv + rowi * 3 * a.C + head * HD,
+                     a.rho[rowi * a.H + head], a.cs + (long)q * 64, acc, a.rsd, lane);
+  }
 }
 
 template <typename T> constexpr int attn_fwd_lds() { return 2 * (AttnCfg<T>::ROWT + AttnCfg<T>::TRT); }

@@ -258,6 +258,15 @@ GemmArgs gargs(const void* A, long lda, const void* B, long ldb, int M, int N, i
   return g;
 }
 
+// Epilogue parameters of the QKV projection (rotary + QK-norm) and of the
+// attention-output input gradient (per-head row dot with o).
+void rope_args(GemmArgs& g, const blk_cfg& c, const float2* cs, float* rho) {
+  g.cs = cs; g.rho = rho; g.T = c.T; g.H = c.H; g.C = c.C; g.eps = c.eps;
+}
+void delta_args(GemmArgs& g, const blk_cfg& c, const void* o, float* delta) {
+  g.aux = o; g.ldaux = c.C; g.delta = delta; g.T = c.T; g.H = c.H; g.C = c.C;
+}
+
 // Weight gradient dW[M, N] (+)= sum_t G[t, m] X[t, n]  (G: [K, M], X: [K, N]).
 template <typename T>
 void wgrad(void (*kern)(GemmArgs), void (*kern_acc)(GemmArgs), const char* name, const T* G, const T* X, float* dW,
@@ -306,15 +315,11 @@ int fwd_impl(const blk_cfg& c, const T* x, const T* wqkv, const T* wo, const T* 
     Timed t("rmsnorm_fwd", st);
     hipLaunchKernelGGL(rmsnorm_fwd_kernel<T>, dim3(row_blocks(N)), dim3(256), 0, st, x, s.h1, s.r1, N, C, c.eps);
   }
-  {  // 2 qkv = h1 W_qkv^T
+  {  // 2-4 qkv = h1 W_qkv^T; rotary and QK-norm of q, k in the epilogue
     GemmArgs g = gargs(s.h1, C, wqkv, C, N, 3 * C, C);
     g.out = s.qkv; g.ldo = 3 * C;
+    rope_args(g, c, s.cs, s.rho);
     gemm<T>(gemm_qkv_fwd<T>, "gemm_qkv_fwd", g, 1, st);
-  }
-  {  // 3-4 rotary, QK-norm (in place on q, k)
-    Timed t("rope_qknorm_fwd", st);
-    hipLaunchKernelGGL(rope_qknorm_fwd_kernel<T>, dim3(row_blocks((long)N * H * 2)), dim3(256), 0, st, s.qkv,
-                       s.rho, (const float2*)s.cs, N, c.T, H, C, c.eps);
   }
   {  // 5 causal attention
     AttnArgs a = attn_args<T>(c);
@@ -395,22 +400,20 @@ int bwd_impl(const blk_cfg& c, const T* dy, const T* x, const T* wqkv, const T* 
     hipLaunchKernelGGL(rmsnorm_bwd_kernel<T>, dim3(row_blocks(N)), dim3(256), 0, st, dy, (const T*)w.dh,
                        (const T*)s.h2, (const float*)s.r2, w.dy1, N, C);
   }
-  {  // 6: do = dy1 W_o
+  {  // 6: do = dy1 W_o; delta = rowsum(do * o) per head in the epilogue
     GemmArgs g = gargs(w.dy1, C, wt_o, C, N, C, C);
     g.out = w.dO; g.ldo = C;
+    delta_args(g, c, s.o, w.delta);
     gemm<T>(gemm_o_dgrad<T>, "gemm_o_dgrad", g, 1, st);
   }
   //    dW_o = dy1^T o
   wgrad<T>(gemm_o_wgrad<T>, gemm_o_wgrad_acc<T>, "gemm_o_wgrad", w.dy1, s.o, dwo, C, C, N, acc, w.part, st);
   {  // 5: attention backward
-    {
-      Timed t("attn_delta", st);
-      hipLaunchKernelGGL(attn_delta_kernel<T>, dim3(row_blocks((long)N * H)), dim3(256), 0, st, (const T*)w.dO,
-                         (const T*)s.o, w.delta, N, c.T, H, C);
-    }
     AttnArgs a = attn_args<T>(c);
     a.qkv = s.qkv; a.lse = s.lse; a.dO = w.dO; a.delta = w.delta; a.dqkv = w.dqkv;
+    a.rho = s.rho; a.cs = s.cs;
     const int nqt = (c.T + 127) / 128;
+    // 5-3: the bf16 kernels also apply the QK-norm and rotary backward to dq, dk
     if constexpr (sizeof(T) == 2) {
       constexpr int DKDV_LDS = 3 * (2 * fa::TILE + 2048);
       need_lds(reinterpret_cast<const void*>(attn_bwd_dkdv_bf16_kernel), DKDV_LDS);
@@ -434,12 +437,12 @@ int bwd_impl(const blk_cfg& c, const T* dy, const T* x, const T* wqkv, const T* 
         Timed t("attn_bwd_dq", st);
         hipLaunchKernelGGL(attn_bwd_dq_kernel<T>, dim3(nqt * c.B * H), dim3(256), attn_dq_lds<T>(), st, a);
       }
+      {  // 4-3: QK-norm and rotary backward (in place on dq, dk)
+        Timed t("qknorm_rope_bwd", st);
+        hipLaunchKernelGGL(qknorm_rope_bwd_kernel<T>, dim3(row_blocks((long)N * H * 2)), dim3(256), 0, st, w.dqkv,
+                           (const T*)s.qkv, (const float*)s.rho, (const float2*)s.cs, N, c.T, H, C);
+      }
     }
-  }
-  {  // 4-3: QK-norm and rotary backward (in place on dq, dk)
-    Timed t("qknorm_rope_bwd", st);
-    hipLaunchKernelGGL(qknorm_rope_bwd_kernel<T>, dim3(row_blocks((long)N * H * 2)), dim3(256), 0, st, w.dqkv,
-                       (const T*)s.qkv, (const float*)s.rho, (const float2*)s.cs, N, c.T, H, C);
   }
   {  // 2: dh1 = dqkv W_qkv
     GemmArgs g = gargs(w.dqkv, 3 * C, wt_qkv, 3 * C, N, C, 3 * C);
@@ -530,12 +533,8 @@ int fwd_fp8(const blk_cfg& c, const bf16* x, const bf16* wqkv, const bf16* wo, c
   {
     GemmArgs g = gargs8(f.h1, C, am + AM_H1, f.wqkv, C, am + AM_WQKV, N, 3 * C, C);
     g.out = s.qkv; g.ldo = 3 * C;
+    rope_args(g, c, s.cs, s.rho);
     gemm<fp8e4>(gemm8_qkv_fwd, "gemm_qkv_fwd", g, 1, st);
-  }
-  {
-    Timed t("rope_qknorm_fwd", st);
-    hipLaunchKernelGGL(rope_qknorm_fwd_kernel<bf16>, dim3(row_blocks((long)N * H * 2)), dim3(256), 0, st, s.qkv,
-                       s.rho, (const float2*)s.cs, N, c.T, H, C, c.eps);
   }
   {
     AttnArgs a = attn_args<bf16>(c);
@@ -613,18 +612,15 @@ int bwd_fp8(const blk_cfg& c, const bf16* dy, const bf16* wqkv, const bf16* wo, 
   {  // do = dy1 W_o
     GemmArgs g = gargs8(w.g8, C, am + AM_DY1, wt_o, C, am + AM_WO, N, C, C);
     g.out = w.dO; g.ldo = C;
+    delta_args(g, c, s.o, w.delta);
     gemm<fp8e4>(gemm8_o_dgrad, "gemm_o_dgrad", g, 1, st);
   }
   wgrad8(gemm8_o_wgrad, gemm8_o_wgrad_acc, "gemm_o_wgrad", w.g8t, am + AM_DY1, s.o_8t, am + AM_O, Np, dwo, C, C, N,
          acc, w.part, st);
   {
-    {
-      Timed t("attn_delta", st);
-      hipLaunchKernelGGL(attn_delta_kernel<bf16>, dim3(row_blocks((long)N * H)), dim3(256), 0, st,
-                         (const bf16*)w.dO, (const bf16*)s.o, w.delta, N, c.T, H, C);
-    }
     AttnArgs a = attn_args<bf16>(c);
     a.qkv = s.qkv; a.lse = s.lse; a.dO = w.dO; a.delta = w.delta; a.dqkv = w.dqkv;
+    a.rho = s.rho; a.cs = s.cs;   // QK-norm and rotary backward in the stores
     constexpr int DKDV_LDS = 3 * (2 * fa::TILE + 2048);
     need_lds(reinterpret_cast<const void*>(attn_bwd_dkdv_bf16_kernel), DKDV_LDS);
     need_lds(reinterpret_cast<const void*>(attn_bwd_dq_bf16_kernel), fa::LDS);
@@ -637,11 +633,6 @@ int bwd_fp8(const blk_cfg& c, const bf16* dy, const bf16* wqkv, const bf16* wo, 
       Timed t("attn_bwd_dq", st);
       hipLaunchKernelGGL(attn_bwd_dq_bf16_kernel, dim3(nqt * c.B * H), dim3(256), fa::LDS, st, a);
     }
-  }
-  {
-    Timed t("qknorm_rope_bwd", st);
-    hipLaunchKernelGGL(qknorm_rope_bwd_kernel<bf16>, dim3(row_blocks((long)N * H * 2)), dim3(256), 0, st, w.dqkv,
-                       (const bf16*)s.qkv, (const float*)s.rho, (const float2*)s.cs, N, c.T, H, C);
   }
   quantize(w.dqkv, N, 3 * C, am + AM_DQKV, w.dqkv8, w.dqkv8t, Np, true, st);
   {  // dh1 = dqkv W_qkv

@@ -107,36 +107,6 @@ __global__ void rope_table_kernel(float2* __restrict__ cs, int T, int D, double 
   cs[idx] = make_float2((float)c, (float)s);
 }
 
-// In place on the q and k parts of qkv [N, 3C]: rotate each pair
-// (z[i], z[i+64]) of a 128-wide head by the token's angle, then RMS-normalise
-// the head (QK-norm).  One wave per (token, head, q|k); lane i owns pair i.
-// rho[(which*N + row)*H + head] = the QK-norm factor.
-// (Rotary embedding and QK-norm: flicky.cc nanochat page, section on the
-// model; CSDN nanochat article, section 一 item 1.)
-template <typename T>
-__global__ __launch_bounds__(256) void rope_qknorm_fwd_kernel(T* __restrict__ qkv, float* __restrict__ rho,
-                                                              const float2* __restrict__ cs, int N, int Tlen,
-                                                              int H, int C, float eps) {
-  const int lane = threadIdx.x & 63;
-  const long w = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const long total = (long)N * H * 2;
-  if (w >= total) return;
-  const int which = w % 2;
-  const int head = (w / 2) % H;
-  const long row = w / (2 * H);
-  const int t = row % Tlen;
-  T* z = qkv + row * 3 * C + which * C + head * 128;
-  const float z1 = to_f32(z[lane]), z2 = to_f32(z[lane + 64]);
-  const float2 a = cs[(long)t * 64 + lane];
-  const float r1 = z1 * a.x - z2 * a.y;
-  const float r2 = z1 * a.y + z2 * a.x;
-  const float ss = wave_sum(r1 * r1 + r2 * r2);
-  const float p = 1.f / sqrtf(ss / 128.f + eps);
-  z[lane] = from_f32<T>(r1 * p);
-  z[lane + 64] = from_f32<T>(r2 * p);
-  if (lane == 0) rho[((long)which * N + row) * H + head] = p;
-}
-
 // In place on the dq, dk parts of dqkv [N, 3C]: QK-norm backward
 // (dz' = rho * (dz'' - z'' * mean(dz'' * z''))) then the transpose rotation.
 // zn = the saved normalised q'' | k'' (qkv layout).
@@ -164,24 +134,6 @@ __global__ __launch_bounds__(256) void qknorm_rope_bwd_kernel(T* __restrict__ dq
   const float2 a = cs[(long)t * 64 + lane];
   g[lane] = from_f32<T>(d1 * a.x + d2 * a.y);
   g[lane + 64] = from_f32<T>(-d1 * a.y + d2 * a.x);
-}
-
-// delta[(b*H + head)*T + t] = sum_d do[row, head*128 + d] * o[row, head*128 + d]
-// for row = b*T + t: the row dot product of attention's backward.  One wave
-// per (token, head).
-template <typename T>
-__global__ __launch_bounds__(256) void attn_delta_kernel(const T* __restrict__ dO, const T* __restrict__ O,
-                                                         float* __restrict__ delta, int N, int Tlen, int H, int C) {
-  const int lane = threadIdx.x & 63;
-  const long w = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (w >= (long)N * H) return;
-  const long row = w / H;
-  const int head = w % H;
-  const long off = row * C + head * 128;
-  float s = to_f32(dO[off + lane]) * to_f32(O[off + lane]) + to_f32(dO[off + lane + 64]) * to_f32(O[off + lane + 64]);
-  s = wave_sum(s);
-  const long b = row / Tlen, t = row % Tlen;
-  if (lane == 0) delta[(b * H + head) * Tlen + t] = s;
 }
 
 // dst[c][r] = src[r][c] for a rows x cols matrix (both multiples of 64):

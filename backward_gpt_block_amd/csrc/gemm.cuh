@@ -32,6 +32,8 @@ enum EpiKind : int {
   EPI_DRELU2 = 3,   // out = alpha*acc * 2*max(aux, 0)         (TO)
   EPI_F32 = 4,      // out[split] = alpha*acc                  (float)
   EPI_F32_ADD = 5,  // out += alpha*acc                        (float)
+  EPI_ROPE = 6,     // q, k columns: rotary then QK-norm; v columns stored (TO)
+  EPI_DELTA = 7,    // out = alpha*acc, and delta = per-head row dot of out with aux (TO)
 };
 
 struct GemmArgs {
@@ -48,6 +50,14 @@ struct GemmArgs {
   // multiplies by (amax_a/448) * (amax_b/448) (a zero amax counts as 448)
   const unsigned* amax_a;
   const unsigned* amax_b;
+  // EPI_ROPE: angle table cs[t*64 + i] = (cos, sin), QK-norm factors
+  // rho[(which*M + row)*H + head], tokens per sequence T, heads H, width C.
+  // EPI_DELTA: delta[(b*H + head)*T + t] for row = b*T + t.
+  const float2* cs;
+  float* rho;
+  float* delta;
+  int T, H, C;
+  float eps;
 };
 
 template <typename TI> struct GemmTile {
@@ -208,6 +218,37 @@ __device__ __forceinline__ void epi8(const GemmArgs& g, int split, int row, int 
     }
     st16(p, a);
     st16(p + 4, b);
+  } else if constexpr (EPI == EPI_ROPE) {
+    // 16 consecutive lanes hold one 128-wide head of the row (8 columns
+    // each); rotary pairs (i, i + 64) sit 8 lanes apart
+    constexpr int EL = Chunk<TO>::N;
+    TO* o = static_cast<TO*>(g.out) + (long)row * g.ldo + col;
+    const int which = col / g.C;          // 0 q, 1 k, 2 v (uniform over the 16 lanes)
+    if (which < 2) {
+      const int cg = (col % 128) >> 3;    // this lane's 8-column group in the head
+      const int t = row % g.T;
+      const float* csp = reinterpret_cast<const float*>(g.cs + (long)t * 64 + (cg & 7) * 8);
+      float c8[16];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) Chunk<float>::unpack(ld16(csp + 4 * h), c8 + 4 * h);
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float other = __shfl_xor(f[e], 8, 64);
+        const float c = c8[2 * e], sn = c8[2 * e + 1];
+        // first half: z1 = own, z2 = partner; second half: z1 = partner, z2 = own
+        f[e] = cg < 8 ? f[e] * c - other * sn : other * sn + f[e] * c;
+        ss += f[e] * f[e];
+      }
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1) ss += __shfl_xor(ss, m, 64);
+      const float r = 1.f / sqrtf(ss / 128.f + g.eps);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] *= r;
+      if (cg == 0) g.rho[((long)which * g.M + row) * g.H + (col % g.C) / 128] = r;
+    }
+#pragma unroll
+    for (int h = 0; h < 8 / EL; ++h) st16(o + h * EL, Chunk<TO>::pack(f + h * EL));
   } else {
     constexpr int EL = Chunk<TO>::N;     // 8 bf16 or 4 float per chunk
     TO* o = static_cast<TO*>(g.out) + (long)row * g.ldo + col;
@@ -221,6 +262,25 @@ __device__ __forceinline__ void epi8(const GemmArgs& g, int split, int row, int 
     }
 #pragma unroll
     for (int h = 0; h < 8 / EL; ++h) st16(o + h * EL, Chunk<TO>::pack(f + h * EL));
+    if constexpr (EPI == EPI_DELTA) {
+      // the dot uses the stored (rounded) values, as the attention kernels read them
+      const TO* x = static_cast<const TO*>(g.aux) + (long)row * g.ldaux + col;
+      float xv[8], rv[8];
+#pragma unroll
+      for (int h = 0; h < 8 / EL; ++h) {
+        Chunk<TO>::unpack(ld16(x + h * EL), xv + h * EL);
+        Chunk<TO>::unpack(Chunk<TO>::pack(f + h * EL), rv + h * EL);
+      }
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) d += rv[e] * xv[e];
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1) d += __shfl_xor(d, m, 64);
+      if ((col & 127) == 0) {
+        const long b = row / g.T, t = row % g.T;
+        g.delta[(b * g.H + col / 128) * g.T + t] = d;
+      }
+    }
     if constexpr (EPI == EPI_RELU2) {
       TO* o2 = static_cast<TO*>(g.out2) + (long)row * g.ldo2 + col;
       float a[8];
@@ -384,13 +444,13 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   }
 
 namespace blk {
-BLK_GEMM_KERNEL(gemm_qkv_fwd, true, true, EPI_STORE, T)
+BLK_GEMM_KERNEL(gemm_qkv_fwd, true, true, EPI_ROPE, T)
 BLK_GEMM_KERNEL(gemm_o_fwd, true, true, EPI_RESID, T)
 BLK_GEMM_KERNEL(gemm_fc_fwd, true, true, EPI_RELU2, T)
 BLK_GEMM_KERNEL(gemm_proj_fwd, true, true, EPI_RESID, T)
 BLK_GEMM_KERNEL(gemm_proj_dgrad, true, true, EPI_DRELU2, T)
 BLK_GEMM_KERNEL(gemm_fc_dgrad, true, true, EPI_STORE, T)
-BLK_GEMM_KERNEL(gemm_o_dgrad, true, true, EPI_STORE, T)
+BLK_GEMM_KERNEL(gemm_o_dgrad, true, true, EPI_DELTA, T)
 BLK_GEMM_KERNEL(gemm_qkv_dgrad, true, true, EPI_STORE, T)
 BLK_GEMM_KERNEL(gemm_proj_wgrad, false, false, EPI_F32, float)
 BLK_GEMM_KERNEL(gemm_fc_wgrad, false, false, EPI_F32, float)
@@ -410,13 +470,13 @@ BLK_GEMM_KERNEL(gemm_qkv_wgrad_acc, false, false, EPI_F32_ADD, float)
   }
 
 namespace blk {
-BLK_GEMM8_KERNEL(gemm8_qkv_fwd, EPI_STORE, bf16)
+BLK_GEMM8_KERNEL(gemm8_qkv_fwd, EPI_ROPE, bf16)
 BLK_GEMM8_KERNEL(gemm8_o_fwd, EPI_RESID, bf16)
 BLK_GEMM8_KERNEL(gemm8_fc_fwd, EPI_RELU2, bf16)
 BLK_GEMM8_KERNEL(gemm8_proj_fwd, EPI_RESID, bf16)
 BLK_GEMM8_KERNEL(gemm8_proj_dgrad, EPI_DRELU2, bf16)
 BLK_GEMM8_KERNEL(gemm8_fc_dgrad, EPI_STORE, bf16)
-BLK_GEMM8_KERNEL(gemm8_o_dgrad, EPI_STORE, bf16)
+BLK_GEMM8_KERNEL(gemm8_o_dgrad, EPI_DELTA, bf16)
 BLK_GEMM8_KERNEL(gemm8_qkv_dgrad, EPI_STORE, bf16)
 BLK_GEMM8_KERNEL(gemm8_proj_wgrad, EPI_F32, float)
 BLK_GEMM8_KERNEL(gemm8_fc_wgrad, EPI_F32, float)
