@@ -101,15 +101,65 @@ def main() -> int:
     ap.add_argument("--workload", default="d20_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device copy (the known-size kernel that scales HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the block step is measured on one GPU's share "
               "(see the sharding notes); --gpus must be 1", file=sys.stderr)
         return 2
+    if args.copy_calibration:
+        return copy_calibration()
     from blockinputs import DECODE_WORKLOADS
     if args.workload in DECODE_WORKLOADS:
         return bench_decode(args)
     return bench_train(args)
+
+
+COPY_BYTES = 1 << 30
+
+
+def copy_calibration() -> int:
+    """Five copies of 1 GiB between two device buffers: each dispatch reads
+    and writes exactly COPY_BYTES, so FETCH_SIZE / WRITE_SIZE of these
+    dispatches give the counters' scale."""
+    import torch
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "copies": 5}), flush=True)
+    return 0
+
+
+def source_digest() -> str:
+    """SHA-256 over the HIP sources: a traffic figure measured on other
+    sources no longer describes the kernel."""
+    import hashlib
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "backward_gpt_block_amd", "csrc")
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".cuh", ".hip")):
+            h.update(name.encode())
+            h.update(open(os.path.join(d, name), "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of launch site `kernel` on `workload` from the
+    committed counter summary profiles/<workload>_hbm_traffic.txt, or None
+    when there is none or it was measured on other sources."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    digest, value = None, None
+    for line in open(path):
+        if line.startswith("source_sha256:"):
+            digest = line.split(":", 1)[1].strip()
+        elif line.startswith(f"traffic {kernel}:"):
+            value = float(line.split(":", 1)[1])
+    return value if digest == source_digest() else None
 
 
 def bench_train(args) -> int:
@@ -184,7 +234,7 @@ def bench_train(args) -> int:
         achieved = fl[dname] / (davg_ms * 1e-3) / 1e12
         peak = PEAK_TFLOPS["fp8" if sh.gemm == "fp8" and dname.startswith("gemm") else dt]
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4), "traffic": None, "kernel": dname,
+                "frac": round(achieved / peak, 4), "traffic": measured_traffic(dname, args.workload), "kernel": dname,
                 "avg_launch_ms": round(davg_ms, 4), "flops_per_launch": fl[dname]}
     else:
         roof = {"bound": "hbm", "achieved": None, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": None,
@@ -313,8 +363,8 @@ def bench_decode(args) -> int:
         log(f"  {k:16s} {1e3 * tot / args.steps:8.1f} us/step {tot / total:6.1%}")
     dname, (dtot, dcnt) = max(sites.items(), key=lambda kv: kv[1][0])
     davg = dtot / dcnt
-    roof = {"bound": "hbm", "achieved": None, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": None, "traffic": None,
-            "kernel": dname, "avg_launch_ms": round(davg, 5)}
+    roof = {"bound": "hbm", "achieved": None, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": None,
+            "traffic": measured_traffic(dname, args.workload), "kernel": dname, "avg_launch_ms": round(davg, 5)}
     if dname == "dec_attn":
         b = decode_attn_bytes(sh, lens_u)
         ach = b / (davg * 1e-3) / 1e9
