@@ -18,6 +18,7 @@
 // article, section "Modelo, escalado y objetivo de speedrun"; QK-norm and
 // rotary precede it: flicky.cc nanochat page, section on the model.)
 #pragma once
+#include <type_traits>
 #include "common.cuh"
 #include "gemm.cuh"
 
@@ -862,18 +863,26 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_bf16_kernel(AttnArgs a) 
     const float* vec = (const float*)(smem + (it % 3) * SLOTB + 2 * TILE);
     if (q0 + QT - 1 < kw0) continue;             // all queries precede all keys of this wave
     const bool need_mask = (q0 < kw0 + 31) || (q0 + QT > a.T);
+    // one copy of the iteration with the causal/edge mask and one without,
+    // so that each is a single scheduling region
+    auto body = [&](auto maskc) {
+    constexpr bool MASK = decltype(maskc)::value;
+    // Two 32-query halves, software-pipelined so that each half's softmax and
+    // dS arithmetic issues between independent MFMAs: S/dP(0); S/dP(1) with
+    // softmax(0); dV/dK(0) with softmax(1); dV/dK(1).
+    f32x16 sv[2], dp[2];
+    auto sdp = [&](int qb) {
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      f32x16 sv, dp;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) { sv[r] = 0.f; dp[r] = 0.f; }
+      for (int r = 0; r < 16; ++r) { sv[qb][r] = 0.f; dp[qb][r] = 0.f; }
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
         const bf16x8 qa = *(lds_bf16x8*)(qt_ + qb * 8192 + ko[ks]);
         const bf16x8 oa = *(lds_bf16x8*)(ot_ + qb * 8192 + ko[ks]);
-        sv = MM::mma(qa, kf[ks], sv);       // S  (query x key)
-        dp = MM::mma(oa, vf[ks], dp);       // dP (query x key)
+        sv[qb] = MM::mma(qa, kf[ks], sv[qb]);       // S  (query x key)
+        dp[qb] = MM::mma(oa, vf[ks], dp[qb]);       // dP (query x key)
       }
+    };
+    auto softmax = [&](int qb) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int qi = qb * 32 + 8 * g + 4 * (lane >> 5);
@@ -882,23 +891,59 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_bf16_kernel(AttnArgs a) 
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g + e;
-          float p = __builtin_amdgcn_exp2f(fmaf(sv[r], a.sl2, -lv[e]));
-          if (need_mask && (key > q0 + qi + e || q0 + qi + e >= a.T)) p = 0.f;
-          sv[r] = p;
-          dp[r] = p * (dp[r] - dl[e]);      // dS
+          float p = __builtin_amdgcn_exp2f(fmaf(sv[qb][r], a.sl2, -lv[e]));
+          if constexpr (MASK) p = (key > q0 + qi + e || q0 + qi + e >= a.T) ? 0.f : p;
+          sv[qb][r] = p;
+          dp[qb][r] = p * (dp[qb][r] - dl[e]);      // dS
         }
       }
+    };
+    auto dvdk = [&](int qb) {
 #pragma unroll
       for (int mm = 0; mm < 2; ++mm) {
-        const bf16x8 pf = frag_regs<bf16>(sv, mm * 8);
-        const bf16x8 sf = frag_regs<bf16>(dp, mm * 8);
+        const bf16x8 pf = frag_regs<bf16>(sv[qb], mm * 8);
+        const bf16x8 sf = frag_regs<bf16>(dp[qb], mm * 8);
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
           dv[db] = MM::mma(frag_vt_at(ot_, vo, 2 * qb + mm, db), pf, dv[db]);
           dk[db] = MM::mma(frag_vt_at(qt_, vo, 2 * qb + mm, db), sf, dk[db]);
         }
       }
+    };
+    sdp(0);
+    sdp(1);
+    softmax(0);
+    dvdk(0);
+    softmax(1);
+    dvdk(1);
+    // schedule: S/dP(0) with its fragment reads; S/dP(1) (and its reads)
+    // between the VALU of softmax(0); dV/dK(0) and its transposed reads
+    // between the VALU of softmax(1); then dV/dK(1)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
     }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // VALU
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    };
+    if (need_mask) body(std::true_type());
+    else body(std::false_type());
   }
   if (kv) {
     const long rowi = (long)b * a.T + key;
