@@ -1004,37 +1004,73 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_bf16_kernel(AttnArgs a) {
     const lds_char* vt_ = kt_ + TILE;
     const int k0 = kt * KT;
     if (k0 > qw0 + 31) continue;
-    f32x16 sv[2], dp[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) { sv[kb][r] = 0.f; dp[kb][r] = 0.f; }
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        sv[kb] = MM::mma(*(lds_bf16x8*)(kt_ + kb * 8192 + ko[ks]), qf[ks], sv[kb]);   // S^T
-        dp[kb] = MM::mma(*(lds_bf16x8*)(vt_ + kb * 8192 + ko[ks]), df[ks], dp[kb]);   // dP^T
-      }
-    }
     const bool need_mask = (k0 + KT - 1 > qw0) || (k0 + KT > a.T);
+    // Two 32-key halves, software-pipelined as in the dK/dV kernel:
+    // S/dP(0); S/dP(1) with dS(0); dQ(0) with dS(1); dQ(1).  Masked and
+    // unmasked tiles are separate copies (one scheduling region each).
+    auto body = [&](auto maskc) {
+      constexpr bool MASK = decltype(maskc)::value;
+      f32x16 sv[2], dp[2];
+      auto sdp = [&](int kb) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+        for (int r = 0; r < 16; ++r) { sv[kb][r] = 0.f; dp[kb][r] = 0.f; }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = __builtin_amdgcn_exp2f(fmaf(sv[kb][r], a.sl2, -lse));
-        if (need_mask) {
-          const int kk = k0 + kb * 32 + acc_row(r, lane);
-          if (kk > q || kk >= a.T) p = 0.f;
+        for (int ks = 0; ks < 8; ++ks) {
+          sv[kb] = MM::mma(*(lds_bf16x8*)(kt_ + kb * 8192 + ko[ks]), qf[ks], sv[kb]);   // S^T
+          dp[kb] = MM::mma(*(lds_bf16x8*)(vt_ + kb * 8192 + ko[ks]), df[ks], dp[kb]);   // dP^T
         }
-        sv[kb][r] = p * (dp[kb][r] - dlt);   // dS^T
+      };
+      auto ds = [&](int kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float p = __builtin_amdgcn_exp2f(fmaf(sv[kb][r], a.sl2, -lse));
+          if constexpr (MASK) {
+            const int kk = k0 + kb * 32 + acc_row(r, lane);
+            p = (kk > q || kk >= a.T) ? 0.f : p;
+          }
+          sv[kb][r] = p * (dp[kb][r] - dlt);   // dS^T
+        }
+      };
+      auto dq = [&](int kb) {
+#pragma unroll
+        for (int m2 = 0; m2 < 2; ++m2) {
+          const int mm = 2 * kb + m2;
+          const bf16x8 sf = frag_regs<bf16>(sv[kb], m2 * 8);
+#pragma unroll
+          for (int db = 0; db < 4; ++db) acc[db] = MM::mma(frag_vt_at(kt_, vo, mm, db), sf, acc[db]);
+        }
+      };
+      sdp(0);
+      sdp(1);
+      ds(0);
+      dq(0);
+      ds(1);
+      dq(1);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
       }
 #pragma unroll
-    for (int mm = 0; mm < 4; ++mm) {
-      const bf16x8 sf = frag_regs<bf16>(sv[mm >> 1], (mm & 1) * 8);
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // VALU
+      }
 #pragma unroll
-      for (int db = 0; db < 4; ++db) acc[db] = MM::mma(frag_vt_at(kt_, vo, mm, db), sf, acc[db]);
-    }
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+    };
+    if (need_mask) body(std::true_type());
+    else body(std::false_type());
   }
   if (qv) {
     const long rowi = (long)b * a.T + q;
