@@ -45,7 +45,6 @@ template <typename T> struct Saved {
   float* lse;    // [B*H][T]
   float* r2;     // [N]
   T* h2;         // [N, C]
-  T* u;          // [N, F]
   T* a;          // [N, F]
   // fp8 mode: transposed E4M3 copies of the weight-gradient operands, [*, Np]
   // with Np = N rounded up to 64 (zero padding), and the 16 amax slots
@@ -69,7 +68,6 @@ template <typename T> Saved<T> carve_saved(const blk_cfg& c, void* p) {
   s.lse = k.take<float>((size_t)c.B * c.H * c.T);
   s.r2 = k.take<float>(N);
   s.h2 = k.take<T>(N * c.C);
-  s.u = k.take<T>(N * c.F);
   s.a = k.take<T>(N * c.F);
   if (c.gemm == BLK_GEMM_FP8_E4M3) {
     const long Np = pad64(N);
@@ -345,9 +343,9 @@ int fwd_impl(const blk_cfg& c, const T* x, const T* wqkv, const T* wo, const T* 
     hipLaunchKernelGGL(rmsnorm_fwd_kernel<T>, dim3(row_blocks(N)), dim3(256), 0, st, (const T*)y, s.h2, s.r2, N,
                        C, c.eps);
   }
-  {  // 8 u = h2 W_fc^T, a = relu(u)^2
+  {  // 8 a = relu(h2 W_fc^T)^2 (u itself is not kept: the backward uses 2 sqrt(a))
     GemmArgs g = gargs(s.h2, C, wfc, C, N, F, C);
-    g.out = s.u; g.ldo = F; g.out2 = s.a; g.ldo2 = F;
+    g.out = s.a; g.ldo = F;
     gemm<T>(gemm_fc_fwd<T>, "gemm_fc_fwd", g, 1, st);
   }
   {  // 9 y = y1 + a W_proj^T   (in place on y)
@@ -380,9 +378,9 @@ int bwd_impl(const blk_cfg& c, const T* dy, const T* x, const T* wqkv, const T* 
     tr(wo, wt_o, C, C);
     tr(wqkv, wt_qkv, 3 * C, C);
   }
-  {  // 9: du = (dy W_proj) * 2 max(u, 0)
+  {  // 9: du = (dy W_proj) * 2 max(u, 0), with max(u, 0) = sqrt(a)
     GemmArgs g = gargs(dy, C, wt_proj, C, N, F, C);
-    g.out = w.du; g.ldo = F; g.aux = s.u; g.ldaux = F;
+    g.out = w.du; g.ldo = F; g.aux = s.a; g.ldaux = F;
     gemm<T>(gemm_proj_dgrad<T>, "gemm_proj_dgrad", g, 1, st);
   }
   //    dW_proj = dy^T a
@@ -558,7 +556,7 @@ int fwd_fp8(const blk_cfg& c, const bf16* x, const bf16* wqkv, const bf16* wo, c
   quantize(s.h2, N, C, am + AM_H2, f.h2, s.h2_8t, Np, true, st);
   {
     GemmArgs g = gargs8(f.h2, C, am + AM_H2, f.wfc, C, am + AM_WFC, N, F, C);
-    g.out = s.u; g.ldo = F; g.out2 = s.a; g.ldo2 = F;
+    g.out = s.a; g.ldo = F;
     gemm<fp8e4>(gemm8_fc_fwd, "gemm_fc_fwd", g, 1, st);
   }
   quantize(s.a, N, F, am + AM_A, f.a, s.a_8t, Np, true, st);
@@ -590,7 +588,7 @@ int bwd_fp8(const blk_cfg& c, const bf16* dy, const bf16* wqkv, const bf16* wo, 
   quantize(dy, N, C, am + AM_DY, w.g8, w.g8t, Np, true, st);
   {  // du = (dy W_proj) * 2 max(u, 0)
     GemmArgs g = gargs8(w.g8, C, am + AM_DY, wt_proj, C, am + AM_WPROJ, N, F, C);
-    g.out = w.du; g.ldo = F; g.aux = s.u; g.ldaux = F;
+    g.out = w.du; g.ldo = F; g.aux = s.a; g.ldaux = F;
     gemm<fp8e4>(gemm8_proj_dgrad, "gemm_proj_dgrad", g, 1, st);
   }
   wgrad8(gemm8_proj_wgrad, gemm8_proj_wgrad_acc, "gemm_proj_wgrad", w.g8t, am + AM_DY, s.a_8t, am + AM_A, Np, dwproj,

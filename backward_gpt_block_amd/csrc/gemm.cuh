@@ -28,8 +28,8 @@ namespace blk {
 enum EpiKind : int {
   EPI_STORE = 0,    // out = alpha*acc                         (element TO)
   EPI_RESID = 1,    // out = aux + alpha*acc                   (TO)
-  EPI_RELU2 = 2,    // out = v, out2 = max(v,0)^2, v = alpha*acc (TO)
-  EPI_DRELU2 = 3,   // out = alpha*acc * 2*max(aux, 0)         (TO)
+  EPI_RELU2 = 2,    // out = max(v,0)^2, v = alpha*acc           (TO)
+  EPI_DRELU2 = 3,   // out = alpha*acc * 2*sqrt(aux), aux = max(u,0)^2 (TO)
   EPI_F32 = 4,      // out[split] = alpha*acc                  (float)
   EPI_F32_ADD = 5,  // out += alpha*acc                        (float)
   EPI_ROPE = 6,     // q, k columns: rotary then QK-norm; v columns stored (TO)
@@ -258,7 +258,12 @@ __device__ __forceinline__ void epi8(const GemmArgs& g, int split, int row, int 
 #pragma unroll
       for (int h = 0; h < 8 / EL; ++h) Chunk<TO>::unpack(ld16(x + h * EL), xv + h * EL);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) f[e] = (EPI == EPI_RESID) ? xv[e] + f[e] : f[e] * 2.f * fmaxf(xv[e], 0.f);
+      // ReLU^2 derivative 2 max(u,0) recovered from the stored a = max(u,0)^2
+      for (int e = 0; e < 8; ++e) f[e] = (EPI == EPI_RESID) ? xv[e] + f[e] : f[e] * 2.f * __builtin_amdgcn_sqrtf(xv[e]);
+    }
+    if constexpr (EPI == EPI_RELU2) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { const float p = fmaxf(f[e], 0.f); f[e] = p * p; }
     }
 #pragma unroll
     for (int h = 0; h < 8 / EL; ++h) st16(o + h * EL, Chunk<TO>::pack(f + h * EL));
@@ -280,14 +285,6 @@ __device__ __forceinline__ void epi8(const GemmArgs& g, int split, int row, int 
         const long b = row / g.T, t = row % g.T;
         g.delta[(b * g.H + col / 128) * g.T + t] = d;
       }
-    }
-    if constexpr (EPI == EPI_RELU2) {
-      TO* o2 = static_cast<TO*>(g.out2) + (long)row * g.ldo2 + col;
-      float a[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) { const float p = fmaxf(f[e], 0.f); a[e] = p * p; }
-#pragma unroll
-      for (int h = 0; h < 8 / EL; ++h) st16(o2 + h * EL, Chunk<TO>::pack(a + h * EL));
     }
   }
 }
