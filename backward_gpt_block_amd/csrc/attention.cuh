@@ -159,8 +159,9 @@ __device__ __forceinline__ void frag_row_global(typename Mfma<T>::frag* f, const
 // Store the 128 x 32 accumulator acc[4] (rows d, column = this lane's row r)
 // times `scale` into dst row (128 contiguous values).
 template <typename T>
-__device__ __forceinline__ void store_acc_row(T* dst, const f32x16* acc, float scale, int lane) {
+__device__ __forceinline__ float store_acc_row(T* dst, const f32x16* acc, float scale, int lane) {
   const int h = lane >> 5;
+  float mx = 0.f;
 #pragma unroll
   for (int db = 0; db < 4; ++db) {
 #pragma unroll
@@ -169,7 +170,11 @@ __device__ __forceinline__ void store_acc_row(T* dst, const f32x16* acc, float s
       if constexpr (sizeof(T) == 2) {
         bf16x4 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (bf16)(acc[db][4 * g + e] * scale);
+        for (int e = 0; e < 4; ++e) {
+          const float x = acc[db][4 * g + e] * scale;
+          mx = fmaxf(mx, fabsf(x));
+          v[e] = (bf16)x;
+        }
         st8(dst + d, __builtin_bit_cast(u32x2, v));
       } else {
         u32x4 v;
@@ -179,6 +184,7 @@ __device__ __forceinline__ void store_acc_row(T* dst, const f32x16* acc, float s
       }
     }
   }
+  return mx;   // largest stored magnitude (bf16 rows), before rounding
 }
 
 // Stores the gradient of q' or k' (before QK-norm and rotary) of one row:
@@ -188,8 +194,8 @@ __device__ __forceinline__ void store_acc_row(T* dst, const f32x16* acc, float s
 // dz' = p (g - z mean(g z)), then the transposed rotation of each pair
 // (d, d + 64).  (Rotary embedding and QK-norm: flicky.cc nanochat page,
 // section on the model.)
-__device__ __forceinline__ void store_acc_row_qk(bf16* dst, const bf16* z, float p, const float2* cs,
-                                                 const f32x16* acc, float scale, int lane) {
+__device__ __forceinline__ float store_acc_row_qk(bf16* dst, const bf16* z, float p, const float2* cs,
+                                                  const f32x16* acc, float scale, int lane) {
   const int h = lane >> 5;
   float gv[4][16], zv[4][16];
   float dot = 0.f;
@@ -207,6 +213,7 @@ __device__ __forceinline__ void store_acc_row_qk(bf16* dst, const bf16* z, float
     }
   dot += __shfl_xor(dot, 32, 64);
   const float mean = dot * (1.f / 128.f);
+  float mx = 0.f;
 #pragma unroll
   for (int db = 0; db < 2; ++db)
 #pragma unroll
@@ -222,12 +229,15 @@ __device__ __forceinline__ void store_acc_row_qk(bf16* dst, const bf16* z, float
         const float d1 = p * (gv[db][r] - zv[db][r] * mean);
         const float d2 = p * (gv[db + 2][r] - zv[db + 2][r] * mean);
         const float c = c8[2 * e], sn = c8[2 * e + 1];
-        lo[e] = (bf16)(d1 * c + d2 * sn);
-        hi[e] = (bf16)(d2 * c - d1 * sn);
+        const float vlo = d1 * c + d2 * sn, vhi = d2 * c - d1 * sn;
+        mx = fmaxf(mx, fmaxf(fabsf(vlo), fabsf(vhi)));
+        lo[e] = (bf16)vlo;
+        hi[e] = (bf16)vhi;
       }
       st8(dst + db * 32 + 8 * i + 4 * h, __builtin_bit_cast(u32x2, lo));
       st8(dst + (db + 2) * 32 + 8 * i + 4 * h, __builtin_bit_cast(u32x2, hi));
     }
+  return mx;   // largest stored magnitude, before rounding
 }
 
 struct AttnArgs {
@@ -239,6 +249,8 @@ struct AttnArgs {
   void* dqkv;        // [B*T, 3C]: dq'' | dk'' | dv; bf16 kernels: dq' | dk' | dv
   const float* rho;    // [2][B*T][H] QK-norm factors (bf16 backward kernels)
   const float2* cs;    // [T][64] rotary angles (bf16 backward kernels)
+  unsigned* amax_o;    // fp8 mode: absolute maxima (float bits) of o and of
+  unsigned* amax_dqkv; //   dq' | dk' | dv, or null
   int B, T, H, C;
   float sl2;         // log2(e) / sqrt(D)
   float rsd;         // 1 / sqrt(D)
@@ -760,15 +772,18 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_bf16_kernel(AttnArgs a) {
       }
     }
   }
+  float mx = 0.f;
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int q = qw0 + qb * 32 + (lane & 31);
     const float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 32, 64);
     if (q < a.T) {
-      store_acc_row<bf16>(static_cast<bf16*>(a.o) + ((long)b * a.T + q) * a.C + head * HD, o[qb], 1.f / l_tot, lane);
+      mx = fmaxf(mx, store_acc_row<bf16>(static_cast<bf16*>(a.o) + ((long)b * a.T + q) * a.C + head * HD, o[qb],
+                                         1.f / l_tot, lane));
       if (h == 0) a.lse[(long)bh * a.T + q] = m_run[qb] + log2f(l_tot);
     }
   }
+  if (a.amax_o) amax_publish<bf16>(a.amax_o, mx);
 }
 
 // ---- backward, bf16, direct-to-LDS pipelines ----------------------------------------
@@ -945,14 +960,16 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_bf16_kernel(AttnArgs a) 
     if (need_mask) body(std::true_type());
     else body(std::false_type());
   }
+  float mx = 0.f;
   if (kv) {
     const long rowi = (long)b * a.T + key;
     bf16* row = static_cast<bf16*>(a.dqkv) + rowi * 3 * a.C + head * HD;
     const bf16* zk = qkv + rowi * 3 * a.C + a.C + head * HD;
-    store_acc_row_qk(row + a.C, zk, a.rho[((long)a.B * a.T + rowi) * a.H + head], a.cs + (long)key * 64, dk, a.rsd,
-                     lane);
-    store_acc_row<bf16>(row + 2 * a.C, dv, 1.f, lane);
+    mx = store_acc_row_qk(row + a.C, zk, a.rho[((long)a.B * a.T + rowi) * a.H + head], a.cs + (long)key * 64, dk,
+                          a.rsd, lane);
+    mx = fmaxf(mx, store_acc_row<bf16>(row + 2 * a.C, dv, 1.f, lane));
   }
+  if (a.amax_dqkv) amax_publish<bf16>(a.amax_dqkv, mx);
 }
 
 // dQ: one workgroup = 128 queries of one (sequence, head), 4 waves x 32
@@ -1072,11 +1089,13 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_bf16_kernel(AttnArgs a) {
     if (need_mask) body(std::true_type());
     else body(std::false_type());
   }
+  float mx = 0.f;
   if (qv) {
     const long rowi = (long)b * a.T + q;
-    store_acc_row_qk(static_cast<bf16*>(a.dqkv) + rowi * 3 * a.C + head * HD, qkv + rowi * 3 * a.C + head * HD,
-                     a.rho[rowi * a.H + head], a.cs + (long)q * 64, acc, a.rsd, lane);
+    mx = store_acc_row_qk(static_cast<bf16*>(a.dqkv) + rowi * 3 * a.C + head * HD, qkv + rowi * 3 * a.C + head * HD,
+                          a.rho[rowi * a.H + head], a.cs + (long)q * 64, acc, a.rsd, lane);
   }
+  if (a.amax_dqkv) amax_publish<bf16>(a.amax_dqkv, mx);
 }
 
 template <typename T> constexpr int attn_fwd_lds() { return 2 * (AttnCfg<T>::ROWT + AttnCfg<T>::TRT); }

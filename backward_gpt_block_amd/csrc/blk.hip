@@ -468,10 +468,11 @@ void quantize(const bf16* x, long rows, long cols, unsigned* am, uint8_t* q, uin
   const long n = rows * cols;
   Timed t("fp8_quantize", st);
   if (amax) hipLaunchKernelGGL(amax_kernel, dim3(elt_grid(n)), dim3(256), 0, st, x, n, am);
-  if (q) hipLaunchKernelGGL(quant_kernel, dim3(elt_grid(n)), dim3(256), 0, st, x, n, (const unsigned*)am, q);
-  if (qt)
+  if (qt)   // transposed codes, and the row-major ones in the same pass
     hipLaunchKernelGGL(quant_trans_kernel, dim3((unsigned)(cols / 64), (unsigned)(ldt / 64)), dim3(256), 0, st, x,
-                       (int)rows, (int)cols, (const unsigned*)am, qt, (int)ldt);
+                       (int)rows, (int)cols, (const unsigned*)am, qt, (int)ldt, q);
+  else if (q)
+    hipLaunchKernelGGL(quant_kernel, dim3(elt_grid(n)), dim3(256), 0, st, x, n, (const unsigned*)am, q);
 }
 
 GemmArgs gargs8(const uint8_t* A, long lda, const unsigned* ama, const uint8_t* B, long ldb, const unsigned* amb,
@@ -521,13 +522,14 @@ int fwd_fp8(const blk_cfg& c, const bf16* x, const bf16* wqkv, const bf16* wo, c
   }
   {
     Timed t("rmsnorm_fwd", st);
-    hipLaunchKernelGGL(rmsnorm_fwd_kernel<bf16>, dim3(row_blocks(N)), dim3(256), 0, st, x, s.h1, s.r1, N, C, c.eps);
+    hipLaunchKernelGGL(rmsnorm_fwd_kernel<bf16>, dim3(row_blocks(N)), dim3(256), 0, st, x, s.h1, s.r1, N, C, c.eps,
+                       am + AM_H1);
   }
   quantize(wqkv, 3 * C, C, am + AM_WQKV, f.wqkv, nullptr, 0, true, st);
   quantize(wo, C, C, am + AM_WO, f.wo, nullptr, 0, true, st);
   quantize(wfc, F, C, am + AM_WFC, f.wfc, nullptr, 0, true, st);
   quantize(wproj, C, F, am + AM_WPROJ, f.wproj, nullptr, 0, true, st);
-  quantize(s.h1, N, C, am + AM_H1, f.h1, s.h1_8t, Np, true, st);
+  quantize(s.h1, N, C, am + AM_H1, f.h1, s.h1_8t, Np, false, st);   // amax from rmsnorm_fwd
   {
     GemmArgs g = gargs8(f.h1, C, am + AM_H1, f.wqkv, C, am + AM_WQKV, N, 3 * C, C);
     g.out = s.qkv; g.ldo = 3 * C;
@@ -536,13 +538,13 @@ int fwd_fp8(const blk_cfg& c, const bf16* x, const bf16* wqkv, const bf16* wo, c
   }
   {
     AttnArgs a = attn_args<bf16>(c);
-    a.qkv = s.qkv; a.o = s.o; a.lse = s.lse;
+    a.qkv = s.qkv; a.o = s.o; a.lse = s.lse; a.amax_o = am + AM_O;
     Timed t("attn_fwd", st);
     need_lds(reinterpret_cast<const void*>(attn_fwd_bf16_kernel), fa::LDS);
     const int nqt = (c.T + fa::QWG - 1) / fa::QWG;
     hipLaunchKernelGGL(attn_fwd_bf16_kernel, dim3(nqt * c.B * H), dim3(256), fa::LDS, st, a);
   }
-  quantize(s.o, N, C, am + AM_O, f.o, s.o_8t, Np, true, st);
+  quantize(s.o, N, C, am + AM_O, f.o, s.o_8t, Np, false, st);       // amax from attn_fwd
   {
     GemmArgs g = gargs8(f.o, C, am + AM_O, f.wo, C, am + AM_WO, N, C, C);
     g.out = y; g.ldo = C; g.aux = x; g.ldaux = C;
@@ -551,15 +553,15 @@ int fwd_fp8(const blk_cfg& c, const bf16* x, const bf16* wqkv, const bf16* wo, c
   {
     Timed t("rmsnorm_fwd", st);
     hipLaunchKernelGGL(rmsnorm_fwd_kernel<bf16>, dim3(row_blocks(N)), dim3(256), 0, st, (const bf16*)y, s.h2, s.r2, N,
-                       C, c.eps);
+                       C, c.eps, am + AM_H2);
   }
-  quantize(s.h2, N, C, am + AM_H2, f.h2, s.h2_8t, Np, true, st);
+  quantize(s.h2, N, C, am + AM_H2, f.h2, s.h2_8t, Np, false, st);   // amax from rmsnorm_fwd
   {
     GemmArgs g = gargs8(f.h2, C, am + AM_H2, f.wfc, C, am + AM_WFC, N, F, C);
-    g.out = s.a; g.ldo = F;
+    g.out = s.a; g.ldo = F; g.amax_out = am + AM_A;
     gemm<fp8e4>(gemm8_fc_fwd, "gemm_fc_fwd", g, 1, st);
   }
-  quantize(s.a, N, F, am + AM_A, f.a, s.a_8t, Np, true, st);
+  quantize(s.a, N, F, am + AM_A, f.a, s.a_8t, Np, false, st);       // amax from gemm_fc_fwd
   {
     GemmArgs g = gargs8(f.a, F, am + AM_A, f.wproj, F, am + AM_WPROJ, N, C, F);
     g.out = y; g.ldo = C; g.aux = y; g.ldaux = C;
@@ -586,14 +588,14 @@ int bwd_fp8(const blk_cfg& c, const bf16* dy, const bf16* wqkv, const bf16* wo, 
   quantize(wqkv, 3 * C, C, am + AM_WQKV, nullptr, wt_qkv, 3 * C, false, st);
 
   quantize(dy, N, C, am + AM_DY, w.g8, w.g8t, Np, true, st);
-  {  // du = (dy W_proj) * 2 max(u, 0)
+  {  // du = (dy W_proj) * 2 max(u, 0), with max(u, 0) = sqrt(a)
     GemmArgs g = gargs8(w.g8, C, am + AM_DY, wt_proj, C, am + AM_WPROJ, N, F, C);
-    g.out = w.du; g.ldo = F; g.aux = s.a; g.ldaux = F;
+    g.out = w.du; g.ldo = F; g.aux = s.a; g.ldaux = F; g.amax_out = am + AM_DU;
     gemm<fp8e4>(gemm8_proj_dgrad, "gemm_proj_dgrad", g, 1, st);
   }
   wgrad8(gemm8_proj_wgrad, gemm8_proj_wgrad_acc, "gemm_proj_wgrad", w.g8t, am + AM_DY, s.a_8t, am + AM_A, Np, dwproj,
          C, F, N, acc, w.part, st);
-  quantize(w.du, N, F, am + AM_DU, w.du8, w.du8t, Np, true, st);
+  quantize(w.du, N, F, am + AM_DU, w.du8, w.du8t, Np, false, st);   // amax from gemm_proj_dgrad
   {  // dh2 = du W_fc
     GemmArgs g = gargs8(w.du8, F, am + AM_DU, wt_fc, F, am + AM_WFC, N, C, F);
     g.out = w.dh; g.ldo = C;
@@ -604,9 +606,9 @@ int bwd_fp8(const blk_cfg& c, const bf16* dy, const bf16* wqkv, const bf16* wo, 
   {
     Timed t("rmsnorm_bwd", st);
     hipLaunchKernelGGL(rmsnorm_bwd_kernel<bf16>, dim3(row_blocks(N)), dim3(256), 0, st, dy, (const bf16*)w.dh,
-                       (const bf16*)s.h2, (const float*)s.r2, w.dy1, N, C);
+                       (const bf16*)s.h2, (const float*)s.r2, w.dy1, N, C, am + AM_DY1);
   }
-  quantize(w.dy1, N, C, am + AM_DY1, w.g8, w.g8t, Np, true, st);
+  quantize(w.dy1, N, C, am + AM_DY1, w.g8, w.g8t, Np, false, st);   // amax from rmsnorm_bwd
   {  // do = dy1 W_o
     GemmArgs g = gargs8(w.g8, C, am + AM_DY1, wt_o, C, am + AM_WO, N, C, C);
     g.out = w.dO; g.ldo = C;
@@ -619,6 +621,7 @@ int bwd_fp8(const blk_cfg& c, const bf16* dy, const bf16* wqkv, const bf16* wo, 
     AttnArgs a = attn_args<bf16>(c);
     a.qkv = s.qkv; a.lse = s.lse; a.dO = w.dO; a.delta = w.delta; a.dqkv = w.dqkv;
     a.rho = s.rho; a.cs = s.cs;   // QK-norm and rotary backward in the stores
+    a.amax_dqkv = am + AM_DQKV;
     constexpr int DKDV_LDS = 3 * (2 * fa::TILE + 2048);
     need_lds(reinterpret_cast<const void*>(attn_bwd_dkdv_bf16_kernel), DKDV_LDS);
     need_lds(reinterpret_cast<const void*>(attn_bwd_dq_bf16_kernel), fa::LDS);
@@ -632,7 +635,7 @@ int bwd_fp8(const blk_cfg& c, const bf16* dy, const bf16* wqkv, const bf16* wo, 
       hipLaunchKernelGGL(attn_bwd_dq_bf16_kernel, dim3(nqt * c.B * H), dim3(256), fa::LDS, st, a);
     }
   }
-  quantize(w.dqkv, N, 3 * C, am + AM_DQKV, w.dqkv8, w.dqkv8t, Np, true, st);
+  quantize(w.dqkv, N, 3 * C, am + AM_DQKV, w.dqkv8, w.dqkv8t, Np, false, st);   // amax from attention bwd
   {  // dh1 = dqkv W_qkv
     GemmArgs g = gargs8(w.dqkv8, 3 * C, am + AM_DQKV, wt_qkv, 3 * C, am + AM_WQKV, N, C, 3 * C);
     g.out = w.dh; g.ldo = C;

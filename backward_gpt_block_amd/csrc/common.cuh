@@ -104,6 +104,24 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Folds the wave's largest stored magnitude into *amax (float bits; a zero
+// word is the identity, and non-negative floats order like their bits).  m
+// is this lane's max |v| before rounding to T: rounding is monotone, so the
+// rounded maximum is the maximum of the rounded values.  Every lane of the
+// wave must call it.
+// Waves whose maximum does not exceed the word's current value (read at
+// device scope, so not a stale L1 copy) skip the atomic: once the word holds
+// the tensor's maximum almost no wave contends for it.  A stale, smaller read
+// only costs an extra atomic; within a kernel the word never decreases.
+template <typename T>
+__device__ __forceinline__ void amax_publish(unsigned* amax, float m) {
+  m = to_f32(from_f32<T>(wave_max(m)));
+  if ((threadIdx.x & 63) == 0) {
+    const unsigned cur = __hip_atomic_load(amax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (__float_as_uint(m) > cur) atomicMax(amax, __float_as_uint(m));
+  }
+}
+
 // LDS tiles are arrays of rows made of 16-byte chunks.  Chunk c of row r is
 // stored at chunk position c ^ swz(r): rows that are read together by the
 // 32 lanes of an MFMA fragment (consecutive rows) and rows written together

@@ -14,7 +14,8 @@ constexpr int MAXCH = 8;   // 16-byte chunks per lane a row kernel keeps in regi
 // and its glossary entry for RMSNorm, without the gain).
 template <typename T>
 __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const T* __restrict__ x, T* __restrict__ h,
-                                                          float* __restrict__ r, int N, int C, float eps) {
+                                                          float* __restrict__ r, int N, int C, float eps,
+                                                          unsigned* __restrict__ amax = nullptr) {
   constexpr int EL = Chunk<T>::N;
   const int lane = threadIdx.x & 63;
   const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -37,6 +38,7 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const T* __restrict__ 
   ss = wave_sum(ss);
   const float rr = 1.f / sqrtf(ss / (float)C + eps);
   if (lane == 0 && r) r[row] = rr;
+  float mx = 0.f;
 #pragma unroll
   for (int i = 0; i < MAXCH; ++i) {
     int ch = lane + i * 64;
@@ -44,10 +46,14 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const T* __restrict__ 
       float f[EL];
       Chunk<T>::unpack(c[i], f);
 #pragma unroll
-      for (int e = 0; e < EL; ++e) f[e] *= rr;
+      for (int e = 0; e < EL; ++e) {
+        f[e] *= rr;
+        mx = fmaxf(mx, fabsf(f[e]));
+      }
       st16(h + row * C + ch * EL, Chunk<T>::pack(f));
     }
   }
+  if (amax) amax_publish<T>(amax, mx);   // fp8 mode: the tensor's absolute maximum
 }
 
 // out = resid + r * (dh - hn * mean(dh * hn)): RMSNorm backward (hn is the
@@ -55,7 +61,8 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const T* __restrict__ 
 template <typename T>
 __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const T* __restrict__ resid, const T* __restrict__ dh,
                                                           const T* __restrict__ hn, const float* __restrict__ r,
-                                                          T* __restrict__ out, int N, int C) {
+                                                          T* __restrict__ out, int N, int C,
+                                                          unsigned* __restrict__ amax = nullptr) {
   constexpr int EL = Chunk<T>::N;
   const int lane = threadIdx.x & 63;
   const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -79,6 +86,7 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const T* __restrict__ 
   dot = wave_sum(dot);
   const float mean = dot / (float)C;
   const float rr = r[row];
+  float mx = 0.f;
 #pragma unroll
   for (int i = 0; i < MAXCH; ++i) {
     int ch = lane + i * 64;
@@ -88,10 +96,14 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const T* __restrict__ 
       Chunk<T>::unpack(ch_[i], b);
       Chunk<T>::unpack(ld16(resid + row * C + ch * EL), g);
 #pragma unroll
-      for (int e = 0; e < EL; ++e) g[e] += rr * (a[e] - b[e] * mean);
+      for (int e = 0; e < EL; ++e) {
+        g[e] += rr * (a[e] - b[e] * mean);
+        mx = fmaxf(mx, fabsf(g[e]));
+      }
       st16(out + row * C + ch * EL, Chunk<T>::pack(g));
     }
   }
+  if (amax) amax_publish<T>(amax, mx);   // fp8 mode: the tensor's absolute maximum
 }
 
 // cs[t][i] = (cos, sin) of t * base^(-2i/D), i < D/2, computed in double

@@ -66,9 +66,10 @@ __global__ __launch_bounds__(256) void quant_kernel(const bf16* __restrict__ x, 
 // qT[c][r] = e4m3(x[r][c] * 448/amax) for a rows x cols bf16 matrix (cols %
 // 64 == 0); qT has leading dimension ldT >= rows (a multiple of 64) and the
 // padding columns rows..ldT-1 are written as 0.  64 x 64 tiles through LDS.
+// When q is given, the row-major codes q[r][c] are written in the same pass.
 __global__ __launch_bounds__(256) void quant_trans_kernel(const bf16* __restrict__ x, int rows, int cols,
                                                           const unsigned* __restrict__ amax, uint8_t* __restrict__ qT,
-                                                          int ldT) {
+                                                          int ldT, uint8_t* __restrict__ q) {
   __shared__ uint8_t t[64][65];
   const float inv = quant_inv(amax_value(amax));
   const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
@@ -83,12 +84,16 @@ __global__ __launch_bounds__(256) void quant_trans_kernel(const bf16* __restrict
 #pragma unroll
       for (int e = 0; e < 8; ++e) f[e] = 0.f;
     }
+    u32x2 row8;
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
       const uint32_t two = e4m3x2(f[e] * inv, f[e + 1] * inv);
       t[tx * 8 + e][r] = (uint8_t)(two & 0xff);
       t[tx * 8 + e + 1][r] = (uint8_t)(two >> 8);
+      if (e < 4) row8[0] = e == 0 ? two : (row8[0] | (two << 16));
+      else row8[1] = e == 4 ? two : (row8[1] | (two << 16));
     }
+    if (q && r0 + r < rows) st8(q + (long)(r0 + r) * cols + c0 + tx * 8, row8);
   }
   __syncthreads();
   // write: row c of qT gets 64 bytes (r0..r0+63); 4 threads x 16 bytes per row

@@ -56,6 +56,7 @@ struct GemmArgs {
   const float2* cs;
   float* rho;
   float* delta;
+  unsigned* amax_out;   // fp8 mode: absolute maximum of the stored output (float bits), or null
   int T, H, C;
   float eps;
 };
@@ -203,7 +204,7 @@ __device__ __forceinline__ void tile_coords(const GemmArgs& g, int& tm, int& tn,
 // ---- epilogue ------------------------------------------------------------------
 // 8 consecutive results of one row (fp32, already scaled) -> memory.
 template <typename TO, int EPI>
-__device__ __forceinline__ void epi8(const GemmArgs& g, int split, int row, int col, float* f) {
+__device__ __forceinline__ void epi8(const GemmArgs& g, int split, int row, int col, float* f, float& mx) {
   if constexpr (EPI == EPI_F32 || EPI == EPI_F32_ADD) {
     float* p = static_cast<float*>(g.out) + (EPI == EPI_F32 ? (long)split * g.M * g.ldo : 0L) + (long)row * g.ldo + col;
     u32x4 a = Chunk<float>::pack(f), b = Chunk<float>::pack(f + 4);
@@ -257,14 +258,16 @@ __device__ __forceinline__ void epi8(const GemmArgs& g, int split, int row, int 
       float xv[8];
 #pragma unroll
       for (int h = 0; h < 8 / EL; ++h) Chunk<TO>::unpack(ld16(x + h * EL), xv + h * EL);
-#pragma unroll
       // ReLU^2 derivative 2 max(u,0) recovered from the stored a = max(u,0)^2
+#pragma unroll
       for (int e = 0; e < 8; ++e) f[e] = (EPI == EPI_RESID) ? xv[e] + f[e] : f[e] * 2.f * __builtin_amdgcn_sqrtf(xv[e]);
     }
     if constexpr (EPI == EPI_RELU2) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) { const float p = fmaxf(f[e], 0.f); f[e] = p * p; }
     }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(f[e]));
 #pragma unroll
     for (int h = 0; h < 8 / EL; ++h) st16(o + h * EL, Chunk<TO>::pack(f + h * EL));
     if constexpr (EPI == EPI_DELTA) {
@@ -304,6 +307,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[4][4],
     alpha *= (a > 0.f ? a / 448.f : 1.f) * (b > 0.f ? b / 448.f : 1.f);
   }
   char* wreg = smem + wave * 32768;
+  float mx = 0.f;
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     __syncthreads();
@@ -326,9 +330,10 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[4][4],
       Chunk<float>::unpack(ld16(wreg + epi_off(row, 2 * cg + 1)), f + 4);
       const int grow = m0 + wm * 128 + pass * 64 + row;
       const int gcol = n0 + wn * 128 + cg * 8;
-      if (grow < g.M && gcol < g.N) epi8<TO, EPI>(g, split, grow, gcol, f);
+      if (grow < g.M && gcol < g.N) epi8<TO, EPI>(g, split, grow, gcol, f, mx);
     }
   }
+  if (g.amax_out) amax_publish<TO>(g.amax_out, mx);
 }
 
 // ---- main body -------------------------------------------------------------------
