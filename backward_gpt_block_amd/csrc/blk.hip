@@ -666,14 +666,13 @@ int check_dcfg(const blk_dcfg* c) {
 
 struct DecSplit { int S, cps; };
 
-// K-splits of a skinny GEMM: enough workgroups for about one per CU, at
-// least 4 K-steps (one per wave) per split.
+// K-splits of a skinny GEMM: one 64-wide K-step per wave (4 per workgroup),
+// so each wave issues all its loads at once; the splits' fp32 partials are
+// summed by the row-wise epilogue kernels.
 DecSplit dec_split(int M, int N, int K) {
-  const int tiles = (N / dec::NBLK) * ((M + dec::MBLK - 1) / dec::MBLK);
+  (void)M; (void)N;
   const int ks = K / dec::KCH;
-  int S = (256 + tiles - 1) / tiles;
-  S = std::max(1, std::min(S, std::max(1, ks / 4)));
-  const int cps = (ks + S - 1) / S;
+  const int cps = std::min(4, ks);
   return {(ks + cps - 1) / cps, cps};
 }
 

@@ -121,9 +121,17 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(const bf16* __restrict
   }
 }
 
+// Sum of the S split partials of one output, in split order.  Loads are
+// issued eight at a time so their latencies overlap.
 __device__ __forceinline__ float sum_parts(const float* __restrict__ part, int S, long stride, long idx) {
   float v = 0.f;
-  for (int s = 0; s < S; ++s) v += part[s * stride + idx];
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = s0 + i < S ? part[(s0 + i) * stride + idx] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v += x[i];
+  }
   return v;
 }
 

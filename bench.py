@@ -68,6 +68,21 @@ def site_flops(sh) -> dict:
     return g
 
 
+def site_bytes(sh) -> dict:
+    """Algorithmic HBM bytes per step of the memory-bound launch sites (all
+    launches of the site in one step).  fp8 quantiser: weights read for the
+    amax and for the codes (2 + 2 B) and written as codes (1 B), and read
+    again for the transposed codes of the backward (2 + 1 B); activations
+    whose maximum the producer folds in read once (2 B) and written as
+    row-major and transposed codes (1 + 1 B); dY read twice (amax, codes)."""
+    N, C, F = sh.B * sh.T, sh.C, sh.F
+    out = {"rmsnorm_fwd": 2.0 * (2 * N * C * 2 + N * 4), "rmsnorm_bwd": 2.0 * (4 * N * C * 2)}
+    if sh.gemm == "fp8":
+        w = 4 * C * C + 2 * C * F
+        out["fp8_quantize"] = float(w * (5 + 3) + N * C * (3 * 4 + 6 + 4 + 3 * 4) + N * F * (4 + 4))
+    return out
+
+
 def cpu_baseline(sh, inp, budget_s: float = 12.0) -> dict:
     """Oracle forward + backward on whole sequences of the workload until the
     budget is spent (at least one sequence)."""
@@ -237,12 +252,23 @@ def bench_train(args) -> int:
                 "frac": round(achieved / peak, 4), "traffic": measured_traffic(dname, args.workload), "kernel": dname,
                 "avg_launch_ms": round(davg_ms, 4), "flops_per_launch": fl[dname]}
     else:
+        sb = site_bytes(sh)
         roof = {"bound": "hbm", "achieved": None, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": None,
-                "traffic": None, "kernel": dname, "avg_launch_ms": round(davg_ms, 4)}
+                "traffic": measured_traffic(dname, args.workload), "kernel": dname, "avg_launch_ms": round(davg_ms, 4)}
+        if dname in sb:   # bytes of all the site's launches in a step over their time in a step
+            gbs = sb[dname] / (dtot / args.steps * 1e-3) / 1e9
+            roof.update(achieved=round(gbs, 1), frac=round(gbs / HBM_PEAK_GBS, 4),
+                        bytes_per_step=sb[dname], launches_per_step=dcnt // args.steps)
 
     tokens = sh.B * sh.T
     tflops = step_flops(sh) / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS["bf16" if dt == "bf16" else dt]
+    frac = tflops / peak
+    if sh.gemm == "fp8":
+        # mixed roofline: the linear layers at the fp8 dense peak, attention at the bf16 one
+        N, C, T = sh.B * sh.T, sh.C, sh.T
+        t_star = N * 72.0 * C * C / (PEAK_TFLOPS["fp8"] * 1e12) + N * 6.0 * C * (T + 1) / (PEAK_TFLOPS["bf16"] * 1e12)
+        frac = t_star / (ms * 1e-3)
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
@@ -251,10 +277,11 @@ def bench_train(args) -> int:
     out = {
         "metric": METRIC, "value": round(tokens / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": dt, "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3+bf16" if sh.gemm == "fp8" else dt,
+        "data": "synthetic",
         "config": {"workload": args.workload, "B": sh.B, "T": sh.T, "C": sh.C, "H": sh.H, "D": sh.D, "F": sh.F,
                    "gemm": sh.gemm, "tokens_per_step": tokens, "parallelism": "none (1 GPU)"},
-        "tflops": round(tflops, 2), "frac_of_peak": round(tflops / peak, 4),
+        "tflops": round(tflops, 2), "frac_of_peak": round(frac, 4),
         "tflops_nanochat_convention": round(step_flops_nanochat(sh) / (ms * 1e-3) / 1e12, 2),
         "roofline": roof, "cpu_baseline": cpu,
     }
