@@ -248,6 +248,20 @@ void gemm(void (*kern)(GemmArgs), const char* name, GemmArgs g, int splits, hipS
   hipLaunchKernelGGL(kern, dim3(g.tiles_m * g.tiles_n, splits), dim3(256), LDS, st, g);
 }
 
+// Forward and input-gradient GEMMs (eight-wave kernels, no split): K and both
+// leading dimensions are multiples of 128 elements here (C = 128 H, F = 4 C),
+// as the kernels' k-step of 128 bytes requires.
+template <typename TI>
+void gemm_pp(void (*kern)(GemmArgs), const char* name, GemmArgs g, hipStream_t st) {
+  constexpr int LDS = GemmTile<TI>::LDS;
+  need_lds(reinterpret_cast<const void*>(kern), LDS);
+  g.tiles_m = (g.M + 255) / 256;
+  g.tiles_n = (g.N + 255) / 256;
+  g.k_split = g.K;
+  Timed t(name, st);
+  hipLaunchKernelGGL(kern, dim3(g.tiles_m * g.tiles_n, 1), dim3(512), LDS, st, g);
+}
+
 GemmArgs gargs(const void* A, long lda, const void* B, long ldb, int M, int N, int K) {
   GemmArgs g{};
   g.A = A; g.lda = lda; g.B = B; g.ldb = ldb;
@@ -317,7 +331,7 @@ int fwd_impl(const blk_cfg& c, const T* x, const T* wqkv, const T* wo, const T* 
     GemmArgs g = gargs(s.h1, C, wqkv, C, N, 3 * C, C);
     g.out = s.qkv; g.ldo = 3 * C;
     rope_args(g, c, s.cs, s.rho);
-    gemm<T>(gemm_qkv_fwd<T>, "gemm_qkv_fwd", g, 1, st);
+    gemm_pp<T>(gemm_qkv_fwd<T>, "gemm_qkv_fwd", g, st);
   }
   {  // 5 causal attention
     AttnArgs a = attn_args<T>(c);
@@ -336,7 +350,7 @@ int fwd_impl(const blk_cfg& c, const T* x, const T* wqkv, const T* wo, const T* 
   {  // 6 y1 = x + o W_o^T   (y1 is kept in y)
     GemmArgs g = gargs(s.o, C, wo, C, N, C, C);
     g.out = y; g.ldo = C; g.aux = x; g.ldaux = C;
-    gemm<T>(gemm_o_fwd<T>, "gemm_o_fwd", g, 1, st);
+    gemm_pp<T>(gemm_o_fwd<T>, "gemm_o_fwd", g, st);
   }
   {  // 7 h2 = rmsnorm(y1)
     Timed t("rmsnorm_fwd", st);
@@ -346,12 +360,12 @@ int fwd_impl(const blk_cfg& c, const T* x, const T* wqkv, const T* wo, const T* 
   {  // 8 a = relu(h2 W_fc^T)^2 (u itself is not kept: the backward uses 2 sqrt(a))
     GemmArgs g = gargs(s.h2, C, wfc, C, N, F, C);
     g.out = s.a; g.ldo = F;
-    gemm<T>(gemm_fc_fwd<T>, "gemm_fc_fwd", g, 1, st);
+    gemm_pp<T>(gemm_fc_fwd<T>, "gemm_fc_fwd", g, st);
   }
   {  // 9 y = y1 + a W_proj^T   (in place on y)
     GemmArgs g = gargs(s.a, F, wproj, F, N, C, F);
     g.out = y; g.ldo = C; g.aux = y; g.ldaux = C;
-    gemm<T>(gemm_proj_fwd<T>, "gemm_proj_fwd", g, 1, st);
+    gemm_pp<T>(gemm_proj_fwd<T>, "gemm_proj_fwd", g, st);
   }
   return launch_status();
 }
@@ -381,7 +395,7 @@ int bwd_impl(const blk_cfg& c, const T* dy, const T* x, const T* wqkv, const T* 
   {  // 9: du = (dy W_proj) * 2 max(u, 0), with max(u, 0) = sqrt(a)
     GemmArgs g = gargs(dy, C, wt_proj, C, N, F, C);
     g.out = w.du; g.ldo = F; g.aux = s.a; g.ldaux = F;
-    gemm<T>(gemm_proj_dgrad<T>, "gemm_proj_dgrad", g, 1, st);
+    gemm_pp<T>(gemm_proj_dgrad<T>, "gemm_proj_dgrad", g, st);
   }
   //    dW_proj = dy^T a
   wgrad<T>(gemm_proj_wgrad<T>, gemm_proj_wgrad_acc<T>, "gemm_proj_wgrad", dy, s.a, dwproj, C, F, N, acc, w.part,
@@ -389,7 +403,7 @@ int bwd_impl(const blk_cfg& c, const T* dy, const T* x, const T* wqkv, const T* 
   {  // 8: dh2 = du W_fc
     GemmArgs g = gargs(w.du, F, wt_fc, F, N, C, F);
     g.out = w.dh; g.ldo = C;
-    gemm<T>(gemm_fc_dgrad<T>, "gemm_fc_dgrad", g, 1, st);
+    gemm_pp<T>(gemm_fc_dgrad<T>, "gemm_fc_dgrad", g, st);
   }
   //    dW_fc = du^T h2
   wgrad<T>(gemm_fc_wgrad<T>, gemm_fc_wgrad_acc<T>, "gemm_fc_wgrad", w.du, s.h2, dwfc, F, C, N, acc, w.part, st);
@@ -402,7 +416,7 @@ int bwd_impl(const blk_cfg& c, const T* dy, const T* x, const T* wqkv, const T* 
     GemmArgs g = gargs(w.dy1, C, wt_o, C, N, C, C);
     g.out = w.dO; g.ldo = C;
     delta_args(g, c, s.o, w.delta);
-    gemm<T>(gemm_o_dgrad<T>, "gemm_o_dgrad", g, 1, st);
+    gemm_pp<T>(gemm_o_dgrad<T>, "gemm_o_dgrad", g, st);
   }
   //    dW_o = dy1^T o
   wgrad<T>(gemm_o_wgrad<T>, gemm_o_wgrad_acc<T>, "gemm_o_wgrad", w.dy1, s.o, dwo, C, C, N, acc, w.part, st);
@@ -445,7 +459,7 @@ int bwd_impl(const blk_cfg& c, const T* dy, const T* x, const T* wqkv, const T* 
   {  // 2: dh1 = dqkv W_qkv
     GemmArgs g = gargs(w.dqkv, 3 * C, wt_qkv, 3 * C, N, C, 3 * C);
     g.out = w.dh; g.ldo = C;
-    gemm<T>(gemm_qkv_dgrad<T>, "gemm_qkv_dgrad", g, 1, st);
+    gemm_pp<T>(gemm_qkv_dgrad<T>, "gemm_qkv_dgrad", g, st);
   }
   //    dW_qkv = dqkv^T h1
   wgrad<T>(gemm_qkv_wgrad<T>, gemm_qkv_wgrad_acc<T>, "gemm_qkv_wgrad", w.dqkv, s.h1, dwqkv, 3 * C, C, N, acc,
@@ -534,7 +548,7 @@ int fwd_fp8(const blk_cfg& c, const bf16* x, const bf16* wqkv, const bf16* wo, c
     GemmArgs g = gargs8(f.h1, C, am + AM_H1, f.wqkv, C, am + AM_WQKV, N, 3 * C, C);
     g.out = s.qkv; g.ldo = 3 * C;
     rope_args(g, c, s.cs, s.rho);
-    gemm<fp8e4>(gemm8_qkv_fwd, "gemm_qkv_fwd", g, 1, st);
+    gemm_pp<fp8e4>(gemm8_qkv_fwd, "gemm_qkv_fwd", g, st);
   }
   {
     AttnArgs a = attn_args<bf16>(c);
@@ -548,7 +562,7 @@ int fwd_fp8(const blk_cfg& c, const bf16* x, const bf16* wqkv, const bf16* wo, c
   {
     GemmArgs g = gargs8(f.o, C, am + AM_O, f.wo, C, am + AM_WO, N, C, C);
     g.out = y; g.ldo = C; g.aux = x; g.ldaux = C;
-    gemm<fp8e4>(gemm8_o_fwd, "gemm_o_fwd", g, 1, st);
+    gemm_pp<fp8e4>(gemm8_o_fwd, "gemm_o_fwd", g, st);
   }
   {
     Timed t("rmsnorm_fwd", st);
@@ -559,13 +573,13 @@ int fwd_fp8(const blk_cfg& c, const bf16* x, const bf16* wqkv, const bf16* wo, c
   {
     GemmArgs g = gargs8(f.h2, C, am + AM_H2, f.wfc, C, am + AM_WFC, N, F, C);
     g.out = s.a; g.ldo = F; g.amax_out = am + AM_A;
-    gemm<fp8e4>(gemm8_fc_fwd, "gemm_fc_fwd", g, 1, st);
+    gemm_pp<fp8e4>(gemm8_fc_fwd, "gemm_fc_fwd", g, st);
   }
   quantize(s.a, N, F, am + AM_A, f.a, s.a_8t, Np, false, st);       // amax from gemm_fc_fwd
   {
     GemmArgs g = gargs8(f.a, F, am + AM_A, f.wproj, F, am + AM_WPROJ, N, C, F);
     g.out = y; g.ldo = C; g.aux = y; g.ldaux = C;
-    gemm<fp8e4>(gemm8_proj_fwd, "gemm_proj_fwd", g, 1, st);
+    gemm_pp<fp8e4>(gemm8_proj_fwd, "gemm_proj_fwd", g, st);
   }
   return launch_status();
 }
@@ -591,7 +605,7 @@ int bwd_fp8(const blk_cfg& c, const bf16* dy, const bf16* wqkv, const bf16* wo, 
   {  // du = (dy W_proj) * 2 max(u, 0), with max(u, 0) = sqrt(a)
     GemmArgs g = gargs8(w.g8, C, am + AM_DY, wt_proj, C, am + AM_WPROJ, N, F, C);
     g.out = w.du; g.ldo = F; g.aux = s.a; g.ldaux = F; g.amax_out = am + AM_DU;
-    gemm<fp8e4>(gemm8_proj_dgrad, "gemm_proj_dgrad", g, 1, st);
+    gemm_pp<fp8e4>(gemm8_proj_dgrad, "gemm_proj_dgrad", g, st);
   }
   wgrad8(gemm8_proj_wgrad, gemm8_proj_wgrad_acc, "gemm_proj_wgrad", w.g8t, am + AM_DY, s.a_8t, am + AM_A, Np, dwproj,
          C, F, N, acc, w.part, st);
@@ -599,7 +613,7 @@ int bwd_fp8(const blk_cfg& c, const bf16* dy, const bf16* wqkv, const bf16* wo, 
   {  // dh2 = du W_fc
     GemmArgs g = gargs8(w.du8, F, am + AM_DU, wt_fc, F, am + AM_WFC, N, C, F);
     g.out = w.dh; g.ldo = C;
-    gemm<fp8e4>(gemm8_fc_dgrad, "gemm_fc_dgrad", g, 1, st);
+    gemm_pp<fp8e4>(gemm8_fc_dgrad, "gemm_fc_dgrad", g, st);
   }
   wgrad8(gemm8_fc_wgrad, gemm8_fc_wgrad_acc, "gemm_fc_wgrad", w.du8t, am + AM_DU, s.h2_8t, am + AM_H2, Np, dwfc, F, C,
          N, acc, w.part, st);
@@ -613,7 +627,7 @@ int bwd_fp8(const blk_cfg& c, const bf16* dy, const bf16* wqkv, const bf16* wo, 
     GemmArgs g = gargs8(w.g8, C, am + AM_DY1, wt_o, C, am + AM_WO, N, C, C);
     g.out = w.dO; g.ldo = C;
     delta_args(g, c, s.o, w.delta);
-    gemm<fp8e4>(gemm8_o_dgrad, "gemm_o_dgrad", g, 1, st);
+    gemm_pp<fp8e4>(gemm8_o_dgrad, "gemm_o_dgrad", g, st);
   }
   wgrad8(gemm8_o_wgrad, gemm8_o_wgrad_acc, "gemm_o_wgrad", w.g8t, am + AM_DY1, s.o_8t, am + AM_O, Np, dwo, C, C, N,
          acc, w.part, st);
@@ -639,7 +653,7 @@ int bwd_fp8(const blk_cfg& c, const bf16* dy, const bf16* wqkv, const bf16* wo, 
   {  // dh1 = dqkv W_qkv
     GemmArgs g = gargs8(w.dqkv8, 3 * C, am + AM_DQKV, wt_qkv, 3 * C, am + AM_WQKV, N, C, 3 * C);
     g.out = w.dh; g.ldo = C;
-    gemm<fp8e4>(gemm8_qkv_dgrad, "gemm_qkv_dgrad", g, 1, st);
+    gemm_pp<fp8e4>(gemm8_qkv_dgrad, "gemm_qkv_dgrad", g, st);
   }
   wgrad8(gemm8_qkv_wgrad, gemm8_qkv_wgrad_acc, "gemm_qkv_wgrad", w.dqkv8t, am + AM_DQKV, s.h1_8t, am + AM_H1, Np,
          dwqkv, 3 * C, C, N, acc, w.part, st);

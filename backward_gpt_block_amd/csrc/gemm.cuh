@@ -183,16 +183,15 @@ __device__ __forceinline__ typename Mfma<TI>::frag load_frag(const char* lds, in
 
 // Workgroup index -> (tile_m, tile_n, split).  Workgroups are dealt round
 // robin to the 8 XCDs; the remap gives each XCD a contiguous run of logical
-// tiles, and tiles are walked in groups of 8 m-tiles so that an XCD's
+// tiles, and tiles are walked in groups of GROUP m-tiles so that an XCD's
 // concurrent tiles share A rows and B columns in its L2.
-__device__ __forceinline__ void tile_coords(const GemmArgs& g, int& tm, int& tn, int& split) {
+__device__ __forceinline__ void tile_coords(const GemmArgs& g, int& tm, int& tn, int& split, int GROUP = 8) {
   const int per_split = g.tiles_m * g.tiles_n;
   const int total = per_split * gridDim.y;
   int pid = blockIdx.x + blockIdx.y * gridDim.x;
   if (total % 8 == 0) pid = (pid % 8) * (total / 8) + pid / 8;
   split = pid / per_split;
   int t = pid % per_split;
-  const int GROUP = 8;
   int group = t / (GROUP * g.tiles_n);
   int first_m = group * GROUP;
   int gsize = min(g.tiles_m - first_m, GROUP);
@@ -202,8 +201,15 @@ __device__ __forceinline__ void tile_coords(const GemmArgs& g, int& tm, int& tn,
 }
 
 // ---- epilogue ------------------------------------------------------------------
+// Output stores; NT marks them non-temporal (streamed past the caches).
+template <bool NT>
+__device__ __forceinline__ void st16_out(void* p, u32x4 v) {
+  if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+  else st16(p, v);
+}
+
 // 8 consecutive results of one row (fp32, already scaled) -> memory.
-template <typename TO, int EPI>
+template <typename TO, int EPI, bool NT = false>
 __device__ __forceinline__ void epi8(const GemmArgs& g, int split, int row, int col, float* f, float& mx) {
   if constexpr (EPI == EPI_F32 || EPI == EPI_F32_ADD) {
     float* p = static_cast<float*>(g.out) + (EPI == EPI_F32 ? (long)split * g.M * g.ldo : 0L) + (long)row * g.ldo + col;
@@ -249,7 +255,7 @@ __device__ __forceinline__ void epi8(const GemmArgs& g, int split, int row, int 
       if (cg == 0) g.rho[((long)which * g.M + row) * g.H + (col % g.C) / 128] = r;
     }
 #pragma unroll
-    for (int h = 0; h < 8 / EL; ++h) st16(o + h * EL, Chunk<TO>::pack(f + h * EL));
+    for (int h = 0; h < 8 / EL; ++h) st16_out<NT>(o + h * EL, Chunk<TO>::pack(f + h * EL));
   } else {
     constexpr int EL = Chunk<TO>::N;     // 8 bf16 or 4 float per chunk
     TO* o = static_cast<TO*>(g.out) + (long)row * g.ldo + col;
@@ -269,7 +275,7 @@ __device__ __forceinline__ void epi8(const GemmArgs& g, int split, int row, int 
 #pragma unroll
     for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(f[e]));
 #pragma unroll
-    for (int h = 0; h < 8 / EL; ++h) st16(o + h * EL, Chunk<TO>::pack(f + h * EL));
+    for (int h = 0; h < 8 / EL; ++h) st16_out<NT>(o + h * EL, Chunk<TO>::pack(f + h * EL));
     if constexpr (EPI == EPI_DELTA) {
       // the dot uses the stored (rounded) values, as the attention kernels read them
       const TO* x = static_cast<const TO*>(g.aux) + (long)row * g.ldaux + col;
@@ -435,6 +441,216 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   epilogue<TO, EPI>(g, acc, smem, m0, n0, split, wave, lane);
 }
 
+// ---- eight-wave ping-pong body (both operands k-contiguous) --------------------
+// Same 256 x 256 workgroup tile and LDS slab layout as the four-wave body
+// (two stages of 128-byte rows), eight waves.  Wave w = 4*grp + q computes
+// rows (q>>1)*128 + grp*64 .. +64 and columns (q&1)*128 .. +128 (2 x 4 MFMA
+// blocks).  The two groups (waves w and w+4 share a SIMD) take turns one
+// phase apart: while one group runs the MFMAs of half a k-step from
+// registers, the other reads its fragments of that half from LDS, so each
+// SIMD's matrix pipe has a wave feeding it while the other waits on LDS.
+// Per k-step kt (grp 0 | grp 1):
+//   A0: read (kt, half 0), issue kt+1's A rows | MFMAs (kt-1, 1), issue kt+1's B rows
+//   B0: MFMAs (kt, 0)                         | read (kt, 0)
+//   A1: read (kt, 1)                          | MFMAs (kt, 0)
+//   B1: MFMAs (kt, 1), wait for kt+1          | read (kt, 1), wait for kt+1
+// Stage kt+1 goes global -> LDS (whole 128-byte rows: one load instruction
+// covers 8 full cache lines) into the slot stage kt-1 vacated.  Requires K
+// and the split length to be multiples of the k-step and both leading
+// dimensions to be multiples of 128 bytes, so row offsets leave the chunk
+// bits free.  Output tiles are stored non-temporally: they are not read
+// again by this kernel and would only evict operand lines from L2.
+template <typename TI>
+struct PPStager {
+  i32x4 rs;        // buffer resource from the tile's first row
+  uint32_t x;      // byte offset (k = 0) of this lane's chunk in the wave's first 8-row group
+  uint32_t step;   // bytes between consecutive 8-row groups
+  // LDS row R = 64q + 8j + lane/8 holds at chunk position lane%8 the global
+  // chunk (lane%8) ^ swz(R) = (lane%8) ^ (lane/8) ^ j
+  __device__ __forceinline__ void init(const void* p, long ld, long rows, int r0, int q, int lane) {
+    const char* base = static_cast<const char*>(p) + (long)r0 * ld * (long)sizeof(TI);
+    const long left = rows > r0 ? (rows - r0) * ld * (long)sizeof(TI) : 0L;
+    rs = make_rsrc(base, (uint32_t)min(left, 0x7fffffffL));
+    x = (uint32_t)((64 * q + (lane >> 3)) * ld * (long)sizeof(TI)) + (uint32_t)(((lane & 7) ^ (lane >> 3)) << 4);
+    step = (uint32_t)(8 * ld * (long)sizeof(TI));
+  }
+  // rows past the matrix edge have offsets >= the resource size and read
+  // zero; so does a whole stage past the end of k (live = false)
+  __device__ __forceinline__ void issue(char* sub, int k0_bytes, bool live, int q) const {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t off = (x ^ (uint32_t)(j << 4)) + (uint32_t)j * step + (uint32_t)k0_bytes;
+      lds_u32* dst = (lds_u32*)(sub + __builtin_amdgcn_readfirstlane((8 * q + j) * 1024));
+      raw_buffer_load_lds(rs, dst, 16, live ? (int)off : (int)0x80000000u, 0, 0, 0);
+    }
+  }
+};
+
+// Workgroup barrier that is also a hard scheduling boundary: no instruction
+// (MFMAs included) moves across it, and no memory wait is implied.
+__device__ __forceinline__ void wg_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <typename TO, int EPI>
+__device__ __forceinline__ void epilogue_pp(const GemmArgs& g, f32x16 (&acc)[2][4], char* smem, int m0, int n0,
+                                            int split, int wave, int lane) {
+  const int grp = wave >> 2, q = wave & 3;
+  float alpha = g.alpha;
+  if (g.amax_a) {
+    const float a = __uint_as_float(*g.amax_a), b = __uint_as_float(*g.amax_b);
+    alpha *= (a > 0.f ? a / 448.f : 1.f) * (b > 0.f ? b / 448.f : 1.f);
+  }
+  // each wave parks 32 rows x 128 fp32 (16 KiB) at a time in its own region;
+  // LDS accesses of one wave complete in order, so no barrier is needed
+  char* wreg = smem + wave * 16384;
+  const int rbase = m0 + (q >> 1) * 128 + grp * 64, cbase = n0 + (q & 1) * 128;
+  float mx = 0.f;
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = acc_row(r, lane), col = j * 32 + (lane & 31);
+        *reinterpret_cast<float*>(wreg + epi_off(row, col >> 2) + (col & 3) * 4) = acc[pass][j][r] * alpha;
+      }
+#pragma unroll 4
+    for (int it = 0; it < 8; ++it) {
+      const int qq = it * 64 + lane;
+      const int row = qq >> 4, cg = qq & 15;
+      float f[8];
+      Chunk<float>::unpack(ld16(wreg + epi_off(row, 2 * cg)), f);
+      Chunk<float>::unpack(ld16(wreg + epi_off(row, 2 * cg + 1)), f + 4);
+      const int grow = rbase + pass * 32 + row, gcol = cbase + cg * 8;
+      if (grow < g.M && gcol < g.N) epi8<TO, EPI, true>(g, split, grow, gcol, f, mx);
+    }
+  }
+  if (g.amax_out) amax_publish<TO>(g.amax_out, mx);
+}
+
+template <typename TI, typename TO, int EPI>
+__device__ __forceinline__ void gemm_pp_body(const GemmArgs& g) {
+  typedef GemmTile<TI> G;
+  typedef Mfma<TI> MM;
+  constexpr int HS = G::BK / MM::KI / 2;                   // MFMA substeps per half k-step
+  constexpr int RD = 6 * HS * (sizeof(TI) == 1 ? 2 : 1);   // LDS reads per read phase
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int lane = threadIdx.x & 63;
+  // wave-uniform: the group's branch and its buffer resource live in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = wave >> 2, q = wave & 3;
+
+  int tm, tn, split;
+  tile_coords(g, tm, tn, split, 4);
+  const int m0 = tm * G::BM, n0 = tn * G::BN;
+  const int kbeg = split * g.k_split;
+  const int nk = (min(g.K, kbeg + g.k_split) - kbeg) / G::BK;
+
+  // grp 0 stages the A rows, grp 1 the B rows
+  PPStager<TI> st;
+  if (grp == 0) st.init(g.A, g.lda, g.M, m0, q, lane);
+  else st.init(g.B, g.ldb, g.N, n0, q, lane);
+  auto issue = [&](int kt) {
+    st.issue(smem + (kt & 1) * G::SLAB + grp * (G::BM * G::ROWB), (kbeg + kt * G::BK) * (int)sizeof(TI), kt < nk, q);
+  };
+
+  const int arow = (q >> 1) * 128 + grp * 64, brow = (q & 1) * 128;
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  typename MM::frag fa[HS][2], fb[HS][4];
+  auto read = [&](int kt, int h) {
+    const char* cur = smem + (kt & 1) * G::SLAB;
+#pragma unroll
+    for (int s = 0; s < HS; ++s) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) fa[s][i] = load_frag<TI>(cur, arow + 32 * i, h * HS + s, lane);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) fb[s][j] = load_frag<TI>(cur + G::BM * G::ROWB, brow + 32 * j, h * HS + s, lane);
+    }
+  };
+  auto mfma = [&]() {
+#pragma unroll
+    for (int s = 0; s < HS; ++s)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = MM::mma(fa[s][i], fb[s][j], acc[i][j]);
+  };
+
+  // A stage past the end (kt + 1 == nk) is issued with out-of-range offsets:
+  // it writes zeros into the free slot and keeps the loop free of branches
+  // that would split the instruction schedule.
+  if (nk > 0) {
+    issue(0);
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
+    wg_barrier();
+    if (grp == 0) {
+      for (int kt = 0; kt < nk; ++kt) {
+        issue(kt + 1);
+        read(kt, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);    // the 8 loads, then the LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
+        wg_barrier();
+        mfma();
+        wg_barrier();
+        read(kt, 1);
+        wg_barrier();
+        mfma();
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): stage kt+1's A rows have landed
+        wg_barrier();
+      }
+      wg_barrier();   // grp 1 runs the last half-step's MFMAs
+    } else {
+      // the slot is refilled after the stage's last barrier, so each read
+      // phase ends with its fragments in registers
+      auto tail = [&](int kt) {
+        read(kt, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+        wg_barrier();
+        mfma();
+        wg_barrier();
+        read(kt, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(0);        // fragments, and stage kt+1's B rows
+        wg_barrier();
+      };
+      issue(1);
+      wg_barrier();
+      tail(0);
+      for (int kt = 1; kt < nk; ++kt) {
+        issue(kt + 1);
+        mfma();
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {           // one load between MFMA pairs
+          __builtin_amdgcn_sched_group_barrier(0x008, HS, 0);
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+        wg_barrier();
+        tail(kt);
+      }
+      mfma();
+      wg_barrier();
+    }
+  }
+  // the past-the-end loads write zeros into LDS: let them land before the
+  // epilogue reuses it
+  __builtin_amdgcn_s_waitcnt(0x0f70);
+  wg_barrier();
+  epilogue_pp<TO, EPI>(g, acc, smem, m0, n0, split, wave, lane);
+}
+
 }  // namespace blk
 
 // One kernel symbol per call site of the block, so that traces and timings
@@ -444,16 +660,21 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   __global__ __launch_bounds__(256, 1) void NAME(GemmArgs g) {                   \
     gemm_body<T, TO, KA, KB, EPI>(g);                                           \
   }
+#define BLK_GEMM_PP_KERNEL(NAME, EPI, TO)                                         \
+  template <typename T>                                                         \
+  __global__ __launch_bounds__(512, 1) void NAME(GemmArgs g) {                   \
+    gemm_pp_body<T, TO, EPI>(g);                                                \
+  }
 
 namespace blk {
-BLK_GEMM_KERNEL(gemm_qkv_fwd, true, true, EPI_ROPE, T)
-BLK_GEMM_KERNEL(gemm_o_fwd, true, true, EPI_RESID, T)
-BLK_GEMM_KERNEL(gemm_fc_fwd, true, true, EPI_RELU2, T)
-BLK_GEMM_KERNEL(gemm_proj_fwd, true, true, EPI_RESID, T)
-BLK_GEMM_KERNEL(gemm_proj_dgrad, true, true, EPI_DRELU2, T)
-BLK_GEMM_KERNEL(gemm_fc_dgrad, true, true, EPI_STORE, T)
-BLK_GEMM_KERNEL(gemm_o_dgrad, true, true, EPI_DELTA, T)
-BLK_GEMM_KERNEL(gemm_qkv_dgrad, true, true, EPI_STORE, T)
+BLK_GEMM_PP_KERNEL(gemm_qkv_fwd, EPI_ROPE, T)
+BLK_GEMM_PP_KERNEL(gemm_o_fwd, EPI_RESID, T)
+BLK_GEMM_PP_KERNEL(gemm_fc_fwd, EPI_RELU2, T)
+BLK_GEMM_PP_KERNEL(gemm_proj_fwd, EPI_RESID, T)
+BLK_GEMM_PP_KERNEL(gemm_proj_dgrad, EPI_DRELU2, T)
+BLK_GEMM_PP_KERNEL(gemm_fc_dgrad, EPI_STORE, T)
+BLK_GEMM_PP_KERNEL(gemm_o_dgrad, EPI_DELTA, T)
+BLK_GEMM_PP_KERNEL(gemm_qkv_dgrad, EPI_STORE, T)
 BLK_GEMM_KERNEL(gemm_proj_wgrad, false, false, EPI_F32, float)
 BLK_GEMM_KERNEL(gemm_fc_wgrad, false, false, EPI_F32, float)
 BLK_GEMM_KERNEL(gemm_o_wgrad, false, false, EPI_F32, float)
@@ -470,16 +691,20 @@ BLK_GEMM_KERNEL(gemm_qkv_wgrad_acc, false, false, EPI_F32_ADD, float)
   __global__ __launch_bounds__(256, 1) void NAME(GemmArgs g) {                   \
     gemm_body<fp8e4, TO, true, true, EPI>(g);                                   \
   }
+#define BLK_GEMM8_PP_KERNEL(NAME, EPI, TO)                                        \
+  __global__ __launch_bounds__(512, 1) void NAME(GemmArgs g) {                   \
+    gemm_pp_body<fp8e4, TO, EPI>(g);                                            \
+  }
 
 namespace blk {
-BLK_GEMM8_KERNEL(gemm8_qkv_fwd, EPI_ROPE, bf16)
-BLK_GEMM8_KERNEL(gemm8_o_fwd, EPI_RESID, bf16)
-BLK_GEMM8_KERNEL(gemm8_fc_fwd, EPI_RELU2, bf16)
-BLK_GEMM8_KERNEL(gemm8_proj_fwd, EPI_RESID, bf16)
-BLK_GEMM8_KERNEL(gemm8_proj_dgrad, EPI_DRELU2, bf16)
-BLK_GEMM8_KERNEL(gemm8_fc_dgrad, EPI_STORE, bf16)
-BLK_GEMM8_KERNEL(gemm8_o_dgrad, EPI_DELTA, bf16)
-BLK_GEMM8_KERNEL(gemm8_qkv_dgrad, EPI_STORE, bf16)
+BLK_GEMM8_PP_KERNEL(gemm8_qkv_fwd, EPI_ROPE, bf16)
+BLK_GEMM8_PP_KERNEL(gemm8_o_fwd, EPI_RESID, bf16)
+BLK_GEMM8_PP_KERNEL(gemm8_fc_fwd, EPI_RELU2, bf16)
+BLK_GEMM8_PP_KERNEL(gemm8_proj_fwd, EPI_RESID, bf16)
+BLK_GEMM8_PP_KERNEL(gemm8_proj_dgrad, EPI_DRELU2, bf16)
+BLK_GEMM8_PP_KERNEL(gemm8_fc_dgrad, EPI_STORE, bf16)
+BLK_GEMM8_PP_KERNEL(gemm8_o_dgrad, EPI_DELTA, bf16)
+BLK_GEMM8_PP_KERNEL(gemm8_qkv_dgrad, EPI_STORE, bf16)
 BLK_GEMM8_KERNEL(gemm8_proj_wgrad, EPI_F32, float)
 BLK_GEMM8_KERNEL(gemm8_fc_wgrad, EPI_F32, float)
 BLK_GEMM8_KERNEL(gemm8_o_wgrad, EPI_F32, float)
