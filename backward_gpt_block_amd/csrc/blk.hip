@@ -8,6 +8,7 @@
 #include <cstring>
 #include <mutex>
 #include <set>
+#include <type_traits>
 #include <vector>
 
 #include "../../include/blk.h"
@@ -229,8 +230,9 @@ void need_lds(const void* kern, int bytes) {
     hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
 
+// threads: 256 for the four-wave GEMM body, 512 for the eight-wave one
 template <typename TI>
-void gemm(void (*kern)(GemmArgs), const char* name, GemmArgs g, int splits, hipStream_t st) {
+void gemm(void (*kern)(GemmArgs), const char* name, GemmArgs g, int splits, hipStream_t st, int threads = 256) {
   constexpr int LDS = GemmTile<TI>::LDS;
   need_lds(reinterpret_cast<const void*>(kern), LDS);
   g.tiles_m = (g.M + 255) / 256;
@@ -245,7 +247,7 @@ void gemm(void (*kern)(GemmArgs), const char* name, GemmArgs g, int splits, hipS
     splits = (g.K + g.k_split - 1) / g.k_split;
   }
   Timed t(name, st);
-  hipLaunchKernelGGL(kern, dim3(g.tiles_m * g.tiles_n, splits), dim3(256), LDS, st, g);
+  hipLaunchKernelGGL(kern, dim3(g.tiles_m * g.tiles_n, splits), dim3(threads), LDS, st, g);
 }
 
 // Forward and input-gradient GEMMs (eight-wave kernels, no split): K and both
@@ -253,13 +255,7 @@ void gemm(void (*kern)(GemmArgs), const char* name, GemmArgs g, int splits, hipS
 // as the kernels' k-step of 128 bytes requires.
 template <typename TI>
 void gemm_pp(void (*kern)(GemmArgs), const char* name, GemmArgs g, hipStream_t st) {
-  constexpr int LDS = GemmTile<TI>::LDS;
-  need_lds(reinterpret_cast<const void*>(kern), LDS);
-  g.tiles_m = (g.M + 255) / 256;
-  g.tiles_n = (g.N + 255) / 256;
-  g.k_split = g.K;
-  Timed t(name, st);
-  hipLaunchKernelGGL(kern, dim3(g.tiles_m * g.tiles_n, 1), dim3(512), LDS, st, g);
+  gemm<TI>(kern, name, g, 1, st, 512);
 }
 
 GemmArgs gargs(const void* A, long lda, const void* B, long ldb, int M, int N, int K) {
@@ -280,18 +276,24 @@ void delta_args(GemmArgs& g, const blk_cfg& c, const void* o, float* delta) {
 }
 
 // Weight gradient dW[M, N] (+)= sum_t G[t, m] X[t, n]  (G: [K, M], X: [K, N]).
+// bf16 operands with K a multiple of the k-step run on the eight-wave body
+// (kernels kp / kp_acc), others on the four-wave one.
+typedef void (*GemmKernel)(GemmArgs);
 template <typename T>
-void wgrad(void (*kern)(GemmArgs), void (*kern_acc)(GemmArgs), const char* name, const T* G, const T* X, float* dW,
-           int M, int N, int K, int accumulate, float* part, hipStream_t st) {
+void wgrad(GemmKernel kern, GemmKernel kern_acc, GemmKernel kp, GemmKernel kp_acc, const char* name, const T* G,
+           const T* X, float* dW, int M, int N, int K, int accumulate, float* part, hipStream_t st) {
   GemmArgs g = gargs(G, M, X, N, M, N, K);
+  const bool pp = std::is_same<T, bf16>::value && K % GemmTile<T>::BK == 0;
+  const int threads = pp ? 512 : 256;
+  if (pp) { kern = kp; kern_acc = kp_acc; }
   int sp = wgrad_splits(M, N, K, GemmTile<T>::BK);
   if (sp <= 1) {
     g.out = dW; g.ldo = N;
-    gemm<T>(accumulate ? kern_acc : kern, name, g, 1, st);
+    gemm<T>(accumulate ? kern_acc : kern, name, g, 1, st, threads);
     return;
   }
   g.out = part; g.ldo = N;
-  gemm<T>(kern, name, g, sp, st);
+  gemm<T>(kern, name, g, sp, st, threads);
   // the launcher may round the split count down; recompute it identically
   constexpr int BK = GemmTile<T>::BK;
   long per = ((long)K + sp - 1) / sp;
@@ -398,7 +400,7 @@ int bwd_impl(const blk_cfg& c, const T* dy, const T* x, const T* wqkv, const T* 
     gemm_pp<T>(gemm_proj_dgrad<T>, "gemm_proj_dgrad", g, st);
   }
   //    dW_proj = dy^T a
-  wgrad<T>(gemm_proj_wgrad<T>, gemm_proj_wgrad_acc<T>, "gemm_proj_wgrad", dy, s.a, dwproj, C, F, N, acc, w.part,
+  wgrad<T>(gemm_proj_wgrad<T>, gemm_proj_wgrad_acc<T>, gemm_proj_wgrad_pp, gemm_proj_wgrad_acc_pp, "gemm_proj_wgrad", dy, s.a, dwproj, C, F, N, acc, w.part,
            st);
   {  // 8: dh2 = du W_fc
     GemmArgs g = gargs(w.du, F, wt_fc, F, N, C, F);
@@ -406,7 +408,7 @@ int bwd_impl(const blk_cfg& c, const T* dy, const T* x, const T* wqkv, const T* 
     gemm_pp<T>(gemm_fc_dgrad<T>, "gemm_fc_dgrad", g, st);
   }
   //    dW_fc = du^T h2
-  wgrad<T>(gemm_fc_wgrad<T>, gemm_fc_wgrad_acc<T>, "gemm_fc_wgrad", w.du, s.h2, dwfc, F, C, N, acc, w.part, st);
+  wgrad<T>(gemm_fc_wgrad<T>, gemm_fc_wgrad_acc<T>, gemm_fc_wgrad_pp, gemm_fc_wgrad_acc_pp, "gemm_fc_wgrad", w.du, s.h2, dwfc, F, C, N, acc, w.part, st);
   {  // 7: dy1 = dy + rmsnorm backward
     Timed t("rmsnorm_bwd", st);
     hipLaunchKernelGGL(rmsnorm_bwd_kernel<T>, dim3(row_blocks(N)), dim3(256), 0, st, dy, (const T*)w.dh,
@@ -419,7 +421,7 @@ int bwd_impl(const blk_cfg& c, const T* dy, const T* x, const T* wqkv, const T* 
     gemm_pp<T>(gemm_o_dgrad<T>, "gemm_o_dgrad", g, st);
   }
   //    dW_o = dy1^T o
-  wgrad<T>(gemm_o_wgrad<T>, gemm_o_wgrad_acc<T>, "gemm_o_wgrad", w.dy1, s.o, dwo, C, C, N, acc, w.part, st);
+  wgrad<T>(gemm_o_wgrad<T>, gemm_o_wgrad_acc<T>, gemm_o_wgrad_pp, gemm_o_wgrad_acc_pp, "gemm_o_wgrad", w.dy1, s.o, dwo, C, C, N, acc, w.part, st);
   {  // 5: attention backward
     AttnArgs a = attn_args<T>(c);
     a.qkv = s.qkv; a.lse = s.lse; a.dO = w.dO; a.delta = w.delta; a.dqkv = w.dqkv;
@@ -462,7 +464,7 @@ int bwd_impl(const blk_cfg& c, const T* dy, const T* x, const T* wqkv, const T* 
     gemm_pp<T>(gemm_qkv_dgrad<T>, "gemm_qkv_dgrad", g, st);
   }
   //    dW_qkv = dqkv^T h1
-  wgrad<T>(gemm_qkv_wgrad<T>, gemm_qkv_wgrad_acc<T>, "gemm_qkv_wgrad", w.dqkv, s.h1, dwqkv, 3 * C, C, N, acc,
+  wgrad<T>(gemm_qkv_wgrad<T>, gemm_qkv_wgrad_acc<T>, gemm_qkv_wgrad_pp, gemm_qkv_wgrad_acc_pp, "gemm_qkv_wgrad", w.dqkv, s.h1, dwqkv, 3 * C, C, N, acc,
            w.part, st);
   {  // 1: dx = dy1 + rmsnorm backward
     Timed t("rmsnorm_bwd", st);
@@ -498,19 +500,24 @@ GemmArgs gargs8(const uint8_t* A, long lda, const unsigned* ama, const uint8_t* 
 }
 
 // dW[M, N] (+)= sum_k GT[m, k] XT[n, k], E4M3 operands [*, ld], fp32 out.
-void wgrad8(void (*kern)(GemmArgs), void (*kern_acc)(GemmArgs), const char* name, const uint8_t* GT, const unsigned* ama,
-            const uint8_t* XT, const unsigned* amb, long ld, float* dW, int M, int N, int K, int accumulate,
-            float* part, hipStream_t st) {
+// Token counts that are a multiple of the k-step (128) run on the eight-wave
+// body (kernels kp / kp_acc).
+void wgrad8(GemmKernel kern, GemmKernel kern_acc, GemmKernel kp, GemmKernel kp_acc, const char* name,
+            const uint8_t* GT, const unsigned* ama, const uint8_t* XT, const unsigned* amb, long ld, float* dW, int M,
+            int N, int K, int accumulate, float* part, hipStream_t st) {
   GemmArgs g = gargs8(GT, ld, ama, XT, ld, amb, M, N, K);
   constexpr int BK = GemmTile<fp8e4>::BK;
+  const bool pp = K % BK == 0 && ld % BK == 0;
+  const int threads = pp ? 512 : 256;
+  if (pp) { kern = kp; kern_acc = kp_acc; }
   const int sp = wgrad_splits(M, N, K, BK);
   if (sp <= 1) {
     g.out = dW; g.ldo = N;
-    gemm<fp8e4>(accumulate ? kern_acc : kern, name, g, 1, st);
+    gemm<fp8e4>(accumulate ? kern_acc : kern, name, g, 1, st, threads);
     return;
   }
   g.out = part; g.ldo = N;
-  gemm<fp8e4>(kern, name, g, sp, st);
+  gemm<fp8e4>(kern, name, g, sp, st, threads);
   long per = ((long)K + sp - 1) / sp;
   int ks = (int)(((per + BK - 1) / BK) * BK);
   int real = (K + ks - 1) / ks;
@@ -607,7 +614,7 @@ int bwd_fp8(const blk_cfg& c, const bf16* dy, const bf16* wqkv, const bf16* wo, 
     g.out = w.du; g.ldo = F; g.aux = s.a; g.ldaux = F; g.amax_out = am + AM_DU;
     gemm_pp<fp8e4>(gemm8_proj_dgrad, "gemm_proj_dgrad", g, st);
   }
-  wgrad8(gemm8_proj_wgrad, gemm8_proj_wgrad_acc, "gemm_proj_wgrad", w.g8t, am + AM_DY, s.a_8t, am + AM_A, Np, dwproj,
+  wgrad8(gemm8_proj_wgrad, gemm8_proj_wgrad_acc, gemm8_proj_wgrad_pp, gemm8_proj_wgrad_acc_pp, "gemm_proj_wgrad", w.g8t, am + AM_DY, s.a_8t, am + AM_A, Np, dwproj,
          C, F, N, acc, w.part, st);
   quantize(w.du, N, F, am + AM_DU, w.du8, w.du8t, Np, false, st);   // amax from gemm_proj_dgrad
   {  // dh2 = du W_fc
@@ -615,7 +622,7 @@ int bwd_fp8(const blk_cfg& c, const bf16* dy, const bf16* wqkv, const bf16* wo, 
     g.out = w.dh; g.ldo = C;
     gemm_pp<fp8e4>(gemm8_fc_dgrad, "gemm_fc_dgrad", g, st);
   }
-  wgrad8(gemm8_fc_wgrad, gemm8_fc_wgrad_acc, "gemm_fc_wgrad", w.du8t, am + AM_DU, s.h2_8t, am + AM_H2, Np, dwfc, F, C,
+  wgrad8(gemm8_fc_wgrad, gemm8_fc_wgrad_acc, gemm8_fc_wgrad_pp, gemm8_fc_wgrad_acc_pp, "gemm_fc_wgrad", w.du8t, am + AM_DU, s.h2_8t, am + AM_H2, Np, dwfc, F, C,
          N, acc, w.part, st);
   {
     Timed t("rmsnorm_bwd", st);
@@ -629,7 +636,7 @@ int bwd_fp8(const blk_cfg& c, const bf16* dy, const bf16* wqkv, const bf16* wo, 
     delta_args(g, c, s.o, w.delta);
     gemm_pp<fp8e4>(gemm8_o_dgrad, "gemm_o_dgrad", g, st);
   }
-  wgrad8(gemm8_o_wgrad, gemm8_o_wgrad_acc, "gemm_o_wgrad", w.g8t, am + AM_DY1, s.o_8t, am + AM_O, Np, dwo, C, C, N,
+  wgrad8(gemm8_o_wgrad, gemm8_o_wgrad_acc, gemm8_o_wgrad_pp, gemm8_o_wgrad_acc_pp, "gemm_o_wgrad", w.g8t, am + AM_DY1, s.o_8t, am + AM_O, Np, dwo, C, C, N,
          acc, w.part, st);
   {
     AttnArgs a = attn_args<bf16>(c);
@@ -655,7 +662,7 @@ int bwd_fp8(const blk_cfg& c, const bf16* dy, const bf16* wqkv, const bf16* wo, 
     g.out = w.dh; g.ldo = C;
     gemm_pp<fp8e4>(gemm8_qkv_dgrad, "gemm_qkv_dgrad", g, st);
   }
-  wgrad8(gemm8_qkv_wgrad, gemm8_qkv_wgrad_acc, "gemm_qkv_wgrad", w.dqkv8t, am + AM_DQKV, s.h1_8t, am + AM_H1, Np,
+  wgrad8(gemm8_qkv_wgrad, gemm8_qkv_wgrad_acc, gemm8_qkv_wgrad_pp, gemm8_qkv_wgrad_acc_pp, "gemm_qkv_wgrad", w.dqkv8t, am + AM_DQKV, s.h1_8t, am + AM_H1, Np,
          dwqkv, 3 * C, C, N, acc, w.part, st);
   {
     Timed t("rmsnorm_bwd", st);

@@ -22,6 +22,7 @@
 // loads of the residual / pre-activation, 16-byte stores.
 #pragma once
 #include "common.cuh"
+#include <type_traits>
 
 namespace blk {
 
@@ -486,6 +487,62 @@ struct PPStager {
   }
 };
 
+// m/n-contiguous bf16 operands (weight gradients: A(m, k) = G[k][m]): the
+// LDS sub-slab holds the tile as 64 k-rows x 256 elements (512 bytes, 32
+// chunks); chunk c of row r sits at c ^ (2 (r & 7)), so the 4 rows x 2
+// chunks one 16-lane transpose read touches fall on distinct banks.
+__device__ __forceinline__ int toff(int row, int chunk) { return row * 512 + ((chunk ^ ((row & 7) << 1)) << 4); }
+
+// One operand's share of a stage for wave q: k-rows 16q .. 16q+15, two
+// 512-byte rows (4 full cache lines each) per 1 KiB load.
+struct PPStagerT {
+  i32x4 rs;        // buffer resource from (k = kbeg, first column of the tile)
+  uint32_t x;      // byte offset of this lane's row at k = 0, load 0
+  uint32_t ldb;    // bytes per k-row
+  uint32_t cl;     // this lane's chunk byte offset before the per-load swizzle term
+  __device__ __forceinline__ void init(const void* p, long ld, long K, int c0, int kbeg, int q, int lane) {
+    const long first = (long)kbeg * ld + c0;
+    const long left = (long)K * ld - first;
+    rs = make_rsrc(static_cast<const char*>(p) + first * 2, (uint32_t)max(0L, min(left * 2, 0x7fffffffL)));
+    ldb = (uint32_t)(ld * 2);
+    x = (uint32_t)(16 * q + (lane >> 5)) * ldb;
+    // LDS row R = 16q + 2j + lane/32 holds at chunk position lane%32 the
+    // global chunk (lane%32) ^ 2 (R & 7), and R & 7 = (2j & 7) | lane/32
+    cl = (uint32_t)(((lane & 31) ^ ((lane >> 5) << 1)) << 4);
+  }
+  // columns past the matrix edge read in-bounds neighbours or zero; they only
+  // feed outputs the epilogue drops.  k past the end (live = false) reads zero.
+  __device__ __forceinline__ void issue(char* sub, int krel, bool live, int q) const {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t off = x + (uint32_t)(krel + 2 * j) * ldb + (cl ^ (uint32_t)(((2 * j) & 7) << 5));
+      lds_u32* dst = (lds_u32*)(sub + __builtin_amdgcn_readfirstlane((8 * q + j) * 1024));
+      raw_buffer_load_lds(rs, dst, 16, live ? (int)off : (int)0x80000000u, 0, 0, 0);
+    }
+  }
+};
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// MFMA 32x32x16 fragment of 32 columns (col0..) at k-substep ks from a
+// k-row sub-slab, by two LDS transpose reads: in each 16-lane group the
+// lanes address a 4-row x 16-column block and lane s receives column s of
+// it.  Lane l gets column col0 + l%32 and the k-slots 4h..4h+3, 8+4h..8+4h+3
+// (h = l/32) of the substep: a fixed permutation of the MFMA's k order,
+// the same for both operands, so the product is unchanged.
+__device__ __forceinline__ bf16x8 frag_t(const char* sub, int col0, int ks, int lane) {
+  const int g = (lane >> 4) & 3, s = lane & 15;
+  const int row = ks * 16 + 4 * (g >> 1) + (s >> 2);
+  const int col = col0 + 16 * (g & 1) + 4 * (s & 3);
+  const char* p0 = sub + toff(row, col >> 3) + (col & 7) * 2;
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 8 * 512));   // rows + 8: same swizzle
+  const s16x8 r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
 // Workgroup barrier that is also a hard scheduling boundary: no instruction
 // (MFMAs included) moves across it, and no memory wait is implied.
 __device__ __forceinline__ void wg_barrier() {
@@ -533,12 +590,15 @@ __device__ __forceinline__ void epilogue_pp(const GemmArgs& g, f32x16 (&acc)[2][
   if (g.amax_out) amax_publish<TO>(g.amax_out, mx);
 }
 
-template <typename TI, typename TO, int EPI>
+// TR: both operands m/n-contiguous (bf16 weight gradients), staged as k-rows
+// and read through the LDS transpose read.
+template <typename TI, typename TO, int EPI, bool TR = false>
 __device__ __forceinline__ void gemm_pp_body(const GemmArgs& g) {
   typedef GemmTile<TI> G;
   typedef Mfma<TI> MM;
-  constexpr int HS = G::BK / MM::KI / 2;                   // MFMA substeps per half k-step
-  constexpr int RD = 6 * HS * (sizeof(TI) == 1 ? 2 : 1);   // LDS reads per read phase
+  static_assert(!TR || sizeof(TI) == 2, "transposed staging is for 16-bit operands");
+  constexpr int HS = G::BK / MM::KI / 2;                              // MFMA substeps per half k-step
+  constexpr int RD = 6 * HS * (sizeof(TI) == 1 || TR ? 2 : 1);        // LDS reads per read phase
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int lane = threadIdx.x & 63;
   // wave-uniform: the group's branch and its buffer resource live in scalar registers
@@ -551,12 +611,19 @@ __device__ __forceinline__ void gemm_pp_body(const GemmArgs& g) {
   const int kbeg = split * g.k_split;
   const int nk = (min(g.K, kbeg + g.k_split) - kbeg) / G::BK;
 
-  // grp 0 stages the A rows, grp 1 the B rows
-  PPStager<TI> st;
-  if (grp == 0) st.init(g.A, g.lda, g.M, m0, q, lane);
-  else st.init(g.B, g.ldb, g.N, n0, q, lane);
+  // grp 0 stages the A operand, grp 1 the B operand
+  typename std::conditional<TR, PPStagerT, PPStager<TI>>::type st;
+  if constexpr (TR) {
+    if (grp == 0) st.init(g.A, g.lda, g.K, m0, kbeg, q, lane);
+    else st.init(g.B, g.ldb, g.K, n0, kbeg, q, lane);
+  } else {
+    if (grp == 0) st.init(g.A, g.lda, g.M, m0, q, lane);
+    else st.init(g.B, g.ldb, g.N, n0, q, lane);
+  }
   auto issue = [&](int kt) {
-    st.issue(smem + (kt & 1) * G::SLAB + grp * (G::BM * G::ROWB), (kbeg + kt * G::BK) * (int)sizeof(TI), kt < nk, q);
+    char* sub = smem + (kt & 1) * G::SLAB + grp * (G::BM * G::ROWB);
+    if constexpr (TR) st.issue(sub, kt * G::BK, kt < nk, q);
+    else st.issue(sub, (kbeg + kt * G::BK) * (int)sizeof(TI), kt < nk, q);
   };
 
   const int arow = (q >> 1) * 128 + grp * 64, brow = (q & 1) * 128;
@@ -572,10 +639,17 @@ __device__ __forceinline__ void gemm_pp_body(const GemmArgs& g) {
     const char* cur = smem + (kt & 1) * G::SLAB;
 #pragma unroll
     for (int s = 0; s < HS; ++s) {
+      if constexpr (TR) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) fa[s][i] = load_frag<TI>(cur, arow + 32 * i, h * HS + s, lane);
+        for (int i = 0; i < 2; ++i) fa[s][i] = frag_t(cur, arow + 32 * i, h * HS + s, lane);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) fb[s][j] = load_frag<TI>(cur + G::BM * G::ROWB, brow + 32 * j, h * HS + s, lane);
+        for (int j = 0; j < 4; ++j) fb[s][j] = frag_t(cur + G::BM * G::ROWB, brow + 32 * j, h * HS + s, lane);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) fa[s][i] = load_frag<TI>(cur, arow + 32 * i, h * HS + s, lane);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) fb[s][j] = load_frag<TI>(cur + G::BM * G::ROWB, brow + 32 * j, h * HS + s, lane);
+      }
     }
   };
   auto mfma = [&]() {
@@ -685,6 +759,23 @@ BLK_GEMM_KERNEL(gemm_o_wgrad_acc, false, false, EPI_F32_ADD, float)
 BLK_GEMM_KERNEL(gemm_qkv_wgrad_acc, false, false, EPI_F32_ADD, float)
 }  // namespace blk
 
+// bf16 weight gradients on the eight-wave body (k = tokens a multiple of 64).
+#define BLK_GEMM_PPT_KERNEL(NAME, EPI)                                            \
+  __global__ __launch_bounds__(512, 1) void NAME(GemmArgs g) {                   \
+    gemm_pp_body<bf16, float, EPI, true>(g);                                    \
+  }
+
+namespace blk {
+BLK_GEMM_PPT_KERNEL(gemm_proj_wgrad_pp, EPI_F32)
+BLK_GEMM_PPT_KERNEL(gemm_fc_wgrad_pp, EPI_F32)
+BLK_GEMM_PPT_KERNEL(gemm_o_wgrad_pp, EPI_F32)
+BLK_GEMM_PPT_KERNEL(gemm_qkv_wgrad_pp, EPI_F32)
+BLK_GEMM_PPT_KERNEL(gemm_proj_wgrad_acc_pp, EPI_F32_ADD)
+BLK_GEMM_PPT_KERNEL(gemm_fc_wgrad_acc_pp, EPI_F32_ADD)
+BLK_GEMM_PPT_KERNEL(gemm_o_wgrad_acc_pp, EPI_F32_ADD)
+BLK_GEMM_PPT_KERNEL(gemm_qkv_wgrad_acc_pp, EPI_F32_ADD)
+}  // namespace blk
+
 // FP8 (E4M3) linear layers: every GEMM takes k-contiguous operands (weights
 // and activations quantised row-major, or transposed for weight gradients).
 #define BLK_GEMM8_KERNEL(NAME, EPI, TO)                                           \
@@ -713,4 +804,13 @@ BLK_GEMM8_KERNEL(gemm8_proj_wgrad_acc, EPI_F32_ADD, float)
 BLK_GEMM8_KERNEL(gemm8_fc_wgrad_acc, EPI_F32_ADD, float)
 BLK_GEMM8_KERNEL(gemm8_o_wgrad_acc, EPI_F32_ADD, float)
 BLK_GEMM8_KERNEL(gemm8_qkv_wgrad_acc, EPI_F32_ADD, float)
+// the same on the eight-wave body (token count a multiple of 128)
+BLK_GEMM8_PP_KERNEL(gemm8_proj_wgrad_pp, EPI_F32, float)
+BLK_GEMM8_PP_KERNEL(gemm8_fc_wgrad_pp, EPI_F32, float)
+BLK_GEMM8_PP_KERNEL(gemm8_o_wgrad_pp, EPI_F32, float)
+BLK_GEMM8_PP_KERNEL(gemm8_qkv_wgrad_pp, EPI_F32, float)
+BLK_GEMM8_PP_KERNEL(gemm8_proj_wgrad_acc_pp, EPI_F32_ADD, float)
+BLK_GEMM8_PP_KERNEL(gemm8_fc_wgrad_acc_pp, EPI_F32_ADD, float)
+BLK_GEMM8_PP_KERNEL(gemm8_o_wgrad_acc_pp, EPI_F32_ADD, float)
+BLK_GEMM8_PP_KERNEL(gemm8_qkv_wgrad_acc_pp, EPI_F32_ADD, float)
 }  // namespace blk

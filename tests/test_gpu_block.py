@@ -37,6 +37,7 @@ def test_d6_f32_full_workload():
     (1, 77, 384),     # one partial tile
     (3, 1, 256),      # T = 1
     (1, 520, 768),    # d12 width, ragged
+    (2, 192, 384),    # token count a multiple of 64 (weight gradients on the eight-wave body), ragged width
 ])
 def test_bf16_ragged(B, T, C):
     _parity(BlockShape(B=B, T=T, C=C, H=C // 128, F=4 * C, dtype="bf16"))
