@@ -28,6 +28,13 @@ positions counted from 0 per sequence; softmax scale 1/sqrt(D); causal mask
 key <= query; fused QKV output split as [q | k | v] with heads contiguous in
 each; weights stored [out, in] and applied as y = x W^T.
 
+Sliding-window attention (optional window W): [RU], same section, names an
+alternation of attention windows, three layers of four with a short window
+of a quarter of the context and one with the full context (the last layer
+always full).  The pages do not fix the window's boundary; read here as:
+query i sees the W keys i - W < j <= i, itself included.  W >= T is the
+causal mask.  Which layer gets which window is the caller's choice.
+
 Backward: the adjoints of the forward steps, derived by hand; pinned in the
 tests by central finite differences, an autograd cross-check and invariants.
 """
@@ -39,7 +46,7 @@ import numpy as np
 
 __all__ = [
     "rmsnorm", "rmsnorm_bwd", "rope_tables", "rope", "rope_bwd",
-    "causal_attention", "causal_attention_bwd", "online_causal_attention",
+    "visible", "causal_attention", "causal_attention_bwd", "online_causal_attention",
     "BlockCache", "block_fwd", "block_bwd", "decode_step", "relu2", "relu2_bwd",
 ]
 
@@ -83,14 +90,25 @@ def rope_bwd(dz: np.ndarray, cos: np.ndarray, sin: np.ndarray) -> np.ndarray:
 
 
 # ---------------------------------------------------------------- attention
-def causal_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray):
-    """softmax(q k^T / sqrt(D)) v with key j <= query i.  Materialises the
-    full score matrix.  q, k, v: [..., T, D].  Returns (o, P)."""
+def visible(T: int, window=None) -> np.ndarray:
+    """[T, T] boolean: query i sees key j when j <= i and, with a window W,
+    j > i - W."""
+    i = np.arange(T)[:, None]
+    j = np.arange(T)[None, :]
+    vis = j <= i
+    if window is not None:
+        vis &= j > i - int(window)
+    return vis
+
+
+def causal_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, window=None):
+    """softmax(q k^T / sqrt(D)) v over the keys :func:`visible` to each query
+    (j <= i, and j > i - W with a window).  Materialises the full score
+    matrix.  q, k, v: [..., T, D].  Returns (o, P)."""
     D = q.shape[-1]
     T = q.shape[-2]
     s = np.matmul(q, np.swapaxes(k, -1, -2)) / np.sqrt(D)
-    mask = np.triu(np.ones((T, T), dtype=bool), k=1)
-    s = np.where(mask, -np.inf, s)
+    s = np.where(visible(T, window), s, -np.inf)
     m = np.max(s, axis=-1, keepdims=True)
     e = np.exp(s - m)
     P = e / np.sum(e, axis=-1, keepdims=True)
@@ -111,7 +129,7 @@ def causal_attention_bwd(do, q, k, v, o, P):
     return dq, dk, dv
 
 
-def online_causal_attention(q, k, v, block: int = 16):
+def online_causal_attention(q, k, v, block: int = 16, window=None):
     """Same result as :func:`causal_attention`, computed key block by key
     block with a running maximum and running denominator (the online softmax
     of flash-style attention).  Used only to cross-check the materialised
@@ -128,7 +146,10 @@ def online_causal_attention(q, k, v, block: int = 16):
         j1 = min(T, j0 + block)
         s = np.matmul(q, np.swapaxes(k[..., j0:j1, :], -1, -2)) / np.sqrt(D)
         kj = np.arange(j0, j1)[None, :]
-        s = np.where(kj > qi, -np.inf, s)
+        hidden = kj > qi
+        if window is not None:
+            hidden = hidden | (kj <= qi - int(window))
+        s = np.where(hidden, -np.inf, s)
         m_new = np.maximum(m, np.max(s, axis=-1))
         alpha = np.where(np.isfinite(m_new), np.exp(m - m_new), 0.0)
         p = np.where(np.isfinite(m_new)[..., None], np.exp(s - m_new[..., None]), 0.0)
@@ -186,13 +207,13 @@ def _merge(z):
 
 
 def block_fwd(x, w_qkv, w_o, w_fc, w_proj, H: int, eps: float = 1e-6,
-              rope_base: float = 10000.0, positions=None) -> BlockCache:
+              rope_base: float = 10000.0, positions=None, window=None) -> BlockCache:
     """Forward of the decoder block on x [B,T,C] (float64).
 
     1 RMSNorm; 2 fused QKV projection (no bias); 3 rotary on q, k;
-    4 QK-norm; 5 causal multi-head attention; 6 output projection plus
-    residual; 7 RMSNorm; 8 MLP up-projection with ReLU^2; 9 down-projection
-    plus residual.  [RU], [CN], [ES]."""
+    4 QK-norm; 5 causal multi-head attention (optionally sliding-window);
+    6 output projection plus residual; 7 RMSNorm; 8 MLP up-projection with
+    ReLU^2; 9 down-projection plus residual.  [RU], [CN], [ES]."""
     x = np.asarray(x, dtype=np.float64)
     B, T, C = x.shape
     D = C // H
@@ -204,7 +225,7 @@ def block_fwd(x, w_qkv, w_o, w_fc, w_proj, H: int, eps: float = 1e-6,
     qr, kr = rope(q, cos, sin), rope(k, cos, sin)
     qn, rho_q = rmsnorm(qr, eps)
     kn, rho_k = rmsnorm(kr, eps)
-    o_heads, P = causal_attention(qn, kn, v)
+    o_heads, P = causal_attention(qn, kn, v, window)
     o = _merge(o_heads)
     y1 = x + o @ w_o.T
     h2, r2 = rmsnorm(y1, eps)
@@ -255,10 +276,11 @@ def block_bwd(dy, cache: BlockCache, w_qkv, w_o, w_fc, w_proj, H: int):
 
 
 def decode_step(x, w_qkv, w_o, w_fc, w_proj, k_cache, v_cache, cache_len,
-                H: int, eps: float = 1e-6, rope_base: float = 10000.0):
+                H: int, eps: float = 1e-6, rope_base: float = 10000.0, window=None):
     """One new token per sequence at position p = cache_len[b]: forward steps
     1-4 on that row, its k (after rotary and QK-norm) and v written at slot
-    p, attention over slots 0..p, then steps 6-9.  Inference with a KV
+    p, attention over slots 0..p (p-W+1..p with a window W), then steps 6-9.
+    Inference with a KV
     cache and prefill/decode is named on the 7minutos.es page (section on
     midtraining, SFT and tool use) and in the launch thread.
 
@@ -283,8 +305,9 @@ def decode_step(x, w_qkv, w_o, w_fc, w_proj, k_cache, v_cache, cache_len,
         kn, _ = rmsnorm(rope(k, cos, sin), eps)
         kc[b, :, p, :] = kn[:, 0, :]
         vc[b, :, p, :] = v[:, 0, :]
-        keys = kc[b, :, :p + 1, :]             # [H, p+1, D]
-        vals = vc[b, :, :p + 1, :]
+        j0 = 0 if window is None else max(0, p - int(window) + 1)
+        keys = kc[b, :, j0:p + 1, :]           # [H, p+1-j0, D]
+        vals = vc[b, :, j0:p + 1, :]
         s = np.matmul(qn, np.swapaxes(keys, -1, -2)) / np.sqrt(D)   # [H,1,p+1]
         e = np.exp(s - np.max(s, axis=-1, keepdims=True))
         Pb = e / np.sum(e, axis=-1, keepdims=True)

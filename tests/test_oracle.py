@@ -156,6 +156,89 @@ def test_online_softmax_matches_materialised():
     assert np.allclose(np.exp(s - lse[..., None]), P, rtol=1e-11, atol=1e-15)
 
 
+# ------------------------------------------------- sliding-window attention
+def test_window_brute_force_loops():
+    # query i averages v over keys max(0, i-W+1) .. i with softmax weights
+    rng = np.random.default_rng(21)
+    T, D, Wn = 9, 4, 3
+    q, k, v = (rng.standard_normal((T, D)) for _ in range(3))
+    o, _ = ob.causal_attention(q, k, v, window=Wn)
+    for i in range(T):
+        keys = range(max(0, i - Wn + 1), i + 1)
+        w = {j: math.exp(sum(q[i, d] * k[j, d] for d in range(D)) / math.sqrt(D)) for j in keys}
+        z = sum(w.values())
+        for d in range(D):
+            ref = sum(w[j] * v[j, d] for j in keys) / z
+            assert math.isclose(o[i, d], ref, rel_tol=1e-12, abs_tol=1e-13)
+
+
+def test_window_row_support_and_wide_window_is_causal():
+    rng = np.random.default_rng(22)
+    T, Wn = 13, 4
+    q, k, v = (rng.standard_normal((2, T, 8)) for _ in range(3))
+    _, P = ob.causal_attention(q, k, v, window=Wn)
+    counts = np.count_nonzero(P, axis=-1)
+    assert np.array_equal(counts[0], np.minimum(np.arange(T) + 1, Wn))
+    o_c, P_c = ob.causal_attention(q, k, v)
+    for wide in (T, T + 5):
+        o_w, P_w = ob.causal_attention(q, k, v, window=wide)
+        assert np.array_equal(o_w, o_c) and np.array_equal(P_w, P_c)
+
+
+def test_window_one_is_value_and_stops_qk_gradients():
+    # a window of one key: each query attends to itself only, so o = v and
+    # the scores carry no gradient back to q and k
+    rng = np.random.default_rng(23)
+    q, k, v, do = (rng.standard_normal((3, 10, 16)) for _ in range(4))
+    o, P = ob.causal_attention(q, k, v, window=1)
+    assert np.array_equal(o, v)
+    dq, dk, dv = ob.causal_attention_bwd(do, q, k, v, o, P)
+    assert np.max(np.abs(dq)) < 1e-13 and np.max(np.abs(dk)) < 1e-13
+    assert np.array_equal(dv, do)
+
+
+@pytest.mark.parametrize("window", [None, 5, 16])
+def test_online_softmax_with_window_matches_materialised(window):
+    rng = np.random.default_rng(24)
+    q, k, v = (rng.standard_normal((2, 3, 37, 16)) * 2 for _ in range(3))
+    o1, _ = ob.causal_attention(q, k, v, window=window)
+    o2, _ = ob.online_causal_attention(q, k, v, block=8, window=window)
+    assert np.allclose(o1, o2, rtol=1e-12, atol=1e-13)
+
+
+def test_window_block_bwd_central_differences():
+    # the adjoint with a window: directional derivatives of <dy, y>
+    rng = np.random.default_rng(25)
+    B, T, C, H, Wn = 1, 7, 256, 2, 3
+    x = rng.standard_normal((B, T, C))
+    W = _weights(rng, C, 4 * C, H, 0.05)
+    dy = rng.standard_normal((B, T, C))
+    g = ob.block_bwd(dy, ob.block_fwd(x, *W, H=H, window=Wn), *W, H=H)
+    h = 1e-7
+    for trial in range(3):
+        dx_dir = rng.standard_normal(x.shape)
+        dW_dir = [rng.standard_normal(w.shape) for w in W]
+        Lp = np.sum(dy * ob.block_fwd(x + h * dx_dir, *[w + h * d for w, d in zip(W, dW_dir)], H=H, window=Wn).y)
+        Lm = np.sum(dy * ob.block_fwd(x - h * dx_dir, *[w - h * d for w, d in zip(W, dW_dir)], H=H, window=Wn).y)
+        num = (Lp - Lm) / (2 * h)
+        ana = np.sum(g["dx"] * dx_dir) + sum(np.sum(g[n] * d) for n, d in zip(("dw_qkv", "dw_o", "dw_fc", "dw_proj"), dW_dir))
+        assert math.isclose(ana, num, rel_tol=1e-7), (ana, num)
+
+
+def test_window_block_locality():
+    # with a window W, output row t depends on input rows t-W+1 .. t only
+    rng = np.random.default_rng(26)
+    B, T, C, H, Wn = 1, 10, 256, 2, 3
+    x = rng.standard_normal((B, T, C))
+    W = _weights(rng, C, 4 * C, H, 0.05)
+    y0 = ob.block_fwd(x, *W, H=H, window=Wn).y
+    x2 = x.copy()
+    x2[0, 2] += 1.0
+    y1 = ob.block_fwd(x2, *W, H=H, window=Wn).y
+    changed = np.any(y0[0] != y1[0], axis=-1)
+    assert np.array_equal(np.nonzero(changed)[0], np.arange(2, 2 + Wn))
+
+
 # ------------------------------------------------------------ block
 def _loss_grads(shape_kw, seed=0, wscale=0.3):
     rng = np.random.default_rng(seed)
@@ -330,8 +413,8 @@ def test_block_adjoint_identity_full_d6_shape():
 
 
 # ------------------------------------------------------------ decode
-@pytest.mark.parametrize("ragged", [False, True])
-def test_decode_equals_prefill_row(ragged):
+@pytest.mark.parametrize("ragged,window", [(False, None), (True, None), (True, 6)])
+def test_decode_equals_prefill_row(ragged, window):
     rng = np.random.default_rng(13)
     B, C, H, S = 3, 256, 2, 20
     F = 4 * C
@@ -342,14 +425,14 @@ def test_decode_equals_prefill_row(ragged):
     vc = rng.standard_normal((B, H, S, 128))
     for b in range(B):
         L = int(lens[b])
-        c = ob.block_fwd(xs[b:b + 1, :L + 1], *W, H=H)
+        c = ob.block_fwd(xs[b:b + 1, :L + 1], *W, H=H, window=window)
         kc[b, :, :L] = c.kn[0, :, :L]
         vc[b, :, :L] = c.v[0, :, :L]
     xnew = np.stack([xs[b, lens[b]] for b in range(B)])
-    y, kc2, vc2 = ob.decode_step(xnew, *W, kc, vc, lens, H=H)
+    y, kc2, vc2 = ob.decode_step(xnew, *W, kc, vc, lens, H=H, window=window)
     for b in range(B):
         L = int(lens[b])
-        ref = ob.block_fwd(xs[b:b + 1, :L + 1], *W, H=H)
+        ref = ob.block_fwd(xs[b:b + 1, :L + 1], *W, H=H, window=window)
         assert np.allclose(y[b], ref.y[0, L], rtol=1e-11, atol=1e-11)
         assert np.allclose(kc2[b, :, L], ref.kn[0, :, L], rtol=1e-12, atol=1e-12)
         assert np.array_equal(kc2[b, :, L + 1:], kc[b, :, L + 1:])
