@@ -10,5 +10,5 @@ from .binding import (  # noqa: F401
     BLK_BF16, BLK_F32, BLK_GEMM_FP8_E4M3, BLK_GEMM_NATIVE, BlkError, BlockConfig, DecodeConfig,
     block_bwd, block_fp8_quantize, block_fwd, block_saved_bytes, block_scratch_bytes, block_strerror, block_timing_enable,
     block_timing_read, decode_scratch_bytes,
-    decode_step, library, library_path,
+    decode_step, layer_window, library, library_path,
 )

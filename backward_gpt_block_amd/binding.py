@@ -26,13 +26,14 @@ class BlkError(RuntimeError):
 class _Cfg(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("C", ctypes.c_int32), ("H", ctypes.c_int32),
                 ("D", ctypes.c_int32), ("F", ctypes.c_int32), ("eps", ctypes.c_float),
-                ("rope_base", ctypes.c_float), ("dtype", ctypes.c_int32), ("gemm", ctypes.c_int32)]
+                ("rope_base", ctypes.c_float), ("dtype", ctypes.c_int32), ("gemm", ctypes.c_int32),
+                ("window", ctypes.c_int32)]
 
 
 class _DCfg(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("C", ctypes.c_int32), ("H", ctypes.c_int32), ("D", ctypes.c_int32),
                 ("F", ctypes.c_int32), ("S_max", ctypes.c_int32), ("eps", ctypes.c_float),
-                ("rope_base", ctypes.c_float), ("dtype", ctypes.c_int32)]
+                ("rope_base", ctypes.c_float), ("dtype", ctypes.c_int32), ("window", ctypes.c_int32)]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -47,9 +48,11 @@ class BlockConfig:
     rope_base: float = 10000.0
     dtype: int = BLK_BF16
     gemm: int = BLK_GEMM_NATIVE
+    window: int = 0          # attention window (0: causal over the whole sequence)
 
     def c(self) -> _Cfg:
-        return _Cfg(self.B, self.T, self.C, self.H, self.D, self.F, self.eps, self.rope_base, self.dtype, self.gemm)
+        return _Cfg(self.B, self.T, self.C, self.H, self.D, self.F, self.eps, self.rope_base, self.dtype, self.gemm,
+                    self.window)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -63,9 +66,27 @@ class DecodeConfig:
     eps: float = 1e-6
     rope_base: float = 10000.0
     dtype: int = BLK_BF16
+    window: int = 0
 
     def c(self) -> _DCfg:
-        return _DCfg(self.B, self.C, self.H, self.D, self.F, self.S_max, self.eps, self.rope_base, self.dtype)
+        return _DCfg(self.B, self.C, self.H, self.D, self.F, self.S_max, self.eps, self.rope_base, self.dtype,
+                     self.window)
+
+
+def layer_window(layer: int, n_layer: int, T: int, pattern: str = "SSSL") -> int:
+    """Attention window (BlockConfig.window) of layer `layer` of `n_layer`
+    under a window pattern: the pattern repeats over the layers, an "S"
+    layer attends within a short window of T // 4 tokens, an "L" layer over
+    the whole context (0), and the last layer is always full.  The
+    flicky.cc course page, section on what changed since GPT-2, gives SSSL
+    as the default alternation."""
+    if not pattern or any(ch not in "SL" for ch in pattern.upper()):
+        raise ValueError(f"window pattern must be a string of S and L, got {pattern!r}")
+    if not 0 <= layer < n_layer:
+        raise ValueError(f"layer {layer} outside 0..{n_layer - 1}")
+    if layer == n_layer - 1 or pattern.upper()[layer % len(pattern)] == "L":
+        return 0
+    return max(1, T // 4)
 
 
 _LIB = None

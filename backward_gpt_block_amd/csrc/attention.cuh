@@ -252,6 +252,7 @@ struct AttnArgs {
   unsigned* amax_o;    // fp8 mode: absolute maxima (float bits) of o and of
   unsigned* amax_dqkv; //   dq' | dk' | dv, or null
   int B, T, H, C;
+  int W;             // attention window: query i sees keys i - W < j <= i (W >= T: causal)
   float sl2;         // log2(e) / sqrt(D)
   float rsd;         // 1 / sqrt(D)
 };
@@ -263,7 +264,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
   typedef Mfma<T> MM;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int STAGE = A::ROWT + A::TRT;      // K rows + V^T
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h = lane >> 5;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), h = lane >> 5;
   const int BH = a.B * a.H;
   const int nqt = (a.T + 127) / 128;
   const int qt = nqt - 1 - (int)(blockIdx.x / BH);   // longest rows first
@@ -288,14 +289,16 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
 
   const int last_key = min(a.T - 1, qt * 128 + 127);
   const int nkt = last_key / A::RT + 1;
-  stage_rows<T>(smem, Kg, ld, 0, a.T);
-  stage_trans<T>(smem + A::ROWT, Vg, ld, 0, a.T);
+  const int kt_lo = max(0, qt * 128 - a.W + 1) / A::RT;   // first tile inside the window
+  stage_rows<T>(smem, Kg, ld, kt_lo * A::RT, a.T);
+  stage_trans<T>(smem + A::ROWT, Vg, ld, kt_lo * A::RT, a.T);
   __syncthreads();
-  for (int kt = 0; kt < nkt; ++kt) {
-    const char* cur = smem + (kt & 1) * STAGE;
-    char* nxt = smem + ((kt + 1) & 1) * STAGE;
+  for (int kt = kt_lo; kt < nkt; ++kt) {
+    const char* cur = smem + ((kt - kt_lo) & 1) * STAGE;
+    char* nxt = smem + ((kt - kt_lo + 1) & 1) * STAGE;
     const int k0 = kt * A::RT;
-    if (k0 <= qw0 + 31) {          // some key of this tile is visible to this wave
+    // some key of this tile is visible to some query of this wave
+    if (k0 <= qw0 + 31 && k0 + A::RT - 1 > qw0 - a.W) {
       f32x16 s[A::NB];
 #pragma unroll
       for (int kb = 0; kb < A::NB; ++kb) {
@@ -305,7 +308,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
         for (int ks = 0; ks < HD / MM::KI; ++ks)
           s[kb] = MM::mma(frag_rows<T>(cur, kb * 32, ks, lane), qf[ks], s[kb]);
       }
-      const bool need_mask = (k0 + A::RT - 1 > qw0) || (k0 + A::RT > a.T);
+      const bool need_mask = (k0 + A::RT - 1 > qw0) || (k0 + A::RT > a.T) || (k0 <= qw0 + 31 - a.W);
       float mt = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < A::NB; ++kb)
@@ -314,7 +317,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
           float v = s[kb][r] * a.sl2;
           if (need_mask) {
             const int key = k0 + kb * 32 + acc_row(r, lane);
-            if (key > q || key >= a.T) v = -INFINITY;
+            if (key > q || key >= a.T || key <= q - a.W) v = -INFINITY;
           }
           s[kb][r] = v;
           mt = fmaxf(mt, v);
@@ -368,7 +371,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(AttnArgs a) {
   typedef Mfma<T> MM;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int STAGE = 2 * A::ROWT + A::TRT;   // K rows, V rows, K^T
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int BH = a.B * a.H;
   const int nqt = (a.T + 127) / 128;
   const int qt = nqt - 1 - (int)(blockIdx.x / BH);
@@ -396,15 +399,16 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(AttnArgs a) {
 
   const int last_key = min(a.T - 1, qt * 128 + 127);
   const int nkt = last_key / A::RT + 1;
-  stage_rows<T>(smem, Kg, ld, 0, a.T);
-  stage_rows<T>(smem + A::ROWT, Vg, ld, 0, a.T);
-  stage_trans<T>(smem + 2 * A::ROWT, Kg, ld, 0, a.T);
+  const int kt_lo = max(0, qt * 128 - a.W + 1) / A::RT;   // first tile inside the window
+  stage_rows<T>(smem, Kg, ld, kt_lo * A::RT, a.T);
+  stage_rows<T>(smem + A::ROWT, Vg, ld, kt_lo * A::RT, a.T);
+  stage_trans<T>(smem + 2 * A::ROWT, Kg, ld, kt_lo * A::RT, a.T);
   __syncthreads();
-  for (int kt = 0; kt < nkt; ++kt) {
-    const char* cur = smem + (kt & 1) * STAGE;
-    char* nxt = smem + ((kt + 1) & 1) * STAGE;
+  for (int kt = kt_lo; kt < nkt; ++kt) {
+    const char* cur = smem + ((kt - kt_lo) & 1) * STAGE;
+    char* nxt = smem + ((kt - kt_lo + 1) & 1) * STAGE;
     const int k0 = kt * A::RT;
-    if (k0 <= qw0 + 31) {
+    if (k0 <= qw0 + 31 && k0 + A::RT - 1 > qw0 - a.W) {
       f32x16 s[A::NB], dp[A::NB];
 #pragma unroll
       for (int kb = 0; kb < A::NB; ++kb) {
@@ -416,7 +420,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(AttnArgs a) {
           dp[kb] = MM::mma(frag_rows<T>(cur + A::ROWT, kb * 32, ks, lane), df[ks], dp[kb]);
         }
       }
-      const bool need_mask = (k0 + A::RT - 1 > qw0) || (k0 + A::RT > a.T);
+      const bool need_mask = (k0 + A::RT - 1 > qw0) || (k0 + A::RT > a.T) || (k0 <= qw0 + 31 - a.W);
 #pragma unroll
       for (int kb = 0; kb < A::NB; ++kb)
 #pragma unroll
@@ -424,7 +428,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(AttnArgs a) {
           float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], a.sl2, -lse));
           if (need_mask) {
             const int key = k0 + kb * 32 + acc_row(r, lane);
-            if (key > q || key >= a.T) p = 0.f;
+            if (key > q || key >= a.T || key <= q - a.W) p = 0.f;
           }
           if (!qv) p = 0.f;
           s[kb][r] = p * (dp[kb][r] - dlt);   // dS^T
@@ -456,7 +460,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   // Q rows, dO rows, Q^T, dO^T, lse[RT], delta[RT]
   constexpr int STAGE = 2 * A::ROWT + 2 * A::TRT + 2 * A::RT * 4;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int BH = a.B * a.H;
   const int kt = (int)(blockIdx.x / BH);          // first key tiles have the most queries
   const int bh = blockIdx.x % BH;
@@ -495,7 +499,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(AttnArgs a) {
   };
 
   const int qt0 = (kt * 128) / A::RT;
-  const int nqt = (a.T + A::RT - 1) / A::RT;
+  // the last query that sees a key of this workgroup is kt*128 + 127 + W - 1
+  const int nqt = min((a.T + A::RT - 1) / A::RT, (int)(((long)kt * 128 + 127 + a.W - 1) / A::RT) + 1);
   if (qt0 < nqt) stage(smem, qt0 * A::RT);
   __syncthreads();
   for (int qt = qt0; qt < nqt; ++qt) {
@@ -505,8 +510,9 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(AttnArgs a) {
     const int q0 = qt * A::RT;
     const float* lsev = reinterpret_cast<const float*>(cur + 2 * A::ROWT + 2 * A::TRT);
     const float* dlv = lsev + A::RT;
-    if (q0 + A::RT - 1 >= kw0) {      // some query of this tile sees a key of this wave
-      const bool need_mask = q0 < kw0 + 31;
+    // some query of this tile sees a key of this wave
+    if (q0 + A::RT - 1 >= kw0 && q0 <= kw0 + 31 + a.W - 1) {
+      const bool need_mask = q0 < kw0 + 31 || q0 + A::RT - 1 >= kw0 + a.W;
 #pragma unroll
       for (int qb = 0; qb < A::NB; ++qb) {
         f32x16 s, dp;
@@ -526,7 +532,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(AttnArgs a) {
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * g + e;
             float p = __builtin_amdgcn_exp2f(fmaf(s[r], a.sl2, -lv[e]));
-            if (need_mask && key > q0 + qi + e) p = 0.f;
+            if (need_mask && (key > q0 + qi + e || q0 + qi + e >= key + a.W)) p = 0.f;
             s[r] = p;
             dp[r] = p * (dp[r] - dv4[e]);    // dS
           }
@@ -653,11 +659,14 @@ __device__ __forceinline__ bf16x8 frag_vt(const char* tile, int mm, int db, int 
 }
 }  // namespace fa
 
+// WIN: a window shorter than the sequence (a.W < a.T); the causal instance
+// carries none of the window's bounds, masks or guards.
+template <bool WIN>
 __global__ __launch_bounds__(256, 1) void attn_fwd_bf16_kernel(AttnArgs a) {
   using namespace fa;
   typedef Mfma<bf16> MM;
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h = lane >> 5;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), h = lane >> 5;
   const int BH = a.B * a.H;
   const int nqt = (a.T + QWG - 1) / QWG;
   const int qt = nqt - 1 - (int)(blockIdx.x / BH);     // longest rows first
@@ -688,19 +697,21 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_bf16_kernel(AttnArgs a) {
   frag_vt_offsets(vo, lane);
 
   const int last_key = min(a.T - 1, qt * QWG + QWG - 1);
-  const int nkt = last_key / KT + 1;
-  issue_kv(smem, rs, 0, ldb, koff, voff, wave, lane);
-  if (nkt > 1) issue_kv(smem + SLOT, rs, KT, ldb, koff, voff, wave, lane);
-  for (int kt = 0; kt < nkt; ++kt) {
-    // tile kt landed (own loads, then everyone's); slot of tile kt-1 is free
-    if (kt + 1 < nkt) __builtin_amdgcn_s_waitcnt(0x3f70 | 8);   // vmcnt(8): the next tile may stay in flight
-    else __builtin_amdgcn_s_waitcnt(0x3f70);                    // vmcnt(0)
+  const int kt_lo = WIN ? max(0, qt * QWG - a.W + 1) / KT : 0;   // first tile inside the window
+  const int n = last_key / KT + 1 - kt_lo;
+  issue_kv(smem, rs, kt_lo * KT, ldb, koff, voff, wave, lane);
+  if (n > 1) issue_kv(smem + SLOT, rs, (kt_lo + 1) * KT, ldb, koff, voff, wave, lane);
+  for (int it = 0; it < n; ++it) {
+    // tile it landed (own loads, then everyone's); slot of tile it-1 is free
+    if (it + 1 < n) __builtin_amdgcn_s_waitcnt(0x3f70 | 8);   // vmcnt(8): the next tile may stay in flight
+    else __builtin_amdgcn_s_waitcnt(0x3f70);                  // vmcnt(0)
     __syncthreads();
-    if (kt + 2 < nkt) issue_kv(smem + ((kt + 2) % NSLOT) * SLOT, rs, (kt + 2) * KT, ldb, koff, voff, wave, lane);
-    const lds_char* kt_ = (const lds_char*)smem + (kt % NSLOT) * SLOT;
+    if (it + 2 < n) issue_kv(smem + ((it + 2) % NSLOT) * SLOT, rs, (kt_lo + it + 2) * KT, ldb, koff, voff, wave, lane);
+    const lds_char* kt_ = (const lds_char*)smem + (it % NSLOT) * SLOT;
     const lds_char* vt_ = kt_ + TILE;
-    const int k0 = kt * KT;
+    const int k0 = (kt_lo + it) * KT;
     if (k0 > qw0 + QW - 1) continue;                  // every key of this tile is in this wave's future
+    if (WIN && k0 + KT - 1 <= qw0 - a.W) continue;    // every key is before this wave's windows
     f32x16 s[2][2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
@@ -725,13 +736,14 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const int q = qw0 + qb * 32 + (lane & 31);
-      if ((k0 + KT - 1 > qw0 + qb * 32) || (k0 + KT > a.T)) {     // diagonal or ragged tile
+      // diagonal, ragged or window-edge tile
+      if ((k0 + KT - 1 > qw0 + qb * 32) || (k0 + KT > a.T) || (WIN && k0 <= qw0 + qb * 32 + 31 - a.W)) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = k0 + kb * 32 + acc_row(r, lane);
-            if (key > q || key >= a.T) s[qb][kb][r] = -INFINITY;
+            if (key > q || key >= a.T || (WIN && key <= q - a.W)) s[qb][kb][r] = -INFINITY;
           }
       }
       float mt = -INFINITY;
@@ -740,15 +752,18 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_bf16_kernel(AttnArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[qb][kb][r]);
       mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * a.sl2;
+      // with a window a query can meet whole tiles of hidden keys before its
+      // first visible one: its running maximum is still -inf (and l, O zero).
+      // Causal: every query sees key 0 in the first tile, so m is finite.
       if (__ballot(mt > m_run[qb] + 8.f) != 0) {
         const float m_new = fmaxf(m_run[qb], mt);
-        const float alpha = exp2f(m_run[qb] - m_new);
+        const float alpha = (WIN && m_new == -INFINITY) ? 0.f : exp2f(m_run[qb] - m_new);
         l_run[qb] *= alpha;
 #pragma unroll
         for (int db = 0; db < 4; ++db) o[qb][db] *= alpha;
         m_run[qb] = m_new;
       }
-      const float ref = m_run[qb];
+      const float ref = (WIN && m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
       float ls = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -859,7 +874,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_bf16_kernel(AttnArgs a) 
     }
   };
   const int qt0 = (kt * 128) / QT;
-  const int nqt = (a.T + QT - 1) / QT;
+  // the last query that sees a key of this workgroup is kt*128 + 127 + W - 1
+  const int nqt = min((a.T + QT - 1) / QT, (int)(((long)kt * 128 + 127 + a.W - 1) / QT) + 1);
   const int n = nqt - qt0;
   issue(0, qt0 * QT);
   if (n > 1) issue(1, (qt0 + 1) * QT);
@@ -877,7 +893,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_bf16_kernel(AttnArgs a) 
     const lds_char* ot_ = qt_ + TILE;
     const float* vec = (const float*)(smem + (it % 3) * SLOTB + 2 * TILE);
     if (q0 + QT - 1 < kw0) continue;             // all queries precede all keys of this wave
-    const bool need_mask = (q0 < kw0 + 31) || (q0 + QT > a.T);
+    if (q0 > kw0 + 31 + a.W - 1) continue;       // all queries are past the keys' windows
+    const bool need_mask = (q0 < kw0 + 31) || (q0 + QT > a.T) || (q0 + QT - 1 >= kw0 + a.W);
     // one copy of the iteration with the causal/edge mask and one without,
     // so that each is a single scheduling region
     auto body = [&](auto maskc) {
@@ -907,7 +924,10 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_bf16_kernel(AttnArgs a) 
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g + e;
           float p = __builtin_amdgcn_exp2f(fmaf(sv[qb][r], a.sl2, -lv[e]));
-          if constexpr (MASK) p = (key > q0 + qi + e || q0 + qi + e >= a.T) ? 0.f : p;
+          if constexpr (MASK) {
+            const int qq = q0 + qi + e;
+            p = (key > qq || qq >= a.T || qq >= key + a.W) ? 0.f : p;
+          }
           sv[qb][r] = p;
           dp[qb][r] = p * (dp[qb][r] - dl[e]);      // dS
         }
@@ -980,7 +1000,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_bf16_kernel(AttnArgs a) {
   using namespace fa;
   typedef Mfma<bf16> MM;
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int BH = a.B * a.H;
   const int nqt = (a.T + 127) / 128;
   const int qt = nqt - 1 - (int)(blockIdx.x / BH);
@@ -1009,19 +1029,21 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_bf16_kernel(AttnArgs a) {
   frag_vt_offsets(vo, lane);
 
   const int last_key = min(a.T - 1, qt * 128 + 127);
-  const int nkt = last_key / KT + 1;
-  issue_kv(smem, rs, 0, ldb, koff, voff, wave, lane);
-  if (nkt > 1) issue_kv(smem + SLOT, rs, KT, ldb, koff, voff, wave, lane);
-  for (int kt = 0; kt < nkt; ++kt) {
-    if (kt + 1 < nkt) __builtin_amdgcn_s_waitcnt(0x0f70 | 8);
+  const int kt_lo = max(0, qt * 128 - a.W + 1) / KT;   // first tile inside the window
+  const int n = last_key / KT + 1 - kt_lo;
+  issue_kv(smem, rs, kt_lo * KT, ldb, koff, voff, wave, lane);
+  if (n > 1) issue_kv(smem + SLOT, rs, (kt_lo + 1) * KT, ldb, koff, voff, wave, lane);
+  for (int it = 0; it < n; ++it) {
+    if (it + 1 < n) __builtin_amdgcn_s_waitcnt(0x0f70 | 8);
     else __builtin_amdgcn_s_waitcnt(0x0f70);
     __syncthreads();
-    if (kt + 2 < nkt) issue_kv(smem + ((kt + 2) % NSLOT) * SLOT, rs, (kt + 2) * KT, ldb, koff, voff, wave, lane);
-    const lds_char* kt_ = (const lds_char*)smem + (kt % NSLOT) * SLOT;
+    if (it + 2 < n) issue_kv(smem + ((it + 2) % NSLOT) * SLOT, rs, (kt_lo + it + 2) * KT, ldb, koff, voff, wave, lane);
+    const lds_char* kt_ = (const lds_char*)smem + (it % NSLOT) * SLOT;
     const lds_char* vt_ = kt_ + TILE;
-    const int k0 = kt * KT;
+    const int k0 = (kt_lo + it) * KT;
     if (k0 > qw0 + 31) continue;
-    const bool need_mask = (k0 + KT - 1 > qw0) || (k0 + KT > a.T);
+    if (k0 + KT - 1 <= qw0 - a.W) continue;           // every key is before this wave's windows
+    const bool need_mask = (k0 + KT - 1 > qw0) || (k0 + KT > a.T) || (k0 <= qw0 + 31 - a.W);
     // Two 32-key halves, software-pipelined as in the dK/dV kernel:
     // S/dP(0); S/dP(1) with dS(0); dQ(0) with dS(1); dQ(1).  Masked and
     // unmasked tiles are separate copies (one scheduling region each).
@@ -1043,7 +1065,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_bf16_kernel(AttnArgs a) {
           float p = __builtin_amdgcn_exp2f(fmaf(sv[kb][r], a.sl2, -lse));
           if constexpr (MASK) {
             const int kk = k0 + kb * 32 + acc_row(r, lane);
-            p = (kk > q || kk >= a.T) ? 0.f : p;
+            p = (kk > q || kk >= a.T || kk <= q - a.W) ? 0.f : p;
           }
           sv[kb][r] = p * (dp[kb][r] - dlt);   // dS^T
         }

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstring>
 #include <mutex>
@@ -170,6 +171,7 @@ int check_cfg(const blk_cfg* c) {
   if (!(c->eps >= 0.f) || !(c->rope_base > 0.f)) return BLK_EINVAL;
   if (c->dtype != BLK_F32 && c->dtype != BLK_BF16) return BLK_EINVAL;
   if (c->gemm != BLK_GEMM_NATIVE && c->gemm != BLK_GEMM_FP8_E4M3) return BLK_EINVAL;
+  if (c->window < 0) return BLK_EINVAL;
   if (c->gemm == BLK_GEMM_FP8_E4M3 && c->dtype != BLK_BF16) return BLK_EUNSUPPORTED;
   // row kernels keep a row in registers: 8 chunks of 16 bytes per lane
   if ((long)c->C * (c->dtype == BLK_BF16 ? 2 : 4) > 8L * 64 * 16) return BLK_EUNSUPPORTED;
@@ -308,9 +310,19 @@ void wgrad(GemmKernel kern, GemmKernel kern_acc, GemmKernel kp, GemmKernel kp_ac
 unsigned row_blocks(long rows) { return (unsigned)((rows + 3) / 4); }
 
 // ---------------------------------------------------------------- forward
+// bf16 flash forward: the windowed instance only when the window is shorter
+// than the sequence.
+void attn_fwd_bf16(const AttnArgs& a, hipStream_t st) {
+  auto kern = a.W < a.T ? attn_fwd_bf16_kernel<true> : attn_fwd_bf16_kernel<false>;
+  need_lds(reinterpret_cast<const void*>(kern), fa::LDS);
+  const int nqt = (a.T + fa::QWG - 1) / fa::QWG;
+  hipLaunchKernelGGL(kern, dim3(nqt * a.B * a.H), dim3(256), fa::LDS, st, a);
+}
+
 template <typename T> AttnArgs attn_args(const blk_cfg& c) {
   AttnArgs a{};
   a.B = c.B; a.T = c.T; a.H = c.H; a.C = c.C;
+  a.W = (c.window <= 0 || c.window >= c.T) ? c.T : c.window;   // W >= T: causal
   a.sl2 = (float)(1.4426950408889634 / std::sqrt(128.0));   // log2(e) / sqrt(D)
   a.rsd = (float)(1.0 / std::sqrt(128.0));
   return a;
@@ -340,9 +352,7 @@ int fwd_impl(const blk_cfg& c, const T* x, const T* wqkv, const T* wo, const T* 
     a.qkv = s.qkv; a.o = s.o; a.lse = s.lse;
     Timed t("attn_fwd", st);
     if constexpr (sizeof(T) == 2) {
-      need_lds(reinterpret_cast<const void*>(attn_fwd_bf16_kernel), fa::LDS);
-      const int nqt = (c.T + fa::QWG - 1) / fa::QWG;
-      hipLaunchKernelGGL(attn_fwd_bf16_kernel, dim3(nqt * c.B * H), dim3(256), fa::LDS, st, a);
+      attn_fwd_bf16(a, st);
     } else {
       need_lds(reinterpret_cast<const void*>(attn_fwd_kernel<T>), attn_fwd_lds<T>());
       const int nqt = (c.T + 127) / 128;
@@ -561,9 +571,7 @@ int fwd_fp8(const blk_cfg& c, const bf16* x, const bf16* wqkv, const bf16* wo, c
     AttnArgs a = attn_args<bf16>(c);
     a.qkv = s.qkv; a.o = s.o; a.lse = s.lse; a.amax_o = am + AM_O;
     Timed t("attn_fwd", st);
-    need_lds(reinterpret_cast<const void*>(attn_fwd_bf16_kernel), fa::LDS);
-    const int nqt = (c.T + fa::QWG - 1) / fa::QWG;
-    hipLaunchKernelGGL(attn_fwd_bf16_kernel, dim3(nqt * c.B * H), dim3(256), fa::LDS, st, a);
+    attn_fwd_bf16(a, st);
   }
   quantize(s.o, N, C, am + AM_O, f.o, s.o_8t, Np, false, st);       // amax from attn_fwd
   {
@@ -679,6 +687,7 @@ int check_dcfg(const blk_dcfg* c) {
     return BLK_EINVAL;
   if (!(c->eps >= 0.f) || !(c->rope_base > 0.f)) return BLK_EINVAL;
   if (c->dtype != BLK_F32 && c->dtype != BLK_BF16) return BLK_EINVAL;
+  if (c->window < 0) return BLK_EINVAL;
   if (c->dtype != BLK_BF16) return BLK_EUNSUPPORTED;   // the decode kernels are bf16 only
   if (c->C > 2048 || c->B > 65535) return BLK_EUNSUPPORTED;
   if ((long)c->B * c->H * c->S_max * 128 >= (1L << 40)) return BLK_EUNSUPPORTED;
@@ -871,16 +880,17 @@ int decode_step(const blk_dcfg* cfg, const void* x, const void* w_qkv, const voi
     hipLaunchKernelGGL(dec::dec_qkv_epi_kernel, dim3(H, B), dim3(192), 0, st, (const float*)d.part, sq.S, B, H,
                        cache_len, c.S_max, c.eps, (double)c.rope_base, d.q, kc, vc);
   }
-  {  // attention of the new token over slots 0..cache_len[b]
+  const int dwin = c.window > 0 ? c.window : INT_MAX;
+  {  // attention of the new token over slots 0..cache_len[b] (the last W with a window)
     Timed t("dec_attn", st);
     hipLaunchKernelGGL(dec::dec_attn_kernel, dim3(NS, H, B), dim3(256), 0, st, (const float*)d.q,
-                       (const bf16*)kc, (const bf16*)vc, cache_len, H, c.S_max, NS,
+                       (const bf16*)kc, (const bf16*)vc, cache_len, H, c.S_max, NS, dwin,
                        (float)(1.4426950408889634 / std::sqrt(128.0)), d.opart, d.ml);
   }
   {
     Timed t("dec_combine", st);
     hipLaunchKernelGGL(dec::dec_combine_kernel, dim3(H, B), dim3(128), 0, st, (const float*)d.opart,
-                       (const float2*)d.ml, cache_len, H, c.S_max, NS, d.o);
+                       (const float2*)d.ml, cache_len, H, c.S_max, NS, dwin, d.o);
   }
   const DecSplit so = dec_split(B, C, C);
   dec_gemm("dec_gemm_o", d.o, B, static_cast<const bf16*>(w_o), C, C, so, d.part, st);

@@ -180,22 +180,27 @@ __global__ __launch_bounds__(192) void dec_qkv_epi_kernel(const float* __restric
 // output sum 2^(t_j - m) v_j, t_j = log2(e) q.k_j / sqrt(128).
 // Grid (NS, H, B), 4 waves of 64 keys.  Lane (g = lane/16, r = lane%16)
 // holds dims 8r..8r+7 of keys base + 4i + g, i = 0..15.
+// With a window W only the keys j0 = max(0, L - W) .. L-1 are visible;
+// splits wholly before j0 write nothing.
+__device__ __forceinline__ int first_visible(int L, int W) { return L > W ? L - W : 0; }
+
 __global__ __launch_bounds__(256) void dec_attn_kernel(const float* __restrict__ qbuf, const bf16* __restrict__ kc,
                                                        const bf16* __restrict__ vc, const int* __restrict__ cache_len,
-                                                       int H, int S_max, int NS, float sl2,
+                                                       int H, int S_max, int NS, int W, float sl2,
                                                        float* __restrict__ opart, float2* __restrict__ ml) {
   __shared__ float wo[4][128];
   __shared__ float wm[4], wl[4];
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int L = clamp_pos(cache_len, b, S_max) + 1;
-  if (s * KEYS >= L) return;
+  const int j0 = first_visible(L, W);
+  if (s * KEYS >= L || (s + 1) * KEYS <= j0) return;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int g = lane >> 4, r = lane & 15;
   const int kb = s * KEYS + wv * 64;
   const long head = (long)(b * H + h);
   float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, l = 0.f;
-  if (kb < L) {
+  if (kb < L && kb + 63 >= j0) {
     float q[8];
     {
       const float* qp = qbuf + head * 128 + r * 8;
@@ -238,7 +243,7 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(const float* __restrict__
         t[i] = keep + __shfl_xor(send, half, 64);
       }
     }
-    const bool valid = kb + 4 * r + g < L;
+    const bool valid = kb + 4 * r + g < L && kb + 4 * r + g >= j0;
     const float sc = valid ? t[0] : -INFINITY;
     m = wave_max(sc);
     const float p = valid ? __builtin_amdgcn_exp2f(sc - m) : 0.f;
@@ -270,7 +275,7 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(const float* __restrict__
   __syncthreads();
   if (threadIdx.x < 128) {
     const int d = threadIdx.x;
-    const float M = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));   // finite: wave 0 has keys
+    const float M = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));   // finite: some wave has keys
     float acc = 0.f, lsum = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -285,19 +290,20 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(const float* __restrict__
 }
 
 // o[b, h*128 + d] = sum_s 2^(m_s - M) o_s[d] / sum_s 2^(m_s - M) l_s over the
-// splits that hold keys.  Grid (H, B), 128 threads.
+// splits that hold visible keys.  Grid (H, B), 128 threads.
 __global__ __launch_bounds__(128) void dec_combine_kernel(const float* __restrict__ opart,
                                                           const float2* __restrict__ ml,
                                                           const int* __restrict__ cache_len, int H, int S_max,
-                                                          int NS, bf16* __restrict__ o) {
+                                                          int NS, int W, bf16* __restrict__ o) {
   const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
   const int L = clamp_pos(cache_len, b, S_max) + 1;
   const int nv = (L + KEYS - 1) / KEYS;
+  const int s0 = first_visible(L, W) / KEYS;
   const long head = (long)(b * H + h);
   float M = -INFINITY;
-  for (int s = 0; s < nv; ++s) M = fmaxf(M, ml[head * NS + s].x);
+  for (int s = s0; s < nv; ++s) M = fmaxf(M, ml[head * NS + s].x);
   float acc = 0.f, lsum = 0.f;
-  for (int s = 0; s < nv; ++s) {
+  for (int s = s0; s < nv; ++s) {
     const float2 v = ml[head * NS + s];
     const float f = __builtin_amdgcn_exp2f(v.x - M);
     acc += f * opart[(head * NS + s) * 128 + d];

@@ -5,7 +5,8 @@
 Prints ONE JSON line on stdout (details go to stderr):
   value       tokens per second of the whole step (inputs resident in HBM)
   tflops      algorithmic FLOP/s of the step (causal attention counted once:
-              per token 72*C^2 for the linear layers + 6*C*(T+1) for attention)
+              per token 72*C^2 for the linear layers + 6*C*(T+1) for attention;
+              with a window W, only the visible query-key pairs)
   roofline    the launch site with the largest share of the step, timed with
               hipEvents around each of its launches over a second pass of the
               same K steps (block_timing_*), against the bf16 dense MFMA peak
@@ -38,23 +39,39 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def window_of(sh) -> int:
+    """Keys a query can see at most: the window, or T for causal."""
+    w = getattr(sh, "window", 0)
+    return sh.T if w <= 0 or w >= sh.T else w
+
+
+def attn_matmul_flops(sh) -> float:
+    """FLOPs of one T x T x D attention matmul over all heads and sequences,
+    counting only the visible (query, key) pairs: sum_i min(i+1, W) per
+    sequence (T(T+1)/2 for causal)."""
+    T, W = sh.T, window_of(sh)
+    pairs = W * (W + 1) / 2.0 + (T - W) * float(W)
+    return 2.0 * sh.B * sh.C * pairs
+
+
 def step_flops(sh) -> float:
-    N, C, T = sh.B * sh.T, sh.C, sh.T
-    return float(N) * (72.0 * C * C + 6.0 * C * (T + 1))
+    N, C = sh.B * sh.T, sh.C
+    # linear layers 72 C^2 per token; attention 2 matmuls forward, 4 backward
+    return float(N) * 72.0 * C * C + 6.0 * attn_matmul_flops(sh)
 
 
 def step_flops_nanochat(sh) -> float:
-    """The convention of nanochat's estimate_flops (6 x matmul params + 12*C*T
-    per token for attention), which reproduces the depth table on the
-    flicky.cc nanochat page."""
-    N, C, T = sh.B * sh.T, sh.C, sh.T
-    return float(N) * (72.0 * C * C + 12.0 * C * T)
+    """The convention of nanochat's estimate_flops (6 x matmul params + 12*C*W
+    per token for attention, W the window or T), which reproduces the depth
+    table on the flicky.cc nanochat page."""
+    N, C = sh.B * sh.T, sh.C
+    return float(N) * (72.0 * C * C + 12.0 * C * window_of(sh))
 
 
 def site_flops(sh) -> dict:
     """Algorithmic FLOPs of one launch of each launch site."""
-    N, C, F, T = sh.B * sh.T, sh.C, sh.F, sh.T
-    att = float(N) * C * (T + 1)          # one causal T x T x D matmul over all heads
+    N, C, F = sh.B * sh.T, sh.C, sh.F
+    att = attn_matmul_flops(sh)           # one attention matmul over the visible pairs
     g = {
         "gemm_qkv_fwd": 2.0 * N * C * 3 * C, "gemm_o_fwd": 2.0 * N * C * C,
         "gemm_fc_fwd": 2.0 * N * C * F, "gemm_proj_fwd": 2.0 * N * F * C,
@@ -96,7 +113,8 @@ def cpu_baseline(sh, inp, budget_s: float = 12.0) -> dict:
     t0 = time.perf_counter()
     nseq = 0
     while nseq < sh.B:
-        c = ob.block_fwd(inp["x"][nseq:nseq + 1], *W, H=sh.H, eps=sh.eps, rope_base=sh.rope_base)
+        c = ob.block_fwd(inp["x"][nseq:nseq + 1], *W, H=sh.H, eps=sh.eps, rope_base=sh.rope_base,
+                         window=sh.window or None)
         ob.block_bwd(inp["dy"][nseq:nseq + 1], c, *W, H=sh.H)
         nseq += 1
         if time.perf_counter() - t0 >= budget_s:
@@ -200,7 +218,7 @@ def bench_train(args) -> int:
     W = [dev(inp[k]) for k in ("w_qkv", "w_o", "w_fc", "w_proj")]
     cfg = bl.BlockConfig(B=sh.B, T=sh.T, C=sh.C, H=sh.H, F=sh.F, eps=sh.eps, rope_base=sh.rope_base,
                          dtype=bl.BLK_BF16 if dt == "bf16" else bl.BLK_F32,
-                         gemm=bl.BLK_GEMM_FP8_E4M3 if sh.gemm == "fp8" else bl.BLK_GEMM_NATIVE)
+                         gemm=bl.BLK_GEMM_FP8_E4M3 if sh.gemm == "fp8" else bl.BLK_GEMM_NATIVE, window=sh.window)
     y, dx = torch.empty_like(x), torch.empty_like(x)
     dW = [torch.empty(w.shape, dtype=torch.float32, device="cuda:0") for w in W]
     saved = torch.empty(bl.block_saved_bytes(cfg), dtype=torch.uint8, device="cuda:0")
@@ -266,8 +284,8 @@ def bench_train(args) -> int:
     frac = tflops / peak
     if sh.gemm == "fp8":
         # mixed roofline: the linear layers at the fp8 dense peak, attention at the bf16 one
-        N, C, T = sh.B * sh.T, sh.C, sh.T
-        t_star = N * 72.0 * C * C / (PEAK_TFLOPS["fp8"] * 1e12) + N * 6.0 * C * (T + 1) / (PEAK_TFLOPS["bf16"] * 1e12)
+        N, C = sh.B * sh.T, sh.C
+        t_star = N * 72.0 * C * C / (PEAK_TFLOPS["fp8"] * 1e12) + 6.0 * attn_matmul_flops(sh) / (PEAK_TFLOPS["bf16"] * 1e12)
         frac = t_star / (ms * 1e-3)
     cpu = None
     if not args.no_cpu_baseline:
@@ -280,7 +298,8 @@ def bench_train(args) -> int:
         "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3+bf16" if sh.gemm == "fp8" else dt,
         "data": "synthetic",
         "config": {"workload": args.workload, "B": sh.B, "T": sh.T, "C": sh.C, "H": sh.H, "D": sh.D, "F": sh.F,
-                   "gemm": sh.gemm, "tokens_per_step": tokens, "parallelism": "none (1 GPU)"},
+                   "gemm": sh.gemm, "window": window_of(sh), "tokens_per_step": tokens,
+                   "parallelism": "none (1 GPU)"},
         "tflops": round(tflops, 2), "frac_of_peak": round(frac, 4),
         "tflops_nanochat_convention": round(step_flops_nanochat(sh) / (ms * 1e-3) / 1e12, 2),
         "roofline": roof, "cpu_baseline": cpu,
@@ -291,9 +310,13 @@ def bench_train(args) -> int:
 
 def decode_attn_bytes(sh, lens) -> float:
     """Algorithmic HBM bytes of one decode attention launch: the keys and
-    values of slots 0..L_b of every (sequence, head), bf16, and the q rows."""
+    values of the visible slots (0..L_b, or the last W of them) of every
+    (sequence, head), bf16, and the q rows."""
     import numpy as np
-    kv = 2.0 * sh.H * 128 * 2 * float(np.sum(np.asarray(lens, dtype=np.int64) + 1))
+    keys = np.asarray(lens, dtype=np.int64) + 1
+    if getattr(sh, "window", 0) > 0:
+        keys = np.minimum(keys, sh.window)
+    kv = 2.0 * sh.H * 128 * 2 * float(np.sum(keys))
     return kv + sh.B * sh.H * 128 * 4.0
 
 
@@ -350,7 +373,8 @@ def bench_decode(args) -> int:
     x = dev(inp["x"])
     W = [dev(inp[k]) for k in ("w_qkv", "w_o", "w_fc", "w_proj")]
     kc, vc = dev(inp["k_cache"]), dev(inp["v_cache"])
-    cfg = bl.DecodeConfig(B=sh.B, C=sh.C, H=sh.H, F=sh.F, S_max=sh.S_max, eps=sh.eps, rope_base=sh.rope_base)
+    cfg = bl.DecodeConfig(B=sh.B, C=sh.C, H=sh.H, F=sh.F, S_max=sh.S_max, eps=sh.eps, rope_base=sh.rope_base,
+                          window=sh.window)
     y = torch.empty_like(x)
     scratch = torch.empty(bl.decode_scratch_bytes(cfg), dtype=torch.uint8, device="cuda:0")
     stream = torch.cuda.current_stream()

@@ -47,6 +47,7 @@ class BlockShape:
     rope_base: float = 10000.0
     dtype: str = "bf16"
     gemm: str = "native"
+    window: int = 0          # attention window (0: causal over the whole sequence)
 
     @property
     def N(self) -> int:
@@ -69,6 +70,7 @@ class DecodeShape:
     eps: float = 1e-6
     rope_base: float = 10000.0
     dtype: str = "bf16"
+    window: int = 0
 
 
 def from_depth(depth: int, aspect: int = 64, head_dim: int = 128) -> tuple[int, int, int]:
@@ -92,6 +94,8 @@ WORKLOADS = {
     "d12_bf16": _shape(12, B=8, T=2048),
     "d20_bf16": _shape(20, B=32, T=2048),
     "d26_fp8": _shape(26, B=16, T=2048, gemm="fp8"),
+    # a short-window layer of the SSSL pattern: window T/4
+    "d20_bf16_swa": _shape(20, B=32, T=2048, window=512),
 }
 _C20, _H20, _F20 = from_depth(20)
 DECODE_WORKLOADS = {

@@ -77,6 +77,13 @@ typedef struct {
   float rope_base;     /* rotary base (10000)                                */
   int32_t dtype;       /* enum blk_dtype                                     */
   int32_t gemm;        /* enum blk_gemm_mode                                 */
+  int32_t window;      /* attention window W: 0 = causal over the whole
+                        * sequence; W >= 1: token i attends to tokens
+                        * i-W < j <= i (W >= T is the same as 0).  The
+                        * flicky.cc course page, section on what changed
+                        * since GPT-2, alternates short windows of a quarter
+                        * of the context with full ones across layers; the
+                        * per-layer choice is the caller's.  < 0: EINVAL.   */
 } blk_cfg;
 
 typedef struct {
@@ -85,6 +92,8 @@ typedef struct {
   int32_t S_max;       /* cache capacity (slots) per sequence and head       */
   float eps, rope_base;
   int32_t dtype;       /* BLK_BF16 or BLK_F32                                */
+  int32_t window;      /* as blk_cfg.window: the new token at position p
+                        * attends to slots p-W < j <= p (0 = all 0..p)       */
 } blk_dcfg;
 
 /* Bytes of the activation store that block_fwd fills for block_bwd.

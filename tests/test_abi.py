@@ -92,6 +92,7 @@ def test_fwd_argument_errors(lib):
     assert _fwd(_cfg(gemm=bl.BLK_GEMM_FP8_E4M3, dtype=bl.BLK_F32)) == bl.binding.BLK_EUNSUPPORTED
     assert _fwd(_cfg(gemm=5)) == bl.binding.BLK_EINVAL
     assert _fwd(_cfg(eps=float("nan"))) == bl.binding.BLK_EINVAL
+    assert _fwd(_cfg(window=-1)) == bl.binding.BLK_EINVAL
 
 
 def test_bwd_argument_errors(lib):
@@ -127,7 +128,8 @@ def test_decode_sizes_and_argument_errors(lib):
     # at least the activations h1, o, h2 (bf16), y1, q (fp32), a (bf16) and the split partials
     assert need >= 64 * (1280 * (2 * 3 + 4) + 1280 * 4 + 5120 * 2)
     assert need < 64 << 20
-    for bad in (_dcfg(D=64), _dcfg(C=1000), _dcfg(F=100), _dcfg(B=0), _dcfg(S_max=0), _dcfg(dtype=7)):
+    for bad in (_dcfg(D=64), _dcfg(C=1000), _dcfg(F=100), _dcfg(B=0), _dcfg(S_max=0), _dcfg(dtype=7),
+                _dcfg(window=-3)):
         assert bl.decode_scratch_bytes(bad) == 0
         assert _dec(bad) == bl.binding.BLK_EINVAL
     assert _dec(_dcfg(dtype=bl.BLK_F32)) == bl.binding.BLK_EUNSUPPORTED
@@ -144,3 +146,18 @@ def test_strerror(lib):
     for code in range(6):
         assert isinstance(bl.block_strerror(code), str) and bl.block_strerror(code)
     assert "unknown" in bl.block_strerror(99)
+
+
+def test_layer_window_pattern():
+    # S layers: a window of a quarter of the context; L layers and the last
+    # layer: the whole context (0)
+    T = 2048
+    assert [bl.layer_window(i, 8, T) for i in range(8)] == [512, 512, 512, 0, 512, 512, 512, 0]
+    assert [bl.layer_window(i, 6, T) for i in range(6)] == [512, 512, 512, 0, 512, 0]
+    assert [bl.layer_window(i, 4, T, "L") for i in range(4)] == [0, 0, 0, 0]
+    assert [bl.layer_window(i, 5, 512, "SL") for i in range(5)] == [128, 0, 128, 0, 0]
+    for bad in ("", "SX"):
+        with pytest.raises(ValueError):
+            bl.layer_window(0, 4, T, bad)
+    with pytest.raises(ValueError):
+        bl.layer_window(4, 4, T)

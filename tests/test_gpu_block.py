@@ -76,6 +76,47 @@ def test_d20_full_size_sampled():
     _sampled_full("d20_bf16", (0, 31))
 
 
+@pytest.mark.parametrize("B,T,C,W", [
+    (2, 300, 256, 1),       # each token attends to itself only
+    (2, 300, 256, 64),      # window of one key tile
+    (2, 300, 256, 100),     # window edge inside tiles, ragged tail
+    (1, 520, 384, 130),     # window crossing query-tile and workgroup boundaries
+    (1, 700, 256, 257),     # just over a 256-query workgroup
+    (2, 192, 256, 300),     # window >= T: the causal path
+])
+def test_bf16_window(B, T, C, W):
+    _parity(BlockShape(B=B, T=T, C=C, H=C // 128, F=4 * C, dtype="bf16", window=W), seed=4)
+
+
+@pytest.mark.parametrize("T,W", [(130, 45), (200, 1), (97, 64)])
+def test_f32_window(T, W):
+    _parity(BlockShape(B=2, T=T, C=256, H=2, F=1024, dtype="f32", window=W), seed=6)
+
+
+def test_d20_window_full_size_sampled():
+    _sampled_full("d20_bf16_swa", (0, 31))
+
+
+def test_window_locality_bitwise():
+    # with a window W, changing input row t changes output rows t .. t+W-1
+    # only; every other row is bitwise the same
+    W = 70
+    sh = BlockShape(B=1, T=400, C=256, H=2, F=1024, dtype="bf16", window=W)
+    note("window locality")
+    inp = make_block_inputs(sh, seed=8)
+    g = GpuBlock(sh, inp)
+    g.fwd()
+    y0 = g.results()["y"].copy()
+    t = 150
+    x2 = inp["x"].copy()
+    x2[:, t] = np.random.default_rng(9).standard_normal(x2[:, t].shape)
+    g.fwd(x=to_dev(x2, "bf16"))
+    y1 = g.results()["y"]
+    changed = np.nonzero(np.any(y0[0] != y1[0], axis=-1))[0]
+    assert changed.min() == t and changed.max() <= t + W - 1, changed
+    assert np.array_equal(y0[:, :t], y1[:, :t]) and np.array_equal(y0[:, t + W:], y1[:, t + W:])
+
+
 def test_causality_bitwise():
     sh = BlockShape(B=2, T=200, C=256, H=2, F=1024, dtype="bf16")
     note("causality")

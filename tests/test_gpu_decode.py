@@ -28,7 +28,7 @@ class GpuDecode:
         import backward_gpt_block_amd as bl
         self.sh = sh
         self.cfg = bl.DecodeConfig(B=sh.B, C=sh.C, H=sh.H, F=sh.F, S_max=sh.S_max, eps=sh.eps,
-                                   rope_base=sh.rope_base)
+                                   rope_base=sh.rope_base, window=sh.window)
         self.w = [to_dev(inp[k], "bf16") for k in WNAMES]
         self.kc = to_dev(inp["k_cache"], "bf16")
         self.vc = to_dev(inp["v_cache"], "bf16")
@@ -59,7 +59,7 @@ def _check_step(sh, inp, g: GpuDecode, x, lens, before_bits, in_place=False):
     y = g.step(x, lens, in_place=in_place)
     W = [inp[k] for k in WNAMES]
     y_ref, kc_ref, vc_ref = ob.decode_step(x, *W, inp["k_cache"], inp["v_cache"], lens, H=sh.H, eps=sh.eps,
-                                           rope_base=sh.rope_base)
+                                           rope_base=sh.rope_base, window=sh.window or None)
     e = rel_err(y, y_ref)
     kb, vb = g.caches_bits()
     bidx = np.arange(sh.B)
@@ -125,3 +125,20 @@ def test_decode_d20_uniform_2048():
 
 def test_decode_d20_ragged_128_2048():
     _decode_case(DECODE_WORKLOADS["d20_decode"], ragged=True, ragged_lo=128, ragged_hi=2048)
+
+
+def test_decode_window_edges():
+    # window W = 100: lengths below, at and past W, and windows that start
+    # inside a later 256-key split
+    sh = DecodeShape(B=6, C=256, H=2, F=1024, S_max=600, window=100)
+    _decode_case(sh, lens=[0, 50, 99, 100, 299, 599])
+
+
+def test_decode_window_two_chained_steps():
+    _decode_case(DecodeShape(B=3, C=256, H=2, F=1024, S_max=520, window=257), lens=[5, 256, 400], steps=2)
+
+
+def test_decode_d20_window_512_ragged():
+    sh = DECODE_WORKLOADS["d20_decode"]
+    sh = DecodeShape(B=sh.B, C=sh.C, H=sh.H, F=sh.F, S_max=sh.S_max, window=512)
+    _decode_case(sh, ragged=True, ragged_lo=128, ragged_hi=2048)

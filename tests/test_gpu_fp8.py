@@ -73,7 +73,7 @@ def _fp8_parity(sh: BlockShape, seed=0, keep=None, deep=()):
         res["y"], res["dx"] = res["y"][list(keep)], res["dx"][list(keep)]
     emu = fp8_block.block_fwd_bwd(inp["x"], inp["w_qkv"], inp["w_o"], inp["w_fc"], inp["w_proj"], inp["dy"],
                                   H=sh.H, eps=sh.eps, rope_base=sh.rope_base,
-                                  batch=None if keep is None else list(keep), log=note)
+                                  batch=None if keep is None else list(keep), log=note, window=sh.window or None)
     keys = [k for k in emu if k not in deep]
     errs = compare(res, emu, TOL["fp8"], keys=keys)
     for k in deep:
@@ -93,6 +93,10 @@ def _fp8_parity(sh: BlockShape, seed=0, keep=None, deep=()):
 @pytest.mark.parametrize("B,T,C", [(2, 256, 256), (1, 77, 384), (3, 130, 256)])
 def test_fp8_block_ragged(B, T, C):
     _fp8_parity(BlockShape(B=B, T=T, C=C, H=C // 128, F=4 * C, dtype="bf16", gemm="fp8"))
+
+
+def test_fp8_block_window():
+    _fp8_parity(BlockShape(B=2, T=300, C=256, H=2, F=1024, dtype="bf16", gemm="fp8", window=100))
 
 
 @pytest.mark.timeout(900)
