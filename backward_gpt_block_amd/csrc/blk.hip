@@ -104,14 +104,19 @@ Fwd8 carve_fwd8(const blk_cfg& c, void* p) {
   return f;
 }
 
-// Split-k factor of a weight-gradient GEMM: enough workgroups to fill the
-// chip about four times over, each split at least 8 k-steps long.
+// Split-K count of a weight gradient: the smallest split count whose
+// workgroups fill at least 85% of their last wave over the 256 CUs (fewer
+// splits, fewer fp32 partials to write and reduce), keeping >= 8 k-steps
+// per split.
 int wgrad_splits(int M, int N, long K, int BK) {
-  const int tiles = ((M + 255) / 256) * ((N + 255) / 256);
-  int s = std::max(1, 1024 / tiles);
+  const long tiles = (long)((M + 255) / 256) * ((N + 255) / 256);
   const long ksteps = (K + BK - 1) / BK;
-  s = (int)std::min<long>(s, std::max<long>(1, ksteps / 8));
-  return s;
+  const long smax = std::max<long>(1, std::min<long>(32, ksteps / 8));
+  for (long s = 1; s <= smax; ++s) {
+    const long wg = tiles * s, waves = (wg + 255) / 256;
+    if (wg * 100 >= 85 * waves * 256) return (int)s;
+  }
+  return (int)smax;
 }
 
 template <typename T> struct BwdScratch {
