@@ -36,6 +36,11 @@ class _DCfg(ctypes.Structure):
                 ("rope_base", ctypes.c_float), ("dtype", ctypes.c_int32), ("window", ctypes.c_int32)]
 
 
+class _HCfg(ctypes.Structure):
+    _fields_ = [("N", ctypes.c_int32), ("C", ctypes.c_int32), ("V", ctypes.c_int32), ("eps", ctypes.c_float),
+                ("dtype", ctypes.c_int32)]
+
+
 @dataclasses.dataclass(frozen=True)
 class BlockConfig:
     B: int
@@ -71,6 +76,18 @@ class DecodeConfig:
     def c(self) -> _DCfg:
         return _DCfg(self.B, self.C, self.H, self.D, self.F, self.S_max, self.eps, self.rope_base, self.dtype,
                      self.window)
+
+
+@dataclasses.dataclass(frozen=True)
+class HeadConfig:
+    N: int
+    C: int
+    V: int
+    eps: float = 1e-6
+    dtype: int = BLK_BF16
+
+    def c(self) -> _HCfg:
+        return _HCfg(self.N, self.C, self.V, self.eps, self.dtype)
 
 
 def layer_window(layer: int, n_layer: int, T: int, pattern: str = "SSSL") -> int:
@@ -119,6 +136,13 @@ def library() -> ctypes.CDLL:
         lib.decode_scratch_bytes.restype = sz
         lib.decode_step.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.decode_step.restype = i32
+        ph = ctypes.POINTER(_HCfg)
+        lib.head_scratch_bytes.argtypes = [ph]
+        lib.head_scratch_bytes.restype = sz
+        lib.head_loss_fwd.argtypes = [ph, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.head_loss_fwd.restype = i32
+        lib.head_loss_bwd.argtypes = [ph, vp, vp, vp, vp, ctypes.c_float, vp, vp, i32, vp, sz, vp]
+        lib.head_loss_bwd.restype = i32
         lib.block_fp8_quantize.argtypes = [vp, sz, vp, vp, vp]
         lib.block_fp8_quantize.restype = i32
         lib.block_timing_enable.argtypes = [i32]
@@ -206,6 +230,25 @@ def decode_step(cfg: DecodeConfig, x, w_qkv, w_o, w_fc, w_proj, k_cache, v_cache
                                  _ptr(k_cache), _ptr(v_cache), _ptr(cache_len), _ptr(y), _ptr(scratch),
                                  _nbytes(scratch, scratch_bytes), _stream(stream))
     return _check(code, "decode_step", raise_on_error)
+
+
+def head_scratch_bytes(cfg: HeadConfig) -> int:
+    return library().head_scratch_bytes(ctypes.byref(cfg.c()))
+
+
+def head_loss_fwd(cfg: HeadConfig, x, w_lm, targets, loss, lse, scratch=None, *, scratch_bytes=None, stream=None,
+                  raise_on_error=True) -> int:
+    code = library().head_loss_fwd(ctypes.byref(cfg.c()), _ptr(x), _ptr(w_lm), _ptr(targets), _ptr(loss), _ptr(lse),
+                                   _ptr(scratch), _nbytes(scratch, scratch_bytes), _stream(stream))
+    return _check(code, "head_loss_fwd", raise_on_error)
+
+
+def head_loss_bwd(cfg: HeadConfig, x, w_lm, targets, lse, dloss: float, dx, dw_lm, accumulate=0, scratch=None, *,
+                  scratch_bytes=None, stream=None, raise_on_error=True) -> int:
+    code = library().head_loss_bwd(ctypes.byref(cfg.c()), _ptr(x), _ptr(w_lm), _ptr(targets), _ptr(lse),
+                                   ctypes.c_float(dloss), _ptr(dx), _ptr(dw_lm), int(accumulate), _ptr(scratch),
+                                   _nbytes(scratch, scratch_bytes), _stream(stream))
+    return _check(code, "head_loss_bwd", raise_on_error)
 
 
 def block_fp8_quantize(x, n: int, codes, amax, *, stream=None, raise_on_error=True) -> int:

@@ -18,6 +18,7 @@
 #include "elementwise.cuh"
 #include "fp8.cuh"
 #include "gemm.cuh"
+#include "head.cuh"
 
 using namespace blk;
 
@@ -766,6 +767,54 @@ size_t fwd_scratch_bytes(const blk_cfg& c, bool with_saved) {
   return b;
 }
 
+// ---------------------------------------------------------------- language-model head
+int check_hcfg(const blk_hcfg* c) {
+  if (!c) return BLK_EINVAL;
+  if (c->N < 1 || c->C < 128 || c->C % 128 != 0 || c->V < 64 || c->V % 64 != 0) return BLK_EINVAL;
+  if (!(c->eps >= 0.f)) return BLK_EINVAL;
+  if (c->dtype != BLK_F32 && c->dtype != BLK_BF16) return BLK_EINVAL;
+  if (c->dtype != BLK_BF16) return BLK_EUNSUPPORTED;                 // the head kernels are bf16 only
+  if ((long)c->C * 2 > 8L * 64 * 16) return BLK_EUNSUPPORTED;        // row kernels keep a row in registers
+  // weight gradient with K = N tokens: the eight-wave body (N a multiple of
+  // 64) handles any size; the four-wave fallback needs 32-bit offsets
+  if (c->N % 64 != 0 && (long)c->N * c->V * 2 >= (1L << 31)) return BLK_EUNSUPPORTED;
+  if ((long)c->N * c->V >= (1L << 40)) return BLK_EUNSUPPORTED;
+  return BLK_OK;
+}
+
+struct HeadScratch {
+  bf16* h; float* r;                                  // normalised rows, 1/rms
+  float2* part; float* tgt_logit;                     // forward: segment pairs, target logits
+  float* nll_part; int* cnt_part; int* count;         // loss reduction
+  bf16* dz; bf16* wt; bf16* dh; float* wpart;         // backward
+  size_t bytes;
+};
+
+int head_lse_blocks(const blk_hcfg& c) { return (c.N + 3) / 4; }
+
+HeadScratch carve_head(const blk_hcfg& c, void* base, bool bwd) {
+  Carver k(base);
+  HeadScratch s{};
+  const long N = c.N, C = c.C, V = c.V;
+  s.h = k.take<bf16>(N * C);
+  s.r = k.take<float>(N);
+  s.nll_part = k.take<float>(head_lse_blocks(c));
+  s.cnt_part = k.take<int>(head_lse_blocks(c));
+  s.count = k.take<int>(1);
+  if (!bwd) {
+    s.part = k.take<float2>(N * ((V + 127) / 128));
+    s.tgt_logit = k.take<float>(N);
+  } else {
+    s.dz = k.take<bf16>(N * V);
+    s.wt = k.take<bf16>(C * V);
+    s.dh = k.take<bf16>(N * C);
+    const int sp = wgrad_splits((int)V, (int)C, N, GemmTile<bf16>::BK);
+    if (sp > 1) s.wpart = k.take<float>((size_t)sp * V * C);
+  }
+  s.bytes = (k.off + 255) & ~size_t(255);
+  return s;
+}
+
 }  // namespace
 
 extern "C" {
@@ -961,6 +1010,94 @@ int block_timing_read(int max, const char** names, double* total_ms, int* counts
   g_recs.clear();
   g_pool_used = 0;
   return n;
+}
+
+size_t head_scratch_bytes(const blk_hcfg* cfg) {
+  if (check_hcfg(cfg) != BLK_OK) return 0;
+  return std::max(carve_head(*cfg, nullptr, false).bytes, carve_head(*cfg, nullptr, true).bytes);
+}
+
+int head_loss_fwd(const blk_hcfg* cfg, const void* x, const void* w_lm, const int32_t* targets, float* loss,
+                  float* lse, void* scratch, size_t scratch_sz, void* stream) {
+  int e = check_hcfg(cfg);
+  if (e) return e;
+  const blk_hcfg& c = *cfg;
+  if (!x || !w_lm || !targets || !loss || !lse || !scratch) return BLK_EINVAL;
+  for (const void* p : {x, w_lm, (const void*)scratch})
+    if (!aligned(p)) return BLK_EALIGN;
+  if ((reinterpret_cast<uintptr_t>(targets) | reinterpret_cast<uintptr_t>(loss) | reinterpret_cast<uintptr_t>(lse)) & 3)
+    return BLK_EALIGN;
+  const HeadScratch s = carve_head(c, scratch, false);
+  if (scratch_sz < s.bytes) return BLK_ENOSPC;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int N = c.N, C = c.C, V = c.V;
+  {
+    Timed t("head_rmsnorm", st);
+    hipLaunchKernelGGL(rmsnorm_fwd_kernel<bf16>, dim3(row_blocks(N)), dim3(256), 0, st, (const bf16*)x, s.h, s.r, N,
+                       C, c.eps, (unsigned*)nullptr);
+  }
+  {
+    GemmArgs g = gargs(s.h, C, w_lm, C, N, V, C);
+    g.tgt = targets; g.lse_part = s.part; g.nseg = (V + 127) / 128; g.tgt_logit = s.tgt_logit;
+    gemm_pp<bf16>(gemm_head_fwd, "gemm_head_fwd", g, st);
+  }
+  {
+    Timed t("head_lse", st);
+    hipLaunchKernelGGL(head::head_lse_kernel, dim3(head_lse_blocks(c)), dim3(256), 0, st, (const float2*)s.part,
+                       (V + 127) / 128, (const float*)s.tgt_logit, (const int*)targets, N, V, lse, s.nll_part,
+                       s.cnt_part);
+    hipLaunchKernelGGL(head::head_loss_kernel, dim3(1), dim3(1024), 0, st, (const float*)s.nll_part,
+                       (const int*)s.cnt_part, head_lse_blocks(c), loss, s.count);
+  }
+  return launch_status();
+}
+
+int head_loss_bwd(const blk_hcfg* cfg, const void* x, const void* w_lm, const int32_t* targets, const float* lse,
+                  float dloss, void* dx, float* dw_lm, int accumulate, void* scratch, size_t scratch_sz,
+                  void* stream) {
+  int e = check_hcfg(cfg);
+  if (e) return e;
+  const blk_hcfg& c = *cfg;
+  if (!x || !w_lm || !targets || !lse || !dx || !dw_lm || !scratch) return BLK_EINVAL;
+  if (accumulate != 0 && accumulate != 1) return BLK_EINVAL;
+  if (x == dx) return BLK_EINVAL;
+  for (const void* p : {x, w_lm, (const void*)dx, (const void*)dw_lm, (const void*)scratch})
+    if (!aligned(p)) return BLK_EALIGN;
+  if ((reinterpret_cast<uintptr_t>(targets) | reinterpret_cast<uintptr_t>(lse)) & 3) return BLK_EALIGN;
+  const HeadScratch s = carve_head(c, scratch, true);
+  if (scratch_sz < s.bytes) return BLK_ENOSPC;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int N = c.N, C = c.C, V = c.V;
+  {
+    Timed t("head_rmsnorm", st);
+    hipLaunchKernelGGL(rmsnorm_fwd_kernel<bf16>, dim3(row_blocks(N)), dim3(256), 0, st, (const bf16*)x, s.h, s.r, N,
+                       C, c.eps, (unsigned*)nullptr);
+    hipLaunchKernelGGL(head::head_count_kernel, dim3(1), dim3(1024), 0, st, (const int*)targets, N, V, s.count);
+  }
+  {  // dz = dloss/count * (softmax(z) - onehot), z recomputed
+    GemmArgs g = gargs(s.h, C, w_lm, C, N, V, C);
+    g.out = s.dz; g.ldo = V;
+    g.tgt = targets; g.lse_in = lse; g.count = s.count; g.dscale = dloss;
+    gemm_pp<bf16>(gemm_head_dz, "gemm_head_dz", g, st);
+  }
+  {
+    Timed t("transpose_head", st);
+    hipLaunchKernelGGL(transpose_kernel<bf16>, dim3(C / 64, V / 64), dim3(256), 0, st, (const bf16*)w_lm, s.wt, V, C);
+  }
+  {  // dh = dz W
+    GemmArgs g = gargs(s.dz, V, s.wt, V, N, C, V);
+    g.out = s.dh; g.ldo = C;
+    gemm_pp<bf16>(gemm_head_dgrad, "gemm_head_dgrad", g, st);
+  }
+  // dW = dz^T h  (fp32, overwrite or accumulate)
+  wgrad<bf16>(gemm_head_wgrad<bf16>, gemm_head_wgrad_acc<bf16>, gemm_head_wgrad_pp, gemm_head_wgrad_acc_pp,
+              "gemm_head_wgrad", s.dz, s.h, dw_lm, V, C, N, accumulate, s.wpart, st);
+  {
+    Timed t("head_rmsnorm_bwd", st);
+    hipLaunchKernelGGL(rmsnorm_bwd_kernel<bf16>, dim3(row_blocks(N)), dim3(256), 0, st, (const bf16*)nullptr,
+                       (const bf16*)s.dh, (const bf16*)s.h, (const float*)s.r, (bf16*)dx, N, C, (unsigned*)nullptr);
+  }
+  return launch_status();
 }
 
 const char* block_strerror(int code) {

@@ -94,7 +94,11 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const T* __restrict__ 
       float a[EL], b[EL], g[EL];
       Chunk<T>::unpack(cd[i], a);
       Chunk<T>::unpack(ch_[i], b);
-      Chunk<T>::unpack(ld16(resid + row * C + ch * EL), g);
+      if (resid) Chunk<T>::unpack(ld16(resid + row * C + ch * EL), g);
+      else {
+#pragma unroll
+        for (int e = 0; e < EL; ++e) g[e] = 0.f;
+      }
 #pragma unroll
       for (int e = 0; e < EL; ++e) {
         g[e] += rr * (a[e] - b[e] * mean);

@@ -35,6 +35,9 @@ enum EpiKind : int {
   EPI_F32_ADD = 5,  // out += alpha*acc                        (float)
   EPI_ROPE = 6,     // q, k columns: rotary then QK-norm; v columns stored (TO)
   EPI_DELTA = 7,    // out = alpha*acc, and delta = per-head row dot of out with aux (TO)
+  EPI_LSE = 8,      // head forward: per row and 128-column segment, max and sum of exp of
+                    // the logits (lse_part), and the logit at the row's target (nothing stored)
+  EPI_DZ = 9,       // head backward: out = dscale/count * (exp(z - lse) - [col == target]) (TO)
 };
 
 struct GemmArgs {
@@ -60,6 +63,18 @@ struct GemmArgs {
   unsigned* amax_out;   // fp8 mode: absolute maximum of the stored output (float bits), or null
   int T, H, C;
   float eps;
+  // EPI_LSE / EPI_DZ (language-model head; rows = tokens, columns = vocabulary):
+  // tgt[row] target id (counted when 0 <= tgt < N); lse_part[row*nseg + col/128]
+  // = (max, sum exp(z - max)) of a 128-column segment; tgt_logit[row] = z at
+  // the target; lse_in[row] the row's log-sum-exp; *count the counted rows;
+  // dscale the upstream gradient of the mean loss.
+  const int* tgt;
+  float2* lse_part;
+  int nseg;
+  float* tgt_logit;
+  const float* lse_in;
+  const int* count;
+  float dscale;
 };
 
 template <typename TI> struct GemmTile {
@@ -226,6 +241,21 @@ __device__ __forceinline__ void epi8(const GemmArgs& g, int split, int row, int 
     }
     st16(p, a);
     st16(p + 4, b);
+  } else if constexpr (EPI == EPI_DZ) {
+    const int t = g.tgt[row];
+    const bool counted = t >= 0 && t < g.N;
+    const float sc = counted ? g.dscale / (float)max(*g.count, 1) : 0.f;
+    const float ls = g.lse_in[row];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float p = __builtin_amdgcn_exp2f((f[e] - ls) * 1.4426950408889634f);
+      if (col + e == t) p -= 1.f;
+      f[e] = p * sc;
+    }
+    constexpr int EL = Chunk<TO>::N;
+    TO* o = static_cast<TO*>(g.out) + (long)row * g.ldo + col;
+#pragma unroll
+    for (int h = 0; h < 8 / EL; ++h) st16_out<NT>(o + h * EL, Chunk<TO>::pack(f + h * EL));
   } else if constexpr (EPI == EPI_ROPE) {
     // 16 consecutive lanes hold one 128-wide head of the row (8 columns
     // each); rotary pairs (i, i + 64) sit 8 lanes apart
@@ -496,26 +526,31 @@ __device__ __forceinline__ int toff(int row, int chunk) { return row * 512 + ((c
 // One operand's share of a stage for wave q: k-rows 16q .. 16q+15, two
 // 512-byte rows (4 full cache lines each) per 1 KiB load.
 struct PPStagerT {
-  i32x4 rs;        // buffer resource from (k = kbeg, first column of the tile)
-  uint32_t x;      // byte offset of this lane's row at k = 0, load 0
-  uint32_t ldb;    // bytes per k-row
-  uint32_t cl;     // this lane's chunk byte offset before the per-load swizzle term
+  const char* base;  // (k = kbeg, first column of the tile)
+  long left;         // bytes from base to the end of the matrix
+  uint32_t x;        // byte offset of this lane's row in a stage, load 0
+  uint32_t ldb;      // bytes per k-row
+  uint32_t cl;       // this lane's chunk byte offset before the per-load swizzle term
   __device__ __forceinline__ void init(const void* p, long ld, long K, int c0, int kbeg, int q, int lane) {
     const long first = (long)kbeg * ld + c0;
-    const long left = (long)K * ld - first;
-    rs = make_rsrc(static_cast<const char*>(p) + first * 2, (uint32_t)max(0L, min(left * 2, 0x7fffffffL)));
+    base = static_cast<const char*>(p) + first * 2;
+    left = ((long)K * ld - first) * 2;
     ldb = (uint32_t)(ld * 2);
     x = (uint32_t)(16 * q + (lane >> 5)) * ldb;
     // LDS row R = 16q + 2j + lane/32 holds at chunk position lane%32 the
     // global chunk (lane%32) ^ 2 (R & 7), and R & 7 = (2j & 7) | lane/32
     cl = (uint32_t)(((lane & 31) ^ ((lane >> 5) << 1)) << 4);
   }
-  // columns past the matrix edge read in-bounds neighbours or zero; they only
-  // feed outputs the epilogue drops.  k past the end (live = false) reads zero.
+  // The buffer resource starts at the stage's first k-row, so offsets stay
+  // below 64 rows whatever the matrix size.  Columns past the matrix edge
+  // read in-bounds neighbours or zero; they only feed outputs the epilogue
+  // drops.  k past the end (live = false) reads zero.
   __device__ __forceinline__ void issue(char* sub, int krel, bool live, int q) const {
+    const long adv = (long)krel * ldb;
+    const i32x4 rs = make_rsrc(base + adv, (uint32_t)max(0L, min(left - adv, 0x7fffffffL)));
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint32_t off = x + (uint32_t)(krel + 2 * j) * ldb + (cl ^ (uint32_t)(((2 * j) & 7) << 5));
+      const uint32_t off = x + (uint32_t)(2 * j) * ldb + (cl ^ (uint32_t)(((2 * j) & 7) << 5));
       lds_u32* dst = (lds_u32*)(sub + __builtin_amdgcn_readfirstlane((8 * q + j) * 1024));
       raw_buffer_load_lds(rs, dst, 16, live ? (int)off : (int)0x80000000u, 0, 0, 0);
     }
@@ -553,6 +588,32 @@ __device__ __forceinline__ void wg_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Head forward epilogue: the 16 lanes holding one 128-column segment of a
+// row (8 logits each) reduce it to (max, sum exp(z - max)); the lane whose
+// columns hold the row's target keeps that logit.  Every lane takes part in
+// the shuffles; columns past the vocabulary count as -inf (the vocabulary
+// is a multiple of 8, so a lane's 8 columns are all in or all out).
+__device__ __forceinline__ void head_lse8(const GemmArgs& g, int row, int col, const float* f) {
+  const bool ok = row < g.M && col < g.N;
+  float m = -INFINITY;
+  if (ok) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m = fmaxf(m, f[e]);
+  }
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  float l = 0.f;
+  if (ok) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) l += __builtin_amdgcn_exp2f((f[e] - m) * 1.4426950408889634f);
+    const int t = g.tgt[row];
+    if (t >= col && t < col + 8) g.tgt_logit[row] = f[t - col];
+  }
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) l += __shfl_xor(l, o, 64);
+  if (ok && (col & 127) == 0) g.lse_part[(long)row * g.nseg + (col >> 7)] = make_float2(m, l);
+}
+
 template <typename TO, int EPI>
 __device__ __forceinline__ void epilogue_pp(const GemmArgs& g, f32x16 (&acc)[2][4], char* smem, int m0, int n0,
                                             int split, int wave, int lane) {
@@ -584,7 +645,8 @@ __device__ __forceinline__ void epilogue_pp(const GemmArgs& g, f32x16 (&acc)[2][
       Chunk<float>::unpack(ld16(wreg + epi_off(row, 2 * cg)), f);
       Chunk<float>::unpack(ld16(wreg + epi_off(row, 2 * cg + 1)), f + 4);
       const int grow = rbase + pass * 32 + row, gcol = cbase + cg * 8;
-      if (grow < g.M && gcol < g.N) epi8<TO, EPI, true>(g, split, grow, gcol, f, mx);
+      if constexpr (EPI == EPI_LSE) head_lse8(g, grow, gcol, f);
+      else if (grow < g.M && gcol < g.N) epi8<TO, EPI, true>(g, split, grow, gcol, f, mx);
     }
   }
   if (g.amax_out) amax_publish<TO>(g.amax_out, mx);
@@ -757,6 +819,8 @@ BLK_GEMM_KERNEL(gemm_proj_wgrad_acc, false, false, EPI_F32_ADD, float)
 BLK_GEMM_KERNEL(gemm_fc_wgrad_acc, false, false, EPI_F32_ADD, float)
 BLK_GEMM_KERNEL(gemm_o_wgrad_acc, false, false, EPI_F32_ADD, float)
 BLK_GEMM_KERNEL(gemm_qkv_wgrad_acc, false, false, EPI_F32_ADD, float)
+BLK_GEMM_KERNEL(gemm_head_wgrad, false, false, EPI_F32, float)
+BLK_GEMM_KERNEL(gemm_head_wgrad_acc, false, false, EPI_F32_ADD, float)
 }  // namespace blk
 
 // bf16 weight gradients on the eight-wave body (k = tokens a multiple of 64).
@@ -766,6 +830,14 @@ BLK_GEMM_KERNEL(gemm_qkv_wgrad_acc, false, false, EPI_F32_ADD, float)
   }
 
 namespace blk {
+// language-model head: logits with the log-sum-exp epilogue, logits again
+// with the softmax-gradient epilogue, the input gradient and the weight
+// gradient (token count a multiple of 64; else the four-wave body)
+__global__ __launch_bounds__(512, 1) void gemm_head_fwd(GemmArgs g) { gemm_pp_body<bf16, bf16, EPI_LSE>(g); }
+__global__ __launch_bounds__(512, 1) void gemm_head_dz(GemmArgs g) { gemm_pp_body<bf16, bf16, EPI_DZ>(g); }
+__global__ __launch_bounds__(512, 1) void gemm_head_dgrad(GemmArgs g) { gemm_pp_body<bf16, bf16, EPI_STORE>(g); }
+BLK_GEMM_PPT_KERNEL(gemm_head_wgrad_pp, EPI_F32)
+BLK_GEMM_PPT_KERNEL(gemm_head_wgrad_acc_pp, EPI_F32_ADD)
 BLK_GEMM_PPT_KERNEL(gemm_proj_wgrad_pp, EPI_F32)
 BLK_GEMM_PPT_KERNEL(gemm_fc_wgrad_pp, EPI_F32)
 BLK_GEMM_PPT_KERNEL(gemm_o_wgrad_pp, EPI_F32)

@@ -23,9 +23,9 @@ import dataclasses
 import numpy as np
 
 __all__ = [
-    "BlockShape", "DecodeShape", "WORKLOADS", "DECODE_WORKLOADS",
+    "BlockShape", "DecodeShape", "HeadShape", "WORKLOADS", "DECODE_WORKLOADS", "HEAD_WORKLOADS",
     "from_depth", "round_to", "to_storage", "from_storage",
-    "make_block_inputs", "make_decode_inputs", "ragged_lengths",
+    "make_block_inputs", "make_decode_inputs", "make_head_inputs", "ragged_lengths",
 ]
 
 
@@ -73,6 +73,17 @@ class DecodeShape:
     window: int = 0
 
 
+@dataclasses.dataclass(frozen=True)
+class HeadShape:
+    """Sizes of the language-model head and loss: N final rows of width C,
+    vocabulary V (a multiple of 64)."""
+    N: int
+    C: int
+    V: int
+    eps: float = 1e-6
+    dtype: str = "bf16"
+
+
 def from_depth(depth: int, aspect: int = 64, head_dim: int = 128) -> tuple[int, int, int]:
     """Width, heads and MLP width from the depth knob: width is depth*aspect
     rounded up to a multiple of the head size, heads = width/head size, MLP
@@ -98,6 +109,10 @@ WORKLOADS = {
     "d20_bf16_swa": _shape(20, B=32, T=2048, window=512),
 }
 _C20, _H20, _F20 = from_depth(20)
+HEAD_WORKLOADS = {
+    # the d20 batch of 32 x 2048 tokens under a 65,536-token vocabulary
+    "d20_head": HeadShape(N=32 * 2048, C=_C20, V=65536),
+}
 DECODE_WORKLOADS = {
     "d20_decode": DecodeShape(B=64, C=_C20, H=_H20, F=_F20, S_max=2049),
 }
@@ -207,3 +222,24 @@ def make_decode_inputs(shape: DecodeShape, seed: int = 0, cache_len: int | None 
 def block_param_count(C: int, F: int) -> int:
     """Weights of one block: W_qkv 3C*C, W_o C*C, W_fc F*C, W_proj C*F."""
     return 3 * C * C + C * C + 2 * F * C
+
+
+def make_head_inputs(shape: HeadShape, seed: int = 0, uncounted: float = 0.05,
+                     counted_rows=None) -> dict[str, np.ndarray]:
+    """x [N,C] ~ N(0,1) (final residual rows), w_lm [V,C] ~ N(0, 0.02), and
+    int32 targets [N] uniform in [0, V).  A fraction `uncounted` of the rows
+    get the target -1 (not counted); with `counted_rows` given, only those
+    rows keep a target in [0, V)."""
+    N, C, V = shape.N, shape.C, shape.V
+    rng = np.random.default_rng(seed)
+    out = {"x": round_to(rng.standard_normal((N, C)), shape.dtype),
+           "w_lm": round_to(rng.standard_normal((V, C)) * 0.02, shape.dtype)}
+    t = rng.integers(0, V, size=N)
+    if counted_rows is not None:
+        keep = np.zeros(N, dtype=bool)
+        keep[list(counted_rows)] = True
+        t = np.where(keep, t, -1)
+    else:
+        t = np.where(rng.random(N) < uncounted, -1, t)
+    out["targets"] = t.astype(np.int32)
+    return out

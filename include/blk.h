@@ -96,6 +96,45 @@ typedef struct {
                         * attends to slots p-W < j <= p (0 = all 0..p)       */
 } blk_dcfg;
 
+/* Language-model head and loss, the step after the block stack.
+ *   h = rmsnorm(x) (parameter-free, eps), z = h W^T with the untied head
+ *   W [V, C] (no bias, no cap), loss = mean over the counted rows of
+ *   lse(z_i) - z_i[t_i]; a row counts when its target t_i is in [0, V).
+ *   (The flicky.cc course page: untied embedding and lm_head, norms without
+ *   parameters, the loss behind the bits-per-byte metric; the CSDN page: a
+ *   Llama-like stack, hence the final norm.)  bf16 only (BLK_EUNSUPPORTED
+ *   for BLK_F32); V a multiple of 64 (the vocabulary is padded to one), C a
+ *   multiple of 128.  The logits are never stored. */
+typedef struct {
+  int32_t N;           /* rows (tokens)                                      */
+  int32_t C;           /* width                                              */
+  int32_t V;           /* vocabulary                                         */
+  float eps;           /* final RMSNorm epsilon (1e-6)                       */
+  int32_t dtype;       /* BLK_BF16                                           */
+} blk_hcfg;
+
+/* Bytes of scratch head_loss_fwd / head_loss_bwd need (the larger of the
+ * two; the backward holds the softmax gradient [N, V] in bf16).  0 for an
+ * invalid cfg. */
+size_t head_scratch_bytes(const blk_hcfg* cfg);
+
+/* Forward: x [N, C] (bf16), w_lm [V, C] (bf16), targets [N] (int32, device);
+ * writes *loss (one float, device) and lse [N] (float32, natural-log
+ * log-sum-exp of each row's logits, kept for the backward).  With no
+ * counted row *loss = 0.  BLK_EINVAL (bad cfg, NULL pointer), BLK_EALIGN
+ * (x, w_lm, scratch not 16-byte, targets/loss/lse not 4-byte aligned),
+ * BLK_ENOSPC (short scratch). */
+int head_loss_fwd(const blk_hcfg* cfg, const void* x, const void* w_lm, const int32_t* targets,
+                  float* loss, float* lse, void* scratch, size_t scratch_bytes, void* stream);
+
+/* Backward of dloss * loss: dx [N, C] (bf16; may not alias x) and
+ * dw_lm [V, C] (float32, overwritten, or added to with accumulate = 1), from
+ * the lse the forward wrote.  Errors as head_loss_fwd, plus BLK_EINVAL for
+ * accumulate not 0/1 or dx == x. */
+int head_loss_bwd(const blk_hcfg* cfg, const void* x, const void* w_lm, const int32_t* targets,
+                  const float* lse, float dloss, void* dx, float* dw_lm, int accumulate,
+                  void* scratch, size_t scratch_bytes, void* stream);
+
 /* Bytes of the activation store that block_fwd fills for block_bwd.
  * Returns 0 for an invalid cfg. */
 size_t block_saved_bytes(const blk_cfg* cfg);

@@ -21,8 +21,8 @@ Readings where the pages are silent (each is listed with its reason in the
 design notes): a parameter-free RMSNorm (eps 1e-6) on the final residual
 rows before the head, as in Llama-like stacks; logits z = h W^T with W
 [V, C], no bias and no logit cap; loss = mean over the counted rows of
-lse(z_i) - z_i[t_i]; rows with a negative target are not counted; with no
-counted row the loss and every gradient are zero.
+lse(z_i) - z_i[t_i]; rows whose target lies outside [0, V) are not counted;
+with no counted row the loss and every gradient are zero.
 """
 from __future__ import annotations
 
@@ -50,12 +50,12 @@ class HeadCache:
     z: np.ndarray        # [N, V] logits
     lse: np.ndarray      # [N]
     targets: np.ndarray  # [N]
-    count: int           # rows with a target >= 0
+    count: int           # rows with a target in [0, V)
 
 
 def head_loss(x, w_lm, targets, eps: float = 1e-6):
     """Mean cross-entropy of the final rows x [N, C] under the untied head
-    w_lm [V, C] for integer targets [N] (negative: not counted).
+    w_lm [V, C] for integer targets [N] (outside [0, V): not counted).
     Returns (loss, cache)."""
     x = np.asarray(x, dtype=np.float64)
     w_lm = np.asarray(w_lm, dtype=np.float64)
@@ -63,7 +63,7 @@ def head_loss(x, w_lm, targets, eps: float = 1e-6):
     h, r = block.rmsnorm(x, eps)
     z = h @ w_lm.T
     lse = lse_rows(z)
-    counted = t >= 0
+    counted = (t >= 0) & (t < w_lm.shape[0])
     n = int(np.count_nonzero(counted))
     rows = np.nonzero(counted)[0]
     nll = lse[rows] - z[rows, t[rows]]
@@ -81,9 +81,10 @@ def head_loss_bwd(dloss: float, cache: HeadCache, w_lm):
     if c.count == 0:
         return {"dx": np.zeros_like(c.h), "dw_lm": np.zeros_like(w_lm)}
     p = np.exp(c.z - c.lse[:, None])
-    rows = np.nonzero(c.targets >= 0)[0]
+    counted = (c.targets >= 0) & (c.targets < V)
+    rows = np.nonzero(counted)[0]
     p[rows, c.targets[rows]] -= 1.0
-    p[c.targets < 0] = 0.0
+    p[~counted] = 0.0
     dz = p * (float(dloss) / c.count)
     dh = dz @ w_lm
     dw = dz.T @ c.h

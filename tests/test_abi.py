@@ -29,7 +29,8 @@ def _header_functions():
 def test_exports_every_declared_function(lib):
     names = _header_functions()
     assert {"block_fwd", "block_bwd", "decode_step", "block_saved_bytes", "block_scratch_bytes",
-            "decode_scratch_bytes", "block_strerror"} <= set(names)
+            "decode_scratch_bytes", "block_strerror", "head_loss_fwd", "head_loss_bwd",
+            "head_scratch_bytes"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -161,3 +162,44 @@ def test_layer_window_pattern():
             bl.layer_window(0, 4, T, bad)
     with pytest.raises(ValueError):
         bl.layer_window(4, 4, T)
+
+
+def _hcfg(**kw):
+    d = dict(N=32 * 2048, C=1280, V=65536)
+    d.update(kw)
+    return bl.HeadConfig(**d)
+
+
+def test_head_sizes_and_argument_errors(lib):
+    c = _hcfg()
+    need = bl.head_scratch_bytes(c)
+    N, C, V = 32 * 2048, 1280, 65536
+    # the backward holds the softmax gradient [N, V] in bf16, W^T and dh
+    assert need >= 2 * N * V + 2 * C * V + 2 * N * C
+    assert need < 2 * N * V * 1.1
+    for bad in (_hcfg(V=1000), _hcfg(V=0), _hcfg(C=1000), _hcfg(N=0), _hcfg(dtype=7), _hcfg(eps=float("nan"))):
+        assert bl.head_scratch_bytes(bad) == 0
+    assert bl.head_scratch_bytes(_hcfg(dtype=bl.BLK_F32)) == 0
+    E = bl.binding
+    fwd = lambda cfg, **kw: bl.head_loss_fwd(cfg, kw.get("x", A), kw.get("w", A + 0x100), kw.get("t", A + 0x200),
+                                             kw.get("loss", A + 0x300), kw.get("lse", A + 0x400),
+                                             kw.get("scr", A + 0x500), scratch_bytes=kw.get("nb", 1 << 40),
+                                             stream=0, raise_on_error=False)
+    bwd = lambda cfg, **kw: bl.head_loss_bwd(cfg, kw.get("x", A), kw.get("w", A + 0x100), kw.get("t", A + 0x200),
+                                             kw.get("lse", A + 0x400), 1.0, kw.get("dx", A + 0x600),
+                                             kw.get("dw", A + 0x700), kw.get("acc", 0), kw.get("scr", A + 0x500),
+                                             scratch_bytes=kw.get("nb", 1 << 40), stream=0, raise_on_error=False)
+    assert fwd(_hcfg(V=1000)) == E.BLK_EINVAL
+    assert fwd(_hcfg(dtype=bl.BLK_F32)) == E.BLK_EUNSUPPORTED
+    assert fwd(c, t=None) == E.BLK_EINVAL
+    assert fwd(c, loss=None) == E.BLK_EINVAL
+    assert fwd(c, x=MIS) == E.BLK_EALIGN
+    assert fwd(c, t=A + 0x202) == E.BLK_EALIGN
+    assert fwd(c, nb=4096) == E.BLK_ENOSPC
+    assert bwd(c, lse=None) == E.BLK_EINVAL
+    assert bwd(c, acc=2) == E.BLK_EINVAL
+    assert bwd(c, dx=A) == E.BLK_EINVAL           # dx aliases x
+    assert bwd(c, dw=MIS) == E.BLK_EALIGN
+    assert bwd(c, nb=4096) == E.BLK_ENOSPC
+    # ragged token counts with a weight gradient past 32-bit offsets
+    assert bl.head_scratch_bytes(_hcfg(N=65537)) == 0

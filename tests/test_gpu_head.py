@@ -1,0 +1,152 @@
+"""GPU parity of head_loss_fwd + head_loss_bwd (final RMSNorm, untied
+lm_head, cross-entropy) through the C ABI against the CPU float64 oracle
+(oracle/lm_head.py), on seeded inputs.
+
+Gate (bf16 operands): relative error of the mean loss and relative Frobenius
+error of lse, dx and dW_lm <= 2e-2.  At the d20 size only a few rows carry
+a counted target, so the oracle computes the loss, dx and the exact dW_lm
+from those rows alone; the lse of every row is spot-checked on a sample."""
+import numpy as np
+import pytest
+
+from blockinputs import HEAD_WORKLOADS, HeadShape, make_head_inputs
+
+from gpu_util import TOL, note, rel_err, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+class GpuHead:
+    def __init__(self, sh: HeadShape, inp: dict):
+        import torch
+        import backward_gpt_block_amd as bl
+        self.cfg = bl.HeadConfig(N=sh.N, C=sh.C, V=sh.V, eps=sh.eps)
+        self.x = to_dev(inp["x"], "bf16")
+        self.w = to_dev(inp["w_lm"], "bf16")
+        self.t = torch.from_numpy(inp["targets"].astype(np.int32)).to("cuda:0")
+        self.loss = torch.zeros(1, dtype=torch.float32, device="cuda:0")
+        self.lse = torch.empty(sh.N, dtype=torch.float32, device="cuda:0")
+        self.dx = torch.empty_like(self.x)
+        self.dw = torch.empty(self.w.shape, dtype=torch.float32, device="cuda:0")
+        self.scratch = torch.empty(bl.head_scratch_bytes(self.cfg), dtype=torch.uint8, device="cuda:0")
+
+    def fwd(self):
+        import backward_gpt_block_amd as bl
+        bl.head_loss_fwd(self.cfg, self.x, self.w, self.t, self.loss, self.lse, self.scratch)
+
+    def bwd(self, dloss=1.0, accumulate=0):
+        import backward_gpt_block_amd as bl
+        bl.head_loss_bwd(self.cfg, self.x, self.w, self.t, self.lse, dloss, self.dx, self.dw, accumulate,
+                         self.scratch)
+
+    def results(self):
+        import torch
+        torch.cuda.synchronize()
+        return {"loss": float(self.loss.item()), "lse": to_np(self.lse), "dx": to_np(self.dx),
+                "dw_lm": to_np(self.dw)}
+
+
+def _check(res, ref_loss, ref, keys=("dx", "dw_lm"), lse_rows=None):
+    from oracle import lm_head as oh  # noqa: F401
+    tol = TOL["bf16"]
+    e_loss = abs(res["loss"] - ref_loss) / max(abs(ref_loss), 1e-30)
+    errs = {"loss": e_loss}
+    for k in keys:
+        errs[k] = rel_err(res[k], ref[k])
+    if lse_rows is not None:
+        errs["lse"] = rel_err(res["lse"][lse_rows], ref["lse"])
+    print("  rel errs: " + ", ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    bad = {k: v for k, v in errs.items() if not (v <= tol)}
+    assert not bad, f"relative error above {tol}: {bad}"
+    for k in keys:
+        assert np.all(np.isfinite(res[k])), k
+
+
+def _parity(sh: HeadShape, seed=0, dloss=1.0, **kw):
+    from oracle import lm_head as oh
+    note(f"head parity N={sh.N} C={sh.C} V={sh.V} seed={seed} dloss={dloss}")
+    inp = make_head_inputs(sh, seed=seed, **kw)
+    g = GpuHead(sh, inp)
+    g.fwd()
+    g.bwd(dloss)
+    res = g.results()
+    loss, cache = oh.head_loss(inp["x"], inp["w_lm"], inp["targets"], eps=sh.eps)
+    ref = oh.head_loss_bwd(dloss, cache, inp["w_lm"])
+    ref["lse"] = cache.lse
+    _check(res, loss, ref, lse_rows=np.arange(sh.N))
+    return g, inp, res
+
+
+@pytest.mark.parametrize("N,C,V", [
+    (300, 256, 960),      # ragged token count (four-wave weight gradient), ragged vocabulary tile
+    (384, 384, 1536),     # token count a multiple of 64 (eight-wave weight gradient), ragged width tile
+    (64, 128, 64),        # the smallest sizes
+])
+def test_head_parity(N, C, V):
+    _parity(HeadShape(N=N, C=C, V=V), seed=N)
+
+
+def test_head_upstream_scale_and_accumulate():
+    sh = HeadShape(N=256, C=256, V=1024)
+    g, inp, r1 = _parity(sh, seed=5, dloss=0.37)
+    dw1 = r1["dw_lm"].copy()
+    g.bwd(0.37, accumulate=1)
+    r2 = g.results()
+    assert np.allclose(r2["dw_lm"], 2 * dw1, rtol=1e-6, atol=1e-9)
+
+
+def test_head_targets_outside_vocabulary_not_counted():
+    sh = HeadShape(N=192, C=256, V=512)
+    from oracle import lm_head as oh
+    inp = make_head_inputs(sh, seed=9, uncounted=0.0)
+    inp["targets"][[3, 50]] = -1
+    inp["targets"][[7, 99]] = sh.V            # past the vocabulary
+    g = GpuHead(sh, inp)
+    g.fwd()
+    g.bwd()
+    res = g.results()
+    loss, cache = oh.head_loss(inp["x"], inp["w_lm"], inp["targets"])
+    ref = oh.head_loss_bwd(1.0, cache, inp["w_lm"])
+    ref["lse"] = cache.lse
+    _check(res, loss, ref, lse_rows=np.arange(sh.N))
+    assert not np.any(res["dx"][[3, 50, 7, 99]])
+
+
+def test_head_nothing_counted():
+    sh = HeadShape(N=128, C=128, V=256)
+    inp = make_head_inputs(sh, seed=2, counted_rows=[])
+    g = GpuHead(sh, inp)
+    g.fwd()
+    g.bwd()
+    res = g.results()
+    assert res["loss"] == 0.0 and not np.any(res["dx"]) and not np.any(res["dw_lm"])
+
+
+@pytest.mark.timeout(600)
+def test_d20_head_full_size_sampled():
+    # 65,536 rows x 65,536-token vocabulary; eight counted rows carry the
+    # loss and every gradient
+    from oracle import lm_head as oh
+    sh = HEAD_WORKLOADS["d20_head"]
+    rows = [0, 1, 4097, 20000, 32767, 40000, 65534, 65535]
+    note(f"head full size N={sh.N} V={sh.V} counted rows {rows}")
+    inp = make_head_inputs(sh, seed=0, counted_rows=rows)
+    g = GpuHead(sh, inp)
+    g.fwd()
+    g.bwd()
+    res = g.results()
+    del g
+    loss, cache = oh.head_loss(inp["x"][rows], inp["w_lm"], inp["targets"][rows])
+    ref = oh.head_loss_bwd(1.0, cache, inp["w_lm"])
+    # uncounted rows: dx exactly zero
+    dx = res["dx"]
+    others = np.ones(sh.N, dtype=bool)
+    others[rows] = False
+    assert not np.any(dx[others])
+    res_s = {"loss": res["loss"], "dx": dx[rows], "dw_lm": res["dw_lm"], "lse": res["lse"]}
+    ref["lse"] = cache.lse
+    _check(res_s, loss, ref, lse_rows=np.array(rows))
+    # lse of some uncounted rows
+    spot = [5, 31000, 65000]
+    _, c2 = oh.head_loss(inp["x"][spot], inp["w_lm"], np.full(3, -1))
+    assert rel_err(res["lse"][spot], c2.lse) <= TOL["bf16"]

@@ -68,8 +68,9 @@ def test_uncounted_rows_drop_out():
     rng = np.random.default_rng(35)
     x, w, t = _case(rng, N=8, C=12, V=10)
     t2 = t.copy()
-    t2[[1, 4, 6]] = -1
-    keep = np.array([i for i in range(8) if t2[i] >= 0])
+    t2[[1, 4]] = -1
+    t2[6] = 10          # = V: outside the vocabulary, not counted either
+    keep = np.array([i for i in range(8) if 0 <= t2[i] < 10])
     loss2, c2 = oh.head_loss(x, w, t2)
     loss_k, ck = oh.head_loss(x[keep], w, t[keep])
     assert math.isclose(loss2, loss_k, rel_tol=1e-14)
