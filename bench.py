@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "training tokens/sec and TFLOP/s per decoder block (d20, T=2048) on 1 MI355X"
 DECODE_METRIC = "decode tokens/sec per decoder block (d20, batch 64, KV cache 2048) on 1 MI355X"
+HEAD_METRIC = "training tokens/sec of the lm_head + cross-entropy (d20, 65,536 tokens, vocabulary 65,536) on 1 MI355X"
 PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3, "fp8": 5033.2}
 HBM_PEAK_GBS = 8000.0
 
@@ -143,9 +144,11 @@ def main() -> int:
         return 2
     if args.copy_calibration:
         return copy_calibration()
-    from blockinputs import DECODE_WORKLOADS
+    from blockinputs import DECODE_WORKLOADS, HEAD_WORKLOADS
     if args.workload in DECODE_WORKLOADS:
         return bench_decode(args)
+    if args.workload in HEAD_WORKLOADS:
+        return bench_head(args)
     return bench_train(args)
 
 
@@ -438,6 +441,105 @@ def bench_decode(args) -> int:
                            "step_gbs": round(decode_step_bytes(sh, rag) / (ms_r * 1e-3) / 1e9, 1),
                            "attn_gbs": None if ra is None else
                            round(decode_attn_bytes(sh, rag) / (ra[0] / ra[1] * 1e-3) / 1e9, 1)},
+        "roofline": roof, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def cpu_head_baseline(sh, inp, budget_s: float) -> dict:
+    """Oracle head forward + backward on the first n rows of the workload,
+    n doubling until the budget is spent."""
+    import threadpoolctl
+    from oracle import lm_head as oh
+    n, spent = 16, 0.0
+    while True:
+        t0 = time.perf_counter()
+        loss, c = oh.head_loss(inp["x"][:n], inp["w_lm"], inp["targets"][:n], eps=sh.eps)
+        oh.head_loss_bwd(1.0, c, inp["w_lm"])
+        spent = time.perf_counter() - t0
+        if spent >= budget_s / 3 or 2 * n > sh.N:
+            break
+        n *= 2
+    info = threadpoolctl.threadpool_info()
+    cores = max([d.get("num_threads", 1) for d in info] or [1])
+    return {"value": round(n / spent, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} rows of the workload (full 65,536-token vocabulary), float64, forward + backward"}
+
+
+def bench_head(args) -> int:
+    import numpy as np
+    import torch
+
+    import backward_gpt_block_amd as bl
+    from blockinputs import HEAD_WORKLOADS, make_head_inputs, to_storage
+
+    sh = HEAD_WORKLOADS[args.workload]
+    log(f"workload {args.workload}: {sh}")
+    t0 = time.perf_counter()
+    inp = make_head_inputs(sh, seed=0, uncounted=0.0)
+    log(f"inputs generated in {time.perf_counter() - t0:.1f} s")
+
+    def dev(a):
+        return torch.from_numpy(to_storage(a, "bf16").view(np.int16)).view(torch.bfloat16).to("cuda:0")
+
+    x, w = dev(inp["x"]), dev(inp["w_lm"])
+    tg = torch.from_numpy(inp["targets"]).to("cuda:0")
+    cfg = bl.HeadConfig(N=sh.N, C=sh.C, V=sh.V, eps=sh.eps)
+    loss = torch.zeros(1, dtype=torch.float32, device="cuda:0")
+    lse = torch.empty(sh.N, dtype=torch.float32, device="cuda:0")
+    dx = torch.empty_like(x)
+    dw = torch.empty(w.shape, dtype=torch.float32, device="cuda:0")
+    scratch = torch.empty(bl.head_scratch_bytes(cfg), dtype=torch.uint8, device="cuda:0")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        bl.head_loss_fwd(cfg, x, w, tg, loss, lse, scratch, stream=stream)
+        bl.head_loss_bwd(cfg, x, w, tg, lse, 1.0, dx, dw, 0, scratch, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    bl.block_timing_enable(True)
+    for _ in range(args.steps):
+        step()
+    sites = bl.block_timing_read()
+    bl.block_timing_enable(False)
+    torch.cuda.synchronize()
+    mm = 2.0 * sh.N * sh.C * sh.V                 # one N x C x V matmul
+    alg = 3 * mm                                   # z, dh, dW (the recomputed z is not counted)
+    tflops = alg / (ms * 1e-3) / 1e12
+    log(f"head step: {ms:.3f} ms, {tflops:.1f} TFLOP/s algorithmic ({alg / 1e12:.2f} TFLOP; "
+        f"{4 * mm / (ms * 1e-3) / 1e12:.1f} TFLOP/s executed with the recompute), loss {loss.item():.4f}")
+    total = sum(v[0] for v in sites.values())
+    gemm_sites = ("gemm_head_fwd", "gemm_head_dz", "gemm_head_dgrad", "gemm_head_wgrad")
+    for k, (tot, cnt) in sorted(sites.items(), key=lambda kv: -kv[1][0]):
+        tf = mm / (tot / cnt * 1e-3) / 1e12 if k in gemm_sites else float("nan")
+        log(f"  {k:18s} {tot / args.steps:8.3f} ms/step {tot / total:6.1%}  {tf:7.1f} TFLOP/s")
+    dname, (dtot, dcnt) = max(sites.items(), key=lambda kv: kv[1][0])
+    davg = dtot / dcnt
+    ach = mm / (davg * 1e-3) / 1e12
+    roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
+            "frac": round(ach / PEAK_TFLOPS["bf16"], 4), "traffic": measured_traffic(dname, args.workload),
+            "kernel": dname, "avg_launch_ms": round(davg, 4), "flops_per_launch": mm}
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        cpu = cpu_head_baseline(sh, inp, args.cpu_budget)
+        log(f"cpu baseline: {cpu}")
+    out = {
+        "metric": HEAD_METRIC, "value": round(sh.N / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "N": sh.N, "C": sh.C, "V": sh.V, "parallelism": "none (1 GPU)"},
+        "tflops": round(tflops, 2), "frac_of_peak": round(tflops / PEAK_TFLOPS["bf16"], 4),
         "roofline": roof, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
