@@ -28,6 +28,13 @@ positions counted from 0 per sequence; softmax scale 1/sqrt(D); causal mask
 key <= query; fused QKV output split as [q | k | v] with heads contiguous in
 each; weights stored [out, in] and applied as y = x W^T.
 
+Grouped-query attention (optional, G key/value heads for H query heads, G
+dividing H): [RU], same section, lists GQA support -- the query heads form
+G groups and each group shares one K/V pair; G = H is multi-head attention.
+The fused projection then has (H + 2G) heads of output, [q | k | v] with q
+in H heads and k, v in G heads each; query head h uses key/value head
+h // (H / G).
+
 Sliding-window attention (optional window W): [RU], same section, names an
 alternation of attention windows, three layers of four with a short window
 of a quarter of the context and one with the full context (the last layer
@@ -183,8 +190,8 @@ class BlockCache:
     rho_q: np.ndarray   # QK-norm factors               [B,H,T]
     rho_k: np.ndarray
     qn: np.ndarray      # after QK-norm                  [B,H,T,D]
-    kn: np.ndarray
-    v: np.ndarray       # [B,H,T,D]
+    kn: np.ndarray      # [B,G,T,D] (G key/value heads; G = H without grouping)
+    v: np.ndarray       # [B,G,T,D]
     P: np.ndarray       # attention probabilities       [B,H,T,T]
     o_heads: np.ndarray  # [B,H,T,D]
     o: np.ndarray       # heads concatenated            [B,T,C]
@@ -206,26 +213,49 @@ def _merge(z):
     return z.transpose(0, 2, 1, 3).reshape(B, T, H * D)
 
 
+def repeat_kv(z, H: int):
+    """[B,G,T,D] -> [B,H,T,D]: key/value head g serves query heads
+    g*(H/G) .. g*(H/G) + H/G - 1."""
+    return np.repeat(z, H // z.shape[1], axis=1)
+
+
+def sum_groups(dz, G: int):
+    """Adjoint of :func:`repeat_kv`: [B,H,T,D] -> [B,G,T,D], summing each
+    group's query heads."""
+    B, H, T, D = dz.shape
+    return dz.reshape(B, G, H // G, T, D).sum(axis=2)
+
+
+def split_qkv(qkv, H: int, G: int, D: int):
+    """Split the fused projection [B,T,(H+2G)D] into q [B,H,T,D] and
+    k, v [B,G,T,D]."""
+    C = H * D
+    return (_heads(qkv[..., :C], H), _heads(qkv[..., C:C + G * D], G), _heads(qkv[..., C + G * D:], G))
+
+
 def block_fwd(x, w_qkv, w_o, w_fc, w_proj, H: int, eps: float = 1e-6,
-              rope_base: float = 10000.0, positions=None, window=None) -> BlockCache:
+              rope_base: float = 10000.0, positions=None, window=None, n_kv_head=None) -> BlockCache:
     """Forward of the decoder block on x [B,T,C] (float64).
 
     1 RMSNorm; 2 fused QKV projection (no bias); 3 rotary on q, k;
-    4 QK-norm; 5 causal multi-head attention (optionally sliding-window);
+    4 QK-norm; 5 causal multi-head attention (optionally sliding-window, and
+    with G = n_kv_head key/value heads shared by groups of query heads);
     6 output projection plus residual; 7 RMSNorm; 8 MLP up-projection with
-    ReLU^2; 9 down-projection plus residual.  [RU], [CN], [ES]."""
+    ReLU^2; 9 down-projection plus residual.  [RU], [CN], [ES].
+    w_qkv is [(H + 2G) D, C]."""
     x = np.asarray(x, dtype=np.float64)
     B, T, C = x.shape
     D = C // H
+    G = H if n_kv_head is None else int(n_kv_head)
     h1, r1 = rmsnorm(x, eps)
     qkv = h1 @ w_qkv.T
-    q, k, v = (_heads(qkv[..., i * C:(i + 1) * C], H) for i in range(3))
+    q, k, v = split_qkv(qkv, H, G, D)
     pos = np.arange(T) if positions is None else np.asarray(positions)
     cos, sin = rope_tables(pos, D, rope_base)
     qr, kr = rope(q, cos, sin), rope(k, cos, sin)
     qn, rho_q = rmsnorm(qr, eps)
     kn, rho_k = rmsnorm(kr, eps)
-    o_heads, P = causal_attention(qn, kn, v, window)
+    o_heads, P = causal_attention(qn, repeat_kv(kn, H), repeat_kv(v, H), window)
     o = _merge(o_heads)
     y1 = x + o @ w_o.T
     h2, r2 = rmsnorm(y1, eps)
@@ -258,8 +288,10 @@ def block_bwd(dy, cache: BlockCache, w_qkv, w_o, w_fc, w_proj, H: int):
     # 6: y1 = x + o W_o^T
     dw_o = _flat(dy1).T @ _flat(c.o)
     do = _heads(dy1 @ w_o, H)
-    # 5: attention
-    dqn, dkn, dv = causal_attention_bwd(do, c.qn, c.kn, c.v, c.o_heads, c.P)
+    # 5: attention (over the key/value heads repeated to the query heads)
+    G = c.kn.shape[1]
+    dqn, dkn_r, dv_r = causal_attention_bwd(do, c.qn, repeat_kv(c.kn, H), repeat_kv(c.v, H), c.o_heads, c.P)
+    dkn, dv = sum_groups(dkn_r, G), sum_groups(dv_r, G)
     # 4: QK-norm
     dqr = rmsnorm_bwd(dqn, c.qn, c.rho_q)
     dkr = rmsnorm_bwd(dkn, c.kn, c.rho_k)
@@ -276,7 +308,7 @@ def block_bwd(dy, cache: BlockCache, w_qkv, w_o, w_fc, w_proj, H: int):
 
 
 def decode_step(x, w_qkv, w_o, w_fc, w_proj, k_cache, v_cache, cache_len,
-                H: int, eps: float = 1e-6, rope_base: float = 10000.0, window=None):
+                H: int, eps: float = 1e-6, rope_base: float = 10000.0, window=None, n_kv_head=None):
     """One new token per sequence at position p = cache_len[b]: forward steps
     1-4 on that row, its k (after rotary and QK-norm) and v written at slot
     p, attention over slots 0..p (p-W+1..p with a window W), then steps 6-9.
@@ -284,11 +316,13 @@ def decode_step(x, w_qkv, w_o, w_fc, w_proj, k_cache, v_cache, cache_len,
     cache and prefill/decode is named on the 7minutos.es page (section on
     midtraining, SFT and tool use) and in the launch thread.
 
-    x [B,C]; caches [B,H,S,D] (post-rotary/QK-norm keys, values);
-    returns (y [B,C], k_cache', v_cache') with the new slots written."""
+    x [B,C]; caches [B,G,S,D] (post-rotary/QK-norm keys, values of the G
+    key/value heads); returns (y [B,C], k_cache', v_cache') with the new
+    slots written."""
     x = np.asarray(x, dtype=np.float64)
     B, C = x.shape
     D = C // H
+    G = H if n_kv_head is None else int(n_kv_head)
     kc = np.array(k_cache, dtype=np.float64, copy=True)
     vc = np.array(v_cache, dtype=np.float64, copy=True)
     y = np.zeros_like(x)
@@ -298,16 +332,16 @@ def decode_step(x, w_qkv, w_o, w_fc, w_proj, k_cache, v_cache, cache_len,
         h1, _ = rmsnorm(xb, eps)
         qkv = h1 @ w_qkv.T
         q = qkv[0, :C].reshape(H, 1, D)
-        k = qkv[0, C:2 * C].reshape(H, 1, D)
-        v = qkv[0, 2 * C:].reshape(H, 1, D)
+        k = qkv[0, C:C + G * D].reshape(G, 1, D)
+        v = qkv[0, C + G * D:].reshape(G, 1, D)
         cos, sin = rope_tables(np.array([p]), D, rope_base)
         qn, _ = rmsnorm(rope(q, cos, sin), eps)
         kn, _ = rmsnorm(rope(k, cos, sin), eps)
         kc[b, :, p, :] = kn[:, 0, :]
         vc[b, :, p, :] = v[:, 0, :]
         j0 = 0 if window is None else max(0, p - int(window) + 1)
-        keys = kc[b, :, j0:p + 1, :]           # [H, p+1-j0, D]
-        vals = vc[b, :, j0:p + 1, :]
+        keys = np.repeat(kc[b, :, j0:p + 1, :], H // G, axis=0)   # [H, p+1-j0, D]
+        vals = np.repeat(vc[b, :, j0:p + 1, :], H // G, axis=0)
         s = np.matmul(qn, np.swapaxes(keys, -1, -2)) / np.sqrt(D)   # [H,1,p+1]
         e = np.exp(s - np.max(s, axis=-1, keepdims=True))
         Pb = e / np.sum(e, axis=-1, keepdims=True)

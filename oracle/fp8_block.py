@@ -53,22 +53,23 @@ def _amax(z) -> float:
     return float(np.max(np.abs(round_bf16(z)))) if z.size else 0.0
 
 
-def _attention_out(h1q, Wq, H, eps, rope_base, window=None):
-    """Rotary, QK-norm and causal (optionally sliding-window) attention of one
-    chunk of sequences from the quantised h1 and W_qkv; returns o (B,T,C) and
-    what the backward needs."""
+def _attention_out(h1q, Wq, H, eps, rope_base, window=None, G=None):
+    """Rotary, QK-norm and causal (optionally sliding-window, optionally
+    grouped: G key/value heads) attention of one chunk of sequences from the
+    quantised h1 and W_qkv; returns o (B,T,C) and what the backward needs."""
     B, T, C = h1q.shape
+    G = H if G is None else G
     qkv = h1q @ Wq.T
-    q, k, v = (_heads(qkv[..., i * C:(i + 1) * C], H) for i in range(3))
+    q, k, v = ob.split_qkv(qkv, H, G, C // H)
     cos, sin = ob.rope_tables(np.arange(T), C // H, rope_base)
     qn, rho_q = ob.rmsnorm(ob.rope(q, cos, sin), eps)
     kn, rho_k = ob.rmsnorm(ob.rope(k, cos, sin), eps)
-    oh, P = ob.causal_attention(qn, kn, v, window)
+    oh, P = ob.causal_attention(qn, ob.repeat_kv(kn, H), ob.repeat_kv(v, H), window)
     return _merge(oh), (cos, sin, qn, rho_q, kn, rho_k, v, oh, P)
 
 
 def forward_amax(x, w_qkv, w_o, w_fc, H: int, eps: float = 1e-6, rope_base: float = 10000.0, quant=quant_bf16,
-                 log=None, window=None):
+                 log=None, window=None, n_kv_head=None):
     """Absolute maxima of the four quantised forward activations h1, o, h2, a
     over the whole batch, computed one sequence at a time (`log(msg)` is
     called after each pass, for long runs)."""
@@ -77,7 +78,7 @@ def forward_amax(x, w_qkv, w_o, w_fc, H: int, eps: float = 1e-6, rope_base: floa
     Wq, Wo, Wf = (quant(w) for w in (w_qkv, w_o, w_fc))
     h1 = ob.rmsnorm(x, eps)[0]
     m_h1 = _amax(h1)
-    o = np.concatenate([_attention_out(quant(h1[b:b + 1], m_h1), Wq, H, eps, rope_base, window)[0]
+    o = np.concatenate([_attention_out(quant(h1[b:b + 1], m_h1), Wq, H, eps, rope_base, window, n_kv_head)[0]
                         for b in range(x.shape[0])])
     m_o = _amax(o)
     log("fp8 oracle: attention pass done")
@@ -89,7 +90,7 @@ def forward_amax(x, w_qkv, w_o, w_fc, H: int, eps: float = 1e-6, rope_base: floa
 
 
 def block_fwd_bwd(x, w_qkv, w_o, w_fc, w_proj, dy, H: int, eps: float = 1e-6, rope_base: float = 10000.0,
-                  batch=None, quant=quant_bf16, log=None, window=None):
+                  batch=None, quant=quant_bf16, log=None, window=None, n_kv_head=None):
     """Returns dict y, dx, dw_qkv, dw_o, dw_fc, dw_proj (float64); with
     `batch` (a list of sequence indices) y and dx cover those sequences only.
     `quant(t, amax=None)` is the operand rounding (E4M3 round trip)."""
@@ -101,14 +102,14 @@ def block_fwd_bwd(x, w_qkv, w_o, w_fc, w_proj, dy, H: int, eps: float = 1e-6, ro
         rest[list(batch)] = False
         if np.any(g[rest] != 0):
             raise ValueError("the upstream gradient must be zero outside the selected sequences")
-        fa = forward_amax(x, w_qkv, w_o, w_fc, H, eps, rope_base, quant, log, window)
+        fa = forward_amax(x, w_qkv, w_o, w_fc, H, eps, rope_base, quant, log, window, n_kv_head)
         x, g = x[list(batch)], g[list(batch)]
     amax = (lambda k: None) if fa is None else fa.get
     Wq, Wo, Wf, Wp = (quant(w) for w in (w_qkv, w_o, w_fc, w_proj))
 
     h1, r1 = ob.rmsnorm(x, eps)
     h1q = quant(h1, amax("h1"))
-    o, (cos, sin, qn, rho_q, kn, rho_k, v, oh, P) = _attention_out(h1q, Wq, H, eps, rope_base, window)
+    o, (cos, sin, qn, rho_q, kn, rho_k, v, oh, P) = _attention_out(h1q, Wq, H, eps, rope_base, window, n_kv_head)
     oq = quant(o, amax("o"))
     y1 = x + oq @ Wo.T
     h2, r2 = ob.rmsnorm(y1, eps)
@@ -129,7 +130,8 @@ def block_fwd_bwd(x, w_qkv, w_o, w_fc, w_proj, dy, H: int, eps: float = 1e-6, ro
     dy1q = quant(dy1)
     do = _heads(dy1q @ Wo, H)
     dw_o = flat(dy1q).T @ flat(oq)
-    dqn, dkn, dv = ob.causal_attention_bwd(do, qn, kn, v, oh, P)
+    dqn, dkn_r, dv_r = ob.causal_attention_bwd(do, qn, ob.repeat_kv(kn, H), ob.repeat_kv(v, H), oh, P)
+    dkn, dv = ob.sum_groups(dkn_r, kn.shape[1]), ob.sum_groups(dv_r, kn.shape[1])
     dq = ob.rope_bwd(ob.rmsnorm_bwd(dqn, qn, rho_q), cos, sin)
     dk = ob.rope_bwd(ob.rmsnorm_bwd(dkn, kn, rho_k), cos, sin)
     dqkv = np.concatenate([_merge(dq), _merge(dk), _merge(dv)], axis=-1)

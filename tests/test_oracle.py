@@ -239,6 +239,97 @@ def test_window_block_locality():
     assert np.array_equal(np.nonzero(changed)[0], np.arange(2, 2 + Wn))
 
 
+# ------------------------------------------------- grouped-query attention
+def _gqa_weights(rng, C, F, H, G, scale=0.05):
+    D = C // H
+    return (rng.standard_normal(((H + 2 * G) * D, C)) * scale, rng.standard_normal((C, C)) * scale,
+            rng.standard_normal((F, C)) * scale, rng.standard_normal((C, F)) * scale)
+
+
+def _as_mha(w_qkv, H, G, D):
+    """MHA projection whose key/value heads repeat the G grouped ones: head h
+    gets the rows of key/value head h // (H/G)."""
+    C = H * D
+    q, k, v = w_qkv[:C], w_qkv[C:C + G * D], w_qkv[C + G * D:]
+    rep = lambda z: np.concatenate([z[(h // (H // G)) * D:(h // (H // G) + 1) * D] for h in range(H)])
+    return np.concatenate([q, rep(k), rep(v)])
+
+
+@pytest.mark.parametrize("G", [1, 2])
+def test_gqa_equals_mha_with_repeated_kv_weights(G):
+    rng = np.random.default_rng(41)
+    B, T, C, H = 2, 6, 512, 4
+    D = C // H
+    W = _gqa_weights(rng, C, 4 * C, H, G)
+    x = rng.standard_normal((B, T, C))
+    dy = rng.standard_normal((B, T, C))
+    Wm = (_as_mha(W[0], H, G, D),) + W[1:]
+    cg = ob.block_fwd(x, *W, H=H, n_kv_head=G)
+    cm = ob.block_fwd(x, *Wm, H=H)
+    assert np.allclose(cg.y, cm.y, rtol=1e-12, atol=1e-12)
+    gg = ob.block_bwd(dy, cg, *W, H=H)
+    gm = ob.block_bwd(dy, cm, *Wm, H=H)
+    assert np.allclose(gg["dx"], gm["dx"], rtol=1e-11, atol=1e-12)
+    for k in ("dw_o", "dw_fc", "dw_proj"):
+        assert np.allclose(gg[k], gm[k], rtol=1e-11, atol=1e-12), k
+    # a shared parameter's gradient is the sum over its copies
+    C_ = H * D
+    dm = gm["dw_qkv"]
+    assert np.allclose(gg["dw_qkv"][:C_], dm[:C_], rtol=1e-11, atol=1e-12)
+    for part in range(2):
+        blk = dm[C_ + part * C_:C_ + (part + 1) * C_].reshape(G, H // G, D, C).sum(axis=1).reshape(G * D, C)
+        got = gg["dw_qkv"][C_ + part * G * D:C_ + (part + 1) * G * D]
+        assert np.allclose(got, blk, rtol=1e-11, atol=1e-12)
+
+
+def test_gqa_g_equals_h_is_mha():
+    rng = np.random.default_rng(42)
+    x = rng.standard_normal((1, 5, 256))
+    W = _weights(rng, 256, 1024, 2, 0.05)
+    assert np.array_equal(ob.block_fwd(x, *W, H=2, n_kv_head=2).y, ob.block_fwd(x, *W, H=2).y)
+
+
+def test_gqa_block_bwd_central_differences():
+    rng = np.random.default_rng(43)
+    B, T, C, H, G = 1, 5, 512, 4, 2
+    x = rng.standard_normal((B, T, C))
+    W = _gqa_weights(rng, C, 4 * C, H, G)
+    dy = rng.standard_normal((B, T, C))
+    g = ob.block_bwd(dy, ob.block_fwd(x, *W, H=H, n_kv_head=G), *W, H=H)
+    h = 1e-7
+    for trial in range(3):
+        dx_dir = rng.standard_normal(x.shape)
+        dW_dir = [rng.standard_normal(w.shape) for w in W]
+        Lp = np.sum(dy * ob.block_fwd(x + h * dx_dir, *[w + h * d for w, d in zip(W, dW_dir)], H=H, n_kv_head=G).y)
+        Lm = np.sum(dy * ob.block_fwd(x - h * dx_dir, *[w - h * d for w, d in zip(W, dW_dir)], H=H, n_kv_head=G).y)
+        num = (Lp - Lm) / (2 * h)
+        ana = np.sum(g["dx"] * dx_dir) + sum(np.sum(g[n] * d) for n, d in zip(("dw_qkv", "dw_o", "dw_fc", "dw_proj"), dW_dir))
+        assert math.isclose(ana, num, rel_tol=1e-7), (ana, num)
+
+
+def test_gqa_decode_equals_prefill_row():
+    rng = np.random.default_rng(44)
+    B, C, H, G, S = 2, 512, 4, 1, 12
+    D = C // H
+    W = _gqa_weights(rng, C, 4 * C, H, G)
+    lens = np.array([4, 9])
+    xs = rng.standard_normal((B, S, C))
+    kc = rng.standard_normal((B, G, S, D))
+    vc = rng.standard_normal((B, G, S, D))
+    for b in range(B):
+        L = int(lens[b])
+        c = ob.block_fwd(xs[b:b + 1, :L + 1], *W, H=H, n_kv_head=G)
+        kc[b, :, :L] = c.kn[0, :, :L]
+        vc[b, :, :L] = c.v[0, :, :L]
+    xnew = np.stack([xs[b, lens[b]] for b in range(B)])
+    y, kc2, _ = ob.decode_step(xnew, *W, kc, vc, lens, H=H, n_kv_head=G)
+    for b in range(B):
+        L = int(lens[b])
+        ref = ob.block_fwd(xs[b:b + 1, :L + 1], *W, H=H, n_kv_head=G)
+        assert np.allclose(y[b], ref.y[0, L], rtol=1e-11, atol=1e-11)
+        assert np.allclose(kc2[b, :, L], ref.kn[0, :, L], rtol=1e-12, atol=1e-12)
+
+
 # ------------------------------------------------------------ block
 def _loss_grads(shape_kw, seed=0, wscale=0.3):
     rng = np.random.default_rng(seed)
