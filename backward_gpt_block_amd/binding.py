@@ -27,13 +27,14 @@ class _Cfg(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("C", ctypes.c_int32), ("H", ctypes.c_int32),
                 ("D", ctypes.c_int32), ("F", ctypes.c_int32), ("eps", ctypes.c_float),
                 ("rope_base", ctypes.c_float), ("dtype", ctypes.c_int32), ("gemm", ctypes.c_int32),
-                ("window", ctypes.c_int32)]
+                ("window", ctypes.c_int32), ("n_kv_head", ctypes.c_int32)]
 
 
 class _DCfg(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("C", ctypes.c_int32), ("H", ctypes.c_int32), ("D", ctypes.c_int32),
                 ("F", ctypes.c_int32), ("S_max", ctypes.c_int32), ("eps", ctypes.c_float),
-                ("rope_base", ctypes.c_float), ("dtype", ctypes.c_int32), ("window", ctypes.c_int32)]
+                ("rope_base", ctypes.c_float), ("dtype", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("n_kv_head", ctypes.c_int32)]
 
 
 class _HCfg(ctypes.Structure):
@@ -54,10 +55,11 @@ class BlockConfig:
     dtype: int = BLK_BF16
     gemm: int = BLK_GEMM_NATIVE
     window: int = 0          # attention window (0: causal over the whole sequence)
+    n_kv_head: int = 0       # key/value heads (0: as many as query heads)
 
     def c(self) -> _Cfg:
         return _Cfg(self.B, self.T, self.C, self.H, self.D, self.F, self.eps, self.rope_base, self.dtype, self.gemm,
-                    self.window)
+                    self.window, self.n_kv_head)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -72,10 +74,11 @@ class DecodeConfig:
     rope_base: float = 10000.0
     dtype: int = BLK_BF16
     window: int = 0
+    n_kv_head: int = 0
 
     def c(self) -> _DCfg:
         return _DCfg(self.B, self.C, self.H, self.D, self.F, self.S_max, self.eps, self.rope_base, self.dtype,
-                     self.window)
+                     self.window, self.n_kv_head)
 
 
 @dataclasses.dataclass(frozen=True)

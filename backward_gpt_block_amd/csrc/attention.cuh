@@ -252,6 +252,9 @@ struct AttnArgs {
   unsigned* amax_o;    // fp8 mode: absolute maxima (float bits) of o and of
   unsigned* amax_dqkv; //   dq' | dk' | dv, or null
   int B, T, H, C;
+  int G;             // key/value heads (query head h uses key/value head h / (H/G))
+  int LD;            // elements per row of qkv / dqkv: C + 2 G D
+  int KO, VO;        // column of the first key / value head in a qkv row: C, C + G D
   int W;             // attention window: query i sees keys i - W < j <= i (W >= T: causal)
   float sl2;         // log2(e) / sqrt(D)
   float rsd;         // 1 / sqrt(D)
@@ -270,10 +273,11 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
   const int qt = nqt - 1 - (int)(blockIdx.x / BH);   // longest rows first
   const int bh = blockIdx.x % BH;
   const int b = bh / a.H, head = bh % a.H;
-  const long ld = 3L * a.C;
+  const long ld = a.LD;
+  const int kvh = head / (a.H / a.G);
   const T* qkv = static_cast<const T*>(a.qkv);
-  const T* Kg = qkv + (long)b * a.T * ld + a.C + head * HD;
-  const T* Vg = Kg + a.C;
+  const T* Kg = qkv + (long)b * a.T * ld + a.KO + kvh * HD;
+  const T* Vg = qkv + (long)b * a.T * ld + a.VO + kvh * HD;
   const int qw0 = qt * 128 + wave * 32;
   const int q = qw0 + (lane & 31);
 
@@ -377,10 +381,11 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(AttnArgs a) {
   const int qt = nqt - 1 - (int)(blockIdx.x / BH);
   const int bh = blockIdx.x % BH;
   const int b = bh / a.H, head = bh % a.H;
-  const long ld = 3L * a.C;
+  const long ld = a.LD;
+  const int kvh = head / (a.H / a.G);
   const T* qkv = static_cast<const T*>(a.qkv);
-  const T* Kg = qkv + (long)b * a.T * ld + a.C + head * HD;
-  const T* Vg = Kg + a.C;
+  const T* Kg = qkv + (long)b * a.T * ld + a.KO + kvh * HD;
+  const T* Vg = qkv + (long)b * a.T * ld + a.VO + kvh * HD;
   const int qw0 = qt * 128 + wave * 32;
   const int q = qw0 + (lane & 31);
   const bool qv = q < a.T;
@@ -461,23 +466,21 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(AttnArgs a) {
   // Q rows, dO rows, Q^T, dO^T, lse[RT], delta[RT]
   constexpr int STAGE = 2 * A::ROWT + 2 * A::TRT + 2 * A::RT * 4;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int BH = a.B * a.H;
-  const int kt = (int)(blockIdx.x / BH);          // first key tiles have the most queries
-  const int bh = blockIdx.x % BH;
-  const int b = bh / a.H, head = bh % a.H;
-  const long ld = 3L * a.C;
+  // one workgroup = 128 keys of one (sequence, key/value head); it walks the
+  // query tiles of every query head of the group
+  const int BG = a.B * a.G, R = a.H / a.G;
+  const int kt = (int)(blockIdx.x / BG);          // first key tiles have the most queries
+  const int bg = blockIdx.x % BG;
+  const int b = bg / a.G, kvh = bg % a.G;
+  const long ld = a.LD;
   const T* qkv = static_cast<const T*>(a.qkv);
-  const T* Qg = qkv + (long)b * a.T * ld + head * HD;
-  const T* dOg = static_cast<const T*>(a.dO) + (long)b * a.T * a.C + head * HD;
-  const float* lseg = a.lse + (long)bh * a.T;
-  const float* dlg = a.delta + (long)bh * a.T;
   const int kw0 = kt * 128 + wave * 32;
   const int key = kw0 + (lane & 31);
   const bool kv = key < a.T;
 
   typename MM::frag kf[HD / MM::KI], vf[HD / MM::KI];
-  frag_row_global<T>(kf, qkv + ((long)b * a.T + key) * ld + a.C + head * HD, kv, lane);
-  frag_row_global<T>(vf, qkv + ((long)b * a.T + key) * ld + 2 * a.C + head * HD, kv, lane);
+  frag_row_global<T>(kf, qkv + ((long)b * a.T + key) * ld + a.KO + kvh * HD, kv, lane);
+  frag_row_global<T>(vf, qkv + ((long)b * a.T + key) * ld + a.VO + kvh * HD, kv, lane);
 
   f32x16 dk[4], dv[4];
 #pragma unroll
@@ -485,7 +488,17 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(AttnArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) { dk[i][r] = 0.f; dv[i][r] = 0.f; }
 
-  auto stage = [&](char* dst, int q0) {
+  const int qt0 = (kt * 128) / A::RT;
+  // the last query that sees a key of this workgroup is kt*128 + 127 + W - 1
+  const int nqt = min((a.T + A::RT - 1) / A::RT, (int)(((long)kt * 128 + 127 + a.W - 1) / A::RT) + 1);
+  const int nq = max(0, nqt - qt0);               // query tiles per head
+  // iteration it: query head kvh*R + it/nq, query tile qt0 + it%nq
+  auto stage = [&](char* dst, int it) {
+    const int h = kvh * R + it / nq, q0 = (qt0 + it % nq) * A::RT;
+    const T* Qg = qkv + (long)b * a.T * ld + h * HD;
+    const T* dOg = static_cast<const T*>(a.dO) + (long)b * a.T * a.C + h * HD;
+    const float* lseg = a.lse + ((long)b * a.H + h) * a.T;
+    const float* dlg = a.delta + ((long)b * a.H + h) * a.T;
     stage_rows<T>(dst, Qg, ld, q0, a.T);
     stage_rows<T>(dst + A::ROWT, dOg, a.C, q0, a.T);
     stage_trans<T>(dst + 2 * A::ROWT, Qg, ld, q0, a.T);
@@ -498,16 +511,13 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(AttnArgs a) {
     }
   };
 
-  const int qt0 = (kt * 128) / A::RT;
-  // the last query that sees a key of this workgroup is kt*128 + 127 + W - 1
-  const int nqt = min((a.T + A::RT - 1) / A::RT, (int)(((long)kt * 128 + 127 + a.W - 1) / A::RT) + 1);
-  if (qt0 < nqt) stage(smem, qt0 * A::RT);
+  const int niter = R * nq;
+  if (niter > 0) stage(smem, 0);
   __syncthreads();
-  for (int qt = qt0; qt < nqt; ++qt) {
-    const int it = qt - qt0;
+  for (int it = 0; it < niter; ++it) {
     const char* cur = smem + (it & 1) * STAGE;
     char* nxt = smem + ((it + 1) & 1) * STAGE;
-    const int q0 = qt * A::RT;
+    const int q0 = (qt0 + it % nq) * A::RT;
     const float* lsev = reinterpret_cast<const float*>(cur + 2 * A::ROWT + 2 * A::TRT);
     const float* dlv = lsev + A::RT;
     // some query of this tile sees a key of this wave
@@ -550,13 +560,13 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(AttnArgs a) {
         }
       }
     }
-    if (qt + 1 < nqt) stage(nxt, q0 + A::RT);
+    if (it + 1 < niter) stage(nxt, it + 1);
     __syncthreads();
   }
   if (kv) {
-    T* row = static_cast<T*>(a.dqkv) + ((long)b * a.T + key) * ld + head * HD;
-    store_acc_row<T>(row + a.C, dk, a.rsd, lane);
-    store_acc_row<T>(row + 2 * a.C, dv, 1.f, lane);
+    T* row = static_cast<T*>(a.dqkv) + ((long)b * a.T + key) * ld;
+    store_acc_row<T>(row + a.KO + kvh * HD, dk, a.rsd, lane);
+    store_acc_row<T>(row + a.VO + kvh * HD, dv, 1.f, lane);
   }
 }
 
@@ -672,17 +682,18 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_bf16_kernel(AttnArgs a) {
   const int qt = nqt - 1 - (int)(blockIdx.x / BH);     // longest rows first
   const int bh = blockIdx.x % BH;
   const int b = bh / a.H, head = bh % a.H;
-  const long ldb = 3L * a.C * 2;                       // row stride in bytes
+  const long ldb = (long)a.LD * 2;                     // row stride in bytes
+  const int kvh = head / (a.H / a.G);
   const bf16* qkv = static_cast<const bf16*>(a.qkv);
-  const i32x4 rs = make_rsrc(qkv + (long)b * a.T * 3 * a.C, clamp_bytes((long)a.T * ldb));
-  const int koff = (a.C + head * HD) * 2, voff = (2 * a.C + head * HD) * 2;
+  const i32x4 rs = make_rsrc(qkv + (long)b * a.T * a.LD, clamp_bytes((long)a.T * ldb));
+  const int koff = (a.KO + kvh * HD) * 2, voff = (a.VO + kvh * HD) * 2;
   const int qw0 = qt * QWG + wave * QW;
 
   bf16x8 qf[2][8];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int q = qw0 + qb * 32 + (lane & 31);
-    frag_row_global<bf16>(qf[qb], qkv + ((long)b * a.T + q) * 3 * a.C + head * HD, q < a.T, lane);
+    frag_row_global<bf16>(qf[qb], qkv + ((long)b * a.T + q) * a.LD + head * HD, q < a.T, lane);
   }
   f32x16 o[2][4];
 #pragma unroll
@@ -837,24 +848,27 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_bf16_kernel(AttnArgs a) 
   constexpr int QT = 64;
   constexpr int SLOTB = 2 * TILE + 2048;      // Q, dO, lse (1 KiB), delta (1 KiB)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int BH = a.B * a.H;
-  const int kt = (int)(blockIdx.x / BH);      // first key tiles have the most queries
-  const int bh = blockIdx.x % BH;
-  const int b = bh / a.H, head = bh % a.H;
-  const long ldq = 3L * a.C * 2, ldo = (long)a.C * 2;
+  // one workgroup = 128 keys of one (sequence, key/value head); it walks the
+  // query tiles of every query head of the group, accumulating into the
+  // same dK, dV
+  const int BG = a.B * a.G, R = a.H / a.G;
+  const int kt = (int)(blockIdx.x / BG);      // first key tiles have the most queries
+  const int bg = blockIdx.x % BG;
+  const int b = bg / a.G, kvh = bg % a.G;
+  const long ldq = (long)a.LD * 2, ldo = (long)a.C * 2;
   const bf16* qkv = static_cast<const bf16*>(a.qkv);
-  const i32x4 rsq = make_rsrc(qkv + (long)b * a.T * 3 * a.C, clamp_bytes((long)a.T * ldq));
+  const i32x4 rsq = make_rsrc(qkv + (long)b * a.T * a.LD, clamp_bytes((long)a.T * ldq));
   const i32x4 rso = make_rsrc(static_cast<const bf16*>(a.dO) + (long)b * a.T * a.C, clamp_bytes((long)a.T * ldo));
-  const i32x4 rsl = make_rsrc(a.lse + (long)bh * a.T, (uint32_t)a.T * 4);
-  const i32x4 rsd = make_rsrc(a.delta + (long)bh * a.T, (uint32_t)a.T * 4);
-  const int qoff = head * HD * 2;
+  // lse, delta rows of all the sequence's query heads ([H][T] each)
+  const i32x4 rsl = make_rsrc(a.lse + (long)b * a.H * a.T, (uint32_t)a.H * a.T * 4);
+  const i32x4 rsd = make_rsrc(a.delta + (long)b * a.H * a.T, (uint32_t)a.H * a.T * 4);
   const int kw0 = kt * 128 + wave * 32;
   const int key = kw0 + (lane & 31);
   const bool kv = key < a.T;
 
   bf16x8 kf[8], vf[8];
-  frag_row_global<bf16>(kf, qkv + ((long)b * a.T + key) * 3 * a.C + a.C + head * HD, kv, lane);
-  frag_row_global<bf16>(vf, qkv + ((long)b * a.T + key) * 3 * a.C + 2 * a.C + head * HD, kv, lane);
+  frag_row_global<bf16>(kf, qkv + ((long)b * a.T + key) * a.LD + a.KO + kvh * HD, kv, lane);
+  frag_row_global<bf16>(vf, qkv + ((long)b * a.T + key) * a.LD + a.VO + kvh * HD, kv, lane);
   f32x16 dk[4], dv[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -864,21 +878,24 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_bf16_kernel(AttnArgs a) 
   frag_k_offsets(ko, lane);
   frag_vt_offsets(vo, lane);
 
-  auto issue = [&](int slot, int q0) {
-    char* d = smem + slot * SLOTB;
-    issue_tile(d, rsq, q0, ldq, qoff, wave, lane);
-    issue_tile(d + TILE, rso, q0, ldo, qoff, wave, lane);
-    if (wave == 0) {
-      issue_vec(d + 2 * TILE, rsl, q0, lane);
-      issue_vec(d + 2 * TILE + 1024, rsd, q0, lane);
-    }
-  };
   const int qt0 = (kt * 128) / QT;
   // the last query that sees a key of this workgroup is kt*128 + 127 + W - 1
   const int nqt = min((a.T + QT - 1) / QT, (int)(((long)kt * 128 + 127 + a.W - 1) / QT) + 1);
-  const int n = nqt - qt0;
-  issue(0, qt0 * QT);
-  if (n > 1) issue(1, (qt0 + 1) * QT);
+  const int nq = nqt - qt0;                   // query tiles per query head
+  const int n = R * nq;                       // iteration it: head kvh*R + it/nq, tile qt0 + it%nq
+  auto issue = [&](int slot, int it) {
+    char* d = smem + slot * SLOTB;
+    const int h = kvh * R + it / nq, q0 = (qt0 + it % nq) * QT;
+    const int qoff = h * HD * 2;
+    issue_tile(d, rsq, q0, ldq, qoff, wave, lane);
+    issue_tile(d + TILE, rso, q0, ldo, qoff, wave, lane);
+    if (wave == 0) {
+      issue_vec(d + 2 * TILE, rsl, h * a.T + q0, lane);
+      issue_vec(d + 2 * TILE + 1024, rsd, h * a.T + q0, lane);
+    }
+  };
+  issue(0, 0);
+  if (n > 1) issue(1, 1);
   for (int it = 0; it < n; ++it) {
     if (it + 1 < n) {
       if (wave == 0) __builtin_amdgcn_s_waitcnt(0x0f70 | 10);  // vmcnt(10): the next tile's 10 issues in flight
@@ -887,8 +904,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_bf16_kernel(AttnArgs a) 
       __builtin_amdgcn_s_waitcnt(0x0f70);
     }
     __syncthreads();
-    if (it + 2 < n) issue((it + 2) % 3, (qt0 + it + 2) * QT);
-    const int q0 = (qt0 + it) * QT;
+    if (it + 2 < n) issue((it + 2) % 3, it + 2);
+    const int q0 = (qt0 + it % nq) * QT;
     const lds_char* qt_ = (const lds_char*)smem + (it % 3) * SLOTB;
     const lds_char* ot_ = qt_ + TILE;
     const float* vec = (const float*)(smem + (it % 3) * SLOTB + 2 * TILE);
@@ -983,11 +1000,12 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_bf16_kernel(AttnArgs a) 
   float mx = 0.f;
   if (kv) {
     const long rowi = (long)b * a.T + key;
-    bf16* row = static_cast<bf16*>(a.dqkv) + rowi * 3 * a.C + head * HD;
-    const bf16* zk = qkv + rowi * 3 * a.C + a.C + head * HD;
-    mx = store_acc_row_qk(row + a.C, zk, a.rho[((long)a.B * a.T + rowi) * a.H + head], a.cs + (long)key * 64, dk,
-                          a.rsd, lane);
-    mx = fmaxf(mx, store_acc_row<bf16>(row + 2 * a.C, dv, 1.f, lane));
+    bf16* row = static_cast<bf16*>(a.dqkv) + rowi * a.LD;
+    const bf16* zk = qkv + rowi * a.LD + a.KO + kvh * HD;
+    // key QK-norm factors: [N][H] after the query ones, head index kvh
+    mx = store_acc_row_qk(row + a.KO + kvh * HD, zk, a.rho[((long)a.B * a.T + rowi) * a.H + kvh],
+                          a.cs + (long)key * 64, dk, a.rsd, lane);
+    mx = fmaxf(mx, store_acc_row<bf16>(row + a.VO + kvh * HD, dv, 1.f, lane));
   }
   if (a.amax_dqkv) amax_publish<bf16>(a.amax_dqkv, mx);
 }
@@ -1006,16 +1024,17 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_bf16_kernel(AttnArgs a) {
   const int qt = nqt - 1 - (int)(blockIdx.x / BH);
   const int bh = blockIdx.x % BH;
   const int b = bh / a.H, head = bh % a.H;
-  const long ldb = 3L * a.C * 2;
+  const long ldb = (long)a.LD * 2;
+  const int kvh = head / (a.H / a.G);
   const bf16* qkv = static_cast<const bf16*>(a.qkv);
-  const i32x4 rs = make_rsrc(qkv + (long)b * a.T * 3 * a.C, clamp_bytes((long)a.T * ldb));
-  const int koff = (a.C + head * HD) * 2, voff = (2 * a.C + head * HD) * 2;
+  const i32x4 rs = make_rsrc(qkv + (long)b * a.T * a.LD, clamp_bytes((long)a.T * ldb));
+  const int koff = (a.KO + kvh * HD) * 2, voff = (a.VO + kvh * HD) * 2;
   const int qw0 = qt * 128 + wave * 32;
   const int q = qw0 + (lane & 31);
   const bool qv = q < a.T;
 
   bf16x8 qf[8], df[8];
-  frag_row_global<bf16>(qf, qkv + ((long)b * a.T + q) * 3 * a.C + head * HD, qv, lane);
+  frag_row_global<bf16>(qf, qkv + ((long)b * a.T + q) * a.LD + head * HD, qv, lane);
   frag_row_global<bf16>(df, static_cast<const bf16*>(a.dO) + ((long)b * a.T + q) * a.C + head * HD, qv, lane);
   const float lse = qv ? a.lse[(long)bh * a.T + q] : INFINITY;
   const float dlt = qv ? a.delta[(long)bh * a.T + q] : 0.f;
@@ -1114,7 +1133,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_bf16_kernel(AttnArgs a) {
   float mx = 0.f;
   if (qv) {
     const long rowi = (long)b * a.T + q;
-    mx = store_acc_row_qk(static_cast<bf16*>(a.dqkv) + rowi * 3 * a.C + head * HD, qkv + rowi * 3 * a.C + head * HD,
+    mx = store_acc_row_qk(static_cast<bf16*>(a.dqkv) + rowi * a.LD + head * HD, qkv + rowi * a.LD + head * HD,
                           a.rho[rowi * a.H + head], a.cs + (long)q * 64, acc, a.rsd, lane);
   }
   if (a.amax_dqkv) amax_publish<bf16>(a.amax_dqkv, mx);

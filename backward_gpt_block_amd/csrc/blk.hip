@@ -58,6 +58,13 @@ template <typename T> struct Saved {
 
 long pad64(long n) { return (n + 63) / 64 * 64; }
 
+// Key/value heads G (grouped-query attention; G = H without grouping) and
+// the width of the fused projection's rows, q | k | v = (H + 2G) x 128.
+int kv_heads(const blk_cfg& c) { return c.n_kv_head > 0 ? c.n_kv_head : c.H; }
+int kv_heads(const blk_dcfg& c) { return c.n_kv_head > 0 ? c.n_kv_head : c.H; }
+long qkv_width(const blk_cfg& c) { return (long)c.C + 256L * kv_heads(c); }
+long qkv_width(const blk_dcfg& c) { return (long)c.C + 256L * kv_heads(c); }
+
 template <typename T> Saved<T> carve_saved(const blk_cfg& c, void* p) {
   const long N = (long)c.B * c.T;
   Carver k(p);
@@ -65,7 +72,7 @@ template <typename T> Saved<T> carve_saved(const blk_cfg& c, void* p) {
   s.cs = k.take<float2>((size_t)c.T * 64);
   s.r1 = k.take<float>(N);
   s.h1 = k.take<T>(N * c.C);
-  s.qkv = k.take<T>(N * 3 * c.C);
+  s.qkv = k.take<T>(N * qkv_width(c));
   s.rho = k.take<float>(2 * N * c.H);
   s.o = k.take<T>(N * c.C);
   s.lse = k.take<float>((size_t)c.B * c.H * c.T);
@@ -97,7 +104,7 @@ Fwd8 carve_fwd8(const blk_cfg& c, void* p) {
   f.o = k.take<uint8_t>(N * C);
   f.h2 = k.take<uint8_t>(N * C);
   f.a = k.take<uint8_t>(N * F);
-  f.wqkv = k.take<uint8_t>(3 * C * C);
+  f.wqkv = k.take<uint8_t>(qkv_width(c) * C);
   f.wo = k.take<uint8_t>(C * C);
   f.wfc = k.take<uint8_t>(F * C);
   f.wproj = k.take<uint8_t>(C * F);
@@ -126,7 +133,7 @@ template <typename T> struct BwdScratch {
   T* dy1;       // [N, C]
   T* dO;        // [N, C]
   T* dqkv;      // [N, 3C]
-  T* wt;        // transposed weights: W_proj^T [F,C], W_fc^T [C,F], W_o^T [C,C], W_qkv^T [C,3C]
+  T* wt;        // transposed weights: W_proj^T [F,C], W_fc^T [C,F], W_o^T [C,C], W_qkv^T [C,(H+2G)128]
   float* delta; // [B*H][T]
   float* part;  // split-k partial sums
   // fp8 mode: E4M3 copies of the gradients (row-major and transposed [*, Np])
@@ -144,11 +151,11 @@ template <typename T> BwdScratch<T> carve_bwd(const blk_cfg& c, void* p) {
   s.dh = k.take<T>(N * c.C);
   s.dy1 = k.take<T>(N * c.C);
   s.dO = k.take<T>(N * c.C);
-  s.dqkv = k.take<T>(N * 3 * c.C);
-  s.wt = k.take<T>(12L * c.C * c.C);
+  s.dqkv = k.take<T>(N * qkv_width(c));
+  s.wt = k.take<T>(9L * c.C * c.C + (long)c.C * qkv_width(c));
   s.delta = k.take<float>((size_t)c.B * c.H * c.T);
   size_t part = 0;
-  const int shapes[4][2] = {{c.C, c.F}, {c.F, c.C}, {c.C, c.C}, {3 * c.C, c.C}};
+  const int shapes[4][2] = {{c.C, c.F}, {c.F, c.C}, {c.C, c.C}, {(int)qkv_width(c), c.C}};
   for (int bk : {GemmTile<T>::BK, GemmTile<fp8e4>::BK})
     for (auto& sh : shapes) {
       int sp = wgrad_splits(sh[0], sh[1], N, bk);
@@ -161,9 +168,9 @@ template <typename T> BwdScratch<T> carve_bwd(const blk_cfg& c, void* p) {
     s.g8t = k.take<uint8_t>(c.C * Np);
     s.du8 = k.take<uint8_t>(N * c.F);
     s.du8t = k.take<uint8_t>(c.F * Np);
-    s.dqkv8 = k.take<uint8_t>(N * 3 * c.C);
-    s.dqkv8t = k.take<uint8_t>(3 * c.C * Np);
-    s.wt8 = k.take<uint8_t>(12L * c.C * c.C);
+    s.dqkv8 = k.take<uint8_t>(N * qkv_width(c));
+    s.dqkv8t = k.take<uint8_t>(qkv_width(c) * Np);
+    s.wt8 = k.take<uint8_t>(9L * c.C * c.C + (long)c.C * qkv_width(c));
   }
   s.bytes = (k.off + 255) & ~size_t(255);
   return s;
@@ -178,10 +185,11 @@ int check_cfg(const blk_cfg* c) {
   if (c->dtype != BLK_F32 && c->dtype != BLK_BF16) return BLK_EINVAL;
   if (c->gemm != BLK_GEMM_NATIVE && c->gemm != BLK_GEMM_FP8_E4M3) return BLK_EINVAL;
   if (c->window < 0) return BLK_EINVAL;
+  if (c->n_kv_head < 0 || (c->n_kv_head > 0 && c->H % c->n_kv_head != 0)) return BLK_EINVAL;
   if (c->gemm == BLK_GEMM_FP8_E4M3 && c->dtype != BLK_BF16) return BLK_EUNSUPPORTED;
   // row kernels keep a row in registers: 8 chunks of 16 bytes per lane
   if ((long)c->C * (c->dtype == BLK_BF16 ? 2 : 4) > 8L * 64 * 16) return BLK_EUNSUPPORTED;
-  if ((long)c->B * c->T * 3L * c->C >= (1L << 31)) return BLK_EUNSUPPORTED;
+  if ((long)c->B * c->T * qkv_width(*c) >= (1L << 31)) return BLK_EUNSUPPORTED;
   return BLK_OK;
 }
 
@@ -277,7 +285,7 @@ GemmArgs gargs(const void* A, long lda, const void* B, long ldb, int M, int N, i
 // Epilogue parameters of the QKV projection (rotary + QK-norm) and of the
 // attention-output input gradient (per-head row dot with o).
 void rope_args(GemmArgs& g, const blk_cfg& c, const float2* cs, float* rho) {
-  g.cs = cs; g.rho = rho; g.T = c.T; g.H = c.H; g.C = c.C; g.eps = c.eps;
+  g.cs = cs; g.rho = rho; g.T = c.T; g.H = c.H; g.C = c.C; g.G = kv_heads(c); g.eps = c.eps;
 }
 void delta_args(GemmArgs& g, const blk_cfg& c, const void* o, float* delta) {
   g.aux = o; g.ldaux = c.C; g.delta = delta; g.T = c.T; g.H = c.H; g.C = c.C;
@@ -329,6 +337,10 @@ template <typename T> AttnArgs attn_args(const blk_cfg& c) {
   AttnArgs a{};
   a.B = c.B; a.T = c.T; a.H = c.H; a.C = c.C;
   a.W = (c.window <= 0 || c.window >= c.T) ? c.T : c.window;   // W >= T: causal
+  a.G = kv_heads(c);
+  a.LD = (int)qkv_width(c);
+  a.KO = c.C;
+  a.VO = c.C + a.G * 128;
   a.sl2 = (float)(1.4426950408889634 / std::sqrt(128.0));   // log2(e) / sqrt(D)
   a.rsd = (float)(1.0 / std::sqrt(128.0));
   return a;
@@ -348,8 +360,8 @@ int fwd_impl(const blk_cfg& c, const T* x, const T* wqkv, const T* wo, const T* 
     hipLaunchKernelGGL(rmsnorm_fwd_kernel<T>, dim3(row_blocks(N)), dim3(256), 0, st, x, s.h1, s.r1, N, C, c.eps);
   }
   {  // 2-4 qkv = h1 W_qkv^T; rotary and QK-norm of q, k in the epilogue
-    GemmArgs g = gargs(s.h1, C, wqkv, C, N, 3 * C, C);
-    g.out = s.qkv; g.ldo = 3 * C;
+    GemmArgs g = gargs(s.h1, C, wqkv, C, N, (int)qkv_width(c), C);
+    g.out = s.qkv; g.ldo = qkv_width(c);
     rope_args(g, c, s.cs, s.rho);
     gemm_pp<T>(gemm_qkv_fwd<T>, "gemm_qkv_fwd", g, st);
   }
@@ -399,7 +411,7 @@ int bwd_impl(const blk_cfg& c, const T* dy, const T* x, const T* wqkv, const T* 
   T* wt_proj = w.wt;                       // [F, C]
   T* wt_fc = wt_proj + (long)F * C;        // [C, F]
   T* wt_o = wt_fc + (long)C * F;           // [C, C]
-  T* wt_qkv = wt_o + (long)C * C;          // [C, 3C]
+  T* wt_qkv = wt_o + (long)C * C;          // [C, (H+2G)128]
   {
     Timed t("transpose_weights", st);
     auto tr = [&](const T* src, T* dst, int rows, int cols) {
@@ -408,7 +420,7 @@ int bwd_impl(const blk_cfg& c, const T* dy, const T* x, const T* wqkv, const T* 
     tr(wproj, wt_proj, C, F);
     tr(wfc, wt_fc, F, C);
     tr(wo, wt_o, C, C);
-    tr(wqkv, wt_qkv, 3 * C, C);
+    tr(wqkv, wt_qkv, (int)qkv_width(c), C);
   }
   {  // 9: du = (dy W_proj) * 2 max(u, 0), with max(u, 0) = sqrt(a)
     GemmArgs g = gargs(dy, C, wt_proj, C, N, F, C);
@@ -450,7 +462,7 @@ int bwd_impl(const blk_cfg& c, const T* dy, const T* x, const T* wqkv, const T* 
       need_lds(reinterpret_cast<const void*>(attn_bwd_dq_bf16_kernel), fa::LDS);
       {
         Timed t("attn_bwd_dkdv", st);
-        hipLaunchKernelGGL(attn_bwd_dkdv_bf16_kernel, dim3(nqt * c.B * H), dim3(256), DKDV_LDS, st, a);
+        hipLaunchKernelGGL(attn_bwd_dkdv_bf16_kernel, dim3(nqt * c.B * a.G), dim3(256), DKDV_LDS, st, a);
       }
       {
         Timed t("attn_bwd_dq", st);
@@ -461,7 +473,7 @@ int bwd_impl(const blk_cfg& c, const T* dy, const T* x, const T* wqkv, const T* 
       need_lds(reinterpret_cast<const void*>(attn_bwd_dkdv_kernel<T>), attn_dkdv_lds<T>());
       {
         Timed t("attn_bwd_dkdv", st);
-        hipLaunchKernelGGL(attn_bwd_dkdv_kernel<T>, dim3(nqt * c.B * H), dim3(256), attn_dkdv_lds<T>(), st, a);
+        hipLaunchKernelGGL(attn_bwd_dkdv_kernel<T>, dim3(nqt * c.B * a.G), dim3(256), attn_dkdv_lds<T>(), st, a);
       }
       {
         Timed t("attn_bwd_dq", st);
@@ -469,18 +481,19 @@ int bwd_impl(const blk_cfg& c, const T* dy, const T* x, const T* wqkv, const T* 
       }
       {  // 4-3: QK-norm and rotary backward (in place on dq, dk)
         Timed t("qknorm_rope_bwd", st);
-        hipLaunchKernelGGL(qknorm_rope_bwd_kernel<T>, dim3(row_blocks((long)N * H * 2)), dim3(256), 0, st, w.dqkv,
-                           (const T*)s.qkv, (const float*)s.rho, (const float2*)s.cs, N, c.T, H, C);
+        hipLaunchKernelGGL(qknorm_rope_bwd_kernel<T>, dim3(row_blocks((long)N * (H + a.G))), dim3(256), 0, st,
+                           w.dqkv, (const T*)s.qkv, (const float*)s.rho, (const float2*)s.cs, N, c.T, H, C, a.G);
       }
     }
   }
   {  // 2: dh1 = dqkv W_qkv
-    GemmArgs g = gargs(w.dqkv, 3 * C, wt_qkv, 3 * C, N, C, 3 * C);
+    const int W3 = (int)qkv_width(c);
+    GemmArgs g = gargs(w.dqkv, W3, wt_qkv, W3, N, C, W3);
     g.out = w.dh; g.ldo = C;
     gemm_pp<T>(gemm_qkv_dgrad<T>, "gemm_qkv_dgrad", g, st);
   }
   //    dW_qkv = dqkv^T h1
-  wgrad<T>(gemm_qkv_wgrad<T>, gemm_qkv_wgrad_acc<T>, gemm_qkv_wgrad_pp, gemm_qkv_wgrad_acc_pp, "gemm_qkv_wgrad", w.dqkv, s.h1, dwqkv, 3 * C, C, N, acc,
+  wgrad<T>(gemm_qkv_wgrad<T>, gemm_qkv_wgrad_acc<T>, gemm_qkv_wgrad_pp, gemm_qkv_wgrad_acc_pp, "gemm_qkv_wgrad", w.dqkv, s.h1, dwqkv, (int)qkv_width(c), C, N, acc,
            w.part, st);
   {  // 1: dx = dy1 + rmsnorm backward
     Timed t("rmsnorm_bwd", st);
@@ -562,14 +575,14 @@ int fwd_fp8(const blk_cfg& c, const bf16* x, const bf16* wqkv, const bf16* wo, c
     hipLaunchKernelGGL(rmsnorm_fwd_kernel<bf16>, dim3(row_blocks(N)), dim3(256), 0, st, x, s.h1, s.r1, N, C, c.eps,
                        am + AM_H1);
   }
-  quantize(wqkv, 3 * C, C, am + AM_WQKV, f.wqkv, nullptr, 0, true, st);
+  quantize(wqkv, qkv_width(c), C, am + AM_WQKV, f.wqkv, nullptr, 0, true, st);
   quantize(wo, C, C, am + AM_WO, f.wo, nullptr, 0, true, st);
   quantize(wfc, F, C, am + AM_WFC, f.wfc, nullptr, 0, true, st);
   quantize(wproj, C, F, am + AM_WPROJ, f.wproj, nullptr, 0, true, st);
   quantize(s.h1, N, C, am + AM_H1, f.h1, s.h1_8t, Np, false, st);   // amax from rmsnorm_fwd
   {
-    GemmArgs g = gargs8(f.h1, C, am + AM_H1, f.wqkv, C, am + AM_WQKV, N, 3 * C, C);
-    g.out = s.qkv; g.ldo = 3 * C;
+    GemmArgs g = gargs8(f.h1, C, am + AM_H1, f.wqkv, C, am + AM_WQKV, N, (int)qkv_width(c), C);
+    g.out = s.qkv; g.ldo = qkv_width(c);
     rope_args(g, c, s.cs, s.rho);
     gemm_pp<fp8e4>(gemm8_qkv_fwd, "gemm_qkv_fwd", g, st);
   }
@@ -616,11 +629,11 @@ int bwd_fp8(const blk_cfg& c, const bf16* dy, const bf16* wqkv, const bf16* wo, 
   uint8_t* wt_proj = w.wt8;                 // [F, C]
   uint8_t* wt_fc = wt_proj + (long)F * C;   // [C, F]
   uint8_t* wt_o = wt_fc + (long)C * F;      // [C, C]
-  uint8_t* wt_qkv = wt_o + (long)C * C;     // [C, 3C]
+  uint8_t* wt_qkv = wt_o + (long)C * C;     // [C, (H+2G)128]
   quantize(wproj, C, F, am + AM_WPROJ, nullptr, wt_proj, C, false, st);
   quantize(wfc, F, C, am + AM_WFC, nullptr, wt_fc, F, false, st);
   quantize(wo, C, C, am + AM_WO, nullptr, wt_o, C, false, st);
-  quantize(wqkv, 3 * C, C, am + AM_WQKV, nullptr, wt_qkv, 3 * C, false, st);
+  quantize(wqkv, qkv_width(c), C, am + AM_WQKV, nullptr, wt_qkv, qkv_width(c), false, st);
 
   quantize(dy, N, C, am + AM_DY, w.g8, w.g8t, Np, true, st);
   {  // du = (dy W_proj) * 2 max(u, 0), with max(u, 0) = sqrt(a)
@@ -663,21 +676,22 @@ int bwd_fp8(const blk_cfg& c, const bf16* dy, const bf16* wqkv, const bf16* wo, 
     const int nqt = (c.T + 127) / 128;
     {
       Timed t("attn_bwd_dkdv", st);
-      hipLaunchKernelGGL(attn_bwd_dkdv_bf16_kernel, dim3(nqt * c.B * H), dim3(256), DKDV_LDS, st, a);
+      hipLaunchKernelGGL(attn_bwd_dkdv_bf16_kernel, dim3(nqt * c.B * a.G), dim3(256), DKDV_LDS, st, a);
     }
     {
       Timed t("attn_bwd_dq", st);
       hipLaunchKernelGGL(attn_bwd_dq_bf16_kernel, dim3(nqt * c.B * H), dim3(256), fa::LDS, st, a);
     }
   }
-  quantize(w.dqkv, N, 3 * C, am + AM_DQKV, w.dqkv8, w.dqkv8t, Np, false, st);   // amax from attention bwd
+  quantize(w.dqkv, N, qkv_width(c), am + AM_DQKV, w.dqkv8, w.dqkv8t, Np, false, st);   // amax from attention bwd
   {  // dh1 = dqkv W_qkv
-    GemmArgs g = gargs8(w.dqkv8, 3 * C, am + AM_DQKV, wt_qkv, 3 * C, am + AM_WQKV, N, C, 3 * C);
+    const int W3 = (int)qkv_width(c);
+    GemmArgs g = gargs8(w.dqkv8, W3, am + AM_DQKV, wt_qkv, W3, am + AM_WQKV, N, C, W3);
     g.out = w.dh; g.ldo = C;
     gemm_pp<fp8e4>(gemm8_qkv_dgrad, "gemm_qkv_dgrad", g, st);
   }
   wgrad8(gemm8_qkv_wgrad, gemm8_qkv_wgrad_acc, gemm8_qkv_wgrad_pp, gemm8_qkv_wgrad_acc_pp, "gemm_qkv_wgrad", w.dqkv8t, am + AM_DQKV, s.h1_8t, am + AM_H1, Np,
-         dwqkv, 3 * C, C, N, acc, w.part, st);
+         dwqkv, (int)qkv_width(c), C, N, acc, w.part, st);
   {
     Timed t("rmsnorm_bwd", st);
     hipLaunchKernelGGL(rmsnorm_bwd_kernel<bf16>, dim3(row_blocks(N)), dim3(256), 0, st, (const bf16*)w.dy1,
@@ -697,6 +711,7 @@ int check_dcfg(const blk_dcfg* c) {
   if (c->dtype != BLK_BF16) return BLK_EUNSUPPORTED;   // the decode kernels are bf16 only
   if (c->C > 2048 || c->B > 65535) return BLK_EUNSUPPORTED;
   if ((long)c->B * c->H * c->S_max * 128 >= (1L << 40)) return BLK_EUNSUPPORTED;
+  if (c->n_kv_head < 0 || (c->n_kv_head > 0 && c->H % c->n_kv_head != 0)) return BLK_EINVAL;
   return BLK_OK;
 }
 
@@ -729,7 +744,7 @@ DecScratch carve_dec(const blk_dcfg& c, void* p) {
   const long B = c.B, C = c.C, F = c.F, H = c.H;
   const long NS = (c.S_max + dec::KEYS - 1) / dec::KEYS;
   long part = 0;
-  const long nk[4][2] = {{3 * C, C}, {C, C}, {F, C}, {C, F}};   // (N, K) of the four GEMMs
+  const long nk[4][2] = {{qkv_width(c), C}, {C, C}, {F, C}, {C, F}};   // (N, K) of the four GEMMs
   for (const auto& g : nk) part = std::max(part, (long)dec_split((int)B, (int)g[0], (int)g[1]).S * B * g[0]);
   Carver k(p);
   DecScratch d;
@@ -927,18 +942,18 @@ int decode_step(const blk_dcfg* cfg, const void* x, const void* w_qkv, const voi
     Timed t("dec_rmsnorm", st);
     hipLaunchKernelGGL(dec::dec_rmsnorm_kernel, dim3(B), dim3(256), 0, st, xb, C, c.eps, d.h1);
   }
-  const DecSplit sq = dec_split(B, 3 * C, C);
-  dec_gemm("dec_gemm_qkv", d.h1, B, static_cast<const bf16*>(w_qkv), 3 * C, C, sq, d.part, st);
+  const DecSplit sq = dec_split(B, (int)qkv_width(c), C);
+  dec_gemm("dec_gemm_qkv", d.h1, B, static_cast<const bf16*>(w_qkv), (int)qkv_width(c), C, sq, d.part, st);
   {  // rotary + QK-norm at position cache_len[b]; k, v into the caches
     Timed t("dec_qkv_epi", st);
     hipLaunchKernelGGL(dec::dec_qkv_epi_kernel, dim3(H, B), dim3(192), 0, st, (const float*)d.part, sq.S, B, H,
-                       cache_len, c.S_max, c.eps, (double)c.rope_base, d.q, kc, vc);
+                       kv_heads(c), cache_len, c.S_max, c.eps, (double)c.rope_base, d.q, kc, vc);
   }
   const int dwin = c.window > 0 ? c.window : INT_MAX;
   {  // attention of the new token over slots 0..cache_len[b] (the last W with a window)
     Timed t("dec_attn", st);
     hipLaunchKernelGGL(dec::dec_attn_kernel, dim3(NS, H, B), dim3(256), 0, st, (const float*)d.q,
-                       (const bf16*)kc, (const bf16*)vc, cache_len, H, c.S_max, NS, dwin,
+                       (const bf16*)kc, (const bf16*)vc, cache_len, H, kv_heads(c), c.S_max, NS, dwin,
                        (float)(1.4426950408889634 / std::sqrt(128.0)), d.opart, d.ml);
   }
   {

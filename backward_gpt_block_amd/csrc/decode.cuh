@@ -141,19 +141,22 @@ __device__ __forceinline__ int clamp_pos(const int* __restrict__ cache_len, int 
 
 // From the QKV partials of row b: q and k rotated by the angle of position
 // p = cache_len[b] and RMS-normalised per head (QK-norm); q (float32) into
-// qbuf[b, h, :], k and v (bf16) into slot p of the caches.  Grid (H, B),
-// 3 waves: q, k, v of head h; lane i owns the pair (i, i + 64).
-__global__ __launch_bounds__(192) void dec_qkv_epi_kernel(const float* __restrict__ part, int S, int B, int H,
+// qbuf[b, h, :], k and v (bf16) into slot p of the caches of key/value head
+// h (h < G).  Grid (H, B), 3 waves: q, k, v of head h; lane i owns the pair
+// (i, i + 64).
+__global__ __launch_bounds__(192) void dec_qkv_epi_kernel(const float* __restrict__ part, int S, int B, int H, int G,
                                                           const int* __restrict__ cache_len, int S_max, float eps,
                                                           double rope_base, float* __restrict__ qbuf,
                                                           bf16* __restrict__ kc, bf16* __restrict__ vc) {
   const int h = blockIdx.x, b = blockIdx.y, which = threadIdx.x >> 6, i = threadIdx.x & 63;
+  if (which > 0 && h >= G) return;
   const int C = H * 128;
-  const long stride = (long)B * 3 * C;
-  const long base = (long)b * 3 * C + which * C + h * 128;
+  const long LD = C + 256L * G;                 // q | k | v columns
+  const long stride = (long)B * LD;
+  const long base = (long)b * LD + (which == 0 ? 0 : which == 1 ? C : C + 128L * G) + h * 128;
   float z1 = sum_parts(part, S, stride, base + i), z2 = sum_parts(part, S, stride, base + i + 64);
   const int p = clamp_pos(cache_len, b, S_max);
-  const long slot = ((long)(b * H + h) * S_max + p) * 128;
+  const long slot = ((long)(b * G + h) * S_max + p) * 128;
   if (which == 2) {
     vc[slot + i] = (bf16)z1;
     vc[slot + i + 64] = (bf16)z2;
@@ -186,7 +189,7 @@ __device__ __forceinline__ int first_visible(int L, int W) { return L > W ? L - 
 
 __global__ __launch_bounds__(256) void dec_attn_kernel(const float* __restrict__ qbuf, const bf16* __restrict__ kc,
                                                        const bf16* __restrict__ vc, const int* __restrict__ cache_len,
-                                                       int H, int S_max, int NS, int W, float sl2,
+                                                       int H, int G, int S_max, int NS, int W, float sl2,
                                                        float* __restrict__ opart, float2* __restrict__ ml) {
   __shared__ float wo[4][128];
   __shared__ float wm[4], wl[4];
@@ -207,8 +210,9 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(const float* __restrict__
 #pragma unroll
       for (int e = 0; e < 8; ++e) q[e] = qp[e] * sl2;
     }
-    const bf16* kp = kc + head * S_max * 128 + r * 8;
-    const bf16* vp = vc + head * S_max * 128 + r * 8;
+    const long kvrow = (long)b * G + h / (H / G);   // this query head's key/value head
+    const bf16* kp = kc + kvrow * S_max * 128 + r * 8;
+    const bf16* vp = vc + kvrow * S_max * 128 + r * 8;
     u32x4 kr[16], vr[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {

@@ -126,20 +126,23 @@ __global__ void rope_table_kernel(float2* __restrict__ cs, int T, int D, double 
 // In place on the dq, dk parts of dqkv [N, 3C]: QK-norm backward
 // (dz' = rho * (dz'' - z'' * mean(dz'' * z''))) then the transpose rotation.
 // zn = the saved normalised q'' | k'' (qkv layout).
+// One wave per (row, head) of the H query heads then the G key heads; rows of
+// qkv / dqkv are C + 2*128*G wide.
 template <typename T>
 __global__ __launch_bounds__(256) void qknorm_rope_bwd_kernel(T* __restrict__ dqkv, const T* __restrict__ zn,
                                                               const float* __restrict__ rho,
                                                               const float2* __restrict__ cs, int N, int Tlen,
-                                                              int H, int C) {
+                                                              int H, int C, int G) {
   const int lane = threadIdx.x & 63;
   const long w = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const long total = (long)N * H * 2;
+  const long total = (long)N * (H + G);
   if (w >= total) return;
-  const int which = w % 2;
-  const int head = (w / 2) % H;
-  const long row = w / (2 * H);
+  const int j = (int)(w % (H + G));
+  const int which = j < H ? 0 : 1;
+  const int head = which ? j - H : j;
+  const long row = w / (H + G);
   const int t = row % Tlen;
-  const long off = row * 3 * C + which * C + head * 128;
+  const long off = row * (C + 256L * G) + which * C + head * 128;
   T* g = dqkv + off;
   const T* z = zn + off;
   const float g1 = to_f32(g[lane]), g2 = to_f32(g[lane + 64]);

@@ -55,13 +55,14 @@ struct GemmArgs {
   const unsigned* amax_a;
   const unsigned* amax_b;
   // EPI_ROPE: angle table cs[t*64 + i] = (cos, sin), QK-norm factors
-  // rho[(which*M + row)*H + head], tokens per sequence T, heads H, width C.
+  // rho[(which*M + row)*H + head], tokens per sequence T, heads H, width C,
+  // key/value heads G (columns [0, C) q, [C, C + 128G) k, then v).
   // EPI_DELTA: delta[(b*H + head)*T + t] for row = b*T + t.
   const float2* cs;
   float* rho;
   float* delta;
   unsigned* amax_out;   // fp8 mode: absolute maximum of the stored output (float bits), or null
-  int T, H, C;
+  int T, H, C, G;
   float eps;
   // EPI_LSE / EPI_DZ (language-model head; rows = tokens, columns = vocabulary):
   // tgt[row] target id (counted when 0 <= tgt < N); lse_part[row*nseg + col/128]
@@ -261,7 +262,9 @@ __device__ __forceinline__ void epi8(const GemmArgs& g, int split, int row, int 
     // each); rotary pairs (i, i + 64) sit 8 lanes apart
     constexpr int EL = Chunk<TO>::N;
     TO* o = static_cast<TO*>(g.out) + (long)row * g.ldo + col;
-    const int which = col / g.C;          // 0 q, 1 k, 2 v (uniform over the 16 lanes)
+    // 0 q, 1 k, 2 v (uniform over the 16 lanes); hd the head within its part
+    const int which = col < g.C ? 0 : (col < g.C + 128 * g.G ? 1 : 2);
+    const int hd = (col - (which == 0 ? 0 : g.C)) / 128;
     if (which < 2) {
       const int cg = (col % 128) >> 3;    // this lane's 8-column group in the head
       const int t = row % g.T;
@@ -283,7 +286,7 @@ __device__ __forceinline__ void epi8(const GemmArgs& g, int split, int row, int 
       const float r = 1.f / sqrtf(ss / 128.f + g.eps);
 #pragma unroll
       for (int e = 0; e < 8; ++e) f[e] *= r;
-      if (cg == 0) g.rho[((long)which * g.M + row) * g.H + (col % g.C) / 128] = r;
+      if (cg == 0) g.rho[((long)which * g.M + row) * g.H + hd] = r;
     }
 #pragma unroll
     for (int h = 0; h < 8 / EL; ++h) st16_out<NT>(o + h * EL, Chunk<TO>::pack(f + h * EL));

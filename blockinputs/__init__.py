@@ -48,6 +48,11 @@ class BlockShape:
     dtype: str = "bf16"
     gemm: str = "native"
     window: int = 0          # attention window (0: causal over the whole sequence)
+    n_kv_head: int = 0       # key/value heads (0: as many as query heads)
+
+    @property
+    def G(self) -> int:
+        return self.n_kv_head or self.H
 
     @property
     def N(self) -> int:
@@ -71,6 +76,11 @@ class DecodeShape:
     rope_base: float = 10000.0
     dtype: str = "bf16"
     window: int = 0
+    n_kv_head: int = 0
+
+    @property
+    def G(self) -> int:
+        return self.n_kv_head or self.H
 
 
 @dataclasses.dataclass(frozen=True)
@@ -160,14 +170,15 @@ def from_storage(bits: np.ndarray, dtype: str) -> np.ndarray:
 
 
 def make_block_inputs(shape: BlockShape, seed: int = 0) -> dict[str, np.ndarray]:
-    """x [B,T,C], W_qkv [3C,C], W_o [C,C], W_fc [F,C], W_proj [C,F], dy
-    [B,T,C], float64 arrays holding values already rounded to shape.dtype."""
+    """x [B,T,C], W_qkv [(H+2G)D,C] (3C without grouping), W_o [C,C],
+    W_fc [F,C], W_proj [C,F], dy [B,T,C], float64 arrays holding values
+    already rounded to shape.dtype."""
     B, T, C, F = shape.B, shape.T, shape.C, shape.F
     rng = np.random.default_rng(seed)
     out = {}
     for name, dims, scale in (
         ("x", (B, T, C), 1.0),
-        ("w_qkv", (3 * C, C), 0.02),
+        ("w_qkv", ((shape.H + 2 * shape.G) * shape.D, C), 0.02),
         ("w_o", (C, C), 0.02),
         ("w_fc", (F, C), 0.02),
         ("w_proj", (C, F), 0.02),
@@ -189,20 +200,21 @@ def ragged_lengths(B: int, lo: int, hi: int, seed: int = 0) -> np.ndarray:
 def make_decode_inputs(shape: DecodeShape, seed: int = 0, cache_len: int | None = None,
                        ragged: bool = False, ragged_lo: int = 128,
                        ragged_hi: int | None = None) -> dict[str, np.ndarray]:
-    """x [B,C], four weights, k_cache/v_cache [B,H,S_max,D] ~ N(0,1) and
+    """x [B,C], four weights, k_cache/v_cache [B,G,S_max,D] ~ N(0,1) and
     int32 lengths [B].  Slots at and beyond a sequence's length hold drawn
     values too (they must not influence the result)."""
     B, C, H, F, S, D = shape.B, shape.C, shape.H, shape.F, shape.S_max, shape.D
+    G = shape.G
     rng = np.random.default_rng(seed)
     out = {}
     for name, dims, scale in (
         ("x", (B, C), 1.0),
-        ("w_qkv", (3 * C, C), 0.02),
+        ("w_qkv", ((H + 2 * G) * D, C), 0.02),
         ("w_o", (C, C), 0.02),
         ("w_fc", (F, C), 0.02),
         ("w_proj", (C, F), 0.02),
-        ("k_cache", (B, H, S, D), 1.0),
-        ("v_cache", (B, H, S, D), 1.0),
+        ("k_cache", (B, G, S, D), 1.0),
+        ("v_cache", (B, G, S, D), 1.0),
     ):
         v = rng.standard_normal(dims)
         if scale != 1.0:

@@ -84,6 +84,14 @@ typedef struct {
                         * since GPT-2, alternates short windows of a quarter
                         * of the context with full ones across layers; the
                         * per-layer choice is the caller's.  < 0: EINVAL.   */
+  int32_t n_kv_head;   /* key/value heads G (0 = H: multi-head attention);
+                        * G must divide H.  Query heads form G groups that
+                        * share one K/V pair (grouped-query attention, listed
+                        * on the flicky.cc course page's model section):
+                        * w_qkv is [(H + 2G) D, C], its output rows
+                        * [q (H heads) | k (G heads) | v (G heads)], and
+                        * query head h attends with key/value head
+                        * h / (H / G).                                       */
 } blk_cfg;
 
 typedef struct {
@@ -94,6 +102,8 @@ typedef struct {
   int32_t dtype;       /* BLK_BF16 or BLK_F32                                */
   int32_t window;      /* as blk_cfg.window: the new token at position p
                         * attends to slots p-W < j <= p (0 = all 0..p)       */
+  int32_t n_kv_head;   /* as blk_cfg.n_kv_head; the caches are
+                        * [B, G, S_max, D]                                   */
 } blk_dcfg;
 
 /* Language-model head and loss, the step after the block stack.

@@ -40,7 +40,8 @@ def cfg_of(sh: BlockShape):
     import backward_gpt_block_amd as bl
     return bl.BlockConfig(B=sh.B, T=sh.T, C=sh.C, H=sh.H, F=sh.F, eps=sh.eps, rope_base=sh.rope_base,
                           dtype=bl.BLK_BF16 if sh.dtype == "bf16" else bl.BLK_F32,
-                          gemm=bl.BLK_GEMM_FP8_E4M3 if sh.gemm == "fp8" else bl.BLK_GEMM_NATIVE, window=sh.window)
+                          gemm=bl.BLK_GEMM_FP8_E4M3 if sh.gemm == "fp8" else bl.BLK_GEMM_NATIVE, window=sh.window,
+                          n_kv_head=sh.n_kv_head)
 
 
 class GpuBlock:
@@ -91,7 +92,8 @@ def oracle_step(sh: BlockShape, inp: dict, batch=None):
     x = inp["x"][sl]
     dy = inp["dy"][sl]
     W = (inp["w_qkv"], inp["w_o"], inp["w_fc"], inp["w_proj"])
-    c = ob.block_fwd(x, *W, H=sh.H, eps=sh.eps, rope_base=sh.rope_base, window=sh.window or None)
+    c = ob.block_fwd(x, *W, H=sh.H, eps=sh.eps, rope_base=sh.rope_base, window=sh.window or None,
+                     n_kv_head=sh.n_kv_head or None)
     g = ob.block_bwd(dy, c, *W, H=sh.H)
     g["y"] = c.y
     return g

@@ -52,9 +52,14 @@ def test_size_queries(lib):
     assert bl.block_scratch_bytes(c) >= saved
     f32 = _cfg(dtype=bl.BLK_F32)
     assert bl.block_saved_bytes(f32) > 1.9 * saved
-    for bad in (_cfg(D=64), _cfg(C=1000), _cfg(F=4000), _cfg(B=0), _cfg(T=0), _cfg(dtype=7)):
+    for bad in (_cfg(D=64), _cfg(C=1000), _cfg(F=4000), _cfg(B=0), _cfg(T=0), _cfg(dtype=7),
+                _cfg(n_kv_head=-2), _cfg(n_kv_head=4)):
         assert bl.block_saved_bytes(bad) == 0
         assert bl.block_scratch_bytes(bad) == 0
+    # grouped-query attention: the saved qkv rows narrow from 3C to C + 2*G*128
+    g2 = _cfg(n_kv_head=2)
+    assert saved - bl.block_saved_bytes(g2) >= 2 * N * 2 * (10 - 2) * 128
+    assert bl.block_saved_bytes(_cfg(n_kv_head=10)) == saved
 
 
 A = 0x10000     # aligned fake addresses: the calls below must fail before any use
@@ -94,6 +99,8 @@ def test_fwd_argument_errors(lib):
     assert _fwd(_cfg(gemm=5)) == bl.binding.BLK_EINVAL
     assert _fwd(_cfg(eps=float("nan"))) == bl.binding.BLK_EINVAL
     assert _fwd(_cfg(window=-1)) == bl.binding.BLK_EINVAL
+    assert _fwd(_cfg(n_kv_head=-1)) == bl.binding.BLK_EINVAL
+    assert _fwd(_cfg(n_kv_head=3)) == bl.binding.BLK_EINVAL     # 10 query heads are not split in groups of 3
 
 
 def test_bwd_argument_errors(lib):
@@ -130,7 +137,7 @@ def test_decode_sizes_and_argument_errors(lib):
     assert need >= 64 * (1280 * (2 * 3 + 4) + 1280 * 4 + 5120 * 2)
     assert need < 64 << 20
     for bad in (_dcfg(D=64), _dcfg(C=1000), _dcfg(F=100), _dcfg(B=0), _dcfg(S_max=0), _dcfg(dtype=7),
-                _dcfg(window=-3)):
+                _dcfg(window=-3), _dcfg(n_kv_head=-1), _dcfg(n_kv_head=4)):
         assert bl.decode_scratch_bytes(bad) == 0
         assert _dec(bad) == bl.binding.BLK_EINVAL
     assert _dec(_dcfg(dtype=bl.BLK_F32)) == bl.binding.BLK_EUNSUPPORTED

@@ -156,3 +156,30 @@ def test_t1_value_path_gradients_vanish_for_q_k():
     r = g.results()
     C = sh.C
     assert np.max(np.abs(r["dw_qkv"][:2 * C])) <= 1e-5 * np.max(np.abs(r["dw_qkv"][2 * C:]))
+
+
+@pytest.mark.parametrize("B,T,C,G,dtype,W", [
+    (2, 300, 512, 1, "bf16", 0),     # one key/value head shared by four query heads
+    (1, 257, 512, 2, "bf16", 0),     # two groups of two, ragged tail of one
+    (2, 130, 768, 3, "bf16", 0),     # six heads in three groups
+    (1, 300, 512, 2, "bf16", 100),   # grouped heads under a sliding window
+    (2, 97, 512, 2, "f32", 0),
+    (2, 130, 512, 1, "f32", 45),
+])
+def test_gqa(B, T, C, G, dtype, W):
+    _parity(BlockShape(B=B, T=T, C=C, H=C // 128, F=4 * C, dtype=dtype, window=W, n_kv_head=G), seed=8)
+
+
+def test_gqa_g_equals_h_matches_mha_bitwise():
+    # n_kv_head = H takes the same kernels over the same layout as MHA
+    sh = BlockShape(B=2, T=200, C=256, H=2, F=1024, dtype="bf16")
+    inp = make_block_inputs(sh, seed=9)
+    outs = []
+    for G in (0, 2):
+        s2 = BlockShape(B=2, T=200, C=256, H=2, F=1024, dtype="bf16", n_kv_head=G)
+        g = GpuBlock(s2, inp)
+        g.fwd()
+        g.bwd()
+        outs.append(g.results())
+    for k in outs[0]:
+        assert np.array_equal(outs[0][k], outs[1][k]), k

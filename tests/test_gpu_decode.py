@@ -28,7 +28,7 @@ class GpuDecode:
         import backward_gpt_block_amd as bl
         self.sh = sh
         self.cfg = bl.DecodeConfig(B=sh.B, C=sh.C, H=sh.H, F=sh.F, S_max=sh.S_max, eps=sh.eps,
-                                   rope_base=sh.rope_base, window=sh.window)
+                                   rope_base=sh.rope_base, window=sh.window, n_kv_head=sh.n_kv_head)
         self.w = [to_dev(inp[k], "bf16") for k in WNAMES]
         self.kc = to_dev(inp["k_cache"], "bf16")
         self.vc = to_dev(inp["v_cache"], "bf16")
@@ -59,7 +59,8 @@ def _check_step(sh, inp, g: GpuDecode, x, lens, before_bits, in_place=False):
     y = g.step(x, lens, in_place=in_place)
     W = [inp[k] for k in WNAMES]
     y_ref, kc_ref, vc_ref = ob.decode_step(x, *W, inp["k_cache"], inp["v_cache"], lens, H=sh.H, eps=sh.eps,
-                                           rope_base=sh.rope_base, window=sh.window or None)
+                                           rope_base=sh.rope_base, window=sh.window or None,
+                                           n_kv_head=sh.n_kv_head or None)
     e = rel_err(y, y_ref)
     kb, vb = g.caches_bits()
     bidx = np.arange(sh.B)
@@ -142,3 +143,14 @@ def test_decode_d20_window_512_ragged():
     sh = DECODE_WORKLOADS["d20_decode"]
     sh = DecodeShape(B=sh.B, C=sh.C, H=sh.H, F=sh.F, S_max=sh.S_max, window=512)
     _decode_case(sh, ragged=True, ragged_lo=128, ragged_hi=2048)
+
+
+def test_decode_gqa_ragged():
+    # four query heads on one key/value head; then two groups of two
+    _decode_case(DecodeShape(B=5, C=512, H=4, F=2048, S_max=600, n_kv_head=1), lens=[0, 1, 255, 256, 599])
+    _decode_case(DecodeShape(B=4, C=512, H=4, F=2048, S_max=520, n_kv_head=2), ragged=True, ragged_lo=0)
+
+
+def test_decode_gqa_window_two_chained_steps():
+    _decode_case(DecodeShape(B=3, C=768, H=6, F=3072, S_max=520, window=200, n_kv_head=3), lens=[5, 256, 400],
+                 steps=2)

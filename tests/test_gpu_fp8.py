@@ -73,7 +73,8 @@ def _fp8_parity(sh: BlockShape, seed=0, keep=None, deep=()):
         res["y"], res["dx"] = res["y"][list(keep)], res["dx"][list(keep)]
     emu = fp8_block.block_fwd_bwd(inp["x"], inp["w_qkv"], inp["w_o"], inp["w_fc"], inp["w_proj"], inp["dy"],
                                   H=sh.H, eps=sh.eps, rope_base=sh.rope_base,
-                                  batch=None if keep is None else list(keep), log=note, window=sh.window or None)
+                                  batch=None if keep is None else list(keep), log=note, window=sh.window or None,
+                                  n_kv_head=sh.n_kv_head or None)
     keys = [k for k in emu if k not in deep]
     errs = compare(res, emu, TOL["fp8"], keys=keys)
     for k in deep:
@@ -104,3 +105,7 @@ def test_d26_fp8_full_size_sampled():
     # the oracle's forward pass over all 16 sequences (for the per-tensor
     # scales) takes a minute or two of host time
     _fp8_parity(WORKLOADS["d26_fp8"], keep=(0, 15), deep=("dw_qkv", "dw_o"))
+
+
+def test_fp8_block_gqa():
+    _fp8_parity(BlockShape(B=2, T=300, C=512, H=4, F=2048, dtype="bf16", gemm="fp8", n_kv_head=1))
