@@ -46,6 +46,21 @@ def window_of(sh) -> int:
     return sh.T if w <= 0 or w >= sh.T else w
 
 
+def kv_heads(sh) -> int:
+    """Key/value heads (grouped-query attention); H without grouping."""
+    return getattr(sh, "n_kv_head", 0) or sh.H
+
+
+def qkv_cols(sh) -> int:
+    """Output columns of the fused projection: H query, G key and G value heads of 128."""
+    return sh.C + 256 * kv_heads(sh)
+
+
+def matmul_params(sh) -> int:
+    """Weights of the block's four linear layers."""
+    return sh.C * (qkv_cols(sh) + sh.C + 2 * sh.F)
+
+
 def attn_matmul_flops(sh) -> float:
     """FLOPs of one T x T x D attention matmul over all heads and sequences,
     counting only the visible (query, key) pairs: sum_i min(i+1, W) per
@@ -55,10 +70,15 @@ def attn_matmul_flops(sh) -> float:
     return 2.0 * sh.B * sh.C * pairs
 
 
+def linear_flops(sh) -> float:
+    """Forward, input-gradient and weight-gradient GEMMs of the four linear
+    layers: 6 x their weights per token (72 C^2 without grouping)."""
+    return float(sh.B * sh.T) * 6.0 * matmul_params(sh)
+
+
 def step_flops(sh) -> float:
-    N, C = sh.B * sh.T, sh.C
-    # linear layers 72 C^2 per token; attention 2 matmuls forward, 4 backward
-    return float(N) * 72.0 * C * C + 6.0 * attn_matmul_flops(sh)
+    # attention: 2 matmuls forward, 4 backward
+    return linear_flops(sh) + 6.0 * attn_matmul_flops(sh)
 
 
 def step_flops_nanochat(sh) -> float:
@@ -66,7 +86,7 @@ def step_flops_nanochat(sh) -> float:
     per token for attention, W the window or T), which reproduces the depth
     table on the flicky.cc nanochat page."""
     N, C = sh.B * sh.T, sh.C
-    return float(N) * (72.0 * C * C + 12.0 * C * window_of(sh))
+    return float(N) * (6.0 * matmul_params(sh) + 12.0 * C * window_of(sh))
 
 
 def site_flops(sh) -> dict:
@@ -74,7 +94,7 @@ def site_flops(sh) -> dict:
     N, C, F = sh.B * sh.T, sh.C, sh.F
     att = attn_matmul_flops(sh)           # one attention matmul over the visible pairs
     g = {
-        "gemm_qkv_fwd": 2.0 * N * C * 3 * C, "gemm_o_fwd": 2.0 * N * C * C,
+        "gemm_qkv_fwd": 2.0 * N * C * qkv_cols(sh), "gemm_o_fwd": 2.0 * N * C * C,
         "gemm_fc_fwd": 2.0 * N * C * F, "gemm_proj_fwd": 2.0 * N * F * C,
         "attn_fwd": 2 * att,
         "attn_bwd_dkdv": 3 * att,      # dV = P^T dO, dP = dO V^T, dK = dS^T Q
@@ -96,7 +116,7 @@ def site_bytes(sh) -> dict:
     N, C, F = sh.B * sh.T, sh.C, sh.F
     out = {"rmsnorm_fwd": 2.0 * (2 * N * C * 2 + N * 4), "rmsnorm_bwd": 2.0 * (4 * N * C * 2)}
     if sh.gemm == "fp8":
-        w = 4 * C * C + 2 * C * F
+        w = matmul_params(sh)
         out["fp8_quantize"] = float(w * (5 + 3) + N * C * (3 * 4 + 6 + 4 + 3 * 4) + N * F * (4 + 4))
     return out
 
@@ -115,7 +135,7 @@ def cpu_baseline(sh, inp, budget_s: float = 12.0) -> dict:
     nseq = 0
     while nseq < sh.B:
         c = ob.block_fwd(inp["x"][nseq:nseq + 1], *W, H=sh.H, eps=sh.eps, rope_base=sh.rope_base,
-                         window=sh.window or None)
+                         window=sh.window or None, n_kv_head=sh.n_kv_head or None)
         ob.block_bwd(inp["dy"][nseq:nseq + 1], c, *W, H=sh.H)
         nseq += 1
         if time.perf_counter() - t0 >= budget_s:
@@ -221,7 +241,8 @@ def bench_train(args) -> int:
     W = [dev(inp[k]) for k in ("w_qkv", "w_o", "w_fc", "w_proj")]
     cfg = bl.BlockConfig(B=sh.B, T=sh.T, C=sh.C, H=sh.H, F=sh.F, eps=sh.eps, rope_base=sh.rope_base,
                          dtype=bl.BLK_BF16 if dt == "bf16" else bl.BLK_F32,
-                         gemm=bl.BLK_GEMM_FP8_E4M3 if sh.gemm == "fp8" else bl.BLK_GEMM_NATIVE, window=sh.window)
+                         gemm=bl.BLK_GEMM_FP8_E4M3 if sh.gemm == "fp8" else bl.BLK_GEMM_NATIVE, window=sh.window,
+                         n_kv_head=sh.n_kv_head)
     y, dx = torch.empty_like(x), torch.empty_like(x)
     dW = [torch.empty(w.shape, dtype=torch.float32, device="cuda:0") for w in W]
     saved = torch.empty(bl.block_saved_bytes(cfg), dtype=torch.uint8, device="cuda:0")
@@ -287,8 +308,7 @@ def bench_train(args) -> int:
     frac = tflops / peak
     if sh.gemm == "fp8":
         # mixed roofline: the linear layers at the fp8 dense peak, attention at the bf16 one
-        N, C = sh.B * sh.T, sh.C
-        t_star = N * 72.0 * C * C / (PEAK_TFLOPS["fp8"] * 1e12) + 6.0 * attn_matmul_flops(sh) / (PEAK_TFLOPS["bf16"] * 1e12)
+        t_star = linear_flops(sh) / (PEAK_TFLOPS["fp8"] * 1e12) + 6.0 * attn_matmul_flops(sh) / (PEAK_TFLOPS["bf16"] * 1e12)
         frac = t_star / (ms * 1e-3)
     cpu = None
     if not args.no_cpu_baseline:
@@ -301,7 +321,7 @@ def bench_train(args) -> int:
         "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3+bf16" if sh.gemm == "fp8" else dt,
         "data": "synthetic",
         "config": {"workload": args.workload, "B": sh.B, "T": sh.T, "C": sh.C, "H": sh.H, "D": sh.D, "F": sh.F,
-                   "gemm": sh.gemm, "window": window_of(sh), "tokens_per_step": tokens,
+                   "gemm": sh.gemm, "window": window_of(sh), "n_kv_head": kv_heads(sh), "tokens_per_step": tokens,
                    "parallelism": "none (1 GPU)"},
         "tflops": round(tflops, 2), "frac_of_peak": round(frac, 4),
         "tflops_nanochat_convention": round(step_flops_nanochat(sh) / (ms * 1e-3) / 1e12, 2),
@@ -314,21 +334,21 @@ def bench_train(args) -> int:
 def decode_attn_bytes(sh, lens) -> float:
     """Algorithmic HBM bytes of one decode attention launch: the keys and
     values of the visible slots (0..L_b, or the last W of them) of every
-    (sequence, head), bf16, and the q rows."""
+    (sequence, key/value head), bf16, and the q rows of every query head."""
     import numpy as np
     keys = np.asarray(lens, dtype=np.int64) + 1
     if getattr(sh, "window", 0) > 0:
         keys = np.minimum(keys, sh.window)
-    kv = 2.0 * sh.H * 128 * 2 * float(np.sum(keys))
+    kv = 2.0 * kv_heads(sh) * 128 * 2 * float(np.sum(keys))
     return kv + sh.B * sh.H * 128 * 4.0
 
 
 def decode_step_bytes(sh, lens) -> float:
     """Algorithmic HBM bytes of one decode step: every weight once (bf16),
     the cache reads, the new slot writes, x in and y out."""
-    C, F = sh.C, sh.F
-    w = 2.0 * (4 * C * C + 2 * C * F)
-    return w + decode_attn_bytes(sh, lens) + sh.B * (2.0 * sh.H * 128 * 2 + 2 * C * 2)
+    C = sh.C
+    w = 2.0 * matmul_params(sh)
+    return w + decode_attn_bytes(sh, lens) + sh.B * (2.0 * kv_heads(sh) * 128 * 2 + 2 * C * 2)
 
 
 def cpu_decode_baseline(sh, inp, lens, budget_s: float) -> dict:
@@ -346,7 +366,7 @@ def cpu_decode_baseline(sh, inp, lens, budget_s: float) -> dict:
     while n < sh.B:
         sl = slice(n, n + 1)
         ob.decode_step(inp["x"][sl], *W, inp["k_cache"][sl], inp["v_cache"][sl], lens[sl], H=sh.H, eps=sh.eps,
-                       rope_base=sh.rope_base)
+                       rope_base=sh.rope_base, window=sh.window or None, n_kv_head=sh.n_kv_head or None)
         n += 1
         if time.perf_counter() - t0 >= budget_s:
             break
@@ -377,7 +397,7 @@ def bench_decode(args) -> int:
     W = [dev(inp[k]) for k in ("w_qkv", "w_o", "w_fc", "w_proj")]
     kc, vc = dev(inp["k_cache"]), dev(inp["v_cache"])
     cfg = bl.DecodeConfig(B=sh.B, C=sh.C, H=sh.H, F=sh.F, S_max=sh.S_max, eps=sh.eps, rope_base=sh.rope_base,
-                          window=sh.window)
+                          window=sh.window, n_kv_head=sh.n_kv_head)
     y = torch.empty_like(x)
     scratch = torch.empty(bl.decode_scratch_bytes(cfg), dtype=torch.uint8, device="cuda:0")
     stream = torch.cuda.current_stream()
@@ -434,7 +454,8 @@ def bench_decode(args) -> int:
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": args.workload, "B": sh.B, "C": sh.C, "H": sh.H, "D": sh.D, "F": sh.F,
-                   "S_max": sh.S_max, "cache_len": int(lens_u[0]), "parallelism": "none (1 GPU)"},
+                   "S_max": sh.S_max, "cache_len": int(lens_u[0]), "window": sh.window, "n_kv_head": kv_heads(sh),
+                   "parallelism": "none (1 GPU)"},
         "step_gbs": round(step_b / (ms * 1e-3) / 1e9, 1), "step_frac_of_hbm": round(step_b / (ms * 1e-3) / 1e12 / 8.0, 4),
         "ragged_variant": {"cache_len": "uniform 128..2048", "ms_per_step": round(ms_r, 5),
                            "value": round(sh.B / (ms_r * 1e-3), 1),

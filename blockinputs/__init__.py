@@ -108,7 +108,7 @@ def _shape(depth: int, B: int, T: int, **kw) -> BlockShape:
     return BlockShape(B=B, T=T, C=C, H=H, F=F, **kw)
 
 
-# The five named workloads (sizes and distributions as the benchmark's configs
+# The named workloads (sizes and distributions as the benchmark's configs
 # state them; d20 is the speedrun width of the pages).
 WORKLOADS = {
     "d6_f32": _shape(6, B=1, T=512, dtype="f32"),
@@ -117,6 +117,8 @@ WORKLOADS = {
     "d26_fp8": _shape(26, B=16, T=2048, gemm="fp8"),
     # a short-window layer of the SSSL pattern: window T/4
     "d20_bf16_swa": _shape(20, B=32, T=2048, window=512),
+    # grouped-query attention at d20: ten query heads on two key/value heads
+    "d20_bf16_gqa": _shape(20, B=32, T=2048, n_kv_head=2),
 }
 _C20, _H20, _F20 = from_depth(20)
 HEAD_WORKLOADS = {
@@ -125,6 +127,7 @@ HEAD_WORKLOADS = {
 }
 DECODE_WORKLOADS = {
     "d20_decode": DecodeShape(B=64, C=_C20, H=_H20, F=_F20, S_max=2049),
+    "d20_decode_gqa": DecodeShape(B=64, C=_C20, H=_H20, F=_F20, S_max=2049, n_kv_head=2),
 }
 
 

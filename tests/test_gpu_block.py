@@ -183,3 +183,7 @@ def test_gqa_g_equals_h_matches_mha_bitwise():
         outs.append(g.results())
     for k in outs[0]:
         assert np.array_equal(outs[0][k], outs[1][k]), k
+
+
+def test_d20_gqa_full_size_sampled():
+    _sampled_full("d20_bf16_gqa", (0, 31))

@@ -154,3 +154,7 @@ def test_decode_gqa_ragged():
 def test_decode_gqa_window_two_chained_steps():
     _decode_case(DecodeShape(B=3, C=768, H=6, F=3072, S_max=520, window=200, n_kv_head=3), lens=[5, 256, 400],
                  steps=2)
+
+
+def test_decode_d20_gqa_ragged_128_2048():
+    _decode_case(DECODE_WORKLOADS["d20_decode_gqa"], ragged=True, ragged_lo=128, ragged_hi=2048)
