@@ -952,9 +952,10 @@ int decode_step(const blk_dcfg* cfg, const void* x, const void* w_qkv, const voi
   const int dwin = c.window > 0 ? c.window : INT_MAX;
   {  // attention of the new token over slots 0..cache_len[b] (the last W with a window)
     Timed t("dec_attn", st);
-    hipLaunchKernelGGL(dec::dec_attn_kernel, dim3(NS, H, B), dim3(256), 0, st, (const float*)d.q,
-                       (const bf16*)kc, (const bf16*)vc, cache_len, H, kv_heads(c), c.S_max, NS, dwin,
-                       (float)(1.4426950408889634 / std::sqrt(128.0)), d.opart, d.ml);
+    const int G = kv_heads(c);
+    hipLaunchKernelGGL(G == H ? dec::dec_attn_kernel<false> : dec::dec_attn_kernel<true>, dim3(NS, G, B), dim3(256),
+                       dec::dec_attn_lds(H / G), st, (const float*)d.q, (const bf16*)kc, (const bf16*)vc, cache_len,
+                       H, G, c.S_max, NS, dwin, (float)(1.4426950408889634 / std::sqrt(128.0)), d.opart, d.ml);
   }
   {
     Timed t("dec_combine", st);

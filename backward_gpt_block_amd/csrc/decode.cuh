@@ -177,40 +177,47 @@ __global__ __launch_bounds__(192) void dec_qkv_epi_kernel(const float* __restric
   }
 }
 
-// One split of KEYS keys of one (sequence, head): keys j in
-// [s*KEYS, min((s+1)*KEYS, L)), L = cache_len[b] + 1.  Writes the split's
-// running maximum m (log2 units), sum l = sum 2^(t_j - m) and unnormalised
-// output sum 2^(t_j - m) v_j, t_j = log2(e) q.k_j / sqrt(128).
-// Grid (NS, H, B), 4 waves of 64 keys.  Lane (g = lane/16, r = lane%16)
-// holds dims 8r..8r+7 of keys base + 4i + g, i = 0..15.
-// With a window W only the keys j0 = max(0, L - W) .. L-1 are visible;
-// splits wholly before j0 write nothing.
+// One split of KEYS keys of one (sequence, key/value head): keys j in
+// [s*KEYS, min((s+1)*KEYS, L)), L = cache_len[b] + 1.  For each of the R =
+// H/G query heads that share the key/value head it writes the split's running
+// maximum m (log2 units), sum l = sum 2^(t_j - m) and unnormalised output
+// sum 2^(t_j - m) v_j, t_j = log2(e) q.k_j / sqrt(128).  The keys and values
+// are loaded once into registers and serve every query head of the group.
+// Grid (NS, G, B), 4 waves of 64 keys, dynamic LDS dec_attn_lds(R).  Lane
+// (g = lane/16, r = lane%16) holds dims 8r..8r+7 of keys base + 4i + g,
+// i = 0..15.  With a window W only the keys j0 = max(0, L - W) .. L-1 are
+// visible; splits wholly before j0 write nothing.
 __device__ __forceinline__ int first_visible(int L, int W) { return L > W ? L - W : 0; }
 
+__host__ __device__ constexpr size_t dec_attn_lds(int R) { return (size_t)R * (5 * 128 + 8) * sizeof(float); }
+
+// GROUPED = false is the R = 1 instance (no head loop; K can be released
+// while V is still in flight).
+template <bool GROUPED>
 __global__ __launch_bounds__(256) void dec_attn_kernel(const float* __restrict__ qbuf, const bf16* __restrict__ kc,
                                                        const bf16* __restrict__ vc, const int* __restrict__ cache_len,
                                                        int H, int G, int S_max, int NS, int W, float sl2,
                                                        float* __restrict__ opart, float2* __restrict__ ml) {
-  __shared__ float wo[4][128];
-  __shared__ float wm[4], wl[4];
-  const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  extern __shared__ float dsm[];
+  const int R = GROUPED ? H / G : 1;
+  float* wo = dsm;                 // [R][4][128] per-wave output sums
+  float* wm = dsm + R * 512;       // [R][4] per-wave maxima
+  float* wl = wm + R * 4;          // [R][4] per-wave sums
+  float* qs = wl + R * 4;          // [R][128] the group's q rows, scaled
+  const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int L = clamp_pos(cache_len, b, S_max) + 1;
   const int j0 = first_visible(L, W);
   if (s * KEYS >= L || (s + 1) * KEYS <= j0) return;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, r = lane & 15;
   const int kb = s * KEYS + wv * 64;
-  const long head = (long)(b * H + h);
-  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, l = 0.f;
+  const long head0 = (long)b * H + (long)kvh * R;   // first query head of the group
+  if constexpr (GROUPED) {
+    for (int e = threadIdx.x; e < R * 128; e += 256) qs[e] = qbuf[head0 * 128 + e] * sl2;
+    __syncthreads();
+  }
   if (kb < L && kb + 63 >= j0) {
-    float q[8];
-    {
-      const float* qp = qbuf + head * 128 + r * 8;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) q[e] = qp[e] * sl2;
-    }
-    const long kvrow = (long)b * G + h / (H / G);   // this query head's key/value head
+    const long kvrow = (long)b * G + kvh;
     const bf16* kp = kc + kvrow * S_max * 128 + r * 8;
     const bf16* vp = vc + kvrow * S_max * 128 + r * 8;
     u32x4 kr[16], vr[16];
@@ -224,70 +231,102 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(const float* __restrict__
       const long j = min(kb + 4 * i + g, L - 1);
       vr[i] = ld16(vp + j * 128);
     }
-    // partial dot products over this lane's 8 dims, then a transposing
-    // butterfly over the 16 lanes of the key group: after the steps with
-    // masks 8, 4, 2, 1 lane r holds the full score of key base + 4r + g
-    float t[16];
+    const bool valid = kb + 4 * r + g < L && kb + 4 * r + g >= j0;
+    for (int hr = 0; hr < R; ++hr) {
+      // keep K and V packed across the head loop: unpacking them once for
+      // every head would take 256 float registers
+      if constexpr (GROUPED) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float f[8];
-      Chunk<bf16>::unpack(kr[i], f);
-      float a = 0.f;
+        for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(kr[i]), "+v"(vr[i]));
+      }
+      float q[8];
+      if constexpr (GROUPED) {
+        Chunk<float>::unpack(*reinterpret_cast<const u32x4*>(qs + hr * 128 + r * 8), q);
+        Chunk<float>::unpack(*reinterpret_cast<const u32x4*>(qs + hr * 128 + r * 8 + 4), q + 4);
+      } else {
+        const float* qp = qbuf + (head0 + hr) * 128 + r * 8;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) a += q[e] * f[e];
-      t[i] = a;
-    }
+        for (int e = 0; e < 8; ++e) q[e] = qp[e] * sl2;
+      }
+      // partial dot products over this lane's 8 dims, then a transposing
+      // butterfly over the 16 lanes of the key group: after the steps with
+      // masks 8, 4, 2, 1 lane r holds the full score of key base + 4r + g
+      float t[16];
 #pragma unroll
-    for (int half = 8; half >= 1; half >>= 1) {
-      const bool up = (r & half) != 0;
+      for (int i = 0; i < 16; ++i) {
+        float f[8];
+        Chunk<bf16>::unpack(kr[i], f);
+        float a = 0.f;
 #pragma unroll
-      for (int i = 0; i < half; ++i) {
-        const float send = up ? t[i] : t[i + half];
-        const float keep = up ? t[i + half] : t[i];
-        t[i] = keep + __shfl_xor(send, half, 64);
+        for (int e = 0; e < 8; ++e) a += q[e] * f[e];
+        t[i] = a;
+      }
+#pragma unroll
+      for (int half = 8; half >= 1; half >>= 1) {
+        const bool up = (r & half) != 0;
+#pragma unroll
+        for (int i = 0; i < half; ++i) {
+          // the empty asm keeps the two picks selects of values: folded
+          // into one load of t at a per-lane index, they would become a
+          // compare-and-select chain over all 16 entries once unrolled
+          float lo = t[i], hi = t[i + half];
+          asm("" : "+v"(lo), "+v"(hi));
+          const float send = up ? lo : hi;
+          const float keep = up ? hi : lo;
+          t[i] = keep + __shfl_xor(send, half, 64);
+        }
+      }
+      const float sc = valid ? t[0] : -INFINITY;
+      const float m = wave_max(sc);
+      const float p = valid ? __builtin_amdgcn_exp2f(sc - m) : 0.f;
+      const float l = wave_sum(p);
+      float pk[16];   // p of the keys this lane multiplies: held by lanes 16g + i
+#pragma unroll
+      for (int i = 0; i < 16; ++i) pk[i] = __shfl(p, 16 * g + i, 64);
+      float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float f[8];
+        Chunk<bf16>::unpack(vr[i], f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] += pk[i] * f[e];
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        o[e] += __shfl_xor(o[e], 16, 64);
+        o[e] += __shfl_xor(o[e], 32, 64);
+      }
+      if (lane < 16) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) wo[(hr * 4 + wv) * 128 + lane * 8 + e] = o[e];
+      }
+      if (lane == 0) {
+        wm[hr * 4 + wv] = m;
+        wl[hr * 4 + wv] = l;
       }
     }
-    const bool valid = kb + 4 * r + g < L && kb + 4 * r + g >= j0;
-    const float sc = valid ? t[0] : -INFINITY;
-    m = wave_max(sc);
-    const float p = valid ? __builtin_amdgcn_exp2f(sc - m) : 0.f;
-    l = wave_sum(p);
-    float pk[16];   // p of the keys this lane multiplies: held by lanes 16g + i
-#pragma unroll
-    for (int i = 0; i < 16; ++i) pk[i] = __shfl(p, 16 * g + i, 64);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float f[8];
-      Chunk<bf16>::unpack(vr[i], f);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] += pk[i] * f[e];
+  } else {
+    // a wave with no visible key contributes nothing to any head
+    for (int e = lane; e < R * 128; e += 64) wo[(e / 128 * 4 + wv) * 128 + e % 128] = 0.f;
+    for (int hr = lane; hr < R; hr += 64) {
+      wm[hr * 4 + wv] = -INFINITY;
+      wl[hr * 4 + wv] = 0.f;
     }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      o[e] += __shfl_xor(o[e], 16, 64);
-      o[e] += __shfl_xor(o[e], 32, 64);
-    }
-  }
-  if (lane < 16) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) wo[wv][lane * 8 + e] = o[e];
-  }
-  if (lane == 0) {
-    wm[wv] = m;
-    wl[wv] = l;
   }
   __syncthreads();
-  if (threadIdx.x < 128) {
-    const int d = threadIdx.x;
-    const float M = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));   // finite: some wave has keys
+  for (int e = threadIdx.x; e < R * 128; e += 256) {
+    const int hr = e / 128, d = e % 128;
+    const float* m4 = wm + hr * 4;
+    const float* l4 = wl + hr * 4;
+    const float M = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));   // finite: some wave has keys
     float acc = 0.f, lsum = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const float f = wm[w] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(wm[w] - M);
-      acc += f * wo[w][d];
-      lsum += f * wl[w];
+      const float f = m4[w] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m4[w] - M);
+      acc += f * wo[(hr * 4 + w) * 128 + d];
+      lsum += f * l4[w];
     }
-    const long slot = head * NS + s;
+    const long slot = (head0 + hr) * NS + s;
     opart[slot * 128 + d] = acc;
     if (d == 0) ml[slot] = make_float2(M, lsum);
   }
