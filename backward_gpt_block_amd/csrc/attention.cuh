@@ -19,12 +19,11 @@
 // rotary precede it: flicky.cc nanochat page, section on the model.)
 #pragma once
 #include <type_traits>
+#include "attn_args.cuh"
 #include "common.cuh"
-#include "gemm.cuh"
 
 namespace blk {
 
-constexpr int HD = 128;   // head size
 
 template <typename T> struct AttnCfg {
   static constexpr int EL = 16 / sizeof(T);          // elements per chunk
@@ -240,25 +239,7 @@ __device__ __forceinline__ float store_acc_row_qk(bf16* dst, const bf16* z, floa
   return mx;   // largest stored magnitude, before rounding
 }
 
-struct AttnArgs {
-  const void* qkv;   // [B*T, 3C]: q'' | k'' | v, heads contiguous in each
-  void* o;           // [B*T, C]
-  float* lse;        // [B*H, T], log2-domain log-sum-exp of the scaled scores
-  const void* dO;    // [B*T, C]
-  const float* delta;  // [B*H, T] rowsum(dO * O)
-  void* dqkv;        // [B*T, 3C]: dq'' | dk'' | dv; bf16 kernels: dq' | dk' | dv
-  const float* rho;    // [2][B*T][H] QK-norm factors (bf16 backward kernels)
-  const float2* cs;    // [T][64] rotary angles (bf16 backward kernels)
-  unsigned* amax_o;    // fp8 mode: absolute maxima (float bits) of o and of
-  unsigned* amax_dqkv; //   dq' | dk' | dv, or null
-  int B, T, H, C;
-  int G;             // key/value heads (query head h uses key/value head h / (H/G))
-  int LD;            // elements per row of qkv / dqkv: C + 2 G D
-  int KO, VO;        // column of the first key / value head in a qkv row: C, C + G D
-  int W;             // attention window: query i sees keys i - W < j <= i (W >= T: causal)
-  float sl2;         // log2(e) / sqrt(D)
-  float rsd;         // 1 / sqrt(D)
-};
+
 
 // ---- forward ----------------------------------------------------------------
 template <typename T>

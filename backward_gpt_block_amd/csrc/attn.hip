@@ -1,0 +1,67 @@
+// Attention kernels and their launchers, a translation unit of its own so
+// that it can be compiled with MFMA results placed in vector registers (see
+// attn_args.cuh).  Everything else in the library launches attention through
+// the three functions below.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <set>
+
+#include "attention.cuh"
+
+namespace blk {
+namespace {
+
+std::mutex g_mu;
+std::set<const void*> g_done;
+
+// Raise a kernel's dynamic LDS limit once (past 64 KiB it must be raised).
+void allow_lds(const void* kern, int bytes) {
+  std::lock_guard<std::mutex> l(g_mu);
+  if (g_done.insert(kern).second) hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+}
+
+int tiles(int n, int t) { return (n + t - 1) / t; }
+
+constexpr int DKDV_LDS = 3 * (2 * fa::TILE + 2048);   // three slots of Q, dO, lse, delta
+
+}  // namespace
+
+void attn_fwd(const AttnArgs& a, bool bf16, hipStream_t st) {
+  if (bf16) {
+    // the windowed instance only when the window is shorter than the sequence
+    auto kern = a.W < a.T ? attn_fwd_bf16_kernel<true> : attn_fwd_bf16_kernel<false>;
+    allow_lds(reinterpret_cast<const void*>(kern), fa::LDS);
+    hipLaunchKernelGGL(kern, dim3(tiles(a.T, fa::QWG) * a.B * a.H), dim3(256), fa::LDS, st, a);
+  } else {
+    allow_lds(reinterpret_cast<const void*>(attn_fwd_kernel<float>), attn_fwd_lds<float>());
+    hipLaunchKernelGGL(attn_fwd_kernel<float>, dim3(tiles(a.T, 128) * a.B * a.H), dim3(256), attn_fwd_lds<float>(),
+                       st, a);
+  }
+}
+
+void attn_bwd_dkdv(const AttnArgs& a, bool bf16, hipStream_t st) {
+  // one workgroup per 128 keys of a (sequence, key/value head)
+  const dim3 grid(tiles(a.T, 128) * a.B * a.G);
+  if (bf16) {
+    allow_lds(reinterpret_cast<const void*>(attn_bwd_dkdv_bf16_kernel), DKDV_LDS);
+    hipLaunchKernelGGL(attn_bwd_dkdv_bf16_kernel, grid, dim3(256), DKDV_LDS, st, a);
+  } else {
+    allow_lds(reinterpret_cast<const void*>(attn_bwd_dkdv_kernel<float>), attn_dkdv_lds<float>());
+    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<float>, grid, dim3(256), attn_dkdv_lds<float>(), st, a);
+  }
+}
+
+void attn_bwd_dq(const AttnArgs& a, bool bf16, hipStream_t st) {
+  // one workgroup per 128 queries of a (sequence, head)
+  const dim3 grid(tiles(a.T, 128) * a.B * a.H);
+  if (bf16) {
+    allow_lds(reinterpret_cast<const void*>(attn_bwd_dq_bf16_kernel), fa::LDS);
+    hipLaunchKernelGGL(attn_bwd_dq_bf16_kernel, grid, dim3(256), fa::LDS, st, a);
+  } else {
+    allow_lds(reinterpret_cast<const void*>(attn_bwd_dq_kernel<float>), attn_dq_lds<float>());
+    hipLaunchKernelGGL(attn_bwd_dq_kernel<float>, grid, dim3(256), attn_dq_lds<float>(), st, a);
+  }
+}
+
+}  // namespace blk

@@ -1,0 +1,41 @@
+// Arguments of the attention kernels and their host launchers.  The kernels
+// themselves (attention.cuh) are compiled in a translation unit of their own
+// (attn.hip), with MFMA results kept in ordinary vector registers: the
+// score and probability blocks feed vector arithmetic after every MFMA chain,
+// and with the compiler's default placement of MFMA results in accumulation
+// registers they were copied back and forth several times per MFMA.
+#pragma once
+#include "common.cuh"
+
+namespace blk {
+
+constexpr int HD = 128;   // head size
+
+struct AttnArgs {
+  const void* qkv;   // [B*T, LD]: q'' (H heads) | k'' (G) | v (G), heads contiguous in each
+  void* o;           // [B*T, C]
+  float* lse;        // [B*H, T], log2-domain log-sum-exp of the scaled scores
+  const void* dO;    // [B*T, C]
+  const float* delta;  // [B*H, T] rowsum(dO * O)
+  void* dqkv;        // [B*T, LD]: dq'' | dk'' | dv; bf16 kernels: dq' | dk' | dv
+  const float* rho;    // [2][B*T][H] QK-norm factors (bf16 backward kernels)
+  const float2* cs;    // [T][64] rotary angles (bf16 backward kernels)
+  unsigned* amax_o;    // fp8 mode: absolute maxima (float bits) of o and of
+  unsigned* amax_dqkv; //   dq' | dk' | dv, or null
+  int B, T, H, C;
+  int G;             // key/value heads (query head h uses key/value head h / (H/G))
+  int LD;            // elements per row of qkv / dqkv: C + 2 G D
+  int KO, VO;        // column of the first key / value head in a qkv row: C, C + G D
+  int W;             // attention window: query i sees keys i - W < j <= i (W >= T: causal)
+  float sl2;         // log2(e) / sqrt(D)
+  float rsd;         // 1 / sqrt(D)
+};
+
+// Launchers (attn.hip).  bf16: the gfx950 pipelines (direct-to-LDS staging,
+// QK-norm and rotary backward applied in the stores of dq and dk); otherwise
+// the float32 kernels.  Grids, LDS sizes and kernel attributes are theirs.
+void attn_fwd(const AttnArgs& a, bool bf16, hipStream_t st);
+void attn_bwd_dkdv(const AttnArgs& a, bool bf16, hipStream_t st);
+void attn_bwd_dq(const AttnArgs& a, bool bf16, hipStream_t st);
+
+}  // namespace blk

@@ -13,7 +13,7 @@
 #include <vector>
 
 #include "../../include/blk.h"
-#include "attention.cuh"
+#include "attn_args.cuh"
 #include "decode.cuh"
 #include "elementwise.cuh"
 #include "fp8.cuh"
@@ -324,15 +324,6 @@ void wgrad(GemmKernel kern, GemmKernel kern_acc, GemmKernel kp, GemmKernel kp_ac
 unsigned row_blocks(long rows) { return (unsigned)((rows + 3) / 4); }
 
 // ---------------------------------------------------------------- forward
-// bf16 flash forward: the windowed instance only when the window is shorter
-// than the sequence.
-void attn_fwd_bf16(const AttnArgs& a, hipStream_t st) {
-  auto kern = a.W < a.T ? attn_fwd_bf16_kernel<true> : attn_fwd_bf16_kernel<false>;
-  need_lds(reinterpret_cast<const void*>(kern), fa::LDS);
-  const int nqt = (a.T + fa::QWG - 1) / fa::QWG;
-  hipLaunchKernelGGL(kern, dim3(nqt * a.B * a.H), dim3(256), fa::LDS, st, a);
-}
-
 template <typename T> AttnArgs attn_args(const blk_cfg& c) {
   AttnArgs a{};
   a.B = c.B; a.T = c.T; a.H = c.H; a.C = c.C;
@@ -369,13 +360,7 @@ int fwd_impl(const blk_cfg& c, const T* x, const T* wqkv, const T* wo, const T* 
     AttnArgs a = attn_args<T>(c);
     a.qkv = s.qkv; a.o = s.o; a.lse = s.lse;
     Timed t("attn_fwd", st);
-    if constexpr (sizeof(T) == 2) {
-      attn_fwd_bf16(a, st);
-    } else {
-      need_lds(reinterpret_cast<const void*>(attn_fwd_kernel<T>), attn_fwd_lds<T>());
-      const int nqt = (c.T + 127) / 128;
-      hipLaunchKernelGGL(attn_fwd_kernel<T>, dim3(nqt * c.B * H), dim3(256), attn_fwd_lds<T>(), st, a);
-    }
+    attn_fwd(a, sizeof(T) == 2, st);
   }
   {  // 6 y1 = x + o W_o^T   (y1 is kept in y)
     GemmArgs g = gargs(s.o, C, wo, C, N, C, C);
@@ -454,31 +439,16 @@ int bwd_impl(const blk_cfg& c, const T* dy, const T* x, const T* wqkv, const T* 
     AttnArgs a = attn_args<T>(c);
     a.qkv = s.qkv; a.lse = s.lse; a.dO = w.dO; a.delta = w.delta; a.dqkv = w.dqkv;
     a.rho = s.rho; a.cs = s.cs;
-    const int nqt = (c.T + 127) / 128;
     // 5-3: the bf16 kernels also apply the QK-norm and rotary backward to dq, dk
-    if constexpr (sizeof(T) == 2) {
-      constexpr int DKDV_LDS = 3 * (2 * fa::TILE + 2048);
-      need_lds(reinterpret_cast<const void*>(attn_bwd_dkdv_bf16_kernel), DKDV_LDS);
-      need_lds(reinterpret_cast<const void*>(attn_bwd_dq_bf16_kernel), fa::LDS);
-      {
-        Timed t("attn_bwd_dkdv", st);
-        hipLaunchKernelGGL(attn_bwd_dkdv_bf16_kernel, dim3(nqt * c.B * a.G), dim3(256), DKDV_LDS, st, a);
-      }
-      {
-        Timed t("attn_bwd_dq", st);
-        hipLaunchKernelGGL(attn_bwd_dq_bf16_kernel, dim3(nqt * c.B * H), dim3(256), fa::LDS, st, a);
-      }
-    } else {
-      need_lds(reinterpret_cast<const void*>(attn_bwd_dq_kernel<T>), attn_dq_lds<T>());
-      need_lds(reinterpret_cast<const void*>(attn_bwd_dkdv_kernel<T>), attn_dkdv_lds<T>());
-      {
-        Timed t("attn_bwd_dkdv", st);
-        hipLaunchKernelGGL(attn_bwd_dkdv_kernel<T>, dim3(nqt * c.B * a.G), dim3(256), attn_dkdv_lds<T>(), st, a);
-      }
-      {
-        Timed t("attn_bwd_dq", st);
-        hipLaunchKernelGGL(attn_bwd_dq_kernel<T>, dim3(nqt * c.B * H), dim3(256), attn_dq_lds<T>(), st, a);
-      }
+    {
+      Timed t("attn_bwd_dkdv", st);
+      attn_bwd_dkdv(a, sizeof(T) == 2, st);
+    }
+    {
+      Timed t("attn_bwd_dq", st);
+      attn_bwd_dq(a, sizeof(T) == 2, st);
+    }
+    if constexpr (sizeof(T) != 2) {
       {  // 4-3: QK-norm and rotary backward (in place on dq, dk)
         Timed t("qknorm_rope_bwd", st);
         hipLaunchKernelGGL(qknorm_rope_bwd_kernel<T>, dim3(row_blocks((long)N * (H + a.G))), dim3(256), 0, st,
@@ -590,7 +560,7 @@ int fwd_fp8(const blk_cfg& c, const bf16* x, const bf16* wqkv, const bf16* wo, c
     AttnArgs a = attn_args<bf16>(c);
     a.qkv = s.qkv; a.o = s.o; a.lse = s.lse; a.amax_o = am + AM_O;
     Timed t("attn_fwd", st);
-    attn_fwd_bf16(a, st);
+    attn_fwd(a, true, st);
   }
   quantize(s.o, N, C, am + AM_O, f.o, s.o_8t, Np, false, st);       // amax from attn_fwd
   {
@@ -670,17 +640,13 @@ int bwd_fp8(const blk_cfg& c, const bf16* dy, const bf16* wqkv, const bf16* wo, 
     a.qkv = s.qkv; a.lse = s.lse; a.dO = w.dO; a.delta = w.delta; a.dqkv = w.dqkv;
     a.rho = s.rho; a.cs = s.cs;   // QK-norm and rotary backward in the stores
     a.amax_dqkv = am + AM_DQKV;
-    constexpr int DKDV_LDS = 3 * (2 * fa::TILE + 2048);
-    need_lds(reinterpret_cast<const void*>(attn_bwd_dkdv_bf16_kernel), DKDV_LDS);
-    need_lds(reinterpret_cast<const void*>(attn_bwd_dq_bf16_kernel), fa::LDS);
-    const int nqt = (c.T + 127) / 128;
     {
       Timed t("attn_bwd_dkdv", st);
-      hipLaunchKernelGGL(attn_bwd_dkdv_bf16_kernel, dim3(nqt * c.B * a.G), dim3(256), DKDV_LDS, st, a);
+      attn_bwd_dkdv(a, true, st);
     }
     {
       Timed t("attn_bwd_dq", st);
-      hipLaunchKernelGGL(attn_bwd_dq_bf16_kernel, dim3(nqt * c.B * H), dim3(256), fa::LDS, st, a);
+      attn_bwd_dq(a, true, st);
     }
   }
   quantize(w.dqkv, N, qkv_width(c), am + AM_DQKV, w.dqkv8, w.dqkv8t, Np, false, st);   // amax from attention bwd

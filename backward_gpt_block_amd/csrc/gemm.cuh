@@ -87,22 +87,7 @@ template <typename TI> struct GemmTile {
   static constexpr int LDS = 2 * SLAB;           // 128 KiB
 };
 
-// ---- buffer resources -------------------------------------------------------
-typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) uint32_t lds_u32;
-
-__device__ void raw_buffer_load_lds(i32x4 rsrc, lds_u32* lds, int size, int voffset, int soffset, int offset,
-                                    int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
-__device__ u32x4 raw_buffer_load_b128(i32x4 rsrc, int voffset, int soffset, int aux) __asm(
-    "llvm.amdgcn.raw.buffer.load.v4i32");
-
-// Buffer resource over [p, p + bytes): loads at offsets >= bytes return 0.
-__device__ __forceinline__ i32x4 make_rsrc(const void* p, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(p);
-  return i32x4{(int)(uint32_t)a, (int)((a >> 32) & 0xffff), (int)bytes, 0x00020000};
-}
-
-__device__ __forceinline__ uint32_t clamp_bytes(long b) { return b > 0xffffffffL ? 0xffffffffu : (uint32_t)b; }
+// buffer resources (i32x4, make_rsrc, raw_buffer_load_lds): common.cuh
 
 // ---- staging ------------------------------------------------------------------
 // k-contiguous slab of R rows: 8 chunks per row, R*8 chunks, 64 per wave issue.
