@@ -633,6 +633,18 @@ __device__ __forceinline__ bf16x8 frag_vt_at(const lds_char* tile, const int* vo
   return __builtin_bit_cast(bf16x8, r);
 }
 
+// frag_vt_at with the offsets rebuilt from one per-lane base (vbase = the
+// run-0, d-block-0 offset): the swizzle XOR and the d-block step touch bits
+// 6-7 only, so offset(run, db) = (vbase ^ (db << 6)) + 2048 * run.
+__device__ __forceinline__ bf16x8 frag_vt_x(const lds_char* tile, int vbase, int mm, int db) {
+  const lds_char* p = tile + mm * 4096 + (vbase ^ (db << 6));
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 2048));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
 // A fragment of V^T for MFMA chunk mm (16 keys) and d-block db: lane l holds
 // d = db*32 + l%32 and keys 16mm + 4h + {0..3}, 16mm + 8 + 4h + {0..3} (h = l/32),
 // the key order of the P^T fragment built from the score registers.
@@ -855,9 +867,15 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_bf16_kernel(AttnArgs a) 
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) { dk[i][r] = 0.f; dv[i][r] = 0.f; }
-  int ko[8], vo[8];
-  frag_k_offsets(ko, lane);
-  frag_vt_offsets(vo, lane);
+  // LDS offsets of the fragment reads from one base each: row-fragment read
+  // ks at kbase ^ (ks << 5), transpose reads as in frag_vt_x
+  int kbase = off(lane & 31, lane >> 5);
+  int vbase;
+  {
+    int vo[8];
+    frag_vt_offsets(vo, lane);
+    vbase = vo[0];
+  }
 
   const int qt0 = (kt * 128) / QT;
   // the last query that sees a key of this workgroup is kt*128 + 127 + W - 1
@@ -885,6 +903,9 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_bf16_kernel(AttnArgs a) 
       __builtin_amdgcn_s_waitcnt(0x0f70);
     }
     __syncthreads();
+    // the bases count as changed here, so that the eight offsets derived from
+    // each are not hoisted out of the loop into sixteen live registers
+    asm volatile("" : "+v"(kbase), "+v"(vbase));
     if (it + 2 < n) issue((it + 2) % 3, it + 2);
     const int q0 = (qt0 + it % nq) * QT;
     const lds_char* qt_ = (const lds_char*)smem + (it % 3) * SLOTB;
@@ -897,82 +918,78 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_bf16_kernel(AttnArgs a) 
     // so that each is a single scheduling region
     auto body = [&](auto maskc) {
     constexpr bool MASK = decltype(maskc)::value;
-    // Two 32-query halves, software-pipelined so that each half's softmax and
-    // dS arithmetic issues between independent MFMAs: S/dP(0); S/dP(1) with
-    // softmax(0); dV/dK(0) with softmax(1); dV/dK(1).
-    f32x16 sv[2], dp[2];
-    auto sdp = [&](int qb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) { sv[qb][r] = 0.f; dp[qb][r] = 0.f; }
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8 qa = *(lds_bf16x8*)(qt_ + qb * 8192 + ko[ks]);
-        const bf16x8 oa = *(lds_bf16x8*)(ot_ + qb * 8192 + ko[ks]);
-        sv[qb] = MM::mma(qa, kf[ks], sv[qb]);       // S  (query x key)
-        dp[qb] = MM::mma(oa, vf[ks], dp[qb]);       // dP (query x key)
+    // Two 32-query halves in 32 steps of two MFMAs: S/dP(0); S/dP(1) with the
+    // softmax of half 0; dV/dK(0) with the softmax of half 1; dV/dK(1).  Each
+    // step issues the LDS reads of the step after next and ends with a
+    // scheduling fence, so every MFMA finds its fragments already loaded
+    // (left to itself the scheduler put each read right before its MFMA,
+    // which then waited out the LDS latency).
+    f32x16 sv[2] = {}, dp[2] = {};
+    bf16x8 fa[32], fb[32];   // the two fragments of step i
+    auto rd = [&](int i) {
+      if (i < 16) {          // Q and dO rows of half i/8, k-step i%8
+        const int qb = i >> 3, ks = i & 7;
+        fa[i] = *(lds_bf16x8*)(qt_ + qb * 8192 + (kbase ^ (ks << 5)));
+        fb[i] = *(lds_bf16x8*)(ot_ + qb * 8192 + (kbase ^ (ks << 5)));
+      } else {               // dO^T and Q^T of half, MFMA chunk and d-block
+        const int u = i - 16, qb = u >> 3, mm = (u >> 2) & 1, db = u & 3;
+        fa[i] = frag_vt_x(ot_, vbase, 2 * qb + mm, db);
+        fb[i] = frag_vt_x(qt_, vbase, 2 * qb + mm, db);
       }
     };
-    auto softmax = [&](int qb) {
+    // lse and delta of the four queries of group g of half qb (one step ahead
+    // of their use)
+    f32x4 lv, dl;
+    auto ldv = [&](int qb, int g) {
+      const int qi = qb * 32 + 8 * g + 4 * (lane >> 5);
+      lv = *(const lds_f32x4*)((const lds_char*)vec + qi * 4);
+      dl = *(const lds_f32x4*)((const lds_char*)vec + 1024 + qi * 4);
+    };
+    // P and dS of scores 4g .. 4g+3 of half qb
+    auto smx = [&](int qb, int g) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int qi = qb * 32 + 8 * g + 4 * (lane >> 5);
-        const f32x4 lv = *(const lds_f32x4*)((const lds_char*)vec + qi * 4);
-        const f32x4 dl = *(const lds_f32x4*)((const lds_char*)vec + 1024 + qi * 4);
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * g + e;
+        float p = __builtin_amdgcn_exp2f(fmaf(sv[qb][r], a.sl2, -lv[e]));
+        if constexpr (MASK) {
+          const int qq = q0 + qb * 32 + 8 * g + 4 * (lane >> 5) + e;
+          p = (key > qq || qq >= a.T || qq >= key + a.W) ? 0.f : p;
+        }
+        sv[qb][r] = p;
+        dp[qb][r] = p * (dp[qb][r] - dl[e]);
+      }
+    };
+    bf16x8 pf[2], sf[2];     // bf16 P and dS of the half being multiplied
+    rd(0);
+    rd(1);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g + e;
-          float p = __builtin_amdgcn_exp2f(fmaf(sv[qb][r], a.sl2, -lv[e]));
-          if constexpr (MASK) {
-            const int qq = q0 + qi + e;
-            p = (key > qq || qq >= a.T || qq >= key + a.W) ? 0.f : p;
+    for (int i = 0; i < 32; ++i) {
+      if (i + 2 < 32) rd(i + 2);
+      if (i < 16) {
+        const int qb = i >> 3, ks = i & 7;
+        sv[qb] = MM::mma(fa[i], kf[ks], sv[qb]);   // S  (query x key)
+        dp[qb] = MM::mma(fb[i], vf[ks], dp[qb]);   // dP (query x key)
+        if (qb == 1) {
+          if ((ks & 1) == 0) ldv(0, ks >> 1);
+          else smx(0, ks >> 1);
+        }
+      } else {
+        const int u = i - 16, qb = u >> 3, mm = (u >> 2) & 1, db = u & 3;
+        if ((u & 7) == 0) {
+#pragma unroll
+          for (int m = 0; m < 2; ++m) {
+            pf[m] = frag_regs<bf16>(sv[qb], m * 8);
+            sf[m] = frag_regs<bf16>(dp[qb], m * 8);
           }
-          sv[qb][r] = p;
-          dp[qb][r] = p * (dp[qb][r] - dl[e]);      // dS
+        }
+        dv[db] = MM::mma(fa[i], pf[mm], dv[db]);     // dV^T += dO^T P
+        dk[db] = MM::mma(fb[i], sf[mm], dk[db]);     // dK^T += Q^T dS
+        if (qb == 0) {
+          if ((u & 1) == 0) ldv(1, u >> 1);
+          else smx(1, u >> 1);
         }
       }
-    };
-    auto dvdk = [&](int qb) {
-#pragma unroll
-      for (int mm = 0; mm < 2; ++mm) {
-        const bf16x8 pf = frag_regs<bf16>(sv[qb], mm * 8);
-        const bf16x8 sf = frag_regs<bf16>(dp[qb], mm * 8);
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          dv[db] = MM::mma(frag_vt_at(ot_, vo, 2 * qb + mm, db), pf, dv[db]);
-          dk[db] = MM::mma(frag_vt_at(qt_, vo, 2 * qb + mm, db), sf, dk[db]);
-        }
-      }
-    };
-    sdp(0);
-    sdp(1);
-    softmax(0);
-    dvdk(0);
-    softmax(1);
-    dvdk(1);
-    // schedule: S/dP(0) with its fragment reads; S/dP(1) (and its reads)
-    // between the VALU of softmax(0); dV/dK(0) and its transposed reads
-    // between the VALU of softmax(1); then dV/dK(1)
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-    }
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // VALU
-    }
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-    }
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
     };
     if (need_mask) body(std::true_type());
