@@ -1041,9 +1041,14 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_bf16_kernel(AttnArgs a) {
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
-  int ko[8], vo[8];
-  frag_k_offsets(ko, lane);
-  frag_vt_offsets(vo, lane);
+  // LDS offsets of the fragment reads from one base each (as in the dK/dV kernel)
+  int kbase = off(lane & 31, lane >> 5);
+  int vbase;
+  {
+    int vo[8];
+    frag_vt_offsets(vo, lane);
+    vbase = vo[0];
+  }
 
   const int last_key = min(a.T - 1, qt * 128 + 127);
   const int kt_lo = max(0, qt * 128 - a.W + 1) / KT;   // first tile inside the window
@@ -1054,6 +1059,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_bf16_kernel(AttnArgs a) {
     if (it + 1 < n) __builtin_amdgcn_s_waitcnt(0x0f70 | 8);
     else __builtin_amdgcn_s_waitcnt(0x0f70);
     __syncthreads();
+    asm volatile("" : "+v"(kbase), "+v"(vbase));   // keep the derived offsets in the loop
     if (it + 2 < n) issue_kv(smem + ((it + 2) % NSLOT) * SLOT, rs, (kt_lo + it + 2) * KT, ldb, koff, voff, wave, lane);
     const lds_char* kt_ = (const lds_char*)smem + (it % NSLOT) * SLOT;
     const lds_char* vt_ = kt_ + TILE;
@@ -1061,68 +1067,61 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_bf16_kernel(AttnArgs a) {
     if (k0 > qw0 + 31) continue;
     if (k0 + KT - 1 <= qw0 - a.W) continue;           // every key is before this wave's windows
     const bool need_mask = (k0 + KT - 1 > qw0) || (k0 + KT > a.T) || (k0 <= qw0 + 31 - a.W);
-    // Two 32-key halves, software-pipelined as in the dK/dV kernel:
-    // S/dP(0); S/dP(1) with dS(0); dQ(0) with dS(1); dQ(1).  Masked and
-    // unmasked tiles are separate copies (one scheduling region each).
+    // Two 32-key halves in 24 steps of two MFMAs: S^T/dP^T(0); S^T/dP^T(1)
+    // with dS(0); dQ(0) with dS(1); dQ(1).  As in the dK/dV kernel, each step
+    // issues the LDS reads of the step after next and ends with a scheduling
+    // fence.  Masked and unmasked tiles are separate copies.
     auto body = [&](auto maskc) {
       constexpr bool MASK = decltype(maskc)::value;
-      f32x16 sv[2], dp[2];
-      auto sdp = [&](int kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) { sv[kb][r] = 0.f; dp[kb][r] = 0.f; }
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          sv[kb] = MM::mma(*(lds_bf16x8*)(kt_ + kb * 8192 + ko[ks]), qf[ks], sv[kb]);   // S^T
-          dp[kb] = MM::mma(*(lds_bf16x8*)(vt_ + kb * 8192 + ko[ks]), df[ks], dp[kb]);   // dP^T
+      f32x16 sv[2] = {}, dp[2] = {};
+      bf16x8 fa[24], fb[24];
+      auto rd = [&](int i) {
+        if (i < 16) {        // K and V rows of half i/8, k-step i%8
+          const int kb = i >> 3, ks = i & 7;
+          fa[i] = *(lds_bf16x8*)(kt_ + kb * 8192 + (kbase ^ (ks << 5)));
+          fb[i] = *(lds_bf16x8*)(vt_ + kb * 8192 + (kbase ^ (ks << 5)));
+        } else {             // K^T of half, MFMA chunk, d-blocks d2 and d2+1
+          const int u = i - 16, kb = u >> 2, m2 = (u >> 1) & 1, d2 = 2 * (u & 1);
+          fa[i] = frag_vt_x(kt_, vbase, 2 * kb + m2, d2);
+          fb[i] = frag_vt_x(kt_, vbase, 2 * kb + m2, d2 + 1);
         }
       };
-      auto ds = [&](int kb) {
+      auto dsr = [&](int kb, int r) {   // dS^T of score r of half kb
+        float p = __builtin_amdgcn_exp2f(fmaf(sv[kb][r], a.sl2, -lse));
+        if constexpr (MASK) {
+          const int kk = k0 + kb * 32 + acc_row(r, lane);
+          p = (kk > q || kk >= a.T || kk <= q - a.W) ? 0.f : p;
+        }
+        sv[kb][r] = p * (dp[kb][r] - dlt);
+      };
+      bf16x8 sf[2];          // bf16 dS^T of the half being multiplied
+      rd(0);
+      rd(1);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float p = __builtin_amdgcn_exp2f(fmaf(sv[kb][r], a.sl2, -lse));
-          if constexpr (MASK) {
-            const int kk = k0 + kb * 32 + acc_row(r, lane);
-            p = (kk > q || kk >= a.T || kk <= q - a.W) ? 0.f : p;
+      for (int i = 0; i < 24; ++i) {
+        if (i + 2 < 24) rd(i + 2);
+        if (i < 16) {
+          const int kb = i >> 3, ks = i & 7;
+          sv[kb] = MM::mma(fa[i], qf[ks], sv[kb]);   // S^T
+          dp[kb] = MM::mma(fb[i], df[ks], dp[kb]);   // dP^T
+          if (kb == 1) {
+            dsr(0, 2 * ks);
+            dsr(0, 2 * ks + 1);
           }
-          sv[kb][r] = p * (dp[kb][r] - dlt);   // dS^T
+        } else {
+          const int u = i - 16, kb = u >> 2, m2 = (u >> 1) & 1, d2 = 2 * (u & 1);
+          if ((u & 3) == 0) {
+            sf[0] = frag_regs<bf16>(sv[kb], 0);
+            sf[1] = frag_regs<bf16>(sv[kb], 8);
+          }
+          acc[d2] = MM::mma(fa[i], sf[m2], acc[d2]);           // dQ^T += K^T dS^T
+          acc[d2 + 1] = MM::mma(fb[i], sf[m2], acc[d2 + 1]);
+          if (kb == 0) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dsr(1, 4 * u + e);
+          }
         }
-      };
-      auto dq = [&](int kb) {
-#pragma unroll
-        for (int m2 = 0; m2 < 2; ++m2) {
-          const int mm = 2 * kb + m2;
-          const bf16x8 sf = frag_regs<bf16>(sv[kb], m2 * 8);
-#pragma unroll
-          for (int db = 0; db < 4; ++db) acc[db] = MM::mma(frag_vt_at(kt_, vo, mm, db), sf, acc[db]);
-        }
-      };
-      sdp(0);
-      sdp(1);
-      ds(0);
-      dq(0);
-      ds(1);
-      dq(1);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // VALU
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     };
     if (need_mask) body(std::true_type());
