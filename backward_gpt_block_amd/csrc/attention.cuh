@@ -568,11 +568,14 @@ constexpr int SLOT = 2 * TILE;         // K + V
 constexpr int NSLOT = 3;
 constexpr int LDS = NSLOT * SLOT;      // 96 KiB
 
-// Chunk c of row r is stored at c ^ sw(r), sw(r) = 2 * (r & 7): the 8
-// consecutive rows an MFMA fragment read touches per LDS cycle land on 8
-// distinct chunks, and the 4 rows x 2 adjacent chunks a 16-lane transpose
-// read touches land on 8 distinct chunks.
-__device__ __forceinline__ int sw(int row) { return (row << 1) & 14; }
+// Chunk c (16 bytes) of row r (256 bytes) is stored at c ^ sw(r),
+// sw(r) = 2 (r & 3) + ((r >> 2) & 1).  With 32 four-byte banks a row covers
+// the banks twice, so what matters is the chunk modulo 8: the 8 consecutive
+// rows of one LDS cycle of a 16-byte fragment read get 8 distinct values of
+// sw mod 8, and the 4 rows x 2 adjacent chunks of a 16-lane transpose read
+// get 4 distinct pairs: both reads are free of bank conflicts.  (An earlier
+// sw = 2 (r & 7) gave the fragment reads only 4 distinct values mod 8.)
+__device__ __forceinline__ int sw(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
 __device__ __forceinline__ int off(int row, int chunk) { return row * 256 + ((chunk ^ sw(row)) << 4); }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
