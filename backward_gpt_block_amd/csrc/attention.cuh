@@ -569,13 +569,13 @@ constexpr int NSLOT = 3;
 constexpr int LDS = NSLOT * SLOT;      // 96 KiB
 
 // Chunk c (16 bytes) of row r (256 bytes) is stored at c ^ sw(r),
-// sw(r) = 2 (r & 3) + ((r >> 2) & 1).  With 32 four-byte banks a row covers
-// the banks twice, so what matters is the chunk modulo 8: the 8 consecutive
-// rows of one LDS cycle of a 16-byte fragment read get 8 distinct values of
-// sw mod 8, and the 4 rows x 2 adjacent chunks of a 16-lane transpose read
-// get 4 distinct pairs: both reads are free of bank conflicts.  (An earlier
-// sw = 2 (r & 7) gave the fragment reads only 4 distinct values mod 8.)
-__device__ __forceinline__ int sw(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+// sw(r) = 4 (r & 3) ^ (r & 2) ^ ((r >> 2) & 3), a function of r & 15.  A
+// 16-byte fragment read touches 8 (or 16) consecutive rows at one chunk per
+// LDS cycle and a 16-lane (32-lane) transpose read 4 consecutive rows x 2 (4)
+// adjacent chunks; with 32 banks (64 banks) of 4 bytes both land on distinct
+// banks, whichever of the two groupings the hardware uses.  Rows r and r + 8
+// differ by sw ^ 2, rows r and r + 16 not at all.
+__device__ __forceinline__ int sw(int row) { return ((row & 3) << 2) ^ (row & 2) ^ ((row >> 2) & 3); }
 __device__ __forceinline__ int off(int row, int chunk) { return row * 256 + ((chunk ^ sw(row)) << 4); }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -613,7 +613,7 @@ __device__ __forceinline__ void frag_k_offsets(int* o, int lane) {
 
 // Per-lane byte offsets of the V^T transpose reads, run (0, 1) and d-block db
 // (add mm*4096 for MFMA chunk mm: 16 rows of 256 bytes, the swizzle only
-// depends on row & 7).
+// depends on row & 15).
 __device__ __forceinline__ void frag_vt_offsets(int* o, int lane) {
   const int g = (lane >> 4) & 3, s = lane & 15;
 #pragma unroll
@@ -637,12 +637,13 @@ __device__ __forceinline__ bf16x8 frag_vt_at(const lds_char* tile, const int* vo
 }
 
 // frag_vt_at with the offsets rebuilt from one per-lane base (vbase = the
-// run-0, d-block-0 offset): the swizzle XOR and the d-block step touch bits
-// 6-7 only, so offset(run, db) = (vbase ^ (db << 6)) + 2048 * run.
+// run-0, d-block-0 offset): the d-block step is an XOR of bits 6-7, and the
+// 8 rows of run 1 add 2048 with chunk bit 1 flipped, so offset(0, db) =
+// vbase ^ (db << 6) and offset(1, db) = (vbase ^ 32 ^ (db << 6)) + 2048.
 __device__ __forceinline__ bf16x8 frag_vt_x(const lds_char* tile, int vbase, int mm, int db) {
-  const lds_char* p = tile + mm * 4096 + (vbase ^ (db << 6));
-  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
-  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 2048));
+  const lds_char* p = tile + mm * 4096;
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + (vbase ^ (db << 6))));
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 2048 + (vbase ^ 32 ^ (db << 6))));
   typedef short s16x8 __attribute__((ext_vector_type(8)));
   const s16x8 r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
   return __builtin_bit_cast(bf16x8, r);
