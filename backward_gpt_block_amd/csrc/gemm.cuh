@@ -212,7 +212,8 @@ __device__ __forceinline__ void st16_out(void* p, u32x4 v) {
 
 // 8 consecutive results of one row (fp32, already scaled) -> memory.
 template <typename TO, int EPI, bool NT = false>
-__device__ __forceinline__ void epi8(const GemmArgs& g, int split, int row, int col, float* f, float& mx) {
+__device__ __forceinline__ void epi8(const GemmArgs& g, int split, int row, int col, float* f, float& mx,
+                                     const u32x4* pre = nullptr) {
   if constexpr (EPI == EPI_F32 || EPI == EPI_F32_ADD) {
     float* p = static_cast<float*>(g.out) + (EPI == EPI_F32 ? (long)split * g.M * g.ldo : 0L) + (long)row * g.ldo + col;
     u32x4 a = Chunk<float>::pack(f), b = Chunk<float>::pack(f + 4);
@@ -282,7 +283,7 @@ __device__ __forceinline__ void epi8(const GemmArgs& g, int split, int row, int 
       const TO* x = static_cast<const TO*>(g.aux) + (long)row * g.ldaux + col;
       float xv[8];
 #pragma unroll
-      for (int h = 0; h < 8 / EL; ++h) Chunk<TO>::unpack(ld16(x + h * EL), xv + h * EL);
+      for (int h = 0; h < 8 / EL; ++h) Chunk<TO>::unpack(pre ? pre[h] : ld16(x + h * EL), xv + h * EL);
       // ReLU^2 derivative 2 max(u,0) recovered from the stored a = max(u,0)^2
 #pragma unroll
       for (int e = 0; e < 8; ++e) f[e] = (EPI == EPI_RESID) ? xv[e] + f[e] : f[e] * 2.f * __builtin_amdgcn_sqrtf(xv[e]);
@@ -301,7 +302,7 @@ __device__ __forceinline__ void epi8(const GemmArgs& g, int split, int row, int 
       float xv[8], rv[8];
 #pragma unroll
       for (int h = 0; h < 8 / EL; ++h) {
-        Chunk<TO>::unpack(ld16(x + h * EL), xv + h * EL);
+        Chunk<TO>::unpack(pre ? pre[h] : ld16(x + h * EL), xv + h * EL);
         Chunk<TO>::unpack(Chunk<TO>::pack(f + h * EL), rv + h * EL);
       }
       float d = 0.f;
@@ -602,9 +603,35 @@ __device__ __forceinline__ void head_lse8(const GemmArgs& g, int row, int col, c
   if (ok && (col & 127) == 0) g.lse_part[(long)row * g.nseg + (col >> 7)] = make_float2(m, l);
 }
 
+// Epilogues that read a bf16 operand of their own (residual, stored
+// activation, o for delta) take it from registers loaded before the
+// epilogue starts: pre[pass][it] is the 16-byte chunk of the row segment
+// that iteration it of pass pass handles (zero outside the matrix).
+template <typename TO, int EPI>
+struct EpiAux {
+  static constexpr bool on = (EPI == EPI_RESID || EPI == EPI_DRELU2 || EPI == EPI_DELTA) && sizeof(TO) == 2;
+};
+template <typename TO, int EPI>
+__device__ __forceinline__ void epi_prefetch(const GemmArgs& g, u32x4 (&pre)[2][8], int m0, int n0, int wave,
+                                             int lane) {
+  if constexpr (EpiAux<TO, EPI>::on) {
+    const int grp = wave >> 2, q = wave & 3;
+    const int rbase = m0 + (q >> 1) * 128 + grp * 64, cbase = n0 + (q & 1) * 128;
+    const TO* aux = static_cast<const TO*>(g.aux);
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass)
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int qq = it * 64 + lane;
+        const int grow = rbase + pass * 32 + (qq >> 4), gcol = cbase + (qq & 15) * 8;
+        pre[pass][it] = (grow < g.M && gcol < g.N) ? ld16(aux + (long)grow * g.ldaux + gcol) : u32x4{0u, 0u, 0u, 0u};
+      }
+  }
+}
+
 template <typename TO, int EPI>
 __device__ __forceinline__ void epilogue_pp(const GemmArgs& g, f32x16 (&acc)[2][4], char* smem, int m0, int n0,
-                                            int split, int wave, int lane) {
+                                            int split, int wave, int lane, const u32x4 (&pre)[2][8]) {
   const int grp = wave >> 2, q = wave & 3;
   float alpha = g.alpha;
   if (g.amax_a) {
@@ -625,7 +652,7 @@ __device__ __forceinline__ void epilogue_pp(const GemmArgs& g, f32x16 (&acc)[2][
         const int row = acc_row(r, lane), col = j * 32 + (lane & 31);
         *reinterpret_cast<float*>(wreg + epi_off(row, col >> 2) + (col & 3) * 4) = acc[pass][j][r] * alpha;
       }
-#pragma unroll 4
+#pragma unroll
     for (int it = 0; it < 8; ++it) {
       const int qq = it * 64 + lane;
       const int row = qq >> 4, cg = qq & 15;
@@ -634,7 +661,8 @@ __device__ __forceinline__ void epilogue_pp(const GemmArgs& g, f32x16 (&acc)[2][
       Chunk<float>::unpack(ld16(wreg + epi_off(row, 2 * cg + 1)), f + 4);
       const int grow = rbase + pass * 32 + row, gcol = cbase + cg * 8;
       if constexpr (EPI == EPI_LSE) head_lse8(g, grow, gcol, f);
-      else if (grow < g.M && gcol < g.N) epi8<TO, EPI, true>(g, split, grow, gcol, f, mx);
+      else if (grow < g.M && gcol < g.N)
+        epi8<TO, EPI, true>(g, split, grow, gcol, f, mx, EpiAux<TO, EPI>::on ? &pre[pass][it] : nullptr);
     }
   }
   if (g.amax_out) amax_publish<TO>(g.amax_out, mx);
@@ -685,6 +713,7 @@ __device__ __forceinline__ void gemm_pp_body(const GemmArgs& g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   typename MM::frag fa[HS][2], fb[HS][4];
+  u32x4 pre[2][8];   // the epilogue's own operand, loaded while the last MFMAs run
   auto read = [&](int kt, int h) {
     const char* cur = smem + (kt & 1) * G::SLAB;
 #pragma unroll
@@ -734,6 +763,7 @@ __device__ __forceinline__ void gemm_pp_body(const GemmArgs& g) {
         __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): stage kt+1's A rows have landed
         wg_barrier();
       }
+      epi_prefetch<TO, EPI>(g, pre, m0, n0, wave, lane);   // in flight while grp 1 finishes
       wg_barrier();   // grp 1 runs the last half-step's MFMAs
     } else {
       // the slot is refilled after the stage's last barrier, so each read
@@ -765,14 +795,16 @@ __device__ __forceinline__ void gemm_pp_body(const GemmArgs& g) {
         tail(kt);
       }
       mfma();
+      epi_prefetch<TO, EPI>(g, pre, m0, n0, wave, lane);
       wg_barrier();
     }
+  } else {
+    epi_prefetch<TO, EPI>(g, pre, m0, n0, wave, lane);
   }
-  // the past-the-end loads write zeros into LDS: let them land before the
-  // epilogue reuses it
-  __builtin_amdgcn_s_waitcnt(0x0f70);
+  // every staging load (the past-the-end one included) was waited for inside
+  // the loops; the barrier frees the LDS for the epilogue
   wg_barrier();
-  epilogue_pp<TO, EPI>(g, acc, smem, m0, n0, split, wave, lane);
+  epilogue_pp<TO, EPI>(g, acc, smem, m0, n0, split, wave, lane, pre);
 }
 
 }  // namespace blk
