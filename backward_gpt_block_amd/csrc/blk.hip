@@ -322,6 +322,8 @@ void wgrad(GemmKernel kern, GemmKernel kern_acc, GemmKernel kp, GemmKernel kp_ac
 }
 
 unsigned row_blocks(long rows) { return (unsigned)((rows + 3) / 4); }
+// row kernels that publish an absolute maximum: a capped grid walking the rows
+unsigned amax_row_blocks(long rows) { return std::min(row_blocks(rows), AMAX_BLOCKS); }
 
 // ---------------------------------------------------------------- forward
 template <typename T> AttnArgs attn_args(const blk_cfg& c) {
@@ -483,7 +485,10 @@ void quantize(const bf16* x, long rows, long cols, unsigned* am, uint8_t* q, uin
   const long n = rows * cols;
   Timed t("fp8_quantize", st);
   if (amax) hipLaunchKernelGGL(amax_kernel, dim3(elt_grid(n)), dim3(256), 0, st, x, n, am);
-  if (qt)   // transposed codes, and the row-major ones in the same pass
+  if (qt && cols % 128 == 0)   // transposed codes, and the row-major ones in the same pass
+    hipLaunchKernelGGL(quant_trans128_kernel, dim3((unsigned)(cols / 128), (unsigned)((ldt + 127) / 128)), dim3(256),
+                       0, st, x, (int)rows, (int)cols, (const unsigned*)am, qt, (int)ldt, q);
+  else if (qt)
     hipLaunchKernelGGL(quant_trans_kernel, dim3((unsigned)(cols / 64), (unsigned)(ldt / 64)), dim3(256), 0, st, x,
                        (int)rows, (int)cols, (const unsigned*)am, qt, (int)ldt, q);
   else if (q)
@@ -542,8 +547,8 @@ int fwd_fp8(const blk_cfg& c, const bf16* x, const bf16* wqkv, const bf16* wo, c
   }
   {
     Timed t("rmsnorm_fwd", st);
-    hipLaunchKernelGGL(rmsnorm_fwd_kernel<bf16>, dim3(row_blocks(N)), dim3(256), 0, st, x, s.h1, s.r1, N, C, c.eps,
-                       am + AM_H1);
+    hipLaunchKernelGGL(rmsnorm_fwd_kernel<bf16>, dim3(amax_row_blocks(N)), dim3(256), 0, st, x, s.h1, s.r1, N, C,
+                       c.eps, am + AM_H1);
   }
   quantize(wqkv, qkv_width(c), C, am + AM_WQKV, f.wqkv, nullptr, 0, true, st);
   quantize(wo, C, C, am + AM_WO, f.wo, nullptr, 0, true, st);
@@ -570,8 +575,8 @@ int fwd_fp8(const blk_cfg& c, const bf16* x, const bf16* wqkv, const bf16* wo, c
   }
   {
     Timed t("rmsnorm_fwd", st);
-    hipLaunchKernelGGL(rmsnorm_fwd_kernel<bf16>, dim3(row_blocks(N)), dim3(256), 0, st, (const bf16*)y, s.h2, s.r2, N,
-                       C, c.eps, am + AM_H2);
+    hipLaunchKernelGGL(rmsnorm_fwd_kernel<bf16>, dim3(amax_row_blocks(N)), dim3(256), 0, st, (const bf16*)y, s.h2,
+                       s.r2, N, C, c.eps, am + AM_H2);
   }
   quantize(s.h2, N, C, am + AM_H2, f.h2, s.h2_8t, Np, false, st);   // amax from rmsnorm_fwd
   {
@@ -623,7 +628,7 @@ int bwd_fp8(const blk_cfg& c, const bf16* dy, const bf16* wqkv, const bf16* wo, 
          N, acc, w.part, st);
   {
     Timed t("rmsnorm_bwd", st);
-    hipLaunchKernelGGL(rmsnorm_bwd_kernel<bf16>, dim3(row_blocks(N)), dim3(256), 0, st, dy, (const bf16*)w.dh,
+    hipLaunchKernelGGL(rmsnorm_bwd_kernel<bf16>, dim3(amax_row_blocks(N)), dim3(256), 0, st, dy, (const bf16*)w.dh,
                        (const bf16*)s.h2, (const float*)s.r2, w.dy1, N, C, am + AM_DY1);
   }
   quantize(w.dy1, N, C, am + AM_DY1, w.g8, w.g8t, Np, false, st);   // amax from rmsnorm_bwd

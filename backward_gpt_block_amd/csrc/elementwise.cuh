@@ -9,6 +9,25 @@ namespace blk {
 
 constexpr int MAXCH = 8;   // 16-byte chunks per lane a row kernel keeps in registers
 
+// The row kernels' absolute maximum (fp8 mode): reduced over the workgroup's
+// four waves, then one atomic per workgroup.  A row kernel launched for an
+// fp8 tensor walks its rows with a grid stride over at most amax_blocks
+// workgroups, so a tensor costs a few hundred atomics on its one word instead
+// of one per row.  Every thread of the workgroup must call it.
+constexpr unsigned AMAX_BLOCKS = 1024;
+template <typename T>
+__device__ __forceinline__ void amax_publish_wg(unsigned* amax, float m) {
+  __shared__ float wm[4];
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = to_f32(from_f32<T>(fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]))));
+    const unsigned cur = __hip_atomic_load(amax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (__float_as_uint(m) > cur) atomicMax(amax, __float_as_uint(m));
+  }
+}
+
 // h = x * r, r = (mean(x^2) + eps)^-1/2 per row of C elements.
 // Parameter-free RMSNorm (flicky.cc nanochat page, section on the model,
 // and its glossary entry for RMSNorm, without the gain).
@@ -18,9 +37,11 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const T* __restrict__ 
                                                           unsigned* __restrict__ amax = nullptr) {
   constexpr int EL = Chunk<T>::N;
   const int lane = threadIdx.x & 63;
-  const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= N) return;
   const int nch = C / EL;
+  float mx = 0.f;
+  // one row per wave; the grid covers all rows (one pass) unless it was
+  // capped for an fp8 tensor
+  for (long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6); row < N; row += (long)gridDim.x * 4) {
   const T* xr = x + row * C;
   u32x4 c[MAXCH];
   float ss = 0.f;
@@ -38,7 +59,6 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const T* __restrict__ 
   ss = wave_sum(ss);
   const float rr = 1.f / sqrtf(ss / (float)C + eps);
   if (lane == 0 && r) r[row] = rr;
-  float mx = 0.f;
 #pragma unroll
   for (int i = 0; i < MAXCH; ++i) {
     int ch = lane + i * 64;
@@ -53,7 +73,8 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const T* __restrict__ 
       st16(h + row * C + ch * EL, Chunk<T>::pack(f));
     }
   }
-  if (amax) amax_publish<T>(amax, mx);   // fp8 mode: the tensor's absolute maximum
+  }
+  if (amax) amax_publish_wg<T>(amax, mx);   // fp8 mode: the tensor's absolute maximum
 }
 
 // out = resid + r * (dh - hn * mean(dh * hn)): RMSNorm backward (hn is the
@@ -65,9 +86,9 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const T* __restrict__ 
                                                           unsigned* __restrict__ amax = nullptr) {
   constexpr int EL = Chunk<T>::N;
   const int lane = threadIdx.x & 63;
-  const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= N) return;
   const int nch = C / EL;
+  float mx = 0.f;
+  for (long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6); row < N; row += (long)gridDim.x * 4) {
   u32x4 cd[MAXCH], ch_[MAXCH];
   float dot = 0.f;
 #pragma unroll
@@ -86,7 +107,6 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const T* __restrict__ 
   dot = wave_sum(dot);
   const float mean = dot / (float)C;
   const float rr = r[row];
-  float mx = 0.f;
 #pragma unroll
   for (int i = 0; i < MAXCH; ++i) {
     int ch = lane + i * 64;
@@ -107,7 +127,8 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const T* __restrict__ 
       st16(out + row * C + ch * EL, Chunk<T>::pack(g));
     }
   }
-  if (amax) amax_publish<T>(amax, mx);   // fp8 mode: the tensor's absolute maximum
+  }
+  if (amax) amax_publish_wg<T>(amax, mx);   // fp8 mode: the tensor's absolute maximum
 }
 
 // cs[t][i] = (cos, sin) of t * base^(-2i/D), i < D/2, computed in double

@@ -109,4 +109,64 @@ __global__ __launch_bounds__(256) void quant_trans_kernel(const bf16* __restrict
   st16(qT + (long)(c0 + wr) * ldT + r0 + wq * 16, v);
 }
 
+// quant_trans_kernel on 128 x 128 tiles (cols % 128 == 0): each thread has
+// 8 row chunks of 16 bytes in flight (rows 8*ty .. 8*ty+7 of its 8-column
+// group), packs the 8 codes of one column into one 8-byte LDS store, and both
+// outputs are written in whole 128-byte lines.  qT columns past ldT are not
+// written (ldT is a multiple of 64).
+__global__ __launch_bounds__(256) void quant_trans128_kernel(const bf16* __restrict__ x, int rows, int cols,
+                                                             const unsigned* __restrict__ amax,
+                                                             uint8_t* __restrict__ qT, int ldT,
+                                                             uint8_t* __restrict__ q) {
+  constexpr int P = 144;                      // LDS row pitch (bytes), a multiple of 16
+  __shared__ __attribute__((aligned(16))) uint8_t t[128 * P];
+  const float inv = quant_inv(amax_value(amax));
+  const int r0 = blockIdx.y * 128, c0 = blockIdx.x * 128;
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;   // 16 chunks of 8 columns x 16 groups of 8 rows
+  u32x4 raw[8];
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int r = r0 + 8 * ty + p;
+    raw[p] = r < rows ? ld16(x + (long)r * cols + c0 + tx * 8) : u32x4{0u, 0u, 0u, 0u};
+  }
+  uint32_t col8[8][2];                        // codes of column tx*8 + e, rows 8*ty .. 8*ty+7
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    float f[8];
+    Chunk<bf16>::unpack(raw[p], f);
+    uint32_t two[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) two[e] = e4m3x2(f[2 * e] * inv, f[2 * e + 1] * inv);
+    const int r = r0 + 8 * ty + p;
+    if (q && r < rows) {
+      u32x2 row8;
+      row8[0] = two[0] | (two[1] << 16);
+      row8[1] = two[2] | (two[3] << 16);
+      st8(q + (long)r * cols + c0 + tx * 8, row8);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t b = (two[e >> 1] >> (8 * (e & 1))) & 0xffu;
+      const int w = p >> 2, sh = 8 * (p & 3);
+      col8[e][w] = (p & 3) == 0 ? b : (col8[e][w] | (b << sh));
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    u32x2 v;
+    v[0] = col8[e][0];
+    v[1] = col8[e][1];
+    *reinterpret_cast<u32x2*>(t + (tx * 8 + e) * P + 8 * ty) = v;
+  }
+  __syncthreads();
+  // row c0 + wr of qT gets bytes r0 + 64 h .. r0 + 64 h + 63: 4 x 16 bytes
+  const int wr = threadIdx.x >> 1, h = threadIdx.x & 1;
+  if (r0 + 64 * h < ldT) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      st16(qT + (long)(c0 + wr) * ldT + r0 + 64 * h + 16 * w,
+           *reinterpret_cast<const u32x4*>(t + wr * P + 64 * h + 16 * w));
+  }
+}
+
 }  // namespace blk
