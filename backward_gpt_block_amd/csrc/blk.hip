@@ -249,7 +249,7 @@ void need_lds(const void* kern, int bytes) {
 // threads: 256 for the four-wave GEMM body, 512 for the eight-wave one
 template <typename TI>
 void gemm(void (*kern)(GemmArgs), const char* name, GemmArgs g, int splits, hipStream_t st, int threads = 256) {
-  const int LDS = threads == 512 ? GemmTile<TI>::PP_LDS : GemmTile<TI>::LDS;   // eight-wave body: 160 KiB
+  constexpr int LDS = GemmTile<TI>::LDS;
   need_lds(reinterpret_cast<const void*>(kern), LDS);
   g.tiles_m = (g.M + 255) / 256;
   g.tiles_n = (g.N + 255) / 256;

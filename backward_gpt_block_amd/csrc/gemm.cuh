@@ -85,8 +85,6 @@ template <typename TI> struct GemmTile {
   static constexpr int ROWB = 128;               // LDS bytes per tile row
   static constexpr int SLAB = (BM + BN) * ROWB;  // one stage, A then B
   static constexpr int LDS = 2 * SLAB;           // 128 KiB
-  // eight-wave body: A rows in a 3-slot ring, B rows in a 2-slot ring
-  static constexpr int PP_LDS = 3 * BM * ROWB + 2 * BN * ROWB;   // 160 KiB
 };
 
 // buffer resources (i32x4, make_rsrc, raw_buffer_load_lds): common.cuh
@@ -700,13 +698,8 @@ __device__ __forceinline__ void gemm_pp_body(const GemmArgs& g) {
     if (grp == 0) st.init(g.A, g.lda, g.M, m0, q, lane);
     else st.init(g.B, g.ldb, g.N, n0, q, lane);
   }
-  // LDS: the A rows of stage kt in slot kt % 3 (issued two stages ahead, so
-  // their load latency is hidden behind two k-steps), the B rows in slot
-  // kt % 2 after them (one stage ahead)
-  auto aslot = [&](int kt) { return smem + (kt % 3) * (G::BM * G::ROWB); };
-  auto bslot = [&](int kt) { return smem + 3 * (G::BM * G::ROWB) + (kt & 1) * (G::BN * G::ROWB); };
   auto issue = [&](int kt) {
-    char* sub = grp == 0 ? aslot(kt) : bslot(kt);
+    char* sub = smem + (kt & 1) * G::SLAB + grp * (G::BM * G::ROWB);
     if constexpr (TR) st.issue(sub, kt * G::BK, kt < nk, q);
     else st.issue(sub, (kbeg + kt * G::BK) * (int)sizeof(TI), kt < nk, q);
   };
@@ -722,20 +715,19 @@ __device__ __forceinline__ void gemm_pp_body(const GemmArgs& g) {
   typename MM::frag fa[HS][2], fb[HS][4];
   u32x4 pre[2][8];   // the epilogue's own operand, loaded while the last MFMAs run
   auto read = [&](int kt, int h) {
-    const char* cur = aslot(kt);
-    const char* curb = bslot(kt);
+    const char* cur = smem + (kt & 1) * G::SLAB;
 #pragma unroll
     for (int s = 0; s < HS; ++s) {
       if constexpr (TR) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) fa[s][i] = frag_t(cur, arow + 32 * i, h * HS + s, lane);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) fb[s][j] = frag_t(curb, brow + 32 * j, h * HS + s, lane);
+        for (int j = 0; j < 4; ++j) fb[s][j] = frag_t(cur + G::BM * G::ROWB, brow + 32 * j, h * HS + s, lane);
       } else {
 #pragma unroll
         for (int i = 0; i < 2; ++i) fa[s][i] = load_frag<TI>(cur, arow + 32 * i, h * HS + s, lane);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) fb[s][j] = load_frag<TI>(curb, brow + 32 * j, h * HS + s, lane);
+        for (int j = 0; j < 4; ++j) fb[s][j] = load_frag<TI>(cur + G::BM * G::ROWB, brow + 32 * j, h * HS + s, lane);
       }
     }
   };
@@ -748,22 +740,16 @@ __device__ __forceinline__ void gemm_pp_body(const GemmArgs& g) {
         for (int j = 0; j < 4; ++j) acc[i][j] = MM::mma(fa[s][i], fb[s][j], acc[i][j]);
   };
 
-  // Stages past the end (kt + 1 == nk for B, kt + 1 and kt + 2 for A) are
-  // issued with out-of-range offsets: they write zeros into free slots and
-  // keep the loop free of branches
+  // A stage past the end (kt + 1 == nk) is issued with out-of-range offsets:
+  // it writes zeros into the free slot and keeps the loop free of branches
   // that would split the instruction schedule.
   if (nk > 0) {
     issue(0);
-    if (grp == 0) {
-      issue(1);
-      __builtin_amdgcn_s_waitcnt(0x0f70 | 8);   // vmcnt(8): stage 0 landed, stage 1 may stay in flight
-    } else {
-      __builtin_amdgcn_s_waitcnt(0x0f70);       // vmcnt(0)
-    }
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
     wg_barrier();
     if (grp == 0) {
       for (int kt = 0; kt < nk; ++kt) {
-        issue(kt + 2);
+        issue(kt + 1);
         read(kt, 0);
         __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);    // the 8 loads, then the LDS reads
         __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
@@ -774,12 +760,9 @@ __device__ __forceinline__ void gemm_pp_body(const GemmArgs& g) {
         wg_barrier();
         mfma();
         __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_waitcnt(0x0f70 | 8);   // vmcnt(8): stage kt+1's A rows have landed
+        __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): stage kt+1's A rows have landed
         wg_barrier();
       }
-      // the two stages issued past the end write zeros into LDS: let them
-      // land before the epilogue reuses it
-      __builtin_amdgcn_s_waitcnt(0x0f70);
       epi_prefetch<TO, EPI>(g, pre, m0, n0, wave, lane);   // in flight while grp 1 finishes
       wg_barrier();   // grp 1 runs the last half-step's MFMAs
     } else {
