@@ -148,6 +148,8 @@ def library() -> ctypes.CDLL:
         lib.head_loss_bwd.restype = i32
         lib.block_fp8_quantize.argtypes = [vp, sz, vp, vp, vp]
         lib.block_fp8_quantize.restype = i32
+        lib.block_fp8_quantize_2d.argtypes = [vp, ctypes.c_int64, ctypes.c_int64, vp, vp, ctypes.c_int64, vp, vp]
+        lib.block_fp8_quantize_2d.restype = i32
         lib.block_timing_enable.argtypes = [i32]
         lib.block_timing_enable.restype = None
         lib.block_timing_read.argtypes = [i32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_double),
@@ -257,6 +259,13 @@ def head_loss_bwd(cfg: HeadConfig, x, w_lm, targets, lse, dloss: float, dx, dw_l
 def block_fp8_quantize(x, n: int, codes, amax, *, stream=None, raise_on_error=True) -> int:
     code = library().block_fp8_quantize(_ptr(x), int(n), _ptr(codes), _ptr(amax), _stream(stream))
     return _check(code, "block_fp8_quantize", raise_on_error)
+
+
+def block_fp8_quantize_2d(x, rows: int, cols: int, codes, codes_t, ldt: int, amax, *, stream=None,
+                          raise_on_error=True) -> int:
+    code = library().block_fp8_quantize_2d(_ptr(x), int(rows), int(cols), _ptr(codes), _ptr(codes_t), int(ldt),
+                                           _ptr(amax), _stream(stream))
+    return _check(code, "block_fp8_quantize_2d", raise_on_error)
 
 
 def block_timing_enable(on: bool) -> None:

@@ -970,6 +970,21 @@ int block_fp8_quantize(const void* x, size_t n, void* codes, uint32_t* amax, voi
   return launch_status();
 }
 
+int block_fp8_quantize_2d(const void* x, int64_t rows, int64_t cols, void* codes, void* codes_t, int64_t ldt,
+                          uint32_t* amax, void* stream) {
+  if (!x || !codes_t || !amax) return BLK_EINVAL;
+  if (rows < 1 || rows >= (1LL << 31) || cols < 64 || cols % 64 != 0 || cols >= (1LL << 31)) return BLK_EINVAL;
+  if (ldt < rows || ldt % 64 != 0 || ldt >= (1LL << 31)) return BLK_EINVAL;
+  if (!aligned(x) || !aligned(codes_t) || (codes && !aligned(codes)) || (reinterpret_cast<uintptr_t>(amax) & 3))
+    return BLK_EALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipGetLastError();
+  hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, st, (unsigned*)amax, 1);
+  quantize(static_cast<const bf16*>(x), rows, cols, (unsigned*)amax, static_cast<uint8_t*>(codes),
+           static_cast<uint8_t*>(codes_t), ldt, true, st);
+  return launch_status();
+}
+
 void block_timing_enable(int on) {
   std::lock_guard<std::mutex> l(g_tmu);
   g_timing = on != 0;

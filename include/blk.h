@@ -215,6 +215,21 @@ int decode_step(const blk_dcfg* cfg, const void* x,
  * device pointers, 16-byte aligned; codes holds n bytes. */
 int block_fp8_quantize(const void* x, size_t n, void* codes, uint32_t* amax, void* stream);
 
+/* The same quantiser on a rows x cols bf16 matrix x (row-major, leading
+ * dimension cols), in the form the fp8 mode applies it to the operands of
+ * its weight-gradient GEMMs: amax = max |x| written to *amax as float bits;
+ * codes[r][c] = E4M3(x[r][c] * 448/amax) when codes is not NULL; and the
+ * transposed copy codes_t[c][r] with leading dimension ldt (>= rows, a
+ * multiple of 64), whose padding columns rows .. ldt-1 are written as 0.
+ * (OCP 8-bit E4M3, per-tensor scale from the current amax: fp8 training as
+ * the flicky.cc nanochat page's repository map and the 36kr/CSDN
+ * leaderboard notes name it.)  rows in [1, 2^31), cols a positive multiple
+ * of 64 below 2^31; device pointers 16-byte aligned (amax 4-byte aligned).
+ * BLK_EINVAL for a NULL x, codes_t or amax, or a bad size; BLK_EALIGN for a
+ * misaligned pointer. */
+int block_fp8_quantize_2d(const void* x, int64_t rows, int64_t cols, void* codes, void* codes_t, int64_t ldt,
+                          uint32_t* amax, void* stream);
+
 /* Measurement hooks (for benchmarks; not needed to compute anything).
  * block_timing_enable(1) starts recording, for every kernel launch site of
  * the calls above, a pair of hipEvents around the launch on the call's

@@ -150,6 +150,25 @@ def test_decode_sizes_and_argument_errors(lib):
     assert _dec(c, scratch_bytes=need - 1) == bl.binding.BLK_ENOSPC
 
 
+def test_fp8_quantize_2d_argument_errors(lib):
+    q = bl.block_fp8_quantize_2d
+    E = bl.binding
+    args = dict(x=A, rows=300, cols=384, codes=A + 0x100, codes_t=A + 0x200, ldt=320, amax=A + 0x300)
+
+    def call(**kw):
+        a = dict(args)
+        a.update(kw)
+        return q(a["x"], a["rows"], a["cols"], a["codes"], a["codes_t"], a["ldt"], a["amax"], raise_on_error=False,
+                 stream=0)
+
+    for bad in (dict(x=None), dict(codes_t=None), dict(amax=None), dict(rows=0), dict(cols=100), dict(cols=0),
+                dict(ldt=299), dict(ldt=330), dict(rows=1 << 31)):
+        assert call(**bad) == E.BLK_EINVAL, bad
+    assert call(x=MIS) == E.BLK_EALIGN
+    assert call(codes=MIS) == E.BLK_EALIGN
+    assert call(amax=A + 0x302) == E.BLK_EALIGN
+
+
 def test_strerror(lib):
     for code in range(6):
         assert isinstance(bl.block_strerror(code), str) and bl.block_strerror(code)

@@ -109,3 +109,36 @@ def test_d26_fp8_full_size_sampled():
 
 def test_fp8_block_gqa():
     _fp8_parity(BlockShape(B=2, T=300, C=512, H=4, F=2048, dtype="bf16", gemm="fp8", n_kv_head=1))
+
+
+@pytest.mark.parametrize("rows,cols,ldt", [
+    (77, 256, 128),      # ragged rows, padding columns 77..127 of the transposed copy
+    (300, 384, 320),     # a partial last 128-row tile (its second half past ldt is not written)
+    (1000, 1664, 1024),  # d26 width
+    (130, 192, 192),     # width not a multiple of 128: the 64 x 64 kernel
+])
+def test_quantizer_2d_transposed_bit_exact(rows, cols, ldt):
+    # row-major and transposed codes of a matrix, as the weight-gradient
+    # GEMMs of the fp8 mode read them, against the oracle's quantiser
+    import torch
+    import backward_gpt_block_amd as bl
+    from oracle import fp8
+    note(f"fp8 2-D quantizer rows={rows} cols={cols} ldt={ldt}")
+    rng = np.random.default_rng(rows + cols)
+    x = round_to(rng.standard_normal((rows, cols)) * 3.0, "bf16")
+    x[0, :4] = [0.0, -0.0, 448.0, -1e-30]
+    x = round_to(x, "bf16")
+    xd = to_dev(x, "bf16")
+    codes = torch.full((rows, cols), 0x55, dtype=torch.uint8, device="cuda:0")
+    codes_t = torch.full((cols, ldt), 0x55, dtype=torch.uint8, device="cuda:0")
+    amax = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    bl.block_fp8_quantize_2d(xd, rows, cols, codes, codes_t, ldt, amax)
+    torch.cuda.synchronize()
+    want, _ = fp8.quantize_tensor(x)
+    want = want.reshape(rows, cols)
+    got, got_t = codes.cpu().numpy(), codes_t.cpu().numpy()
+    assert np.array_equal(got, want), f"{np.count_nonzero(got != want)} row-major codes differ"
+    assert np.array_equal(got_t[:, :rows], want.T), f"{np.count_nonzero(got_t[:, :rows] != want.T)} transposed codes differ"
+    assert not np.any(got_t[:, rows:]), "padding columns of the transposed copy are not zero"
+    amax_got = np.array([amax.cpu().item()], dtype=np.int32).view(np.float32)[0]
+    assert amax_got == np.float32(np.max(np.abs(x)))
