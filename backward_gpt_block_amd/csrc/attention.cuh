@@ -1,18 +1,25 @@
 // Causal multi-head attention, head size 128, for gfx950 (flash-style: the
-// T x T score matrix never reaches HBM).
+// T x T score matrix never reaches HBM), with an optional sliding window and
+// grouped key/value heads.
 //
-// Forward: each wave owns 32 queries and walks key tiles.  It computes the
-// TRANSPOSED score block S^T = K Q^T with MFMA 32x32, so the lane that holds
-// column l%32 of S^T holds every score of one query: the running maximum and
-// denominator of the online softmax are per-lane scalars (plus one exchange
-// with lane l^32), and the rescale of the output accumulator O^T (d x query)
-// is a per-lane multiply.  P^T feeds O^T += V^T P^T straight from registers:
-// the MFMA k-slots of P^T are the keys this lane already holds, and V^T is
-// read from LDS with the same key order.
+// Forward: each wave owns 32 queries (float32) or two blocks of 32 (bf16)
+// and walks key tiles.  It computes the TRANSPOSED score block S^T = K Q^T
+// with MFMA 32x32, so the lane that holds column l%32 of S^T holds every
+// score of one query: the running maximum and denominator of the online
+// softmax are per-lane scalars (plus one exchange with lane l^32), and the
+// rescale of the output accumulator O^T (d x query) is a per-lane multiply.
+// P^T feeds O^T += V^T P^T straight from registers: the MFMA k-slots of P^T
+// are the keys this lane already holds, and V^T is read from LDS with the
+// same key order.
 //
 // Backward (no atomics, deterministic): a pass over key tiles per query tile
 // for dQ, and a pass over query tiles per key tile for dK and dV, both
-// recomputing P from the saved log-sum-exp.
+// recomputing P from the saved log-sum-exp.  The bf16 backward loops are
+// written as explicit steps of two MFMAs whose LDS reads are issued two
+// steps ahead, with a scheduling fence per step.
+//
+// This header is compiled only in attn.hip, with MFMA results in vector
+// registers (the softmax reads them after every MFMA chain).
 //
 // (Causal multi-head attention with 128-dim heads: 7minutos.es nanochat
 // article, section "Modelo, escalado y objetivo de speedrun"; QK-norm and
@@ -598,12 +605,6 @@ __device__ __forceinline__ void issue_kv(char* slot, i32x4 rs, int k0, long ldb,
   }
 }
 
-// A fragment (rows = keys kb*32 + l%32, k-substep ks over d) of a row tile.
-__device__ __forceinline__ bf16x8 frag_k(const char* tile, int kb, int ks, int lane) {
-  const int row = kb * 32 + (lane & 31);
-  return __builtin_bit_cast(bf16x8, ld16(tile + off(row, 2 * ks + (lane >> 5))));
-}
-
 // Per-lane byte offsets of the row-tile fragment reads, k-substep ks (add
 // kb*8192 for key block kb): row l%32, chunk 2ks + l/32, swizzled.
 __device__ __forceinline__ void frag_k_offsets(int* o, int lane) {
@@ -628,6 +629,10 @@ __device__ __forceinline__ void frag_vt_offsets(int* o, int lane) {
 
 typedef __attribute__((address_space(3))) char lds_char;
 
+// A fragment of V^T for MFMA chunk mm (16 keys) and d-block db from the
+// precomputed offsets: lane l holds d = db*32 + l%32 and keys 16mm + 4h +
+// {0..3}, 16mm + 8 + 4h + {0..3} (h = l/32), the key order of the P^T
+// fragment built from the score registers.
 __device__ __forceinline__ bf16x8 frag_vt_at(const lds_char* tile, const int* vo, int mm, int db) {
   const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + mm * 4096 + vo[db]));
   const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + mm * 4096 + vo[4 + db]));
@@ -649,21 +654,6 @@ __device__ __forceinline__ bf16x8 frag_vt_x(const lds_char* tile, int vbase, int
   return __builtin_bit_cast(bf16x8, r);
 }
 
-// A fragment of V^T for MFMA chunk mm (16 keys) and d-block db: lane l holds
-// d = db*32 + l%32 and keys 16mm + 4h + {0..3}, 16mm + 8 + 4h + {0..3} (h = l/32),
-// the key order of the P^T fragment built from the score registers.
-__device__ __forceinline__ bf16x8 frag_vt(const char* tile, int mm, int db, int lane) {
-  const int g = (lane >> 4) & 3, s = lane & 15;
-  const int key = 16 * mm + 4 * (g >> 1) + (s >> 2);
-  const int col = db * 32 + 16 * (g & 1) + 4 * (s & 3);
-  const char* p0 = tile + off(key, col >> 3) + (col & 7) * 2;
-  const char* p1 = tile + off(key + 8, col >> 3) + (col & 7) * 2;
-  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
-  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p1);
-  typedef short s16x8 __attribute__((ext_vector_type(8)));
-  const s16x8 r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-  return __builtin_bit_cast(bf16x8, r);
-}
 }  // namespace fa
 
 // WIN: a window shorter than the sequence (a.W < a.T); the causal instance
