@@ -484,7 +484,7 @@ void quantize(const bf16* x, long rows, long cols, unsigned* am, uint8_t* q, uin
               hipStream_t st) {
   const long n = rows * cols;
   Timed t("fp8_quantize", st);
-  if (amax) hipLaunchKernelGGL(amax_kernel, dim3(elt_grid(n)), dim3(256), 0, st, x, n, am);
+  if (amax) hipLaunchKernelGGL(amax_kernel, dim3(std::min(elt_grid(n), AMAX_GRID)), dim3(256), 0, st, x, n, am);
   if (qt && cols % 128 == 0)   // transposed codes, and the row-major ones in the same pass
     hipLaunchKernelGGL(quant_trans128_kernel, dim3((unsigned)(cols / 128), (unsigned)((ldt + 127) / 128)), dim3(256),
                        0, st, x, (int)rows, (int)cols, (const unsigned*)am, qt, (int)ldt, q);

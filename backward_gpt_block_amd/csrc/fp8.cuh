@@ -30,10 +30,28 @@ __global__ void zero_u32_kernel(unsigned* p, int n) {
   if (i < n) p[i] = 0u;
 }
 
-// out = max(out, max |x|) over n elements (n % 8 == 0), bf16 input.
+// out = max(out, max |x|) over n elements (n % 8 == 0), bf16 input.  Every
+// workgroup ends in one atomic on the same word, and those serialise: the
+// host caps the grid (AMAX_GRID workgroups) and each thread keeps eight
+// 16-byte loads in flight per iteration instead.
+constexpr unsigned AMAX_GRID = 256;
 __global__ __launch_bounds__(256) void amax_kernel(const bf16* __restrict__ x, long n, unsigned* __restrict__ out) {
   float m = 0.f;
-  for (long i = ((long)blockIdx.x * 256 + threadIdx.x) * 8; i < n; i += (long)gridDim.x * 256 * 8) {
+  const long stride = (long)gridDim.x * 256 * 8;
+  long i = ((long)blockIdx.x * 256 + threadIdx.x) * 8;
+  for (; i + 7 * stride < n; i += 8 * stride) {
+    u32x4 c[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) c[u] = ld16(x + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      float f[8];
+      Chunk<bf16>::unpack(c[u], f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(f[e]));
+    }
+  }
+  for (; i < n; i += stride) {
     float f[8];
     Chunk<bf16>::unpack(ld16(x + i), f);
 #pragma unroll
@@ -45,7 +63,8 @@ __global__ __launch_bounds__(256) void amax_kernel(const bf16* __restrict__ x, l
   __syncthreads();
   if (threadIdx.x == 0) {
     m = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
-    atomicMax(out, __float_as_uint(m));
+    const unsigned cur = __hip_atomic_load(out, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (__float_as_uint(m) > cur) atomicMax(out, __float_as_uint(m));
   }
 }
 
