@@ -104,6 +104,34 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Lane moves inside a row of 16 lanes through DPP (a VALU operand modifier;
+// __shfl_xor goes through ds_bpermute, an LDS round trip).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+constexpr int DPP_XOR1 = 0xB1;     // quad_perm [1,0,3,2]: lane i <- lane i^1
+constexpr int DPP_XOR2 = 0x4E;     // quad_perm [2,3,0,1]: lane i <- lane i^2
+constexpr int DPP_MIRROR = 0x140;  // row_mirror: lane i <- lane 15-i of the row
+constexpr int DPP_XOR8 = 0x128;    // row_ror:8: lane i <- lane i^8 of the row
+
+// Sum and maximum over each row of 16 lanes.  Every lane of the row ends
+// with the same bits: each step combines two values that the partner lanes
+// hold in swapped order (after the quad steps all four lanes of a quad agree;
+// the mirror pairs quad k with quad 3-k, the rotation quad k with quad k^2).
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_mov<DPP_XOR1>(v);
+  v += dpp_mov<DPP_XOR2>(v);
+  v += dpp_mov<DPP_MIRROR>(v);
+  return v + dpp_mov<DPP_XOR8>(v);
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_mov<DPP_XOR1>(v));
+  v = fmaxf(v, dpp_mov<DPP_XOR2>(v));
+  v = fmaxf(v, dpp_mov<DPP_MIRROR>(v));
+  return fmaxf(v, dpp_mov<DPP_XOR8>(v));
+}
+
 // Folds the wave's largest stored magnitude into *amax (float bits; a zero
 // word is the identity, and non-negative floats order like their bits).  m
 // is this lane's max |v| before rounding to T: rounding is monotone, so the

@@ -203,6 +203,9 @@ __device__ __forceinline__ void tile_coords(const GemmArgs& g, int& tm, int& tn,
 }
 
 // ---- epilogue ------------------------------------------------------------------
+// Position of token row `row` in its sequence of T (a mask when T is a power of two).
+__device__ __forceinline__ int seq_pos(int row, int T) { return (T & (T - 1)) == 0 ? (row & (T - 1)) : row % T; }
+
 // Output stores; NT marks them non-temporal (streamed past the caches).
 template <bool NT>
 __device__ __forceinline__ void st16_out(void* p, u32x4 v) {
@@ -244,8 +247,10 @@ __device__ __forceinline__ void epi8(const GemmArgs& g, int split, int row, int 
 #pragma unroll
     for (int h = 0; h < 8 / EL; ++h) st16_out<NT>(o + h * EL, Chunk<TO>::pack(f + h * EL));
   } else if constexpr (EPI == EPI_ROPE) {
-    // 16 consecutive lanes hold one 128-wide head of the row (8 columns
-    // each); rotary pairs (i, i + 64) sit 8 lanes apart
+    // 16 consecutive lanes (a DPP row) hold one 128-wide head of the row (8
+    // columns each); rotary pairs (i, i + 64) sit 8 lanes apart.  pre, if
+    // given, holds this lane's 16 floats of the angle table (cos, sin of its
+    // 8 column pairs), loaded ahead by the caller.
     constexpr int EL = Chunk<TO>::N;
     TO* o = static_cast<TO*>(g.out) + (long)row * g.ldo + col;
     // 0 q, 1 k, 2 v (uniform over the 16 lanes); hd the head within its part
@@ -253,23 +258,26 @@ __device__ __forceinline__ void epi8(const GemmArgs& g, int split, int row, int 
     const int hd = (col - (which == 0 ? 0 : g.C)) / 128;
     if (which < 2) {
       const int cg = (col % 128) >> 3;    // this lane's 8-column group in the head
-      const int t = row % g.T;
-      const float* csp = reinterpret_cast<const float*>(g.cs + (long)t * 64 + (cg & 7) * 8);
       float c8[16];
+      if (pre) {
 #pragma unroll
-      for (int h = 0; h < 4; ++h) Chunk<float>::unpack(ld16(csp + 4 * h), c8 + 4 * h);
+        for (int h = 0; h < 4; ++h) Chunk<float>::unpack(pre[h], c8 + 4 * h);
+      } else {
+        const float* csp = reinterpret_cast<const float*>(g.cs + (long)seq_pos(row, g.T) * 64 + (cg & 7) * 8);
+#pragma unroll
+        for (int h = 0; h < 4; ++h) Chunk<float>::unpack(ld16(csp + 4 * h), c8 + 4 * h);
+      }
       float ss = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float other = __shfl_xor(f[e], 8, 64);
+        const float other = dpp_mov<DPP_XOR8>(f[e]);
         const float c = c8[2 * e], sn = c8[2 * e + 1];
         // first half: z1 = own, z2 = partner; second half: z1 = partner, z2 = own
         f[e] = cg < 8 ? f[e] * c - other * sn : other * sn + f[e] * c;
         ss += f[e] * f[e];
       }
-#pragma unroll
-      for (int m = 1; m < 16; m <<= 1) ss += __shfl_xor(ss, m, 64);
-      const float r = 1.f / sqrtf(ss / 128.f + g.eps);
+      ss = row16_sum(ss);
+      const float r = __builtin_amdgcn_rsqf(ss / 128.f + g.eps);
 #pragma unroll
       for (int e = 0; e < 8; ++e) f[e] *= r;
       if (cg == 0) g.rho[((long)which * g.M + row) * g.H + hd] = r;
@@ -308,8 +316,7 @@ __device__ __forceinline__ void epi8(const GemmArgs& g, int split, int row, int 
       float d = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) d += rv[e] * xv[e];
-#pragma unroll
-      for (int m = 1; m < 16; m <<= 1) d += __shfl_xor(d, m, 64);
+      d = row16_sum(d);
       if ((col & 127) == 0) {
         const long b = row / g.T, t = row % g.T;
         g.delta[(b * g.H + col / 128) * g.T + t] = d;
@@ -589,8 +596,7 @@ __device__ __forceinline__ void head_lse8(const GemmArgs& g, int row, int col, c
 #pragma unroll
     for (int e = 0; e < 8; ++e) m = fmaxf(m, f[e]);
   }
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  m = row16_max(m);
   float l = 0.f;
   if (ok) {
 #pragma unroll
@@ -598,8 +604,7 @@ __device__ __forceinline__ void head_lse8(const GemmArgs& g, int row, int col, c
     const int t = g.tgt[row];
     if (t >= col && t < col + 8) g.tgt_logit[row] = f[t - col];
   }
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) l += __shfl_xor(l, o, 64);
+  l = row16_sum(l);
   if (ok && (col & 127) == 0) g.lse_part[(long)row * g.nseg + (col >> 7)] = make_float2(m, l);
 }
 
@@ -643,6 +648,22 @@ __device__ __forceinline__ void epilogue_pp(const GemmArgs& g, f32x16 (&acc)[2][
   char* wreg = smem + wave * 16384;
   const int rbase = m0 + (q >> 1) * 128 + grp * 64, cbase = n0 + (q & 1) * 128;
   float mx = 0.f;
+  // EPI_ROPE on a q or k head (the wave's 128 columns are one head): the
+  // angle-table chunks of step s = 8 pass + it are loaded during step s - 2
+  bool rot = false;
+  if constexpr (EPI == EPI_ROPE) rot = cbase < g.C + 128 * g.G;
+  u32x4 csr[2][4];
+  auto cs_load = [&](int s) {
+    const int qq = (s & 7) * 64 + lane;
+    const int grow = rbase + (s >> 3) * 32 + (qq >> 4), cg = qq & 7;
+    const float* p = reinterpret_cast<const float*>(g.cs + (long)seq_pos(grow, g.T) * 64 + cg * 8);
+#pragma unroll
+    for (int h = 0; h < 4; ++h) csr[s & 1][h] = ld16(p + 4 * h);
+  };
+  if (rot) {
+    cs_load(0);
+    cs_load(1);
+  }
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
@@ -661,8 +682,12 @@ __device__ __forceinline__ void epilogue_pp(const GemmArgs& g, f32x16 (&acc)[2][
       Chunk<float>::unpack(ld16(wreg + epi_off(row, 2 * cg + 1)), f + 4);
       const int grow = rbase + pass * 32 + row, gcol = cbase + cg * 8;
       if constexpr (EPI == EPI_LSE) head_lse8(g, grow, gcol, f);
-      else if (grow < g.M && gcol < g.N)
-        epi8<TO, EPI, true>(g, split, grow, gcol, f, mx, EpiAux<TO, EPI>::on ? &pre[pass][it] : nullptr);
+      else if (grow < g.M && gcol < g.N) {
+        // (the v heads do not read the ring)
+        if constexpr (EPI == EPI_ROPE) epi8<TO, EPI, true>(g, split, grow, gcol, f, mx, csr[it & 1]);
+        else epi8<TO, EPI, true>(g, split, grow, gcol, f, mx, EpiAux<TO, EPI>::on ? &pre[pass][it] : nullptr);
+      }
+      if (rot && pass * 8 + it + 2 < 16) cs_load(pass * 8 + it + 2);
     }
   }
   if (g.amax_out) amax_publish<TO>(g.amax_out, mx);
