@@ -92,18 +92,6 @@ template <> struct Mfma<fp8e4> {
 
 __device__ __forceinline__ int acc_row(int j, int lane) { return 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3); }
 
-// Wave-wide reductions (64 lanes).
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
-}
-
 // Lane moves inside a row of 16 lanes through DPP (a VALU operand modifier;
 // __shfl_xor goes through ds_bpermute, an LDS round trip).
 template <int CTRL>
@@ -130,6 +118,21 @@ __device__ __forceinline__ float row16_max(float v) {
   v = fmaxf(v, dpp_mov<DPP_XOR2>(v));
   v = fmaxf(v, dpp_mov<DPP_MIRROR>(v));
   return fmaxf(v, dpp_mov<DPP_XOR8>(v));
+}
+
+// Wave-wide reductions (64 lanes, all of them active): the rows' results
+// are read into scalar registers and combined in one order, so every lane
+// returns the same bits.
+__device__ __forceinline__ float lane_value(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = row16_max(v);
+  return fmaxf(fmaxf(lane_value(v, 0), lane_value(v, 16)), fmaxf(lane_value(v, 32), lane_value(v, 48)));
 }
 
 // Folds the wave's largest stored magnitude into *amax (float bits; a zero
