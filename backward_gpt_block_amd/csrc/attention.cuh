@@ -193,15 +193,40 @@ __device__ __forceinline__ float store_acc_row(T* dst, const f32x16* acc, float 
   return mx;   // largest stored magnitude (bf16 rows), before rounding
 }
 
+// The operands the QK-norm / rotary backward of one row reads besides the
+// accumulator: this lane's 64 values of the normalised row z (dims db*32 +
+// 8i + 4h + e, h = lane/32) and the (cos, sin) pairs of its 32 first-half
+// dims.  Loaded apart from the arithmetic so that a caller can put other
+// loads in flight between the two.
+struct QkRowIn {
+  bf16x4 z[4][4];
+  u32x4 c[2][4][2];
+};
+__device__ __forceinline__ void qk_row_load(QkRowIn& in, const bf16* z, const float2* cs, int lane) {
+  const int h = lane >> 5;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) in.z[db][i] = __builtin_bit_cast(bf16x4, ld8(z + db * 32 + 8 * i + 4 * h));
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float* cp = reinterpret_cast<const float*>(cs + db * 32 + 8 * i + 4 * h);
+      in.c[db][i][0] = ld16(cp);
+      in.c[db][i][1] = ld16(cp + 4);
+    }
+}
+
 // Stores the gradient of q' or k' (before QK-norm and rotary) of one row:
 // g = acc * scale is the gradient of the normalised row z (this lane holds
 // dims db*32 + 8i + 4h + e, h = lane/32; lane ^ 32 the rest), p its QK-norm
-// factor, cs the row's 64 angles.  QK-norm backward
+// factor, in.c the row's angles.  QK-norm backward
 // dz' = p (g - z mean(g z)), then the transposed rotation of each pair
 // (d, d + 64).  (Rotary embedding and QK-norm: flicky.cc nanochat page,
 // section on the model.)
-__device__ __forceinline__ float store_acc_row_qk(bf16* dst, const bf16* z, float p, const float2* cs,
-                                                  const f32x16* acc, float scale, int lane) {
+__device__ __forceinline__ float store_acc_row_qk(bf16* dst, const QkRowIn& in, float p, const f32x16* acc,
+                                                  float scale, int lane) {
   const int h = lane >> 5;
   float gv[4][16], zv[4][16];
   float dot = 0.f;
@@ -209,7 +234,7 @@ __device__ __forceinline__ float store_acc_row_qk(bf16* dst, const bf16* z, floa
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const bf16x4 zz = __builtin_bit_cast(bf16x4, ld8(z + db * 32 + 8 * i + 4 * h));
+      const bf16x4 zz = in.z[db][i];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         gv[db][4 * i + e] = acc[db][4 * i + e] * scale;
@@ -224,10 +249,9 @@ __device__ __forceinline__ float store_acc_row_qk(bf16* dst, const bf16* z, floa
   for (int db = 0; db < 2; ++db)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float* cp = reinterpret_cast<const float*>(cs + db * 32 + 8 * i + 4 * h);
       float c8[8];
-      Chunk<float>::unpack(ld16(cp), c8);
-      Chunk<float>::unpack(ld16(cp + 4), c8 + 4);
+      Chunk<float>::unpack(in.c[db][i][0], c8);
+      Chunk<float>::unpack(in.c[db][i][1], c8 + 4);
       bf16x4 lo, hi;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -244,6 +268,12 @@ __device__ __forceinline__ float store_acc_row_qk(bf16* dst, const bf16* z, floa
       st8(dst + (db + 2) * 32 + 8 * i + 4 * h, __builtin_bit_cast(u32x2, hi));
     }
   return mx;   // largest stored magnitude, before rounding
+}
+__device__ __forceinline__ float store_acc_row_qk(bf16* dst, const bf16* z, float p, const float2* cs,
+                                                  const f32x16* acc, float scale, int lane) {
+  QkRowIn in;
+  qk_row_load(in, z, cs, lane);
+  return store_acc_row_qk(dst, in, p, acc, scale, lane);
 }
 
 
@@ -824,10 +854,20 @@ typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) const f32x4 lds_f32x4;
 }  // namespace fa
 
-// dK, dV: one workgroup = 128 keys of one (sequence, head), 4 waves x 32 keys
-// (K and V fragments in registers); walks the 64-query tiles at and after the
-// diagonal.  Q and dO tiles are row-major in LDS (3-slot ring); their
-// transposes for dV^T += dO^T P and dK^T += Q^T dS come from transpose reads.
+// dK, dV: one unit of work = 128 keys of one (sequence, key/value head), 4
+// waves x 32 keys (K and V fragments in registers); it walks the 64-query
+// tiles at and after the diagonal of every query head of the group.  Q and dO
+// tiles are row-major in LDS (3-slot ring); their transposes for
+// dV^T += dO^T P and dK^T += Q^T dS come from transpose reads.
+//
+// The grid holds one workgroup per CU and each workgroup walks units (longest
+// first, every other round in reverse so that the workgroups' totals even
+// out).  Between units every global access is row-contiguous: the unit's K
+// and V rows arrive as direct-to-LDS tiles and the fragments are read from
+// LDS; dV and dK go through LDS to row layout and out in 16-byte pieces, the
+// QK-norm and rotary backward of dK computed in that layout (a row's 128
+// values on 16 lanes).  Lane-per-row loads and stores, 32 rows per
+// instruction, made this boundary cost as much as six query tiles.
 __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_bf16_kernel(AttnArgs a) {
   using namespace fa;
   typedef Mfma<bf16> MM;
@@ -835,32 +875,52 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_bf16_kernel(AttnArgs a) 
   constexpr int QT = 64;
   constexpr int SLOTB = 2 * TILE + 2048;      // Q, dO, lse (1 KiB), delta (1 KiB)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // one workgroup = 128 keys of one (sequence, key/value head); it walks the
-  // query tiles of every query head of the group, accumulating into the
-  // same dK, dV
   const int BG = a.B * a.G, R = a.H / a.G;
-  const int kt = (int)(blockIdx.x / BG);      // first key tiles have the most queries
-  const int bg = blockIdx.x % BG;
-  const int b = bg / a.G, kvh = bg % a.G;
+  const int units = ((a.T + 127) / 128) * BG;
   const long ldq = (long)a.LD * 2, ldo = (long)a.C * 2;
   const bf16* qkv = static_cast<const bf16*>(a.qkv);
-  const i32x4 rsq = make_rsrc(qkv + (long)b * a.T * a.LD, clamp_bytes((long)a.T * ldq));
-  const i32x4 rso = make_rsrc(static_cast<const bf16*>(a.dO) + (long)b * a.T * a.C, clamp_bytes((long)a.T * ldo));
-  // lse, delta rows of all the sequence's query heads ([H][T] each)
-  const i32x4 rsl = make_rsrc(a.lse + (long)b * a.H * a.T, (uint32_t)a.H * a.T * 4);
-  const i32x4 rsd = make_rsrc(a.delta + (long)b * a.H * a.T, (uint32_t)a.H * a.T * 4);
-  const int kw0 = kt * 128 + wave * 32;
-  const int key = kw0 + (lane & 31);
-  const bool kv = key < a.T;
+  const int nqt_all = (a.T + QT - 1) / QT;
 
-  bf16x8 kf[8], vf[8];
-  frag_row_global<bf16>(kf, qkv + ((long)b * a.T + key) * a.LD + a.KO + kvh * HD, kv, lane);
-  frag_row_global<bf16>(vf, qkv + ((long)b * a.T + key) * a.LD + a.VO + kvh * HD, kv, lane);
-  f32x16 dk[4], dv[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) { dk[i][r] = 0.f; dv[i][r] = 0.f; }
+  // unit of round j for this workgroup (>= units: none)
+  auto unit_of = [&](int j) {
+    const int i = (j & 1) ? (int)gridDim.x - 1 - (int)blockIdx.x : (int)blockIdx.x;
+    return j * (int)gridDim.x + i;
+  };
+  // a unit: key tile kt (first key tiles have the most queries), sequence b,
+  // key/value head kvh; n iterations = R query heads x nq query tiles
+  struct Unit {
+    int kt, b, kvh, qt0, nq, n;
+  };
+  auto make_unit = [&](int u) {
+    Unit p;
+    p.kt = u / BG;
+    const int bg = u % BG;
+    p.b = bg / a.G;
+    p.kvh = bg % a.G;
+    p.qt0 = (p.kt * 128) / QT;
+    // the last query that sees a key of the unit is kt*128 + 127 + W - 1
+    const int nqt = min(nqt_all, (int)(((long)p.kt * 128 + 127 + a.W - 1) / QT) + 1);
+    p.nq = nqt - p.qt0;
+    p.n = R * p.nq;
+    return p;
+  };
+  // iteration it of unit p: query head kvh*R + it/nq, query tile qt0 + it%nq
+  auto issue = [&](const Unit& p, int slot, int it) {
+    char* d = smem + slot * SLOTB;
+    const int h = p.kvh * R + it / p.nq, q0 = (p.qt0 + it % p.nq) * QT;
+    const int qoff = h * HD * 2;
+    const i32x4 rsq = make_rsrc(qkv + (long)p.b * a.T * a.LD, clamp_bytes((long)a.T * ldq));
+    const i32x4 rso = make_rsrc(static_cast<const bf16*>(a.dO) + (long)p.b * a.T * a.C, clamp_bytes((long)a.T * ldo));
+    issue_tile(d, rsq, q0, ldq, qoff, wave, lane);
+    issue_tile(d + TILE, rso, q0, ldo, qoff, wave, lane);
+    if (wave == 0) {
+      // lse, delta rows of all the sequence's query heads ([H][T] each)
+      const i32x4 rsl = make_rsrc(a.lse + (long)p.b * a.H * a.T, (uint32_t)a.H * a.T * 4);
+      const i32x4 rsd = make_rsrc(a.delta + (long)p.b * a.H * a.T, (uint32_t)a.H * a.T * 4);
+      issue_vec(d + 2 * TILE, rsl, h * a.T + q0, lane);
+      issue_vec(d + 2 * TILE + 1024, rsd, h * a.T + q0, lane);
+    }
+  };
   // LDS offsets of the fragment reads from one base each: row-fragment read
   // ks at kbase ^ (ks << 5), transpose reads as in frag_vt_x
   int kbase = off(lane & 31, lane >> 5);
@@ -870,134 +930,249 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_bf16_kernel(AttnArgs a) 
     frag_vt_offsets(vo, lane);
     vbase = vo[0];
   }
-
-  const int qt0 = (kt * 128) / QT;
-  // the last query that sees a key of this workgroup is kt*128 + 127 + W - 1
-  const int nqt = min((a.T + QT - 1) / QT, (int)(((long)kt * 128 + 127 + a.W - 1) / QT) + 1);
-  const int nq = nqt - qt0;                   // query tiles per query head
-  const int n = R * nq;                       // iteration it: head kvh*R + it/nq, tile qt0 + it%nq
-  auto issue = [&](int slot, int it) {
-    char* d = smem + slot * SLOTB;
-    const int h = kvh * R + it / nq, q0 = (qt0 + it % nq) * QT;
-    const int qoff = h * HD * 2;
-    issue_tile(d, rsq, q0, ldq, qoff, wave, lane);
-    issue_tile(d + TILE, rso, q0, ldo, qoff, wave, lane);
-    if (wave == 0) {
-      issue_vec(d + 2 * TILE, rsl, h * a.T + q0, lane);
-      issue_vec(d + 2 * TILE + 1024, rsd, h * a.T + q0, lane);
-    }
+  // K and V rows of a unit (k rows 0-63, 64-127, then v): ring slot 2 and
+  // past the ring, used only between units
+  char* const kvs = smem + 2 * SLOTB;
+  auto issue_kv_rows = [&](const Unit& p) {
+    const i32x4 rsq = make_rsrc(qkv + (long)p.b * a.T * a.LD, clamp_bytes((long)a.T * ldq));
+    const int k0 = p.kt * 128, ko = (a.KO + p.kvh * HD) * 2, vo = (a.VO + p.kvh * HD) * 2;
+    issue_tile(kvs, rsq, k0, ldq, ko, wave, lane);
+    issue_tile(kvs + TILE, rsq, k0 + 64, ldq, ko, wave, lane);
+    issue_tile(kvs + 2 * TILE, rsq, k0, ldq, vo, wave, lane);
+    issue_tile(kvs + 3 * TILE, rsq, k0 + 64, ldq, vo, wave, lane);
   };
-  issue(0, 0);
-  if (n > 1) issue(1, 1);
-  for (int it = 0; it < n; ++it) {
-    if (it + 1 < n) {
-      if (wave == 0) __builtin_amdgcn_s_waitcnt(0x0f70 | 10);  // vmcnt(10): the next tile's 10 issues in flight
-      else __builtin_amdgcn_s_waitcnt(0x0f70 | 8);             // vmcnt(8)
-    } else {
-      __builtin_amdgcn_s_waitcnt(0x0f70);
+  bf16x8 kf[8], vf[8];
+  auto read_kv = [&]() {   // this wave's 32 keys: rows 32 (wave & 1) .. of tile wave / 2
+    const lds_char* kb = (const lds_char*)kvs + (wave >> 1) * TILE + (wave & 1) * 8192;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      kf[ks] = *(lds_bf16x8*)(kb + (kbase ^ (ks << 5)));
+      vf[ks] = *(lds_bf16x8*)(kb + 2 * TILE + (kbase ^ (ks << 5)));
     }
-    __syncthreads();
-    // the bases count as changed here, so that the eight offsets derived from
-    // each are not hoisted out of the loop into sixteen live registers
-    asm volatile("" : "+v"(kbase), "+v"(vbase));
-    if (it + 2 < n) issue((it + 2) % 3, it + 2);
-    const int q0 = (qt0 + it % nq) * QT;
-    const lds_char* qt_ = (const lds_char*)smem + (it % 3) * SLOTB;
-    const lds_char* ot_ = qt_ + TILE;
-    const float* vec = (const float*)(smem + (it % 3) * SLOTB + 2 * TILE);
-    if (q0 + QT - 1 < kw0) continue;             // all queries precede all keys of this wave
-    if (q0 > kw0 + 31 + a.W - 1) continue;       // all queries are past the keys' windows
-    const bool need_mask = (q0 < kw0 + 31) || (q0 + QT > a.T) || (q0 + QT - 1 >= kw0 + a.W);
-    // one copy of the iteration with the causal/edge mask and one without,
-    // so that each is a single scheduling region
-    auto body = [&](auto maskc) {
-    constexpr bool MASK = decltype(maskc)::value;
-    // Two 32-query halves in 32 steps of two MFMAs: S/dP(0); S/dP(1) with the
-    // softmax of half 0; dV/dK(0) with the softmax of half 1; dV/dK(1).  Each
-    // step issues the LDS reads of the step after next and ends with a
-    // scheduling fence, so every MFMA finds its fragments already loaded
-    // (left to itself the scheduler put each read right before its MFMA,
-    // which then waited out the LDS latency).
-    f32x16 sv[2] = {}, dp[2] = {};
-    bf16x8 fa[32], fb[32];   // the two fragments of step i
-    auto rd = [&](int i) {
-      if (i < 16) {          // Q and dO rows of half i/8, k-step i%8
-        const int qb = i >> 3, ks = i & 7;
-        fa[i] = *(lds_bf16x8*)(qt_ + qb * 8192 + (kbase ^ (ks << 5)));
-        fb[i] = *(lds_bf16x8*)(ot_ + qb * 8192 + (kbase ^ (ks << 5)));
-      } else {               // dO^T and Q^T of half, MFMA chunk and d-block
-        const int u = i - 16, qb = u >> 3, mm = (u >> 2) & 1, db = u & 3;
-        fa[i] = frag_vt_x(ot_, vbase, 2 * qb + mm, db);
-        fb[i] = frag_vt_x(qt_, vbase, 2 * qb + mm, db);
-      }
-    };
-    // lse and delta of the four queries of group g of half qb (one step ahead
-    // of their use)
-    f32x4 lv, dl;
-    auto ldv = [&](int qb, int g) {
-      const int qi = qb * 32 + 8 * g + 4 * (lane >> 5);
-      lv = *(const lds_f32x4*)((const lds_char*)vec + qi * 4);
-      dl = *(const lds_f32x4*)((const lds_char*)vec + 1024 + qi * 4);
-    };
-    // P and dS of scores 4g .. 4g+3 of half qb
-    auto smx = [&](int qb, int g) {
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): read before the ring slot 2 is refilled
+  };
+  // workgroup barrier over LDS only (global accesses in flight stay in flight)
+  auto lds_barrier = [&]() {
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_s_barrier();
+  };
+
+  int j = 0;
+  if (unit_of(0) >= units) return;
+  Unit cur = make_unit(unit_of(0));
+  issue_kv_rows(cur);
+  __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
+  lds_barrier();
+  read_kv();
+  issue(cur, 0, 0);
+  if (cur.n > 1) issue(cur, 1, 1);
+  float mx = 0.f;
+  for (;;) {
+    const int kw0 = cur.kt * 128 + wave * 32;
+    const int key = kw0 + (lane & 31);
+    const int n = cur.n;
+    f32x16 dk[4], dv[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * g + e;
-        float p = __builtin_amdgcn_exp2f(fmaf(sv[qb][r], a.sl2, -lv[e]));
-        if constexpr (MASK) {
-          const int qq = q0 + qb * 32 + 8 * g + 4 * (lane >> 5) + e;
-          p = (key > qq || qq >= a.T || qq >= key + a.W) ? 0.f : p;
-        }
-        sv[qb][r] = p;
-        dp[qb][r] = p * (dp[qb][r] - dl[e]);
-      }
-    };
-    bf16x8 pf[2], sf[2];     // bf16 P and dS of the half being multiplied
-    rd(0);
-    rd(1);
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      if (i + 2 < 32) rd(i + 2);
-      if (i < 16) {
-        const int qb = i >> 3, ks = i & 7;
-        sv[qb] = MM::mma(fa[i], kf[ks], sv[qb]);   // S  (query x key)
-        dp[qb] = MM::mma(fb[i], vf[ks], dp[qb]);   // dP (query x key)
-        if (qb == 1) {
-          if ((ks & 1) == 0) ldv(0, ks >> 1);
-          else smx(0, ks >> 1);
-        }
+      for (int r = 0; r < 16; ++r) { dk[i][r] = 0.f; dv[i][r] = 0.f; }
+    for (int it = 0; it < n; ++it) {
+      if (it + 1 < n) {
+        if (wave == 0) __builtin_amdgcn_s_waitcnt(0x0f70 | 10);  // vmcnt(10): the next tile's 10 issues in flight
+        else __builtin_amdgcn_s_waitcnt(0x0f70 | 8);             // vmcnt(8)
       } else {
-        const int u = i - 16, qb = u >> 3, mm = (u >> 2) & 1, db = u & 3;
-        if ((u & 7) == 0) {
-#pragma unroll
-          for (int m = 0; m < 2; ++m) {
-            pf[m] = frag_regs<bf16>(sv[qb], m * 8);
-            sf[m] = frag_regs<bf16>(dp[qb], m * 8);
+        __builtin_amdgcn_s_waitcnt(0x0f70);
+      }
+      __syncthreads();
+      // the bases count as changed here, so that the eight offsets derived from
+      // each are not hoisted out of the loop into sixteen live registers
+      asm volatile("" : "+v"(kbase), "+v"(vbase));
+      if (it + 2 < n) issue(cur, (it + 2) % 3, it + 2);
+      const int q0 = (cur.qt0 + it % cur.nq) * QT;
+      const lds_char* qt_ = (const lds_char*)smem + (it % 3) * SLOTB;
+      const lds_char* ot_ = qt_ + TILE;
+      const float* vec = (const float*)(smem + (it % 3) * SLOTB + 2 * TILE);
+      if (q0 + QT - 1 < kw0) continue;             // all queries precede all keys of this wave
+      if (q0 > kw0 + 31 + a.W - 1) continue;       // all queries are past the keys' windows
+      const bool need_mask = (q0 < kw0 + 31) || (q0 + QT > a.T) || (q0 + QT - 1 >= kw0 + a.W);
+      // one copy of the iteration with the causal/edge mask and one without,
+      // so that each is a single scheduling region
+      auto body = [&](auto maskc) {
+      constexpr bool MASK = decltype(maskc)::value;
+      // Two 32-query halves in 32 steps of two MFMAs: S/dP(0); S/dP(1) with the
+      // softmax of half 0; dV/dK(0) with the softmax of half 1; dV/dK(1).  Each
+      // step issues the LDS reads of the step after next and ends with a
+      // scheduling fence, so every MFMA finds its fragments already loaded
+      // (left to itself the scheduler put each read right before its MFMA,
+      // which then waited out the LDS latency).
+      f32x16 sv[2] = {}, dp[2] = {};
+      bf16x8 fa[32], fb[32];   // the two fragments of step i
+      auto rd = [&](int i) {
+        if (i < 16) {          // Q and dO rows of half i/8, k-step i%8
+          const int qb = i >> 3, ks = i & 7;
+          fa[i] = *(lds_bf16x8*)(qt_ + qb * 8192 + (kbase ^ (ks << 5)));
+          fb[i] = *(lds_bf16x8*)(ot_ + qb * 8192 + (kbase ^ (ks << 5)));
+        } else {               // dO^T and Q^T of half, MFMA chunk and d-block
+          const int u = i - 16, qb = u >> 3, mm = (u >> 2) & 1, db = u & 3;
+          fa[i] = frag_vt_x(ot_, vbase, 2 * qb + mm, db);
+          fb[i] = frag_vt_x(qt_, vbase, 2 * qb + mm, db);
+        }
+      };
+      // lse and delta of the four queries of group g of half qb (one step ahead
+      // of their use)
+      f32x4 lv, dl;
+      auto ldv = [&](int qb, int g) {
+        const int qi = qb * 32 + 8 * g + 4 * (lane >> 5);
+        lv = *(const lds_f32x4*)((const lds_char*)vec + qi * 4);
+        dl = *(const lds_f32x4*)((const lds_char*)vec + 1024 + qi * 4);
+      };
+      // P and dS of scores 4g .. 4g+3 of half qb
+      auto smx = [&](int qb, int g) {
+  #pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          float p = __builtin_amdgcn_exp2f(fmaf(sv[qb][r], a.sl2, -lv[e]));
+          if constexpr (MASK) {
+            const int qq = q0 + qb * 32 + 8 * g + 4 * (lane >> 5) + e;
+            p = (key > qq || qq >= a.T || qq >= key + a.W) ? 0.f : p;
+          }
+          sv[qb][r] = p;
+          dp[qb][r] = p * (dp[qb][r] - dl[e]);
+        }
+      };
+      bf16x8 pf[2], sf[2];     // bf16 P and dS of the half being multiplied
+      rd(0);
+      rd(1);
+  #pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        if (i + 2 < 32) rd(i + 2);
+        if (i < 16) {
+          const int qb = i >> 3, ks = i & 7;
+          sv[qb] = MM::mma(fa[i], kf[ks], sv[qb]);   // S  (query x key)
+          dp[qb] = MM::mma(fb[i], vf[ks], dp[qb]);   // dP (query x key)
+          if (qb == 1) {
+            if ((ks & 1) == 0) ldv(0, ks >> 1);
+            else smx(0, ks >> 1);
+          }
+        } else {
+          const int u = i - 16, qb = u >> 3, mm = (u >> 2) & 1, db = u & 3;
+          if ((u & 7) == 0) {
+  #pragma unroll
+            for (int m = 0; m < 2; ++m) {
+              pf[m] = frag_regs<bf16>(sv[qb], m * 8);
+              sf[m] = frag_regs<bf16>(dp[qb], m * 8);
+            }
+          }
+          dv[db] = MM::mma(fa[i], pf[mm], dv[db]);     // dV^T += dO^T P
+          dk[db] = MM::mma(fb[i], sf[mm], dk[db]);     // dK^T += Q^T dS
+          if (qb == 0) {
+            if ((u & 1) == 0) ldv(1, u >> 1);
+            else smx(1, u >> 1);
           }
         }
-        dv[db] = MM::mma(fa[i], pf[mm], dv[db]);     // dV^T += dO^T P
-        dk[db] = MM::mma(fb[i], sf[mm], dk[db]);     // dK^T += Q^T dS
-        if (qb == 0) {
-          if ((u & 1) == 0) ldv(1, u >> 1);
-          else smx(1, u >> 1);
-        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
+      };
+      if (need_mask) body(std::true_type());
+      else body(std::false_type());
     }
+    // ---- unit boundary
+    ++j;
+    const int un = unit_of(j);
+    const bool more = un < units;
+    const Unit nxt = more ? make_unit(un) : cur;
+    lds_barrier();                 // the ring is free
+    if (more) issue_kv_rows(nxt);  // into slot 2 and past the ring
+    // dV, then dK, through this wave's staging rows (32 keys x 132 floats in
+    // slots 0-1); read back, pass i gives this lane key row 4i + lane/16 and
+    // dims 8 (lane & 15) .. + 7
+    constexpr int SP = 132;
+    float* stg = reinterpret_cast<float*>(smem) + wave * 32 * SP;
+    const int cg = lane & 15;
+    auto stage = [&](const f32x16* acc, float scale) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const int d = db * 32 + acc_row(r, lane);
+          *reinterpret_cast<float2*>(stg + (lane & 31) * SP + d) = make_float2(acc[db][r] * scale, acc[db][r + 1] * scale);
+        }
     };
-    if (need_mask) body(std::true_type());
-    else body(std::false_type());
-  }
-  float mx = 0.f;
-  if (kv) {
-    const long rowi = (long)b * a.T + key;
-    bf16* row = static_cast<bf16*>(a.dqkv) + rowi * a.LD;
-    const bf16* zk = qkv + rowi * a.LD + a.KO + kvh * HD;
-    // key QK-norm factors: [N][H] after the query ones, head index kvh
-    mx = store_acc_row_qk(row + a.KO + kvh * HD, zk, a.rho[((long)a.B * a.T + rowi) * a.H + kvh],
-                          a.cs + (long)key * 64, dk, a.rsd, lane);
-    mx = fmaxf(mx, store_acc_row<bf16>(row + a.VO + kvh * HD, dv, 1.f, lane));
+    auto unstage = [&](int i, float* f) {
+      const float* src = stg + (4 * i + (lane >> 4)) * SP + 8 * cg;
+      Chunk<float>::unpack(*reinterpret_cast<const u32x4*>(src), f);
+      Chunk<float>::unpack(*reinterpret_cast<const u32x4*>(src + 4), f + 4);
+    };
+    const long row0 = (long)cur.b * a.T + kw0;   // global row of this wave's first key
+    bf16* const dqkv = static_cast<bf16*>(a.dqkv);
+    // QK-norm operands of dK's rows: the normalised k rows and their factors
+    u32x4 zr[8];
+    float rk[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int kr = kw0 + 4 * i + (lane >> 4);
+      const long rowi = row0 + 4 * i + (lane >> 4);
+      zr[i] = kr < a.T ? ld16(qkv + rowi * a.LD + a.KO + cur.kvh * HD + 8 * cg) : u32x4{0u, 0u, 0u, 0u};
+      rk[i] = kr < a.T ? a.rho[((long)a.B * a.T + rowi) * a.H + cur.kvh] : 0.f;
+    }
+    stage(dv, 1.f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float f[8];
+      unstage(i, f);
+      const int kr = kw0 + 4 * i + (lane >> 4);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(f[e]));
+      if (kr < a.T) st16(dqkv + (row0 + 4 * i + (lane >> 4)) * a.LD + a.VO + cur.kvh * HD + 8 * cg, Chunk<bf16>::pack(f));
+    }
+    stage(dk, a.rsd);
+    // angle-table chunks of pass i + 2 loaded during pass i
+    u32x4 csr[2][4];
+    auto cs_load = [&](int i) {
+      const int kr = min(kw0 + 4 * i + (lane >> 4), a.T - 1);
+      const float* cp = reinterpret_cast<const float*>(a.cs + (long)kr * 64 + (cg & 7) * 8);
+#pragma unroll
+      for (int h = 0; h < 4; ++h) csr[i & 1][h] = ld16(cp + 4 * h);
+    };
+    cs_load(0);
+    cs_load(1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float g[8], z[8], c8[16];
+      unstage(i, g);
+      Chunk<bf16>::unpack(zr[i], z);
+#pragma unroll
+      for (int h = 0; h < 4; ++h) Chunk<float>::unpack(csr[i & 1][h], c8 + 4 * h);
+      if (i + 2 < 8) cs_load(i + 2);
+      // dz' = rho (g - z mean(g z)) over the row's 128 dims (16 lanes), then
+      // the transposed rotation of the pairs (d, d + 64), 8 lanes apart
+      float dot = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dot += g[e] * z[e];
+      const float mean = row16_sum(dot) * (1.f / 128.f);
+      float o[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float d = rk[i] * (g[e] - z[e] * mean);
+        const float other = dpp_mov<DPP_XOR8>(d);
+        const float c = c8[2 * e], sn = c8[2 * e + 1];
+        // first half: d1 = own, d2 = partner -> d1 c + d2 s; second half: d2 c - d1 s
+        o[e] = cg < 8 ? d * c + other * sn : d * c - other * sn;
+        mx = fmaxf(mx, fabsf(o[e]));
+      }
+      const int kr = kw0 + 4 * i + (lane >> 4);
+      if (kr < a.T) st16(dqkv + (row0 + 4 * i + (lane >> 4)) * a.LD + a.KO + cur.kvh * HD + 8 * cg, Chunk<bf16>::pack(o));
+    }
+    if (!more) break;
+    // the next unit's K, V rows have landed (each wave waits for its own
+    // loads, the barrier for everyone's; the stores above drain too) and the
+    // staging rows are free
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
+    lds_barrier();
+    cur = nxt;
+    read_kv();
+    issue(cur, 0, 0);
+    if (cur.n > 1) issue(cur, 1, 1);
   }
   if (a.amax_dqkv) amax_publish<bf16>(a.amax_dqkv, mx);
 }

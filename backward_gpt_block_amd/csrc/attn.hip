@@ -4,6 +4,7 @@
 // the three functions below.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <mutex>
 #include <set>
 
@@ -23,7 +24,28 @@ void allow_lds(const void* kern, int bytes) {
 
 int tiles(int n, int t) { return (n + t - 1) / t; }
 
-constexpr int DKDV_LDS = 3 * (2 * fa::TILE + 2048);   // three slots of Q, dO, lse, delta
+// dK/dV: three ring slots of Q, dO, lse, delta; between units the K, V rows
+// of a unit take slot 2 and 30 KiB past it
+constexpr int DKDV_SLOT = 2 * fa::TILE + 2048;
+constexpr int DKDV_LDS = 2 * DKDV_SLOT + 4 * fa::TILE;
+static_assert(DKDV_LDS >= 3 * DKDV_SLOT && DKDV_LDS <= 160 * 1024, "dK/dV LDS");
+static_assert(4 * 32 * 132 * 4 <= 2 * DKDV_SLOT, "dK/dV staging rows fit in ring slots 0-1");
+
+// Compute units of the current device (the grid of the persistent kernels:
+// one workgroup per CU); looked up once per device.
+int cu_count() {
+  static std::mutex mu;
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> l(mu);
+  if (cached[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
 
 }  // namespace
 
@@ -41,11 +63,13 @@ void attn_fwd(const AttnArgs& a, bool bf16, hipStream_t st) {
 }
 
 void attn_bwd_dkdv(const AttnArgs& a, bool bf16, hipStream_t st) {
-  // one workgroup per 128 keys of a (sequence, key/value head)
-  const dim3 grid(tiles(a.T, 128) * a.B * a.G);
+  // a unit of work per 128 keys of a (sequence, key/value head)
+  const int units = tiles(a.T, 128) * a.B * a.G;
+  const dim3 grid(units);
   if (bf16) {
+    // persistent: one workgroup per CU walks the units
     allow_lds(reinterpret_cast<const void*>(attn_bwd_dkdv_bf16_kernel), DKDV_LDS);
-    hipLaunchKernelGGL(attn_bwd_dkdv_bf16_kernel, grid, dim3(256), DKDV_LDS, st, a);
+    hipLaunchKernelGGL(attn_bwd_dkdv_bf16_kernel, dim3(std::min(units, cu_count())), dim3(256), DKDV_LDS, st, a);
   } else {
     allow_lds(reinterpret_cast<const void*>(attn_bwd_dkdv_kernel<float>), attn_dkdv_lds<float>());
     hipLaunchKernelGGL(attn_bwd_dkdv_kernel<float>, grid, dim3(256), attn_dkdv_lds<float>(), st, a);
