@@ -852,6 +852,107 @@ __device__ __forceinline__ void issue_vec(char* dst, i32x4 rv, int r0, int lane)
 }
 typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) const f32x4 lds_f32x4;
+
+// ---- row layout of a wave's 128 x 32 accumulator (backward kernels) ----------
+// A wave's accumulator acc[4] holds a 128 x 32 block: rows d (acc[db] covers
+// d = 32 db ..), column = one of the wave's 32 rows (lane & 31).  It is staged
+// in LDS as 32 rows x 128 floats, 16-byte chunks XOR-swizzled by row (the 32
+// rows one instruction writes fall in distinct chunks), and read back in
+// passes: pass i gives this lane row 4i + lane/16 and dims 8 (lane & 15) .. +7.
+__device__ __forceinline__ int stg_idx(int row, int d) { return row * 128 + ((((d >> 2) ^ row) & 31) << 2) + (d & 3); }
+__device__ __forceinline__ void stage_acc(float* stg, const f32x16* acc, float scale, int lane) {
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const int d = db * 32 + acc_row(r, lane);
+      *reinterpret_cast<float2*>(stg + stg_idx(lane & 31, d)) = make_float2(acc[db][r] * scale, acc[db][r + 1] * scale);
+    }
+}
+__device__ __forceinline__ void unstage_row(const float* stg, int i, int lane, float* f) {
+  const int row = 4 * i + (lane >> 4), d = 8 * (lane & 15);
+  Chunk<float>::unpack(*reinterpret_cast<const u32x4*>(stg + stg_idx(row, d)), f);
+  Chunk<float>::unpack(*reinterpret_cast<const u32x4*>(stg + stg_idx(row, d + 4)), f + 4);
+}
+// The staged rows as bf16 to out (row r at out + r*ld), rows < nrows; returns
+// the largest stored magnitude before rounding.
+__device__ __forceinline__ float store_rows(const float* stg, bf16* out, long ld, int nrows, int lane) {
+  float mx = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float f[8];
+    unstage_row(stg, i, lane, f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(f[e]));
+    const int r = 4 * i + (lane >> 4);
+    if (r < nrows) st16(out + r * ld + 8 * (lane & 15), Chunk<bf16>::pack(f));
+  }
+  return mx;
+}
+// Operands of the QK-norm backward of the wave's 32 rows: the normalised rows
+// z (row r at z + r*ld) and their factors rho[r * rs], zero past nrows.
+struct QkRows {
+  u32x4 z[8];
+  float p[8];
+};
+__device__ __forceinline__ void qk_rows_load(QkRows& q, const bf16* z, long ld, const float* rho, long rs, int nrows,
+                                             int lane) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = 4 * i + (lane >> 4);
+    q.z[i] = r < nrows ? ld16(z + r * ld + 8 * (lane & 15)) : u32x4{0u, 0u, 0u, 0u};
+    q.p[i] = r < nrows ? rho[r * rs] : 0.f;
+  }
+}
+// Gradient of q' or k' from the staged gradient g of the normalised rows:
+// QK-norm backward dz' = p (g - z mean(g z)) over the row's 128 dims (16
+// lanes), then the transposed rotation of each pair (d, d + 64), 8 lanes
+// apart, with the angles of sequence position t0 + r (cs: [T][64]).  Row r to
+// out + r*ld for r < nrows; returns the largest stored magnitude before
+// rounding.  (Rotary embedding and QK-norm: flicky.cc nanochat page, section
+// on the model.)
+__device__ __forceinline__ float store_rows_qk(const float* stg, const QkRows& q, bf16* out, long ld,
+                                               const float2* cs, int t0, int nrows, int lane) {
+  const int cg = lane & 15;
+  float mx = 0.f;
+  // angle-table chunks of pass i + 2 loaded during pass i
+  u32x4 csr[2][4];
+  auto cs_load = [&](int i) {
+    // rows past nrows read a valid row (their results are not stored)
+    const int t = nrows > 0 ? t0 + min(4 * i + (lane >> 4), nrows - 1) : 0;
+    const float* cp = reinterpret_cast<const float*>(cs + (long)t * 64 + (cg & 7) * 8);
+#pragma unroll
+    for (int h = 0; h < 4; ++h) csr[i & 1][h] = ld16(cp + 4 * h);
+  };
+  cs_load(0);
+  cs_load(1);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float g[8], z[8], c8[16];
+    unstage_row(stg, i, lane, g);
+    Chunk<bf16>::unpack(q.z[i], z);
+#pragma unroll
+    for (int h = 0; h < 4; ++h) Chunk<float>::unpack(csr[i & 1][h], c8 + 4 * h);
+    if (i + 2 < 8) cs_load(i + 2);
+    float dot = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dot += g[e] * z[e];
+    const float mean = row16_sum(dot) * (1.f / 128.f);
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float d = q.p[i] * (g[e] - z[e] * mean);
+      const float other = dpp_mov<DPP_XOR8>(d);
+      const float c = c8[2 * e], sn = c8[2 * e + 1];
+      // first half: d1 = own, d2 = partner -> d1 c + d2 s; second half: d2 c - d1 s
+      o[e] = cg < 8 ? d * c + other * sn : d * c - other * sn;
+      mx = fmaxf(mx, fabsf(o[e]));
+    }
+    const int r = 4 * i + (lane >> 4);
+    if (r < nrows) st16(out + r * ld + 8 * cg, Chunk<bf16>::pack(o));
+  }
+  return mx;
+}
 }  // namespace fa
 
 // dK, dV: one unit of work = 128 keys of one (sequence, key/value head), 4
@@ -1083,86 +1184,20 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_bf16_kernel(AttnArgs a) 
     const Unit nxt = more ? make_unit(un) : cur;
     lds_barrier();                 // the ring is free
     if (more) issue_kv_rows(nxt);  // into slot 2 and past the ring
-    // dV, then dK, through this wave's staging rows (32 keys x 132 floats in
-    // slots 0-1); read back, pass i gives this lane key row 4i + lane/16 and
-    // dims 8 (lane & 15) .. + 7
-    constexpr int SP = 132;
-    float* stg = reinterpret_cast<float*>(smem) + wave * 32 * SP;
-    const int cg = lane & 15;
-    auto stage = [&](const f32x16* acc, float scale) {
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const int d = db * 32 + acc_row(r, lane);
-          *reinterpret_cast<float2*>(stg + (lane & 31) * SP + d) = make_float2(acc[db][r] * scale, acc[db][r + 1] * scale);
-        }
-    };
-    auto unstage = [&](int i, float* f) {
-      const float* src = stg + (4 * i + (lane >> 4)) * SP + 8 * cg;
-      Chunk<float>::unpack(*reinterpret_cast<const u32x4*>(src), f);
-      Chunk<float>::unpack(*reinterpret_cast<const u32x4*>(src + 4), f + 4);
-    };
+    // dV, then dK, through this wave's staging rows (slots 0-1), out in row
+    // layout; the QK-norm operands of dK's rows are loaded first
+    float* stg = reinterpret_cast<float*>(smem) + wave * 32 * 128;
     const long row0 = (long)cur.b * a.T + kw0;   // global row of this wave's first key
-    bf16* const dqkv = static_cast<bf16*>(a.dqkv);
-    // QK-norm operands of dK's rows: the normalised k rows and their factors
-    u32x4 zr[8];
-    float rk[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int kr = kw0 + 4 * i + (lane >> 4);
-      const long rowi = row0 + 4 * i + (lane >> 4);
-      zr[i] = kr < a.T ? ld16(qkv + rowi * a.LD + a.KO + cur.kvh * HD + 8 * cg) : u32x4{0u, 0u, 0u, 0u};
-      rk[i] = kr < a.T ? a.rho[((long)a.B * a.T + rowi) * a.H + cur.kvh] : 0.f;
-    }
-    stage(dv, 1.f);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float f[8];
-      unstage(i, f);
-      const int kr = kw0 + 4 * i + (lane >> 4);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(f[e]));
-      if (kr < a.T) st16(dqkv + (row0 + 4 * i + (lane >> 4)) * a.LD + a.VO + cur.kvh * HD + 8 * cg, Chunk<bf16>::pack(f));
-    }
-    stage(dk, a.rsd);
-    // angle-table chunks of pass i + 2 loaded during pass i
-    u32x4 csr[2][4];
-    auto cs_load = [&](int i) {
-      const int kr = min(kw0 + 4 * i + (lane >> 4), a.T - 1);
-      const float* cp = reinterpret_cast<const float*>(a.cs + (long)kr * 64 + (cg & 7) * 8);
-#pragma unroll
-      for (int h = 0; h < 4; ++h) csr[i & 1][h] = ld16(cp + 4 * h);
-    };
-    cs_load(0);
-    cs_load(1);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float g[8], z[8], c8[16];
-      unstage(i, g);
-      Chunk<bf16>::unpack(zr[i], z);
-#pragma unroll
-      for (int h = 0; h < 4; ++h) Chunk<float>::unpack(csr[i & 1][h], c8 + 4 * h);
-      if (i + 2 < 8) cs_load(i + 2);
-      // dz' = rho (g - z mean(g z)) over the row's 128 dims (16 lanes), then
-      // the transposed rotation of the pairs (d, d + 64), 8 lanes apart
-      float dot = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) dot += g[e] * z[e];
-      const float mean = row16_sum(dot) * (1.f / 128.f);
-      float o[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float d = rk[i] * (g[e] - z[e] * mean);
-        const float other = dpp_mov<DPP_XOR8>(d);
-        const float c = c8[2 * e], sn = c8[2 * e + 1];
-        // first half: d1 = own, d2 = partner -> d1 c + d2 s; second half: d2 c - d1 s
-        o[e] = cg < 8 ? d * c + other * sn : d * c - other * sn;
-        mx = fmaxf(mx, fabsf(o[e]));
-      }
-      const int kr = kw0 + 4 * i + (lane >> 4);
-      if (kr < a.T) st16(dqkv + (row0 + 4 * i + (lane >> 4)) * a.LD + a.KO + cur.kvh * HD + 8 * cg, Chunk<bf16>::pack(o));
-    }
+    const int nrows = min(32, a.T - kw0);
+    bf16* const drow = static_cast<bf16*>(a.dqkv) + row0 * a.LD;
+    QkRows qk;
+    // key QK-norm factors: [N][H] after the query ones, head index kvh
+    qk_rows_load(qk, qkv + row0 * a.LD + a.KO + cur.kvh * HD, a.LD, a.rho + ((long)a.B * a.T + row0) * a.H + cur.kvh,
+                 a.H, nrows, lane);
+    stage_acc(stg, dv, 1.f, lane);
+    mx = fmaxf(mx, store_rows(stg, drow + a.VO + cur.kvh * HD, a.LD, nrows, lane));
+    stage_acc(stg, dk, a.rsd, lane);
+    mx = fmaxf(mx, store_rows_qk(stg, qk, drow + a.KO + cur.kvh * HD, a.LD, a.cs, kw0, nrows, lane));
     if (!more) break;
     // the next unit's K, V rows have landed (each wave waits for its own
     // loads, the barrier for everyone's; the stores above drain too) and the
@@ -1177,10 +1212,15 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_bf16_kernel(AttnArgs a) 
   if (a.amax_dqkv) amax_publish<bf16>(a.amax_dqkv, mx);
 }
 
-// dQ: one workgroup = 128 queries of one (sequence, head), 4 waves x 32
-// queries (Q and dO fragments in registers); walks the 64-key tiles up to the
-// diagonal.  K and V tiles row-major in LDS (3-slot ring); K^T for
-// dQ^T += K^T dS^T comes from transpose reads.
+// dQ: one unit of work = 128 queries of one (sequence, head), 4 waves x 32
+// queries (Q and dO fragments in registers); it walks the 64-key tiles up to
+// the diagonal.  K and V tiles row-major in LDS (3-slot ring); K^T for
+// dQ^T += K^T dS^T comes from transpose reads.  Persistent like the dK/dV
+// kernel: one workgroup per CU walks the units (longest first, alternate
+// rounds reversed); between units the Q and dO rows arrive as direct-to-LDS
+// tiles (Q past the ring, dO in ring slot 2) and dQ leaves through LDS
+// staging (ring slots 0-1) in row layout, QK-norm and rotary backward
+// included.
 __global__ __launch_bounds__(256, 1) void attn_bwd_dq_bf16_kernel(AttnArgs a) {
   using namespace fa;
   typedef Mfma<bf16> MM;
@@ -1188,28 +1228,48 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_bf16_kernel(AttnArgs a) {
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int BH = a.B * a.H;
   const int nqt = (a.T + 127) / 128;
-  const int qt = nqt - 1 - (int)(blockIdx.x / BH);
-  const int bh = blockIdx.x % BH;
-  const int b = bh / a.H, head = bh % a.H;
-  const long ldb = (long)a.LD * 2;
-  const int kvh = head / (a.H / a.G);
+  const int units = nqt * BH;
+  const long ldb = (long)a.LD * 2, ldo = (long)a.C * 2;
   const bf16* qkv = static_cast<const bf16*>(a.qkv);
-  const i32x4 rs = make_rsrc(qkv + (long)b * a.T * a.LD, clamp_bytes((long)a.T * ldb));
-  const int koff = (a.KO + kvh * HD) * 2, voff = (a.VO + kvh * HD) * 2;
-  const int qw0 = qt * 128 + wave * 32;
-  const int q = qw0 + (lane & 31);
-  const bool qv = q < a.T;
 
-  bf16x8 qf[8], df[8];
-  frag_row_global<bf16>(qf, qkv + ((long)b * a.T + q) * a.LD + head * HD, qv, lane);
-  frag_row_global<bf16>(df, static_cast<const bf16*>(a.dO) + ((long)b * a.T + q) * a.C + head * HD, qv, lane);
-  const float lse = qv ? a.lse[(long)bh * a.T + q] : INFINITY;
-  const float dlt = qv ? a.delta[(long)bh * a.T + q] : 0.f;
-  f32x16 acc[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+  auto unit_of = [&](int j) {
+    const int i = (j & 1) ? (int)gridDim.x - 1 - (int)blockIdx.x : (int)blockIdx.x;
+    return j * (int)gridDim.x + i;
+  };
+  // a unit: query tile qt (last tiles have the most keys), sequence b, head;
+  // n key tiles from kt_lo
+  struct Unit {
+    int qt, b, head, kvh, kt_lo, n;
+  };
+  auto make_unit = [&](int u) {
+    Unit p;
+    p.qt = nqt - 1 - u / BH;
+    const int bh = u % BH;
+    p.b = bh / a.H;
+    p.head = bh % a.H;
+    p.kvh = p.head / (a.H / a.G);
+    const int last_key = min(a.T - 1, p.qt * 128 + 127);
+    p.kt_lo = max(0, p.qt * 128 - a.W + 1) / KT;   // first tile inside the window
+    p.n = last_key / KT + 1 - p.kt_lo;
+    return p;
+  };
+  auto issue = [&](const Unit& p, int slot, int it) {   // K, V tile it of unit p
+    const i32x4 rs = make_rsrc(qkv + (long)p.b * a.T * a.LD, clamp_bytes((long)a.T * ldb));
+    issue_kv(smem + slot * SLOT, rs, (p.kt_lo + it) * KT, ldb, (a.KO + p.kvh * HD) * 2, (a.VO + p.kvh * HD) * 2, wave,
+             lane);
+  };
+  // Q rows of a unit past the ring, dO rows in ring slot 2 (between units)
+  char* const qrows = smem + NSLOT * SLOT;
+  char* const orows = smem + 2 * SLOT;
+  auto issue_rows = [&](const Unit& p) {
+    const i32x4 rs = make_rsrc(qkv + (long)p.b * a.T * a.LD, clamp_bytes((long)a.T * ldb));
+    const i32x4 ro = make_rsrc(static_cast<const bf16*>(a.dO) + (long)p.b * a.T * a.C, clamp_bytes((long)a.T * ldo));
+    const int q0 = p.qt * 128, co = p.head * HD * 2;
+    issue_tile(qrows, rs, q0, ldb, co, wave, lane);
+    issue_tile(qrows + TILE, rs, q0 + 64, ldb, co, wave, lane);
+    issue_tile(orows, ro, q0, ldo, co, wave, lane);
+    issue_tile(orows + TILE, ro, q0 + 64, ldo, co, wave, lane);
+  };
   // LDS offsets of the fragment reads from one base each (as in the dK/dV kernel)
   int kbase = off(lane & 31, lane >> 5);
   int vbase;
@@ -1218,89 +1278,139 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_bf16_kernel(AttnArgs a) {
     frag_vt_offsets(vo, lane);
     vbase = vo[0];
   }
+  bf16x8 qf[8], df[8];
+  auto read_rows = [&]() {   // this wave's 32 queries: rows 32 (wave & 1) .. of tile wave / 2
+    const int o = (wave >> 1) * TILE + (wave & 1) * 8192;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      qf[ks] = *(lds_bf16x8*)((const lds_char*)qrows + o + (kbase ^ (ks << 5)));
+      df[ks] = *(lds_bf16x8*)((const lds_char*)orows + o + (kbase ^ (ks << 5)));
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): read before ring slot 2 is refilled
+  };
+  auto lds_barrier = [&]() {
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_s_barrier();
+  };
 
-  const int last_key = min(a.T - 1, qt * 128 + 127);
-  const int kt_lo = max(0, qt * 128 - a.W + 1) / KT;   // first tile inside the window
-  const int n = last_key / KT + 1 - kt_lo;
-  issue_kv(smem, rs, kt_lo * KT, ldb, koff, voff, wave, lane);
-  if (n > 1) issue_kv(smem + SLOT, rs, (kt_lo + 1) * KT, ldb, koff, voff, wave, lane);
-  for (int it = 0; it < n; ++it) {
-    if (it + 1 < n) __builtin_amdgcn_s_waitcnt(0x0f70 | 8);
-    else __builtin_amdgcn_s_waitcnt(0x0f70);
-    __syncthreads();
-    asm volatile("" : "+v"(kbase), "+v"(vbase));   // keep the derived offsets in the loop
-    if (it + 2 < n) issue_kv(smem + ((it + 2) % NSLOT) * SLOT, rs, (kt_lo + it + 2) * KT, ldb, koff, voff, wave, lane);
-    const lds_char* kt_ = (const lds_char*)smem + (it % NSLOT) * SLOT;
-    const lds_char* vt_ = kt_ + TILE;
-    const int k0 = (kt_lo + it) * KT;
-    if (k0 > qw0 + 31) continue;
-    if (k0 + KT - 1 <= qw0 - a.W) continue;           // every key is before this wave's windows
-    const bool need_mask = (k0 + KT - 1 > qw0) || (k0 + KT > a.T) || (k0 <= qw0 + 31 - a.W);
-    // Two 32-key halves in 24 steps of two MFMAs: S^T/dP^T(0); S^T/dP^T(1)
-    // with dS(0); dQ(0) with dS(1); dQ(1).  As in the dK/dV kernel, each step
-    // issues the LDS reads of the step after next and ends with a scheduling
-    // fence.  Masked and unmasked tiles are separate copies.
-    auto body = [&](auto maskc) {
-      constexpr bool MASK = decltype(maskc)::value;
-      f32x16 sv[2] = {}, dp[2] = {};
-      bf16x8 fa[24], fb[24];
-      auto rd = [&](int i) {
-        if (i < 16) {        // K and V rows of half i/8, k-step i%8
-          const int kb = i >> 3, ks = i & 7;
-          fa[i] = *(lds_bf16x8*)(kt_ + kb * 8192 + (kbase ^ (ks << 5)));
-          fb[i] = *(lds_bf16x8*)(vt_ + kb * 8192 + (kbase ^ (ks << 5)));
-        } else {             // K^T of half, MFMA chunk, d-blocks d2 and d2+1
-          const int u = i - 16, kb = u >> 2, m2 = (u >> 1) & 1, d2 = 2 * (u & 1);
-          fa[i] = frag_vt_x(kt_, vbase, 2 * kb + m2, d2);
-          fb[i] = frag_vt_x(kt_, vbase, 2 * kb + m2, d2 + 1);
-        }
-      };
-      auto dsr = [&](int kb, int r) {   // dS^T of score r of half kb
-        float p = __builtin_amdgcn_exp2f(fmaf(sv[kb][r], a.sl2, -lse));
-        if constexpr (MASK) {
-          const int kk = k0 + kb * 32 + acc_row(r, lane);
-          p = (kk > q || kk >= a.T || kk <= q - a.W) ? 0.f : p;
-        }
-        sv[kb][r] = p * (dp[kb][r] - dlt);
-      };
-      bf16x8 sf[2];          // bf16 dS^T of the half being multiplied
-      rd(0);
-      rd(1);
-#pragma unroll
-      for (int i = 0; i < 24; ++i) {
-        if (i + 2 < 24) rd(i + 2);
-        if (i < 16) {
-          const int kb = i >> 3, ks = i & 7;
-          sv[kb] = MM::mma(fa[i], qf[ks], sv[kb]);   // S^T
-          dp[kb] = MM::mma(fb[i], df[ks], dp[kb]);   // dP^T
-          if (kb == 1) {
-            dsr(0, 2 * ks);
-            dsr(0, 2 * ks + 1);
-          }
-        } else {
-          const int u = i - 16, kb = u >> 2, m2 = (u >> 1) & 1, d2 = 2 * (u & 1);
-          if ((u & 3) == 0) {
-            sf[0] = frag_regs<bf16>(sv[kb], 0);
-            sf[1] = frag_regs<bf16>(sv[kb], 8);
-          }
-          acc[d2] = MM::mma(fa[i], sf[m2], acc[d2]);           // dQ^T += K^T dS^T
-          acc[d2 + 1] = MM::mma(fb[i], sf[m2], acc[d2 + 1]);
-          if (kb == 0) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) dsr(1, 4 * u + e);
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    };
-    if (need_mask) body(std::true_type());
-    else body(std::false_type());
-  }
+  int j = 0;
+  if (unit_of(0) >= units) return;
+  Unit cur = make_unit(unit_of(0));
+  issue_rows(cur);
+  __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
+  lds_barrier();
+  read_rows();
+  issue(cur, 0, 0);
+  if (cur.n > 1) issue(cur, 1, 1);
   float mx = 0.f;
-  if (qv) {
-    const long rowi = (long)b * a.T + q;
-    mx = store_acc_row_qk(static_cast<bf16*>(a.dqkv) + rowi * a.LD + head * HD, qkv + rowi * a.LD + head * HD,
-                          a.rho[rowi * a.H + head], a.cs + (long)q * 64, acc, a.rsd, lane);
+  for (;;) {
+    const int qw0 = cur.qt * 128 + wave * 32;
+    const int q = qw0 + (lane & 31);
+    const bool qv = q < a.T;
+    const long bhT = ((long)cur.b * a.H + cur.head) * a.T;
+    const float lse = qv ? a.lse[bhT + q] : INFINITY;
+    const float dlt = qv ? a.delta[bhT + q] : 0.f;
+    const int kt_lo = cur.kt_lo, n = cur.n;
+    f32x16 acc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+    for (int it = 0; it < n; ++it) {
+      if (it + 1 < n) __builtin_amdgcn_s_waitcnt(0x0f70 | 8);
+      else __builtin_amdgcn_s_waitcnt(0x0f70);
+      __syncthreads();
+      asm volatile("" : "+v"(kbase), "+v"(vbase));   // keep the derived offsets in the loop
+      if (it + 2 < n) issue(cur, (it + 2) % NSLOT, it + 2);
+      const lds_char* kt_ = (const lds_char*)smem + (it % NSLOT) * SLOT;
+      const lds_char* vt_ = kt_ + TILE;
+      const int k0 = (kt_lo + it) * KT;
+      if (k0 > qw0 + 31) continue;
+      if (k0 + KT - 1 <= qw0 - a.W) continue;           // every key is before this wave's windows
+      const bool need_mask = (k0 + KT - 1 > qw0) || (k0 + KT > a.T) || (k0 <= qw0 + 31 - a.W);
+      // Two 32-key halves in 24 steps of two MFMAs: S^T/dP^T(0); S^T/dP^T(1)
+      // with dS(0); dQ(0) with dS(1); dQ(1).  As in the dK/dV kernel, each step
+      // issues the LDS reads of the step after next and ends with a scheduling
+      // fence.  Masked and unmasked tiles are separate copies.
+      auto body = [&](auto maskc) {
+        constexpr bool MASK = decltype(maskc)::value;
+        f32x16 sv[2] = {}, dp[2] = {};
+        bf16x8 fa[24], fb[24];
+        auto rd = [&](int i) {
+          if (i < 16) {        // K and V rows of half i/8, k-step i%8
+            const int kb = i >> 3, ks = i & 7;
+            fa[i] = *(lds_bf16x8*)(kt_ + kb * 8192 + (kbase ^ (ks << 5)));
+            fb[i] = *(lds_bf16x8*)(vt_ + kb * 8192 + (kbase ^ (ks << 5)));
+          } else {             // K^T of half, MFMA chunk, d-blocks d2 and d2+1
+            const int u = i - 16, kb = u >> 2, m2 = (u >> 1) & 1, d2 = 2 * (u & 1);
+            fa[i] = frag_vt_x(kt_, vbase, 2 * kb + m2, d2);
+            fb[i] = frag_vt_x(kt_, vbase, 2 * kb + m2, d2 + 1);
+          }
+        };
+        auto dsr = [&](int kb, int r) {   // dS^T of score r of half kb
+          float p = __builtin_amdgcn_exp2f(fmaf(sv[kb][r], a.sl2, -lse));
+          if constexpr (MASK) {
+            const int kk = k0 + kb * 32 + acc_row(r, lane);
+            p = (kk > q || kk >= a.T || kk <= q - a.W) ? 0.f : p;
+          }
+          sv[kb][r] = p * (dp[kb][r] - dlt);
+        };
+        bf16x8 sf[2];          // bf16 dS^T of the half being multiplied
+        rd(0);
+        rd(1);
+  #pragma unroll
+        for (int i = 0; i < 24; ++i) {
+          if (i + 2 < 24) rd(i + 2);
+          if (i < 16) {
+            const int kb = i >> 3, ks = i & 7;
+            sv[kb] = MM::mma(fa[i], qf[ks], sv[kb]);   // S^T
+            dp[kb] = MM::mma(fb[i], df[ks], dp[kb]);   // dP^T
+            if (kb == 1) {
+              dsr(0, 2 * ks);
+              dsr(0, 2 * ks + 1);
+            }
+          } else {
+            const int u = i - 16, kb = u >> 2, m2 = (u >> 1) & 1, d2 = 2 * (u & 1);
+            if ((u & 3) == 0) {
+              sf[0] = frag_regs<bf16>(sv[kb], 0);
+              sf[1] = frag_regs<bf16>(sv[kb], 8);
+            }
+            acc[d2] = MM::mma(fa[i], sf[m2], acc[d2]);           // dQ^T += K^T dS^T
+            acc[d2 + 1] = MM::mma(fb[i], sf[m2], acc[d2 + 1]);
+            if (kb == 0) {
+  #pragma unroll
+              for (int e = 0; e < 4; ++e) dsr(1, 4 * u + e);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      if (need_mask) body(std::true_type());
+      else body(std::false_type());
+    }
+    // ---- unit boundary
+    ++j;
+    const int un = unit_of(j);
+    const bool more = un < units;
+    const Unit nxt = more ? make_unit(un) : cur;
+    lds_barrier();                 // the ring is free
+    if (more) issue_rows(nxt);     // past the ring and into slot 2
+    float* stg = reinterpret_cast<float*>(smem) + wave * 32 * 128;   // slots 0-1
+    const long row0 = (long)cur.b * a.T + qw0;
+    const int nrows = min(32, a.T - qw0);
+    QkRows qk;
+    qk_rows_load(qk, qkv + row0 * a.LD + cur.head * HD, a.LD, a.rho + row0 * a.H + cur.head, a.H, nrows, lane);
+    stage_acc(stg, acc, a.rsd, lane);
+    mx = fmaxf(mx, store_rows_qk(stg, qk, static_cast<bf16*>(a.dqkv) + row0 * a.LD + cur.head * HD, a.LD, a.cs, qw0,
+                                 nrows, lane));
+    if (!more) break;
+    // the next unit's Q, dO rows have landed and the staging rows are free
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
+    lds_barrier();
+    cur = nxt;
+    read_rows();
+    issue(cur, 0, 0);
+    if (cur.n > 1) issue(cur, 1, 1);
   }
   if (a.amax_dqkv) amax_publish<bf16>(a.amax_dqkv, mx);
 }

@@ -29,7 +29,10 @@ int tiles(int n, int t) { return (n + t - 1) / t; }
 constexpr int DKDV_SLOT = 2 * fa::TILE + 2048;
 constexpr int DKDV_LDS = 2 * DKDV_SLOT + 4 * fa::TILE;
 static_assert(DKDV_LDS >= 3 * DKDV_SLOT && DKDV_LDS <= 160 * 1024, "dK/dV LDS");
-static_assert(4 * 32 * 132 * 4 <= 2 * DKDV_SLOT, "dK/dV staging rows fit in ring slots 0-1");
+static_assert(4 * 32 * 128 * 4 <= 2 * DKDV_SLOT, "dK/dV staging rows fit in ring slots 0-1");
+// dQ: the K/V ring, then the Q rows of a unit (its dO rows use ring slot 2)
+constexpr int DQ_LDS = fa::LDS + 2 * fa::TILE;
+static_assert(DQ_LDS <= 160 * 1024 && 4 * 32 * 128 * 4 <= 2 * fa::SLOT && 2 * fa::TILE <= fa::SLOT, "dQ LDS");
 
 // Compute units of the current device (the grid of the persistent kernels:
 // one workgroup per CU); looked up once per device.
@@ -77,11 +80,13 @@ void attn_bwd_dkdv(const AttnArgs& a, bool bf16, hipStream_t st) {
 }
 
 void attn_bwd_dq(const AttnArgs& a, bool bf16, hipStream_t st) {
-  // one workgroup per 128 queries of a (sequence, head)
-  const dim3 grid(tiles(a.T, 128) * a.B * a.H);
+  // a unit of work per 128 queries of a (sequence, head)
+  const int units = tiles(a.T, 128) * a.B * a.H;
+  const dim3 grid(units);
   if (bf16) {
-    allow_lds(reinterpret_cast<const void*>(attn_bwd_dq_bf16_kernel), fa::LDS);
-    hipLaunchKernelGGL(attn_bwd_dq_bf16_kernel, grid, dim3(256), fa::LDS, st, a);
+    // persistent: one workgroup per CU walks the units
+    allow_lds(reinterpret_cast<const void*>(attn_bwd_dq_bf16_kernel), DQ_LDS);
+    hipLaunchKernelGGL(attn_bwd_dq_bf16_kernel, dim3(std::min(units, cu_count())), dim3(256), DQ_LDS, st, a);
   } else {
     allow_lds(reinterpret_cast<const void*>(attn_bwd_dq_kernel<float>), attn_dq_lds<float>());
     hipLaunchKernelGGL(attn_bwd_dq_kernel<float>, grid, dim3(256), attn_dq_lds<float>(), st, a);
