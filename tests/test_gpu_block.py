@@ -170,6 +170,21 @@ def test_gqa(B, T, C, G, dtype, W):
     _parity(BlockShape(B=B, T=T, C=C, H=C // 128, F=4 * C, dtype=dtype, window=W, n_kv_head=G), seed=8)
 
 
+@pytest.mark.parametrize("B,T,C,G,W", [
+    # dK/dV 2 x 160 x 2 = 640 units, dQ 640, forward 320: workgroups walk
+    # several units; the second key tile of each sequence holds 2 keys, so
+    # three of its four waves have no rows at all
+    (160, 130, 256, 0, 0),
+    # grouped heads under a window: 384 dK/dV units of 2 query heads each,
+    # 768 dQ units
+    (96, 200, 512, 2, 100),
+])
+def test_attention_units_beyond_one_per_cu(B, T, C, G, W):
+    # the backward attention grids hold one workgroup per CU (256 on MI355X);
+    # these shapes need more units than that, at sizes compared in full
+    _parity(BlockShape(B=B, T=T, C=C, H=C // 128, F=4 * C, dtype="bf16", window=W, n_kv_head=G), seed=11)
+
+
 def test_gqa_g_equals_h_matches_mha_bitwise():
     # n_kv_head = H takes the same kernels over the same layout as MHA
     sh = BlockShape(B=2, T=200, C=256, H=2, F=1024, dtype="bf16")
