@@ -16,7 +16,10 @@
 // for dQ, and a pass over query tiles per key tile for dK and dV, both
 // recomputing P from the saved log-sum-exp.  The bf16 backward loops are
 // written as explicit steps of two MFMAs whose LDS reads are issued two
-// steps ahead, with a scheduling fence per step.
+// steps ahead, with a scheduling fence per step.  The bf16 backward kernels
+// are persistent (one workgroup per CU walking units of 128 rows), and their
+// per-unit row operands and results pass through LDS so that every global
+// access between units is row-contiguous.
 //
 // This header is compiled only in attn.hip, with MFMA results in vector
 // registers (the softmax reads them after every MFMA chain).
