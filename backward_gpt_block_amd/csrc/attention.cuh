@@ -687,15 +687,39 @@ __device__ __forceinline__ bf16x8 frag_vt_x(const lds_char* tile, int vbase, int
   return __builtin_bit_cast(bf16x8, r);
 }
 
+// K and V tiles of 64 rows through an LDS slot, issued by eight waves (two
+// 16-byte chunks per lane and tile; layout as in issue_kv).
+__device__ __forceinline__ void issue_kv8(char* slot, i32x4 rs, int k0, long ldb, int koff, int voff, int wave,
+                                          int lane) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {                 // K, then V
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int base = wave * 128 + i * 64;     // chunk index in the tile (64 per issue)
+      const int p = base + lane;
+      const int row = p >> 4, c = (p & 15) ^ sw(row);
+      const uint32_t o = (uint32_t)((long)(k0 + row) * ldb + (t ? voff : koff) + c * 16);
+      lds_u32* dst = (lds_u32*)(slot + t * TILE + __builtin_amdgcn_readfirstlane(base) * 16);
+      raw_buffer_load_lds(rs, dst, 16, (int)o, 0, 0, 0);
+    }
+  }
+}
+typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
+
 }  // namespace fa
 
+// Forward: one workgroup = 256 queries of one (sequence, head), eight waves of
+// 32 queries (two waves per SIMD: while one runs the softmax arithmetic of a
+// key tile the other's MFMAs proceed); key tiles of 64 through a 3-slot LDS
+// ring.
 // WIN: a window shorter than the sequence (a.W < a.T); the causal instance
 // carries none of the window's bounds, masks or guards.
 template <bool WIN>
-__global__ __launch_bounds__(256, 1) void attn_fwd_bf16_kernel(AttnArgs a) {
+__global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(AttnArgs a) {
   using namespace fa;
   typedef Mfma<bf16> MM;
   extern __shared__ __attribute__((aligned(16))) char smem[];
+  constexpr int QW8 = 32;                              // queries per wave
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), h = lane >> 5;
   const int BH = a.B * a.H;
   const int nqt = (a.T + QWG - 1) / QWG;
@@ -707,22 +731,17 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_bf16_kernel(AttnArgs a) {
   const bf16* qkv = static_cast<const bf16*>(a.qkv);
   const i32x4 rs = make_rsrc(qkv + (long)b * a.T * a.LD, clamp_bytes((long)a.T * ldb));
   const int koff = (a.KO + kvh * HD) * 2, voff = (a.VO + kvh * HD) * 2;
-  const int qw0 = qt * QWG + wave * QW;
+  const int qw0 = qt * QWG + wave * QW8;
+  const int q = qw0 + (lane & 31);
 
-  bf16x8 qf[2][8];
+  bf16x8 qf[8];
+  frag_row_global<bf16>(qf, qkv + ((long)b * a.T + q) * a.LD + head * HD, q < a.T, lane);
+  f32x16 o[4];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int q = qw0 + qb * 32 + (lane & 31);
-    frag_row_global<bf16>(qf[qb], qkv + ((long)b * a.T + q) * a.LD + head * HD, q < a.T, lane);
-  }
-  f32x16 o[2][4];
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[qb][i][r] = 0.f;
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+    for (int r = 0; r < 16; ++r) o[i][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
   int ko[8], vo[8];
   frag_k_offsets(ko, lane);
   frag_vt_offsets(vo, lane);
@@ -730,104 +749,84 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_bf16_kernel(AttnArgs a) {
   const int last_key = min(a.T - 1, qt * QWG + QWG - 1);
   const int kt_lo = WIN ? max(0, qt * QWG - a.W + 1) / KT : 0;   // first tile inside the window
   const int n = last_key / KT + 1 - kt_lo;
-  issue_kv(smem, rs, kt_lo * KT, ldb, koff, voff, wave, lane);
-  if (n > 1) issue_kv(smem + SLOT, rs, (kt_lo + 1) * KT, ldb, koff, voff, wave, lane);
+  issue_kv8(smem, rs, kt_lo * KT, ldb, koff, voff, wave, lane);
+  if (n > 1) issue_kv8(smem + SLOT, rs, (kt_lo + 1) * KT, ldb, koff, voff, wave, lane);
   for (int it = 0; it < n; ++it) {
     // tile it landed (own loads, then everyone's); slot of tile it-1 is free
-    if (it + 1 < n) __builtin_amdgcn_s_waitcnt(0x3f70 | 8);   // vmcnt(8): the next tile may stay in flight
+    if (it + 1 < n) __builtin_amdgcn_s_waitcnt(0x3f70 | 4);   // vmcnt(4): the next tile may stay in flight
     else __builtin_amdgcn_s_waitcnt(0x3f70);                  // vmcnt(0)
     __syncthreads();
-    if (it + 2 < n) issue_kv(smem + ((it + 2) % NSLOT) * SLOT, rs, (kt_lo + it + 2) * KT, ldb, koff, voff, wave, lane);
+    if (it + 2 < n) issue_kv8(smem + ((it + 2) % NSLOT) * SLOT, rs, (kt_lo + it + 2) * KT, ldb, koff, voff, wave, lane);
     const lds_char* kt_ = (const lds_char*)smem + (it % NSLOT) * SLOT;
     const lds_char* vt_ = kt_ + TILE;
     const int k0 = (kt_lo + it) * KT;
-    if (k0 > qw0 + QW - 1) continue;                  // every key of this tile is in this wave's future
+    if (k0 > qw0 + QW8 - 1) continue;                 // every key of this tile is in this wave's future
     if (WIN && k0 + KT - 1 <= qw0 - a.W) continue;    // every key is before this wave's windows
-    f32x16 s[2][2];
+    f32x16 s[2];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[qb][kb][r] = 0.f;
+      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
       const bf16x8 k0f = *(lds_bf16x8*)(kt_ + ko[ks]);
       const bf16x8 k1f = *(lds_bf16x8*)(kt_ + 8192 + ko[ks]);
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        s[qb][0] = MM::mma(k0f, qf[qb][ks], s[qb][0]);
-        s[qb][1] = MM::mma(k1f, qf[qb][ks], s[qb][1]);
-      }
+      s[0] = MM::mma(k0f, qf[ks], s[0]);
+      s[1] = MM::mma(k1f, qf[ks], s[1]);
     }
     // Online softmax with a lazily updated reference: scores are exponentiated
     // against m_run, which only moves (rescaling l and O) when some lane's tile
     // maximum exceeds it by more than 8 (a factor 256, far from overflow).
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const int q = qw0 + qb * 32 + (lane & 31);
-      // diagonal, ragged or window-edge tile
-      if ((k0 + KT - 1 > qw0 + qb * 32) || (k0 + KT > a.T) || (WIN && k0 <= qw0 + qb * 32 + 31 - a.W)) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + kb * 32 + acc_row(r, lane);
-            if (key > q || key >= a.T || (WIN && key <= q - a.W)) s[qb][kb][r] = -INFINITY;
-          }
-      }
-      float mt = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[qb][kb][r]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * a.sl2;
-      // with a window a query can meet whole tiles of hidden keys before its
-      // first visible one: its running maximum is still -inf (and l, O zero).
-      // Causal: every query sees key 0 in the first tile, so m is finite.
-      if (__ballot(mt > m_run[qb] + 8.f) != 0) {
-        const float m_new = fmaxf(m_run[qb], mt);
-        const float alpha = (WIN && m_new == -INFINITY) ? 0.f : exp2f(m_run[qb] - m_new);
-        l_run[qb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) o[qb][db] *= alpha;
-        m_run[qb] = m_new;
-      }
-      const float ref = (WIN && m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
-      float ls = 0.f;
+    // diagonal, ragged or window-edge tile
+    if ((k0 + KT - 1 > qw0) || (k0 + KT > a.T) || (WIN && k0 <= qw0 + 31 - a.W)) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][r], a.sl2, -ref));
-          s[qb][kb][r] = p;
-          ls += p;
+          const int key = k0 + kb * 32 + acc_row(r, lane);
+          if (key > q || key >= a.T || (WIN && key <= q - a.W)) s[kb][r] = -INFINITY;
         }
-      l_run[qb] += ls;
     }
+    float mt = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * a.sl2;
+    // with a window a query can meet whole tiles of hidden keys before its
+    // first visible one: its running maximum is still -inf (and l, O zero).
+    // Causal: every query sees key 0 in the first tile, so m is finite.
+    if (__ballot(mt > m_run + 8.f) != 0) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = (WIN && m_new == -INFINITY) ? 0.f : exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] *= alpha;
+      m_run = m_new;
+    }
+    const float ref = (WIN && m_run == -INFINITY) ? 0.f : m_run;
+    float ls = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], a.sl2, -ref));
+        s[kb][r] = p;
+        ls += p;
+      }
+    l_run += ls;
 #pragma unroll
     for (int mm = 0; mm < 4; ++mm) {
-      const bf16x8 p0 = frag_regs<bf16>(s[0][mm >> 1], (mm & 1) * 8);
-      const bf16x8 p1 = frag_regs<bf16>(s[1][mm >> 1], (mm & 1) * 8);
+      const bf16x8 p0 = frag_regs<bf16>(s[mm >> 1], (mm & 1) * 8);
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const bf16x8 vf = frag_vt_at(vt_, vo, mm, db);
-        o[0][db] = MM::mma(vf, p0, o[0][db]);
-        o[1][db] = MM::mma(vf, p1, o[1][db]);
-      }
+      for (int db = 0; db < 4; ++db) o[db] = MM::mma(frag_vt_at(vt_, vo, mm, db), p0, o[db]);
     }
   }
   float mx = 0.f;
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int q = qw0 + qb * 32 + (lane & 31);
-    const float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 32, 64);
-    if (q < a.T) {
-      mx = fmaxf(mx, store_acc_row<bf16>(static_cast<bf16*>(a.o) + ((long)b * a.T + q) * a.C + head * HD, o[qb],
-                                         1.f / l_tot, lane));
-      if (h == 0) a.lse[(long)bh * a.T + q] = m_run[qb] + log2f(l_tot);
-    }
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  if (q < a.T) {
+    mx = store_acc_row<bf16>(static_cast<bf16*>(a.o) + ((long)b * a.T + q) * a.C + head * HD, o, 1.f / l_tot, lane);
+    if (h == 0) a.lse[(long)bh * a.T + q] = m_run + log2f(l_tot);
   }
   if (a.amax_o) amax_publish<bf16>(a.amax_o, mx);
 }
@@ -853,7 +852,6 @@ __device__ __forceinline__ void issue_vec(char* dst, i32x4 rv, int r0, int lane)
   const uint32_t o = lane < 16 ? (uint32_t)((r0 + lane * 4) * 4) : 0xffffffffu;
   raw_buffer_load_lds(rv, (lds_u32*)dst, 16, (int)o, 0, 0, 0);
 }
-typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) const f32x4 lds_f32x4;
 
 // ---- row layout of a wave's 128 x 32 accumulator (backward kernels) ----------

@@ -57,7 +57,7 @@ void attn_fwd(const AttnArgs& a, bool bf16, hipStream_t st) {
     // the windowed instance only when the window is shorter than the sequence
     auto kern = a.W < a.T ? attn_fwd_bf16_kernel<true> : attn_fwd_bf16_kernel<false>;
     allow_lds(reinterpret_cast<const void*>(kern), fa::LDS);
-    hipLaunchKernelGGL(kern, dim3(tiles(a.T, fa::QWG) * a.B * a.H), dim3(256), fa::LDS, st, a);
+    hipLaunchKernelGGL(kern, dim3(tiles(a.T, fa::QWG) * a.B * a.H), dim3(512), fa::LDS, st, a);
   } else {
     allow_lds(reinterpret_cast<const void*>(attn_fwd_kernel<float>), attn_fwd_lds<float>());
     hipLaunchKernelGGL(attn_fwd_kernel<float>, dim3(tiles(a.T, 128) * a.B * a.H), dim3(256), attn_fwd_lds<float>(),
