@@ -169,6 +169,49 @@ def _ptr(t):
     return t.data_ptr()
 
 
+_DT = {"bf16": "torch.bfloat16", "f32": "torch.float32", "i32": "torch.int32"}
+
+
+def _arg(t, name: str, where: str, kind=None, numel: int = 0, nbytes: int = 0):
+    """Device pointer of argument `name`.  A torch tensor must be dense
+    (contiguous), of element type `kind` ('bf16', 'f32', 'i32', or None for a
+    byte buffer of any type), hold at least `numel` elements (or `nbytes`
+    bytes) and live on the GPU; otherwise BlkError(BLK_EINVAL) is raised
+    before the library is called.  Plain integers (raw device addresses) and
+    None pass through unchecked."""
+    if t is None or isinstance(t, int):
+        return t
+    bad = None
+    if kind is not None and str(t.dtype) != _DT[kind]:
+        bad = f"dtype {t.dtype}, expected {_DT[kind]}"
+    elif not t.is_contiguous():
+        bad = "not contiguous"
+    elif t.numel() < numel:
+        bad = f"{t.numel()} elements, expected at least {numel}"
+    elif t.numel() * t.element_size() < nbytes:
+        bad = f"{t.numel() * t.element_size()} bytes, expected at least {nbytes}"
+    elif t.device.type != "cuda":
+        bad = f"on {t.device}, expected a GPU tensor"
+    if bad:
+        raise BlkError(BLK_EINVAL, f"{where}: argument {name}: {bad}")
+    return t.data_ptr()
+
+
+def _kind(dtype: int):
+    return "bf16" if dtype == BLK_BF16 else ("f32" if dtype == BLK_F32 else None)
+
+
+def _qkv_width(C: int, H: int, n_kv_head: int) -> int:
+    return C + 2 * 128 * (n_kv_head or H)
+
+
+def _weights(cfg, where, w_qkv, w_o, w_fc, w_proj, kind, prefix=""):
+    C, F = cfg.C, cfg.F
+    return (_arg(w_qkv, prefix + "w_qkv", where, kind, _qkv_width(C, cfg.H, cfg.n_kv_head) * C),
+            _arg(w_o, prefix + "w_o", where, kind, C * C), _arg(w_fc, prefix + "w_fc", where, kind, F * C),
+            _arg(w_proj, prefix + "w_proj", where, kind, C * F))
+
+
 def _nbytes(t, given):
     if given is not None:
         return given
@@ -213,28 +256,37 @@ def _check(code, where, raise_on_error):
 
 def block_fwd(cfg: BlockConfig, x, w_qkv, w_o, w_fc, w_proj, y, saved=None, scratch=None, *,
               saved_bytes=None, scratch_bytes=None, stream=None, raise_on_error=True) -> int:
-    code = library().block_fwd(ctypes.byref(cfg.c()), _ptr(x), _ptr(w_qkv), _ptr(w_o), _ptr(w_fc), _ptr(w_proj),
-                               _ptr(y), _ptr(saved), _nbytes(saved, saved_bytes), _ptr(scratch),
-                               _nbytes(scratch, scratch_bytes), _stream(stream))
-    return _check(code, "block_fwd", raise_on_error)
+    w, k, n = "block_fwd", _kind(cfg.dtype), cfg.B * cfg.T * cfg.C
+    px, py = _arg(x, "x", w, k, n), _arg(y, "y", w, k, n)
+    W = _weights(cfg, w, w_qkv, w_o, w_fc, w_proj, k)
+    code = library().block_fwd(ctypes.byref(cfg.c()), px, *W, py, _arg(saved, "saved", w), _nbytes(saved, saved_bytes),
+                               _arg(scratch, "scratch", w), _nbytes(scratch, scratch_bytes), _stream(stream))
+    return _check(code, w, raise_on_error)
 
 
 def block_bwd(cfg: BlockConfig, dy, x, w_qkv, w_o, w_fc, w_proj, saved, dx, dw_qkv, dw_o, dw_fc, dw_proj,
               accumulate=0, scratch=None, *, saved_bytes=None, scratch_bytes=None, stream=None,
               raise_on_error=True) -> int:
-    code = library().block_bwd(ctypes.byref(cfg.c()), _ptr(dy), _ptr(x), _ptr(w_qkv), _ptr(w_o), _ptr(w_fc),
-                               _ptr(w_proj), _ptr(saved), _nbytes(saved, saved_bytes), _ptr(dx), _ptr(dw_qkv),
-                               _ptr(dw_o), _ptr(dw_fc), _ptr(dw_proj), int(accumulate), _ptr(scratch),
+    w, k, n = "block_bwd", _kind(cfg.dtype), cfg.B * cfg.T * cfg.C
+    pdy, px, pdx = _arg(dy, "dy", w, k, n), _arg(x, "x", w, k, n), _arg(dx, "dx", w, k, n)
+    W = _weights(cfg, w, w_qkv, w_o, w_fc, w_proj, k)
+    dW = _weights(cfg, w, dw_qkv, dw_o, dw_fc, dw_proj, "f32", prefix="d")
+    code = library().block_bwd(ctypes.byref(cfg.c()), pdy, px, *W, _arg(saved, "saved", w),
+                               _nbytes(saved, saved_bytes), pdx, *dW, int(accumulate), _arg(scratch, "scratch", w),
                                _nbytes(scratch, scratch_bytes), _stream(stream))
-    return _check(code, "block_bwd", raise_on_error)
+    return _check(code, w, raise_on_error)
 
 
 def decode_step(cfg: DecodeConfig, x, w_qkv, w_o, w_fc, w_proj, k_cache, v_cache, cache_len, y, scratch=None, *,
                 scratch_bytes=None, stream=None, raise_on_error=True) -> int:
-    code = library().decode_step(ctypes.byref(cfg.c()), _ptr(x), _ptr(w_qkv), _ptr(w_o), _ptr(w_fc), _ptr(w_proj),
-                                 _ptr(k_cache), _ptr(v_cache), _ptr(cache_len), _ptr(y), _ptr(scratch),
+    w, k = "decode_step", _kind(cfg.dtype)
+    ncache = cfg.B * (cfg.n_kv_head or cfg.H) * cfg.S_max * 128
+    args = (_arg(x, "x", w, k, cfg.B * cfg.C), *_weights(cfg, w, w_qkv, w_o, w_fc, w_proj, k),
+            _arg(k_cache, "k_cache", w, k, ncache), _arg(v_cache, "v_cache", w, k, ncache),
+            _arg(cache_len, "cache_len", w, "i32", cfg.B), _arg(y, "y", w, k, cfg.B * cfg.C))
+    code = library().decode_step(ctypes.byref(cfg.c()), *args, _arg(scratch, "scratch", w),
                                  _nbytes(scratch, scratch_bytes), _stream(stream))
-    return _check(code, "decode_step", raise_on_error)
+    return _check(code, w, raise_on_error)
 
 
 def head_scratch_bytes(cfg: HeadConfig) -> int:
@@ -243,29 +295,41 @@ def head_scratch_bytes(cfg: HeadConfig) -> int:
 
 def head_loss_fwd(cfg: HeadConfig, x, w_lm, targets, loss, lse, scratch=None, *, scratch_bytes=None, stream=None,
                   raise_on_error=True) -> int:
-    code = library().head_loss_fwd(ctypes.byref(cfg.c()), _ptr(x), _ptr(w_lm), _ptr(targets), _ptr(loss), _ptr(lse),
-                                   _ptr(scratch), _nbytes(scratch, scratch_bytes), _stream(stream))
-    return _check(code, "head_loss_fwd", raise_on_error)
+    w, k = "head_loss_fwd", _kind(cfg.dtype)
+    args = (_arg(x, "x", w, k, cfg.N * cfg.C), _arg(w_lm, "w_lm", w, k, cfg.V * cfg.C),
+            _arg(targets, "targets", w, "i32", cfg.N), _arg(loss, "loss", w, "f32", 1), _arg(lse, "lse", w, "f32", cfg.N))
+    code = library().head_loss_fwd(ctypes.byref(cfg.c()), *args, _arg(scratch, "scratch", w),
+                                   _nbytes(scratch, scratch_bytes), _stream(stream))
+    return _check(code, w, raise_on_error)
 
 
 def head_loss_bwd(cfg: HeadConfig, x, w_lm, targets, lse, dloss: float, dx, dw_lm, accumulate=0, scratch=None, *,
                   scratch_bytes=None, stream=None, raise_on_error=True) -> int:
-    code = library().head_loss_bwd(ctypes.byref(cfg.c()), _ptr(x), _ptr(w_lm), _ptr(targets), _ptr(lse),
-                                   ctypes.c_float(dloss), _ptr(dx), _ptr(dw_lm), int(accumulate), _ptr(scratch),
-                                   _nbytes(scratch, scratch_bytes), _stream(stream))
-    return _check(code, "head_loss_bwd", raise_on_error)
+    w, k = "head_loss_bwd", _kind(cfg.dtype)
+    args = (_arg(x, "x", w, k, cfg.N * cfg.C), _arg(w_lm, "w_lm", w, k, cfg.V * cfg.C),
+            _arg(targets, "targets", w, "i32", cfg.N), _arg(lse, "lse", w, "f32", cfg.N))
+    code = library().head_loss_bwd(ctypes.byref(cfg.c()), *args, ctypes.c_float(dloss),
+                                   _arg(dx, "dx", w, k, cfg.N * cfg.C), _arg(dw_lm, "dw_lm", w, "f32", cfg.V * cfg.C),
+                                   int(accumulate), _arg(scratch, "scratch", w), _nbytes(scratch, scratch_bytes),
+                                   _stream(stream))
+    return _check(code, w, raise_on_error)
 
 
 def block_fp8_quantize(x, n: int, codes, amax, *, stream=None, raise_on_error=True) -> int:
-    code = library().block_fp8_quantize(_ptr(x), int(n), _ptr(codes), _ptr(amax), _stream(stream))
-    return _check(code, "block_fp8_quantize", raise_on_error)
+    w = "block_fp8_quantize"
+    code = library().block_fp8_quantize(_arg(x, "x", w, "bf16", int(n)), int(n), _arg(codes, "codes", w, nbytes=int(n)),
+                                        _arg(amax, "amax", w, nbytes=4), _stream(stream))
+    return _check(code, w, raise_on_error)
 
 
 def block_fp8_quantize_2d(x, rows: int, cols: int, codes, codes_t, ldt: int, amax, *, stream=None,
                           raise_on_error=True) -> int:
-    code = library().block_fp8_quantize_2d(_ptr(x), int(rows), int(cols), _ptr(codes), _ptr(codes_t), int(ldt),
-                                           _ptr(amax), _stream(stream))
-    return _check(code, "block_fp8_quantize_2d", raise_on_error)
+    w = "block_fp8_quantize_2d"
+    code = library().block_fp8_quantize_2d(_arg(x, "x", w, "bf16", rows * cols), int(rows), int(cols),
+                                           _arg(codes, "codes", w, nbytes=rows * cols),
+                                           _arg(codes_t, "codes_t", w, nbytes=cols * ldt), int(ldt),
+                                           _arg(amax, "amax", w, nbytes=4), _stream(stream))
+    return _check(code, w, raise_on_error)
 
 
 def block_timing_enable(on: bool) -> None:

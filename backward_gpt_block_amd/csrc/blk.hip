@@ -178,6 +178,28 @@ template <typename T> BwdScratch<T> carve_bwd(const blk_cfg& c, void* p) {
 
 size_t elt_size(const blk_cfg& c) { return c.dtype == BLK_BF16 ? 2 : 4; }
 
+// Weight gradients run on the four-wave GEMM body when the eight-wave one
+// does not apply: always in float32, and when the token count is not a
+// multiple of the eight-wave body's k-step (bf16 64 tokens, E4M3 128).  The
+// four-wave body forms 32-bit byte offsets from each operand's base, so
+// every operand it reads must stay below 4 GiB.
+bool four_wave_wgrad(const blk_cfg& c) {
+  const long N = (long)c.B * c.T;
+  if (c.dtype != BLK_BF16) return true;
+  if (c.gemm == BLK_GEMM_FP8_E4M3) return N % GemmTile<fp8e4>::BK != 0;
+  return N % GemmTile<bf16>::BK != 0;
+}
+
+// Bytes of the largest weight-gradient operand: [N, F] tokens x MLP width
+// (F = 4C is at least the fused projection's C + 256G); the fp8 mode reads
+// transposed E4M3 copies [F, N rounded up to 64].
+long wgrad_operand_bytes(const blk_cfg& c) {
+  const long N = (long)c.B * c.T;
+  const long wide = std::max<long>(c.F, qkv_width(c));
+  if (c.gemm == BLK_GEMM_FP8_E4M3) return wide * pad64(N);
+  return wide * N * (long)elt_size(c);
+}
+
 int check_cfg(const blk_cfg* c) {
   if (!c) return BLK_EINVAL;
   if (c->B < 1 || c->T < 1 || c->H < 1 || c->D != 128 || c->C != c->H * c->D || c->F != 4 * c->C) return BLK_EINVAL;
@@ -190,6 +212,7 @@ int check_cfg(const blk_cfg* c) {
   // row kernels keep a row in registers: 8 chunks of 16 bytes per lane
   if ((long)c->C * (c->dtype == BLK_BF16 ? 2 : 4) > 8L * 64 * 16) return BLK_EUNSUPPORTED;
   if ((long)c->B * c->T * qkv_width(*c) >= (1L << 31)) return BLK_EUNSUPPORTED;
+  if (four_wave_wgrad(*c) && wgrad_operand_bytes(*c) >= (1L << 32)) return BLK_EUNSUPPORTED;
   return BLK_OK;
 }
 

@@ -103,6 +103,30 @@ def test_fwd_argument_errors(lib):
     assert _fwd(_cfg(n_kv_head=3)) == bl.binding.BLK_EINVAL     # 10 query heads are not split in groups of 3
 
 
+def test_four_wave_weight_gradient_operand_limit(lib):
+    # weight gradients that run on the four-wave GEMM body (float32; bf16
+    # token counts not a multiple of 64; E4M3 token counts not a multiple of
+    # 128) address operands with 32-bit byte offsets: a [N, F] operand (or
+    # the fp8 mode's transposed [F, N rounded up to 64] codes) of 4 GiB or
+    # more is refused before any launch; the eight-wave body has no limit
+    E = bl.binding
+    f32 = lambda T: _cfg(B=1, T=T, dtype=bl.BLK_F32)
+    assert bl.block_saved_bytes(f32(209715)) > 0                 # 209715 * 5120 * 4 < 2^32
+    assert bl.block_saved_bytes(f32(209716)) == 0
+    assert _fwd(f32(209716)) == E.BLK_EUNSUPPORTED
+    assert _bwd(f32(209716)) == E.BLK_EUNSUPPORTED
+    bf = lambda T: _cfg(B=1, T=T)
+    assert bl.block_saved_bytes(bf(419430)) > 0                  # ragged, 419430 * 5120 * 2 < 2^32
+    assert bl.block_saved_bytes(bf(419431)) == 0
+    assert _fwd(bf(419431)) == E.BLK_EUNSUPPORTED
+    assert bl.block_saved_bytes(bf(419456)) > 0                  # a multiple of 64: eight-wave body
+    f8 = lambda T: _cfg(B=1, T=T, gemm=bl.BLK_GEMM_FP8_E4M3, n_kv_head=1)
+    assert bl.block_saved_bytes(f8(838848)) > 0                  # 838848 * 5120 < 2^32
+    assert bl.block_saved_bytes(f8(838850)) == 0                 # padded to 838912 tokens
+    assert _bwd(f8(838850)) == E.BLK_EUNSUPPORTED
+    assert bl.block_saved_bytes(f8(838912)) > 0                  # a multiple of 128: eight-wave body
+
+
 def test_bwd_argument_errors(lib):
     c = _cfg()
     assert _bwd(c, saved=None) == bl.binding.BLK_EINVAL
@@ -229,3 +253,35 @@ def test_head_sizes_and_argument_errors(lib):
     assert bwd(c, nb=4096) == E.BLK_ENOSPC
     # ragged token counts with a weight gradient past 32-bit offsets
     assert bl.head_scratch_bytes(_hcfg(N=65537)) == 0
+
+
+def test_binding_rejects_bad_tensors(lib):
+    # the binding checks each tensor's element type, density, size and
+    # device before calling the library (one host tensor per call, the other
+    # arguments raw addresses; every check runs before the device check,
+    # which refuses a host tensor last)
+    import torch
+    E = bl.binding
+    c = bl.BlockConfig(B=1, T=8, C=128, H=1, F=512)
+    bf = lambda n: torch.zeros(n, dtype=torch.bfloat16)
+
+    def fwd_err(**kw):
+        a = dict(x=A, w_qkv=A, w_o=A, w_fc=A, w_proj=A, y=A + 0x100)
+        a.update(kw)
+        with pytest.raises(E.BlkError) as e:
+            bl.block_fwd(c, a["x"], a["w_qkv"], a["w_o"], a["w_fc"], a["w_proj"], a["y"], None, A)
+        assert e.value.code == E.BLK_EINVAL
+        return str(e.value)
+
+    assert "dtype" in fwd_err(x=torch.zeros(8 * 128, dtype=torch.float32))
+    assert "elements" in fwd_err(y=bf(8 * 128 - 1))
+    assert "contiguous" in fwd_err(x=bf(8 * 256)[::2])
+    assert "w_fc" in fwd_err(w_fc=bf(512 * 128 - 8))
+    assert "GPU" in fwd_err(w_qkv=bf(384 * 128))      # right type and size, but host memory
+    with pytest.raises(E.BlkError, match="dw_proj"):
+        bl.block_bwd(c, A, A, A, A, A, A, A, A, A, A, A, bf(128 * 512), 0, A)   # weight gradients are float32
+    d = bl.DecodeConfig(B=2, C=128, H=1, F=512, S_max=16)
+    with pytest.raises(E.BlkError, match="cache_len"):
+        bl.decode_step(d, A, A, A, A, A, A, A + 0x100, torch.zeros(2, dtype=torch.int64), A, A, scratch_bytes=1 << 30)
+    with pytest.raises(E.BlkError, match="amax"):
+        bl.block_fp8_quantize(A, 64, A, torch.zeros(1, dtype=torch.uint8))

@@ -10,20 +10,24 @@
   oracle's own (the recipe's rounding error, 0.05-0.10 for the weight
   gradients here), within 15%: the kernels add no error of their own.
 
-Exception, at the d26 width only: dW_qkv and dW_o sit at the end of a chain
-of eight quantisations, where a difference of one bf16 rounding upstream
-moves a growing share of later E4M3 codes to the neighbouring code.  Two
-exact emulations that differ only in the precision of their code decisions
-(float64 against bf16) already differ there by 6.1% and 5.5% relative (one
-sequence of 1024 tokens at width 1664), so
-the fp8 result is not defined to 6e-2 at those two outputs: they are held to
-0.10 against the fp8 oracle, beside the accuracy check above."""
+The gates of gpu_util.compare apply to every output: Frobenius error <= 6e-2
+against the fp8 oracle, max|err|/max|ref| <= 6e-2 for y and dx and <= 0.12
+for the weight gradients, each row of y and dx within 5x.  A weight-gradient
+element is a sum over the tokens of products of E4M3 codes, and the
+attention kernels' own bf16 roundings (of P and dS, which the oracle does
+not take) move a share of the downstream codes to a neighbouring code: at a
+few dozen tokens the largest element error sits at about twice the
+Frobenius error.  Against
+the unquantised block the recipe itself (per-tensor E4M3 on all three GEMMs
+of every linear layer) does not reach 6e-2 for the deepest weight gradients
+at the d26 width; those distances are printed, and held to the fp8 oracle's
+own distance by the ratio check."""
 import numpy as np
 import pytest
 
 from blockinputs import WORKLOADS, BlockShape, make_block_inputs, round_to
 
-from gpu_util import TOL, GpuBlock, compare, note, oracle_step, rel_err, to_dev
+from gpu_util import TOL, GpuBlock, compare, max_err, note, oracle_step, poison_, rel_err, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -40,8 +44,8 @@ def test_quantizer_bit_exact():
             x[:8] = [0.0, -0.0, 1e-30, -1e-30, 2.0 ** -20, 448.0, -448.0, 3.0]
             x = round_to(x, "bf16")
         xd = to_dev(x, "bf16")
-        codes = torch.empty(n, dtype=torch.uint8, device="cuda:0")
-        amax = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+        codes = poison_(torch.empty(n, dtype=torch.uint8, device="cuda:0"))
+        amax = poison_(torch.empty(1, dtype=torch.int32, device="cuda:0"))
         bl.block_fp8_quantize(xd, n, codes, amax)
         torch.cuda.synchronize()
         want, s = fp8.quantize_tensor(x)
@@ -53,10 +57,9 @@ def test_quantizer_bit_exact():
 
 
 ACCURACY_RATIO = 1.15
-DEEP_TOL = 0.10
 
 
-def _fp8_parity(sh: BlockShape, seed=0, keep=None, deep=()):
+def _fp8_parity(sh: BlockShape, seed=0, keep=None):
     from oracle import fp8_block
     note(f"fp8 block B={sh.B} T={sh.T} C={sh.C} keep={keep} seed={seed}")
     inp = make_block_inputs(sh, seed=seed)
@@ -75,17 +78,15 @@ def _fp8_parity(sh: BlockShape, seed=0, keep=None, deep=()):
                                   H=sh.H, eps=sh.eps, rope_base=sh.rope_base,
                                   batch=None if keep is None else list(keep), log=note, window=sh.window or None,
                                   n_kv_head=sh.n_kv_head or None)
-    keys = [k for k in emu if k not in deep]
-    errs = compare(res, emu, TOL["fp8"], keys=keys)
-    for k in deep:
-        errs[k] = rel_err(res[k], emu[k])
-        print(f"  {k} vs fp8 oracle {errs[k]:.2e} (held to {DEEP_TOL})", flush=True)
-        assert errs[k] <= DEEP_TOL, (k, errs[k])
+    errs = compare(res, emu, TOL["fp8"], keys=list(emu),
+                   max_tol={k: 2 * TOL["fp8"] for k in ("dw_qkv", "dw_o", "dw_fc", "dw_proj")})
     ref = oracle_step(sh, inp, batch=None if keep is None else list(keep))
     gpu_acc = {k: rel_err(res[k], ref[k]) for k in ref}
     emu_acc = {k: rel_err(emu[k], ref[k]) for k in ref}
     print("  distance from the unquantised block, GPU / fp8 oracle: "
           + ", ".join(f"{k}={gpu_acc[k]:.2e}/{emu_acc[k]:.2e}" for k in ref), flush=True)
+    print("  max|err|/max|ref| from the unquantised block, GPU: "
+          + ", ".join(f"{k}={max_err(res[k], ref[k]):.2e}" for k in ref), flush=True)
     for k in ref:
         assert gpu_acc[k] <= ACCURACY_RATIO * emu_acc[k] + 1e-3, (k, gpu_acc[k], emu_acc[k])
     return errs
@@ -104,7 +105,7 @@ def test_fp8_block_window():
 def test_d26_fp8_full_size_sampled():
     # the oracle's forward pass over all 16 sequences (for the per-tensor
     # scales) takes a minute or two of host time
-    _fp8_parity(WORKLOADS["d26_fp8"], keep=(0, 15), deep=("dw_qkv", "dw_o"))
+    _fp8_parity(WORKLOADS["d26_fp8"], keep=(0, 15))
 
 
 def test_fp8_block_gqa():
@@ -131,7 +132,7 @@ def test_quantizer_2d_transposed_bit_exact(rows, cols, ldt):
     xd = to_dev(x, "bf16")
     codes = torch.full((rows, cols), 0x55, dtype=torch.uint8, device="cuda:0")
     codes_t = torch.full((cols, ldt), 0x55, dtype=torch.uint8, device="cuda:0")
-    amax = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    amax = poison_(torch.empty(1, dtype=torch.int32, device="cuda:0"))
     bl.block_fp8_quantize_2d(xd, rows, cols, codes, codes_t, ldt, amax)
     torch.cuda.synchronize()
     want, _ = fp8.quantize_tensor(x)

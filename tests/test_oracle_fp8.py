@@ -99,7 +99,7 @@ def test_fp8_block_without_rounding_is_the_exact_block():
     from oracle import fp8_block
     x, W, dy = _small_block(3)
     ident = lambda t, amax=None: np.asarray(t, dtype=np.float64)
-    got = fp8_block.block_fwd_bwd(x, *W, dy, H=2, quant=ident)
+    got = fp8_block.block_fwd_bwd(x, *W, dy, H=2, quant=ident, store=ident)
     ref = _exact(x, W, dy, 2)
     for k in ref:
         assert np.allclose(got[k], ref[k], rtol=1e-12, atol=1e-12), k
@@ -122,6 +122,38 @@ def test_fp8_block_rounds_every_gemm_operand():
     assert sorted(seen) == sorted([(3 * C, C), (C, C), (4 * C, C), (C, 4 * C),
                                    act, act, act, (1, 5, 4 * C),            # h1, o, h2, a
                                    act, (1, 5, 4 * C), act, (1, 5, 3 * C)])  # dy, du, dy1, dqkv
+
+
+def test_fp8_block_rounds_every_stored_intermediate():
+    # the bf16 pipeline's stored intermediates, each rounded once: h1, q, k,
+    # v (per head), o, y1, h2, a; du, dh2, dy1, dO, dqkv, dh1
+    from oracle import fp8_block
+    x, W, dy = _small_block(6, B=1, T=5)
+    seen = []
+
+    def rec(t):
+        seen.append(np.shape(t))
+        return np.asarray(t, dtype=np.float64)
+
+    fp8_block.block_fwd_bwd(x, *W, dy, H=2, store=rec)
+    C = x.shape[-1]
+    act, head = (1, 5, C), (1, 2, 5, C // 2)
+    assert sorted(seen) == sorted([act, head, head, head, act, act, act, (1, 5, 4 * C),     # h1 q k v o y1 h2 a
+                                   (1, 5, 4 * C), act, act, act, (1, 5, 3 * C), act])      # du dh2 dy1 dO dqkv dh1
+
+
+def test_fp8_block_stored_rounding_moves_codes_downstream():
+    # one bf16 rounding of a stored intermediate moves E4M3 codes downstream:
+    # with and without the store rounding the weight gradients differ by far
+    # more than a bf16 rounding (2^-9), and y by a few percent at most
+    from oracle import fp8_block
+    x, W, dy = _small_block(7, B=2, T=64)
+    ident = lambda t: np.asarray(t, dtype=np.float64)
+    a = fp8_block.block_fwd_bwd(x, *W, dy, H=2)
+    b = fp8_block.block_fwd_bwd(x, *W, dy, H=2, store=ident)
+    rel = {k: np.linalg.norm(a[k] - b[k]) / np.linalg.norm(b[k]) for k in a}
+    assert rel["y"] < 5e-2, rel
+    assert min(rel[k] for k in ("dw_qkv", "dw_o", "dw_fc", "dw_proj")) > 4 * 2.0 ** -9, rel
 
 
 def test_fp8_emulating_block_tracks_exact_block():
