@@ -22,6 +22,13 @@
 
 using namespace blk;
 
+// decode_step_noalloc's temporaries live in this array: each GPU the library
+// runs on holds one copy of it, from the load of the library's code to the
+// end of the process.  Host code never names it: its device address (per
+// device) comes from hipGetSymbolAddress, taken once per device on the
+// entry point's first call there, with that device current.
+static __device__ __align__(256) char noalloc_scratch[BLK_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 // ---------------------------------------------------------------- layout
@@ -762,6 +769,100 @@ void dec_gemm(const char* name, const bf16* A, int M, const bf16* W, int N, int 
                      0, st, A, M, W, N, K, sp.cps, part);
 }
 
+// Arguments of a decode step other than its workspace.
+int check_decode_args(const blk_dcfg* cfg, const void* x, const void* w_qkv, const void* w_o, const void* w_fc,
+                      const void* w_proj, const void* k_cache, const void* v_cache, const int32_t* cache_len,
+                      const void* y) {
+  if (int e = check_dcfg(cfg)) return e;
+  for (const void* p : {x, w_qkv, w_o, w_fc, w_proj, k_cache, v_cache, y})
+    if (!p) return BLK_EINVAL;
+  if (!cache_len || k_cache == v_cache) return BLK_EINVAL;
+  for (const void* p : {x, w_qkv, w_o, w_fc, w_proj, k_cache, v_cache, y})
+    if (!aligned(p)) return BLK_EALIGN;
+  if (reinterpret_cast<uintptr_t>(cache_len) & 3) return BLK_EALIGN;
+  return BLK_OK;
+}
+
+// The launch sequence of one decode step, its temporaries carved from
+// `scratch` (decode_scratch_bytes(cfg) bytes of device memory).
+int decode_run(const blk_dcfg& c, const void* x, const void* w_qkv, const void* w_o, const void* w_fc,
+               const void* w_proj, void* k_cache, void* v_cache, const int32_t* cache_len, void* y, void* scratch,
+               hipStream_t st) {
+  const DecScratch d = carve_dec(c, scratch);
+  hipGetLastError();
+  const int B = c.B, C = c.C, H = c.H, F = c.F;
+  const bf16* xb = static_cast<const bf16*>(x);
+  bf16* kc = static_cast<bf16*>(k_cache);
+  bf16* vc = static_cast<bf16*>(v_cache);
+  const int NS = (c.S_max + dec::KEYS - 1) / dec::KEYS;
+  {  // h1 = rmsnorm(x)
+    Timed t("dec_rmsnorm", st);
+    hipLaunchKernelGGL(dec::dec_rmsnorm_kernel, dim3(B), dim3(256), 0, st, xb, C, c.eps, d.h1);
+  }
+  const DecSplit sq = dec_split(B, (int)qkv_width(c), C);
+  dec_gemm("dec_gemm_qkv", d.h1, B, static_cast<const bf16*>(w_qkv), (int)qkv_width(c), C, sq, d.part, st);
+  {  // rotary + QK-norm at position cache_len[b]; k, v into the caches
+    Timed t("dec_qkv_epi", st);
+    hipLaunchKernelGGL(dec::dec_qkv_epi_kernel, dim3(H, B), dim3(192), 0, st, (const float*)d.part, sq.S, B, H,
+                       kv_heads(c), cache_len, c.S_max, c.eps, (double)c.rope_base, d.q, kc, vc);
+  }
+  const int dwin = c.window > 0 ? c.window : INT_MAX;
+  {  // attention of the new token over slots 0..cache_len[b] (the last W with a window)
+    Timed t("dec_attn", st);
+    const int G = kv_heads(c);
+    hipLaunchKernelGGL(G == H ? dec::dec_attn_kernel<false> : dec::dec_attn_kernel<true>, dim3(NS, G, B), dim3(256),
+                       dec::dec_attn_lds(H / G), st, (const float*)d.q, (const bf16*)kc, (const bf16*)vc, cache_len,
+                       H, G, c.S_max, NS, dwin, (float)(1.4426950408889634 / std::sqrt(128.0)), d.opart, d.ml);
+  }
+  {
+    Timed t("dec_combine", st);
+    hipLaunchKernelGGL(dec::dec_combine_kernel, dim3(H, B), dim3(128), 0, st, (const float*)d.opart,
+                       (const float2*)d.ml, cache_len, H, c.S_max, NS, dwin, d.o);
+  }
+  const DecSplit so = dec_split(B, C, C);
+  dec_gemm("dec_gemm_o", d.o, B, static_cast<const bf16*>(w_o), C, C, so, d.part, st);
+  {  // y1 = x + o W_o^T; h2 = rmsnorm(y1)
+    Timed t("dec_resid_norm", st);
+    hipLaunchKernelGGL(dec::dec_resid_norm_kernel, dim3(B), dim3(256), 0, st, (const float*)d.part, so.S, B, C, xb,
+                       c.eps, d.y1, d.h2);
+  }
+  const DecSplit sf = dec_split(B, F, C);
+  dec_gemm("dec_gemm_fc", d.h2, B, static_cast<const bf16*>(w_fc), F, C, sf, d.part, st);
+  {
+    Timed t("dec_relu2", st);
+    const long n = (long)B * F;
+    hipLaunchKernelGGL(dec::dec_relu2_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                       (const float*)d.part, sf.S, n, d.a);
+  }
+  const DecSplit sp = dec_split(B, C, F);
+  dec_gemm("dec_gemm_proj", d.a, B, static_cast<const bf16*>(w_proj), C, F, sp, d.part, st);
+  {
+    Timed t("dec_out", st);
+    const long n = (long)B * C;
+    hipLaunchKernelGGL(dec::dec_out_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                       (const float*)d.part, sp.S, n, (const float*)d.y1, static_cast<bf16*>(y));
+  }
+  return launch_status();
+}
+
+// ---------------------------------------------------------------- workspace without allocation
+constexpr int MAX_DEVICES = 64;
+std::mutex g_noalloc_mu;
+void* g_noalloc_ptr[MAX_DEVICES] = {};
+
+int noalloc_workspace(void** ws) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return BLK_ELAUNCH;
+  std::lock_guard<std::mutex> l(g_noalloc_mu);
+  if (!g_noalloc_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(noalloc_scratch)) != hipSuccess || !p) return BLK_ELAUNCH;
+    g_noalloc_ptr[dev] = p;
+  }
+  *ws = g_noalloc_ptr[dev];
+  return BLK_OK;
+}
+
 size_t saved_bytes(const blk_cfg& c) {
   return c.dtype == BLK_BF16 ? carve_saved<bf16>(c, nullptr).bytes : carve_saved<float>(c, nullptr).bytes;
 }
@@ -913,73 +1014,23 @@ size_t decode_scratch_bytes(const blk_dcfg* cfg) {
 int decode_step(const blk_dcfg* cfg, const void* x, const void* w_qkv, const void* w_o, const void* w_fc,
                 const void* w_proj, void* k_cache, void* v_cache, const int32_t* cache_len, void* y, void* scratch,
                 size_t scratch_bytes, void* stream) {
-  if (int e = check_dcfg(cfg)) return e;
-  const blk_dcfg& c = *cfg;
-  for (const void* p : {x, w_qkv, w_o, w_fc, w_proj, (const void*)k_cache, (const void*)v_cache, (const void*)y,
-                        (const void*)scratch})
-    if (!p) return BLK_EINVAL;
-  if (!cache_len || k_cache == v_cache) return BLK_EINVAL;
-  for (const void* p : {x, w_qkv, w_o, w_fc, w_proj, (const void*)k_cache, (const void*)v_cache, (const void*)y,
-                        (const void*)scratch})
-    if (!aligned(p)) return BLK_EALIGN;
-  if (reinterpret_cast<uintptr_t>(cache_len) & 3) return BLK_EALIGN;
-  const DecScratch d = carve_dec(c, scratch);
-  if (scratch_bytes < d.bytes) return BLK_ENOSPC;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  hipGetLastError();
-  const int B = c.B, C = c.C, H = c.H, F = c.F;
-  const bf16* xb = static_cast<const bf16*>(x);
-  bf16* kc = static_cast<bf16*>(k_cache);
-  bf16* vc = static_cast<bf16*>(v_cache);
-  const int NS = (c.S_max + dec::KEYS - 1) / dec::KEYS;
-  {  // h1 = rmsnorm(x)
-    Timed t("dec_rmsnorm", st);
-    hipLaunchKernelGGL(dec::dec_rmsnorm_kernel, dim3(B), dim3(256), 0, st, xb, C, c.eps, d.h1);
-  }
-  const DecSplit sq = dec_split(B, (int)qkv_width(c), C);
-  dec_gemm("dec_gemm_qkv", d.h1, B, static_cast<const bf16*>(w_qkv), (int)qkv_width(c), C, sq, d.part, st);
-  {  // rotary + QK-norm at position cache_len[b]; k, v into the caches
-    Timed t("dec_qkv_epi", st);
-    hipLaunchKernelGGL(dec::dec_qkv_epi_kernel, dim3(H, B), dim3(192), 0, st, (const float*)d.part, sq.S, B, H,
-                       kv_heads(c), cache_len, c.S_max, c.eps, (double)c.rope_base, d.q, kc, vc);
-  }
-  const int dwin = c.window > 0 ? c.window : INT_MAX;
-  {  // attention of the new token over slots 0..cache_len[b] (the last W with a window)
-    Timed t("dec_attn", st);
-    const int G = kv_heads(c);
-    hipLaunchKernelGGL(G == H ? dec::dec_attn_kernel<false> : dec::dec_attn_kernel<true>, dim3(NS, G, B), dim3(256),
-                       dec::dec_attn_lds(H / G), st, (const float*)d.q, (const bf16*)kc, (const bf16*)vc, cache_len,
-                       H, G, c.S_max, NS, dwin, (float)(1.4426950408889634 / std::sqrt(128.0)), d.opart, d.ml);
-  }
-  {
-    Timed t("dec_combine", st);
-    hipLaunchKernelGGL(dec::dec_combine_kernel, dim3(H, B), dim3(128), 0, st, (const float*)d.opart,
-                       (const float2*)d.ml, cache_len, H, c.S_max, NS, dwin, d.o);
-  }
-  const DecSplit so = dec_split(B, C, C);
-  dec_gemm("dec_gemm_o", d.o, B, static_cast<const bf16*>(w_o), C, C, so, d.part, st);
-  {  // y1 = x + o W_o^T; h2 = rmsnorm(y1)
-    Timed t("dec_resid_norm", st);
-    hipLaunchKernelGGL(dec::dec_resid_norm_kernel, dim3(B), dim3(256), 0, st, (const float*)d.part, so.S, B, C, xb,
-                       c.eps, d.y1, d.h2);
-  }
-  const DecSplit sf = dec_split(B, F, C);
-  dec_gemm("dec_gemm_fc", d.h2, B, static_cast<const bf16*>(w_fc), F, C, sf, d.part, st);
-  {
-    Timed t("dec_relu2", st);
-    const long n = (long)B * F;
-    hipLaunchKernelGGL(dec::dec_relu2_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                       (const float*)d.part, sf.S, n, d.a);
-  }
-  const DecSplit sp = dec_split(B, C, F);
-  dec_gemm("dec_gemm_proj", d.a, B, static_cast<const bf16*>(w_proj), C, F, sp, d.part, st);
-  {
-    Timed t("dec_out", st);
-    const long n = (long)B * C;
-    hipLaunchKernelGGL(dec::dec_out_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                       (const float*)d.part, sp.S, n, (const float*)d.y1, static_cast<bf16*>(y));
-  }
-  return launch_status();
+  if (int e = check_decode_args(cfg, x, w_qkv, w_o, w_fc, w_proj, k_cache, v_cache, cache_len, y)) return e;
+  if (!scratch) return BLK_EINVAL;
+  if (!aligned(scratch)) return BLK_EALIGN;
+  if (scratch_bytes < carve_dec(*cfg, nullptr).bytes) return BLK_ENOSPC;
+  return decode_run(*cfg, x, w_qkv, w_o, w_fc, w_proj, k_cache, v_cache, cache_len, y, scratch,
+                    static_cast<hipStream_t>(stream));
+}
+
+int decode_step_noalloc(const blk_dcfg* cfg, const void* x, const void* w_qkv, const void* w_o, const void* w_fc,
+                        const void* w_proj, void* k_cache, void* v_cache, const int32_t* cache_len, void* y,
+                        void* stream) {
+  if (int e = check_decode_args(cfg, x, w_qkv, w_o, w_fc, w_proj, k_cache, v_cache, cache_len, y)) return e;
+  if (carve_dec(*cfg, nullptr).bytes > BLK_NOALLOC_SCRATCH_BYTES) return BLK_ELIMIT;
+  void* ws = nullptr;
+  if (int e = noalloc_workspace(&ws)) return e;
+  return decode_run(*cfg, x, w_qkv, w_o, w_fc, w_proj, k_cache, v_cache, cache_len, y, ws,
+                    static_cast<hipStream_t>(stream));
 }
 
 int block_fp8_quantize(const void* x, size_t n, void* codes, uint32_t* amax, void* stream) {
@@ -1133,6 +1184,7 @@ const char* block_strerror(int code) {
     case BLK_ENOSPC: return "saved or scratch buffer too small";
     case BLK_EUNSUPPORTED: return "configuration not supported";
     case BLK_ELAUNCH: return "kernel launch failed";
+    case BLK_ELIMIT: return "workspace needed exceeds the library's static workspace (decode_step_noalloc)";
     default: return "unknown status";
   }
 }

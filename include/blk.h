@@ -25,7 +25,8 @@
  *   - Every data pointer is a DEVICE pointer, 16-byte aligned, to a dense
  *     row-major array; the caller allocates and owns every buffer.  The
  *     library allocates no memory, keeps no pointer after returning, and
- *     holds no state between calls (except the lazily loaded kernels).
+ *     holds no state between calls (except the lazily loaded kernels and
+ *     the static device workspace of decode_step_noalloc).
  *   - Weights are [out, in] and act as y = x W^T (the PyTorch Linear layout).
  *   - Element type of activations and weights: cfg->dtype (BLK_F32 or
  *     BLK_BF16).  Weight gradients are always float32.  Statistics, softmax
@@ -38,7 +39,12 @@
  *     enqueued.  Device faults surface at the caller's next synchronisation.
  *     No C++ exception crosses this interface.
  *   - Sizes: D must be 128, C == H*D, F == 4*C; B, T >= 1.  Any T is
- *     accepted (ragged tiles are masked inside the kernels).
+ *     accepted (ragged tiles are masked inside the kernels).  Limits
+ *     (BLK_EUNSUPPORTED): B*T*(C + 256*G) < 2^31 elements; and when a weight
+ *     gradient runs on the four-wave GEMM body (float32 always; bf16 when
+ *     B*T is not a multiple of 64; fp8 when it is not a multiple of 128),
+ *     its widest operand, B*T x max(F, C + 256*G) elements (fp8: the
+ *     transposed E4M3 copy, B*T rounded up to 64), stays below 4 GiB.
  */
 #ifndef BLK_H
 #define BLK_H
@@ -56,7 +62,9 @@ enum blk_status {
   BLK_EALIGN = 2,        /* a pointer is not 16-byte aligned                 */
   BLK_ENOSPC = 3,        /* saved/scratch buffer smaller than required       */
   BLK_EUNSUPPORTED = 4,  /* valid but not provided (e.g. fp8 with float32)   */
-  BLK_ELAUNCH = 5        /* a kernel launch failed (hipGetLastError)          */
+  BLK_ELAUNCH = 5,       /* a kernel launch failed (hipGetLastError)          */
+  BLK_ELIMIT = 6         /* the call needs more workspace than the library's
+                          * static workspace holds (decode_step_noalloc)      */
 };
 
 enum blk_dtype { BLK_F32 = 0, BLK_BF16 = 1 };
@@ -191,7 +199,8 @@ size_t decode_scratch_bytes(const blk_dcfg* cfg);
  * SFT and tool use, and in the launch thread on the same subject; the block
  * computed for the new row is the one described at the top of this file.
  *   x       [B,C]               new rows (bf16)
- *   k_cache, v_cache [B,H,S_max,D]  (bf16) keys after rotary and QK-norm,
+ *   k_cache, v_cache [B,G,S_max,D]  (bf16; G = n_kv_head, or H when 0) keys
+ *           after rotary and QK-norm,
  *           and values; slot p_b of each (b, h) is written here, slots
  *           0..p_b are attended, slots beyond p_b are neither read nor written
  *   cache_len [B] int32 DEVICE array, read only (the caller advances it);
@@ -208,6 +217,25 @@ int decode_step(const blk_dcfg* cfg, const void* x,
                 void* k_cache, void* v_cache, const int32_t* cache_len, void* y,
                 void* scratch, size_t scratch_bytes, void* stream);
 
+/* Bytes of the static workspace decode_step_noalloc uses on each device. */
+#define BLK_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* decode_step without a caller-supplied scratch buffer, for callers that
+ * cannot allocate device memory on the call path (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation).  Same
+ * arguments, results and errors as decode_step, with the temporaries in a
+ * static workspace of BLK_NOALLOC_SCRATCH_BYTES (32 MiB) that the library
+ * keeps on each device for the life of the process (its address is looked
+ * up on the first call on each device).  Returns BLK_ELIMIT, with nothing
+ * enqueued, when decode_scratch_bytes(cfg) exceeds that size (d20 with 64
+ * sequences and 2049 cache slots needs 10.8 MiB).  The call allocates
+ * nothing.  Every call on one GPU uses that GPU's single workspace: calls
+ * whose work overlaps on one GPU (other streams, other host threads) race
+ * and give wrong results; calls enqueued in order on one stream do not. */
+int decode_step_noalloc(const blk_dcfg* cfg, const void* x,
+                        const void* w_qkv, const void* w_o, const void* w_fc, const void* w_proj,
+                        void* k_cache, void* v_cache, const int32_t* cache_len, void* y, void* stream);
+
 /* The quantiser of the fp8 mode as a standalone call: amax = max |x| over
  * the n bf16 values at x (n a multiple of 8), written as float bits to the
  * device word *amax, and codes[i] = E4M3(x[i] * 448/amax) rounded to nearest
@@ -222,8 +250,9 @@ int block_fp8_quantize(const void* x, size_t n, void* codes, uint32_t* amax, voi
  * transposed copy codes_t[c][r] with leading dimension ldt (>= rows, a
  * multiple of 64), whose padding columns rows .. ldt-1 are written as 0.
  * (OCP 8-bit E4M3, per-tensor scale from the current amax: fp8 training as
- * the flicky.cc nanochat page's repository map and the 36kr/CSDN
- * leaderboard notes name it.)  rows in [1, 2^31), cols a positive multiple
+ * the flicky.cc nanochat page's repository map row for nanochat/fp8.py and
+ * the leaderboard row "d26 ... +fp8" of the pigsec.cn README mirror name
+ * it.)  rows in [1, 2^31), cols a positive multiple
  * of 64 below 2^31; device pointers 16-byte aligned (amax 4-byte aligned).
  * BLK_EINVAL for a NULL x, codes_t or amax, or a bad size; BLK_EALIGN for a
  * misaligned pointer. */

@@ -193,8 +193,23 @@ def test_fp8_quantize_2d_argument_errors(lib):
     assert call(amax=A + 0x302) == E.BLK_EALIGN
 
 
+def test_decode_noalloc_workspace_limit(lib):
+    # the static workspace holds the d20 decode workload; a configuration that
+    # needs more is refused before any launch, argument errors as decode_step
+    E = bl.binding
+    assert bl.decode_scratch_bytes(_dcfg()) <= E.BLK_NOALLOC_SCRATCH_BYTES
+    big = _dcfg(B=1024, S_max=8192)
+    assert bl.decode_scratch_bytes(big) > E.BLK_NOALLOC_SCRATCH_BYTES
+    call = lambda cfg, **kw: bl.decode_step_noalloc(cfg, kw.get("x", A), A, A, A, A, A + 0x100, kw.get("v", A + 0x200),
+                                                    A + 0x300, A + 0x400, stream=0, raise_on_error=False)
+    assert call(big) == E.BLK_ELIMIT
+    assert call(_dcfg(), x=None) == E.BLK_EINVAL
+    assert call(_dcfg(), v=A + 0x100) == E.BLK_EINVAL
+    assert call(_dcfg(dtype=bl.BLK_F32)) == E.BLK_EUNSUPPORTED
+
+
 def test_strerror(lib):
-    for code in range(6):
+    for code in range(7):
         assert isinstance(bl.block_strerror(code), str) and bl.block_strerror(code)
     assert "unknown" in bl.block_strerror(99)
 
