@@ -633,7 +633,7 @@ __device__ __forceinline__ void issue_kv(char* slot, i32x4 rs, int k0, long ldb,
       const int row = p >> 4, c = (p & 15) ^ sw(row);
       const uint32_t o = (uint32_t)((long)(k0 + row) * ldb + (t ? voff : koff) + c * 16);
       lds_u32* dst = (lds_u32*)(slot + t * TILE + __builtin_amdgcn_readfirstlane(base) * 16);
-      raw_buffer_load_lds(rs, dst, 16, (int)o, 0, 0, 0);
+      dma16(rs, dst, o);
     }
   }
 }
@@ -700,7 +700,7 @@ __device__ __forceinline__ void issue_kv8(char* slot, i32x4 rs, int k0, long ldb
       const int row = p >> 4, c = (p & 15) ^ sw(row);
       const uint32_t o = (uint32_t)((long)(k0 + row) * ldb + (t ? voff : koff) + c * 16);
       lds_u32* dst = (lds_u32*)(slot + t * TILE + __builtin_amdgcn_readfirstlane(base) * 16);
-      raw_buffer_load_lds(rs, dst, 16, (int)o, 0, 0, 0);
+      dma16(rs, dst, o);
     }
   }
 }
@@ -736,6 +736,10 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(AttnArgs a) {
 
   bf16x8 qf[8];
   frag_row_global<bf16>(qf, qkv + ((long)b * a.T + q) * a.LD + head * HD, q < a.T, lane);
+  // the q fragments have landed before any tile is in flight (a wait the
+  // compiler placed at their first use inside the loop would, with the
+  // ring's loads outstanding, drain the ring every tile)
+  wait_vm<0>();
   f32x16 o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -753,9 +757,9 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(AttnArgs a) {
   if (n > 1) issue_kv8(smem + SLOT, rs, (kt_lo + 1) * KT, ldb, koff, voff, wave, lane);
   for (int it = 0; it < n; ++it) {
     // tile it landed (own loads, then everyone's); slot of tile it-1 is free
-    if (it + 1 < n) __builtin_amdgcn_s_waitcnt(0x3f70 | 4);   // vmcnt(4): the next tile may stay in flight
-    else __builtin_amdgcn_s_waitcnt(0x3f70);                  // vmcnt(0)
-    __syncthreads();
+    if (it + 1 < n) wait_vm<4>();   // the next tile may stay in flight
+    else wait_vm<0>();
+    ring_barrier();
     if (it + 2 < n) issue_kv8(smem + ((it + 2) % NSLOT) * SLOT, rs, (kt_lo + it + 2) * KT, ldb, koff, voff, wave, lane);
     const lds_char* kt_ = (const lds_char*)smem + (it % NSLOT) * SLOT;
     const lds_char* vt_ = kt_ + TILE;
@@ -842,7 +846,7 @@ __device__ __forceinline__ void issue_tile(char* dst, i32x4 rs, int r0, long ldb
     const int p = base + lane;
     const int row = p >> 4, c = (p & 15) ^ sw(row);
     const uint32_t o = (uint32_t)((long)(r0 + row) * ldb + coff + c * 16);
-    raw_buffer_load_lds(rs, (lds_u32*)(dst + __builtin_amdgcn_readfirstlane(base) * 16), 16, (int)o, 0, 0, 0);
+    dma16(rs, (lds_u32*)(dst + base * 16), o);
   }
 }
 // 64 floats of a vector at index r0.. into dst[0..63] (one issue: lanes 0-15
@@ -850,7 +854,7 @@ __device__ __forceinline__ void issue_tile(char* dst, i32x4 rs, int r0, long ldb
 // dst[64..255], so dst must hold 1 KiB).
 __device__ __forceinline__ void issue_vec(char* dst, i32x4 rv, int r0, int lane) {
   const uint32_t o = lane < 16 ? (uint32_t)((r0 + lane * 4) * 4) : 0xffffffffu;
-  raw_buffer_load_lds(rv, (lds_u32*)dst, 16, (int)o, 0, 0, 0);
+  dma16(rv, (lds_u32*)dst, o);
 }
 typedef __attribute__((address_space(3))) const f32x4 lds_f32x4;
 
@@ -861,13 +865,15 @@ typedef __attribute__((address_space(3))) const f32x4 lds_f32x4;
 // rows one instruction writes fall in distinct chunks), and read back in
 // passes: pass i gives this lane row 4i + lane/16 and dims 8 (lane & 15) .. +7.
 __device__ __forceinline__ int stg_idx(int row, int d) { return row * 128 + ((((d >> 2) ^ row) & 31) << 2) + (d & 3); }
-__device__ __forceinline__ void stage_acc(float* stg, const f32x16* acc, float scale, int lane) {
+// (row: the staging row of this lane's column; lane & 31 unless permuted)
+__device__ __forceinline__ void stage_acc(float* stg, const f32x16* acc, float scale, int lane, int row = -1) {
+  if (row < 0) row = lane & 31;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
       const int d = db * 32 + acc_row(r, lane);
-      *reinterpret_cast<float2*>(stg + stg_idx(lane & 31, d)) = make_float2(acc[db][r] * scale, acc[db][r + 1] * scale);
+      *reinterpret_cast<float2*>(stg + stg_idx(row, d)) = make_float2(acc[db][r] * scale, acc[db][r + 1] * scale);
     }
 }
 __device__ __forceinline__ void unstage_row(const float* stg, int i, int lane, float* f) {
@@ -970,6 +976,13 @@ __device__ __forceinline__ float store_rows_qk(const float* stg, const QkRows& q
 // QK-norm and rotary backward of dK computed in that layout (a row's 128
 // values on 16 lanes).  Lane-per-row loads and stores, 32 rows per
 // instruction, made this boundary cost as much as six query tiles.
+//
+// DS: the kernel also stores the bf16 dS of every (query, key) pair it
+// computes into a.ds (layout in AttnArgs): each dS fragment the dK MFMAs take
+// (16 bytes per lane) is one store of 1 KiB, whole cache lines; a wave whose
+// keys all follow a query tile (the diagonal tile) stores zeros there, so
+// that every block is complete.
+template <bool DS>
 __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_bf16_kernel(AttnArgs a) {
   using namespace fa;
   typedef Mfma<bf16> MM;
@@ -983,20 +996,37 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_bf16_kernel(AttnArgs a) 
   const bf16* qkv = static_cast<const bf16*>(a.qkv);
   const int nqt_all = (a.T + QT - 1) / QT;
 
-  // unit of round j for this workgroup (>= units: none)
-  auto unit_of = [&](int j) {
-    const int i = (j & 1) ? (int)gridDim.x - 1 - (int)blockIdx.x : (int)blockIdx.x;
-    return j * (int)gridDim.x + i;
+  // The units form one queue (key tile major: longest first), or, with the
+  // grid and the (sequence, key/value head) pairs both multiples of the 8
+  // XCDs (workgroups are dealt to them round robin), one queue per XCD: XCD
+  // x takes the pairs x BG/8 .. (x+1) BG/8 - 1, pair by pair, each pair's
+  // units longest first, so that the Q and dO tiles the units of a pair all
+  // read are fetched into that XCD's L2 once.  Round j of a queue: its
+  // workgroups take the next entries, every other round in reverse order.
+  const int nku = (a.T + 127) / 128;
+  const bool xcd = gridDim.x % 8 == 0 && BG % 8 == 0;
+  const int qlen = xcd ? units / 8 : units;
+  const int per = xcd ? (int)gridDim.x / 8 : (int)gridDim.x;
+  const int wg = xcd ? (int)blockIdx.x / 8 : (int)blockIdx.x;
+  auto unit_of = [&](int j) {   // queue entry of round j for this workgroup (>= qlen: none)
+    const int i = (j & 1) ? per - 1 - wg : wg;
+    return j * per + i;
   };
   // a unit: key tile kt (first key tiles have the most queries), sequence b,
   // key/value head kvh; n iterations = R query heads x nq query tiles
   struct Unit {
     int kt, b, kvh, qt0, nq, n;
   };
-  auto make_unit = [&](int u) {
+  auto make_unit = [&](int e) {
     Unit p;
-    p.kt = u / BG;
-    const int bg = u % BG;
+    int bg;
+    if (xcd) {
+      bg = ((int)blockIdx.x % 8) * (BG / 8) + e / nku;
+      p.kt = e % nku;
+    } else {
+      p.kt = e / BG;
+      bg = e % BG;
+    }
     p.b = bg / a.G;
     p.kvh = bg % a.G;
     p.qt0 = (p.kt * 128) / QT;
@@ -1060,7 +1090,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_bf16_kernel(AttnArgs a) 
   };
 
   int j = 0;
-  if (unit_of(0) >= units) return;
+  if (unit_of(0) >= qlen) return;
   Unit cur = make_unit(unit_of(0));
   issue_kv_rows(cur);
   __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
@@ -1079,13 +1109,25 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_bf16_kernel(AttnArgs a) 
 #pragma unroll
       for (int r = 0; r < 16; ++r) { dk[i][r] = 0.f; dv[i][r] = 0.f; }
     for (int it = 0; it < n; ++it) {
-      if (it + 1 < n) {
-        if (wave == 0) __builtin_amdgcn_s_waitcnt(0x0f70 | 10);  // vmcnt(10): the next tile's 10 issues in flight
-        else __builtin_amdgcn_s_waitcnt(0x0f70 | 8);             // vmcnt(8)
+      // tile it landed: the operations issued after its loads may stay in
+      // flight, namely the next tile's loads (10 issues on wave 0, 8 on the
+      // others) and, with DS, the 4 dS stores of each of the two previous
+      // iterations (every iteration issues exactly 4)
+      const bool next = it + 1 < n;
+      if (!DS || it == 0) {
+        if (!next) wait_vm<0>();
+        else if (wave == 0) wait_vm<10>();
+        else wait_vm<8>();
+      } else if (it == 1) {
+        if (!next) wait_vm<4>();
+        else if (wave == 0) wait_vm<14>();
+        else wait_vm<12>();
       } else {
-        __builtin_amdgcn_s_waitcnt(0x0f70);
+        if (!next) wait_vm<8>();
+        else if (wave == 0) wait_vm<18>();
+        else wait_vm<16>();
       }
-      __syncthreads();
+      ring_barrier();
       // the bases count as changed here, so that the eight offsets derived from
       // each are not hoisted out of the loop into sixteen live registers
       asm volatile("" : "+v"(kbase), "+v"(vbase));
@@ -1094,7 +1136,21 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_bf16_kernel(AttnArgs a) 
       const lds_char* qt_ = (const lds_char*)smem + (it % 3) * SLOTB;
       const lds_char* ot_ = qt_ + TILE;
       const float* vec = (const float*)(smem + (it % 3) * SLOTB + 2 * TILE);
-      if (q0 + QT - 1 < kw0) continue;             // all queries precede all keys of this wave
+      // dS block of (query head, key unit, query tile): row = key in the unit
+      bf16* dsb = nullptr;
+      if constexpr (DS) {
+        const int qt = cur.qt0 + it % cur.nq;
+        const long pair = (long)cur.kt * nqt_all - (long)cur.kt * (cur.kt - 1) + (qt - 2 * cur.kt);
+        dsb = static_cast<bf16*>(a.ds) + (((long)cur.b * a.H + cur.kvh * R + it / cur.nq) * a.dsP + pair) * 8192 +
+              wave * 2048 + lane * 8;   // chunk 4 wave, this lane's 16 bytes
+      }
+      if (q0 + QT - 1 < kw0) {                     // all queries precede all keys of this wave
+        if constexpr (DS) {   // zeros, in 4 stores like the computed iterations
+#pragma unroll
+          for (int c = 0; c < 4; ++c) st16(dsb + 512 * c, u32x4{0u, 0u, 0u, 0u});
+        }
+        continue;
+      }
       if (q0 > kw0 + 31 + a.W - 1) continue;       // all queries are past the keys' windows
       const bool need_mask = (q0 < kw0 + 31) || (q0 + QT > a.T) || (q0 + QT - 1 >= kw0 + a.W);
       // one copy of the iteration with the causal/edge mask and one without,
@@ -1164,6 +1220,11 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_bf16_kernel(AttnArgs a) 
               pf[m] = frag_regs<bf16>(sv[qb], m * 8);
               sf[m] = frag_regs<bf16>(dp[qb], m * 8);
             }
+            if constexpr (DS) {
+              // chunk 4 wave + 2 qb + m: queries qb*32 + 16m + 4(lane/32) + 0..3 and + 8
+  #pragma unroll
+              for (int m = 0; m < 2; ++m) st16(dsb + 512 * (2 * qb + m), __builtin_bit_cast(u32x4, sf[m]));
+            }
           }
           dv[db] = MM::mma(fa[i], pf[mm], dv[db]);     // dV^T += dO^T P
           dk[db] = MM::mma(fb[i], sf[mm], dk[db]);     // dK^T += Q^T dS
@@ -1181,7 +1242,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_bf16_kernel(AttnArgs a) 
     // ---- unit boundary
     ++j;
     const int un = unit_of(j);
-    const bool more = un < units;
+    const bool more = un < qlen;
     const Unit nxt = more ? make_unit(un) : cur;
     lds_barrier();                 // the ring is free
     if (more) issue_kv_rows(nxt);  // into slot 2 and past the ring
@@ -1311,6 +1372,10 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_bf16_kernel(AttnArgs a) {
     const long bhT = ((long)cur.b * a.H + cur.head) * a.T;
     const float lse = qv ? a.lse[bhT + q] : INFINITY;
     const float dlt = qv ? a.delta[bhT + q] : 0.f;
+    // these two loads complete here, behind the unit's first two tiles (a
+    // wait at their first use inside the loop would drain the ring there
+    // every tile)
+    wait_vm<0>();
     const int kt_lo = cur.kt_lo, n = cur.n;
     f32x16 acc[4];
 #pragma unroll
@@ -1318,9 +1383,9 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
     for (int it = 0; it < n; ++it) {
-      if (it + 1 < n) __builtin_amdgcn_s_waitcnt(0x0f70 | 8);
-      else __builtin_amdgcn_s_waitcnt(0x0f70);
-      __syncthreads();
+      if (it + 1 < n) wait_vm<8>();
+      else wait_vm<0>();
+      ring_barrier();
       asm volatile("" : "+v"(kbase), "+v"(vbase));   // keep the derived offsets in the loop
       if (it + 2 < n) issue(cur, (it + 2) % NSLOT, it + 2);
       const lds_char* kt_ = (const lds_char*)smem + (it % NSLOT) * SLOT;
@@ -1413,6 +1478,113 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_bf16_kernel(AttnArgs a) {
     issue(cur, 0, 0);
     if (cur.n > 1) issue(cur, 1, 1);
   }
+  if (a.amax_dqkv) amax_publish<bf16>(a.amax_dqkv, mx);
+}
+
+// dQ from the stored dS: dQ^T (d x query) = K^T dS^T per unit of 128
+// queries of one (sequence, query head), over the 32-key tiles up to the
+// diagonal.  Four waves of 32 queries; per key tile the K rows and the dS^T
+// rows (keys x the unit's 128 queries, 4 KiB of each of its two 64-query
+// blocks) arrive in LDS by direct-to-LDS loads, four tiles ahead in a
+// five-slot ring (the kernel streams dS from HBM once: the bytes in flight
+// set its speed); both fragments come from the LDS transpose read in the
+// same key order.  A dS^T row in LDS holds the stored 16-byte pieces, so
+// within each 16 queries its positions 4..7 and 8..11 hold queries 8..11 and
+// 4..7: lane l of a wave accumulates query qperm(l % 32), and the epilogue
+// (the dQ kernel's: QK-norm and rotary backward in row layout) stages it in
+// that row.  One workgroup per unit, two per CU; the units of one (sequence,
+// head) run on one XCD, longest first, so that its K rows stay in that L2.
+namespace fa {
+constexpr int DSQ_KT = 32;                       // keys per tile
+constexpr int DSQ_TILE = DSQ_KT * 256;           // bytes of a [32][128] bf16 tile
+constexpr int DSQ_SLOT = 2 * DSQ_TILE;           // K tile, dS^T tile
+constexpr int DSQ_NSLOT = 5;
+constexpr int DSQ_LDS = DSQ_NSLOT * DSQ_SLOT;    // 80 KiB: two workgroups fill a CU's LDS
+}  // namespace fa
+__global__ __launch_bounds__(256, 2) void attn_bwd_dq_ds_kernel(AttnArgs a) {
+  using namespace fa;
+  typedef Mfma<bf16> MM;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int BH = a.B * a.H;
+  const int nu = (a.T + 127) / 128, nqt_all = (a.T + 63) / 64;
+  // workgroups are dealt round robin to the 8 XCDs: XCD x walks the units
+  // x * total/8 .. in order, (sequence, head) by (sequence, head)
+  const int total = nu * BH;
+  int pid = blockIdx.x;
+  if (total % 8 == 0) pid = (pid % 8) * (total / 8) + pid / 8;
+  const int bh = pid / nu;
+  const int u = nu - 1 - pid % nu;                    // longest units first
+  const int b = bh / a.H, head = bh % a.H, kvh = head / (a.H / a.G);
+  const long ldb = (long)a.LD * 2;
+  const bf16* qkv = static_cast<const bf16*>(a.qkv);
+  const i32x4 rk = make_rsrc(qkv + (long)b * a.T * a.LD, clamp_bytes((long)a.T * ldb));
+  const i32x4 rd = make_rsrc(static_cast<const bf16*>(a.ds) + (long)bh * a.dsP * 8192,
+                             clamp_bytes((long)a.dsP * 16384));
+  const int koff = (a.KO + kvh * HD) * 2;
+  const int n = min(4 * u + 4, (a.T + DSQ_KT - 1) / DSQ_KT);   // key tiles 0 .. n-1
+  // key tile t: K rows 32t..; the dS pieces of keys 32 (t & 3).. (1 KiB chunks
+  // 4 (t & 3) .. 4 (t & 3) + 3) of blocks (t / 4, 2u) and (t / 4, 2u + 1)
+  auto issue = [&](int slot, int t) {
+    char* d = smem + slot * DSQ_SLOT;
+    const int kt = t >> 2;
+    const long pair = (long)kt * nqt_all - (long)kt * (kt - 1) + (2 * u - 2 * kt);
+    const long row0 = pair * 16384 + (long)(t & 3) * 4096;   // bytes: block (kt, 2u), chunk 4 (t & 3)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int base = wave * 128 + i * 64;
+      const int p = base + lane;
+      const int row = p >> 4, c = (p & 15) ^ sw(row);
+      const uint32_t ok = (uint32_t)((long)(t * DSQ_KT + row) * ldb + koff + c * 16);
+      dma16(rk, (lds_u32*)(d + base * 16), ok);
+      // LDS chunk c of key row `row`: block 2u + c/8, 1 KiB chunk (c/2) % 4,
+      // piece of key row + 32 (c & 1)
+      const uint32_t od = (uint32_t)(row0 + (c >> 3) * 16384 + ((c >> 1) & 3) * 1024 + (row + 32 * (c & 1)) * 16);
+      dma16(rd, (lds_u32*)(d + DSQ_TILE + base * 16), od);
+    }
+  };
+  int vbase;
+  {
+    int vo[8];
+    frag_vt_offsets(vo, lane);
+    vbase = vo[0];
+  }
+  f32x16 acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+  for (int t = 0; t < DSQ_NSLOT - 1 && t < n; ++t) issue(t, t);
+  for (int t = 0; t < n; ++t) {
+    // tile t landed (own loads, then everyone's; each tile is 4 issues per
+    // wave, tiles t+1 .. t+3 may stay in flight); the slot of tile t-1 is free
+    if (t + 3 < n) wait_vm<12>();
+    else if (t + 2 < n) wait_vm<8>();
+    else if (t + 1 < n) wait_vm<4>();
+    else wait_vm<0>();
+    ring_barrier();
+    if (t + 4 < n) issue((t + 4) % DSQ_NSLOT, t + 4);
+    const lds_char* kt_ = (const lds_char*)smem + (t % DSQ_NSLOT) * DSQ_SLOT;
+    const lds_char* st_ = kt_ + DSQ_TILE;
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm) {
+      const bf16x8 bf = frag_vt_x(st_, vbase, mm, wave);   // dS^T: this wave's 32 queries
+#pragma unroll
+      for (int db = 0; db < 4; ++db) acc[db] = MM::mma(frag_vt_x(kt_, vbase, mm, db), bf, acc[db]);
+    }
+  }
+  __syncthreads();   // every wave is done with the slots: they become staging rows
+  const int qw0 = u * 128 + wave * 32;
+  const long row0 = (long)b * a.T + qw0;
+  const int nrows = min(32, a.T - qw0);
+  float* stg = reinterpret_cast<float*>(smem) + wave * 32 * 128;
+  QkRows qk;
+  qk_rows_load(qk, qkv + row0 * a.LD + head * HD, a.LD, a.rho + row0 * a.H + head, a.H, nrows, lane);
+  // lane l holds query qperm(l % 32): bits 2 and 3 of the position swapped
+  const int l32 = lane & 31;
+  stage_acc(stg, acc, a.rsd, lane, (l32 & 0x13) | ((l32 & 4) << 1) | ((l32 & 8) >> 1));
+  const float mx =
+      store_rows_qk(stg, qk, static_cast<bf16*>(a.dqkv) + row0 * a.LD + head * HD, a.LD, a.cs, qw0, nrows, lane);
   if (a.amax_dqkv) amax_publish<bf16>(a.amax_dqkv, mx);
 }
 

@@ -30,6 +30,7 @@ constexpr int DKDV_SLOT = 2 * fa::TILE + 2048;
 constexpr int DKDV_LDS = 2 * DKDV_SLOT + 4 * fa::TILE;
 static_assert(DKDV_LDS >= 3 * DKDV_SLOT && DKDV_LDS <= 160 * 1024, "dK/dV LDS");
 static_assert(4 * 32 * 128 * 4 <= 2 * DKDV_SLOT, "dK/dV staging rows fit in ring slots 0-1");
+static_assert(4 * 32 * 128 * 4 <= fa::DSQ_LDS, "dQ-from-dS staging rows fit in its two slots");
 // dQ: the K/V ring, then the Q rows of a unit (its dO rows use ring slot 2)
 constexpr int DQ_LDS = fa::LDS + 2 * fa::TILE;
 static_assert(DQ_LDS <= 160 * 1024 && 4 * 32 * 128 * 4 <= 2 * fa::SLOT && 2 * fa::TILE <= fa::SLOT, "dQ LDS");
@@ -70,9 +71,11 @@ void attn_bwd_dkdv(const AttnArgs& a, bool bf16, hipStream_t st) {
   const int units = tiles(a.T, 128) * a.B * a.G;
   const dim3 grid(units);
   if (bf16) {
-    // persistent: one workgroup per CU walks the units
-    allow_lds(reinterpret_cast<const void*>(attn_bwd_dkdv_bf16_kernel), DKDV_LDS);
-    hipLaunchKernelGGL(attn_bwd_dkdv_bf16_kernel, dim3(std::min(units, cu_count())), dim3(256), DKDV_LDS, st, a);
+    // persistent: one workgroup per CU walks the units; with a.ds it also
+    // stores dS for the dQ kernel
+    auto kern = a.ds ? attn_bwd_dkdv_bf16_kernel<true> : attn_bwd_dkdv_bf16_kernel<false>;
+    allow_lds(reinterpret_cast<const void*>(kern), DKDV_LDS);
+    hipLaunchKernelGGL(kern, dim3(std::min(units, cu_count())), dim3(256), DKDV_LDS, st, a);
   } else {
     allow_lds(reinterpret_cast<const void*>(attn_bwd_dkdv_kernel<float>), attn_dkdv_lds<float>());
     hipLaunchKernelGGL(attn_bwd_dkdv_kernel<float>, grid, dim3(256), attn_dkdv_lds<float>(), st, a);
@@ -83,7 +86,11 @@ void attn_bwd_dq(const AttnArgs& a, bool bf16, hipStream_t st) {
   // a unit of work per 128 queries of a (sequence, head)
   const int units = tiles(a.T, 128) * a.B * a.H;
   const dim3 grid(units);
-  if (bf16) {
+  if (bf16 && a.ds) {
+    // dQ = dS K from the dS the dK/dV kernel stored: a workgroup per unit
+    allow_lds(reinterpret_cast<const void*>(attn_bwd_dq_ds_kernel), fa::DSQ_LDS);
+    hipLaunchKernelGGL(attn_bwd_dq_ds_kernel, grid, dim3(256), fa::DSQ_LDS, st, a);
+  } else if (bf16) {
     // persistent: one workgroup per CU walks the units
     allow_lds(reinterpret_cast<const void*>(attn_bwd_dq_bf16_kernel), DQ_LDS);
     hipLaunchKernelGGL(attn_bwd_dq_bf16_kernel, dim3(std::min(units, cu_count())), dim3(256), DQ_LDS, st, a);

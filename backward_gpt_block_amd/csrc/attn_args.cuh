@@ -22,6 +22,16 @@ struct AttnArgs {
   const float2* cs;    // [T][64] rotary angles (bf16 backward kernels)
   unsigned* amax_o;    // fp8 mode: absolute maxima (float bits) of o and of
   unsigned* amax_dqkv; //   dq' | dk' | dv, or null
+  // bf16 causal backward: the dK/dV kernel stores dS here and dQ = dS K is
+  // computed from it (null: the dQ kernel recomputes dS).  Per (sequence,
+  // query head) dsP blocks of 16 KiB, one per pair of a 128-key unit kt and a
+  // 64-query tile qt >= 2 kt, in the order of kt, then qt; dsP = sum over kt
+  // of (query tiles - 2 kt).  A block holds the 128 x 64 bf16 dS values as 16
+  // chunks of 1 KiB, chunk 4w + 2qb + m for keys 32w .. 32w+31 and queries
+  // 32qb + 16m .. +15; within a chunk, 16 bytes per key k and half h (at
+  // byte 16 (k + 32h)): queries 4h + {0..3} and 8 + 4h + {0..3} of the 16.
+  void* ds;
+  int dsP;
   int B, T, H, C;
   int G;             // key/value heads (query head h uses key/value head h / (H/G))
   int LD;            // elements per row of qkv / dqkv: C + 2 G D

@@ -134,6 +134,22 @@ int wgrad_splits(int M, int N, long K, int BK) {
   return (int)smax;
 }
 
+// Stored-dS backward attention (bf16, causal, T <= 4096): the dK/dV kernel
+// writes the bf16 dS of every visible (query, key) pair and dQ = dS K is a
+// pass over it, instead of a pass that recomputes S and dP.  Per (sequence,
+// query head): one [128 keys][64 queries] block per pair of a 128-key unit kt
+// and a 64-query tile qt >= 2 kt, ds_pairs of them (about T^2 / 2 values).
+// With a window, or past T = 4096 (where the store would outgrow the other
+// activations many times), the dQ pass recomputes dS.
+bool stored_ds(const blk_cfg& c) {
+  const bool causal = c.window <= 0 || c.window >= c.T;
+  return c.dtype == BLK_BF16 && causal && c.T <= 4096;
+}
+long ds_pairs(const blk_cfg& c) {
+  const long nk = (c.T + 127) / 128, nq = (c.T + 63) / 64;
+  return nk * nq - nk * (nk - 1);   // sum over kt < nk of (nq - 2 kt)
+}
+
 template <typename T> struct BwdScratch {
   T* du;        // [N, F]
   T* dh;        // [N, C] (dh2, later dh1)
@@ -142,6 +158,7 @@ template <typename T> struct BwdScratch {
   T* dqkv;      // [N, 3C]
   T* wt;        // transposed weights: W_proj^T [F,C], W_fc^T [C,F], W_o^T [C,C], W_qkv^T [C,(H+2G)128]
   float* delta; // [B*H][T]
+  bf16* ds = nullptr;   // stored dS ([B*H][ds_pairs][128][64]), or null
   float* part;  // split-k partial sums
   // fp8 mode: E4M3 copies of the gradients (row-major and transposed [*, Np])
   // and of the transposed weights
@@ -161,6 +178,7 @@ template <typename T> BwdScratch<T> carve_bwd(const blk_cfg& c, void* p) {
   s.dqkv = k.take<T>(N * qkv_width(c));
   s.wt = k.take<T>(9L * c.C * c.C + (long)c.C * qkv_width(c));
   s.delta = k.take<float>((size_t)c.B * c.H * c.T);
+  if (stored_ds(c)) s.ds = k.take<bf16>((size_t)c.B * c.H * ds_pairs(c) * 128 * 64);
   size_t part = 0;
   const int shapes[4][2] = {{c.C, c.F}, {c.F, c.C}, {c.C, c.C}, {(int)qkv_width(c), c.C}};
   for (int bk : {GemmTile<T>::BK, GemmTile<fp8e4>::BK})
@@ -471,6 +489,7 @@ int bwd_impl(const blk_cfg& c, const T* dy, const T* x, const T* wqkv, const T* 
     AttnArgs a = attn_args<T>(c);
     a.qkv = s.qkv; a.lse = s.lse; a.dO = w.dO; a.delta = w.delta; a.dqkv = w.dqkv;
     a.rho = s.rho; a.cs = s.cs;
+    a.ds = w.ds; a.dsP = (int)ds_pairs(c);
     // 5-3: the bf16 kernels also apply the QK-norm and rotary backward to dq, dk
     {
       Timed t("attn_bwd_dkdv", st);
@@ -675,6 +694,7 @@ int bwd_fp8(const blk_cfg& c, const bf16* dy, const bf16* wqkv, const bf16* wo, 
     a.qkv = s.qkv; a.lse = s.lse; a.dO = w.dO; a.delta = w.delta; a.dqkv = w.dqkv;
     a.rho = s.rho; a.cs = s.cs;   // QK-norm and rotary backward in the stores
     a.amax_dqkv = am + AM_DQKV;
+    a.ds = w.ds; a.dsP = (int)ds_pairs(c);
     {
       Timed t("attn_bwd_dkdv", st);
       attn_bwd_dkdv(a, true, st);

@@ -90,6 +90,15 @@ template <> struct Mfma<fp8e4> {
   }
 };
 
+// s_waitcnt vmcnt(N): wait until at most N vector memory operations of this
+// wave are outstanding (loads and stores both count, and complete in issue
+// order); the LDS and export counters are not waited for.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
+  __builtin_amdgcn_s_waitcnt(0x0f70 | (N & 15) | ((N >> 4) << 14));
+}
+
 __device__ __forceinline__ int acc_row(int j, int lane) { return 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3); }
 
 // Lane moves inside a row of 16 lanes through DPP (a VALU operand modifier;
@@ -207,6 +216,35 @@ __device__ void raw_buffer_load_lds(i32x4 rsrc, lds_u32* lds, int size, int voff
                                     int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
 __device__ u32x4 raw_buffer_load_b128(i32x4 rsrc, int voffset, int soffset, int aux) __asm(
     "llvm.amdgcn.raw.buffer.load.v4i32");
+
+// A direct-to-LDS load of 16 bytes per lane (the lanes write 16 consecutive
+// bytes each from `lds`, the destination of lane 0, uniform), written in
+// assembly: the compiler does not see it as a write to LDS.  After a write
+// it does see, it makes the next LDS read wait for every vector memory
+// operation in flight (vmcnt(0)), which empties a prefetch ring at every
+// tile.  Kernels that use it wait for their loads with explicit counts
+// (wait_vm) before the barrier (ring_barrier) that publishes a tile; the
+// instruction writes no register, so nothing of the compiler's is in flight.
+__device__ __forceinline__ void dma16(i32x4 rsrc, const lds_u32* lds, uint32_t voffset) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(m0), "v"(voffset), "s"(rsrc)
+               : "memory", "m0");
+}
+
+// Workgroup barrier for LDS rings filled by dma16: waits for this wave's
+// own LDS accesses, then for every wave; unlike __syncthreads (whose memory
+// fence waits for all global loads in flight) it leaves the prefetched
+// tiles in flight.  Also a hard scheduling and memory-ordering boundary.
+__device__ __forceinline__ void ring_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+  __builtin_amdgcn_sched_barrier(0);
+  __asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
 
 // Buffer resource over [p, p + bytes): loads at offsets >= bytes return 0.
 __device__ __forceinline__ i32x4 make_rsrc(const void* p, uint32_t bytes) {
