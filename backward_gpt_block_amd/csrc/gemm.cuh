@@ -540,15 +540,19 @@ struct PPStagerT {
   // The buffer resource starts at the stage's first k-row, so offsets stay
   // below 64 rows whatever the matrix size.  Columns past the matrix edge
   // read in-bounds neighbours or zero; they only feed outputs the epilogue
-  // drops.  k past the end (live = false) reads zero.
+  // drops.  k past the end (live = false) reads zero.  The loads are the
+  // assembly form (dma16): the fragments of this operand come from the LDS
+  // transpose read, and after a direct-to-LDS load the compiler knows of it
+  // would make that read wait for the stage just issued; the body waits for
+  // each stage explicitly.
   __device__ __forceinline__ void issue(char* sub, int krel, bool live, int q) const {
     const long adv = (long)krel * ldb;
     const i32x4 rs = make_rsrc(base + adv, (uint32_t)max(0L, min(left - adv, 0x7fffffffL)));
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const uint32_t off = x + (uint32_t)(2 * j) * ldb + (cl ^ (uint32_t)(((2 * j) & 7) << 5));
-      lds_u32* dst = (lds_u32*)(sub + __builtin_amdgcn_readfirstlane((8 * q + j) * 1024));
-      raw_buffer_load_lds(rs, dst, 16, live ? (int)off : (int)0x80000000u, 0, 0, 0);
+      lds_u32* dst = (lds_u32*)(sub + (8 * q + j) * 1024);
+      dma16(rs, dst, live ? off : 0x80000000u);
     }
   }
 };
