@@ -153,6 +153,8 @@ def library() -> ctypes.CDLL:
         lib.block_fp8_quantize.restype = i32
         lib.block_fp8_quantize_2d.argtypes = [vp, ctypes.c_int64, ctypes.c_int64, vp, vp, ctypes.c_int64, vp, vp]
         lib.block_fp8_quantize_2d.restype = i32
+        lib.block_mfma_probe.argtypes = [i32, i32, i32, vp, vp]
+        lib.block_mfma_probe.restype = i32
         lib.block_timing_enable.argtypes = [i32]
         lib.block_timing_enable.restype = None
         lib.block_timing_read.argtypes = [i32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_double),
@@ -345,6 +347,15 @@ def block_fp8_quantize_2d(x, rows: int, cols: int, codes, codes_t, ldt: int, ama
                                            _arg(codes, "codes", w, nbytes=rows * cols),
                                            _arg(codes_t, "codes_t", w, nbytes=cols * ldt), int(ldt),
                                            _arg(amax, "amax", w, nbytes=4), _stream(stream))
+    return _check(code, w, raise_on_error)
+
+
+def block_mfma_probe(kind: int, workgroups: int, iters: int, sink, *, stream=None, raise_on_error=True) -> int:
+    """Register-only MFMA loop (kind 0 bf16, 1 E4M3) for measuring the
+    matrix cores' achievable rate; sink holds workgroups * 256 floats."""
+    w = "block_mfma_probe"
+    code = library().block_mfma_probe(int(kind), int(workgroups), int(iters),
+                                      _arg(sink, "sink", w, "f32", int(workgroups) * 256), _stream(stream))
     return _check(code, w, raise_on_error)
 
 

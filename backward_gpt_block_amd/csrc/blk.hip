@@ -245,6 +245,49 @@ bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0;
 
 int launch_status() { return hipGetLastError() == hipSuccess ? BLK_OK : BLK_ELAUNCH; }
 
+// ---------------------------------------------------------------- MFMA rate probe
+// Register-only MFMA loop: each wave runs `iters` rounds of four independent
+// 32x32 MFMA chains (bf16 32x32x16, or E4M3 32x32x64 with unit scales) and
+// writes one float per lane, so the loop is not removed.  Its rate is the
+// matrix cores' achievable throughput at the clock the chip holds under this
+// load, a yardstick for the kernels (not part of any computation).
+template <int KIND>
+__global__ __launch_bounds__(256) void mfma_probe_kernel(int iters, float* sink) {
+  f32x16 c[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) c[j][r] = 0.f;
+  const int t = threadIdx.x;
+  if constexpr (KIND == 0) {
+    bf16x8 a, b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      a[e] = (bf16)(1e-3f * (float)((t + e) & 7));
+      b[e] = (bf16)(1e-3f * (float)((t * 3 + e) & 7));
+    }
+    for (int i = 0; i < iters; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) c[j] = Mfma<bf16>::mma(a, b, c[j]);
+  } else {
+    i32x8 a, b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      a[e] = 0x38383838 + ((t + e) & 3);
+      b[e] = 0x30303030 + ((t * 3 + e) & 3);
+    }
+    for (int i = 0; i < iters; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) c[j] = Mfma<fp8e4>::mma(a, b, c[j]);
+  }
+  float v = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) v += c[j][r];
+  sink[(long)blockIdx.x * 256 + t] = v;
+}
+
 // ---------------------------------------------------------------- timing
 // Optional per-launch timing: while enabled, every launch site records a
 // pair of hipEvents around its kernel(s) on the call's stream.
@@ -1076,6 +1119,16 @@ int block_fp8_quantize_2d(const void* x, int64_t rows, int64_t cols, void* codes
   hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, st, (unsigned*)amax, 1);
   quantize(static_cast<const bf16*>(x), rows, cols, (unsigned*)amax, static_cast<uint8_t*>(codes),
            static_cast<uint8_t*>(codes_t), ldt, true, st);
+  return launch_status();
+}
+
+int block_mfma_probe(int kind, int workgroups, int iters, float* sink, void* stream) {
+  if ((kind != 0 && kind != 1) || workgroups < 1 || iters < 1 || !sink) return BLK_EINVAL;
+  if (reinterpret_cast<uintptr_t>(sink) & 3) return BLK_EALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipGetLastError();
+  hipLaunchKernelGGL(kind == 0 ? mfma_probe_kernel<0> : mfma_probe_kernel<1>, dim3(workgroups), dim3(256), 0, st,
+                     iters, sink);
   return launch_status();
 }
 

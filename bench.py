@@ -30,6 +30,15 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "training tokens/sec and TFLOP/s per decoder block (d20, T=2048) on 1 MI355X"
+# the metric as it reads for each training workload (the d20 bf16 one is the headline)
+WORKLOAD_METRIC = {
+    "d20_bf16": METRIC,
+    "d6_f32": "training tokens/sec and TFLOP/s per decoder block (d6, T=512, fp32) on 1 MI355X",
+    "d12_bf16": "training tokens/sec and TFLOP/s per decoder block (d12, T=2048) on 1 MI355X",
+    "d26_fp8": "training tokens/sec and TFLOP/s per decoder block (d26, T=2048, E4M3 linear GEMMs) on 1 MI355X",
+    "d20_bf16_swa": "training tokens/sec and TFLOP/s per decoder block (d20, T=2048, window 512) on 1 MI355X",
+    "d20_bf16_gqa": "training tokens/sec and TFLOP/s per decoder block (d20, T=2048, 2 key/value heads) on 1 MI355X",
+}
 DECODE_METRIC = "decode tokens/sec per decoder block (d20, batch 64, KV cache 2048) on 1 MI355X"
 HEAD_METRIC = "training tokens/sec of the lm_head + cross-entropy (d20, 65,536 tokens, vocabulary 65,536) on 1 MI355X"
 PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3, "fp8": 5033.2}
@@ -119,6 +128,81 @@ def site_bytes(sh) -> dict:
         w = matmul_params(sh)
         out["fp8_quantize"] = float(w * (5 + 3) + N * C * (3 * 4 + 6 + 4 + 3 * 4) + N * F * (4 + 4))
     return out
+
+
+def smi_state() -> dict:
+    """Clock and power of the GPU as the box's SMI tool reports them (called
+    while steps are running, so the figures are those under load)."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--json"], capture_output=True, text=True,
+                           timeout=30)
+        data = json.loads(r.stdout)
+    except Exception as e:   # the report notes the failure instead of failing
+        return {"error": f"{type(e).__name__}: {e}"}
+    card = next((v for k, v in data.items() if k.startswith("card")), {})
+    keep = {k: v for k, v in card.items() if any(w in k.lower() for w in ("sclk", "mclk", "fclk", "power"))}
+    return {"tool": "rocm-smi --showclocks --showpower", **keep}
+
+
+def under_load(launch, seconds: float = 2.0) -> dict:
+    """Queue about `seconds` of work (launch() enqueues one step) and read
+    the SMI state while it runs."""
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    launch()
+    torch.cuda.synchronize()
+    one = max(time.perf_counter() - t0, 1e-4)
+    for _ in range(max(1, int(seconds / one))):
+        launch()
+    state = smi_state()
+    torch.cuda.synchronize()
+    return state
+
+
+def mfma_rates() -> dict:
+    """Achievable matrix-core rate from a register-only MFMA loop
+    (block_mfma_probe): 4 workgroups of four waves per CU, best of three."""
+    import torch
+    import backward_gpt_block_amd as bl
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    wg, out = 4 * cus, {}
+    sink = torch.empty(wg * 256, dtype=torch.float32, device="cuda:0")
+    for kind, name, flop, iters in ((0, "bf16", 2 * 32 * 32 * 16, 20000), (1, "fp8", 2 * 32 * 32 * 64, 10000)):
+        best = None
+        for _ in range(4):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            bl.block_mfma_probe(kind, wg, iters, sink)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            best = ms if best is None else min(best, ms)
+        tf = wg * 4 * iters * 4 * flop / (best * 1e-3) / 1e12
+        out[name] = {"tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_TFLOPS[name], 4)}
+    out["method"] = "register-only MFMA loop, 4 independent 32x32 chains per wave, 4 waves per SIMD, best of 4"
+    return out
+
+
+def split_timing(fwd, bwd, steps: int) -> dict:
+    """Median and minimum of the forward, the backward and their sum over
+    `steps` iterations, each bracketed by events on the stream."""
+    import statistics
+    import torch
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for e in ev:
+        e[0].record()
+        fwd()
+        e[1].record()
+        bwd()
+        e[2].record()
+    torch.cuda.synchronize()
+    f = [e[0].elapsed_time(e[1]) for e in ev]
+    b = [e[1].elapsed_time(e[2]) for e in ev]
+    t = [x + y for x, y in zip(f, b)]
+    r = lambda v: {"median": round(statistics.median(v), 4), "min": round(min(v), 4)}
+    return {"iterations": steps, "fwd_ms": r(f), "bwd_ms": r(b), "fwd_bwd_ms": r(t)}
 
 
 def cpu_baseline(sh, inp, budget_s: float = 12.0) -> dict:
@@ -254,9 +338,15 @@ def bench_train(args) -> int:
     scratch = torch.empty(bl.block_scratch_bytes(cfg), dtype=torch.uint8, device="cuda:0")
     stream = torch.cuda.current_stream()
 
-    def step():
+    def fwd():
         bl.block_fwd(cfg, x, *W, y, saved, scratch, stream=stream)
+
+    def bwd():
         bl.block_bwd(cfg, dy, x, *W, saved, dx, *dW, 0, scratch, stream=stream)
+
+    def step():
+        fwd()
+        bwd()
 
     for _ in range(args.warmup):
         step()
@@ -274,6 +364,14 @@ def bench_train(args) -> int:
     wall = time.perf_counter() - w0
     ms = ev0.elapsed_time(ev1) / args.steps
     log(f"step: {ms:.3f} ms (wall {1e3 * wall / args.steps:.3f} ms)")
+
+    # forward and backward separately: median and minimum over max(K, 20) iterations
+    split = split_timing(fwd, bwd, max(args.steps, 20))
+    log(f"split: {split}")
+    smi = under_load(step)
+    log(f"smi under load: {smi}")
+    mfma = mfma_rates()
+    log(f"mfma probe: {mfma}")
 
     # per-launch-site times over a second pass of the same K steps
     bl.block_timing_enable(True)
@@ -321,7 +419,8 @@ def bench_train(args) -> int:
         cpu = cpu_baseline(sh, inp, args.cpu_budget)
         log(f"cpu baseline: {cpu}")
     out = {
-        "metric": METRIC, "value": round(tokens / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "metric": WORKLOAD_METRIC.get(args.workload, METRIC), "value": round(tokens / (ms * 1e-3), 1),
+        "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3+bf16" if sh.gemm == "fp8" else dt,
         "data": "synthetic",
@@ -331,6 +430,7 @@ def bench_train(args) -> int:
         "tflops": round(tflops, 2), "frac_of_peak": round(frac, 4),
         "tflops_nanochat_convention": round(step_flops_nanochat(sh) / (ms * 1e-3) / 1e12, 2),
         "roofline": roof, "cpu_baseline": cpu,
+        "split": split, "smi_under_load": smi, "mfma_probe": mfma,
     }
     print(json.dumps(out), flush=True)
     return 0

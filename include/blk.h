@@ -270,6 +270,15 @@ int block_fp8_quantize_2d(const void* x, int64_t rows, int64_t cols, void* codes
 void block_timing_enable(int on);
 int block_timing_read(int max, const char** names, double* total_ms, int* counts);
 
+/* Measurement hook: the matrix cores' achievable rate.  Launches
+ * `workgroups` workgroups of four waves; each wave runs `iters` rounds of
+ * four independent 32x32 MFMAs from registers (kind 0: bf16 32x32x16,
+ * 2*32*32*16 FLOP each; kind 1: OCP E4M3 32x32x64, 2*32*32*64 FLOP each)
+ * and writes one float per lane to sink (workgroups * 256 floats, device,
+ * 4-byte aligned).  Time it with events on the stream.  BLK_EINVAL for a bad
+ * kind, count or NULL sink. */
+int block_mfma_probe(int kind, int workgroups, int iters, float* sink, void* stream);
+
 /* Static, human-readable text of a status code. */
 const char* block_strerror(int code);
 

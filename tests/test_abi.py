@@ -300,3 +300,13 @@ def test_binding_rejects_bad_tensors(lib):
         bl.decode_step(d, A, A, A, A, A, A, A + 0x100, torch.zeros(2, dtype=torch.int64), A, A, scratch_bytes=1 << 30)
     with pytest.raises(E.BlkError, match="amax"):
         bl.block_fp8_quantize(A, 64, A, torch.zeros(1, dtype=torch.uint8))
+
+
+def test_mfma_probe_argument_errors(lib):
+    E = bl.binding
+    probe = lambda kind, wg, it, sink: bl.block_mfma_probe(kind, wg, it, sink, stream=0, raise_on_error=False)
+    assert probe(2, 4, 10, A) == E.BLK_EINVAL
+    assert probe(0, 0, 10, A) == E.BLK_EINVAL
+    assert probe(1, 4, 0, A) == E.BLK_EINVAL
+    assert probe(0, 4, 10, None) == E.BLK_EINVAL
+    assert probe(0, 4, 10, A + 2) == E.BLK_EALIGN
