@@ -138,9 +138,9 @@ def library() -> ctypes.CDLL:
         lib.block_bwd.restype = i32
         lib.decode_scratch_bytes.argtypes = [pd]
         lib.decode_scratch_bytes.restype = sz
-        lib.decode_step.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.decode_step.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.decode_step.restype = i32
-        lib.decode_step_noalloc.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.decode_step_noalloc.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.decode_step_noalloc.restype = i32
         ph = ctypes.POINTER(_HCfg)
         lib.head_scratch_bytes.argtypes = [ph]
@@ -283,26 +283,30 @@ def block_bwd(cfg: BlockConfig, dy, x, w_qkv, w_o, w_fc, w_proj, saved, dx, dw_q
 
 
 def decode_step(cfg: DecodeConfig, x, w_qkv, w_o, w_fc, w_proj, k_cache, v_cache, cache_len, y, scratch=None, *,
-                scratch_bytes=None, stream=None, raise_on_error=True) -> int:
+                status=None, scratch_bytes=None, stream=None, raise_on_error=True) -> int:
+    """status: optional int32 device word, set to the number of sequences
+    whose cache_len is out of range (their y rows are NaN)."""
     w, k = "decode_step", _kind(cfg.dtype)
     ncache = cfg.B * (cfg.n_kv_head or cfg.H) * cfg.S_max * 128
     args = (_arg(x, "x", w, k, cfg.B * cfg.C), *_weights(cfg, w, w_qkv, w_o, w_fc, w_proj, k),
             _arg(k_cache, "k_cache", w, k, ncache), _arg(v_cache, "v_cache", w, k, ncache),
-            _arg(cache_len, "cache_len", w, "i32", cfg.B), _arg(y, "y", w, k, cfg.B * cfg.C))
+            _arg(cache_len, "cache_len", w, "i32", cfg.B), _arg(status, "status", w, "i32", 1),
+            _arg(y, "y", w, k, cfg.B * cfg.C))
     code = library().decode_step(ctypes.byref(cfg.c()), *args, _arg(scratch, "scratch", w),
                                  _nbytes(scratch, scratch_bytes), _stream(stream))
     return _check(code, w, raise_on_error)
 
 
 def decode_step_noalloc(cfg: DecodeConfig, x, w_qkv, w_o, w_fc, w_proj, k_cache, v_cache, cache_len, y, *,
-                        stream=None, raise_on_error=True) -> int:
+                        status=None, stream=None, raise_on_error=True) -> int:
     """decode_step with its temporaries in the library's static per-device
     workspace (no scratch argument; nothing allocated)."""
     w, k = "decode_step_noalloc", _kind(cfg.dtype)
     ncache = cfg.B * (cfg.n_kv_head or cfg.H) * cfg.S_max * 128
     args = (_arg(x, "x", w, k, cfg.B * cfg.C), *_weights(cfg, w, w_qkv, w_o, w_fc, w_proj, k),
             _arg(k_cache, "k_cache", w, k, ncache), _arg(v_cache, "v_cache", w, k, ncache),
-            _arg(cache_len, "cache_len", w, "i32", cfg.B), _arg(y, "y", w, k, cfg.B * cfg.C))
+            _arg(cache_len, "cache_len", w, "i32", cfg.B), _arg(status, "status", w, "i32", 1),
+            _arg(y, "y", w, k, cfg.B * cfg.C))
     code = library().decode_step_noalloc(ctypes.byref(cfg.c()), *args, _stream(stream))
     return _check(code, w, raise_on_error)
 

@@ -835,22 +835,22 @@ void dec_gemm(const char* name, const bf16* A, int M, const bf16* W, int N, int 
 // Arguments of a decode step other than its workspace.
 int check_decode_args(const blk_dcfg* cfg, const void* x, const void* w_qkv, const void* w_o, const void* w_fc,
                       const void* w_proj, const void* k_cache, const void* v_cache, const int32_t* cache_len,
-                      const void* y) {
+                      const int32_t* status, const void* y) {
   if (int e = check_dcfg(cfg)) return e;
   for (const void* p : {x, w_qkv, w_o, w_fc, w_proj, k_cache, v_cache, y})
     if (!p) return BLK_EINVAL;
   if (!cache_len || k_cache == v_cache) return BLK_EINVAL;
   for (const void* p : {x, w_qkv, w_o, w_fc, w_proj, k_cache, v_cache, y})
     if (!aligned(p)) return BLK_EALIGN;
-  if (reinterpret_cast<uintptr_t>(cache_len) & 3) return BLK_EALIGN;
+  if ((reinterpret_cast<uintptr_t>(cache_len) | reinterpret_cast<uintptr_t>(status)) & 3) return BLK_EALIGN;
   return BLK_OK;
 }
 
 // The launch sequence of one decode step, its temporaries carved from
 // `scratch` (decode_scratch_bytes(cfg) bytes of device memory).
 int decode_run(const blk_dcfg& c, const void* x, const void* w_qkv, const void* w_o, const void* w_fc,
-               const void* w_proj, void* k_cache, void* v_cache, const int32_t* cache_len, void* y, void* scratch,
-               hipStream_t st) {
+               const void* w_proj, void* k_cache, void* v_cache, const int32_t* cache_len, int32_t* status, void* y,
+               void* scratch, hipStream_t st) {
   const DecScratch d = carve_dec(c, scratch);
   hipGetLastError();
   const int B = c.B, C = c.C, H = c.H, F = c.F;
@@ -860,14 +860,14 @@ int decode_run(const blk_dcfg& c, const void* x, const void* w_qkv, const void* 
   const int NS = (c.S_max + dec::KEYS - 1) / dec::KEYS;
   {  // h1 = rmsnorm(x)
     Timed t("dec_rmsnorm", st);
-    hipLaunchKernelGGL(dec::dec_rmsnorm_kernel, dim3(B), dim3(256), 0, st, xb, C, c.eps, d.h1);
+    hipLaunchKernelGGL(dec::dec_rmsnorm_kernel, dim3(B), dim3(256), 0, st, xb, C, c.eps, d.h1, (int*)status);
   }
   const DecSplit sq = dec_split(B, (int)qkv_width(c), C);
   dec_gemm("dec_gemm_qkv", d.h1, B, static_cast<const bf16*>(w_qkv), (int)qkv_width(c), C, sq, d.part, st);
   {  // rotary + QK-norm at position cache_len[b]; k, v into the caches
     Timed t("dec_qkv_epi", st);
     hipLaunchKernelGGL(dec::dec_qkv_epi_kernel, dim3(H, B), dim3(192), 0, st, (const float*)d.part, sq.S, B, H,
-                       kv_heads(c), cache_len, c.S_max, c.eps, (double)c.rope_base, d.q, kc, vc);
+                       kv_heads(c), cache_len, c.S_max, c.eps, (double)c.rope_base, d.q, kc, vc, (int*)status);
   }
   const int dwin = c.window > 0 ? c.window : INT_MAX;
   {  // attention of the new token over slots 0..cache_len[b] (the last W with a window)
@@ -903,7 +903,7 @@ int decode_run(const blk_dcfg& c, const void* x, const void* w_qkv, const void* 
     Timed t("dec_out", st);
     const long n = (long)B * C;
     hipLaunchKernelGGL(dec::dec_out_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                       (const float*)d.part, sp.S, n, (const float*)d.y1, static_cast<bf16*>(y));
+                       (const float*)d.part, sp.S, n, (const float*)d.y1, static_cast<bf16*>(y), cache_len, c.S_max, C);
   }
   return launch_status();
 }
@@ -1075,24 +1075,24 @@ size_t decode_scratch_bytes(const blk_dcfg* cfg) {
 }
 
 int decode_step(const blk_dcfg* cfg, const void* x, const void* w_qkv, const void* w_o, const void* w_fc,
-                const void* w_proj, void* k_cache, void* v_cache, const int32_t* cache_len, void* y, void* scratch,
-                size_t scratch_bytes, void* stream) {
-  if (int e = check_decode_args(cfg, x, w_qkv, w_o, w_fc, w_proj, k_cache, v_cache, cache_len, y)) return e;
+                const void* w_proj, void* k_cache, void* v_cache, const int32_t* cache_len, int32_t* status, void* y,
+                void* scratch, size_t scratch_bytes, void* stream) {
+  if (int e = check_decode_args(cfg, x, w_qkv, w_o, w_fc, w_proj, k_cache, v_cache, cache_len, status, y)) return e;
   if (!scratch) return BLK_EINVAL;
   if (!aligned(scratch)) return BLK_EALIGN;
   if (scratch_bytes < carve_dec(*cfg, nullptr).bytes) return BLK_ENOSPC;
-  return decode_run(*cfg, x, w_qkv, w_o, w_fc, w_proj, k_cache, v_cache, cache_len, y, scratch,
+  return decode_run(*cfg, x, w_qkv, w_o, w_fc, w_proj, k_cache, v_cache, cache_len, status, y, scratch,
                     static_cast<hipStream_t>(stream));
 }
 
 int decode_step_noalloc(const blk_dcfg* cfg, const void* x, const void* w_qkv, const void* w_o, const void* w_fc,
-                        const void* w_proj, void* k_cache, void* v_cache, const int32_t* cache_len, void* y,
-                        void* stream) {
-  if (int e = check_decode_args(cfg, x, w_qkv, w_o, w_fc, w_proj, k_cache, v_cache, cache_len, y)) return e;
+                        const void* w_proj, void* k_cache, void* v_cache, const int32_t* cache_len, int32_t* status,
+                        void* y, void* stream) {
+  if (int e = check_decode_args(cfg, x, w_qkv, w_o, w_fc, w_proj, k_cache, v_cache, cache_len, status, y)) return e;
   if (carve_dec(*cfg, nullptr).bytes > BLK_NOALLOC_SCRATCH_BYTES) return BLK_ELIMIT;
   void* ws = nullptr;
   if (int e = noalloc_workspace(&ws)) return e;
-  return decode_run(*cfg, x, w_qkv, w_o, w_fc, w_proj, k_cache, v_cache, cache_len, y, ws,
+  return decode_run(*cfg, x, w_qkv, w_o, w_fc, w_proj, k_cache, v_cache, cache_len, status, y, ws,
                     static_cast<hipStream_t>(stream));
 }
 

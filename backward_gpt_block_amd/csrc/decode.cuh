@@ -35,10 +35,12 @@ __device__ __forceinline__ float block_sum256(float v, float* sh) {
 }
 
 // h[b, :] = bf16(x[b, :] / rms(x[b, :])), C % 8 == 0, C <= 256 * 8 * 4.
+// The first kernel of a step: it also clears the step's status word.
 __global__ __launch_bounds__(256) void dec_rmsnorm_kernel(const bf16* __restrict__ x, int C, float eps,
-                                                          bf16* __restrict__ h) {
+                                                          bf16* __restrict__ h, int* __restrict__ status) {
   __shared__ float sh[4];
   const long row = blockIdx.x;
+  if (status && row == 0 && threadIdx.x == 0) *status = 0;
   const int nch = C / 8;
   float f[4][8];
   float ss = 0.f;
@@ -135,8 +137,16 @@ __device__ __forceinline__ float sum_parts(const float* __restrict__ part, int S
   return v;
 }
 
+// Position of sequence b's new token.  A length outside [0, S_max - 1] is
+// an argument error of that sequence: the kernels that read the cache use
+// the clamped value (every access stays inside the cache), the slot is not
+// written, the status word counts the sequence and its output row is NaN.
 __device__ __forceinline__ int clamp_pos(const int* __restrict__ cache_len, int b, int S_max) {
   return min(max(cache_len[b], 0), S_max - 1);
+}
+__device__ __forceinline__ bool pos_ok(const int* __restrict__ cache_len, int b, int S_max) {
+  const int p = cache_len[b];
+  return p >= 0 && p < S_max;
 }
 
 // From the QKV partials of row b: q and k rotated by the angle of position
@@ -147,9 +157,12 @@ __device__ __forceinline__ int clamp_pos(const int* __restrict__ cache_len, int 
 __global__ __launch_bounds__(192) void dec_qkv_epi_kernel(const float* __restrict__ part, int S, int B, int H, int G,
                                                           const int* __restrict__ cache_len, int S_max, float eps,
                                                           double rope_base, float* __restrict__ qbuf,
-                                                          bf16* __restrict__ kc, bf16* __restrict__ vc) {
+                                                          bf16* __restrict__ kc, bf16* __restrict__ vc,
+                                                          int* __restrict__ status) {
   const int h = blockIdx.x, b = blockIdx.y, which = threadIdx.x >> 6, i = threadIdx.x & 63;
-  if (which > 0 && h >= G) return;
+  const bool ok = pos_ok(cache_len, b, S_max);
+  if (!ok && status && h == 0 && threadIdx.x == 0) atomicAdd(status, 1);
+  if (which > 0 && (h >= G || !ok)) return;   // no cache write for an out-of-range length
   const int C = H * 128;
   const long LD = C + 256L * G;                 // q | k | v columns
   const long stride = (long)B * LD;
@@ -394,12 +407,15 @@ __global__ __launch_bounds__(256) void dec_relu2_kernel(const float* __restrict_
   a[i] = (bf16)(u * u);
 }
 
-// y = bf16(y1 + sum_s part[s]) over n values.
+// y = bf16(y1 + sum_s part[s]) over n = B*C values; NaN in the rows of
+// sequences whose length is out of range.
 __global__ __launch_bounds__(256) void dec_out_kernel(const float* __restrict__ part, int S, long n,
-                                                      const float* __restrict__ y1, bf16* __restrict__ y) {
+                                                      const float* __restrict__ y1, bf16* __restrict__ y,
+                                                      const int* __restrict__ cache_len, int S_max, int C) {
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
-  y[i] = (bf16)(y1[i] + sum_parts(part, S, n, i));
+  const float v = y1[i] + sum_parts(part, S, n, i);
+  y[i] = (bf16)(pos_ok(cache_len, (int)(i / C), S_max) ? v : __builtin_nanf(""));
 }
 
 }  // namespace dec

@@ -204,17 +204,22 @@ size_t decode_scratch_bytes(const blk_dcfg* cfg);
  *           and values; slot p_b of each (b, h) is written here, slots
  *           0..p_b are attended, slots beyond p_b are neither read nor written
  *   cache_len [B] int32 DEVICE array, read only (the caller advances it);
- *           every entry must satisfy 0 <= cache_len[b] <= S_max-1 (entries
- *           outside that range are clamped into it by the kernels)
+ *           every entry must satisfy 0 <= cache_len[b] <= S_max-1.  The
+ *           lengths live on the device, so the host cannot check them: a
+ *           sequence whose entry is outside that range is an error of that
+ *           sequence only: its cache slots are not written, its row of y is
+ *           NaN, and the step counts it in *status
+ *   status  one int32 DEVICE word, or NULL: set by the step to the number of
+ *           sequences whose cache_len is out of range (0 when all are valid)
  *   y       [B,C] output (bf16); may be the same buffer as x
  *   scratch at least decode_scratch_bytes(cfg) bytes of device memory
  * Only cfg->dtype == BLK_BF16 and C <= 2048 are implemented (else
  * BLK_EUNSUPPORTED).  BLK_EINVAL for a bad cfg, a NULL pointer, or
  * k_cache == v_cache; BLK_EALIGN for a data pointer not 16-byte aligned or
- * cache_len not 4-byte aligned; BLK_ENOSPC for a short scratch. */
+ * cache_len / status not 4-byte aligned; BLK_ENOSPC for a short scratch. */
 int decode_step(const blk_dcfg* cfg, const void* x,
                 const void* w_qkv, const void* w_o, const void* w_fc, const void* w_proj,
-                void* k_cache, void* v_cache, const int32_t* cache_len, void* y,
+                void* k_cache, void* v_cache, const int32_t* cache_len, int32_t* status, void* y,
                 void* scratch, size_t scratch_bytes, void* stream);
 
 /* Bytes of the static workspace decode_step_noalloc uses on each device. */
@@ -234,7 +239,8 @@ int decode_step(const blk_dcfg* cfg, const void* x,
  * and give wrong results; calls enqueued in order on one stream do not. */
 int decode_step_noalloc(const blk_dcfg* cfg, const void* x,
                         const void* w_qkv, const void* w_o, const void* w_fc, const void* w_proj,
-                        void* k_cache, void* v_cache, const int32_t* cache_len, void* y, void* stream);
+                        void* k_cache, void* v_cache, const int32_t* cache_len, int32_t* status, void* y,
+                        void* stream);
 
 /* The quantiser of the fp8 mode as a standalone call: amax = max |x| over
  * the n bf16 values at x (n a multiple of 8), written as float bits to the

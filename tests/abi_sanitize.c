@@ -97,16 +97,18 @@ int main(void) {
   expect("decode scratch nonzero", dneed > 0, 1);
   expect("decode null cfg", (int)decode_scratch_bytes(NULL), 0);
   expect("decode null x", decode_step(&d, NULL, P(A), P(A), P(A), P(A), P(A + 0x100), P(A + 0x200), (int32_t*)P(A),
-                                      P(A), P(A), big, 0), BLK_EINVAL);
+                                      NULL, P(A), P(A), big, 0), BLK_EINVAL);
   expect("decode caches alias", decode_step(&d, P(A), P(A), P(A), P(A), P(A), P(A + 0x100), P(A + 0x100),
-                                            (int32_t*)P(A), P(A), P(A), big, 0), BLK_EINVAL);
+                                            (int32_t*)P(A), NULL, P(A), P(A), big, 0), BLK_EINVAL);
   expect("decode misaligned len", decode_step(&d, P(A), P(A), P(A), P(A), P(A), P(A + 0x100), P(A + 0x200),
-                                              (int32_t*)P(A + 2), P(A), P(A), big, 0), BLK_EALIGN);
+                                              (int32_t*)P(A + 2), NULL, P(A), P(A), big, 0), BLK_EALIGN);
   expect("decode short scratch", decode_step(&d, P(A), P(A), P(A), P(A), P(A), P(A + 0x100), P(A + 0x200),
-                                             (int32_t*)P(A), P(A), P(A), dneed - 1, 0), BLK_ENOSPC);
+                                             (int32_t*)P(A), NULL, P(A), P(A), dneed - 1, 0), BLK_ENOSPC);
+  expect("decode misaligned status", decode_step(&d, P(A), P(A), P(A), P(A), P(A), P(A + 0x100), P(A + 0x200),
+                                                 (int32_t*)P(A), (int32_t*)P(A + 6), P(A), P(A), big, 0), BLK_EALIGN);
   blk_dcfg dbad = d;
   dbad.dtype = BLK_F32;
-  expect("decode f32", decode_step(&dbad, P(A), P(A), P(A), P(A), P(A), P(A + 0x100), P(A + 0x200), (int32_t*)P(A),
+  expect("decode f32", decode_step(&dbad, P(A), P(A), P(A), P(A), P(A), P(A + 0x100), P(A + 0x200), (int32_t*)P(A), NULL,
                                    P(A), P(A), big, 0), BLK_EUNSUPPORTED);
 
   /* head */

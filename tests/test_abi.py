@@ -171,6 +171,7 @@ def test_decode_sizes_and_argument_errors(lib):
     assert _dec(c, v_cache=A + 0x500) == bl.binding.BLK_EINVAL      # v_cache aliases k_cache
     assert _dec(c, w_fc=MIS) == bl.binding.BLK_EALIGN
     assert _dec(c, cache_len=A + 0x702) == bl.binding.BLK_EALIGN
+    assert _dec(c, status=A + 0x906) == bl.binding.BLK_EALIGN
     assert _dec(c, scratch_bytes=need - 1) == bl.binding.BLK_ENOSPC
 
 

@@ -167,3 +167,38 @@ def test_decode_gqa_window_two_chained_steps():
 
 def test_decode_d20_gqa_ragged_128_2048():
     _decode_case(DECODE_WORKLOADS["d20_decode_gqa"], ragged=True, ragged_lo=128, ragged_hi=2048)
+
+
+def test_decode_out_of_range_lengths_reported():
+    # lengths outside [0, S_max - 1] are errors of their sequences: no cache
+    # write, a NaN row of y, counted in the status word; the other sequences
+    # are computed as usual
+    import torch
+    import backward_gpt_block_amd as bl
+    from oracle import block as ob
+    sh = DecodeShape(B=4, C=256, H=2, F=1024, S_max=64)
+    note("decode out-of-range lengths")
+    inp = make_decode_inputs(sh, seed=12)
+    lens = np.array([5, -1, 64, 63], dtype=np.int32)
+    g = GpuDecode(sh, inp)
+    before = [t.clone() for t in (g.kc, g.vc)]
+    x = to_dev(inp["x"], "bf16")
+    y = poison_(torch.empty_like(x))
+    status = torch.full((1,), -7, dtype=torch.int32, device="cuda:0")
+    bl.decode_step(g.cfg, x, *g.w, g.kc, g.vc, torch.from_numpy(lens).to("cuda:0"), y, g.scratch, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 2
+    yn = to_np(y)
+    assert np.all(np.isnan(yn[[1, 2]]))
+    for t, t0 in zip((g.kc, g.vc), before):
+        assert torch.equal(t[[1, 2]], t0[[1, 2]]), "a sequence with an invalid length changed its cache"
+    ok = [0, 3]
+    W = [inp[k] for k in WNAMES]
+    y_ref, _, _ = ob.decode_step(inp["x"][ok], *W, inp["k_cache"][ok], inp["v_cache"][ok], lens[ok], H=sh.H,
+                                 eps=sh.eps, rope_base=sh.rope_base)
+    assert rel_err(yn[ok], y_ref) <= TOL["bf16"]
+    # a valid step afterwards resets the word
+    bl.decode_step(g.cfg, x, *g.w, g.kc, g.vc, torch.from_numpy(np.array([1, 2, 3, 4], dtype=np.int32)).to("cuda:0"),
+                   y, g.scratch, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
