@@ -792,7 +792,6 @@ DecSplit dec_split(int M, int N, int K) {
 }
 
 struct DecScratch {
-  bf16* h1;       // [B, C]
   float* part;    // [S][B][N], the largest of the four GEMMs
   float* q;       // [B, H, 128]
   float* opart;   // [B, H, NS, 128]
@@ -812,7 +811,6 @@ DecScratch carve_dec(const blk_dcfg& c, void* p) {
   for (const auto& g : nk) part = std::max(part, (long)dec_split((int)B, (int)g[0], (int)g[1]).S * B * g[0]);
   Carver k(p);
   DecScratch d;
-  d.h1 = k.take<bf16>(B * C);
   d.part = k.take<float>(part);
   d.q = k.take<float>(B * H * 128);
   d.opart = k.take<float>(B * H * NS * 128);
@@ -858,16 +856,13 @@ int decode_run(const blk_dcfg& c, const void* x, const void* w_qkv, const void* 
   bf16* kc = static_cast<bf16*>(k_cache);
   bf16* vc = static_cast<bf16*>(v_cache);
   const int NS = (c.S_max + dec::KEYS - 1) / dec::KEYS;
-  {  // h1 = rmsnorm(x)
-    Timed t("dec_rmsnorm", st);
-    hipLaunchKernelGGL(dec::dec_rmsnorm_kernel, dim3(B), dim3(256), 0, st, xb, C, c.eps, d.h1, (int*)status);
-  }
+  // x W_qkv^T (the row scale r1 of rmsnorm(x) is applied in the epilogue kernel)
   const DecSplit sq = dec_split(B, (int)qkv_width(c), C);
-  dec_gemm("dec_gemm_qkv", d.h1, B, static_cast<const bf16*>(w_qkv), (int)qkv_width(c), C, sq, d.part, st);
-  {  // rotary + QK-norm at position cache_len[b]; k, v into the caches
+  dec_gemm("dec_gemm_qkv", xb, B, static_cast<const bf16*>(w_qkv), (int)qkv_width(c), C, sq, d.part, st);
+  {  // r1; rotary + QK-norm at position cache_len[b]; k, v into the caches
     Timed t("dec_qkv_epi", st);
     hipLaunchKernelGGL(dec::dec_qkv_epi_kernel, dim3(H, B), dim3(192), 0, st, (const float*)d.part, sq.S, B, H,
-                       kv_heads(c), cache_len, c.S_max, c.eps, (double)c.rope_base, d.q, kc, vc, (int*)status);
+                       kv_heads(c), xb, cache_len, c.S_max, c.eps, (double)c.rope_base, d.q, kc, vc);
   }
   const int dwin = c.window > 0 ? c.window : INT_MAX;
   {  // attention of the new token over slots 0..cache_len[b] (the last W with a window)
@@ -903,7 +898,8 @@ int decode_run(const blk_dcfg& c, const void* x, const void* w_qkv, const void* 
     Timed t("dec_out", st);
     const long n = (long)B * C;
     hipLaunchKernelGGL(dec::dec_out_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                       (const float*)d.part, sp.S, n, (const float*)d.y1, static_cast<bf16*>(y), cache_len, c.S_max, C);
+                       (const float*)d.part, sp.S, n, (const float*)d.y1, static_cast<bf16*>(y), cache_len, c.S_max, C,
+                       (int*)status);
   }
   return launch_status();
 }

@@ -6,9 +6,11 @@
 // The step reads every weight once (12 C^2 values) and each sequence's cache
 // (2 x H x L x 128 values): it is bound by HBM bandwidth, not by MFMA.
 //
-//   dec_rmsnorm_kernel     h1 = rmsnorm(x)                          [B, C]
 //   skinny_gemm_kernel     part[s] = A W^T over K-split s           (x4)
-//   dec_qkv_epi_kernel     rotary + QK-norm of q, k; k, v into slot p
+//                          (the QKV one on x itself: rmsnorm(x) W^T =
+//                          r1 (x W^T), with r1 = 1/rms(x) a row scale)
+//   dec_qkv_epi_kernel     r1 of the row; rotary + QK-norm of q, k; k, v
+//                          into slot p
 //   dec_attn_kernel        per 256-key split: max, sum, sum p v
 //   dec_combine_kernel     merge the splits -> o                    [B, C]
 //   dec_resid_norm_kernel  y1 = x + o W_o^T; h2 = rmsnorm(y1)
@@ -32,38 +34,6 @@ __device__ __forceinline__ float block_sum256(float v, float* sh) {
   v = sh[0] + sh[1] + sh[2] + sh[3];
   __syncthreads();
   return v;
-}
-
-// h[b, :] = bf16(x[b, :] / rms(x[b, :])), C % 8 == 0, C <= 256 * 8 * 4.
-// The first kernel of a step: it also clears the step's status word.
-__global__ __launch_bounds__(256) void dec_rmsnorm_kernel(const bf16* __restrict__ x, int C, float eps,
-                                                          bf16* __restrict__ h, int* __restrict__ status) {
-  __shared__ float sh[4];
-  const long row = blockIdx.x;
-  if (status && row == 0 && threadIdx.x == 0) *status = 0;
-  const int nch = C / 8;
-  float f[4][8];
-  float ss = 0.f;
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int ch = threadIdx.x + 256 * u;
-    if (ch < nch) {
-      Chunk<bf16>::unpack(ld16(x + row * C + ch * 8), f[u]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ss += f[u][e] * f[u][e];
-    }
-  }
-  const float r = 1.f / sqrtf(block_sum256(ss, sh) / (float)C + eps);
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int ch = threadIdx.x + 256 * u;
-    if (ch < nch) {
-      float g[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) g[e] = f[u][e] * r;
-      st16(h + row * C + ch * 8, Chunk<bf16>::pack(g));
-    }
-  }
 }
 
 // Skinny GEMM for a few rows: part[s][m][n] = sum over K-split s of
@@ -149,25 +119,32 @@ __device__ __forceinline__ bool pos_ok(const int* __restrict__ cache_len, int b,
   return p >= 0 && p < S_max;
 }
 
-// From the QKV partials of row b: q and k rotated by the angle of position
-// p = cache_len[b] and RMS-normalised per head (QK-norm); q (float32) into
-// qbuf[b, h, :], k and v (bf16) into slot p of the caches of key/value head
-// h (h < G).  Grid (H, B), 3 waves: q, k, v of head h; lane i owns the pair
-// (i, i + 64).
+// From the QKV partials of row b (products with x itself): times r1 =
+// 1/rms(x[b]) they are rmsnorm(x) W^T; q and k rotated by the angle of
+// position p = cache_len[b] and RMS-normalised per head (QK-norm); q
+// (float32) into qbuf[b, h, :], k and v (bf16) into slot p of the caches of
+// key/value head h (h < G).  Grid (H, B), 3 waves: q, k, v of head h; lane i
+// owns the pair (i, i + 64); each wave computes r1 of the row itself.
 __global__ __launch_bounds__(192) void dec_qkv_epi_kernel(const float* __restrict__ part, int S, int B, int H, int G,
-                                                          const int* __restrict__ cache_len, int S_max, float eps,
-                                                          double rope_base, float* __restrict__ qbuf,
-                                                          bf16* __restrict__ kc, bf16* __restrict__ vc,
-                                                          int* __restrict__ status) {
+                                                          const bf16* __restrict__ x, const int* __restrict__ cache_len,
+                                                          int S_max, float eps, double rope_base,
+                                                          float* __restrict__ qbuf, bf16* __restrict__ kc,
+                                                          bf16* __restrict__ vc) {
   const int h = blockIdx.x, b = blockIdx.y, which = threadIdx.x >> 6, i = threadIdx.x & 63;
-  const bool ok = pos_ok(cache_len, b, S_max);
-  if (!ok && status && h == 0 && threadIdx.x == 0) atomicAdd(status, 1);
-  if (which > 0 && (h >= G || !ok)) return;   // no cache write for an out-of-range length
+  if (which > 0 && (h >= G || !pos_ok(cache_len, b, S_max))) return;   // no cache write for an out-of-range length
   const int C = H * 128;
+  float ss = 0.f;
+  for (int c = 8 * i; c < C; c += 512) {
+    float f[8];
+    Chunk<bf16>::unpack(ld16(x + (long)b * C + c), f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss += f[e] * f[e];
+  }
+  const float r1 = 1.f / sqrtf(wave_sum(ss) / (float)C + eps);
   const long LD = C + 256L * G;                 // q | k | v columns
   const long stride = (long)B * LD;
   const long base = (long)b * LD + (which == 0 ? 0 : which == 1 ? C : C + 128L * G) + h * 128;
-  float z1 = sum_parts(part, S, stride, base + i), z2 = sum_parts(part, S, stride, base + i + 64);
+  float z1 = r1 * sum_parts(part, S, stride, base + i), z2 = r1 * sum_parts(part, S, stride, base + i + 64);
   const int p = clamp_pos(cache_len, b, S_max);
   const long slot = ((long)(b * G + h) * S_max + p) * 128;
   if (which == 2) {
@@ -408,11 +385,18 @@ __global__ __launch_bounds__(256) void dec_relu2_kernel(const float* __restrict_
 }
 
 // y = bf16(y1 + sum_s part[s]) over n = B*C values; NaN in the rows of
-// sequences whose length is out of range.
+// sequences whose length is out of range, whose count thread 0 writes to
+// *status (when given).
 __global__ __launch_bounds__(256) void dec_out_kernel(const float* __restrict__ part, int S, long n,
                                                       const float* __restrict__ y1, bf16* __restrict__ y,
-                                                      const int* __restrict__ cache_len, int S_max, int C) {
+                                                      const int* __restrict__ cache_len, int S_max, int C,
+                                                      int* __restrict__ status) {
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (status && i == 0) {
+    int bad = 0;
+    for (int b = 0; b < (int)(n / C); ++b) bad += pos_ok(cache_len, b, S_max) ? 0 : 1;
+    *status = bad;
+  }
   if (i >= n) return;
   const float v = y1[i] + sum_parts(part, S, n, i);
   y[i] = (bf16)(pos_ok(cache_len, (int)(i / C), S_max) ? v : __builtin_nanf(""));
