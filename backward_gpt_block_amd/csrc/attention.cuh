@@ -1500,6 +1500,13 @@ constexpr int DSQ_TILE = DSQ_KT * 256;           // bytes of a [32][128] bf16 ti
 constexpr int DSQ_SLOT = 2 * DSQ_TILE;           // K tile, dS^T tile
 constexpr int DSQ_NSLOT = 5;
 constexpr int DSQ_LDS = DSQ_NSLOT * DSQ_SLOT;    // 80 KiB: two workgroups fill a CU's LDS
+// The dS^T tile is two sub-tiles (the unit's two 64-query blocks) of 32 key
+// rows x 128 bytes; chunk c (16 bytes) of row r sits at c ^ dsq_sw(r).  A
+// 16-lane transpose read touches 4 consecutive rows x 2 adjacent chunks: the
+// 8 pieces fall in distinct 16-byte bank groups of a 128-byte (32-bank) line,
+// and a 32-lane read's 16 pieces in distinct groups of a 256-byte (64-bank)
+// line.
+__device__ __forceinline__ int dsq_sw(int row) { return 2 * (row & 3); }
 }  // namespace fa
 __global__ __launch_bounds__(256, 2) void attn_bwd_dq_ds_kernel(AttnArgs a) {
   using namespace fa;
@@ -1537,9 +1544,12 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_ds_kernel(AttnArgs a) {
       const int row = p >> 4, c = (p & 15) ^ sw(row);
       const uint32_t ok = (uint32_t)((long)(t * DSQ_KT + row) * ldb + koff + c * 16);
       dma16(rk, (lds_u32*)(d + base * 16), ok);
-      // LDS chunk c of key row `row`: block 2u + c/8, 1 KiB chunk (c/2) % 4,
-      // piece of key row + 32 (c & 1)
-      const uint32_t od = (uint32_t)(row0 + (c >> 3) * 16384 + ((c >> 1) & 3) * 1024 + (row + 32 * (c & 1)) * 16);
+      // dS^T slot p: sub-tile blk (query block 2u + blk), key row r, chunk cd
+      // (8 queries: 1 KiB chunk cd/2 of the block's stored fragments, piece
+      // of key row r + 32 (cd & 1)); one issue covers 8 key rows of a
+      // sub-tile, so it reads 8 whole 128-byte lines
+      const int blk = p >> 8, r = (p >> 3) & 31, cd = (p & 7) ^ dsq_sw(r);
+      const uint32_t od = (uint32_t)(row0 + blk * 16384 + (cd >> 1) * 1024 + (r + 32 * (cd & 1)) * 16);
       dma16(rd, (lds_u32*)(d + DSQ_TILE + base * 16), od);
     }
   };
@@ -1549,6 +1559,23 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_ds_kernel(AttnArgs a) {
     frag_vt_offsets(vo, lane);
     vbase = vo[0];
   }
+  // dS^T transpose read of this lane (as frag_vt_x: keys 4 (g/2) + s/4, the
+  // 4 queries from 16 (g & 1) + 4 (s & 3) of the wave's 32); keys + 8 (the
+  // second read) and + 16 (MFMA chunk 1) keep the swizzle
+  int sbase;
+  {
+    const int g = (lane >> 4) & 3, s = lane & 15;
+    const int key = 4 * (g >> 1) + (s >> 2), col = (wave & 1) * 32 + 16 * (g & 1) + 4 * (s & 3);
+    sbase = (wave >> 1) * 4096 + key * 128 + (((col >> 3) ^ dsq_sw(key)) << 4) + (col & 7) * 2;
+  }
+  auto frag_ds = [&](const lds_char* st, int mm) {
+    const lds_char* q = st + mm * 2048 + sbase;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)q);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(q + 1024));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const s16x8 r = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, r);
+  };
   f32x16 acc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -1568,7 +1595,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_ds_kernel(AttnArgs a) {
     const lds_char* st_ = kt_ + DSQ_TILE;
 #pragma unroll
     for (int mm = 0; mm < 2; ++mm) {
-      const bf16x8 bf = frag_vt_x(st_, vbase, mm, wave);   // dS^T: this wave's 32 queries
+      const bf16x8 bf = frag_ds(st_, mm);   // dS^T: this wave's 32 queries
 #pragma unroll
       for (int db = 0; db < 4; ++db) acc[db] = MM::mma(frag_vt_x(kt_, vbase, mm, db), bf, acc[db]);
     }
