@@ -1203,15 +1203,19 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_bf16_kernel(AttnArgs a) 
       rd(1);
   #pragma unroll
       for (int i = 0; i < 32; ++i) {
+        // lse and delta for the softmax of the next step, read ahead of this
+        // step's fragments: LDS reads complete in order, so waiting for them
+        // then leaves the fragment reads in flight
+        if ((i & 1) == 0 && i >= 8 && i < 24) {
+          ldv(i < 16 ? 0 : 1, (i & 7) >> 1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
         if (i + 2 < 32) rd(i + 2);
         if (i < 16) {
           const int qb = i >> 3, ks = i & 7;
           sv[qb] = MM::mma(fa[i], kf[ks], sv[qb]);   // S  (query x key)
           dp[qb] = MM::mma(fb[i], vf[ks], dp[qb]);   // dP (query x key)
-          if (qb == 1) {
-            if ((ks & 1) == 0) ldv(0, ks >> 1);
-            else smx(0, ks >> 1);
-          }
+          if (qb == 1 && (ks & 1)) smx(0, ks >> 1);
         } else {
           const int u = i - 16, qb = u >> 3, mm = (u >> 2) & 1, db = u & 3;
           if ((u & 7) == 0) {
@@ -1228,10 +1232,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_bf16_kernel(AttnArgs a) 
           }
           dv[db] = MM::mma(fa[i], pf[mm], dv[db]);     // dV^T += dO^T P
           dk[db] = MM::mma(fb[i], sf[mm], dk[db]);     // dK^T += Q^T dS
-          if (qb == 0) {
-            if ((u & 1) == 0) ldv(1, u >> 1);
-            else smx(1, u >> 1);
-          }
+          if (qb == 0 && (u & 1)) smx(1, u >> 1);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
