@@ -1147,7 +1147,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_bf16_kernel(AttnArgs a) 
       if (q0 + QT - 1 < kw0) {                     // all queries precede all keys of this wave
         if constexpr (DS) {   // zeros, in 4 stores like the computed iterations
 #pragma unroll
-          for (int c = 0; c < 4; ++c) st16(dsb + 512 * c, u32x4{0u, 0u, 0u, 0u});
+          for (int c = 0; c < 4; ++c) __builtin_nontemporal_store(u32x4{0u, 0u, 0u, 0u}, (u32x4*)(dsb + 512 * c));
         }
         continue;
       }
@@ -1227,7 +1227,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_bf16_kernel(AttnArgs a) 
             if constexpr (DS) {
               // chunk 4 wave + 2 qb + m: queries qb*32 + 16m + 4(lane/32) + 0..3 and + 8
   #pragma unroll
-              for (int m = 0; m < 2; ++m) st16(dsb + 512 * (2 * qb + m), __builtin_bit_cast(u32x4, sf[m]));
+              for (int m = 0; m < 2; ++m)
+                __builtin_nontemporal_store(__builtin_bit_cast(u32x4, sf[m]), (u32x4*)(dsb + 512 * (2 * qb + m)));
             }
           }
           dv[db] = MM::mma(fa[i], pf[mm], dv[db]);     // dV^T += dO^T P
@@ -1551,7 +1552,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_ds_kernel(AttnArgs a) {
       // sub-tile, so it reads 8 whole 128-byte lines
       const int blk = p >> 8, r = (p >> 3) & 31, cd = (p & 7) ^ dsq_sw(r);
       const uint32_t od = (uint32_t)(row0 + blk * 16384 + (cd >> 1) * 1024 + (r + 32 * (cd & 1)) * 16);
-      dma16(rd, (lds_u32*)(d + DSQ_TILE + base * 16), od);
+      dma16_nt(rd, (lds_u32*)(d + DSQ_TILE + base * 16), od);
     }
   };
   int vbase;

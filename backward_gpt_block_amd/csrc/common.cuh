@@ -233,6 +233,16 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, const lds_u32* lds, uint32_t v
                : "memory", "m0");
 }
 
+// dma16 with the non-temporal cache policy: for data read once (streamed
+// through L2 without displacing what other workgroups still re-read).
+__device__ __forceinline__ void dma16_nt(i32x4 rsrc, const lds_u32* lds, uint32_t voffset) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+               :
+               : "s"(m0), "v"(voffset), "s"(rsrc)
+               : "memory", "m0");
+}
+
 // Workgroup barrier for LDS rings filled by dma16: waits for this wave's
 // own LDS accesses, then for every wave; unlike __syncthreads (whose memory
 // fence waits for all global loads in flight) it leaves the prefetched
