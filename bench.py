@@ -40,6 +40,10 @@ WORKLOAD_METRIC = {
     "d20_bf16_gqa": "training tokens/sec and TFLOP/s per decoder block (d20, T=2048, 2 key/value heads) on 1 MI355X",
 }
 DECODE_METRIC = "decode tokens/sec per decoder block (d20, batch 64, KV cache 2048) on 1 MI355X"
+DECODE_WORKLOAD_METRIC = {
+    "d20_decode": DECODE_METRIC,
+    "d20_decode_gqa": "decode tokens/sec per decoder block (d20, batch 64, KV cache 2048, 2 key/value heads) on 1 MI355X",
+}
 HEAD_METRIC = "training tokens/sec of the lm_head + cross-entropy (d20, 65,536 tokens, vocabulary 65,536) on 1 MI355X"
 PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3, "fp8": 5033.2}
 HBM_PEAK_GBS = 8000.0
@@ -555,7 +559,7 @@ def bench_decode(args) -> int:
         log(f"cpu baseline: {cpu}")
     ra = sites_r.get("dec_attn")
     out = {
-        "metric": DECODE_METRIC, "value": round(sh.B / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "metric": DECODE_WORKLOAD_METRIC.get(args.workload, DECODE_METRIC), "value": round(sh.B / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": args.workload, "B": sh.B, "C": sh.C, "H": sh.H, "D": sh.D, "F": sh.F,
