@@ -771,13 +771,27 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(AttnArgs a) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+    // K fragments read two k-steps ahead of their MFMAs (read just before
+    // them, every MFMA pair waited out the LDS latency)
+    bf16x8 kf0[8], kf1[8];
+    auto rdk = [&](int ks) {
+      kf0[ks] = *(lds_bf16x8*)(kt_ + ko[ks]);
+      kf1[ks] = *(lds_bf16x8*)(kt_ + 8192 + ko[ks]);
+    };
+    rdk(0);
+    rdk(1);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      const bf16x8 k0f = *(lds_bf16x8*)(kt_ + ko[ks]);
-      const bf16x8 k1f = *(lds_bf16x8*)(kt_ + 8192 + ko[ks]);
-      s[0] = MM::mma(k0f, qf[ks], s[0]);
-      s[1] = MM::mma(k1f, qf[ks], s[1]);
+      if (ks + 2 < 8) rdk(ks + 2);
+      s[0] = MM::mma(kf0[ks], qf[ks], s[0]);
+      s[1] = MM::mma(kf1[ks], qf[ks], s[1]);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    // the first V^T fragments of the PV product, read while the softmax runs
+    bf16x8 vf[16];
+    auto rdv = [&](int i) { vf[i] = frag_vt_at(vt_, vo, i >> 2, i & 3); };
+    rdv(0);
+    rdv(1);
     // Online softmax with a lazily updated reference: scores are exponentiated
     // against m_run, which only moves (rescaling l and O) when some lane's tile
     // maximum exceeds it by more than 8 (a factor 256, far from overflow).
@@ -819,11 +833,15 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(AttnArgs a) {
         ls += p;
       }
     l_run += ls;
+    // O^T += V^T P^T, the V^T fragments read two MFMAs ahead
+    bf16x8 p0;
 #pragma unroll
-    for (int mm = 0; mm < 4; ++mm) {
-      const bf16x8 p0 = frag_regs<bf16>(s[mm >> 1], (mm & 1) * 8);
-#pragma unroll
-      for (int db = 0; db < 4; ++db) o[db] = MM::mma(frag_vt_at(vt_, vo, mm, db), p0, o[db]);
+    for (int i = 0; i < 16; ++i) {
+      if (i + 2 < 16) rdv(i + 2);
+      const int mm = i >> 2, db = i & 3;
+      if (db == 0) p0 = frag_regs<bf16>(s[mm >> 1], (mm & 1) * 8);
+      o[db] = MM::mma(vf[i], p0, o[db]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   float mx = 0.f;
