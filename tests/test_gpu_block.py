@@ -40,6 +40,8 @@ def test_d6_f32_full_workload():
     (3, 1, 256),      # T = 1
     (1, 520, 768),    # d12 width, ragged
     (2, 192, 384),    # token count a multiple of 64 (weight gradients on the eight-wave body), ragged width
+    (1, 4096, 256),   # the longest sequence whose dS the dK/dV pass stores for the dQ pass
+    (1, 4160, 256),   # past it: the dQ pass recomputes dS (causal), ragged last tiles
 ])
 def test_bf16_ragged(B, T, C):
     _parity(BlockShape(B=B, T=T, C=C, H=C // 128, F=4 * C, dtype="bf16"))
