@@ -884,14 +884,16 @@ typedef __attribute__((address_space(3))) const f32x4 lds_f32x4;
 // passes: pass i gives this lane row 4i + lane/16 and dims 8 (lane & 15) .. +7.
 __device__ __forceinline__ int stg_idx(int row, int d) { return row * 128 + ((((d >> 2) ^ row) & 31) << 2) + (d & 3); }
 // (row: the staging row of this lane's column; lane & 31 unless permuted)
+// (registers r .. r+3, r % 4 == 0, are 4 consecutive dims: one 16-byte chunk)
 __device__ __forceinline__ void stage_acc(float* stg, const f32x16* acc, float scale, int lane, int row = -1) {
   if (row < 0) row = lane & 31;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) {
+    for (int r = 0; r < 16; r += 4) {
       const int d = db * 32 + acc_row(r, lane);
-      *reinterpret_cast<float2*>(stg + stg_idx(row, d)) = make_float2(acc[db][r] * scale, acc[db][r + 1] * scale);
+      *reinterpret_cast<f32x4*>(stg + stg_idx(row, d)) =
+          f32x4{acc[db][r] * scale, acc[db][r + 1] * scale, acc[db][r + 2] * scale, acc[db][r + 3] * scale};
     }
 }
 __device__ __forceinline__ void unstage_row(const float* stg, int i, int lane, float* f) {
@@ -916,18 +918,31 @@ __device__ __forceinline__ float store_rows(const float* stg, bf16* out, long ld
 }
 // Operands of the QK-norm backward of the wave's 32 rows: the normalised rows
 // z (row r at z + r*ld) and their factors rho[r * rs], zero past nrows.
+// Also the rotary angles (cs: [T][64]) of the first two passes of rows
+// t0 .. (the later passes load theirs two passes ahead).
 struct QkRows {
   u32x4 z[8];
   float p[8];
+  u32x4 cs[2][4];
 };
+// angle-table chunks of pass i (rows 4i + lane/16 of t0 ..; rows past nrows
+// read a valid row, their results are not stored)
+__device__ __forceinline__ void cs_rows_load(u32x4* c, const float2* cs, int t0, int i, int nrows, int lane) {
+  const int t = nrows > 0 ? t0 + min(4 * i + (lane >> 4), nrows - 1) : 0;
+  const float* cp = reinterpret_cast<const float*>(cs + (long)t * 64 + (lane & 7) * 8);
+#pragma unroll
+  for (int h = 0; h < 4; ++h) c[h] = ld16(cp + 4 * h);
+}
 __device__ __forceinline__ void qk_rows_load(QkRows& q, const bf16* z, long ld, const float* rho, long rs, int nrows,
-                                             int lane) {
+                                             int lane, const float2* cs, int t0) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int r = 4 * i + (lane >> 4);
     q.z[i] = r < nrows ? ld16(z + r * ld + 8 * (lane & 15)) : u32x4{0u, 0u, 0u, 0u};
     q.p[i] = r < nrows ? rho[r * rs] : 0.f;
   }
+  cs_rows_load(q.cs[0], cs, t0, 0, nrows, lane);
+  cs_rows_load(q.cs[1], cs, t0, 1, nrows, lane);
 }
 // Gradient of q' or k' from the staged gradient g of the normalised rows:
 // QK-norm backward dz' = p (g - z mean(g z)) over the row's 128 dims (16
@@ -940,17 +955,15 @@ __device__ __forceinline__ float store_rows_qk(const float* stg, const QkRows& q
                                                const float2* cs, int t0, int nrows, int lane) {
   const int cg = lane & 15;
   float mx = 0.f;
-  // angle-table chunks of pass i + 2 loaded during pass i
+  // angle-table chunks of pass i + 2 loaded during pass i (passes 0 and 1
+  // came with the rows)
   u32x4 csr[2][4];
-  auto cs_load = [&](int i) {
-    // rows past nrows read a valid row (their results are not stored)
-    const int t = nrows > 0 ? t0 + min(4 * i + (lane >> 4), nrows - 1) : 0;
-    const float* cp = reinterpret_cast<const float*>(cs + (long)t * 64 + (cg & 7) * 8);
+  auto cs_load = [&](int i) { cs_rows_load(csr[i & 1], cs, t0, i, nrows, lane); };
 #pragma unroll
-    for (int h = 0; h < 4; ++h) csr[i & 1][h] = ld16(cp + 4 * h);
-  };
-  cs_load(0);
-  cs_load(1);
+  for (int h = 0; h < 4; ++h) {
+    csr[0][h] = q.cs[0][h];
+    csr[1][h] = q.cs[1][h];
+  }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     float g[8], z[8], c8[16];
@@ -1275,7 +1288,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_bf16_kernel(AttnArgs a) 
     QkRows qk;
     // key QK-norm factors: [N][H] after the query ones, head index kvh
     qk_rows_load(qk, qkv + row0 * a.LD + a.KO + cur.kvh * HD, a.LD, a.rho + ((long)a.B * a.T + row0) * a.H + cur.kvh,
-                 a.H, nrows, lane);
+                 a.H, nrows, lane, a.cs, kw0);
     stage_acc(stg, dv, 1.f, lane);
     mx = fmaxf(mx, store_rows(stg, drow + a.VO + cur.kvh * HD, a.LD, nrows, lane));
     stage_acc(stg, dk, a.rsd, lane);
@@ -1485,7 +1498,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_bf16_kernel(AttnArgs a) {
     const long row0 = (long)cur.b * a.T + qw0;
     const int nrows = min(32, a.T - qw0);
     QkRows qk;
-    qk_rows_load(qk, qkv + row0 * a.LD + cur.head * HD, a.LD, a.rho + row0 * a.H + cur.head, a.H, nrows, lane);
+    qk_rows_load(qk, qkv + row0 * a.LD + cur.head * HD, a.LD, a.rho + row0 * a.H + cur.head, a.H, nrows, lane, a.cs,
+                 qw0);
     stage_acc(stg, acc, a.rsd, lane);
     mx = fmaxf(mx, store_rows_qk(stg, qk, static_cast<bf16*>(a.dqkv) + row0 * a.LD + cur.head * HD, a.LD, a.cs, qw0,
                                  nrows, lane));
@@ -1626,7 +1640,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_ds_kernel(AttnArgs a) {
   const int nrows = min(32, a.T - qw0);
   float* stg = reinterpret_cast<float*>(smem) + wave * 32 * 128;
   QkRows qk;
-  qk_rows_load(qk, qkv + row0 * a.LD + head * HD, a.LD, a.rho + row0 * a.H + head, a.H, nrows, lane);
+  qk_rows_load(qk, qkv + row0 * a.LD + head * HD, a.LD, a.rho + row0 * a.H + head, a.H, nrows, lane, a.cs, qw0);
   // lane l holds query qperm(l % 32): bits 2 and 3 of the position swapped
   const int l32 = lane & 31;
   stage_acc(stg, acc, a.rsd, lane, (l32 & 0x13) | ((l32 & 4) << 1) | ((l32 & 8) >> 1));
