@@ -35,6 +35,8 @@ static_assert(4 * 32 * 128 * 4 <= fa::DSQ_LDS, "dQ-from-dS staging rows fit in i
 constexpr int DQ_LDS = fa::LDS + 2 * fa::TILE;
 static_assert(DQ_LDS <= 160 * 1024 && 4 * 32 * 128 * 4 <= 2 * fa::SLOT && 2 * fa::TILE <= fa::SLOT, "dQ LDS");
 
+}  // namespace
+
 // Compute units of the current device (the grid of the persistent kernels:
 // one workgroup per CU); looked up once per device.
 int cu_count() {
@@ -51,7 +53,6 @@ int cu_count() {
   return cached[dev];
 }
 
-}  // namespace
 
 void attn_fwd(const AttnArgs& a, bool bf16, hipStream_t st) {
   if (bf16) {

@@ -47,5 +47,8 @@ struct AttnArgs {
 void attn_fwd(const AttnArgs& a, bool bf16, hipStream_t st);
 void attn_bwd_dkdv(const AttnArgs& a, bool bf16, hipStream_t st);
 void attn_bwd_dq(const AttnArgs& a, bool bf16, hipStream_t st);
+// Compute units of the current device (the grid of the persistent kernels;
+// attn.hip, looked up once per device).
+int cu_count();
 
 }  // namespace blk

@@ -353,8 +353,15 @@ void gemm(void (*kern)(GemmArgs), const char* name, GemmArgs g, int splits, hipS
     g.k_split = (int)(((per + BK - 1) / BK) * BK);
     splits = (g.K + g.k_split - 1) / g.k_split;
   }
+  g.nsplit = splits;
   Timed t(name, st);
-  hipLaunchKernelGGL(kern, dim3(g.tiles_m * g.tiles_n, splits), dim3(threads), LDS, st, g);
+  if (threads == 512) {
+    // the eight-wave kernels are persistent: one workgroup per CU walks the tiles
+    const int total = g.tiles_m * g.tiles_n * splits;
+    hipLaunchKernelGGL(kern, dim3(std::min(total, cu_count())), dim3(threads), LDS, st, g);
+  } else {
+    hipLaunchKernelGGL(kern, dim3(g.tiles_m * g.tiles_n, splits), dim3(threads), LDS, st, g);
+  }
 }
 
 // Forward and input-gradient GEMMs (eight-wave kernels, no split): K and both

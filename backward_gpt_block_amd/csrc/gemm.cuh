@@ -46,6 +46,7 @@ struct GemmArgs {
   int M, N, K;
   int k_split;          // k-range per split (multiple of BK); grid splits = ceil(K / k_split)
   int tiles_m, tiles_n;
+  int nsplit;           // splits (the persistent eight-wave kernels walk tiles_m * tiles_n * nsplit tiles)
   void* out; long ldo;  // EPI_F32: split s writes out + s*M*ldo
   void* out2; long ldo2;
   const void* aux; long ldaux;
@@ -192,6 +193,25 @@ __device__ __forceinline__ void tile_coords(const GemmArgs& g, int& tm, int& tn,
   const int total = per_split * gridDim.y;
   int pid = blockIdx.x + blockIdx.y * gridDim.x;
   if (total % 8 == 0) pid = (pid % 8) * (total / 8) + pid / 8;
+  split = pid / per_split;
+  int t = pid % per_split;
+  int group = t / (GROUP * g.tiles_n);
+  int first_m = group * GROUP;
+  int gsize = min(g.tiles_m - first_m, GROUP);
+  int in_group = t % (GROUP * g.tiles_n);
+  tm = first_m + in_group % gsize;
+  tn = in_group / gsize;
+}
+// The same for tile v of a persistent grid of workgroups that walk the
+// total tiles in steps of the grid size: workgroup b runs on XCD b % 8 (the
+// grid is a multiple of 8 whenever total is), so tile v = b + i * grid
+// lands on the same XCD for every i, and the remap gives each XCD a
+// contiguous run of logical tiles exactly as for one workgroup per tile.
+__device__ __forceinline__ void tile_coords_v(const GemmArgs& g, int v, int total, int& tm, int& tn, int& split,
+                                              int GROUP = 8) {
+  const int per_split = g.tiles_m * g.tiles_n;
+  int pid = v;
+  if (total % 8 == 0 && gridDim.x % 8 == 0) pid = (pid % 8) * (total / 8) + pid / 8;
   split = pid / per_split;
   int t = pid % per_split;
   int group = t / (GROUP * g.tiles_n);
@@ -638,8 +658,9 @@ __device__ __forceinline__ void epi_prefetch(const GemmArgs& g, u32x4 (&pre)[2][
   }
 }
 
+// stage: 64 KiB of LDS (one operand slot), 8 KiB per wave
 template <typename TO, int EPI>
-__device__ __forceinline__ void epilogue_pp(const GemmArgs& g, f32x16 (&acc)[2][4], char* smem, int m0, int n0,
+__device__ __forceinline__ void epilogue_pp(const GemmArgs& g, f32x16 (&acc)[2][4], char* stage, int m0, int n0,
                                             int split, int wave, int lane, const u32x4 (&pre)[2][8]) {
   const int grp = wave >> 2, q = wave & 3;
   float alpha = g.alpha;
@@ -647,9 +668,10 @@ __device__ __forceinline__ void epilogue_pp(const GemmArgs& g, f32x16 (&acc)[2][
     const float a = __uint_as_float(*g.amax_a), b = __uint_as_float(*g.amax_b);
     alpha *= (a > 0.f ? a / 448.f : 1.f) * (b > 0.f ? b / 448.f : 1.f);
   }
-  // each wave parks 32 rows x 128 fp32 (16 KiB) at a time in its own region;
+  // each wave parks 16 rows x 128 fp32 (8 KiB) at a time in its own region
+  // (the other operand slot takes the next tile's first stage meanwhile);
   // LDS accesses of one wave complete in order, so no barrier is needed
-  char* wreg = smem + wave * 16384;
+  char* wreg = stage + wave * 8192;
   const int rbase = m0 + (q >> 1) * 128 + grp * 64, cbase = n0 + (q & 1) * 128;
   float mx = 0.f;
   // EPI_ROPE on a q or k head (the wave's 128 columns are one head): the
@@ -668,23 +690,27 @@ __device__ __forceinline__ void epilogue_pp(const GemmArgs& g, f32x16 (&acc)[2][
     cs_load(0);
     cs_load(1);
   }
+  // registers 8h .. 8h+7 of a 32-row block hold its rows 16h .. 16h+15
 #pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
+  for (int pass = 0; pass < 2; ++pass)
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = acc_row(r, lane), col = j * 32 + (lane & 31);
+      for (int r = 8 * half; r < 8 * half + 8; ++r) {
+        const int row = acc_row(r, lane) - 16 * half, col = j * 32 + (lane & 31);
         *reinterpret_cast<float*>(wreg + epi_off(row, col >> 2) + (col & 3) * 4) = acc[pass][j][r] * alpha;
       }
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int qq = it * 64 + lane;
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int it = 4 * half + i4;           // step of the pass: rows 4 it .. 4 it + 3
+      const int qq = i4 * 64 + lane;
       const int row = qq >> 4, cg = qq & 15;
       float f[8];
       Chunk<float>::unpack(ld16(wreg + epi_off(row, 2 * cg)), f);
       Chunk<float>::unpack(ld16(wreg + epi_off(row, 2 * cg + 1)), f + 4);
-      const int grow = rbase + pass * 32 + row, gcol = cbase + cg * 8;
+      const int grow = rbase + pass * 32 + 16 * half + row, gcol = cbase + cg * 8;
       if constexpr (EPI == EPI_LSE) head_lse8(g, grow, gcol, f);
       else if (grow < g.M && gcol < g.N) {
         // (the v heads do not read the ring)
@@ -712,21 +738,31 @@ __device__ __forceinline__ void gemm_pp_body(const GemmArgs& g) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int grp = wave >> 2, q = wave & 3;
 
-  int tm, tn, split;
-  tile_coords(g, tm, tn, split, 4);
-  const int m0 = tm * G::BM, n0 = tn * G::BN;
-  const int kbeg = split * g.k_split;
-  const int nk = (min(g.K, kbeg + g.k_split) - kbeg) / G::BK;
-
+  // Persistent: the grid walks the tiles (all splits) in steps of its size;
+  // while a tile's epilogue runs through operand slot 1, the next tile's
+  // first stage loads into slot 0.
+  static_assert(8 * 8192 <= G::SLAB, "the epilogue's staging fits one operand slot");
+  const int total = g.tiles_m * g.tiles_n * g.nsplit;
+  int v = blockIdx.x;
+  if (v >= total) return;
+  int m0, n0, split, kbeg, nk;
   // grp 0 stages the A operand, grp 1 the B operand
   typename std::conditional<TR, PPStagerT, PPStager<TI>>::type st;
-  if constexpr (TR) {
-    if (grp == 0) st.init(g.A, g.lda, g.K, m0, kbeg, q, lane);
-    else st.init(g.B, g.ldb, g.K, n0, kbeg, q, lane);
-  } else {
-    if (grp == 0) st.init(g.A, g.lda, g.M, m0, q, lane);
-    else st.init(g.B, g.ldb, g.N, n0, q, lane);
-  }
+  auto setup = [&](int tile) {
+    int tm, tn;
+    tile_coords_v(g, tile, total, tm, tn, split, 4);
+    m0 = tm * G::BM;
+    n0 = tn * G::BN;
+    kbeg = split * g.k_split;
+    nk = (min(g.K, kbeg + g.k_split) - kbeg) / G::BK;
+    if constexpr (TR) {
+      if (grp == 0) st.init(g.A, g.lda, g.K, m0, kbeg, q, lane);
+      else st.init(g.B, g.ldb, g.K, n0, kbeg, q, lane);
+    } else {
+      if (grp == 0) st.init(g.A, g.lda, g.M, m0, q, lane);
+      else st.init(g.B, g.ldb, g.N, n0, q, lane);
+    }
+  };
   auto issue = [&](int kt) {
     char* sub = smem + (kt & 1) * G::SLAB + grp * (G::BM * G::ROWB);
     if constexpr (TR) st.issue(sub, kt * G::BK, kt < nk, q);
@@ -735,12 +771,6 @@ __device__ __forceinline__ void gemm_pp_body(const GemmArgs& g) {
 
   const int arow = (q >> 1) * 128 + grp * 64, brow = (q & 1) * 128;
   f32x16 acc[2][4];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   typename MM::frag fa[HS][2], fb[HS][4];
   u32x4 pre[2][8];   // the epilogue's own operand, loaded while the last MFMAs run
   auto read = [&](int kt, int h) {
@@ -769,71 +799,89 @@ __device__ __forceinline__ void gemm_pp_body(const GemmArgs& g) {
         for (int j = 0; j < 4; ++j) acc[i][j] = MM::mma(fa[s][i], fb[s][j], acc[i][j]);
   };
 
-  // A stage past the end (kt + 1 == nk) is issued with out-of-range offsets:
-  // it writes zeros into the free slot and keeps the loop free of branches
-  // that would split the instruction schedule.
-  if (nk > 0) {
-    issue(0);
-    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
-    wg_barrier();
-    if (grp == 0) {
-      for (int kt = 0; kt < nk; ++kt) {
-        issue(kt + 1);
-        read(kt, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);    // the 8 loads, then the LDS reads
-        __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
-        wg_barrier();
-        mfma();
-        wg_barrier();
-        read(kt, 1);
-        wg_barrier();
-        mfma();
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): stage kt+1's A rows have landed
-        wg_barrier();
-      }
-      epi_prefetch<TO, EPI>(g, pre, m0, n0, wave, lane);   // in flight while grp 1 finishes
-      wg_barrier();   // grp 1 runs the last half-step's MFMAs
-    } else {
-      // the slot is refilled after the stage's last barrier, so each read
-      // phase ends with its fragments in registers
-      auto tail = [&](int kt) {
-        read(kt, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
-        wg_barrier();
-        mfma();
-        wg_barrier();
-        read(kt, 1);
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_waitcnt(0);        // fragments, and stage kt+1's B rows
-        wg_barrier();
-      };
-      issue(1);
-      wg_barrier();
-      tail(0);
-      for (int kt = 1; kt < nk; ++kt) {
-        issue(kt + 1);
-        mfma();
+  setup(v);
+  if (nk > 0) issue(0);
+  for (;;) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {           // one load between MFMA pairs
-          __builtin_amdgcn_sched_group_barrier(0x008, HS, 0);
-          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        }
-        wg_barrier();
-        tail(kt);
-      }
-      mfma();
-      epi_prefetch<TO, EPI>(g, pre, m0, n0, wave, lane);
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    // A stage past the end (kt + 1 == nk) is issued with out-of-range offsets:
+    // it writes zeros into the free slot and keeps the loop free of branches
+    // that would split the instruction schedule.
+    if (nk > 0) {
+      __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): stage 0 (and the last epilogue's stores)
       wg_barrier();
+      if (grp == 0) {
+        for (int kt = 0; kt < nk; ++kt) {
+          issue(kt + 1);
+          read(kt, 0);
+          __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);    // the 8 loads, then the LDS reads
+          __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
+          wg_barrier();
+          mfma();
+          wg_barrier();
+          read(kt, 1);
+          wg_barrier();
+          mfma();
+          __builtin_amdgcn_sched_barrier(0);
+          __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): stage kt+1's A rows have landed
+          wg_barrier();
+        }
+        epi_prefetch<TO, EPI>(g, pre, m0, n0, wave, lane);   // in flight while grp 1 finishes
+        wg_barrier();   // grp 1 runs the last half-step's MFMAs
+      } else {
+        // the slot is refilled after the stage's last barrier, so each read
+        // phase ends with its fragments in registers
+        auto tail = [&](int kt) {
+          read(kt, 0);
+          __builtin_amdgcn_sched_barrier(0);
+          __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+          wg_barrier();
+          mfma();
+          wg_barrier();
+          read(kt, 1);
+          __builtin_amdgcn_sched_barrier(0);
+          __builtin_amdgcn_s_waitcnt(0);        // fragments, and stage kt+1's B rows
+          wg_barrier();
+        };
+        issue(1);
+        wg_barrier();
+        tail(0);
+        for (int kt = 1; kt < nk; ++kt) {
+          issue(kt + 1);
+          mfma();
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {           // one load between MFMA pairs
+            __builtin_amdgcn_sched_group_barrier(0x008, HS, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+          }
+          wg_barrier();
+          tail(kt);
+        }
+        mfma();
+        epi_prefetch<TO, EPI>(g, pre, m0, n0, wave, lane);
+        wg_barrier();
+      }
+    } else {
+      epi_prefetch<TO, EPI>(g, pre, m0, n0, wave, lane);
     }
-  } else {
-    epi_prefetch<TO, EPI>(g, pre, m0, n0, wave, lane);
+    // every staging load (the past-the-end one included) was waited for
+    // inside the loops; after the barrier both slots are free: the next
+    // tile's first stage goes to slot 0, this tile's epilogue through slot 1
+    wg_barrier();
+    const int cm0 = m0, cn0 = n0, csplit = split;
+    const int vn = v + (int)gridDim.x;
+    if (vn < total) {
+      setup(vn);
+      if (nk > 0) issue(0);
+    }
+    epilogue_pp<TO, EPI>(g, acc, smem + G::SLAB, cm0, cn0, csplit, wave, lane, pre);
+    if (vn >= total) break;
+    v = vn;
   }
-  // every staging load (the past-the-end one included) was waited for inside
-  // the loops; the barrier frees the LDS for the epilogue
-  wg_barrier();
-  epilogue_pp<TO, EPI>(g, acc, smem, m0, n0, split, wave, lane, pre);
 }
 
 }  // namespace blk
