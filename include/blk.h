@@ -233,7 +233,7 @@ int decode_step(const blk_dcfg* cfg, const void* x,
  * keeps on each device for the life of the process (its address is looked
  * up on the first call on each device).  Returns BLK_ELIMIT, with nothing
  * enqueued, when decode_scratch_bytes(cfg) exceeds that size (d20 with 64
- * sequences and 2049 cache slots needs 10.8 MiB).  The call allocates
+ * sequences and 2049 cache slots needs 10.7 MiB).  The call allocates
  * nothing.  Every call on one GPU uses that GPU's single workspace: calls
  * whose work overlaps on one GPU (other streams, other host threads) race
  * and give wrong results; calls enqueued in order on one stream do not. */
