@@ -355,8 +355,9 @@ void gemm(void (*kern)(GemmArgs), const char* name, GemmArgs g, int splits, hipS
   }
   g.nsplit = splits;
   Timed t(name, st);
-  if (threads == 512) {
-    // the eight-wave kernels are persistent: one workgroup per CU walks the tiles
+  if (threads == 512 && (!g.aux || sizeof(TI) == 2)) {
+    // the eight-wave kernels are persistent, one workgroup per CU walking the
+    // tiles, except the E4M3 ones whose epilogue reads an operand of its own
     const int total = g.tiles_m * g.tiles_n * splits;
     hipLaunchKernelGGL(kern, dim3(std::min(total, cu_count())), dim3(threads), LDS, st, g);
   } else {

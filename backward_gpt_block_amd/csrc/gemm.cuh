@@ -207,11 +207,11 @@ __device__ __forceinline__ void tile_coords(const GemmArgs& g, int& tm, int& tn,
 // grid is a multiple of 8 whenever total is), so tile v = b + i * grid
 // lands on the same XCD for every i, and the remap gives each XCD a
 // contiguous run of logical tiles exactly as for one workgroup per tile.
-__device__ __forceinline__ void tile_coords_v(const GemmArgs& g, int v, int total, int& tm, int& tn, int& split,
-                                              int GROUP = 8) {
+__device__ __forceinline__ void tile_coords_v(const GemmArgs& g, int v, int total, bool persistent, int& tm, int& tn,
+                                              int& split, int GROUP = 8) {
   const int per_split = g.tiles_m * g.tiles_n;
   int pid = v;
-  if (total % 8 == 0 && gridDim.x % 8 == 0) pid = (pid % 8) * (total / 8) + pid / 8;
+  if (total % 8 == 0 && (!persistent || gridDim.x % 8 == 0)) pid = (pid % 8) * (total / 8) + pid / 8;
   split = pid / per_split;
   int t = pid % per_split;
   int group = t / (GROUP * g.tiles_n);
@@ -740,17 +740,21 @@ __device__ __forceinline__ void gemm_pp_body(const GemmArgs& g) {
 
   // Persistent: the grid walks the tiles (all splits) in steps of its size;
   // while a tile's epilogue runs through operand slot 1, the next tile's
-  // first stage loads into slot 0.
+  // first stage loads into slot 0.  Not for E4M3 operands with an epilogue
+  // that loads an operand of its own: beside that operand's registers the
+  // next tile's state made them spill (58 registers, 14-35% slower); they run
+  // one workgroup per tile (grid tiles x splits).
+  constexpr bool PERSIST = !EpiAux<TO, EPI>::on || sizeof(TI) == 2;
   static_assert(8 * 8192 <= G::SLAB, "the epilogue's staging fits one operand slot");
   const int total = g.tiles_m * g.tiles_n * g.nsplit;
-  int v = blockIdx.x;
+  int v = PERSIST ? (int)blockIdx.x : (int)(blockIdx.x + blockIdx.y * gridDim.x);
   if (v >= total) return;
   int m0, n0, split, kbeg, nk;
   // grp 0 stages the A operand, grp 1 the B operand
   typename std::conditional<TR, PPStagerT, PPStager<TI>>::type st;
   auto setup = [&](int tile) {
     int tm, tn;
-    tile_coords_v(g, tile, total, tm, tn, split, 4);
+    tile_coords_v(g, tile, total, PERSIST, tm, tn, split, 4);
     m0 = tm * G::BM;
     n0 = tn * G::BN;
     kbeg = split * g.k_split;
@@ -872,15 +876,20 @@ __device__ __forceinline__ void gemm_pp_body(const GemmArgs& g) {
     // inside the loops; after the barrier both slots are free: the next
     // tile's first stage goes to slot 0, this tile's epilogue through slot 1
     wg_barrier();
-    const int cm0 = m0, cn0 = n0, csplit = split;
-    const int vn = v + (int)gridDim.x;
-    if (vn < total) {
-      setup(vn);
-      if (nk > 0) issue(0);
+    if constexpr (PERSIST) {
+      const int cm0 = m0, cn0 = n0, csplit = split;
+      const int vn = v + (int)gridDim.x;
+      if (vn < total) {
+        setup(vn);
+        if (nk > 0) issue(0);
+      }
+      epilogue_pp<TO, EPI>(g, acc, smem + G::SLAB, cm0, cn0, csplit, wave, lane, pre);
+      if (vn >= total) break;
+      v = vn;
+    } else {
+      epilogue_pp<TO, EPI>(g, acc, smem + G::SLAB, m0, n0, split, wave, lane, pre);
+      break;
     }
-    epilogue_pp<TO, EPI>(g, acc, smem + G::SLAB, cm0, cn0, csplit, wave, lane, pre);
-    if (vn >= total) break;
-    v = vn;
   }
 }
 
