@@ -11,13 +11,13 @@
   gradients here), within 15%: the kernels add no error of their own.
 
 The gates of gpu_util.compare apply to every output: Frobenius error <= 6e-2
-against the fp8 oracle, max|err|/max|ref| <= 6e-2 for y and dx and <= 0.12
-for the weight gradients, each row of y and dx within 5x.  A weight-gradient
-element is a sum over the tokens of products of E4M3 codes, and the
-attention kernels' own bf16 roundings (of P and dS, which the oracle does
-not take) move a share of the downstream codes to a neighbouring code: at a
-few dozen tokens the largest element error sits at about twice the
-Frobenius error.  Against
+against the fp8 oracle, max|err|/max|ref| <= 6e-2 for y and dx, each row of
+y and dx within 5x; the weight gradients' max|err|/max|ref| <= 6e-2 at the
+d26 workload and <= 0.12 at the small shapes.  A weight-gradient element
+is a sum over the tokens of products of E4M3 codes, and the attention
+kernels' own bf16 roundings (of P and dS, which the oracle does not take)
+move a share of the downstream codes to a neighbouring code: at a few dozen
+tokens the largest element error sits at about twice the Frobenius error.  Against
 the unquantised block the recipe itself (per-tensor E4M3 on all three GEMMs
 of every linear layer) does not reach 6e-2 for the deepest weight gradients
 at the d26 width; those distances are printed, and held to the fp8 oracle's
@@ -59,7 +59,7 @@ def test_quantizer_bit_exact():
 ACCURACY_RATIO = 1.15
 
 
-def _fp8_parity(sh: BlockShape, seed=0, keep=None):
+def _fp8_parity(sh: BlockShape, seed=0, keep=None, dw_max_factor=2.0):
     from oracle import fp8_block
     note(f"fp8 block B={sh.B} T={sh.T} C={sh.C} keep={keep} seed={seed}")
     inp = make_block_inputs(sh, seed=seed)
@@ -79,7 +79,7 @@ def _fp8_parity(sh: BlockShape, seed=0, keep=None):
                                   batch=None if keep is None else list(keep), log=note, window=sh.window or None,
                                   n_kv_head=sh.n_kv_head or None)
     errs = compare(res, emu, TOL["fp8"], keys=list(emu),
-                   max_tol={k: 2 * TOL["fp8"] for k in ("dw_qkv", "dw_o", "dw_fc", "dw_proj")})
+                   max_tol={k: dw_max_factor * TOL["fp8"] for k in ("dw_qkv", "dw_o", "dw_fc", "dw_proj")})
     ref = oracle_step(sh, inp, batch=None if keep is None else list(keep))
     gpu_acc = {k: rel_err(res[k], ref[k]) for k in ref}
     emu_acc = {k: rel_err(emu[k], ref[k]) for k in ref}
@@ -104,8 +104,9 @@ def test_fp8_block_window():
 @pytest.mark.timeout(900)
 def test_d26_fp8_full_size_sampled():
     # the oracle's forward pass over all 16 sequences (for the per-tensor
-    # scales) takes a minute or two of host time
-    _fp8_parity(WORKLOADS["d26_fp8"], keep=(0, 15))
+    # scales) takes a minute or two of host time; at this size every gate is
+    # the stated 6e-2, the weight gradients' max ratio included
+    _fp8_parity(WORKLOADS["d26_fp8"], keep=(0, 15), dw_max_factor=1.0)
 
 
 def test_fp8_block_gqa():
