@@ -497,10 +497,14 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
 // registers, the other reads its fragments of that half from LDS, so each
 // SIMD's matrix pipe has a wave feeding it while the other waits on LDS.
 // Per k-step kt (grp 0 | grp 1):
-//   A0: read (kt, half 0), issue kt+1's A rows | MFMAs (kt-1, 1), issue kt+1's B rows
-//   B0: MFMAs (kt, 0)                         | read (kt, 0)
-//   A1: read (kt, 1)                          | MFMAs (kt, 0)
-//   B1: MFMAs (kt, 1), wait for kt+1          | read (kt, 1), wait for kt+1
+//   A0: issue half of kt+1's A rows, read (kt, half 0) | MFMAs (kt-1, 1), half of kt+1's B rows
+//   B0: MFMAs (kt, 0), the other half of the A rows   | read (kt, 0)
+//   A1: read (kt, 1)                                 | MFMAs (kt, 0), the other half of the B rows
+//   B1: MFMAs (kt, 1), wait for kt+1                 | read (kt, 1), wait for kt+1
+// Spreading each stage's loads over two phases keeps a phase from holding
+// all 64 KiB of them: with every load in A0 the vector-memory path backed up
+// and stalled the MFMAs interleaved with them (d20 step 9.47 -> 9.25 ms;
+// fewer in the first part, or the reads ahead of the loads, were slower).
 // Stage kt+1 goes global -> LDS (whole 128-byte rows: one load instruction
 // covers 8 full cache lines) into the slot stage kt-1 vacated.  Requires K
 // and the split length to be multiples of the k-step and both leading
@@ -523,9 +527,10 @@ struct PPStager {
   }
   // rows past the matrix edge have offsets >= the resource size and read
   // zero; so does a whole stage past the end of k (live = false)
+  template <int J0 = 0, int J1 = 8>
   __device__ __forceinline__ void issue(char* sub, int k0_bytes, bool live, int q) const {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = J0; j < J1; ++j) {
       const uint32_t off = (x ^ (uint32_t)(j << 4)) + (uint32_t)j * step + (uint32_t)k0_bytes;
       lds_u32* dst = (lds_u32*)(sub + __builtin_amdgcn_readfirstlane((8 * q + j) * 1024));
       raw_buffer_load_lds(rs, dst, 16, live ? (int)off : (int)0x80000000u, 0, 0, 0);
@@ -565,11 +570,12 @@ struct PPStagerT {
   // transpose read, and after a direct-to-LDS load the compiler knows of it
   // would make that read wait for the stage just issued; the body waits for
   // each stage explicitly.
+  template <int J0 = 0, int J1 = 8>
   __device__ __forceinline__ void issue(char* sub, int krel, bool live, int q) const {
     const long adv = (long)krel * ldb;
     const i32x4 rs = make_rsrc(base + adv, (uint32_t)max(0L, min(left - adv, 0x7fffffffL)));
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = J0; j < J1; ++j) {
       const uint32_t off = x + (uint32_t)(2 * j) * ldb + (cl ^ (uint32_t)(((2 * j) & 7) << 5));
       lds_u32* dst = (lds_u32*)(sub + (8 * q + j) * 1024);
       dma16(rs, dst, live ? off : 0x80000000u);
@@ -772,6 +778,21 @@ __device__ __forceinline__ void gemm_pp_body(const GemmArgs& g) {
     if constexpr (TR) st.issue(sub, kt * G::BK, kt < nk, q);
     else st.issue(sub, (kbeg + kt * G::BK) * (int)sizeof(TI), kt < nk, q);
   };
+  // a stage's eight loads per wave in two parts of L0 and 8 - L0, issued in
+  // different phases (see the schedule above)
+  constexpr int L0 = 4;
+  auto issue0 = [&](int kt) {
+    char* sub = smem + (kt & 1) * G::SLAB + grp * (G::BM * G::ROWB);
+    if constexpr (TR) st.template issue<0, L0>(sub, kt * G::BK, kt < nk, q);
+    else st.template issue<0, L0>(sub, (kbeg + kt * G::BK) * (int)sizeof(TI), kt < nk, q);
+  };
+  auto issue1 = [&](int kt) {
+    char* sub = smem + (kt & 1) * G::SLAB + grp * (G::BM * G::ROWB);
+    if constexpr (TR) st.template issue<L0, 8>(sub, kt * G::BK, kt < nk, q);
+    else st.template issue<L0, 8>(sub, (kbeg + kt * G::BK) * (int)sizeof(TI), kt < nk, q);
+  };
+  constexpr int NMF = 8 * HS;                 // MFMAs per phase
+  constexpr int P0 = NMF / L0, P1 = NMF / (8 - L0);
 
   const int arow = (q >> 1) * 128 + grp * 64, brow = (q & 1) * 128;
   f32x16 acc[2][4];
@@ -820,12 +841,18 @@ __device__ __forceinline__ void gemm_pp_body(const GemmArgs& g) {
       wg_barrier();
       if (grp == 0) {
         for (int kt = 0; kt < nk; ++kt) {
-          issue(kt + 1);
+          issue0(kt + 1);
           read(kt, 0);
-          __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);    // the 8 loads, then the LDS reads
+          __builtin_amdgcn_sched_group_barrier(0x020, L0, 0);   // the first loads, then the LDS reads
           __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
           wg_barrier();
+          issue1(kt + 1);
           mfma();
+#pragma unroll
+          for (int i = 0; i < 8 - L0; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, P1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+          }
           wg_barrier();
           read(kt, 1);
           wg_barrier();
@@ -839,12 +866,22 @@ __device__ __forceinline__ void gemm_pp_body(const GemmArgs& g) {
       } else {
         // the slot is refilled after the stage's last barrier, so each read
         // phase ends with its fragments in registers
-        auto tail = [&](int kt) {
+        auto tail = [&](int kt, bool more) {
           read(kt, 0);
           __builtin_amdgcn_sched_barrier(0);
           __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
           wg_barrier();
-          mfma();
+          if (more) {
+            issue1(kt + 1);
+            mfma();
+#pragma unroll
+            for (int i = 0; i < 8 - L0; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, P1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            }
+          } else {
+            mfma();
+          }
           wg_barrier();
           read(kt, 1);
           __builtin_amdgcn_sched_barrier(0);
@@ -853,17 +890,17 @@ __device__ __forceinline__ void gemm_pp_body(const GemmArgs& g) {
         };
         issue(1);
         wg_barrier();
-        tail(0);
+        tail(0, false);
         for (int kt = 1; kt < nk; ++kt) {
-          issue(kt + 1);
+          issue0(kt + 1);
           mfma();
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {           // one load between MFMA pairs
-            __builtin_amdgcn_sched_group_barrier(0x008, HS, 0);
+          for (int i = 0; i < L0; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, P0, 0);
             __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
           }
           wg_barrier();
-          tail(kt);
+          tail(kt, true);
         }
         mfma();
         epi_prefetch<TO, EPI>(g, pre, m0, n0, wave, lane);
