@@ -242,6 +242,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="d20_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-smi", action="store_true",
+                    help="skip the SMI clock/power query (for runs under a profiler, whose preloaded "
+                         "library would follow the SMI tool's own start-up)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (the known-size kernel that scales HBM counters)")
@@ -372,7 +375,7 @@ def bench_train(args) -> int:
     # forward and backward separately: median and minimum over max(K, 20) iterations
     split = split_timing(fwd, bwd, max(args.steps, 20))
     log(f"split: {split}")
-    smi = under_load(step)
+    smi = {"skipped": "--no-smi"} if args.no_smi else under_load(step)
     log(f"smi under load: {smi}")
     mfma = mfma_rates()
     log(f"mfma probe: {mfma}")
