@@ -918,12 +918,15 @@ __device__ __forceinline__ float store_rows(const float* stg, bf16* out, long ld
 }
 // Operands of the QK-norm backward of the wave's 32 rows: the normalised rows
 // z (row r at z + r*ld) and their factors rho[r * rs], zero past nrows.
-// Also the rotary angles (cs: [T][64]) of the first two passes of rows
-// t0 .. (the later passes load theirs two passes ahead).
+// Also the rotary angles (cs: [T][64]) of this lane's 8 angle indices at its
+// first pass's position and at position 4: pass i + 1's rows sit 4
+// positions after pass i's, so each pass turns the previous pass's angles by
+// the angle at position 4 (angle addition) instead of loading its own.
 struct QkRows {
   u32x4 z[8];
   float p[8];
-  u32x4 cs[2][4];
+  u32x4 cs0[4];
+  u32x4 cs4[4];
 };
 // angle-table chunks of pass i (rows 4i + lane/16 of t0 ..; rows past nrows
 // read a valid row, their results are not stored)
@@ -934,15 +937,18 @@ __device__ __forceinline__ void cs_rows_load(u32x4* c, const float2* cs, int t0,
   for (int h = 0; h < 4; ++h) c[h] = ld16(cp + 4 * h);
 }
 __device__ __forceinline__ void qk_rows_load(QkRows& q, const bf16* z, long ld, const float* rho, long rs, int nrows,
-                                             int lane, const float2* cs, int t0) {
+                                             int lane, const float2* cs, int t0, int T) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int r = 4 * i + (lane >> 4);
     q.z[i] = r < nrows ? ld16(z + r * ld + 8 * (lane & 15)) : u32x4{0u, 0u, 0u, 0u};
     q.p[i] = r < nrows ? rho[r * rs] : 0.f;
   }
-  cs_rows_load(q.cs[0], cs, t0, 0, nrows, lane);
-  cs_rows_load(q.cs[1], cs, t0, 1, nrows, lane);
+  cs_rows_load(q.cs0, cs, t0, 0, nrows, lane);
+  // position 4 (T <= 4: any row; no row of a later pass is stored then)
+  const float* cp = reinterpret_cast<const float*>(cs + (long)min(4, T - 1) * 64 + (lane & 7) * 8);
+#pragma unroll
+  for (int h = 0; h < 4; ++h) q.cs4[h] = ld16(cp + 4 * h);
 }
 // Gradient of q' or k' from the staged gradient g of the normalised rows:
 // QK-norm backward dz' = p (g - z mean(g z)) over the row's 128 dims (16
@@ -951,27 +957,30 @@ __device__ __forceinline__ void qk_rows_load(QkRows& q, const bf16* z, long ld, 
 // out + r*ld for r < nrows; returns the largest stored magnitude before
 // rounding.  (Rotary embedding and QK-norm: flicky.cc nanochat page, section
 // on the model.)
-__device__ __forceinline__ float store_rows_qk(const float* stg, const QkRows& q, bf16* out, long ld,
-                                               const float2* cs, int t0, int nrows, int lane) {
+__device__ __forceinline__ float store_rows_qk(const float* stg, const QkRows& q, bf16* out, long ld, int nrows,
+                                               int lane) {
   const int cg = lane & 15;
   float mx = 0.f;
-  // angle-table chunks of pass i + 2 loaded during pass i (passes 0 and 1
-  // came with the rows)
-  u32x4 csr[2][4];
-  auto cs_load = [&](int i) { cs_rows_load(csr[i & 1], cs, t0, i, nrows, lane); };
+  // (cos, sin) of this lane's 8 angles at the current pass's position, and at position 4
+  float c8[16], c4[16];
 #pragma unroll
   for (int h = 0; h < 4; ++h) {
-    csr[0][h] = q.cs[0][h];
-    csr[1][h] = q.cs[1][h];
+    Chunk<float>::unpack(q.cs0[h], c8 + 4 * h);
+    Chunk<float>::unpack(q.cs4[h], c4 + 4 * h);
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    float g[8], z[8], c8[16];
+    float g[8], z[8];
     unstage_row(stg, i, lane, g);
     Chunk<bf16>::unpack(q.z[i], z);
+    if (i > 0) {   // 4 positions on: cos(a + b), sin(a + b) from a and b = the angle at position 4
 #pragma unroll
-    for (int h = 0; h < 4; ++h) Chunk<float>::unpack(csr[i & 1][h], c8 + 4 * h);
-    if (i + 2 < 8) cs_load(i + 2);
+      for (int e = 0; e < 8; ++e) {
+        const float c = c8[2 * e], sn = c8[2 * e + 1];
+        c8[2 * e] = fmaf(c, c4[2 * e], -sn * c4[2 * e + 1]);
+        c8[2 * e + 1] = fmaf(sn, c4[2 * e], c * c4[2 * e + 1]);
+      }
+    }
     float dot = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) dot += g[e] * z[e];
@@ -1288,11 +1297,11 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_bf16_kernel(AttnArgs a) 
     QkRows qk;
     // key QK-norm factors: [N][H] after the query ones, head index kvh
     qk_rows_load(qk, qkv + row0 * a.LD + a.KO + cur.kvh * HD, a.LD, a.rho + ((long)a.B * a.T + row0) * a.H + cur.kvh,
-                 a.H, nrows, lane, a.cs, kw0);
+                 a.H, nrows, lane, a.cs, kw0, a.T);
     stage_acc(stg, dv, 1.f, lane);
     mx = fmaxf(mx, store_rows(stg, drow + a.VO + cur.kvh * HD, a.LD, nrows, lane));
     stage_acc(stg, dk, a.rsd, lane);
-    mx = fmaxf(mx, store_rows_qk(stg, qk, drow + a.KO + cur.kvh * HD, a.LD, a.cs, kw0, nrows, lane));
+    mx = fmaxf(mx, store_rows_qk(stg, qk, drow + a.KO + cur.kvh * HD, a.LD, nrows, lane));
     if (!more) break;
     // the next unit's K, V rows have landed (each wave waits for its own
     // loads, the barrier for everyone's; the stores above drain too) and the
@@ -1499,10 +1508,10 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_bf16_kernel(AttnArgs a) {
     const int nrows = min(32, a.T - qw0);
     QkRows qk;
     qk_rows_load(qk, qkv + row0 * a.LD + cur.head * HD, a.LD, a.rho + row0 * a.H + cur.head, a.H, nrows, lane, a.cs,
-                 qw0);
+                 qw0, a.T);
     stage_acc(stg, acc, a.rsd, lane);
-    mx = fmaxf(mx, store_rows_qk(stg, qk, static_cast<bf16*>(a.dqkv) + row0 * a.LD + cur.head * HD, a.LD, a.cs, qw0,
-                                 nrows, lane));
+    mx = fmaxf(mx, store_rows_qk(stg, qk, static_cast<bf16*>(a.dqkv) + row0 * a.LD + cur.head * HD, a.LD, nrows,
+                                 lane));
     if (!more) break;
     // the next unit's Q, dO rows have landed and the staging rows are free
     __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
@@ -1564,6 +1573,14 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_ds_kernel(AttnArgs a) {
                              clamp_bytes((long)a.dsP * 16384));
   const int koff = (a.KO + kvh * HD) * 2;
   const int n = min(4 * u + 4, (a.T + DSQ_KT - 1) / DSQ_KT);   // key tiles 0 .. n-1
+  // the QK-norm and rotary operands of the epilogue, loaded first: every
+  // tile wait below also covers them (completion follows issue order), and
+  // the epilogue finds them in registers
+  const int qw0 = u * 128 + wave * 32;
+  const long row0 = (long)b * a.T + qw0;
+  const int nrows = min(32, a.T - qw0);
+  QkRows qk;
+  qk_rows_load(qk, qkv + row0 * a.LD + head * HD, a.LD, a.rho + row0 * a.H + head, a.H, nrows, lane, a.cs, qw0, a.T);
   // key tile t: K rows 32t..; the dS pieces of keys 32 (t & 3).. (1 KiB chunks
   // 4 (t & 3) .. 4 (t & 3) + 3) of blocks (t / 4, 2u) and (t / 4, 2u + 1)
   auto issue = [&](int slot, int t) {
@@ -1635,17 +1652,12 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_ds_kernel(AttnArgs a) {
     }
   }
   __syncthreads();   // every wave is done with the slots: they become staging rows
-  const int qw0 = u * 128 + wave * 32;
-  const long row0 = (long)b * a.T + qw0;
-  const int nrows = min(32, a.T - qw0);
   float* stg = reinterpret_cast<float*>(smem) + wave * 32 * 128;
-  QkRows qk;
-  qk_rows_load(qk, qkv + row0 * a.LD + head * HD, a.LD, a.rho + row0 * a.H + head, a.H, nrows, lane, a.cs, qw0);
   // lane l holds query qperm(l % 32): bits 2 and 3 of the position swapped
   const int l32 = lane & 31;
   stage_acc(stg, acc, a.rsd, lane, (l32 & 0x13) | ((l32 & 4) << 1) | ((l32 & 8) >> 1));
   const float mx =
-      store_rows_qk(stg, qk, static_cast<bf16*>(a.dqkv) + row0 * a.LD + head * HD, a.LD, a.cs, qw0, nrows, lane);
+      store_rows_qk(stg, qk, static_cast<bf16*>(a.dqkv) + row0 * a.LD + head * HD, a.LD, nrows, lane);
   if (a.amax_dqkv) amax_publish<bf16>(a.amax_dqkv, mx);
 }
 
