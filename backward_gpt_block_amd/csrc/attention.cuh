@@ -885,6 +885,9 @@ typedef __attribute__((address_space(3))) const f32x4 lds_f32x4;
 __device__ __forceinline__ int stg_idx(int row, int d) { return row * 128 + ((((d >> 2) ^ row) & 31) << 2) + (d & 3); }
 // (row: the staging row of this lane's column; lane & 31 unless permuted)
 // (registers r .. r+3, r % 4 == 0, are 4 consecutive dims: one 16-byte chunk)
+// The rows are read back by other lanes of the same wave (whose LDS accesses
+// execute in order): the compiler fence keeps those reads after these writes,
+// which the compiler, reasoning per lane, would see as independent.
 __device__ __forceinline__ void stage_acc(float* stg, const f32x16* acc, float scale, int lane, int row = -1) {
   if (row < 0) row = lane & 31;
 #pragma unroll
@@ -895,6 +898,7 @@ __device__ __forceinline__ void stage_acc(float* stg, const f32x16* acc, float s
       *reinterpret_cast<f32x4*>(stg + stg_idx(row, d)) =
           f32x4{acc[db][r] * scale, acc[db][r + 1] * scale, acc[db][r + 2] * scale, acc[db][r + 3] * scale};
     }
+  __asm volatile("" ::: "memory");
 }
 __device__ __forceinline__ void unstage_row(const float* stg, int i, int lane, float* f) {
   const int row = 4 * i + (lane >> 4), d = 8 * (lane & 15);
@@ -1002,11 +1006,21 @@ __device__ __forceinline__ float store_rows_qk(const float* stg, const QkRows& q
 }
 }  // namespace fa
 
-// dK, dV: one unit of work = 128 keys of one (sequence, key/value head), 4
-// waves x 32 keys (K and V fragments in registers); it walks the 64-query
-// tiles at and after the diagonal of every query head of the group.  Q and dO
-// tiles are row-major in LDS (3-slot ring); their transposes for
-// dV^T += dO^T P and dK^T += Q^T dS come from transpose reads.
+// dK, dV: one unit of work = 128 keys of one (sequence, key/value head); it
+// walks the 64-query tiles at and after the diagonal of every query head of
+// the group.  Eight waves, two per SIMD, in pairs that share 32 keys and
+// split the work of a tile between them:
+// - the P wave (waves 0-3) holds the pair's K fragments, computes the scores
+//   S = Q K^T, the probabilities P = exp2(S sl2 - lse) and dV^T += dO^T P;
+// - the dS wave (waves 4-7) holds the V fragments, computes dP = dO V^T,
+//   takes P from its partner through LDS (bf16, the operand dV takes too),
+//   forms dS = P (dP - delta) and dK^T += Q^T dS.
+// Each wave issues 32 MFMAs per tile (one wave of 32 keys issued all 64
+// before and held too many registers to share its SIMD); while one wave of
+// a SIMD runs its exponentials or dS arithmetic the other's MFMAs proceed.
+// The exchange costs one barrier per tile between the two halves.  Q and dO
+// tiles are row-major in LDS (3-slot ring, loaded by the P waves); the
+// transposes for dV^T and dK^T come from transpose reads.
 //
 // The grid holds one workgroup per CU and each workgroup walks units (longest
 // first, every other round in reverse so that the workgroups' totals even
@@ -1014,22 +1028,24 @@ __device__ __forceinline__ float store_rows_qk(const float* stg, const QkRows& q
 // and V rows arrive as direct-to-LDS tiles and the fragments are read from
 // LDS; dV and dK go through LDS to row layout and out in 16-byte pieces, the
 // QK-norm and rotary backward of dK computed in that layout (a row's 128
-// values on 16 lanes).  Lane-per-row loads and stores, 32 rows per
-// instruction, made this boundary cost as much as six query tiles.
+// values on 16 lanes).
 //
-// DS: the kernel also stores the bf16 dS of every (query, key) pair it
-// computes into a.ds (layout in AttnArgs): each dS fragment the dK MFMAs take
-// (16 bytes per lane) is one store of 1 KiB, whole cache lines; a wave whose
-// keys all follow a query tile (the diagonal tile) stores zeros there, so
-// that every block is complete.
-template <bool DS>
-__global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_bf16_kernel(AttnArgs a) {
+// DS: the dS waves also store the bf16 dS of every (query, key) pair into
+// a.ds (layout in AttnArgs): each dS fragment the dK MFMAs take (16 bytes
+// per lane) is one store of 1 KiB, whole cache lines; a pair whose keys all
+// follow a query tile (the diagonal tile) stores zeros there, so that every
+// block is complete.
+// The body of one role (PW: the P waves, else the dS waves): the two roles
+// run the same unit walk and barriers, each with its own loop and registers.
+template <bool DS, bool PW>
+__device__ __forceinline__ void dkdv_bf16_role(const AttnArgs& a, char* smem, int wave) {
   using namespace fa;
   typedef Mfma<bf16> MM;
-  extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int QT = 64;
   constexpr int SLOTB = 2 * TILE + 2048;      // Q, dO, lse (1 KiB), delta (1 KiB)
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr bool pw = PW;
+  const int lane = threadIdx.x & 63;
+  const int kw = wave & 3;                    // key group of the pair: keys 32 kw .. of the unit
   const int BG = a.B * a.G, R = a.H / a.G;
   const int units = ((a.T + 127) / 128) * BG;
   const long ldq = (long)a.LD * 2, ldo = (long)a.C * 2;
@@ -1077,6 +1093,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_bf16_kernel(AttnArgs a) 
     return p;
   };
   // iteration it of unit p: query head kvh*R + it/nq, query tile qt0 + it%nq
+  // (issued by the P waves)
   auto issue = [&](const Unit& p, int slot, int it) {
     char* d = smem + slot * SLOTB;
     const int h = p.kvh * R + it / p.nq, q0 = (p.qt0 + it % p.nq) * QT;
@@ -1103,8 +1120,10 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_bf16_kernel(AttnArgs a) 
     vbase = vo[0];
   }
   // K and V rows of a unit (k rows 0-63, 64-127, then v): ring slot 2 and
-  // past the ring, used only between units
+  // past the ring, used only between units; the P exchange past those
   char* const kvs = smem + 2 * SLOTB;
+  // P of the pair kw, fragment f (half f/2, MFMA chunk f%2): 16 bytes per lane
+  lds_char* const pex = (lds_char*)(smem + 2 * SLOTB + 4 * TILE) + kw * 4096 + lane * 16;
   auto issue_kv_rows = [&](const Unit& p) {
     const i32x4 rsq = make_rsrc(qkv + (long)p.b * a.T * a.LD, clamp_bytes((long)a.T * ldq));
     const int k0 = p.kt * 128, ko = (a.KO + p.kvh * HD) * 2, vo = (a.VO + p.kvh * HD) * 2;
@@ -1113,14 +1132,13 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_bf16_kernel(AttnArgs a) 
     issue_tile(kvs + 2 * TILE, rsq, k0, ldq, vo, wave, lane);
     issue_tile(kvs + 3 * TILE, rsq, k0 + 64, ldq, vo, wave, lane);
   };
-  bf16x8 kf[8], vf[8];
-  auto read_kv = [&]() {   // this wave's 32 keys: rows 32 (wave & 1) .. of tile wave / 2
-    const lds_char* kb = (const lds_char*)kvs + (wave >> 1) * TILE + (wave & 1) * 8192;
+  // the pair's 32 key rows (rows 32 (kw & 1) .. of tile kw / 2): K fragments
+  // on the P wave, V fragments on the dS wave
+  bf16x8 kvf[8];
+  auto read_kv = [&]() {
+    const lds_char* kb = (const lds_char*)kvs + (pw ? 0 : 2 * TILE) + (kw >> 1) * TILE + (kw & 1) * 8192;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      kf[ks] = *(lds_bf16x8*)(kb + (kbase ^ (ks << 5)));
-      vf[ks] = *(lds_bf16x8*)(kb + 2 * TILE + (kbase ^ (ks << 5)));
-    }
+    for (int ks = 0; ks < 8; ++ks) kvf[ks] = *(lds_bf16x8*)(kb + (kbase ^ (ks << 5)));
     __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): read before the ring slot 2 is refilled
   };
   // workgroup barrier over LDS only (global accesses in flight stay in flight)
@@ -1132,188 +1150,253 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_bf16_kernel(AttnArgs a) 
   int j = 0;
   if (unit_of(0) >= qlen) return;
   Unit cur = make_unit(unit_of(0));
-  issue_kv_rows(cur);
+  if (pw) issue_kv_rows(cur);
   __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
   lds_barrier();
   read_kv();
-  issue(cur, 0, 0);
-  if (cur.n > 1) issue(cur, 1, 1);
+  if (pw) {
+    issue(cur, 0, 0);
+    if (cur.n > 1) issue(cur, 1, 1);
+  }
   float mx = 0.f;
   for (;;) {
-    const int kw0 = cur.kt * 128 + wave * 32;
+    const int kw0 = cur.kt * 128 + kw * 32;
     const int key = kw0 + (lane & 31);
     const int n = cur.n;
-    f32x16 dk[4], dv[4];
+    // dV^T (P wave) or dK^T (dS wave): 128 dims x the pair's 32 keys
+    f32x16 acc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) { dk[i][r] = 0.f; dv[i][r] = 0.f; }
+      for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
     for (int it = 0; it < n; ++it) {
-      // tile it landed: the operations issued after its loads may stay in
-      // flight, namely the next tile's loads (10 issues on wave 0, 8 on the
-      // others) and, with DS, the 4 dS stores of each of the two previous
-      // iterations (every iteration issues exactly 4)
+      // tile it landed: the P waves' loads issued after it (the next tile's:
+      // 10 issues on wave 0, 8 on the others) may stay in flight.  The dS
+      // waves issue no loads; they keep at most two tiles of dS stores (4
+      // each) in flight.
       const bool next = it + 1 < n;
-      if (!DS || it == 0) {
+      if (pw) {
         if (!next) wait_vm<0>();
         else if (wave == 0) wait_vm<10>();
         else wait_vm<8>();
-      } else if (it == 1) {
-        if (!next) wait_vm<4>();
-        else if (wave == 0) wait_vm<14>();
-        else wait_vm<12>();
-      } else {
-        if (!next) wait_vm<8>();
-        else if (wave == 0) wait_vm<18>();
-        else wait_vm<16>();
+      } else if (DS) {
+        wait_vm<8>();
       }
       ring_barrier();
       // the bases count as changed here, so that the eight offsets derived from
       // each are not hoisted out of the loop into sixteen live registers
       asm volatile("" : "+v"(kbase), "+v"(vbase));
-      if (it + 2 < n) issue(cur, (it + 2) % 3, it + 2);
+      if (pw && it + 2 < n) issue(cur, (it + 2) % 3, it + 2);
       const int q0 = (cur.qt0 + it % cur.nq) * QT;
       const lds_char* qt_ = (const lds_char*)smem + (it % 3) * SLOTB;
       const lds_char* ot_ = qt_ + TILE;
-      const float* vec = (const float*)(smem + (it % 3) * SLOTB + 2 * TILE);
+      const lds_char* vec = qt_ + 2 * TILE;   // lse (P wave), delta at +1024 (dS wave)
+      const bool zero = q0 + QT - 1 < kw0;              // all queries precede all keys of this pair
+      const bool skip = zero || q0 > kw0 + 31 + a.W - 1;  // or are past the keys' windows
       // dS block of (query head, key unit, query tile): row = key in the unit
       bf16* dsb = nullptr;
       if constexpr (DS) {
-        const int qt = cur.qt0 + it % cur.nq;
-        const long pair = (long)cur.kt * nqt_all - (long)cur.kt * (cur.kt - 1) + (qt - 2 * cur.kt);
-        dsb = static_cast<bf16*>(a.ds) + (((long)cur.b * a.H + cur.kvh * R + it / cur.nq) * a.dsP + pair) * 8192 +
-              wave * 2048 + lane * 8;   // chunk 4 wave, this lane's 16 bytes
-      }
-      if (q0 + QT - 1 < kw0) {                     // all queries precede all keys of this wave
-        if constexpr (DS) {   // zeros, in 4 stores like the computed iterations
+        if (!pw) {
+          const int qt = cur.qt0 + it % cur.nq;
+          const long pair = (long)cur.kt * nqt_all - (long)cur.kt * (cur.kt - 1) + (qt - 2 * cur.kt);
+          dsb = static_cast<bf16*>(a.ds) + (((long)cur.b * a.H + cur.kvh * R + it / cur.nq) * a.dsP + pair) * 8192 +
+                kw * 2048 + lane * 8;   // chunk 4 kw, this lane's 16 bytes
+          if (zero) {   // zeros, in 4 stores like the computed iterations
 #pragma unroll
-          for (int c = 0; c < 4; ++c) __builtin_nontemporal_store(u32x4{0u, 0u, 0u, 0u}, (u32x4*)(dsb + 512 * c));
+            for (int c = 0; c < 4; ++c) __builtin_nontemporal_store(u32x4{0u, 0u, 0u, 0u}, (u32x4*)(dsb + 512 * c));
+          }
         }
-        continue;
       }
-      if (q0 > kw0 + 31 + a.W - 1) continue;       // all queries are past the keys' windows
       const bool need_mask = (q0 < kw0 + 31) || (q0 + QT > a.T) || (q0 + QT - 1 >= kw0 + a.W);
-      // one copy of the iteration with the causal/edge mask and one without,
-      // so that each is a single scheduling region
-      auto body = [&](auto maskc) {
-      constexpr bool MASK = decltype(maskc)::value;
-      // Two 32-query halves in 32 steps of two MFMAs: S/dP(0); S/dP(1) with the
-      // softmax of half 0; dV/dK(0) with the softmax of half 1; dV/dK(1).  Each
-      // step issues the LDS reads of the step after next and ends with a
-      // scheduling fence, so every MFMA finds its fragments already loaded
-      // (left to itself the scheduler put each read right before its MFMA,
-      // which then waited out the LDS latency).
-      f32x16 sv[2] = {}, dp[2] = {};
-      bf16x8 fa[32], fb[32];   // the two fragments of step i
-      auto rd = [&](int i) {
-        if (i < 16) {          // Q and dO rows of half i/8, k-step i%8
-          const int qb = i >> 3, ks = i & 7;
-          fa[i] = *(lds_bf16x8*)(qt_ + qb * 8192 + (kbase ^ (ks << 5)));
-          fb[i] = *(lds_bf16x8*)(ot_ + qb * 8192 + (kbase ^ (ks << 5)));
-        } else {               // dO^T and Q^T of half, MFMA chunk and d-block
-          const int u = i - 16, qb = u >> 3, mm = (u >> 2) & 1, db = u & 3;
-          fa[i] = frag_vt_x(ot_, vbase, 2 * qb + mm, db);
-          fb[i] = frag_vt_x(qt_, vbase, 2 * qb + mm, db);
-        }
-      };
-      // lse and delta of the four queries of group g of half qb (one step ahead
-      // of their use)
-      f32x4 lv, dl;
-      auto ldv = [&](int qb, int g) {
-        const int qi = qb * 32 + 8 * g + 4 * (lane >> 5);
-        lv = *(const lds_f32x4*)((const lds_char*)vec + qi * 4);
-        dl = *(const lds_f32x4*)((const lds_char*)vec + 1024 + qi * 4);
-      };
-      // P and dS of scores 4g .. 4g+3 of half qb
-      auto smx = [&](int qb, int g) {
-  #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g + e;
-          float p = __builtin_amdgcn_exp2f(fmaf(sv[qb][r], a.sl2, -lv[e]));
-          if constexpr (MASK) {
-            const int qq = q0 + qb * 32 + 8 * g + 4 * (lane >> 5) + e;
-            p = (key > qq || qq >= a.T || qq >= key + a.W) ? 0.f : p;
+      // s: S then P (P wave) or dP then dP - delta (dS wave), per 32-query
+      // half qb: rows = queries, column = this lane's key (the first MFMA of
+      // each half takes a zero accumulator operand, so no register clearing)
+      f32x16 s[2];
+      const f32x16 zero16 = {};
+      bf16x8 f[16];    // fragments read ahead of their MFMAs
+      bf16x8 op[4];    // bf16 P or dS fragments of half f/2, MFMA chunk f%2
+      if (!skip) {
+        if (pw) {
+          // S in 16 steps of one MFMA (Q row fragments three steps ahead);
+          // the exponentials of half 0 between the MFMAs of half 1
+          auto phase1 = [&](auto maskc) {
+            constexpr bool MASK = decltype(maskc)::value;
+            f32x4 lv;
+            auto pexp = [&](int qb, int g) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int r = 4 * g + e;
+                float p = __builtin_amdgcn_exp2f(fmaf(s[qb][r], a.sl2, -lv[e]));
+                if constexpr (MASK) {
+                  const int qq = q0 + qb * 32 + 8 * g + 4 * (lane >> 5) + e;
+                  p = (key > qq || qq >= a.T || qq >= key + a.W) ? 0.f : p;
+                }
+                s[qb][r] = p;
+              }
+            };
+            auto ldl = [&](int qb, int g) { lv = *(const lds_f32x4*)(vec + (qb * 32 + 8 * g + 4 * (lane >> 5)) * 4); };
+            auto rd = [&](int i) { f[i] = *(lds_bf16x8*)(qt_ + (i >> 3) * 8192 + (kbase ^ ((i & 7) << 5))); };
+            rd(0);
+            rd(1);
+            rd(2);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              if (i >= 8 && (i & 1) == 0) {   // lse ahead of this step's fragment read
+                ldl(0, (i - 8) >> 1);
+                __builtin_amdgcn_sched_barrier(0);
+              }
+              if (i + 3 < 16) rd(i + 3);
+              s[i >> 3] = MM::mma(f[i], kvf[i & 7], (i & 7) ? s[i >> 3] : zero16);
+              if (i >= 8 && (i & 1)) pexp(0, (i - 8) >> 1);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              ldl(1, g);
+              pexp(1, g);
+            }
+          };
+          if (need_mask) phase1(std::true_type());
+          else phase1(std::false_type());
+          // P as bf16 fragments, kept for dV and written for the partner
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            op[q] = frag_regs<bf16>(s[q >> 1], (q & 1) * 8);
+            *(__attribute__((address_space(3))) bf16x8*)(pex + q * 1024) = op[q];
           }
-          sv[qb][r] = p;
-          dp[qb][r] = p * (dp[qb][r] - dl[e]);
-        }
-      };
-      bf16x8 pf[2], sf[2];     // bf16 P and dS of the half being multiplied
-      rd(0);
-      rd(1);
-  #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        // lse and delta for the softmax of the next step, read ahead of this
-        // step's fragments: LDS reads complete in order, so waiting for them
-        // then leaves the fragment reads in flight
-        if ((i & 1) == 0 && i >= 8 && i < 24) {
-          ldv(i < 16 ? 0 : 1, (i & 7) >> 1);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        if (i + 2 < 32) rd(i + 2);
-        if (i < 16) {
-          const int qb = i >> 3, ks = i & 7;
-          sv[qb] = MM::mma(fa[i], kf[ks], sv[qb]);   // S  (query x key)
-          dp[qb] = MM::mma(fb[i], vf[ks], dp[qb]);   // dP (query x key)
-          if (qb == 1 && (ks & 1)) smx(0, ks >> 1);
         } else {
-          const int u = i - 16, qb = u >> 3, mm = (u >> 2) & 1, db = u & 3;
-          if ((u & 7) == 0) {
-  #pragma unroll
-            for (int m = 0; m < 2; ++m) {
-              pf[m] = frag_regs<bf16>(sv[qb], m * 8);
-              sf[m] = frag_regs<bf16>(dp[qb], m * 8);
+          // dP in 16 steps of one MFMA (dO row fragments three steps ahead);
+          // dP - delta of half 0 between the MFMAs of half 1
+          f32x4 dl;
+          auto sub = [&](int qb, int g) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s[qb][4 * g + e] -= dl[e];
+          };
+          auto ldd = [&](int qb, int g) {
+            dl = *(const lds_f32x4*)(vec + 1024 + (qb * 32 + 8 * g + 4 * (lane >> 5)) * 4);
+          };
+          auto rd = [&](int i) { f[i] = *(lds_bf16x8*)(ot_ + (i >> 3) * 8192 + (kbase ^ ((i & 7) << 5))); };
+          rd(0);
+          rd(1);
+          rd(2);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            if (i >= 8 && (i & 1) == 0) {
+              ldd(0, (i - 8) >> 1);
+              __builtin_amdgcn_sched_barrier(0);
             }
-            if constexpr (DS) {
-              // chunk 4 wave + 2 qb + m: queries qb*32 + 16m + 4(lane/32) + 0..3 and + 8
-  #pragma unroll
-              for (int m = 0; m < 2; ++m)
-                __builtin_nontemporal_store(__builtin_bit_cast(u32x4, sf[m]), (u32x4*)(dsb + 512 * (2 * qb + m)));
-            }
+            if (i + 3 < 16) rd(i + 3);
+            s[i >> 3] = MM::mma(f[i], kvf[i & 7], (i & 7) ? s[i >> 3] : zero16);
+            if (i >= 8 && (i & 1)) sub(0, (i - 8) >> 1);
+            __builtin_amdgcn_sched_barrier(0);
           }
-          dv[db] = MM::mma(fa[i], pf[mm], dv[db]);     // dV^T += dO^T P
-          dk[db] = MM::mma(fb[i], sf[mm], dk[db]);     // dK^T += Q^T dS
-          if (qb == 0 && (u & 1)) smx(1, u >> 1);
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            ldd(1, g);
+            sub(1, g);
+          }
         }
-        __builtin_amdgcn_sched_barrier(0);
       }
-      };
-      if (need_mask) body(std::true_type());
-      else body(std::false_type());
+      // P written (the barrier waits for this wave's LDS accesses first)
+      ring_barrier();
+      if (!skip) {
+        // 16 MFMAs over (half qb, MFMA chunk mm, d-block db) = (u >> 3,
+        // (u >> 2) & 1, u & 3), transposed fragments three steps ahead
+        if (pw) {
+          // dV^T += dO^T P
+          auto rd = [&](int u) { f[u] = frag_vt_x(ot_, vbase, 2 * (u >> 3) + ((u >> 2) & 1), u & 3); };
+          rd(0);
+          rd(1);
+          rd(2);
+#pragma unroll
+          for (int u = 0; u < 16; ++u) {
+            if (u + 3 < 16) rd(u + 3);
+            acc[u & 3] = MM::mma(f[u], op[u >> 2], acc[u & 3]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        } else {
+          // dS = P (dP - delta) from the partner's P, then dK^T += Q^T dS
+          auto rd = [&](int u) { f[u] = frag_vt_x(qt_, vbase, 2 * (u >> 3) + ((u >> 2) & 1), u & 3); };
+          bf16x8 pp[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) pp[q] = *(const lds_bf16x8*)(pex + q * 1024);
+          rd(0);
+          rd(1);
+          rd(2);
+          auto dsh = [&](int qb) {
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+#pragma unroll
+              for (int e = 0; e < 8; ++e) s[qb][8 * m + e] *= (float)pp[2 * qb + m][e];
+              op[2 * qb + m] = frag_regs<bf16>(s[qb], m * 8);
+              // chunk 4 kw + 2 qb + m: queries qb*32 + 16m + 4(lane/32) + 0..3 and + 8
+              if constexpr (DS)
+                __builtin_nontemporal_store(__builtin_bit_cast(u32x4, op[2 * qb + m]),
+                                            (u32x4*)(dsb + 512 * (2 * qb + m)));
+            }
+          };
+          dsh(0);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int u = 0; u < 16; ++u) {
+            if (u + 3 < 16) rd(u + 3);
+            acc[u & 3] = MM::mma(f[u], op[u >> 2], acc[u & 3]);
+            if (u == 1) dsh(1);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
     }
     // ---- unit boundary
     ++j;
     const int un = unit_of(j);
     const bool more = un < qlen;
     const Unit nxt = more ? make_unit(un) : cur;
-    lds_barrier();                 // the ring is free
-    if (more) issue_kv_rows(nxt);  // into slot 2 and past the ring
-    // dV, then dK, through this wave's staging rows (slots 0-1), out in row
-    // layout; the QK-norm operands of dK's rows are loaded first
-    float* stg = reinterpret_cast<float*>(smem) + wave * 32 * 128;
-    const long row0 = (long)cur.b * a.T + kw0;   // global row of this wave's first key
+    lds_barrier();                       // the ring is free
+    if (more && pw) issue_kv_rows(nxt);  // into slot 2 and past the ring
+    // dV (P waves), then dK (dS waves), through the pair's staging rows in
+    // ring slots 0-1, out in row layout; the QK-norm operands of dK's rows
+    // are loaded while dV is stored
+    float* stg = reinterpret_cast<float*>(smem) + kw * 32 * 128;
+    const long row0 = (long)cur.b * a.T + kw0;   // global row of the pair's first key
     const int nrows = min(32, a.T - kw0);
     bf16* const drow = static_cast<bf16*>(a.dqkv) + row0 * a.LD;
     QkRows qk;
-    // key QK-norm factors: [N][H] after the query ones, head index kvh
-    qk_rows_load(qk, qkv + row0 * a.LD + a.KO + cur.kvh * HD, a.LD, a.rho + ((long)a.B * a.T + row0) * a.H + cur.kvh,
-                 a.H, nrows, lane, a.cs, kw0, a.T);
-    stage_acc(stg, dv, 1.f, lane);
-    mx = fmaxf(mx, store_rows(stg, drow + a.VO + cur.kvh * HD, a.LD, nrows, lane));
-    stage_acc(stg, dk, a.rsd, lane);
-    mx = fmaxf(mx, store_rows_qk(stg, qk, drow + a.KO + cur.kvh * HD, a.LD, nrows, lane));
+    if (pw) {
+      stage_acc(stg, acc, 1.f, lane);
+      mx = fmaxf(mx, store_rows(stg, drow + a.VO + cur.kvh * HD, a.LD, nrows, lane));
+    } else {
+      // key QK-norm factors: [N][H] after the query ones, head index kvh
+      qk_rows_load(qk, qkv + row0 * a.LD + a.KO + cur.kvh * HD, a.LD,
+                   a.rho + ((long)a.B * a.T + row0) * a.H + cur.kvh, a.H, nrows, lane, a.cs, kw0, a.T);
+    }
+    lds_barrier();                       // dV's staging rows read
+    if (!pw) {
+      stage_acc(stg, acc, a.rsd, lane);
+      mx = fmaxf(mx, store_rows_qk(stg, qk, drow + a.KO + cur.kvh * HD, a.LD, nrows, lane));
+    }
     if (!more) break;
-    // the next unit's K, V rows have landed (each wave waits for its own
-    // loads, the barrier for everyone's; the stores above drain too) and the
-    // staging rows are free
-    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
+    // the next unit's K, V rows have landed (the P waves wait for their
+    // loads, the barrier for everyone's) and the staging rows are free
+    if (pw) __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
     lds_barrier();
     cur = nxt;
     read_kv();
-    issue(cur, 0, 0);
-    if (cur.n > 1) issue(cur, 1, 1);
+    if (pw) {
+      issue(cur, 0, 0);
+      if (cur.n > 1) issue(cur, 1, 1);
+    }
   }
   if (a.amax_dqkv) amax_publish<bf16>(a.amax_dqkv, mx);
+}
+
+template <bool DS>
+__global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_bf16_kernel(AttnArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  // the wave index as a scalar: the role branch is uniform
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (wave < 4) dkdv_bf16_role<DS, true>(a, smem, wave);
+  else dkdv_bf16_role<DS, false>(a, smem, wave);
 }
 
 // dQ: one unit of work = 128 queries of one (sequence, head), 4 waves x 32

@@ -25,10 +25,10 @@ void allow_lds(const void* kern, int bytes) {
 int tiles(int n, int t) { return (n + t - 1) / t; }
 
 // dK/dV: three ring slots of Q, dO, lse, delta; between units the K, V rows
-// of a unit take slot 2 and 30 KiB past it
+// of a unit take slot 2 and 30 KiB past it; then 16 KiB of P exchange
 constexpr int DKDV_SLOT = 2 * fa::TILE + 2048;
-constexpr int DKDV_LDS = 2 * DKDV_SLOT + 4 * fa::TILE;
-static_assert(DKDV_LDS >= 3 * DKDV_SLOT && DKDV_LDS <= 160 * 1024, "dK/dV LDS");
+constexpr int DKDV_LDS = 2 * DKDV_SLOT + 4 * fa::TILE + 16384;
+static_assert(DKDV_LDS - 16384 >= 3 * DKDV_SLOT && DKDV_LDS <= 160 * 1024, "dK/dV LDS");
 static_assert(4 * 32 * 128 * 4 <= 2 * DKDV_SLOT, "dK/dV staging rows fit in ring slots 0-1");
 static_assert(4 * 32 * 128 * 4 <= fa::DSQ_LDS, "dQ-from-dS staging rows fit in its two slots");
 // dQ: the K/V ring, then the Q rows of a unit (its dO rows use ring slot 2)
@@ -76,7 +76,7 @@ void attn_bwd_dkdv(const AttnArgs& a, bool bf16, hipStream_t st) {
     // stores dS for the dQ kernel
     auto kern = a.ds ? attn_bwd_dkdv_bf16_kernel<true> : attn_bwd_dkdv_bf16_kernel<false>;
     allow_lds(reinterpret_cast<const void*>(kern), DKDV_LDS);
-    hipLaunchKernelGGL(kern, dim3(std::min(units, cu_count())), dim3(256), DKDV_LDS, st, a);
+    hipLaunchKernelGGL(kern, dim3(std::min(units, cu_count())), dim3(512), DKDV_LDS, st, a);
   } else {
     allow_lds(reinterpret_cast<const void*>(attn_bwd_dkdv_kernel<float>), attn_dkdv_lds<float>());
     hipLaunchKernelGGL(attn_bwd_dkdv_kernel<float>, grid, dim3(256), attn_dkdv_lds<float>(), st, a);
