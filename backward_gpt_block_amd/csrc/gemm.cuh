@@ -184,15 +184,24 @@ __device__ __forceinline__ typename Mfma<TI>::frag load_frag(const char* lds, in
   }
 }
 
-// Workgroup index -> (tile_m, tile_n, split).  Workgroups are dealt round
-// robin to the 8 XCDs; the remap gives each XCD a contiguous run of logical
-// tiles, and tiles are walked in groups of GROUP m-tiles so that an XCD's
-// concurrent tiles share A rows and B columns in its L2.
+// Index v of a workgroup (or of a persistent grid's tile walk) -> logical
+// tile: workgroups are dealt round robin to the 8 XCDs, so index v runs on
+// XCD v % 8; the remap gives XCD x the contiguous run of logical tiles that
+// starts at x q + min(x, r) (q = total / 8, r = total % 8; the first r XCDs
+// take q + 1), which is exactly the number of indices v < total with
+// v % 8 = x, so the map is a bijection for any total.
+__device__ __forceinline__ int xcd_run(int v, int total) {
+  const int q = total / 8, r = total % 8, x = v % 8;
+  return x * q + min(x, r) + v / 8;
+}
+// Workgroup index -> (tile_m, tile_n, split): the XCD remap, then tiles are
+// walked in groups of GROUP m-tiles so that an XCD's concurrent tiles share A
+// rows and B columns in its L2 (and, for split-K weight gradients, one
+// k-slice).
 __device__ __forceinline__ void tile_coords(const GemmArgs& g, int& tm, int& tn, int& split, int GROUP = 8) {
   const int per_split = g.tiles_m * g.tiles_n;
   const int total = per_split * gridDim.y;
-  int pid = blockIdx.x + blockIdx.y * gridDim.x;
-  if (total % 8 == 0) pid = (pid % 8) * (total / 8) + pid / 8;
+  const int pid = xcd_run(blockIdx.x + blockIdx.y * gridDim.x, total);
   split = pid / per_split;
   int t = pid % per_split;
   int group = t / (GROUP * g.tiles_n);
@@ -203,15 +212,16 @@ __device__ __forceinline__ void tile_coords(const GemmArgs& g, int& tm, int& tn,
   tn = in_group / gsize;
 }
 // The same for tile v of a persistent grid of workgroups that walk the
-// total tiles in steps of the grid size: workgroup b runs on XCD b % 8 (the
-// grid is a multiple of 8 whenever total is), so tile v = b + i * grid
-// lands on the same XCD for every i, and the remap gives each XCD a
-// contiguous run of logical tiles exactly as for one workgroup per tile.
+// total tiles in steps of the grid size: workgroup b runs on XCD b % 8, so
+// with a grid that is a multiple of 8 (or no larger than the tile count's
+// one round) tile v = b + i * grid lands on the same XCD for every i, and
+// the remap gives each XCD a contiguous run of logical tiles exactly as for
+// one workgroup per tile.
 __device__ __forceinline__ void tile_coords_v(const GemmArgs& g, int v, int total, bool persistent, int& tm, int& tn,
                                               int& split, int GROUP = 8) {
   const int per_split = g.tiles_m * g.tiles_n;
   int pid = v;
-  if (total % 8 == 0 && (!persistent || gridDim.x % 8 == 0)) pid = (pid % 8) * (total / 8) + pid / 8;
+  if (!persistent || gridDim.x % 8 == 0 || total <= (int)gridDim.x) pid = xcd_run(v, total);
   split = pid / per_split;
   int t = pid % per_split;
   int group = t / (GROUP * g.tiles_n);
