@@ -121,15 +121,19 @@ Fwd8 carve_fwd8(const blk_cfg& c, void* p) {
 
 // Split-K count of a weight gradient: the smallest split count whose
 // workgroups fill at least 85% of their last wave over the 256 CUs (fewer
-// splits, fewer fp32 partials to write and reduce), keeping >= 8 k-steps
-// per split.
+// splits, fewer fp32 partials to write and reduce), then the largest count
+// with the same number of waves (each split's k-range, and so the wave,
+// gets shorter), keeping >= 8 k-steps per split.
 int wgrad_splits(int M, int N, long K, int BK) {
   const long tiles = (long)((M + 255) / 256) * ((N + 255) / 256);
   const long ksteps = (K + BK - 1) / BK;
   const long smax = std::max<long>(1, std::min<long>(32, ksteps / 8));
+  auto waves = [&](long s) { return (tiles * s + 255) / 256; };
   for (long s = 1; s <= smax; ++s) {
-    const long wg = tiles * s, waves = (wg + 255) / 256;
-    if (wg * 100 >= 85 * waves * 256) return (int)s;
+    if (tiles * s * 100 >= 85 * waves(s) * 256) {
+      while (s < smax && waves(s + 1) == waves(s)) ++s;
+      return (int)s;
+    }
   }
   return (int)smax;
 }
