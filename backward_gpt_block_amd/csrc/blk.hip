@@ -819,7 +819,7 @@ DecScratch carve_dec(const blk_dcfg& c, void* p) {
   const long B = c.B, C = c.C, F = c.F, H = c.H;
   const long NS = (c.S_max + dec::KEYS - 1) / dec::KEYS;
   long part = 0;
-  const long nk[4][2] = {{qkv_width(c), C}, {C, C}, {F, C}, {C, F}};   // (N, K) of the four GEMMs
+  const long nk[3][2] = {{qkv_width(c), C}, {C, C}, {C, F}};   // (N, K) of the split GEMMs (FC is unsplit)
   for (const auto& g : nk) part = std::max(part, (long)dec_split((int)B, (int)g[0], (int)g[1]).S * B * g[0]);
   Carver k(p);
   DecScratch d;
@@ -896,13 +896,10 @@ int decode_run(const blk_dcfg& c, const void* x, const void* w_qkv, const void* 
     hipLaunchKernelGGL(dec::dec_resid_norm_kernel, dim3(B), dim3(256), 0, st, (const float*)d.part, so.S, B, C, xb,
                        c.eps, d.y1, d.h2);
   }
-  const DecSplit sf = dec_split(B, F, C);
-  dec_gemm("dec_gemm_fc", d.h2, B, static_cast<const bf16*>(w_fc), F, C, sf, d.part, st);
-  {
-    Timed t("dec_relu2", st);
-    const long n = (long)B * F;
-    hipLaunchKernelGGL(dec::dec_relu2_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                       (const float*)d.part, sf.S, n, d.a);
+  {  // a = relu(h2 W_fc^T)^2 (unsplit: K = C)
+    Timed t("dec_gemm_fc", st);
+    hipLaunchKernelGGL(dec::skinny_gemm_relu2_kernel, dim3(F / dec::NBLK, (B + dec::MBLK - 1) / dec::MBLK), dim3(256),
+                       0, st, (const bf16*)d.h2, B, static_cast<const bf16*>(w_fc), F, C, d.a);
   }
   const DecSplit sp = dec_split(B, C, F);
   dec_gemm("dec_gemm_proj", d.a, B, static_cast<const bf16*>(w_proj), C, F, sp, d.part, st);

@@ -14,7 +14,7 @@
 //   dec_attn_kernel        per 256-key split: max, sum, sum p v
 //   dec_combine_kernel     merge the splits -> o                    [B, C]
 //   dec_resid_norm_kernel  y1 = x + o W_o^T; h2 = rmsnorm(y1)
-//   dec_relu2_kernel       a = relu(h2 W_fc^T)^2
+//   skinny_gemm_relu2      a = relu(h2 W_fc^T)^2, unsplit, in one kernel
 //   dec_out_kernel         y = y1 + a W_proj^T
 #pragma once
 #include "common.cuh"
@@ -117,6 +117,76 @@ __device__ __forceinline__ int clamp_pos(const int* __restrict__ cache_len, int 
 __device__ __forceinline__ bool pos_ok(const int* __restrict__ cache_len, int b, int S_max) {
   const int p = cache_len[b];
   return p >= 0 && p < S_max;
+}
+
+// The FC skinny GEMM with ReLU^2 in its own epilogue: a = bf16(relu(A W^T)^2)
+// over the whole K range in one workgroup per 64 x 32 tile (no split, so no
+// partials and no second kernel; with K = C the A rows a workgroup reads, 64
+// x K, stay small).  Operand layout and MFMA use as in skinny_gemm_kernel;
+// each wave takes the K-steps c = wave, wave + 4, ... and issues the loads
+// of step c + 4 before the MFMAs of step c (two register stages), so its
+// step loop waits about one memory latency instead of one per step.
+// Grid (N/32, ceil(M/64)).
+__global__ __launch_bounds__(256) void skinny_gemm_relu2_kernel(const bf16* __restrict__ A, int M,
+                                                                const bf16* __restrict__ W, int N, int K,
+                                                                bf16* __restrict__ out) {
+  __shared__ float red[4][MBLK * NBLK];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int n0 = blockIdx.x * NBLK, m0 = blockIdx.y * MBLK;
+  const int ksteps = K / KCH;
+  const int l32 = lane & 31, g = lane >> 5;
+  const bf16* wrow = W + (long)(n0 + l32) * K + 32 * g;
+  const int ra = m0 + l32, rb = m0 + 32 + l32;
+  const bool oka = ra < M, okb = rb < M;
+  const bf16* arow = A + (long)(oka ? ra : 0) * K + 32 * g;
+  const bf16* brow = A + (long)(okb ? rb : 0) * K + 32 * g;
+  f32x16 acc0 = {}, acc1 = {};
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  u32x4 w0[4], a0[4], b0[4], w1[4], a1[4], b1[4];
+  auto load = [&](int c, u32x4* wb, u32x4* xa, u32x4* xb) {
+    const long k0 = (long)c * KCH;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      wb[e] = ld16(wrow + k0 + 8 * e);
+      xa[e] = oka ? ld16(arow + k0 + 8 * e) : zero;
+      xb[e] = okb ? ld16(brow + k0 + 8 * e) : zero;
+    }
+  };
+  auto mma = [&](const u32x4* wb, const u32x4* xa, const u32x4* xb) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bf16x8 w8 = __builtin_bit_cast(bf16x8, wb[e]);
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xa[e]), w8, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xb[e]), w8, acc1, 0, 0, 0);
+    }
+  };
+  int c = wv;
+  if (c < ksteps) load(c, w0, a0, b0);
+  while (c < ksteps) {          // stage 0 holds step c
+    const bool n1 = c + 4 < ksteps;
+    if (n1) load(c + 4, w1, a1, b1);
+    mma(w0, a0, b0);
+    if (!n1) break;
+    if (c + 8 < ksteps) load(c + 8, w0, a0, b0);
+    mma(w1, a1, b1);
+    c += 8;
+  }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int r = acc_row(j, lane);
+    red[wv][r * NBLK + l32] = acc0[j];
+    red[wv][(r + 32) * NBLK + l32] = acc1[j];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < MBLK * NBLK / 256; ++i) {
+    const int e = threadIdx.x + 256 * i;
+    const int r = e / NBLK, col = e % NBLK;
+    if (m0 + r < M) {
+      const float u = fmaxf(red[0][e] + red[1][e] + red[2][e] + red[3][e], 0.f);
+      out[(long)(m0 + r) * N + n0 + col] = (bf16)(u * u);
+    }
+  }
 }
 
 // From the QKV partials of row b (products with x itself): times r1 =
@@ -373,15 +443,6 @@ __global__ __launch_bounds__(256) void dec_resid_norm_kernel(const float* __rest
       h2[row * C + c] = (bf16)(v[u] * r);
     }
   }
-}
-
-// a = bf16(relu(sum_s part[s])^2) over n values.
-__global__ __launch_bounds__(256) void dec_relu2_kernel(const float* __restrict__ part, int S, long n,
-                                                        bf16* __restrict__ a) {
-  const long i = (long)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
-  const float u = fmaxf(sum_parts(part, S, n, i), 0.f);
-  a[i] = (bf16)(u * u);
 }
 
 // y = bf16(y1 + sum_s part[s]) over n = B*C values; NaN in the rows of
